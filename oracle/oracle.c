@@ -1,0 +1,326 @@
+/*
+ * oracle.c -- the plain, slow CPU oracle for the fused-epilogue GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, loads or
+ * calls this file; only the tests, the smoke check and the CPU-baseline leg
+ * of the benchmark do.  It shares no code, header, table or constant with the
+ * GPU kernels.
+ *
+ * What it computes, for each requested output element (i, j):
+ *
+ *   D(i,j) = act( alpha * s_a * s_b * sum_p a'(i,p) * b'(p,j)
+ *                 + beta * C(i,j) + bias(i) )
+ *
+ * - The linear-combination surface alpha*op(A)*op(B) + beta*C and the BLAS
+ *   column-major storage convention with op in {N, T}: "CUTLASS" knowledge-base
+ *   page, opening section (the fixed cuBLAS surface) and "CuTe and layouts"
+ *   (column-major strides); "Technical Documentation: NVIDIA/cutlass",
+ *   "Layouts, Tensor Alignment Requirements" (T = row-major, N = column-major).
+ * - The block-scaled sum a'(i,p) = A(i,p) * SFA(i, floor(p/32)), and likewise
+ *   for B with SFB(j, floor(p/32)): same document, "Blackwell SM100 GEMMs",
+ *   "Block Scaled GEMMs" (index-notation formula), vector size 32 for the OCP
+ *   mx types ("Blackwell Block Scaled Narrow Precision Data Types" table).
+ * - The element formats (e4m3, e2m1, ue8m0 bit counts and signedness): same
+ *   document, "Blackwell Narrow Precision Data Types" table; the bit-level
+ *   meaning of each code follows the OCP formats that table points to.
+ * - The epilogue (bias, activation) applied to the GEMM result before the
+ *   store: knowledge-base page, "Epilogues".
+ *
+ * Precision: every element is decoded to an exact double (int64 for int8);
+ * the sum runs in ascending p in double (int64 for the integer path).  Every
+ * product of two decoded operands is exact in double (at most 22 significant
+ * bits), so the only rounding is the fp64 summation, ~1e-12 relative at
+ * K = 8192.  The result is returned unrounded; rounding to the output type is
+ * the comparison's business.
+ *
+ * Built with gcc -O2 (no fast-math) and OpenMP over output elements.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Element type codes used by this file alone. */
+enum {
+    ORC_F32 = 0,
+    ORC_F16 = 1,
+    ORC_BF16 = 2,
+    ORC_I8 = 3,
+    ORC_I32 = 4,
+    ORC_E4M3 = 5,
+    ORC_E2M1 = 6, /* two OCP fp4 codes per byte, even element in the low nibble */
+    ORC_E8M0 = 7,
+};
+
+enum { ORC_ACT_NONE = 0, ORC_ACT_RELU = 1, ORC_ACT_GELU = 2 };
+
+typedef struct {
+    int64_t m, n, k;
+    const void *a;
+    int64_t lda;
+    int32_t op_a; /* 0 = N: A(i,p) at a[i + p*lda];  1 = T: at a[p + i*lda] */
+    int32_t type_a;
+    const void *b;
+    int64_t ldb;
+    int32_t op_b; /* 0 = N: B(p,j) at b[p + j*ldb];  1 = T: at b[j + p*ldb] */
+    int32_t type_b;
+    const void *c; /* may be NULL when beta == 0 */
+    int64_t ldc;   /* C(i,j) at c[i + j*ldc] */
+    int32_t type_c;
+    int32_t type_bias;
+    const void *bias; /* length m, NULL for none */
+    double alpha, beta;
+    double a_scale, b_scale; /* per-tensor scales (fp8); 1 otherwise */
+    const uint8_t *sfa;      /* E8M0 block scales, SFA(i,kb) at sfa[i*ld_sfa + kb]; NULL for none */
+    int64_t ld_sfa;
+    const uint8_t *sfb; /* SFB(j,kb) at sfb[j*ld_sfb + kb] */
+    int64_t ld_sfb;
+    int32_t act;
+    int32_t block; /* scale-vector size along K (32 for MX) */
+} oracle_problem;
+
+/* ---------------------------------------------------------------- decoders */
+
+/* IEEE binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits. */
+static double dec_f16(uint16_t h)
+{
+    int s = h >> 15, e = (h >> 10) & 0x1f, f = h & 0x3ff;
+    double mag;
+    if (e == 0)
+        mag = ldexp((double)f, -24); /* subnormal: f * 2^-10 * 2^-14 */
+    else if (e == 31)
+        mag = f ? NAN : INFINITY;
+    else
+        mag = ldexp((double)(1024 + f), e - 25); /* (1 + f/1024) * 2^(e-15) */
+    return s ? -mag : mag;
+}
+
+/* bfloat16: 1 sign, 8 exponent (bias 127), 7 fraction bits. */
+static double dec_bf16(uint16_t h)
+{
+    int s = h >> 15, e = (h >> 7) & 0xff, f = h & 0x7f;
+    double mag;
+    if (e == 0)
+        mag = ldexp((double)f, -133); /* f * 2^-7 * 2^-126 */
+    else if (e == 255)
+        mag = f ? NAN : INFINITY;
+    else
+        mag = ldexp((double)(128 + f), e - 134);
+    return s ? -mag : mag;
+}
+
+/* IEEE binary32, read from its bits the same way. */
+static double dec_f32(uint32_t w)
+{
+    int s = w >> 31, e = (w >> 23) & 0xff;
+    uint32_t f = w & 0x7fffff;
+    double mag;
+    if (e == 0)
+        mag = ldexp((double)f, -149);
+    else if (e == 255)
+        mag = f ? NAN : INFINITY;
+    else
+        mag = ldexp((double)(0x800000u + f), e - 150);
+    return s ? -mag : mag;
+}
+
+/* OCP E4M3 ("fn"): 1 sign, 4 exponent (bias 7), 3 mantissa bits; no
+ * infinities, S.1111.111 is NaN, largest finite magnitude 448. */
+static double dec_e4m3(uint8_t q)
+{
+    int s = q >> 7, e = (q >> 3) & 0xf, f = q & 7;
+    double mag;
+    if ((q & 0x7f) == 0x7f)
+        mag = NAN;
+    else if (e == 0)
+        mag = ldexp((double)f, -9); /* f/8 * 2^-6 */
+    else
+        mag = ldexp((double)(8 + f), e - 10); /* (1 + f/8) * 2^(e-7) */
+    return s ? -mag : mag;
+}
+
+/* OCP E2M1: 1 sign, 2 exponent (bias 1), 1 mantissa bit; all codes finite. */
+static double dec_e2m1(unsigned nib)
+{
+    int s = (nib >> 3) & 1, e = (nib >> 1) & 3, f = nib & 1;
+    double mag;
+    if (e == 0)
+        mag = 0.5 * f; /* subnormal: f/2 * 2^0 */
+    else
+        mag = ldexp((double)(2 + f), e - 2); /* (1 + f/2) * 2^(e-1) */
+    return s ? -mag : mag;
+}
+
+/* OCP E8M0 scale: 8 exponent bits, bias 127, no sign or mantissa; 0xff NaN. */
+static double dec_e8m0(uint8_t x)
+{
+    return x == 0xff ? NAN : ldexp(1.0, (int)x - 127);
+}
+
+/* Decode element `idx` (in elements) of a buffer of the given type. */
+static double load_real(const void *base, int32_t type, int64_t idx)
+{
+    switch (type) {
+    case ORC_F32: {
+        uint32_t w;
+        memcpy(&w, (const char *)base + 4 * idx, 4);
+        return dec_f32(w);
+    }
+    case ORC_F16: {
+        uint16_t h;
+        memcpy(&h, (const char *)base + 2 * idx, 2);
+        return dec_f16(h);
+    }
+    case ORC_BF16: {
+        uint16_t h;
+        memcpy(&h, (const char *)base + 2 * idx, 2);
+        return dec_bf16(h);
+    }
+    case ORC_I8:
+        return (double)((const int8_t *)base)[idx];
+    case ORC_I32: {
+        int32_t v;
+        memcpy(&v, (const char *)base + 4 * idx, 4);
+        return (double)v;
+    }
+    case ORC_E4M3:
+        return dec_e4m3(((const uint8_t *)base)[idx]);
+    case ORC_E2M1: {
+        uint8_t byte = ((const uint8_t *)base)[idx >> 1];
+        return dec_e2m1((idx & 1) ? (byte >> 4) : (byte & 0xf));
+    }
+    case ORC_E8M0:
+        return dec_e8m0(((const uint8_t *)base)[idx]);
+    }
+    return NAN;
+}
+
+static int64_t load_int(const void *base, int32_t type, int64_t idx)
+{
+    if (type == ORC_I8)
+        return ((const int8_t *)base)[idx];
+    if (type == ORC_I32) {
+        int32_t v;
+        memcpy(&v, (const char *)base + 4 * idx, 4);
+        return v;
+    }
+    return 0;
+}
+
+/* Public decoder, so that tests can pin each format on every code. */
+int oracle_decode(int32_t type, const void *src, int64_t count, double *out)
+{
+    if (type < ORC_F32 || type > ORC_E8M0)
+        return -1;
+    for (int64_t t = 0; t < count; ++t)
+        out[t] = load_real(src, type, t);
+    return 0;
+}
+
+/* ---------------------------------------------------------------- indexing */
+
+static int64_t a_index(const oracle_problem *p, int64_t i, int64_t q)
+{
+    return p->op_a == 0 ? i + q * p->lda : q + i * p->lda;
+}
+
+static int64_t b_index(const oracle_problem *p, int64_t q, int64_t j)
+{
+    return p->op_b == 0 ? q + j * p->ldb : j + q * p->ldb;
+}
+
+/* ---------------------------------------------------------------- epilogue */
+
+static double activate(int32_t act, double t)
+{
+    if (act == ORC_ACT_RELU)
+        return t > 0.0 ? t : 0.0;
+    if (act == ORC_ACT_GELU)
+        return 0.5 * t * (1.0 + erf(t / sqrt(2.0))); /* erf form of GELU */
+    return t;
+}
+
+static int is_integer_path(const oracle_problem *p)
+{
+    return p->type_a == ORC_I8 && p->type_b == ORC_I8;
+}
+
+/* One output element, floating-point path. */
+static double element_real(const oracle_problem *p, int64_t i, int64_t j)
+{
+    double acc = 0.0;
+    for (int64_t q = 0; q < p->k; ++q) {
+        double a = load_real(p->a, p->type_a, a_index(p, i, q));
+        double b = load_real(p->b, p->type_b, b_index(p, q, j));
+        if (p->sfa)
+            a *= dec_e8m0(p->sfa[i * p->ld_sfa + q / p->block]);
+        if (p->sfb)
+            b *= dec_e8m0(p->sfb[j * p->ld_sfb + q / p->block]);
+        acc += a * b;
+    }
+    /* Per-tensor scales multiply the finished sum (one rounding). */
+    double t = p->alpha * (p->a_scale * p->b_scale * acc);
+    if (p->beta != 0.0)
+        t += p->beta * load_real(p->c, p->type_c, i + j * p->ldc);
+    if (p->bias)
+        t += load_real(p->bias, p->type_bias, i);
+    return activate(p->act, t);
+}
+
+/* One output element, integer path: exact in int64. */
+static int64_t element_int(const oracle_problem *p, int64_t i, int64_t j)
+{
+    int64_t acc = 0;
+    for (int64_t q = 0; q < p->k; ++q)
+        acc += load_int(p->a, ORC_I8, a_index(p, i, q)) * load_int(p->b, ORC_I8, b_index(p, q, j));
+    int64_t t = (int64_t)p->alpha * acc;
+    if (p->beta != 0.0)
+        t += (int64_t)p->beta * load_int(p->c, p->type_c, i + j * p->ldc);
+    if (p->bias)
+        t += load_int(p->bias, p->type_bias, i);
+    if (p->act == ORC_ACT_RELU && t < 0)
+        t = 0;
+    return t;
+}
+
+/*
+ * Evaluate `count` output elements (rows[t], cols[t]).  Floating results go
+ * to out_real, integer results (int8 x int8) to out_int; the other pointer
+ * may be NULL.  nthreads <= 0 means "all OpenMP threads".  Returns 0, or -1
+ * on a request outside the problem.
+ */
+int oracle_gemm_elements(const oracle_problem *p, int64_t count, const int64_t *rows,
+                         const int64_t *cols, double *out_real, int64_t *out_int, int nthreads)
+{
+    for (int64_t t = 0; t < count; ++t)
+        if (rows[t] < 0 || rows[t] >= p->m || cols[t] < 0 || cols[t] >= p->n)
+            return -1;
+    int integer = is_integer_path(p);
+    if ((integer && !out_int) || (!integer && !out_real))
+        return -1;
+#ifdef _OPENMP
+    int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 16) num_threads(nt)
+#endif
+    for (int64_t t = 0; t < count; ++t) {
+        if (integer)
+            out_int[t] = element_int(p, rows[t], cols[t]);
+        else
+            out_real[t] = element_real(p, rows[t], cols[t]);
+    }
+    (void)nthreads;
+    return 0;
+}
+
+/* Number of threads an OpenMP region would use here (for reporting). */
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
