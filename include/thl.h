@@ -1,0 +1,206 @@
+/*
+ * thl.h -- C ABI of the MI355X (gfx950) tiled GEMM with a fused epilogue,
+ *
+ *     D = act(alpha * s_a * s_b * op(A) * op(B) + beta * C + bias)
+ *
+ * and of the host-side Shape:Stride layout module that generates and checks
+ * the kernels' index maps.  Plain C: no C++ or torch types cross it; the only
+ * HIP type is the stream, declared as the struct pointer hipStream_t is.
+ *
+ * Sources of the operation (page titles and sections):
+ *  - "CUTLASS" (knowledge-base page), opening section: the fixed BLAS surface
+ *    C = alpha*op(A)*op(B) + beta*C, and "Epilogues": bias, activation and
+ *    scaling applied in the GEMM's output stage with no second pass over C.
+ *  - same page: the device GEMM call takes {m,n,k}, {A,lda}, {B,ldb},
+ *    {C,ldc}, {D,ldd}, {alpha,beta} and returns a status; "Technical
+ *    Documentation: NVIDIA/cutlass", "Launching a GEMM kernel in CUDA": D may
+ *    be the same tensor as C.
+ *  - same document, "CUTLASS Library": the library picks the first kernel
+ *    whose data types, layouts and alignment fit the problem.
+ *  - same document, "Blackwell SM100 GEMMs": T = row-major, N = column-major
+ *    ("Layouts, Tensor Alignment Requirements"); block-scaled GEMM
+ *    D_ij = C_ij + sum_k (A_ik * SFA_{i,k/32}) * (B_jk * SFB_{j,k/32})
+ *    ("Block Scaled GEMMs"); element formats e4m3, e2m1, ue8m0 and the
+ *    OCP mx types with 32-element scale vectors (the two format tables).
+ *  - "CuTe's layout algebra": every layout operation below.
+ */
+#ifndef THL_H_
+#define THL_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t; /* hipStream_t is `struct ihipStream_t*`; NULL = the default stream */
+
+typedef enum {
+  THL_OK = 0,
+  THL_ERR_INVALID = -1,     /* bad dimension, leading dimension, pointer, overlap or argument */
+  THL_ERR_UNSUPPORTED = -2, /* a dtype / op / epilogue / scale combination that is not built */
+  THL_ERR_MISALIGNED = -3,  /* a pointer or leading dimension breaks every kernel's alignment */
+  THL_ERR_HIP = -4,         /* the HIP runtime reported an error while launching */
+  THL_ERR_UNDEFINED = -5    /* layout algebra: the operation is undefined (divisibility, overlap) */
+} thl_status;
+
+/* op(X): N = X as stored, T = its transpose (BLAS convention). */
+typedef enum { THL_OP_N = 0, THL_OP_T = 1 } thl_op;
+
+typedef enum {
+  THL_F32 = 0,
+  THL_F16 = 1,
+  THL_BF16 = 2,
+  THL_I8 = 3,
+  THL_I32 = 4,
+  THL_E4M3 = 5,   /* OCP fp8 E4M3 ("fn": bias 7, no infinities, S.1111.111 NaN, max 448) */
+  THL_E2M1X2 = 6, /* OCP fp4 E2M1, two per byte along the contiguous dimension, even element low nibble */
+  THL_E8M0 = 7,   /* OCP E8M0 scale: 2^(code-127), 0xff NaN */
+  THL_NONE = 8    /* "no such operand" (bias dtype when there is no bias) */
+} thl_dtype;
+
+typedef struct {
+  thl_dtype a, b; /* operand formats; a == b is required (F16, BF16, I8, E4M3, E2M1X2) */
+  thl_dtype c;    /* format of C: F32, F16 or BF16 for float paths, I32 for the int8 path */
+  thl_dtype d;    /* format of D: F32, F16 or BF16 (float paths), I32 (int8 path) */
+  thl_dtype bias; /* format of the bias vector: F32, F16, BF16, or I32 (int8 path) */
+  thl_dtype acc;  /* accumulation: F32 for float paths, I32 for int8 */
+} thl_dtypes;
+
+/* Epilogue flags: RELU and GELU exclusive.  Order: act(alpha*acc + beta*C + bias).
+ * GELU is the erf form 0.5*x*(1+erf(x/sqrt 2)). */
+enum { THL_EPI_NONE = 0, THL_EPI_BIAS = 1, THL_EPI_RELU = 2, THL_EPI_GELU = 4 };
+
+typedef struct {
+  unsigned flags;   /* THL_EPI_* bits */
+  const void* bias; /* device pointer, length m (bias[i] is added to row i), when THL_EPI_BIAS */
+} thl_epilogue;
+
+typedef struct {
+  float a_scale, b_scale; /* per-tensor scales (host values), used for E4M3; 1.0f otherwise */
+  const uint8_t* sfa;     /* E2M1X2: E8M0 block scales of A, SFA(i,kb) at sfa[i*ld_sfa + kb], device */
+  int64_t ld_sfa;         /* >= k/32 */
+  const uint8_t* sfb;     /* E2M1X2: SFB(j,kb) at sfb[j*ld_sfb + kb], device */
+  int64_t ld_sfb;         /* >= k/32 */
+} thl_scales;
+
+/*
+ * thl_gemm -- D = act(alpha * s_a * s_b * op(A) * op(B) + beta * C + bias[i]).
+ *
+ * Shapes: op(A) is m x k, op(B) is k x n, C and D are m x n.  Storage is BLAS
+ * column-major with leading dimensions in elements:
+ *   opA = N: A(i,p) at A[i + p*lda], lda >= max(1,m);   opA = T: at A[p + i*lda], lda >= max(1,k)
+ *   opB = N: B(p,j) at B[p + j*ldb], ldb >= max(1,k);   opB = T: at B[j + p*ldb], ldb >= max(1,n)
+ *   C(i,j) at C[i + j*ldc], ldc >= max(1,m);  D(i,j) at D[i + j*ldd], ldd >= max(1,m).
+ * For E2M1X2 the leading dimension counts fp4 elements and must be even.
+ *
+ * Built combinations (first fitting kernel is launched):
+ *   F16 or BF16 operands, opA/opB in {N,T}: F32 accumulate; C, D in F32/F16/BF16.
+ *   I8 operands, opA = T, opB = N: I32 accumulate, C and D I32, bias I32;
+ *     alpha must be 1 and beta 0 or 1 (the integer epilogue is exact, in int32).
+ *   E4M3 operands, opA = T, opB = N: F32 accumulate, s_a, s_b = scales->a_scale,
+ *     b_scale folded with alpha into one fp32 factor.
+ *   E2M1X2 operands, opA = T, opB = N, k % 32 == 0: F32 accumulate, element
+ *     (i,p) of A multiplied by 2^(SFA(i, p/32) - 127), likewise B with SFB(j, p/32).
+ *
+ * Ownership: A, B, C, D, bias, sfa, sfb are device pointers owned by the
+ * caller; the library allocates nothing and keeps no pointer after return.
+ * alpha, beta and the per-tensor scales are host values.
+ *
+ * Semantics: beta == 0 means C is not read (it may be NULL and may hold NaN).
+ * D may alias C exactly (same pointer, ldc == ldd, c and d the same format);
+ * any other overlap of D with A, B, C, bias or the scales is THL_ERR_INVALID.
+ * m == 0 or n == 0 returns THL_OK with no launch; k == 0 gives
+ * D = act(beta*C + bias).
+ *
+ * Errors: every check runs before any HIP call; on an error nothing is
+ * enqueued and D is untouched.  The call is asynchronous: it returns once
+ * the kernel is enqueued on `stream`, and faults during execution surface at
+ * the caller's next synchronisation on that stream.  Reentrant; thread-safe.
+ */
+thl_status thl_gemm(int64_t m, int64_t n, int64_t k,
+                    const void* A, int64_t lda, thl_op opA,
+                    const void* B, int64_t ldb, thl_op opB,
+                    const void* C, int64_t ldc,
+                    void* D, int64_t ldd,
+                    float alpha, float beta,
+                    const thl_dtypes* dtypes, const thl_epilogue* epilogue,
+                    const thl_scales* scales, struct ihipStream_t* stream);
+
+/* Static text for a status code. */
+const char* thl_status_string(int status);
+
+/* Name of the kernel variant the calling thread's last successful thl_gemm
+ * launched ("" before any); the storage is thread-local and stays valid until
+ * the thread's next thl_gemm call. */
+const char* thl_last_variant(void);
+
+/* Number of kernel variants built into the library, and the name of each
+ * (static strings).  Setting THL_FORCE_VARIANT=<name> in the environment makes
+ * thl_gemm launch that variant, or fail with THL_ERR_UNSUPPORTED when it does
+ * not fit the problem (tests use it to cover every variant). */
+int thl_variant_count(void);
+const char* thl_variant_name(int index);
+
+/*
+ * thl_kernel_index_map -- evaluate one of the kernels' closed-form index
+ * functions on the host, for checking against the layout module.
+ *   map     name of the map (thl_kernel_index_map_names lists them)
+ *   params  map parameters (e.g. tile counts), may be NULL when none
+ *   n       number of points; in[2*t], in[2*t+1] are the two arguments
+ *   out     out[2*t], out[2*t+1] receive the two results
+ * These are the same `__host__ __device__` functions the kernels call.
+ * Returns THL_OK, or THL_ERR_INVALID for an unknown name or bad arguments.
+ */
+int thl_kernel_index_map(const char* map, const int64_t* params, int64_t n, const int64_t* in, int64_t* out);
+/* Comma-separated names of every map thl_kernel_index_map knows (static). */
+const char* thl_kernel_index_map_names(void);
+
+/*
+ * Layout algebra ("CuTe's layout algebra").  Host only, run-time integers,
+ * full simplification.  A layout is text "shape:stride" with nested tuples,
+ * e.g. "(4,(2,4)):(2,(1,8))"; a bare shape means the compact column-major
+ * layout; underscores are ignored so "_12:_1" parses.  A tiler is one layout
+ * per mode, separated by ';' ("2:1;2:1").  Results are written to `out` as
+ * NUL-terminated text of at most `cap` bytes.  Each returns THL_OK,
+ * THL_ERR_INVALID (parse error, mismatched structure, output too small, index
+ * out of range) or THL_ERR_UNDEFINED (the operation is undefined: a shape or
+ * stride divisibility condition fails, or the modes overlap).
+ */
+int thl_layout_coalesce(const char* a, char* out, size_t cap);
+/* R = A o B, R(c) = A(B(c)), R has B's shape; b may be a ';' tiler (mode by mode). */
+int thl_layout_composition(const char* a, const char* b, char* out, size_t cap);
+/* A* such that (A, A*) covers [0, cotarget) exactly once. */
+int thl_layout_complement(const char* a, int64_t cotarget, char* out, size_t cap);
+/* A o (B, complement(B, size A)); b may be a ';' tiler. */
+int thl_layout_logical_divide(const char* a, const char* b, char* out, size_t cap);
+/* ((within-tile modes), (tile-index modes)). */
+int thl_layout_zipped_divide(const char* a, const char* tiler, char* out, size_t cap);
+/* ((within-tile modes), tile-index mode 0, tile-index mode 1, ...). */
+int thl_layout_tiled_divide(const char* a, const char* tiler, char* out, size_t cap);
+/* (within-tile modes..., tile-index modes...). */
+int thl_layout_flat_divide(const char* a, const char* tiler, char* out, size_t cap);
+/* The tile with one-dimensional tile index `tile`: its layout, and *offset = index of its origin. */
+int thl_layout_local_tile(const char* a, const char* tiler, int64_t tile, int64_t* offset, char* out, size_t cap);
+/* Thread `tid`'s values when A is divided by the shape of `threads`: *offset is
+ * the index of its within-tile position p (threads(p) == tid); the layout is the tile-index mode. */
+int thl_layout_local_partition(const char* a, const char* threads, int64_t tid, int64_t* offset, char* out,
+                               size_t cap);
+/* out[i] = A(crd[i]) for one-dimensional coordinates. */
+int thl_layout_eval(const char* a, const int64_t* crd, int64_t n, int64_t* out);
+/* *out = A(coord) for a top-level or nested coordinate written as text, e.g. "(1,(1,2))". */
+int thl_layout_eval_coord(const char* a, const char* coord, int64_t* out);
+/* size, cosize (largest index + 1) and rank (top-level modes); any pointer may be NULL. */
+int thl_layout_info(const char* a, int64_t* size, int64_t* cosize, int64_t* rank);
+/* Mode i of A as a layout. */
+int thl_layout_mode(const char* a, int64_t i, char* out, size_t cap);
+/* out[i] = swz(A(crd[i])) with swz(x) = x ^ (((x >> (m+s)) & (2^b - 1)) << m):
+ * the XOR function composed on top of a layout (used for LDS bank spreading). */
+int thl_swizzle_eval(int b, int m, int s, const char* a, const int64_t* crd, int64_t n, int64_t* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* THL_H_ */

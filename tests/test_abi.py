@@ -1,0 +1,147 @@
+"""The C-ABI library loads, exports every function include/thl.h declares,
+and rejects bad problems before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tile_hierarchy_linear_amd as thl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "thl.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(thl_[a-z0-9_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for must in ("thl_gemm", "thl_status_string", "thl_last_variant", "thl_layout_coalesce",
+                 "thl_layout_composition", "thl_layout_complement", "thl_layout_logical_divide",
+                 "thl_layout_zipped_divide", "thl_layout_local_tile", "thl_layout_local_partition",
+                 "thl_kernel_index_map"):
+        assert must in names
+
+
+@pytest.mark.parametrize("name", _declared_functions())
+def test_every_declared_symbol_is_exported(name):
+    lib = ctypes.CDLL(thl.LIB_PATH)
+    assert hasattr(lib, name), name
+
+
+def test_binding_names_match_the_c_entry_points():
+    for name in _declared_functions():
+        assert hasattr(thl, name), f"binding lacks {name}"
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, -5):
+        assert thl.thl_status_string(s)
+    assert "unknown" in thl.thl_status_string(7)
+
+
+def test_variants_are_listed():
+    vs = thl.variants()
+    assert len(vs) == thl.thl_variant_count() > 0
+    for fam in ("bf16", "f16", "i8", "e4m3", "e2m1"):
+        assert any(v.startswith(fam + "_") for v in vs)
+    assert thl.thl_variant_name(-1) is None and thl.thl_variant_name(len(vs)) is None
+
+
+# Fake (never dereferenced) device addresses, 256-byte aligned and far apart.
+A, B, C, D, BIAS, SFA, SFB = (0x10000000 * i for i in range(1, 8))
+
+
+def call(m=64, n=64, k=64, a=A, lda=None, opa="T", b=B, ldb=None, opb="N", c=None, ldc=None, d=D, ldd=None,
+         alpha=1.0, beta=0.0, types=("bf16", "f32", "f32", "none"), flags=0, bias=None, sc=None):
+    ta, tc, td, tb = types
+    lda = lda if lda is not None else max(1, k if opa == "T" else m)
+    ldb = ldb if ldb is not None else max(1, k if opb == "N" else n)
+    ldc = ldc if ldc is not None else max(1, m)
+    ldd = ldd if ldd is not None else max(1, m)
+    dts = thl.make_dtypes(ta, ta, tc, td, tb)
+    epi = thl.thl_epilogue(flags, bias)
+    return thl.thl_gemm(m, n, k, a, lda, opa, b, ldb, opb, c, ldc, d, ldd, alpha, beta, dts, epi, sc, None)
+
+
+def test_negative_dimensions():
+    assert call(m=-1) == thl.THL_ERR_INVALID
+    assert call(k=-5) == thl.THL_ERR_INVALID
+
+
+def test_leading_dimension_too_small():
+    assert call(lda=63) == thl.THL_ERR_INVALID
+    assert call(ldb=10) == thl.THL_ERR_INVALID
+    assert call(ldd=32) == thl.THL_ERR_INVALID
+    assert call(beta=1.0, c=C, ldc=8) == thl.THL_ERR_INVALID
+
+
+def test_null_pointers():
+    assert call(d=None) == thl.THL_ERR_INVALID
+    assert call(a=None) == thl.THL_ERR_INVALID
+    assert call(beta=1.0, c=None) == thl.THL_ERR_INVALID
+    assert call(flags=thl.THL_EPI_BIAS, bias=None, types=("bf16", "f32", "f32", "f32")) == thl.THL_ERR_INVALID
+
+
+def test_bad_flags_and_ops():
+    assert call(flags=thl.THL_EPI_RELU | thl.THL_EPI_GELU) == thl.THL_ERR_INVALID
+    assert call(flags=64) == thl.THL_ERR_INVALID
+    assert call(opa=7) == thl.THL_ERR_INVALID
+
+
+def test_unsupported_combinations():
+    assert call(types=("f32", "f32", "f32", "none")) == thl.THL_ERR_UNSUPPORTED  # fp32 operands
+    dts = thl.make_dtypes("bf16", "f16", "f32", "f32")
+    assert thl.thl_gemm(64, 64, 64, A, 64, "T", B, 64, "N", None, 64, D, 64, 1.0, 0.0, dts, None, None,
+                        None) == thl.THL_ERR_UNSUPPORTED
+    assert call(types=("i8", "f32", "f32", "none")) == thl.THL_ERR_UNSUPPORTED  # int8 needs int32 out
+    assert call(types=("i8", "i32", "i32", "none"), alpha=2.0) == thl.THL_ERR_UNSUPPORTED
+    assert call(types=("i8", "i32", "i32", "none"), beta=0.5, c=C) == thl.THL_ERR_UNSUPPORTED
+    assert call(types=("i8", "i32", "i32", "none"), opa="N") == thl.THL_ERR_UNSUPPORTED
+    sc = thl.thl_scales(1.0, 1.0, SFA, 1, SFB, 1)
+    assert call(types=("e2m1", "f32", "bf16", "none"), k=48, sc=sc) == thl.THL_ERR_UNSUPPORTED  # k % 32
+    assert call(types=("e4m3", "f32", "bf16", "none"), opb="T") == thl.THL_ERR_UNSUPPORTED
+
+
+def test_mxfp4_needs_scales():
+    assert call(types=("e2m1", "f32", "bf16", "none"), sc=None) == thl.THL_ERR_INVALID
+    sc = thl.thl_scales(1.0, 1.0, SFA, 1, SFB, 2)  # ld_sfa < k/32
+    assert call(types=("e2m1", "f32", "bf16", "none"), sc=sc) == thl.THL_ERR_INVALID
+    sc = thl.thl_scales(1.0, 1.0, SFA, 2, SFB, 2)
+    assert call(types=("e2m1", "f32", "bf16", "none"), lda=65, sc=sc) == thl.THL_ERR_INVALID  # odd ld
+
+
+def test_misaligned():
+    # bf16 rows of 63 elements = 126 bytes: not 4-byte aligned for any variant
+    assert call(k=63, lda=63, ldb=64) == thl.THL_ERR_MISALIGNED
+    assert call(a=A + 2) == thl.THL_ERR_MISALIGNED
+
+
+def test_overlaps():
+    # D over A
+    assert call(d=A) == thl.THL_ERR_INVALID
+    assert call(d=B + 64) == thl.THL_ERR_INVALID
+    # partial overlap with C
+    assert call(beta=1.0, c=C, d=C + 4) == thl.THL_ERR_INVALID
+    # bias overlapping D
+    assert call(flags=thl.THL_EPI_BIAS, bias=D + 8, types=("bf16", "f32", "f32", "f32")) == thl.THL_ERR_INVALID
+
+
+def test_quick_returns_do_not_launch():
+    # m == 0 or n == 0: OK without touching the device (works without a GPU)
+    assert call(m=0) == thl.THL_OK
+    assert call(n=0) == thl.THL_OK
+    assert call(m=0, n=0, k=0, a=None, b=None, d=None) == thl.THL_OK
+
+
+def test_forced_variant_must_fit():
+    os.environ["THL_FORCE_VARIANT"] = "i8_tn_256x256_w2x2_v16"
+    try:
+        assert call(m=0) == thl.THL_ERR_UNSUPPORTED  # bf16 problem, int8 variant
+    finally:
+        del os.environ["THL_FORCE_VARIANT"]

@@ -1,0 +1,220 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle
+on the same seeded inputs.
+
+Bar: int8 bit-exact; float outputs within
+2^-20 * K * |alpha| * max|a'| * max|b'| (* 1.13 for GELU) + one output ulp.
+Small shapes are checked in full (several tiles plus ragged tails); the
+large configurations on a seeded sample of 4096 outputs plus, for ragged
+shapes, the full last row and column.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    _gpu()
+    import oracle
+
+    oracle.build(force=False)
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _check_full(w, prob=None, variant=None):
+    import oracle
+    from oracle import compare
+    from workloads.device import DeviceProblem
+
+    if variant:
+        os.environ["THL_FORCE_VARIANT"] = variant
+    try:
+        _say(f"[parity full] {w.name} m={w.m} n={w.n} k={w.k} op={w.op_a}{w.op_b} act={w.act} "
+             f"beta={w.beta} bias={w.bias is not None} variant={variant}")
+        dp = DeviceProblem(w)
+        st = dp.run()
+        assert st == 0, f"thl_gemm status {st}"
+        torch.cuda.synchronize()
+    finally:
+        os.environ.pop("THL_FORCE_VARIANT", None)
+    got = dp.d_all()
+    ii, jj = np.meshgrid(np.arange(w.m), np.arange(w.n), indexing="ij")
+    res = compare.parity_check(w, got.ravel(), ii.ravel(), jj.ravel())
+    assert res["ok"], res
+    return dp
+
+
+def _check_sampled(w, extra_edges=False):
+    from oracle import compare
+    from workloads.device import DeviceProblem
+
+    _say(f"[parity sampled] {w.name} m={w.m} n={w.n} k={w.k}")
+    dp = DeviceProblem(w)
+    st = dp.run()
+    assert st == 0, f"thl_gemm status {st}"
+    torch.cuda.synchronize()
+    rows, cols = w.sample(4096)
+    if extra_edges:
+        rows = np.concatenate([rows, np.full(w.n, w.m - 1), np.arange(w.m)])
+        cols = np.concatenate([cols, np.arange(w.n), np.full(w.m, w.n - 1)])
+    res = compare.parity_check(w, dp.d_values(rows, cols), rows, cols)
+    assert res["ok"], res
+    # nothing outside D was written: the padding rows of ld stay untouched
+    return dp
+
+
+# ------------------------------------------------------------ configuration 1
+
+def test_fp16_256_full():
+    import workloads as wl
+
+    _check_full(wl.make("fp16", 256, 256, 256))
+
+
+# ------------------------------------------------------------ small sweeps
+
+SHAPES = [(1, 1, 1), (2, 3, 5), (7, 17, 33), (64, 64, 64), (65, 127, 129), (129, 65, 255), (257, 255, 64),
+          (300, 200, 520)]
+
+
+def _pad(x, q):
+    return (x + q - 1) // q * q
+
+
+@pytest.mark.parametrize("kind", ["fp16", "int8", "fp8"])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_small_shapes_full(kind, shape):
+    import workloads as wl
+
+    m, n, k = shape
+    # leading dimensions padded to 16 bytes so the fast variants apply with ragged K
+    q = 8 if kind == "fp16" else 16
+    w = wl.make(kind, m, n, k, lda=_pad(k, q), ldb=_pad(k, q))
+    _check_full(w)
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 32), (7, 17, 64), (65, 127, 288), (129, 65, 512), (300, 200, 1024)])
+def test_small_shapes_mxfp4_full(shape):
+    import workloads as wl
+
+    m, n, k = shape
+    _check_full(wl.make("mxfp4", m, n, k, lda=_pad(k, 32), ldb=_pad(k, 32)))
+
+
+@pytest.mark.parametrize("act", ["none", "relu", "gelu"])
+@pytest.mark.parametrize("kind", ["fp16", "fp8"])
+def test_epilogue_variants(kind, act):
+    import workloads as wl
+
+    w = wl.make(kind, 190, 130, 96, act=act, bias=True, beta=0.75)
+    if w.c is None:
+        pytest.skip("kind without C")
+    _check_full(w)
+
+
+def test_int8_epilogue_bias_beta_relu():
+    import workloads as wl
+
+    _check_full(wl.make("int8", 130, 70, 200, lda=208, ldb=208, act="relu", bias=True, beta=1.0))
+
+
+@pytest.mark.parametrize("variant_family", ["f16", "bf16", "i8", "e4m3", "e2m1"])
+def test_every_variant(variant_family):
+    import tile_hierarchy_linear_amd as thl
+    import workloads as wl
+
+    kind = {"f16": "fp16", "bf16": "fp16", "i8": "int8", "e4m3": "fp8", "e2m1": "mxfp4"}[variant_family]
+    for v in thl.variants():
+        if not v.startswith(variant_family + "_"):
+            continue
+        m, n, k = 300, 260, 512
+        if variant_family == "bf16":
+            w = wl.make("bf16", m, n, k, op_a="T", op_b="N")
+        else:
+            w = wl.make(kind, m, n, k)
+        _check_full(w, variant=v)
+
+
+def test_k_zero_is_epilogue_only():
+    import workloads as wl
+
+    w = wl.make("fp16", 70, 40, 0, beta=1.0, bias=True, act="relu", lda=8, ldb=8)
+    _check_full(w)
+
+
+def test_d_aliases_c_in_place():
+    import oracle
+    from oracle import compare
+    import workloads as wl
+    from workloads.device import DeviceProblem
+
+    w = wl.make("fp16", 130, 70, 64, beta=0.5, bias=True)  # C and D f32, ldc == ldd
+    ref_w = w
+    dp = DeviceProblem(w)
+    dp.d.view(-1)[: dp.c.numel() // 4].copy_(dp.c.view(torch.float32))
+    st = dp.run(c=dp.d)
+    assert st == 0
+    torch.cuda.synchronize()
+    got = dp.d_all()
+    ii, jj = np.meshgrid(np.arange(w.m), np.arange(w.n), indexing="ij")
+    res = compare.parity_check(ref_w, got.ravel(), ii.ravel(), jj.ravel())
+    assert res["ok"], res
+
+
+def test_output_padding_untouched():
+    import workloads as wl
+    from workloads.device import DeviceProblem
+
+    w = wl.make("fp16", 100, 50, 64)
+    dp = DeviceProblem(w, ldd=112)
+    assert dp.run() == 0
+    torch.cuda.synchronize()
+    pad = dp.d[:, 100:].cpu()
+    assert torch.isnan(pad).all()
+
+
+# ------------------------------------------------------------ large configurations
+
+def test_config_int8_4096_sampled_exact():
+    import workloads as wl
+
+    _check_sampled(wl.make("int8", 4096, 4096, 4096))
+
+
+def test_config_fp8_8192_sampled():
+    import workloads as wl
+
+    _check_sampled(wl.make("fp8", 8192, 8192, 8192))
+
+
+def test_config_fp8_ragged_tail():
+    import workloads as wl
+
+    _check_sampled(wl.make("fp8", 4097, 1000, 2040), extra_edges=True)
+
+
+def test_config_fp8_single_row():
+    import workloads as wl
+
+    _check_sampled(wl.make("fp8", 1, 8192, 8192), extra_edges=True)
+
+
+def test_config_mxfp4_8192_sampled():
+    import workloads as wl
+
+    _check_sampled(wl.make("mxfp4", 8192, 8192, 8192))

@@ -1,0 +1,134 @@
+"""The kernels' closed-form index functions, evaluated on the host through
+the C ABI (the same __host__ __device__ code the kernels run), against the
+layouts the Shape:Stride module computes for the same maps.  This is the
+"hand arithmetic against the layout algebra" gate of "cute_layouts.cu"
+applied to every map the GEMM kernels rely on.
+"""
+import pytest
+
+import tile_hierarchy_linear_amd as thl
+
+
+def _eval(layout, n):
+    return thl.thl_layout_eval(layout, range(n))
+
+
+def test_map_names_are_all_known():
+    names = thl.thl_kernel_index_map_names()
+    for n in names:
+        pts = [(0, 0)]
+        params = {"xcd_remap": (8,), "grouped_tile": (4, 4, 2), "copy_source": (16,),
+                  "mfma32_operand": (8,)}.get(n, ())
+        thl.thl_kernel_index_map(n, pts, params)
+    with pytest.raises(thl.ThlError):
+        thl.thl_kernel_index_map("no_such_map", [(0, 0)])
+
+
+@pytest.mark.parametrize("vals", [8, 16, 32])
+def test_mfma_operand_map_is_the_tv_layout(vals):
+    # lane l, value v -> (row l%32, k (l/32)*vals + v), as the TV layout
+    # ((32,2),vals):((1,32*vals),32) onto the column-major index row + 32*k.
+    tv = f"((32,2),{vals}):((1,{32 * vals}),32)"
+    pts = [(l, v) for v in range(vals) for l in range(64)]
+    got = thl.thl_kernel_index_map("mfma32_operand", pts, (vals,))
+    want = _eval(tv, 64 * vals)
+    assert [r + 32 * k for r, k in got] == want
+    assert sorted(want) == list(range(64 * vals))  # every operand element once
+
+
+def test_mfma_accumulator_map_is_the_tv_layout():
+    tv = "((32,2),(4,4)):((32,4),(1,8))"
+    pts = [(l, v) for v in range(16) for l in range(64)]
+    got = thl.thl_kernel_index_map("mfma32_acc", pts)
+    want = _eval(tv, 1024)
+    assert [r + 32 * c for r, c in got] == want
+    assert sorted(want) == list(range(1024))
+    # runs of four consecutive rows per lane (vector stores along M)
+    for l in range(64):
+        rows = [got[v * 64 + l][0] for v in range(16)]
+        for q in range(4):
+            assert rows[4 * q:4 * q + 4] == list(range(rows[4 * q], rows[4 * q] + 4))
+
+
+def test_fp8_k_order_covers_each_k_once_per_row():
+    for row in range(32):
+        ks = sorted(k for lane in (row, row + 32) for (k, _) in
+                    thl.thl_kernel_index_map("fp8_32x32_k", [(lane, j) for j in range(32)]))
+        assert ks == list(range(64))
+
+
+def test_tr16_source_is_a_transpose_layout():
+    # out[i][v] = element i%4 of the chunk of lane 4v + i/4: flat source index
+    # 4*src + elem = i + 16 v, i.e. the layout (16,4):(1,16) over (i, v).
+    pts = [(i, v) for v in range(4) for i in range(16)]
+    got = thl.thl_kernel_index_map("tr16_source", pts)
+    assert [4 * s + e for s, e in got] == _eval("(16,4):(1,16)", 64)
+
+
+def test_lds_swizzle_is_the_xor_composition():
+    # lds_offset(row, b) = Swz<1,4,6>(Swz<3,4,3>(row*128 + b)) over 256 rows.
+    rows = 256
+    pts = [(r, b) for r in range(rows) for b in range(128)]
+    got = [o for o, _ in thl.thl_kernel_index_map("lds_offset", pts)]
+    linear = f"{rows * 128}:1"
+    first = thl.thl_swizzle_eval(3, 4, 3, linear, range(rows * 128))
+    both = thl.thl_swizzle_eval(1, 4, 6, linear, first)
+    assert got == both
+    assert sorted(got) == list(range(rows * 128))
+
+
+def test_swizzle_spreads_a_chunk_over_banks():
+    # For one logical chunk read from 32 consecutive rows: 8 consecutive rows
+    # hit 8 distinct 16-byte slots, 16 consecutive rows 16 distinct
+    # (row parity, slot) pairs.
+    for chunk in range(8):
+        for r0 in range(0, 256, 8):
+            slots = [thl.thl_kernel_index_map("lds_offset", [(r, chunk * 16)])[0][0] % 128 // 16
+                     for r in range(r0, r0 + 8)]
+            assert len(set(slots)) == 8
+        for r0 in range(0, 256, 16):
+            pairs = {(r % 2, thl.thl_kernel_index_map("lds_offset", [(r, chunk * 16)])[0][0] % 128 // 16)
+                     for r in range(r0, r0 + 16)}
+            assert len(pairs) == 16
+
+
+@pytest.mark.parametrize("loadw", [16, 4])
+def test_copy_source_inverts_the_lds_layout(loadw):
+    # Lane `lane` of the copy instruction at LDS byte `base` writes LDS bytes
+    # base + lane*loadw; the (row, byte) it fetches must be stored exactly there.
+    rows = 256
+    total = rows * 128
+    pts = [(base, lane) for base in range(0, total, 64 * loadw) for lane in range(64)]
+    src = thl.thl_kernel_index_map("copy_source", pts, (loadw,))
+    back = thl.thl_kernel_index_map("lds_offset", src)
+    assert [o for o, _ in back] == [base + lane * loadw for base, lane in pts]
+    # one wave instruction covers 64*loadw/128 whole rows: a coalesced burst per row
+    for base in range(0, total, 64 * loadw):
+        rs = {thl.thl_kernel_index_map("copy_source", [(base, lane)], (loadw,))[0][0] for lane in range(64)}
+        assert len(rs) == max(1, 64 * loadw // 128)
+
+
+@pytest.mark.parametrize("count", [8, 64, 1024, 1000])
+def test_xcd_remap_is_the_layout(count):
+    got = [r for r, _ in thl.thl_kernel_index_map("xcd_remap", [(w, 0) for w in range(count)], (count,))]
+    if count % 8 == 0:
+        assert got == _eval(f"(8,{count // 8}):({count // 8},1)", count)
+    else:
+        assert got == list(range(count))
+    assert sorted(got) == list(range(count))
+
+
+@pytest.mark.parametrize("tm,tn,group", [(32, 32, 8), (16, 8, 4), (8, 8, 8), (17, 4, 8), (5, 3, 2)])
+def test_grouped_raster_is_the_layout(tm, tn, group):
+    count = tm * tn
+    got = thl.thl_kernel_index_map("grouped_tile", [(i, 0) for i in range(count)], (tm, tn, group))
+    flat = [a + tm * b for a, b in got]
+    assert sorted(flat) == list(range(count))  # every tile exactly once
+    if tm % group == 0:
+        assert flat == _eval(f"({group},{tn},{tm // group}):(1,{tm},{group})", count)
+    else:
+        full = (tm // group) * group * tn  # whole bands follow the layout
+        if full:
+            assert flat[:full] == _eval(f"({group},{tn},{tm // group}):(1,{tm},{group})", full)
+        rest = tm - (tm // group) * group  # the last band is narrower
+        assert flat[full:] == [(tm - rest) + a + tm * b for b in range(tn) for a in range(rest)]

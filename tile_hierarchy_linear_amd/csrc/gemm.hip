@@ -1,0 +1,327 @@
+// gemm.hip -- the thl_gemm C ABI: validation, first-fit variant selection,
+// launch, and host evaluation of the kernels' index maps.
+//
+// Selection follows the page's rule for the library's host API: the first
+// built kernel whose data types, layouts and alignment fit the problem
+// ("Technical Documentation: NVIDIA/cutlass", "CUTLASS Library"), with one
+// shape rule on top: problems whose 256x256 tile count cannot fill the 256
+// compute units take the 128x128 variant.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <type_traits>
+
+#include "../../include/thl.h"
+#include "gemm_kernels.hpp"
+#include "index_maps.hpp"
+
+namespace thl {
+namespace {
+
+using LaunchFn = hipError_t (*)(const GemmArgs&, dim3, hipStream_t);
+
+struct Variant {
+  const char* name;
+  int family;
+  int bm, bn, threads, loadw;
+  bool small;  // preferred when the large tile cannot fill the device
+  LaunchFn launch;
+};
+
+// hipLaunchKernel reports this launch's own status (a stale error left by
+// an unrelated earlier HIP call in the process is not picked up).
+template <int F, int BM, int BN, int WM, int WN, int LOADW>
+hipError_t launch_kmajor(const GemmArgs& a, dim3 grid, hipStream_t s) {
+  GemmArgs arg = a;
+  void* args[] = {&arg};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_kmajor_kernel<F, BM, BN, WM, WN, LOADW>), grid,
+                         dim3(WM * WN * 64), args, 0, s);
+}
+
+#define THL_KMAJOR_VARIANTS(FAM, NAME)                                                                      \
+  {NAME "_tn_256x256_w2x2_v16", FAM, 256, 256, 256, 16, false, &launch_kmajor<FAM, 256, 256, 2, 2, 16>},   \
+      {NAME "_tn_128x128_w2x2_v16", FAM, 128, 128, 256, 16, true, &launch_kmajor<FAM, 128, 128, 2, 2, 16>}, \
+      {NAME "_tn_128x128_w2x2_v4", FAM, 128, 128, 256, 4, true, &launch_kmajor<FAM, 128, 128, 2, 2, 4>}
+
+const Variant kVariants[] = {
+    THL_KMAJOR_VARIANTS(FAM_BF16, "bf16"), THL_KMAJOR_VARIANTS(FAM_F16, "f16"),
+    THL_KMAJOR_VARIANTS(FAM_I8, "i8"),     THL_KMAJOR_VARIANTS(FAM_FP8, "e4m3"),
+    THL_KMAJOR_VARIANTS(FAM_FP4, "e2m1"),
+};
+constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
+
+thread_local const char* t_last_variant = "";
+
+int family_of(thl_dtype t) {
+  switch (t) {
+    case THL_F16:
+      return FAM_F16;
+    case THL_BF16:
+      return FAM_BF16;
+    case THL_I8:
+      return FAM_I8;
+    case THL_E4M3:
+      return FAM_FP8;
+    case THL_E2M1X2:
+      return FAM_FP4;
+    default:
+      return -1;
+  }
+}
+
+// Bytes of `count` elements of a format (fp4: two per byte, rounded up).
+int64_t bytes_of(thl_dtype t, int64_t count) {
+  switch (t) {
+    case THL_F32:
+    case THL_I32:
+      return 4 * count;
+    case THL_F16:
+    case THL_BF16:
+      return 2 * count;
+    case THL_I8:
+    case THL_E4M3:
+    case THL_E8M0:
+      return count;
+    case THL_E2M1X2:
+      return (count + 1) / 2;
+    default:
+      return 0;
+  }
+}
+
+bool is_float_io(thl_dtype t) { return t == THL_F32 || t == THL_F16 || t == THL_BF16; }
+
+struct Range {
+  uintptr_t lo = 0, hi = 0;  // [lo, hi), empty when lo == hi
+};
+
+// Byte range spanned by a column-major r x c matrix with leading dimension ld.
+Range matrix_range(const void* p, thl_dtype t, int64_t r, int64_t c, int64_t ld) {
+  Range g;
+  if (!p || r <= 0 || c <= 0) return g;
+  g.lo = reinterpret_cast<uintptr_t>(p);
+  g.hi = g.lo + static_cast<uintptr_t>(bytes_of(t, (c - 1) * ld + r));
+  if (t == THL_E2M1X2) g.hi = g.lo + static_cast<uintptr_t>(((c - 1) * ld + r + 1) / 2);
+  return g;
+}
+
+bool overlaps(const Range& a, const Range& b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned(const void* p, int64_t pitch_bytes, int w) {
+  return (reinterpret_cast<uintptr_t>(p) % w) == 0 && (pitch_bytes % w) == 0;
+}
+
+}  // namespace
+}  // namespace thl
+
+using namespace thl;
+
+extern "C" {
+
+const char* thl_status_string(int s) {
+  switch (s) {
+    case THL_OK:
+      return "THL_OK";
+    case THL_ERR_INVALID:
+      return "THL_ERR_INVALID: bad dimension, leading dimension, pointer, overlap or argument";
+    case THL_ERR_UNSUPPORTED:
+      return "THL_ERR_UNSUPPORTED: combination not built";
+    case THL_ERR_MISALIGNED:
+      return "THL_ERR_MISALIGNED: pointer or leading dimension breaks every kernel's alignment";
+    case THL_ERR_HIP:
+      return "THL_ERR_HIP: the HIP runtime reported a launch error";
+    case THL_ERR_UNDEFINED:
+      return "THL_ERR_UNDEFINED: layout operation undefined (divisibility or overlap)";
+    default:
+      return "unknown status";
+  }
+}
+
+const char* thl_last_variant(void) { return t_last_variant; }
+
+int thl_variant_count(void) { return kNumVariants; }
+
+const char* thl_variant_name(int i) { return (i >= 0 && i < kNumVariants) ? kVariants[i].name : nullptr; }
+
+thl_status thl_gemm(int64_t m, int64_t n, int64_t k, const void* A, int64_t lda, thl_op opA, const void* B,
+                    int64_t ldb, thl_op opB, const void* C, int64_t ldc, void* D, int64_t ldd, float alpha,
+                    float beta, const thl_dtypes* dt, const thl_epilogue* epi, const thl_scales* sc,
+                    struct ihipStream_t* stream) {
+  // ---- arguments
+  if (!dt || m < 0 || n < 0 || k < 0) return THL_ERR_INVALID;
+  if ((opA != THL_OP_N && opA != THL_OP_T) || (opB != THL_OP_N && opB != THL_OP_T)) return THL_ERR_INVALID;
+  if (m > INT32_MAX || n > INT32_MAX || k > INT32_MAX) return THL_ERR_UNSUPPORTED;
+  const unsigned flags = epi ? epi->flags : 0u;
+  if (flags & ~static_cast<unsigned>(THL_EPI_BIAS | THL_EPI_RELU | THL_EPI_GELU)) return THL_ERR_INVALID;
+  if ((flags & THL_EPI_RELU) && (flags & THL_EPI_GELU)) return THL_ERR_INVALID;
+  const bool has_bias = (flags & THL_EPI_BIAS) != 0;
+
+  // ---- supported combinations
+  const int fam = family_of(dt->a);
+  if (fam < 0 || dt->b != dt->a) return THL_ERR_UNSUPPORTED;
+  const bool int_path = fam == FAM_I8;
+  if (int_path) {
+    if (dt->acc != THL_I32 || dt->d != THL_I32) return THL_ERR_UNSUPPORTED;
+    if (beta != 0.0f && dt->c != THL_I32) return THL_ERR_UNSUPPORTED;
+    if (has_bias && dt->bias != THL_I32) return THL_ERR_UNSUPPORTED;
+    if (alpha != 1.0f || (beta != 0.0f && beta != 1.0f)) return THL_ERR_UNSUPPORTED;
+    if (flags & THL_EPI_GELU) return THL_ERR_UNSUPPORTED;
+  } else {
+    if (dt->acc != THL_F32 || !is_float_io(dt->d)) return THL_ERR_UNSUPPORTED;
+    if (beta != 0.0f && !is_float_io(dt->c)) return THL_ERR_UNSUPPORTED;
+    if (has_bias && !is_float_io(dt->bias)) return THL_ERR_UNSUPPORTED;
+  }
+  // K-major operands only: op(A) rows and op(B) columns contiguous along K.
+  if (opA != THL_OP_T || opB != THL_OP_N) return THL_ERR_UNSUPPORTED;
+  if (fam == FAM_FP4 && (k % 32 != 0)) return THL_ERR_UNSUPPORTED;
+
+  // ---- leading dimensions and pointers
+  const int64_t rows_a = (opA == THL_OP_N) ? m : k, cols_a = (opA == THL_OP_N) ? k : m;
+  const int64_t rows_b = (opB == THL_OP_N) ? k : n, cols_b = (opB == THL_OP_N) ? n : k;
+  if (lda < (rows_a > 1 ? rows_a : 1) || ldb < (rows_b > 1 ? rows_b : 1)) return THL_ERR_INVALID;
+  if (ldd < (m > 1 ? m : 1)) return THL_ERR_INVALID;
+  if (beta != 0.0f && ldc < (m > 1 ? m : 1)) return THL_ERR_INVALID;
+  if (fam == FAM_FP4 && ((lda % 2) != 0 || (ldb % 2) != 0)) return THL_ERR_INVALID;
+  const bool work = m > 0 && n > 0;
+  if (work && !D) return THL_ERR_INVALID;
+  if (work && k > 0 && (!A || !B)) return THL_ERR_INVALID;
+  if (work && beta != 0.0f && !C) return THL_ERR_INVALID;
+  if (work && has_bias && !epi->bias) return THL_ERR_INVALID;
+  const thl_scales unit_scales = {1.0f, 1.0f, nullptr, 0, nullptr, 0};
+  const thl_scales& s = sc ? *sc : unit_scales;
+  if (fam == FAM_FP4 && work && k > 0) {
+    if (!s.sfa || !s.sfb) return THL_ERR_INVALID;
+    if (s.ld_sfa < k / 32 || s.ld_sfb < k / 32) return THL_ERR_INVALID;
+  }
+
+  // ---- overlap: D may alias C exactly; nothing else may overlap D
+  if (work) {
+    const Range rd = matrix_range(D, dt->d, m, n, ldd);
+    if (overlaps(rd, matrix_range(A, dt->a, rows_a, cols_a, lda))) return THL_ERR_INVALID;
+    if (overlaps(rd, matrix_range(B, dt->b, rows_b, cols_b, ldb))) return THL_ERR_INVALID;
+    if (beta != 0.0f) {
+      const bool exact_alias = (C == D) && (ldc == ldd) && (dt->c == dt->d);
+      if (!exact_alias && overlaps(rd, matrix_range(C, dt->c, m, n, ldc))) return THL_ERR_INVALID;
+    }
+    if (has_bias && overlaps(rd, matrix_range(epi->bias, dt->bias, m, 1, m))) return THL_ERR_INVALID;
+    if (fam == FAM_FP4 && k > 0) {
+      if (overlaps(rd, matrix_range(s.sfa, THL_E8M0, k / 32, m, s.ld_sfa))) return THL_ERR_INVALID;
+      if (overlaps(rd, matrix_range(s.sfb, THL_E8M0, k / 32, n, s.ld_sfb))) return THL_ERR_INVALID;
+    }
+  }
+
+  // ---- variant: first fit on family, alignment and shape
+  const int64_t lda_bytes = bytes_of(dt->a, lda), ldb_bytes = bytes_of(dt->b, ldb);
+  const char* forced = std::getenv("THL_FORCE_VARIANT");
+  const int64_t big_tiles = ((m + 255) / 256) * ((n + 255) / 256);
+  const bool want_small = big_tiles < 256;
+  const Variant* pick = nullptr;
+  bool family_built = false;
+  for (int pass = 0; pass < 2 && !pick; ++pass) {
+    for (const Variant& v : kVariants) {
+      if (v.family != fam) continue;
+      family_built = true;
+      if (forced && *forced) {
+        if (std::strcmp(forced, v.name) != 0) continue;
+      } else if (pass == 0 && v.small != want_small) {
+        continue;  // first pass: the variant the shape rule prefers
+      }
+      const bool fits = k == 0 || (aligned(A, lda_bytes, v.loadw) && aligned(B, ldb_bytes, v.loadw));
+      if (fits) {
+        pick = &v;
+        break;
+      }
+    }
+    if (forced && *forced) break;
+  }
+  if (!pick) {
+    if (forced && *forced) return THL_ERR_UNSUPPORTED;
+    return family_built ? THL_ERR_MISALIGNED : THL_ERR_UNSUPPORTED;
+  }
+  if (!work) {
+    t_last_variant = pick->name;
+    return THL_OK;
+  }
+
+  // ---- launch
+  GemmArgs a{};
+  a.a = static_cast<const uint8_t*>(A);
+  a.b = static_cast<const uint8_t*>(B);
+  a.c = C;
+  a.d = D;
+  a.bias = has_bias ? epi->bias : nullptr;
+  a.sfa = s.sfa;
+  a.sfb = s.sfb;
+  a.lda_bytes = lda_bytes;
+  a.ldb_bytes = ldb_bytes;
+  a.ldc = ldc;
+  a.ldd = ldd;
+  a.ld_sfa = s.ld_sfa;
+  a.ld_sfb = s.ld_sfb;
+  a.m = static_cast<int32_t>(m);
+  a.n = static_cast<int32_t>(n);
+  a.k = static_cast<int32_t>(k);
+  a.kbytes = static_cast<int32_t>(bytes_of(dt->a, k));
+  a.tiles_m = static_cast<int32_t>((m + pick->bm - 1) / pick->bm);
+  a.tiles_n = static_cast<int32_t>((n + pick->bn - 1) / pick->bn);
+  a.group_m = 8;
+  a.alpha = (fam == FAM_FP8) ? alpha * s.a_scale * s.b_scale : alpha;
+  a.beta = beta;
+  a.flags = static_cast<int32_t>(flags);
+  a.c_type = static_cast<int32_t>(dt->c);
+  a.d_type = static_cast<int32_t>(dt->d);
+  a.bias_type = static_cast<int32_t>(dt->bias);
+  const int64_t tiles = static_cast<int64_t>(a.tiles_m) * a.tiles_n;
+  if (tiles > INT32_MAX) return THL_ERR_UNSUPPORTED;
+  if (pick->launch(a, dim3(static_cast<unsigned>(tiles)), reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return THL_ERR_HIP;
+  t_last_variant = pick->name;
+  return THL_OK;
+}
+
+// ---------------------------------------------------------------- index maps
+
+const char* thl_kernel_index_map_names(void) {
+  return "xcd_remap,grouped_tile,swz,lds_offset,copy_source,mfma32_operand,mfma32_acc,fp8_32x32_k,tr16_source";
+}
+
+int thl_kernel_index_map(const char* map, const int64_t* params, int64_t n, const int64_t* in, int64_t* out) {
+  if (!map || n < 0 || (n > 0 && (!in || !out))) return THL_ERR_INVALID;
+  auto param = [&](int i) { return params ? params[i] : 0; };
+  for (int64_t t = 0; t < n; ++t) {
+    const int64_t x = in[2 * t], y = in[2 * t + 1];
+    int64_t r0 = 0, r1 = 0;
+    if (!std::strcmp(map, "xcd_remap")) {
+      if (!params || param(0) <= 0) return THL_ERR_INVALID;
+      r0 = maps::xcd_remap(x, param(0));
+    } else if (!std::strcmp(map, "grouped_tile")) {
+      if (!params || param(0) <= 0 || param(1) <= 0 || param(2) <= 0) return THL_ERR_INVALID;
+      maps::grouped_tile(x, param(0), param(1), param(2), &r0, &r1);
+    } else if (!std::strcmp(map, "swz")) {
+      r0 = maps::swz(x);
+    } else if (!std::strcmp(map, "lds_offset")) {
+      r0 = maps::lds_offset(x, y);
+    } else if (!std::strcmp(map, "copy_source")) {
+      if (!params || (param(0) != 4 && param(0) != 16)) return THL_ERR_INVALID;
+      maps::copy_source(x, y, param(0), &r0, &r1);
+    } else if (!std::strcmp(map, "mfma32_operand")) {
+      if (!params || param(0) <= 0) return THL_ERR_INVALID;
+      maps::mfma32_operand(x, y, param(0), &r0, &r1);
+    } else if (!std::strcmp(map, "mfma32_acc")) {
+      maps::mfma32_acc(x, y, &r0, &r1);
+    } else if (!std::strcmp(map, "fp8_32x32_k")) {
+      r0 = maps::fp8_32x32_k_of(x, y);
+    } else if (!std::strcmp(map, "tr16_source")) {
+      maps::tr16_source(x, y, &r0, &r1);
+    } else {
+      return THL_ERR_INVALID;
+    }
+    out[2 * t] = r0;
+    out[2 * t + 1] = r1;
+  }
+  return THL_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,116 @@
+// index_maps.hpp -- the closed-form index functions the GEMM kernels use.
+//
+// Each is `__host__ __device__` so the library can evaluate it on the host
+// (thl_kernel_index_map) and the tests can compare it, point by point, with
+// the layout the Shape:Stride module computes for the same map -- the "host
+// arithmetic against the layout algebra" check of the page "cute_layouts.cu"
+// (gate 2), extended to every map the kernels rely on.
+//
+// Tile hierarchy ("CUTLASS" knowledge-base page, "The tile hierarchy"):
+//   workgroup tile BM x BN  ->  wavefront tile (BM/WM) x (BN/WN)  ->  32x32 MFMA tiles.
+// Operands are staged in LDS as rows of 128 bytes of K (one K-step), each row
+// split into eight 16-byte chunks whose order is XOR-swizzled per row.
+#pragma once
+
+#include <stdint.h>
+
+#ifndef THL_HD
+#define THL_HD __host__ __device__ __forceinline__
+#endif
+
+namespace thl {
+namespace maps {
+
+// ------------------------------------------------------------ a2: tiles
+// Workgroups are handed to the 8 XCDs round-robin (workgroup w runs on XCD
+// w % 8).  The remap makes each XCD own a contiguous range of logical tile
+// ids, so tiles that share A/B panels share that XCD's L2:
+//   logical = (w % 8) * (count / 8) + w / 8     when count % 8 == 0,
+// and the identity otherwise.  As a layout: (8, count/8):(count/8, 1).
+THL_HD int64_t xcd_remap(int64_t w, int64_t count) {
+  if (count % 8 != 0) return w;
+  return (w % 8) * (count / 8) + w / 8;
+}
+
+// Grouped raster: logical tile ids walk down a band of `group` tile rows
+// (tile row fastest) before moving to the next tile column; bands follow one
+// another.  With tm fastest this is the layout (group, tiles_n, tiles_m/group)
+// : (1, tiles_m, group) onto the column-major tile index tm + tiles_m*tn, for
+// tiles_m % group == 0; the last band is narrower otherwise.
+THL_HD void grouped_tile(int64_t id, int64_t tiles_m, int64_t tiles_n, int64_t group, int64_t* tm,
+                         int64_t* tn) {
+  const int64_t band = group * tiles_n;
+  const int64_t first = (id / band) * group;
+  const int64_t rows = (tiles_m - first) < group ? (tiles_m - first) : group;
+  const int64_t in_band = id % band;
+  *tm = first + in_band % rows;
+  *tn = in_band / rows;
+}
+
+// ------------------------------------------------------------ a3: LDS staging
+// Chunk order within a staged row: chunk c of row r is stored in slot
+// c ^ swz(r).  swz(r) = (r % 8) ^ ((r / 8) % 2): any 8 consecutive rows use 8
+// distinct slots for the same chunk, and any 16 consecutive rows use 16
+// distinct (row parity, slot) pairs, so a wavefront reading one chunk from
+// 32 consecutive rows spreads over all banks of a 128- or 256-byte bank
+// window.  On a 16-byte granule it is the XOR swizzle with b = 3, m = 4,
+// s = 3 composed on the row-major (rows, 128) byte layout, plus the parity
+// term.
+THL_HD int swz(int64_t row) { return static_cast<int>((row & 7) ^ ((row >> 3) & 1)); }
+
+// Byte offset, inside one staged operand buffer, of byte `b` (0..127) of row `row`.
+THL_HD int64_t lds_offset(int64_t row, int64_t b) {
+  return row * 128 + ((((b >> 4) ^ swz(row)) & 7) << 4) + (b & 15);
+}
+
+// Direct global->LDS loads write `loadw` bytes per lane at consecutive LDS
+// addresses: lane `lane` of the instruction that starts at LDS byte `base`
+// fills LDS bytes base + lane*loadw ... .  The lane therefore fetches the row
+// and in-row byte that the inverse of lds_offset assigns to that LDS byte.
+THL_HD void copy_source(int64_t base, int64_t lane, int64_t loadw, int64_t* row, int64_t* byte_in_row) {
+  const int64_t off = base + lane * loadw;
+  const int64_t r = off >> 7;
+  const int64_t slot = (off >> 4) & 7;
+  *row = r;
+  *byte_in_row = (((slot ^ swz(r)) & 7) << 4) | (off & 15);
+}
+
+// ------------------------------------------------------------ a4/a5: MFMA maps
+// 32x32 MFMA operand fragment: lane l holds row l % 32 of the 32-row operand
+// tile and `vals` consecutive K elements starting at (l / 32) * vals, where
+// vals = 8 for 16-bit types (32x32x16), 16 for int8 (32x32x32) and 32 for fp4
+// (32x32x64): the TV layout ((32,2),vals):((1, 32*vals), 32) onto the
+// column-major (row + 32*k) tile index.
+THL_HD void mfma32_operand(int64_t lane, int64_t v, int64_t vals, int64_t* row, int64_t* k) {
+  *row = lane & 31;
+  *k = (lane >> 5) * vals + v;
+}
+
+// 32x32 MFMA accumulator: register v of lane l is element
+//   (row, col) = (8*(v/4) + 4*(l/32) + v%4, l % 32)
+// i.e. the TV layout ((32,2),(4,4)):((32,4),(1,8)) onto the column-major
+// (row + 32*col) tile index.  Each lane holds runs of 4 consecutive rows.
+THL_HD void mfma32_acc(int64_t lane, int64_t v, int64_t* row, int64_t* col) {
+  *row = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+  *col = lane & 31;
+}
+
+// fp8 32x32x64 (f8f6f4 with 8-bit data): each lane supplies 32 bytes; the
+// instruction reads them as K = 16*(l/32) + j for j < 16 and 32 + 16*(l/32) +
+// (j - 16) for j >= 16.  The kernels load both operands with the same per-lane
+// byte order, so any such fixed permutation of K cancels in the dot product.
+THL_HD int64_t fp8_32x32_k_of(int64_t lane, int64_t j) {
+  return j < 16 ? 16 * (lane >> 5) + j : 32 + 16 * (lane >> 5) + (j - 16);
+}
+
+// Transposed 16-bit LDS read (ds_read_b64_tr_b16): inside each group of 16
+// lanes, lane i receives element i % 4 of the 8-byte chunk that lane
+// 4*v + i/4 of its group addressed, as its value v (v = 0..3).  Returned:
+// (source lane within the group, element within that lane's chunk).
+THL_HD void tr16_source(int64_t lane_in_group, int64_t v, int64_t* src_lane, int64_t* elem) {
+  *src_lane = 4 * v + (lane_in_group >> 2);
+  *elem = lane_in_group & 3;
+}
+
+}  // namespace maps
+}  // namespace thl

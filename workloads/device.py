@@ -1,0 +1,76 @@
+"""Run a Workload on the GPU through the C ABI: upload the stored bits,
+call thl_gemm on the current stream, read D back.  Device memory and streams
+come from torch; every arithmetic step runs in libthl's kernels."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import tile_hierarchy_linear_amd as thl
+
+_TORCH_D = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "i32": torch.int32}
+
+
+def upload(arr, device="cuda"):
+    if arr is None:
+        return None
+    raw = np.ascontiguousarray(arr).view(np.uint8).reshape(-1)
+    return torch.from_numpy(raw.copy()).to(device)
+
+
+class DeviceProblem:
+    """Device copies of a workload's buffers plus its output."""
+
+    def __init__(self, w, device="cuda", d_fill=float("nan"), ldd=None):
+        self.w = w
+        self.a = upload(w.a, device)
+        self.b = upload(w.b, device)
+        self.c = upload(w.c, device) if w.c is not None and w.beta != 0.0 else None
+        self.bias = upload(w.bias, device)
+        self.sfa = upload(w.sfa, device)
+        self.sfb = upload(w.sfb, device)
+        self.ldd = ldd or w.ldd
+        self.d = torch.empty((max(1, w.n), self.ldd), dtype=_TORCH_D[w.type_d], device=device)
+        if w.type_d == "i32":
+            self.d.fill_(-(2 ** 31) + 7)
+        else:
+            self.d.fill_(d_fill)
+
+    def run(self, stream=None, d=None, c=None, ldc=None):
+        w = self.w
+        dt = thl.make_dtypes(w.type_a, w.type_b, w.type_c, w.type_d,
+                             w.type_bias if w.bias is not None else "none")
+        flags = (thl.THL_EPI_BIAS if w.bias is not None else 0) | \
+            {"none": 0, "relu": thl.THL_EPI_RELU, "gelu": thl.THL_EPI_GELU}[w.act]
+        epi = thl.thl_epilogue(flags, self.bias.data_ptr() if self.bias is not None else None)
+        sc = thl.thl_scales(float(w.a_scale), float(w.b_scale),
+                            self.sfa.data_ptr() if self.sfa is not None else None, int(w.ld_sfa),
+                            self.sfb.data_ptr() if self.sfb is not None else None, int(w.ld_sfb))
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        dd = self.d if d is None else d
+        cc = self.c if c is None else c
+        status = thl.thl_gemm(w.m, w.n, w.k, self.a.data_ptr() if self.a is not None and self.a.numel() else None,
+                              w.lda, w.op_a,
+                              self.b.data_ptr() if self.b is not None and self.b.numel() else None, w.ldb,
+                              w.op_b, cc.data_ptr() if cc is not None else None,
+                              ldc or w.ldc or max(1, w.m), dd.data_ptr(), self.ldd, w.alpha, w.beta, dt, epi,
+                              sc, stream)
+        return status
+
+    def d_values(self, rows, cols) -> np.ndarray:
+        """D at (rows[t], cols[t]) as float64 (int64 for int32 outputs)."""
+        host = self.d.cpu()
+        r = torch.as_tensor(np.asarray(rows, dtype=np.int64))
+        c = torch.as_tensor(np.asarray(cols, dtype=np.int64))
+        vals = host[c, r]
+        if self.w.type_d == "i32":
+            return vals.to(torch.int64).numpy()
+        return vals.to(torch.float64).numpy()
+
+    def d_all(self) -> np.ndarray:
+        """All of D as an (m, n) array [i, j]."""
+        host = self.d.cpu()[: self.w.n, : self.w.m].T
+        if self.w.type_d == "i32":
+            return host.to(torch.int64).numpy()
+        return host.to(torch.float64).numpy()
