@@ -83,11 +83,12 @@ def cpu_baseline(w, budget_s):
     import oracle
 
     nthreads = oracle.max_threads()
-    rows, cols = w.sample(64)
+    pilot = 16 * nthreads
+    rows, cols = w.sample(pilot)
     t0 = time.perf_counter()
     oracle.gemm_elements(w.oracle_problem(), rows, cols, nthreads)
     t1 = time.perf_counter() - t0
-    count = int(min(max(64, 64 * budget_s / max(t1, 1e-6)), w.m * w.n))
+    count = int(min(max(pilot, pilot * budget_s / max(t1, 1e-6)), w.m * w.n))
     rows, cols = w.sample(count)
     t0 = time.perf_counter()
     oracle.gemm_elements(w.oracle_problem(), rows, cols, nthreads)
@@ -122,6 +123,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0)
+    ap.add_argument("--sweep-variants", action="store_true",
+                    help="also time every built variant of each dtype (stderr)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -173,6 +176,19 @@ def main():
             headline = (w, ms, byt, variant)
         if headline is None and key == sorted(only)[0]:
             headline = (w, ms, byt, variant)
+        if args.sweep_variants:
+            fam = {"bf16": "bf16", "e4m3": "e4m3", "e2m1": "e2m1"}[key]
+            for v in thl.variants():
+                if not v.startswith(fam + "_"):
+                    continue
+                os.environ["THL_FORCE_VARIANT"] = v
+                try:
+                    vms = time_gemm(dp, max(3, args.steps // 2), 2, stream)
+                    log(f"   sweep {v}: {vms:.3f} ms {flops / (vms * 1e-3) / 1e12:.1f} TFLOP/s")
+                except AssertionError as e:
+                    log(f"   sweep {v}: not applicable ({e})")
+                finally:
+                    os.environ.pop("THL_FORCE_VARIANT", None)
         del dp
         torch.cuda.empty_cache()
 

@@ -112,8 +112,15 @@ def test_mxfp4_needs_scales():
     assert call(types=("e2m1", "f32", "bf16", "none"), sc=None) == thl.THL_ERR_INVALID
     sc = thl.thl_scales(1.0, 1.0, SFA, 1, SFB, 2)  # ld_sfa < k/32
     assert call(types=("e2m1", "f32", "bf16", "none"), sc=sc) == thl.THL_ERR_INVALID
-    sc = thl.thl_scales(1.0, 1.0, SFA, 2, SFB, 2)
+    sc = thl.thl_scales(1.0, 1.0, SFA, 4, SFB, 4)
     assert call(types=("e2m1", "f32", "bf16", "none"), lda=65, sc=sc) == thl.THL_ERR_INVALID  # odd ld
+
+
+def test_mxfp4_scale_rows_must_be_4_byte_aligned():
+    sc = thl.thl_scales(1.0, 1.0, SFA, 2, SFB, 4)  # ld_sfa = 2: not a multiple of 4
+    assert call(types=("e2m1", "f32", "bf16", "none"), sc=sc) == thl.THL_ERR_MISALIGNED
+    sc = thl.thl_scales(1.0, 1.0, SFA + 1, 4, SFB, 4)
+    assert call(types=("e2m1", "f32", "bf16", "none"), sc=sc) == thl.THL_ERR_MISALIGNED
 
 
 def test_misaligned():
@@ -140,7 +147,7 @@ def test_quick_returns_do_not_launch():
 
 
 def test_forced_variant_must_fit():
-    os.environ["THL_FORCE_VARIANT"] = "i8_tn_256x256_w2x2_v16"
+    os.environ["THL_FORCE_VARIANT"] = "i8_tn_256x256_w2x2_v16_s4"
     try:
         assert call(m=0) == thl.THL_ERR_UNSUPPORTED  # bf16 problem, int8 variant
     finally:

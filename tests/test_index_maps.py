@@ -65,31 +65,39 @@ def test_tr16_source_is_a_transpose_layout():
     assert [4 * s + e for s, e in got] == _eval("(16,4):(1,16)", 64)
 
 
+ROW = 64  # bytes of K staged per operand row (one K-step)
+
+
 def test_lds_swizzle_is_the_xor_composition():
-    # lds_offset(row, b) = Swz<1,4,6>(Swz<3,4,3>(row*128 + b)) over 256 rows.
+    # lds_offset(row, b) = Swz<2,4,5>(Swz<2,4,3>(row*64 + b)) over 256 rows.
     rows = 256
-    pts = [(r, b) for r in range(rows) for b in range(128)]
+    pts = [(r, b) for r in range(rows) for b in range(ROW)]
     got = [o for o, _ in thl.thl_kernel_index_map("lds_offset", pts)]
-    linear = f"{rows * 128}:1"
-    first = thl.thl_swizzle_eval(3, 4, 3, linear, range(rows * 128))
-    both = thl.thl_swizzle_eval(1, 4, 6, linear, first)
+    linear = f"{rows * ROW}:1"
+    first = thl.thl_swizzle_eval(2, 4, 3, linear, range(rows * ROW))
+    both = thl.thl_swizzle_eval(2, 4, 5, linear, first)
     assert got == both
-    assert sorted(got) == list(range(rows * 128))
+    assert sorted(got) == list(range(rows * ROW))
+
+
+def _banks(offsets, window):
+    """4-byte banks touched within a `window`-byte bank window."""
+    return [(o % window) // 4 for o in offsets]
 
 
 def test_swizzle_spreads_a_chunk_over_banks():
-    # For one logical chunk read from 32 consecutive rows: 8 consecutive rows
-    # hit 8 distinct 16-byte slots, 16 consecutive rows 16 distinct
-    # (row parity, slot) pairs.
-    for chunk in range(8):
+    # One logical chunk (16 bytes) read from consecutive rows: any 8 rows
+    # cover all 32 banks of a 128-byte window, any 16 rows all 64 banks of a
+    # 256-byte window -- no bank is hit twice.
+    for chunk in range(ROW // 16):
         for r0 in range(0, 256, 8):
-            slots = [thl.thl_kernel_index_map("lds_offset", [(r, chunk * 16)])[0][0] % 128 // 16
-                     for r in range(r0, r0 + 8)]
-            assert len(set(slots)) == 8
+            offs = [thl.thl_kernel_index_map("lds_offset", [(r, chunk * 16 + q)])[0][0]
+                    for r in range(r0, r0 + 8) for q in range(0, 16, 4)]
+            assert sorted(_banks(offs, 128)) == list(range(32))
         for r0 in range(0, 256, 16):
-            pairs = {(r % 2, thl.thl_kernel_index_map("lds_offset", [(r, chunk * 16)])[0][0] % 128 // 16)
-                     for r in range(r0, r0 + 16)}
-            assert len(pairs) == 16
+            offs = [thl.thl_kernel_index_map("lds_offset", [(r, chunk * 16 + q)])[0][0]
+                    for r in range(r0, r0 + 16) for q in range(0, 16, 4)]
+            assert sorted(_banks(offs, 256)) == list(range(64))
 
 
 @pytest.mark.parametrize("loadw", [16, 4])
@@ -97,15 +105,21 @@ def test_copy_source_inverts_the_lds_layout(loadw):
     # Lane `lane` of the copy instruction at LDS byte `base` writes LDS bytes
     # base + lane*loadw; the (row, byte) it fetches must be stored exactly there.
     rows = 256
-    total = rows * 128
+    total = rows * ROW
     pts = [(base, lane) for base in range(0, total, 64 * loadw) for lane in range(64)]
     src = thl.thl_kernel_index_map("copy_source", pts, (loadw,))
     back = thl.thl_kernel_index_map("lds_offset", src)
     assert [o for o, _ in back] == [base + lane * loadw for base, lane in pts]
-    # one wave instruction covers 64*loadw/128 whole rows: a coalesced burst per row
+    # one wave instruction covers whole rows, each a contiguous 64-byte run of K
     for base in range(0, total, 64 * loadw):
-        rs = {thl.thl_kernel_index_map("copy_source", [(base, lane)], (loadw,))[0][0] for lane in range(64)}
-        assert len(rs) == max(1, 64 * loadw // 128)
+        got = thl.thl_kernel_index_map("copy_source", [(base, lane) for lane in range(64)], (loadw,))
+        rows_hit = {}
+        for r, b in got:
+            rows_hit.setdefault(r, []).append(b)
+        assert len(rows_hit) == max(1, 64 * loadw // ROW)
+        for r, bs in rows_hit.items():
+            spans = sorted(x for b in bs for x in range(b, b + loadw))
+            assert spans == list(range(min(spans), min(spans) + len(spans)))
 
 
 @pytest.mark.parametrize("count", [8, 64, 1024, 1000])

@@ -14,7 +14,7 @@
 #include <type_traits>
 
 #include "../../include/thl.h"
-#include "gemm_kernels.hpp"
+#include "gemm_args.hpp"
 #include "index_maps.hpp"
 
 namespace thl {
@@ -26,29 +26,27 @@ struct Variant {
   const char* name;
   int family;
   int bm, bn, threads, loadw;
-  bool small;  // preferred when the large tile cannot fill the device
+  bool small;       // preferred when the large tile cannot fill the device
+  int scale_width;  // fp4 scale copies: 4-byte lanes, so scale rows must be 4-byte aligned
   LaunchFn launch;
 };
 
-// hipLaunchKernel reports this launch's own status (a stale error left by
-// an unrelated earlier HIP call in the process is not picked up).
-template <int F, int BM, int BN, int WM, int WN, int LOADW>
-hipError_t launch_kmajor(const GemmArgs& a, dim3 grid, hipStream_t s) {
-  GemmArgs arg = a;
-  void* args[] = {&arg};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_kmajor_kernel<F, BM, BN, WM, WN, LOADW>), grid,
-                         dim3(WM * WN * 64), args, 0, s);
-}
-
-#define THL_KMAJOR_VARIANTS(FAM, NAME)                                                                      \
-  {NAME "_tn_256x256_w2x2_v16", FAM, 256, 256, 256, 16, false, &launch_kmajor<FAM, 256, 256, 2, 2, 16>},   \
-      {NAME "_tn_128x128_w2x2_v16", FAM, 128, 128, 256, 16, true, &launch_kmajor<FAM, 128, 128, 2, 2, 16>}, \
-      {NAME "_tn_128x128_w2x2_v4", FAM, 128, 128, 256, 4, true, &launch_kmajor<FAM, 128, 128, 2, 2, 4>}
+// Must list exactly the instantiations of THL_INSTANTIATE_KMAJOR.  Order is
+// the first-fit order: large tiles first, then the small-problem tiles.
+#define THL_KMAJOR_VARIANTS(FAM, NAME, SCW, SUFFIX)                                                       \
+  {NAME "_tn_256x128_w2x2_v16_s3_o2" SUFFIX, FAM, 256, 128, 256, 16, false, SCW,                           \
+   &launch_kmajor<FAM, 256, 128, 2, 2, 16, 3, 2, SCW>},                                                    \
+      {NAME "_tn_256x256_w2x2_v16_s4" SUFFIX, FAM, 256, 256, 256, 16, false, SCW,                           \
+       &launch_kmajor<FAM, 256, 256, 2, 2, 16, 4, 1, SCW>},                                                 \
+      {NAME "_tn_128x128_w2x2_v16_s4_o2" SUFFIX, FAM, 128, 128, 256, 16, true, SCW,                         \
+       &launch_kmajor<FAM, 128, 128, 2, 2, 16, 4, 2, SCW>},                                                 \
+      {NAME "_tn_128x128_w2x2_v4_s4_o2" SUFFIX, FAM, 128, 128, 256, 4, true, SCW,                           \
+       &launch_kmajor<FAM, 128, 128, 2, 2, 4, 4, 2, SCW>}
 
 const Variant kVariants[] = {
-    THL_KMAJOR_VARIANTS(FAM_BF16, "bf16"), THL_KMAJOR_VARIANTS(FAM_F16, "f16"),
-    THL_KMAJOR_VARIANTS(FAM_I8, "i8"),     THL_KMAJOR_VARIANTS(FAM_FP8, "e4m3"),
-    THL_KMAJOR_VARIANTS(FAM_FP4, "e2m1"),
+    THL_KMAJOR_VARIANTS(FAM_BF16, "bf16", 4, ""), THL_KMAJOR_VARIANTS(FAM_F16, "f16", 4, ""),
+    THL_KMAJOR_VARIANTS(FAM_I8, "i8", 4, ""),     THL_KMAJOR_VARIANTS(FAM_FP8, "e4m3", 4, ""),
+    THL_KMAJOR_VARIANTS(FAM_FP4, "e2m1", 4, ""),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -212,6 +210,10 @@ thl_status thl_gemm(int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
     }
   }
 
+  // Copy offsets inside a 256-row tile are 32-bit.
+  if (k > 0 && (bytes_of(dt->a, lda) > (INT64_C(1) << 24) || bytes_of(dt->b, ldb) > (INT64_C(1) << 24)))
+    return THL_ERR_UNSUPPORTED;
+
   // ---- variant: first fit on family, alignment and shape
   const int64_t lda_bytes = bytes_of(dt->a, lda), ldb_bytes = bytes_of(dt->b, ldb);
   const char* forced = std::getenv("THL_FORCE_VARIANT");
@@ -228,7 +230,9 @@ thl_status thl_gemm(int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
       } else if (pass == 0 && v.small != want_small) {
         continue;  // first pass: the variant the shape rule prefers
       }
-      const bool fits = k == 0 || (aligned(A, lda_bytes, v.loadw) && aligned(B, ldb_bytes, v.loadw));
+      bool fits = k == 0 || (aligned(A, lda_bytes, v.loadw) && aligned(B, ldb_bytes, v.loadw));
+      if (fam == FAM_FP4 && k > 0 && v.scale_width == 4)
+        fits = fits && aligned(s.sfa, s.ld_sfa, 4) && aligned(s.sfb, s.ld_sfb, 4);
       if (fits) {
         pick = &v;
         break;

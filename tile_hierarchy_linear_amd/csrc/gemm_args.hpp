@@ -1,0 +1,41 @@
+// gemm_args.hpp -- kernel arguments and codes shared by the GEMM kernels and
+// the host dispatch (no device code).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace thl {
+
+// Operand families (one MFMA instruction each).
+enum Family { FAM_F16 = 0, FAM_BF16 = 1, FAM_I8 = 2, FAM_FP8 = 3, FAM_FP4 = 4 };
+
+// Element-type codes, equal to the public thl_dtype values.
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_I8 = 3, DT_I32 = 4 };
+enum : int { EPI_BIAS = 1, EPI_RELU = 2, EPI_GELU = 4 };
+
+struct GemmArgs {
+  const uint8_t* a;  // K-major A: row i (of op(A)) at a + i*lda_bytes
+  const uint8_t* b;  // K-major B: column j (of op(B)) at b + j*ldb_bytes
+  const void* c;
+  void* d;
+  const void* bias;
+  const uint8_t* sfa;  // fp4: E8M0 scales, row i block kb at sfa[i*ld_sfa + kb]
+  const uint8_t* sfb;
+  int64_t lda_bytes, ldb_bytes;
+  int64_t ldc, ldd;  // elements
+  int64_t ld_sfa, ld_sfb;
+  int32_t m, n, k;  // k in elements
+  int32_t kbytes;   // bytes of K per operand row
+  int32_t tiles_m, tiles_n, group_m;
+  float alpha, beta;  // alpha already holds the per-tensor fp8 scales
+  int32_t flags;      // EPI_* bits
+  int32_t c_type, d_type, bias_type;
+};
+
+
+// Launches one K-major kernel variant on `stream`; returns the launch status.
+template <int F, int BM, int BN, int WM, int WN, int LOADW, int STAGES, int OCC, int SCW>
+hipError_t launch_kmajor(const GemmArgs& a, dim3 grid, hipStream_t stream);
+
+}  // namespace thl

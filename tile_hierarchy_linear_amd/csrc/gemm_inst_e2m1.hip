@@ -1,0 +1,8 @@
+// Kernel instantiations for the e2m1 operand family (one unit per family
+// so the library builds in parallel).
+#include "gemm_launch.hpp"
+
+using thl::GemmArgs;
+using thl::FAM_FP4;
+
+THL_INSTANTIATE_KMAJOR(FAM_FP4, 4)

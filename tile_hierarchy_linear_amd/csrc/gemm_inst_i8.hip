@@ -1,0 +1,8 @@
+// Kernel instantiations for the i8 operand family (one unit per family
+// so the library builds in parallel).
+#include "gemm_launch.hpp"
+
+using thl::GemmArgs;
+using thl::FAM_I8;
+
+THL_INSTANTIATE_KMAJOR(FAM_I8, 4)

@@ -23,6 +23,7 @@
 #include <type_traits>
 #include <utility>
 
+#include "gemm_args.hpp"
 #include "index_maps.hpp"
 
 namespace thl {
@@ -36,41 +37,15 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
-// Operand families (one MFMA instruction each).
-enum Family { FAM_F16 = 0, FAM_BF16 = 1, FAM_I8 = 2, FAM_FP8 = 3, FAM_FP4 = 4 };
-
-// Element-type codes, equal to the public thl_dtype values.
-enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_I8 = 3, DT_I32 = 4 };
-enum : int { EPI_BIAS = 1, EPI_RELU = 2, EPI_GELU = 4 };
-
-struct GemmArgs {
-  const uint8_t* a;  // K-major A: row i (of op(A)) at a + i*lda_bytes
-  const uint8_t* b;  // K-major B: column j (of op(B)) at b + j*ldb_bytes
-  const void* c;
-  void* d;
-  const void* bias;
-  const uint8_t* sfa;  // fp4: E8M0 scales, row i block kb at sfa[i*ld_sfa + kb]
-  const uint8_t* sfb;
-  int64_t lda_bytes, ldb_bytes;
-  int64_t ldc, ldd;  // elements
-  int64_t ld_sfa, ld_sfb;
-  int32_t m, n, k;  // k in elements
-  int32_t kbytes;   // bytes of K per operand row
-  int32_t tiles_m, tiles_n, group_m;
-  float alpha, beta;  // alpha already holds the per-tensor fp8 scales
-  int32_t flags;      // EPI_* bits
-  int32_t c_type, d_type, bias_type;
-};
-
 // ------------------------------------------------------------ MFMA families
 // Each family: LANE_CHUNKS 16-byte chunks per lane per MFMA, KSUB MFMAs per
-// 128-byte K-step, the accumulator type, and the instruction.
+// 64-byte K-step, the accumulator type, and the instruction.
 template <int F>
 struct Fam;
 
 template <>
 struct Fam<FAM_BF16> {
-  static constexpr int LANE_CHUNKS = 1, KSUB = 4;
+  static constexpr int LANE_CHUNKS = 1, KSUB = 2;
   static constexpr bool INT = false, SCALED = false;
   using Acc = v16f;
   template <int KS>
@@ -82,7 +57,7 @@ struct Fam<FAM_BF16> {
 
 template <>
 struct Fam<FAM_F16> {
-  static constexpr int LANE_CHUNKS = 1, KSUB = 4;
+  static constexpr int LANE_CHUNKS = 1, KSUB = 2;
   static constexpr bool INT = false, SCALED = false;
   using Acc = v16f;
   template <int KS>
@@ -94,7 +69,7 @@ struct Fam<FAM_F16> {
 
 template <>
 struct Fam<FAM_I8> {
-  static constexpr int LANE_CHUNKS = 1, KSUB = 4;
+  static constexpr int LANE_CHUNKS = 1, KSUB = 2;
   static constexpr bool INT = true, SCALED = false;
   using Acc = v16i;
   template <int KS>
@@ -105,7 +80,7 @@ struct Fam<FAM_I8> {
 
 template <>
 struct Fam<FAM_FP8> {
-  static constexpr int LANE_CHUNKS = 2, KSUB = 2;
+  static constexpr int LANE_CHUNKS = 2, KSUB = 1;
   static constexpr bool INT = false, SCALED = false;
   using Acc = v16f;
   template <int KS>
@@ -120,12 +95,12 @@ struct Fam<FAM_FP8> {
 
 template <>
 struct Fam<FAM_FP4> {
-  static constexpr int LANE_CHUNKS = 1, KSUB = 4;
+  static constexpr int LANE_CHUNKS = 1, KSUB = 2;
   static constexpr bool INT = false, SCALED = true;
   using Acc = v16f;
-  // Scale registers hold this lane's E8M0 bytes for the step: blocks 2*KS
-  // and 2*KS+1 of the step alternate between lane halves, pre-shifted so the
-  // lane's own byte sits at bit 0 (KS even) or bit 16 (KS odd) of the word.
+  // The scale register holds this lane's row's four E8M0 bytes for the step
+  // (blocks 4kt .. 4kt+3), shifted right by 8*(lane/32) so that the lane's
+  // block for sub-step KS (2KS + lane/32) sits in byte 2*KS.
   template <int KS>
   static __device__ __forceinline__ Acc mma(const v4i* a, const v4i* b, Acc c, int sa, int sb) {
     const v4i z = {0, 0, 0, 0};
@@ -228,98 +203,169 @@ __device__ __forceinline__ void load_lds(const void* src, void* lds) {
   }
 }
 
-// ------------------------------------------------------------ the kernel
+// Wait until at most N vector-memory operations of this wave are in flight
+// (gfx9 s_waitcnt: vmcnt low bits [3:0], high bits [15:14]; expcnt and
+// lgkmcnt left at their maxima, i.e. not waited for).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 
-template <int F, int BM, int BN, int WM, int WN, int LOADW>
-__global__ void __launch_bounds__(WM* WN * 64) gemm_kmajor_kernel(GemmArgs p) {
+// ------------------------------------------------------------ the kernel
+//
+// Pipeline (per wavefront, K-steps of 64 bytes per operand row, a ring of
+// STAGES = 4 LDS buffers, copies always issued STAGES-1 steps ahead):
+//
+//   step kt, phase A:  first half of step kt's MFMAs; LDS reads of the
+//                      fragments for the second half (from buffer kt).
+//   barrier:           after this wave's copies of stage kt+1 have landed
+//                      (only stage kt+2's may still be in flight); past it,
+//                      stage kt+1 is visible and every wave has finished
+//                      step kt-1, so buffer kt-1 is free.
+//   step kt, phase B:  second half of step kt's MFMAs; LDS reads of step
+//                      kt+1's first fragments; copies of stage kt+3 into
+//                      the freed buffer.
+//
+// One barrier per step, placed so that the LDS latency of the next step's
+// first fragments hides behind the current step's last MFMAs.  The copies
+// past the last full step re-read the last full step (uniform, in bounds)
+// so every step issues the same number of copies; a partial final K-step is
+// loaded and computed after the loop with bytes past K masked to zero.
+template <int F, int BM, int BN, int WM, int WN, int LOADW, int STAGES, int OCC, int SCW>
+__global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+gemm_kmajor_kernel(GemmArgs p) {
   using T = Fam<F>;
   using Acc = typename T::Acc;
+  constexpr int KB = maps::kStepBytes;
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
-  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, STAGE = A_BYTES + B_BYTES;
-  constexpr int A_INSTR = A_BYTES / (64 * LOADW), B_INSTR = B_BYTES / (64 * LOADW);
-  constexpr int CHUNKS_PER_MFMA = 8 / T::KSUB;
+  constexpr int LC = T::LANE_CHUNKS, KSUB = T::KSUB, CPM = (KB / 16) / KSUB;
+  constexpr int A_BYTES = BM * KB, B_BYTES = BN * KB;
+  constexpr int A_LOADS = A_BYTES / (64 * LOADW * NW), B_LOADS = B_BYTES / (64 * LOADW * NW);
+  constexpr int COPIES = A_LOADS + B_LOADS;  // operand copies per wave per stage
+  constexpr int NSC = T::SCALED ? FM + FN : 1;
+  // fp4 block scales travel with their stage: one dword (the 4 E8M0 bytes of
+  // the K-step) per A and B row, copied with 4-byte lanes (scale rows must be
+  // 4-byte aligned); the per-wave count is padded to a whole number with
+  // copies into a dummy area so every wave issues the same.
+  static_assert(SCW == 4, "scale copies are dwords");
+  constexpr int SC_BYTES = T::SCALED ? (BM + BN) * 4 : 0;
+  constexpr int SC_INSTR = T::SCALED ? (BM + BN) * 4 / (64 * SCW) : 0;
+  constexpr int SC_LOADS = (SC_INSTR + NW - 1) / NW;
+  constexpr int SC_PAD = T::SCALED ? 64 * SCW : 0;
+  constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES + SC_PAD;
+  constexpr int VM_STAGE = COPIES + SC_LOADS;  // vector-memory instructions per wave per stage
+  static_assert(STAGE % 16 == 0, "stages stay 16-byte aligned");
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole MFMA tiles");
-  static_assert(A_INSTR % NW == 0 && B_INSTR % NW == 0, "copy instructions must split evenly over waves");
+  static_assert(A_LOADS * 64 * LOADW * NW == A_BYTES && B_LOADS * 64 * LOADW * NW == B_BYTES,
+                "copies must split evenly over waves");
+  static_assert(STAGES >= 3 && STAGES <= 5, "three to five stages");
+  static_assert(VM_STAGE * (STAGES - 2) < 64, "vmcnt range");
+  // Steps per unrolled loop body: ring slots and fragment-slot parities are
+  // compile-time constants inside it.
+  constexpr int UNROLL = (STAGES % 2 == 0) ? STAGES : 2 * STAGES;
+  static_assert(KSUB == 2 || (KSUB == 1 && FM % 2 == 0), "a step splits into two halves");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE];
 
   const int lane = static_cast<int>(threadIdx.x) & 63;
-  const int wave = static_cast<int>(threadIdx.x) >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int wm = wave % WM, wn = wave / WM;
   int64_t tm, tn;
   maps::grouped_tile(maps::xcd_remap(blockIdx.x, gridDim.x), p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
   const int64_t m0 = tm * BM, n0 = tn * BN;
-  const int nk = (p.kbytes + 127) >> 7;
+  const int nk = (p.kbytes + KB - 1) / KB;  // K-steps, the last one possibly partial
+  const int nkf = p.kbytes / KB;            // full K-steps
 
-  // One K-step of A and B, global -> LDS stage `buf`, as direct loads.
-  auto issue = [&](int kt, int buf) {
-    uint8_t* sa = smem + buf * STAGE;
-    uint8_t* sb = sa + A_BYTES;
-    const int64_t kbase = static_cast<int64_t>(kt) * 128;
+  // Per-tile operand bases (uniform) and per-lane 32-bit byte offsets of
+  // every copy this wave issues; rows past M (N) re-read the last valid row.
+  const uint8_t* a_tile = p.a + m0 * p.lda_bytes;
+  const uint8_t* b_tile = p.b + n0 * p.ldb_bytes;
+  uint32_t a_off[A_LOADS], b_off[B_LOADS];
 #pragma unroll
-    for (int j = 0; j < A_INSTR / NW; ++j) {
-      const int base = (j * NW + wave) * 64 * LOADW;
-      int64_t row, byte;
-      maps::copy_source(base, lane, LOADW, &row, &byte);
-      int64_t g = m0 + row;
-      g = g < p.m ? g : p.m - 1;  // rows past M: any valid row (their outputs are not stored)
-      int64_t kb = kbase + byte;
-      kb = kb < p.kbytes ? kb : 0;  // bytes past K: any valid byte (masked before the MFMA)
-      load_lds<LOADW>(p.a + g * p.lda_bytes + kb, sa + base);
+  for (int j = 0; j < A_LOADS; ++j) {
+    int64_t row, byte;
+    maps::copy_source((j * NW + wave) * 64 * LOADW, lane, LOADW, &row, &byte);
+    const int64_t r = (m0 + row < p.m ? m0 + row : p.m - 1) - m0;
+    a_off[j] = static_cast<uint32_t>(r * p.lda_bytes + byte);
+  }
+#pragma unroll
+  for (int j = 0; j < B_LOADS; ++j) {
+    int64_t row, byte;
+    maps::copy_source((j * NW + wave) * 64 * LOADW, lane, LOADW, &row, &byte);
+    const int64_t r = (n0 + row < p.n ? n0 + row : p.n - 1) - n0;
+    b_off[j] = static_cast<uint32_t>(r * p.ldb_bytes + byte);
+  }
+
+  // fp4 scale copies: per lane, the source row base of each copy it issues.
+  const int nkb = p.k >> 5;
+  const uint8_t* sc_src[T::SCALED ? SC_LOADS : 1];
+  int sc_dst[T::SCALED ? SC_LOADS : 1];
+  if constexpr (T::SCALED) {
+#pragma unroll
+    for (int t = 0; t < SC_LOADS; ++t) {
+      const int j = t * NW + wave;
+      const int row_all = j < SC_INSTR ? j * 64 + lane : 0;
+      if (row_all < BM) {
+        const int64_t r = m0 + row_all < p.m ? m0 + row_all : p.m - 1;
+        sc_src[t] = p.sfa + r * p.ld_sfa;
+      } else {
+        const int64_t r = n0 + (row_all - BM) < p.n ? n0 + (row_all - BM) : p.n - 1;
+        sc_src[t] = p.sfb + r * p.ld_sfb;
+      }
+      sc_dst[t] = A_BYTES + B_BYTES + (j < SC_INSTR ? j * 64 * SCW : SC_BYTES);
     }
+  }
+  // Scale copies of step kt into a stage: bytes 4kt .. 4kt+3 of each row; an
+  // offset at or past the row's last block reads the row's first dword (those
+  // bytes are replaced before use).
+  auto issue_scales = [&](int kt, uint8_t* stage) {
+    if constexpr (T::SCALED) {
 #pragma unroll
-    for (int j = 0; j < B_INSTR / NW; ++j) {
-      const int base = (j * NW + wave) * 64 * LOADW;
-      int64_t row, byte;
-      maps::copy_source(base, lane, LOADW, &row, &byte);
-      int64_t g = n0 + row;
-      g = g < p.n ? g : p.n - 1;
-      int64_t kb = kbase + byte;
-      kb = kb < p.kbytes ? kb : 0;
-      load_lds<LOADW>(p.b + g * p.ldb_bytes + kb, sb + base);
+      for (int t = 0; t < SC_LOADS; ++t) {
+        const int o = 4 * kt;
+        load_lds<SCW>(sc_src[t] + (o < nkb ? o : 0), stage + sc_dst[t]);
+      }
     }
   };
 
-  // fp4 block scales of this lane's rows for K-step kt: bytes 8*kt .. 8*kt+7
-  // of each row, shifted so the lane half's byte is at bit 0 / bit 16.
-  auto load_scales = [&](int kt, int (&sa)[FM][2], int (&sb)[FN][2]) {
-    const int nkb = p.k >> 5;
-    const int shift = 8 * (lane >> 5);
+  // Copies of one full K-step into ring slot BUF: uniform base + 32-bit offset.
+  auto issue_full = [&](int kt, auto buf_tag) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    uint8_t* sa = smem + BUF * STAGE;
+    uint8_t* sb = sa + A_BYTES;
+    const int64_t kofs = static_cast<int64_t>(kt) * KB;
+    issue_scales(kt, sa);
+    const uint8_t* ak = a_tile + kofs;
+    const uint8_t* bk = b_tile + kofs;
 #pragma unroll
-    for (int f = 0; f < FM; ++f) {
-      int64_t r = m0 + wm * TM + f * 32 + (lane & 31);
-      r = r < p.m ? r : p.m - 1;
-      const uint8_t* s = p.sfa + r * p.ld_sfa + 8 * kt;
+    for (int j = 0; j < A_LOADS; ++j) load_lds<LOADW>(ak + a_off[j], sa + (j * NW + wave) * 64 * LOADW);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        unsigned w = 0x7f7f7f7fu;
-        if (8 * kt + 4 * h + 4 <= nkb && (reinterpret_cast<uintptr_t>(s + 4 * h) & 3) == 0) {
-          w = *reinterpret_cast<const unsigned*>(s + 4 * h);
-        } else {
-          for (int q = 0; q < 4; ++q)
-            if (8 * kt + 4 * h + q < nkb) w = (w & ~(0xffu << (8 * q))) | (static_cast<unsigned>(s[4 * h + q]) << (8 * q));
-        }
-        sa[f][h] = static_cast<int>(w >> shift);
-      }
+    for (int j = 0; j < B_LOADS; ++j) load_lds<LOADW>(bk + b_off[j], sb + (j * NW + wave) * 64 * LOADW);
+  };
+
+  // The partial last K-step into slot 0: bytes at or past K read from the
+  // row's first byte instead (masked before the MFMAs).
+  auto issue_partial = [&](int kt) {
+    uint8_t* sa = smem;
+    uint8_t* sb = sa + A_BYTES;
+    const int64_t kofs = static_cast<int64_t>(kt) * KB;
+    issue_scales(kt, sa);
+#pragma unroll
+    for (int j = 0; j < A_LOADS; ++j) {
+      int64_t row, byte;
+      maps::copy_source((j * NW + wave) * 64 * LOADW, lane, LOADW, &row, &byte);
+      const uint8_t* src = a_tile + a_off[j] + (kofs + byte < p.kbytes ? kofs : -byte);
+      load_lds<LOADW>(src, sa + (j * NW + wave) * 64 * LOADW);
     }
 #pragma unroll
-    for (int f = 0; f < FN; ++f) {
-      int64_t r = n0 + wn * TN + f * 32 + (lane & 31);
-      r = r < p.n ? r : p.n - 1;
-      const uint8_t* s = p.sfb + r * p.ld_sfb + 8 * kt;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        unsigned w = 0x7f7f7f7fu;
-        if (8 * kt + 4 * h + 4 <= nkb && (reinterpret_cast<uintptr_t>(s + 4 * h) & 3) == 0) {
-          w = *reinterpret_cast<const unsigned*>(s + 4 * h);
-        } else {
-          for (int q = 0; q < 4; ++q)
-            if (8 * kt + 4 * h + q < nkb) w = (w & ~(0xffu << (8 * q))) | (static_cast<unsigned>(s[4 * h + q]) << (8 * q));
-        }
-        sb[f][h] = static_cast<int>(w >> shift);
-      }
+    for (int j = 0; j < B_LOADS; ++j) {
+      int64_t row, byte;
+      maps::copy_source((j * NW + wave) * 64 * LOADW, lane, LOADW, &row, &byte);
+      const uint8_t* src = b_tile + b_off[j] + (kofs + byte < p.kbytes ? kofs : -byte);
+      load_lds<LOADW>(src, sb + (j * NW + wave) * 64 * LOADW);
     }
   };
 
@@ -329,71 +375,157 @@ __global__ void __launch_bounds__(WM* WN * 64) gemm_kmajor_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = Acc{};
 
-  int sc_a[FM][2] = {}, sc_b[FN][2] = {};
-  if (nk > 0) {
-    issue(0, 0);
-    if constexpr (T::SCALED) load_scales(0, sc_a, sc_b);
+  // Per-lane LDS offset of the chunk read for MFMA sub-step ks: fragment rows
+  // differ by multiples of 32, which leave the swizzle unchanged, so one
+  // offset per sub-step serves every fragment row (plus a constant).
+  const int lrow = lane & 31;
+  int chunk_off[KSUB][LC];
+#pragma unroll
+  for (int ks = 0; ks < KSUB; ++ks)
+#pragma unroll
+    for (int c = 0; c < LC; ++c)
+      chunk_off[ks][c] = static_cast<int>(maps::lds_offset(lrow, (ks * CPM + (lane >> 5) * LC + c) * 16));
+  const int a_wave_off = wm * TM * KB, b_wave_off = A_BYTES + wn * TN * KB;
+
+  v4i af[2][FM][LC], bf[2][FN][LC];  // fragment slots: (kt*KSUB + ks) & 1
+
+  auto read = [&](const uint8_t* stage, auto ks_tag, auto slot_tag, int kvalid) {
+    constexpr int KS = decltype(ks_tag)::value, SL = decltype(slot_tag)::value;
+#pragma unroll
+    for (int f = 0; f < FM; ++f)
+#pragma unroll
+      for (int c = 0; c < LC; ++c) {
+        af[SL][f][c] = *reinterpret_cast<const v4i*>(stage + a_wave_off + f * 32 * KB + chunk_off[KS][c]);
+        if (kvalid < KB) af[SL][f][c] = mask_bytes(af[SL][f][c], kvalid - (KS * CPM + (lane >> 5) * LC + c) * 16);
+      }
+#pragma unroll
+    for (int f = 0; f < FN; ++f)
+#pragma unroll
+      for (int c = 0; c < LC; ++c) {
+        bf[SL][f][c] = *reinterpret_cast<const v4i*>(stage + b_wave_off + f * 32 * KB + chunk_off[KS][c]);
+        if (kvalid < KB) bf[SL][f][c] = mask_bytes(bf[SL][f][c], kvalid - (KS * CPM + (lane >> 5) * LC + c) * 16);
+      }
+  };
+
+  // MFMAs of sub-step KS on rows [I0, I1) of the wave tile from slot SL.
+  auto mma = [&](auto ks_tag, auto slot_tag, auto i0_tag, auto i1_tag, const int (&scl)[NSC]) {
+    constexpr int KS = decltype(ks_tag)::value, SL = decltype(slot_tag)::value;
+    constexpr int I0 = decltype(i0_tag)::value, I1 = decltype(i1_tag)::value;
+#pragma unroll
+    for (int i = I0; i < I1; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        int s_a = 0, s_b = 0;
+        if constexpr (T::SCALED) {
+          s_a = scl[i];
+          s_b = scl[FM + j];
+        }
+        acc[i][j] = T::template mma<KS>(af[SL][i], bf[SL][j], acc[i][j], s_a, s_b);
+      }
+  };
+
+  // This lane's scale dword for each fragment row, read from a stage, shifted
+  // right by 8*(lane/32) so sub-step KS finds its block in byte 2*KS.
+  auto scales_of = [&](const uint8_t* stage, int (&scl)[NSC], bool tail) {
+    if constexpr (T::SCALED) {
+      const int shift = 8 * (lane >> 5);
+#pragma unroll
+      for (int f = 0; f < NSC; ++f) {
+        const int row_all = f < FM ? wm * TM + f * 32 + (lane & 31) : BM + wn * TN + (f - FM) * 32 + (lane & 31);
+        int v = *reinterpret_cast<const int*>(stage + A_BYTES + B_BYTES + row_all * 4);
+        if (tail) {
+          // blocks at or past K get scale 1.0 (their data is zero)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (4 * nkf + q >= nkb) v = (v & ~(0xff << (8 * q))) | (127 << (8 * q));
+        }
+        scl[f] = v >> shift;
+      }
+    } else {
+      scl[0] = 0;
+    }
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using IFM = std::integral_constant<int, FM>;
+  using IH = std::integral_constant<int, FM / 2>;
+
+  if (nkf > 0) {
+    // Prologue: stages 0 .. STAGES-2, then step 0's first fragments.
+    static_for<STAGES - 1>([&](auto sc) {
+      constexpr int S = decltype(sc)::value;
+      issue_full(S < nkf ? S : nkf - 1, std::integral_constant<int, S>{});
+    });
+    wait_vm<(STAGES - 2) * VM_STAGE>();
+    __syncthreads();
+    read(smem, I0{}, I0{}, KB);
+
+    for (int kb = 0; kb < nkf; kb += UNROLL) {
+      static_for<UNROLL>([&](auto uc) {
+        constexpr int U = decltype(uc)::value;
+        constexpr int S = U % STAGES;  // ring slot of step kt
+        constexpr int NEXT = (S + 1) % STAGES, ISSUE = (S + STAGES - 1) % STAGES;
+        constexpr int PAR = U & 1;     // parity of kt (kb is even)
+        const int kt = kb + U;
+        if (kt < nkf) {
+          const uint8_t* cur = smem + S * STAGE;
+          int scl[NSC];
+          scales_of(cur, scl, false);
+          // ---- phase A
+          if constexpr (KSUB == 2) {
+            mma(I0{}, I0{}, I0{}, IFM{}, scl);
+            read(cur, I1{}, I1{}, KB);
+            static_for<FM * FN>([&](auto t) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              if constexpr (decltype(t)::value % 2 == 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            });
+          } else {
+            mma(I0{}, std::integral_constant<int, PAR>{}, I0{}, IH{}, scl);
+          }
+          // ---- barrier: stage kt+1 visible, buffer kt-1 free
+          wait_vm<(STAGES - 3) * VM_STAGE>();
+          __syncthreads();
+          // ---- phase B
+          const int nxt = kt + STAGES - 1 < nkf ? kt + STAGES - 1 : nkf - 1;
+          issue_full(nxt, std::integral_constant<int, ISSUE>{});
+          if constexpr (KSUB == 2) {
+            mma(I1{}, I1{}, I0{}, IFM{}, scl);
+            read(smem + NEXT * STAGE, I0{}, I0{}, KB);
+          } else {
+            mma(I0{}, std::integral_constant<int, PAR>{}, IH{}, IFM{}, scl);
+            read(smem + NEXT * STAGE, I0{}, std::integral_constant<int, PAR ^ 1>{}, KB);
+          }
+          constexpr int NM = (KSUB == 2) ? FM * FN : FM * FN / 2;
+          constexpr int NR = (FM + FN) * LC;
+          static_for<NM>([&](auto t) {
+            constexpr int T_ = decltype(t)::value;
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if constexpr ((T_ * NR) / NM != ((T_ + 1) * NR) / NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if constexpr ((T_ * VM_STAGE) / NM != ((T_ + 1) * VM_STAGE) / NM)
+              __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          });
+        }
+      });
+    }
   }
 
-  for (int kt = 0; kt < nk; ++kt) {
-    __builtin_amdgcn_s_waitcnt(0);  // this thread's loads of stage kt have landed
-    __syncthreads();                // ... everyone's, and stage kt-1 is no longer read
-    if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
-    int cur_a[FM][2], cur_b[FN][2];
-    if constexpr (T::SCALED) {
-#pragma unroll
-      for (int f = 0; f < FM; ++f) cur_a[f][0] = sc_a[f][0], cur_a[f][1] = sc_a[f][1];
-#pragma unroll
-      for (int f = 0; f < FN; ++f) cur_b[f][0] = sc_b[f][0], cur_b[f][1] = sc_b[f][1];
-      if (kt + 1 < nk) load_scales(kt + 1, sc_a, sc_b);
+  // The partial last K-step, if any: load it alone, then compute masked.
+  if (nk > nkf) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // every buffer is free
+    issue_partial(nkf);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    int scl[NSC];
+    scales_of(smem, scl, true);
+    const int kvalid = p.kbytes - nkf * KB;
+    read(smem, I0{}, I0{}, kvalid);
+    mma(I0{}, I0{}, I0{}, IFM{}, scl);
+    if constexpr (KSUB == 2) {
+      read(smem, I1{}, I1{}, kvalid);
+      mma(I1{}, I1{}, I0{}, IFM{}, scl);
     }
-    const uint8_t* sa = smem + (kt & 1) * STAGE;
-    const uint8_t* sb = sa + A_BYTES;
-    const int kvalid = p.kbytes - kt * 128;
-
-    auto step = [&](auto ks_tag) {
-      constexpr int KS = decltype(ks_tag)::value;
-      v4i af[FM][T::LANE_CHUNKS], bf[FN][T::LANE_CHUNKS];
-#pragma unroll
-      for (int f = 0; f < FM; ++f) {
-        const int row = wm * TM + f * 32 + (lane & 31);
-#pragma unroll
-        for (int c = 0; c < T::LANE_CHUNKS; ++c) {
-          const int chunk = KS * CHUNKS_PER_MFMA + (lane >> 5) * T::LANE_CHUNKS + c;
-          af[f][c] = *reinterpret_cast<const v4i*>(sa + maps::lds_offset(row, chunk * 16));
-          if (kvalid < 128) af[f][c] = mask_bytes(af[f][c], kvalid - chunk * 16);
-        }
-      }
-#pragma unroll
-      for (int f = 0; f < FN; ++f) {
-        const int row = wn * TN + f * 32 + (lane & 31);
-#pragma unroll
-        for (int c = 0; c < T::LANE_CHUNKS; ++c) {
-          const int chunk = KS * CHUNKS_PER_MFMA + (lane >> 5) * T::LANE_CHUNKS + c;
-          bf[f][c] = *reinterpret_cast<const v4i*>(sb + maps::lds_offset(row, chunk * 16));
-          if (kvalid < 128) bf[f][c] = mask_bytes(bf[f][c], kvalid - chunk * 16);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          int s_a = 0, s_b = 0;
-          if constexpr (T::SCALED) {
-            s_a = cur_a[i][KS >> 1];
-            s_b = cur_b[j][KS >> 1];
-          }
-          acc[i][j] = T::template mma<KS>(af[i], bf[j], acc[i][j], s_a, s_b);
-        }
-    };
-    step(std::integral_constant<int, 0>{});
-    if constexpr (T::KSUB > 1) step(std::integral_constant<int, 1>{});
-    if constexpr (T::KSUB > 2) {
-      step(std::integral_constant<int, 2>{});
-      step(std::integral_constant<int, 3>{});
-    }
-    (void)cur_a;
-    (void)cur_b;
   }
 
   // ---------------------------------------------------------- epilogue

@@ -8,8 +8,8 @@
 //
 // Tile hierarchy ("CUTLASS" knowledge-base page, "The tile hierarchy"):
 //   workgroup tile BM x BN  ->  wavefront tile (BM/WM) x (BN/WN)  ->  32x32 MFMA tiles.
-// Operands are staged in LDS as rows of 128 bytes of K (one K-step), each row
-// split into eight 16-byte chunks whose order is XOR-swizzled per row.
+// Operands are staged in LDS as rows of 64 bytes of K (one K-step), each row
+// split into four 16-byte chunks whose order is XOR-swizzled per row.
 #pragma once
 
 #include <stdint.h>
@@ -48,19 +48,21 @@ THL_HD void grouped_tile(int64_t id, int64_t tiles_m, int64_t tiles_n, int64_t g
 }
 
 // ------------------------------------------------------------ a3: LDS staging
-// Chunk order within a staged row: chunk c of row r is stored in slot
-// c ^ swz(r).  swz(r) = (r % 8) ^ ((r / 8) % 2): any 8 consecutive rows use 8
-// distinct slots for the same chunk, and any 16 consecutive rows use 16
-// distinct (row parity, slot) pairs, so a wavefront reading one chunk from
-// 32 consecutive rows spreads over all banks of a 128- or 256-byte bank
-// window.  On a 16-byte granule it is the XOR swizzle with b = 3, m = 4,
-// s = 3 composed on the row-major (rows, 128) byte layout, plus the parity
-// term.
-THL_HD int swz(int64_t row) { return static_cast<int>((row & 7) ^ ((row >> 3) & 1)); }
+// One K-step stages 64 bytes of K per operand row: four 16-byte chunks whose
+// order is XOR-swizzled per row.  Chunk c of row r is stored in slot
+// c ^ swz(r) with swz(r) = ((r >> 1) ^ (r >> 3)) & 3.  Reading one chunk from
+// consecutive rows (what the MFMA fragment reads do), any 8 rows land on 8
+// distinct (row parity, slot) pairs -- all 32 banks of a 128-byte window --
+// and any 16 rows on 16 distinct (row % 4, slot) pairs -- all 64 banks of a
+// 256-byte window.  On the row-major (rows, 64) byte layout it is two XOR
+// swizzles (b=2, m=4, s=3) and (b=2, m=4, s=5) composed on top.
+constexpr int kStepBytes = 64;
 
-// Byte offset, inside one staged operand buffer, of byte `b` (0..127) of row `row`.
+THL_HD int swz(int64_t row) { return static_cast<int>(((row >> 1) ^ (row >> 3)) & 3); }
+
+// Byte offset, inside one staged operand buffer, of byte `b` (0..63) of row `row`.
 THL_HD int64_t lds_offset(int64_t row, int64_t b) {
-  return row * 128 + ((((b >> 4) ^ swz(row)) & 7) << 4) + (b & 15);
+  return row * kStepBytes + ((((b >> 4) ^ swz(row)) & 3) << 4) + (b & 15);
 }
 
 // Direct global->LDS loads write `loadw` bytes per lane at consecutive LDS
@@ -69,10 +71,10 @@ THL_HD int64_t lds_offset(int64_t row, int64_t b) {
 // and in-row byte that the inverse of lds_offset assigns to that LDS byte.
 THL_HD void copy_source(int64_t base, int64_t lane, int64_t loadw, int64_t* row, int64_t* byte_in_row) {
   const int64_t off = base + lane * loadw;
-  const int64_t r = off >> 7;
-  const int64_t slot = (off >> 4) & 7;
+  const int64_t r = off / kStepBytes;
+  const int64_t slot = (off >> 4) & 3;
   *row = r;
-  *byte_in_row = (((slot ^ swz(r)) & 7) << 4) | (off & 15);
+  *byte_in_row = (((slot ^ swz(r)) & 3) << 4) | (off & 15);
 }
 
 // ------------------------------------------------------------ a4/a5: MFMA maps

@@ -259,10 +259,14 @@ def make(kind: str, m: int, n: int, k: int, seed: int | None = None, *, op_a=Non
         xa, xb = ga.standard_normal((m, k)), gb.standard_normal((n, k))  # B drawn as its stored N x K
         ca_codes, w["sfa"] = mx_quantize(xa) if k else (np.zeros((m, 0), np.uint8), np.zeros((m, 0), np.uint8))
         cb_codes, w["sfb"] = mx_quantize(xb) if k else (np.zeros((n, 0), np.uint8), np.zeros((n, 0), np.uint8))
-        w["ld_sfa"] = w["ld_sfb"] = max(1, k // 32)
-        if k == 0:
-            w["sfa"] = np.zeros((m, 1), np.uint8)
-            w["sfb"] = np.zeros((n, 1), np.uint8)
+        # scale rows padded to a multiple of 4 bytes (the kernels copy dwords)
+        ld_sf = max(4, (k // 32 + 3) // 4 * 4)
+        w["ld_sfa"] = w["ld_sfb"] = ld_sf
+        pad_a = np.full((m, ld_sf), 127, np.uint8)
+        pad_a[:, : k // 32] = w["sfa"]
+        pad_b = np.full((n, ld_sf), 127, np.uint8)
+        pad_b[:, : k // 32] = w["sfb"]
+        w["sfa"], w["sfb"] = pad_a, pad_b
         mem_a = np.zeros((m, lda), np.uint8)
         mem_a[:, :k] = ca_codes
         mem_b = np.zeros((n, ldb), np.uint8)
