@@ -148,8 +148,7 @@ def main():
 
     results = {}
     headline = None
-    for key, kind, kw in (("bf16", "bf16", dict(op_a="T", op_b="N")), ("e4m3", "fp8", {}),
-                          ("e2m1", "mxfp4", {})):
+    for key, kind, kw in (("bf16", "bf16", {}), ("e4m3", "fp8", {}), ("e2m1", "mxfp4", {})):
         if key not in only:
             continue
         t0 = time.perf_counter()
@@ -178,8 +177,9 @@ def main():
             headline = (w, ms, byt, variant)
         if args.sweep_variants:
             fam = {"bf16": "bf16", "e4m3": "e4m3", "e2m1": "e2m1"}[key]
+            ops = (w.op_a + w.op_b).lower()
             for v in thl.variants():
-                if not v.startswith(fam + "_"):
+                if not v.startswith(f"{fam}_{ops}_"):
                     continue
                 os.environ["THL_FORCE_VARIANT"] = v
                 try:

@@ -147,7 +147,7 @@ def test_quick_returns_do_not_launch():
 
 
 def test_forced_variant_must_fit():
-    os.environ["THL_FORCE_VARIANT"] = "i8_tn_256x256_w2x2_v16_s4"
+    os.environ["THL_FORCE_VARIANT"] = "i8_tn_256x256_v16_s4_o1"
     try:
         assert call(m=0) == thl.THL_ERR_UNSUPPORTED  # bf16 problem, int8 variant
     finally:

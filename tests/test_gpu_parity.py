@@ -138,16 +138,35 @@ def test_every_variant(variant_family):
     import tile_hierarchy_linear_amd as thl
     import workloads as wl
 
-    kind = {"f16": "fp16", "bf16": "fp16", "i8": "int8", "e4m3": "fp8", "e2m1": "mxfp4"}[variant_family]
+    kind = {"f16": "fp16", "bf16": "bf16", "i8": "int8", "e4m3": "fp8", "e2m1": "mxfp4"}[variant_family]
+    ops = {"tn": ("T", "N"), "nn": ("N", "N"), "tt": ("T", "T"), "nt": ("N", "T")}
     for v in thl.variants():
         if not v.startswith(variant_family + "_"):
             continue
-        m, n, k = 300, 260, 512
-        if variant_family == "bf16":
-            w = wl.make("bf16", m, n, k, op_a="T", op_b="N")
+        op_a, op_b = ops[v.split("_")[1]]
+        m, n, k = 300, 260, 520
+        if kind in ("fp16", "bf16"):
+            lda = _pad(m if op_a == "N" else k, 8)  # 16-byte leading dimensions
+            ldb = _pad(k if op_b == "N" else n, 8)
+            w = wl.make(kind, m, n, k, op_a=op_a, op_b=op_b, lda=lda, ldb=ldb)
         else:
-            w = wl.make(kind, m, n, k)
+            w = wl.make(kind, m, n, 512)
         _check_full(w, variant=v)
+
+
+@pytest.mark.parametrize("ops", [("N", "N"), ("T", "T"), ("N", "T"), ("T", "N")])
+@pytest.mark.parametrize("shape", [(1, 1, 1), (7, 17, 33), (64, 64, 64), (129, 65, 255), (257, 300, 130)])
+def test_all_four_layouts_16bit(ops, shape):
+    import workloads as wl
+
+    m, n, k = shape
+    pad = lambda x: (x + 7) // 8 * 8  # noqa: E731 -- 16-byte leading dimensions
+    ra, ca = (m, k) if ops[0] == "N" else (k, m)
+    rb, cb = (k, n) if ops[1] == "N" else (n, k)
+    w = wl.make("bf16", m, n, k, op_a=ops[0], op_b=ops[1], lda=pad(ra), ldb=pad(rb))
+    _check_full(w)
+    w = wl.make("fp16", m, n, k, op_a=ops[0], op_b=ops[1], lda=pad(ra), ldb=pad(rb))
+    _check_full(w)
 
 
 def test_k_zero_is_epilogue_only():
@@ -189,6 +208,21 @@ def test_output_padding_untouched():
 
 
 # ------------------------------------------------------------ large configurations
+
+def test_config_bf16_nn_4096_relu_bias_residual():
+    import workloads as wl
+
+    w = wl.make("bf16", 4096, 4096, 4096)  # N/N, D = relu(A.B + C + bias[m]), bf16 out
+    assert (w.op_a, w.op_b, w.act, w.beta) == ("N", "N", "relu", 1.0)
+    _check_sampled(w)
+
+
+def test_config_bf16_nn_ragged():
+    import workloads as wl
+
+    w = wl.make("bf16", 1000, 777, 1030)
+    _check_sampled(w, extra_edges=True)
+
 
 def test_config_int8_4096_sampled_exact():
     import workloads as wl

@@ -18,7 +18,7 @@ def test_map_names_are_all_known():
     for n in names:
         pts = [(0, 0)]
         params = {"xcd_remap": (8,), "grouped_tile": (4, 4, 2), "copy_source": (16,),
-                  "mfma32_operand": (8,)}.get(n, ())
+                  "mfma32_operand": (8,), "mm_lds_offset": (256,), "mm_copy_source": (16, 256)}.get(n, ())
         thl.thl_kernel_index_map(n, pts, params)
     with pytest.raises(thl.ThlError):
         thl.thl_kernel_index_map("no_such_map", [(0, 0)])
@@ -146,3 +146,50 @@ def test_grouped_raster_is_the_layout(tm, tn, group):
             assert flat[:full] == _eval(f"({group},{tn},{tm // group}):(1,{tm},{group})", full)
         rest = tm - (tm // group) * group  # the last band is narrower
         assert flat[full:] == [(tm - rest) + a + tm * b for b in range(tn) for a in range(rest)]
+
+
+def test_transposed_read_lands_the_mfma_operand_layout():
+    # Compose: lane l of group G addresses chunk (k, m) = tr16_operand(l, h);
+    # after the transposed read, lane i of the group holds, as value v,
+    # element i%4 of the chunk addressed by lane 4v + i/4.  The result must be
+    # the 32x32x16 operand map: row l % 32, k = 8*(l/32) + 4h + v.
+    for h in (0, 1):
+        for l in range(64):
+            g, i = l // 16, l % 16
+            for v in range(4):
+                (src, elem), = thl.thl_kernel_index_map("tr16_source", [(i, v)])
+                (k, m), = thl.thl_kernel_index_map("tr16_operand", [(16 * g + src, h)])
+                got = (m + elem, k)
+                (row, kk), = thl.thl_kernel_index_map("mfma32_operand", [(l, 4 * h + v)], (8,))
+                assert got == (row, kk), (h, l, v)
+
+
+@pytest.mark.parametrize("pitch", [256, 512])
+def test_mm_lds_layout_is_a_bijection_and_copy_inverts_it(pitch):
+    rows = 32
+    pts = [(k, b) for k in range(rows) for b in range(pitch)]
+    offs = [o for o, _ in thl.thl_kernel_index_map("mm_lds_offset", pts, (pitch,))]
+    assert sorted(offs) == list(range(rows * pitch))
+    for loadw in (16, 4):
+        src = thl.thl_kernel_index_map(
+            "mm_copy_source", [(base, lane) for base in range(0, rows * pitch, 64 * loadw) for lane in range(64)],
+            (loadw, pitch))
+        back = thl.thl_kernel_index_map("mm_lds_offset", src, (pitch,))
+        assert [o for o, _ in back] == [base + lane * loadw for base in range(0, rows * pitch, 64 * loadw)
+                                        for lane in range(64)]
+
+
+@pytest.mark.parametrize("pitch", [256, 512])
+def test_transposed_reads_spread_over_banks(pitch):
+    # Each 16-lane group reads 16 eight-byte chunks (4 k-rows x 32 bytes):
+    # with the k-row swizzle no 4-byte bank of a 256-byte window is hit twice.
+    for r0 in (0, 32, 64, 96):
+        for ks in (0, 1):
+            for h in (0, 1):
+                for g in range(4):
+                    banks = []
+                    for i in range(16):
+                        (k, m), = thl.thl_kernel_index_map("tr16_operand", [(16 * g + i, h)])
+                        (o, _), = thl.thl_kernel_index_map("mm_lds_offset", [(k + 16 * ks, 2 * (r0 + m))], (pitch,))
+                        banks += [(o % 256) // 4, (o % 256) // 4 + 1]
+                    assert len(set(banks)) == 32

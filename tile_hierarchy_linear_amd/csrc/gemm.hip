@@ -25,28 +25,40 @@ using LaunchFn = hipError_t (*)(const GemmArgs&, dim3, hipStream_t);
 struct Variant {
   const char* name;
   int family;
+  bool a_kmajor, b_kmajor;  // opA == T, opB == N
   int bm, bn, threads, loadw;
-  bool small;       // preferred when the large tile cannot fill the device
-  int scale_width;  // fp4 scale copies: 4-byte lanes, so scale rows must be 4-byte aligned
+  bool small;  // preferred when the large tile cannot fill the device
   LaunchFn launch;
 };
 
-// Must list exactly the instantiations of THL_INSTANTIATE_KMAJOR.  Order is
-// the first-fit order: large tiles first, then the small-problem tiles.
-#define THL_KMAJOR_VARIANTS(FAM, NAME, SCW, SUFFIX)                                                       \
-  {NAME "_tn_256x128_w2x2_v16_s3_o2" SUFFIX, FAM, 256, 128, 256, 16, false, SCW,                           \
-   &launch_kmajor<FAM, 256, 128, 2, 2, 16, 3, 2, SCW>},                                                    \
-      {NAME "_tn_256x256_w2x2_v16_s4" SUFFIX, FAM, 256, 256, 256, 16, false, SCW,                           \
-       &launch_kmajor<FAM, 256, 256, 2, 2, 16, 4, 1, SCW>},                                                 \
-      {NAME "_tn_128x128_w2x2_v16_s4_o2" SUFFIX, FAM, 128, 128, 256, 16, true, SCW,                         \
-       &launch_kmajor<FAM, 128, 128, 2, 2, 16, 4, 2, SCW>},                                                 \
-      {NAME "_tn_128x128_w2x2_v4_s4_o2" SUFFIX, FAM, 128, 128, 256, 4, true, SCW,                           \
-       &launch_kmajor<FAM, 128, 128, 2, 2, 4, 4, 2, SCW>}
+#define THL_V(FAM, NAME, OPS, AK, BK, BM, BN, LOADW, ST, OCC, SMALL)                                       \
+  {NAME "_" OPS "_" #BM "x" #BN "_v" #LOADW "_s" #ST "_o" #OCC, FAM, AK, BK, BM, BN, 256, LOADW, SMALL,   \
+   &launch_gemm<FAM, BM, BN, 2, 2, LOADW, ST, OCC, 4, AK, BK>}
+
+// Must list exactly the instantiations of THL_INSTANTIATE_TN / _OPS.  Order
+// is the first-fit order: large tiles first, then the small-problem tiles.
+#define THL_TN_VARIANTS(FAM, NAME)                                  \
+  THL_V(FAM, NAME, "tn", true, true, 256, 128, 16, 3, 2, false),    \
+      THL_V(FAM, NAME, "tn", true, true, 256, 256, 16, 4, 1, false), \
+      THL_V(FAM, NAME, "tn", true, true, 128, 128, 16, 4, 2, true),  \
+      THL_V(FAM, NAME, "tn", true, true, 128, 128, 4, 4, 2, true)
+#define THL_OPS_VARIANTS(FAM, NAME, OPS, AK, BK)                 \
+  THL_V(FAM, NAME, OPS, AK, BK, 256, 128, 16, 3, 2, false),      \
+      THL_V(FAM, NAME, OPS, AK, BK, 128, 128, 16, 4, 2, true),   \
+      THL_V(FAM, NAME, OPS, AK, BK, 128, 128, 4, 4, 2, true)
 
 const Variant kVariants[] = {
-    THL_KMAJOR_VARIANTS(FAM_BF16, "bf16", 4, ""), THL_KMAJOR_VARIANTS(FAM_F16, "f16", 4, ""),
-    THL_KMAJOR_VARIANTS(FAM_I8, "i8", 4, ""),     THL_KMAJOR_VARIANTS(FAM_FP8, "e4m3", 4, ""),
-    THL_KMAJOR_VARIANTS(FAM_FP4, "e2m1", 4, ""),
+    THL_TN_VARIANTS(FAM_BF16, "bf16"),
+    THL_OPS_VARIANTS(FAM_BF16, "bf16", "nn", false, true),
+    THL_OPS_VARIANTS(FAM_BF16, "bf16", "tt", true, false),
+    THL_OPS_VARIANTS(FAM_BF16, "bf16", "nt", false, false),
+    THL_TN_VARIANTS(FAM_F16, "f16"),
+    THL_OPS_VARIANTS(FAM_F16, "f16", "nn", false, true),
+    THL_OPS_VARIANTS(FAM_F16, "f16", "tt", true, false),
+    THL_OPS_VARIANTS(FAM_F16, "f16", "nt", false, false),
+    THL_TN_VARIANTS(FAM_I8, "i8"),
+    THL_TN_VARIANTS(FAM_FP8, "e4m3"),
+    THL_TN_VARIANTS(FAM_FP4, "e2m1"),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -171,8 +183,9 @@ thl_status thl_gemm(int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
     if (beta != 0.0f && !is_float_io(dt->c)) return THL_ERR_UNSUPPORTED;
     if (has_bias && !is_float_io(dt->bias)) return THL_ERR_UNSUPPORTED;
   }
-  // K-major operands only: op(A) rows and op(B) columns contiguous along K.
-  if (opA != THL_OP_T || opB != THL_OP_N) return THL_ERR_UNSUPPORTED;
+  // 8- and 4-bit operands: K-major only (op(A) rows, op(B) columns contiguous along K).
+  const bool a_kmajor = opA == THL_OP_T, b_kmajor = opB == THL_OP_N;
+  if (fam != FAM_BF16 && fam != FAM_F16 && (!a_kmajor || !b_kmajor)) return THL_ERR_UNSUPPORTED;
   if (fam == FAM_FP4 && (k % 32 != 0)) return THL_ERR_UNSUPPORTED;
 
   // ---- leading dimensions and pointers
@@ -223,7 +236,7 @@ thl_status thl_gemm(int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
   bool family_built = false;
   for (int pass = 0; pass < 2 && !pick; ++pass) {
     for (const Variant& v : kVariants) {
-      if (v.family != fam) continue;
+      if (v.family != fam || v.a_kmajor != a_kmajor || v.b_kmajor != b_kmajor) continue;
       family_built = true;
       if (forced && *forced) {
         if (std::strcmp(forced, v.name) != 0) continue;
@@ -231,8 +244,7 @@ thl_status thl_gemm(int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
         continue;  // first pass: the variant the shape rule prefers
       }
       bool fits = k == 0 || (aligned(A, lda_bytes, v.loadw) && aligned(B, ldb_bytes, v.loadw));
-      if (fam == FAM_FP4 && k > 0 && v.scale_width == 4)
-        fits = fits && aligned(s.sfa, s.ld_sfa, 4) && aligned(s.sfb, s.ld_sfb, 4);
+      if (fam == FAM_FP4 && k > 0) fits = fits && aligned(s.sfa, s.ld_sfa, 4) && aligned(s.sfb, s.ld_sfb, 4);
       if (fits) {
         pick = &v;
         break;
@@ -288,7 +300,8 @@ thl_status thl_gemm(int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
 // ---------------------------------------------------------------- index maps
 
 const char* thl_kernel_index_map_names(void) {
-  return "xcd_remap,grouped_tile,swz,lds_offset,copy_source,mfma32_operand,mfma32_acc,fp8_32x32_k,tr16_source";
+  return "xcd_remap,grouped_tile,swz,lds_offset,copy_source,mfma32_operand,mfma32_acc,fp8_32x32_k,tr16_source,"
+         "mm_lds_offset,mm_copy_source,tr16_operand";
 }
 
 int thl_kernel_index_map(const char* map, const int64_t* params, int64_t n, const int64_t* in, int64_t* out) {
@@ -319,6 +332,14 @@ int thl_kernel_index_map(const char* map, const int64_t* params, int64_t n, cons
       r0 = maps::fp8_32x32_k_of(x, y);
     } else if (!std::strcmp(map, "tr16_source")) {
       maps::tr16_source(x, y, &r0, &r1);
+    } else if (!std::strcmp(map, "mm_lds_offset")) {
+      if (!params || param(0) <= 0 || param(0) % 256 != 0) return THL_ERR_INVALID;
+      r0 = maps::mm_lds_offset(x, y, param(0));
+    } else if (!std::strcmp(map, "mm_copy_source")) {
+      if (!params || (param(0) != 4 && param(0) != 16) || param(1) <= 0 || param(1) % 256 != 0) return THL_ERR_INVALID;
+      maps::mm_copy_source(x, y, param(0), param(1), &r0, &r1);
+    } else if (!std::strcmp(map, "tr16_operand")) {
+      maps::tr16_operand(x, y, &r0, &r1);
     } else {
       return THL_ERR_INVALID;
     }

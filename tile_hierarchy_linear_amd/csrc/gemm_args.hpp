@@ -15,8 +15,8 @@ enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_I8 = 3, DT_I32 = 4 };
 enum : int { EPI_BIAS = 1, EPI_RELU = 2, EPI_GELU = 4 };
 
 struct GemmArgs {
-  const uint8_t* a;  // K-major A: row i (of op(A)) at a + i*lda_bytes
-  const uint8_t* b;  // K-major B: column j (of op(B)) at b + j*ldb_bytes
+  const uint8_t* a;  // A as stored: leading dimension lda_bytes
+  const uint8_t* b;  // B as stored: leading dimension ldb_bytes
   const void* c;
   void* d;
   const void* bias;
@@ -34,8 +34,8 @@ struct GemmArgs {
 };
 
 
-// Launches one K-major kernel variant on `stream`; returns the launch status.
-template <int F, int BM, int BN, int WM, int WN, int LOADW, int STAGES, int OCC, int SCW>
-hipError_t launch_kmajor(const GemmArgs& a, dim3 grid, hipStream_t stream);
+// Launches one kernel variant on `stream`; returns the launch status.
+template <int F, int BM, int BN, int WM, int WN, int LOADW, int STAGES, int OCC, int SCW, bool AK, bool BK>
+hipError_t launch_gemm(const GemmArgs& a, dim3 grid, hipStream_t stream);
 
 }  // namespace thl

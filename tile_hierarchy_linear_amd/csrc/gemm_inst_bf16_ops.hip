@@ -1,0 +1,10 @@
+// Kernel instantiations for the bf16 operand family with an M-major A
+// and/or an N-major B (opA = N, opB = T).
+#include "gemm_launch.hpp"
+
+using thl::GemmArgs;
+using thl::FAM_BF16;
+
+THL_INSTANTIATE_OPS(FAM_BF16, false, true)
+THL_INSTANTIATE_OPS(FAM_BF16, true, false)
+THL_INSTANTIATE_OPS(FAM_BF16, false, false)

@@ -1,8 +1,8 @@
-// Kernel instantiations for the e4m3 operand family (one unit per family
-// so the library builds in parallel).
+// Kernel instantiations for the e4m3 operand family, K-major operands
+// (one unit per family so the library builds in parallel).
 #include "gemm_launch.hpp"
 
 using thl::GemmArgs;
 using thl::FAM_FP8;
 
-THL_INSTANTIATE_KMAJOR(FAM_FP8, 4)
+THL_INSTANTIATE_TN(FAM_FP8)

@@ -1,8 +1,8 @@
-// Kernel instantiations for the f16 operand family (one unit per family
-// so the library builds in parallel).
+// Kernel instantiations for the f16 operand family, K-major operands
+// (one unit per family so the library builds in parallel).
 #include "gemm_launch.hpp"
 
 using thl::GemmArgs;
 using thl::FAM_F16;
 
-THL_INSTANTIATE_KMAJOR(FAM_F16, 4)
+THL_INSTANTIATE_TN(FAM_F16)

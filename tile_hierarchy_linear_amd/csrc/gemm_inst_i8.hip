@@ -1,8 +1,8 @@
-// Kernel instantiations for the i8 operand family (one unit per family
-// so the library builds in parallel).
+// Kernel instantiations for the i8 operand family, K-major operands
+// (one unit per family so the library builds in parallel).
 #include "gemm_launch.hpp"
 
 using thl::GemmArgs;
 using thl::FAM_I8;
 
-THL_INSTANTIATE_KMAJOR(FAM_I8, 4)
+THL_INSTANTIATE_TN(FAM_I8)

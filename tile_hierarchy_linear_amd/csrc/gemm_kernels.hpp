@@ -232,9 +232,15 @@ __device__ __forceinline__ void wait_vm() {
 // past the last full step re-read the last full step (uniform, in bounds)
 // so every step issues the same number of copies; a partial final K-step is
 // loaded and computed after the loop with bytes past K masked to zero.
-template <int F, int BM, int BN, int WM, int WN, int LOADW, int STAGES, int OCC, int SCW>
+//
+// Operand storage: AK (BK) true when op(A) rows (op(B) columns) are
+// contiguous along K (opA = T, opB = N), staged as rows of 64 bytes of K;
+// false when they are contiguous along M (N) -- 16-bit types only -- staged
+// as 32 k-rows of the tile's M (N) extent and turned into K-contiguous
+// fragments by two transposed 16-bit LDS reads each.
+template <int F, int BM, int BN, int WM, int WN, int LOADW, int STAGES, int OCC, int SCW, bool AK, bool BK>
 __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
-gemm_kmajor_kernel(GemmArgs p) {
+gemm_kernel(GemmArgs p) {
   using T = Fam<F>;
   using Acc = typename T::Acc;
   constexpr int KB = maps::kStepBytes;
@@ -267,6 +273,10 @@ gemm_kmajor_kernel(GemmArgs p) {
   // compile-time constants inside it.
   constexpr int UNROLL = (STAGES % 2 == 0) ? STAGES : 2 * STAGES;
   static_assert(KSUB == 2 || (KSUB == 1 && FM % 2 == 0), "a step splits into two halves");
+  static_assert((AK && BK) || F == FAM_BF16 || F == FAM_F16, "M/N-major operands are 16-bit only");
+  constexpr int PA = BM * 2, PB = BN * 2;  // k-row pitch of M- (N-) major stages
+  static_assert(AK || PA % 256 == 0, "M-major k-rows are whole 256-byte bank windows");
+  static_assert(BK || PB % 256 == 0, "N-major k-rows are whole 256-byte bank windows");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE];
 
@@ -279,24 +289,40 @@ gemm_kmajor_kernel(GemmArgs p) {
   const int nk = (p.kbytes + KB - 1) / KB;  // K-steps, the last one possibly partial
   const int nkf = p.kbytes / KB;            // full K-steps
 
-  // Per-tile operand bases (uniform) and per-lane 32-bit byte offsets of
-  // every copy this wave issues; rows past M (N) re-read the last valid row.
-  const uint8_t* a_tile = p.a + m0 * p.lda_bytes;
-  const uint8_t* b_tile = p.b + n0 * p.ldb_bytes;
+  // Per-tile operand bases (uniform), the per-step advance, and per-lane
+  // 32-bit byte offsets of every copy this wave issues.  K-major: rows past M
+  // (N) re-read the last valid row.  M-major: 16-byte chunks wholly past M
+  // (N) re-read the tile's first chunk of that k-row.
+  const uint8_t* a_tile = AK ? p.a + m0 * p.lda_bytes : p.a + m0 * 2;
+  const uint8_t* b_tile = BK ? p.b + n0 * p.ldb_bytes : p.b + n0 * 2;
+  const int64_t a_step = AK ? KB : 32 * p.lda_bytes;
+  const int64_t b_step = BK ? KB : 32 * p.ldb_bytes;
   uint32_t a_off[A_LOADS], b_off[B_LOADS];
 #pragma unroll
   for (int j = 0; j < A_LOADS; ++j) {
     int64_t row, byte;
-    maps::copy_source((j * NW + wave) * 64 * LOADW, lane, LOADW, &row, &byte);
-    const int64_t r = (m0 + row < p.m ? m0 + row : p.m - 1) - m0;
-    a_off[j] = static_cast<uint32_t>(r * p.lda_bytes + byte);
+    if constexpr (AK) {
+      maps::copy_source((j * NW + wave) * 64 * LOADW, lane, LOADW, &row, &byte);
+      const int64_t r = (m0 + row < p.m ? m0 + row : p.m - 1) - m0;
+      a_off[j] = static_cast<uint32_t>(r * p.lda_bytes + byte);
+    } else {
+      maps::mm_copy_source((j * NW + wave) * 64 * LOADW, lane, LOADW, PA, &row, &byte);
+      if (m0 + (byte & ~15) / 2 >= p.m) byte &= 15;
+      a_off[j] = static_cast<uint32_t>(row * p.lda_bytes + byte);
+    }
   }
 #pragma unroll
   for (int j = 0; j < B_LOADS; ++j) {
     int64_t row, byte;
-    maps::copy_source((j * NW + wave) * 64 * LOADW, lane, LOADW, &row, &byte);
-    const int64_t r = (n0 + row < p.n ? n0 + row : p.n - 1) - n0;
-    b_off[j] = static_cast<uint32_t>(r * p.ldb_bytes + byte);
+    if constexpr (BK) {
+      maps::copy_source((j * NW + wave) * 64 * LOADW, lane, LOADW, &row, &byte);
+      const int64_t r = (n0 + row < p.n ? n0 + row : p.n - 1) - n0;
+      b_off[j] = static_cast<uint32_t>(r * p.ldb_bytes + byte);
+    } else {
+      maps::mm_copy_source((j * NW + wave) * 64 * LOADW, lane, LOADW, PB, &row, &byte);
+      if (n0 + (byte & ~15) / 2 >= p.n) byte &= 15;
+      b_off[j] = static_cast<uint32_t>(row * p.ldb_bytes + byte);
+    }
   }
 
   // fp4 scale copies: per lane, the source row base of each copy it issues.
@@ -336,18 +362,18 @@ gemm_kmajor_kernel(GemmArgs p) {
     constexpr int BUF = decltype(buf_tag)::value;
     uint8_t* sa = smem + BUF * STAGE;
     uint8_t* sb = sa + A_BYTES;
-    const int64_t kofs = static_cast<int64_t>(kt) * KB;
     issue_scales(kt, sa);
-    const uint8_t* ak = a_tile + kofs;
-    const uint8_t* bk = b_tile + kofs;
+    const uint8_t* ak = a_tile + kt * a_step;
+    const uint8_t* bk = b_tile + kt * b_step;
 #pragma unroll
     for (int j = 0; j < A_LOADS; ++j) load_lds<LOADW>(ak + a_off[j], sa + (j * NW + wave) * 64 * LOADW);
 #pragma unroll
     for (int j = 0; j < B_LOADS; ++j) load_lds<LOADW>(bk + b_off[j], sb + (j * NW + wave) * 64 * LOADW);
   };
 
-  // The partial last K-step into slot 0: bytes at or past K read from the
-  // row's first byte instead (masked before the MFMAs).
+  // The partial last K-step into slot 0: K-major bytes at or past K read the
+  // row's first byte instead, M-major k-rows at or past K read the step's
+  // first k-row (masked before the MFMAs).
   auto issue_partial = [&](int kt) {
     uint8_t* sa = smem;
     uint8_t* sb = sa + A_BYTES;
@@ -356,15 +382,29 @@ gemm_kmajor_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < A_LOADS; ++j) {
       int64_t row, byte;
-      maps::copy_source((j * NW + wave) * 64 * LOADW, lane, LOADW, &row, &byte);
-      const uint8_t* src = a_tile + a_off[j] + (kofs + byte < p.kbytes ? kofs : -byte);
+      const uint8_t* src;
+      if constexpr (AK) {
+        maps::copy_source((j * NW + wave) * 64 * LOADW, lane, LOADW, &row, &byte);
+        src = a_tile + a_off[j] + (kofs + byte < p.kbytes ? kofs : -byte);
+      } else {
+        maps::mm_copy_source((j * NW + wave) * 64 * LOADW, lane, LOADW, PA, &row, &byte);
+        const int64_t k = 32 * static_cast<int64_t>(kt) + row;
+        src = a_tile + kt * a_step + a_off[j] - (k < p.k ? 0 : row * p.lda_bytes);
+      }
       load_lds<LOADW>(src, sa + (j * NW + wave) * 64 * LOADW);
     }
 #pragma unroll
     for (int j = 0; j < B_LOADS; ++j) {
       int64_t row, byte;
-      maps::copy_source((j * NW + wave) * 64 * LOADW, lane, LOADW, &row, &byte);
-      const uint8_t* src = b_tile + b_off[j] + (kofs + byte < p.kbytes ? kofs : -byte);
+      const uint8_t* src;
+      if constexpr (BK) {
+        maps::copy_source((j * NW + wave) * 64 * LOADW, lane, LOADW, &row, &byte);
+        src = b_tile + b_off[j] + (kofs + byte < p.kbytes ? kofs : -byte);
+      } else {
+        maps::mm_copy_source((j * NW + wave) * 64 * LOADW, lane, LOADW, PB, &row, &byte);
+        const int64_t k = 32 * static_cast<int64_t>(kt) + row;
+        src = b_tile + kt * b_step + b_off[j] - (k < p.k ? 0 : row * p.ldb_bytes);
+      }
       load_lds<LOADW>(src, sb + (j * NW + wave) * 64 * LOADW);
     }
   };
@@ -389,22 +429,74 @@ gemm_kmajor_kernel(GemmArgs p) {
 
   v4i af[2][FM][LC], bf[2][FN][LC];  // fragment slots: (kt*KSUB + ks) & 1
 
+  // M/N-major fragments: lane addresses for the two transposed reads of
+  // sub-step ks (k within the step and the row within a 32-row fragment).
+  int tr_k[KSUB][2], tr_m[2];
+#pragma unroll
+  for (int ks = 0; ks < KSUB; ++ks)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      int64_t k, m;
+      maps::tr16_operand(lane, h, &k, &m);
+      tr_k[ks][h] = static_cast<int>(k) + ks * 16;
+      tr_m[h] = static_cast<int>(m);
+    }
+
+  // Read one M-major 16-bit fragment (rows r0 .. r0+31 of the stage's
+  // operand, k-range of sub-step KS) and zero the values at or past k = kv.
+  auto read_mm = [&](const uint8_t* base, int pitch, int r0, auto ks_tag, int kv) -> v4i {
+    constexpr int KS = decltype(ks_tag)::value;
+    v2i half[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = tr_k[KS][h];
+      const int off = static_cast<int>(maps::mm_lds_offset(k, 2 * (r0 + tr_m[h]), pitch));
+      typedef short v4s __attribute__((ext_vector_type(4)));
+      const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s*)(base + off));
+      v2i w = __builtin_bit_cast(v2i, r);
+      if (kv < 32) {
+        // after the transpose, value v of this lane is k = kr + v
+        const int kr = KS * 16 + 8 * (lane >> 5) + 4 * h;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          unsigned x = static_cast<unsigned>(w[q]);
+          if (kr + 2 * q >= kv) x &= 0xffff0000u;
+          if (kr + 2 * q + 1 >= kv) x &= 0x0000ffffu;
+          w[q] = static_cast<int>(x);
+        }
+      }
+      half[h] = w;
+    }
+    return __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3);
+  };
+
   auto read = [&](const uint8_t* stage, auto ks_tag, auto slot_tag, int kvalid) {
     constexpr int KS = decltype(ks_tag)::value, SL = decltype(slot_tag)::value;
 #pragma unroll
-    for (int f = 0; f < FM; ++f)
+    for (int f = 0; f < FM; ++f) {
+      if constexpr (AK) {
 #pragma unroll
-      for (int c = 0; c < LC; ++c) {
-        af[SL][f][c] = *reinterpret_cast<const v4i*>(stage + a_wave_off + f * 32 * KB + chunk_off[KS][c]);
-        if (kvalid < KB) af[SL][f][c] = mask_bytes(af[SL][f][c], kvalid - (KS * CPM + (lane >> 5) * LC + c) * 16);
+        for (int c = 0; c < LC; ++c) {
+          af[SL][f][c] = *reinterpret_cast<const v4i*>(stage + a_wave_off + f * 32 * KB + chunk_off[KS][c]);
+          if (kvalid < KB) af[SL][f][c] = mask_bytes(af[SL][f][c], kvalid - (KS * CPM + (lane >> 5) * LC + c) * 16);
+        }
+      } else {
+        af[SL][f][0] = read_mm(stage, PA, wm * TM + f * 32, ks_tag, kvalid / 2);
       }
+    }
 #pragma unroll
-    for (int f = 0; f < FN; ++f)
+    for (int f = 0; f < FN; ++f) {
+      if constexpr (BK) {
 #pragma unroll
-      for (int c = 0; c < LC; ++c) {
-        bf[SL][f][c] = *reinterpret_cast<const v4i*>(stage + b_wave_off + f * 32 * KB + chunk_off[KS][c]);
-        if (kvalid < KB) bf[SL][f][c] = mask_bytes(bf[SL][f][c], kvalid - (KS * CPM + (lane >> 5) * LC + c) * 16);
+        for (int c = 0; c < LC; ++c) {
+          bf[SL][f][c] = *reinterpret_cast<const v4i*>(stage + b_wave_off + f * 32 * KB + chunk_off[KS][c]);
+          if (kvalid < KB) bf[SL][f][c] = mask_bytes(bf[SL][f][c], kvalid - (KS * CPM + (lane >> 5) * LC + c) * 16);
+        }
+      } else {
+        bf[SL][f][0] = read_mm(stage + A_BYTES, PB, wn * TN + f * 32, ks_tag, kvalid / 2);
       }
+    }
   };
 
   // MFMAs of sub-step KS on rows [I0, I1) of the wave tile from slot SL.

@@ -105,6 +105,35 @@ THL_HD int64_t fp8_32x32_k_of(int64_t lane, int64_t j) {
   return j < 16 ? 16 * (lane >> 5) + j : 32 + 16 * (lane >> 5) + (j - 16);
 }
 
+// ------------------------------------------------------------ M-major operands
+// An operand whose storage is contiguous along M (or N) -- opA = N, opB = T --
+// is staged as k-rows: row k holds the tile's `pitch`/2 consecutive 16-bit
+// elements of that k.  Its 32-byte blocks are XOR-swizzled by k % 8, so the
+// 4 k-rows a transposed read touches land in 4 different 32-byte blocks
+// (distinct banks in a 128- or 256-byte window).  pitch is a multiple of 256.
+THL_HD int64_t mm_lds_offset(int64_t k, int64_t b, int64_t pitch) {
+  return k * pitch + ((((b >> 5) ^ (k & 7))) << 5) + (b & 31);
+}
+
+// Inverse for the direct copies: the (k-row, byte within the row) that lane
+// `lane` of the copy instruction starting at LDS byte `base` fetches.
+THL_HD void mm_copy_source(int64_t base, int64_t lane, int64_t loadw, int64_t pitch, int64_t* k,
+                           int64_t* byte_in_row) {
+  const int64_t off = base + lane * loadw;
+  const int64_t r = off / pitch;
+  const int64_t pb = off % pitch;
+  *k = r;
+  *byte_in_row = ((((pb >> 5) ^ (r & 7))) << 5) | (pb & 31);
+}
+
+// The 8-byte chunk lane `lane` addresses for transposed read h (h = 0, 1) of a
+// 32x32x16 16-bit MFMA operand: 4 consecutive rows m at one k, chosen so that
+// after the transpose lane l holds row l % 32, k = 8*(l/32) + 4h + (0..3).
+THL_HD void tr16_operand(int64_t lane, int64_t h, int64_t* k, int64_t* m) {
+  *k = 8 * (lane >> 5) + 4 * h + ((lane & 15) >> 2);
+  *m = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+}
+
 // Transposed 16-bit LDS read (ds_read_b64_tr_b16): inside each group of 16
 // lanes, lane i receives element i % 4 of the 8-byte chunk that lane
 // 4*v + i/4 of its group addressed, as its value v (v = 0..3).  Returned:
