@@ -2,8 +2,9 @@
 
 A step is one pass of the hot path: one thl_gemm call (validation, dispatch,
 the tiled MFMA kernel with its fused epilogue) over inputs already resident
-in HBM.  The headline workload is the bf16 GEMM at M = N = K = 8192 with the
-relu(A.B + C + bias[m]) epilogue (bf16 out, fp32 accumulate); the fp8 (e4m3,
+in HBM.  The headline workload is the bf16 GEMM at M = N = K = 8192, all
+operands column-major (op N/N), with the relu(A.B + C + bias[m]) epilogue
+(bf16 out, fp32 accumulate); the fp8 (e4m3,
 per-tensor scales) and MXFP4 (e2m1 with E8M0 block scales, D = A.B + C)
 GEMMs at 8192^3 are timed the same way and reported in the same line.
 
@@ -12,6 +13,7 @@ Prints ONE JSON line on stdout (diagnostics go to stderr).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -23,6 +25,10 @@ sys.path.insert(0, ROOT)
 # MI355X published dense peaks (TFLOP/s, TOP/s for int8) and HBM bandwidth.
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2, "e2m1": 10066.3, "i8": 5033.2}
 HBM_PEAK_GBS = 8000.0
+
+CSRC = os.path.join(ROOT, "tile_hierarchy_linear_amd", "csrc")
+# Summary of the FETCH_SIZE / WRITE_SIZE counter runs over this script.
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_8192_hbm_traffic.md")
 
 
 def log(*a):
@@ -48,6 +54,35 @@ def compulsory_bytes(w):
     if w.sfa is not None:
         total += (w.m + w.n) * (w.k // 32)
     return total
+
+
+def kernel_source_hash():
+    """Hash of every source the GEMM kernels and their launch are built from."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.startswith("gemm") or name == "index_maps.hpp":
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(variant, m, n, k):
+    """HBM bytes per launch (read + written) of `variant` at this shape from the
+    committed counter summary, each counter scaled by what it read for a plain
+    copy of known size.  None when no summary covers it or the kernel sources
+    have changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            lines = [l.split()[1:] for l in f if l.startswith("traffic ")]
+    except OSError:
+        return None
+    here = kernel_source_hash()
+    for fields in lines:
+        kv = dict(x.split("=", 1) for x in fields)
+        if (kv.get("variant") == variant and kv.get("mnk") == f"{m}x{n}x{k}" and kv.get("sources") == here):
+            return int(kv["read_bytes"]) + int(kv["write_bytes"])
+    return None
 
 
 def time_gemm(dp, steps, warmup, stream):
@@ -163,7 +198,8 @@ def main():
         entry = {"tflops": round(tflops, 1), "frac_of_peak": round(tflops / PEAK_TFLOPS[key], 4),
                  "peak_tflops": PEAK_TFLOPS[key], "ms": round(ms, 4), "variant": variant,
                  "op": w.op_a + w.op_b, "epilogue": {"act": w.act, "beta": w.beta, "bias": w.bias is not None},
-                 "hbm_gbs_compulsory": round(byt / (ms * 1e-3) / 1e9, 1)}
+                 "hbm_gbs_compulsory": round(byt / (ms * 1e-3) / 1e9, 1), "algorithmic_bytes": byt,
+                 "traffic": measured_traffic(variant, w.m, w.n, w.k)}
         try:
             entry["parity_sampled"] = quick_parity(w, dp)
         except Exception as e:  # noqa: BLE001 -- reported, not fatal for timing
@@ -218,8 +254,9 @@ def main():
                                f"fp32 accumulate, {w.type_d} out", "m": w.m, "n": w.n, "k": w.k,
                    "kernel_variant": variant},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_TFLOPS[key], "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_TFLOPS[key], 4), "traffic": None,
-                     "algorithmic_bytes": byt},
+                     "frac": round(tflops / PEAK_TFLOPS[key], 4),
+                     "traffic": measured_traffic(variant, w.m, w.n, w.k),
+                     "algorithmic_bytes": byt, "kernel_sources": kernel_source_hash()},
         "dtypes": results,
         "cpu_baseline": cpu,
     }
