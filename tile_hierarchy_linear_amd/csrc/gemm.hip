@@ -4,8 +4,9 @@
 // Selection follows the page's rule for the library's host API: the first
 // built kernel whose data types, layouts and alignment fit the problem
 // ("Technical Documentation: NVIDIA/cutlass", "CUTLASS Library"), with one
-// shape rule on top: problems whose 256x256 tile count cannot fill the 256
-// compute units take the 128x128 variant.
+// shape rule on top: the largest tile whose tile count still fills the 256
+// compute units (256x256 tiles, one workgroup per CU; then 256x128, two per
+// CU; then 128x128) is tried first.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -27,38 +28,34 @@ struct Variant {
   int family;
   bool a_kmajor, b_kmajor;  // opA == T, opB == N
   int bm, bn, threads, loadw;
-  bool small;  // preferred when the large tile cannot fill the device
+  int tier;  // 0: 256x256, 1: 256x128, 2: 128x128 (the shape rule's preference order)
   LaunchFn launch;
 };
 
-#define THL_V(FAM, NAME, OPS, AK, BK, BM, BN, LOADW, ST, OCC, SMALL)                                       \
-  {NAME "_" OPS "_" #BM "x" #BN "_v" #LOADW "_s" #ST "_o" #OCC, FAM, AK, BK, BM, BN, 256, LOADW, SMALL,   \
+#define THL_V(FAM, NAME, OPS, AK, BK, BM, BN, LOADW, ST, OCC, TIER)                                       \
+  {NAME "_" OPS "_" #BM "x" #BN "_v" #LOADW "_s" #ST "_o" #OCC, FAM, AK, BK, BM, BN, 256, LOADW, TIER,   \
    &launch_gemm<FAM, BM, BN, 2, 2, LOADW, ST, OCC, 4, AK, BK>}
 
-// Must list exactly the instantiations of THL_INSTANTIATE_TN / _OPS.  Order
-// is the first-fit order: large tiles first, then the small-problem tiles.
-#define THL_TN_VARIANTS(FAM, NAME)                                  \
-  THL_V(FAM, NAME, "tn", true, true, 256, 128, 16, 3, 2, false),    \
-      THL_V(FAM, NAME, "tn", true, true, 256, 256, 16, 4, 1, false), \
-      THL_V(FAM, NAME, "tn", true, true, 128, 128, 16, 4, 2, true),  \
-      THL_V(FAM, NAME, "tn", true, true, 128, 128, 4, 4, 2, true)
-#define THL_OPS_VARIANTS(FAM, NAME, OPS, AK, BK)                 \
-  THL_V(FAM, NAME, OPS, AK, BK, 256, 128, 16, 3, 2, false),      \
-      THL_V(FAM, NAME, OPS, AK, BK, 128, 128, 16, 4, 2, true),   \
-      THL_V(FAM, NAME, OPS, AK, BK, 128, 128, 4, 4, 2, true)
+// Must list exactly the instantiations of THL_INSTANTIATE_VARIANTS.  Order is
+// the first-fit order within a tier: 16-byte copies before 4-byte ones.
+#define THL_VARIANTS(FAM, NAME, OPS, AK, BK)                  \
+  THL_V(FAM, NAME, OPS, AK, BK, 256, 256, 16, 4, 1, 0),       \
+      THL_V(FAM, NAME, OPS, AK, BK, 256, 128, 16, 3, 2, 1),   \
+      THL_V(FAM, NAME, OPS, AK, BK, 128, 128, 16, 4, 2, 2),   \
+      THL_V(FAM, NAME, OPS, AK, BK, 128, 128, 4, 4, 2, 2)
 
 const Variant kVariants[] = {
-    THL_TN_VARIANTS(FAM_BF16, "bf16"),
-    THL_OPS_VARIANTS(FAM_BF16, "bf16", "nn", false, true),
-    THL_OPS_VARIANTS(FAM_BF16, "bf16", "tt", true, false),
-    THL_OPS_VARIANTS(FAM_BF16, "bf16", "nt", false, false),
-    THL_TN_VARIANTS(FAM_F16, "f16"),
-    THL_OPS_VARIANTS(FAM_F16, "f16", "nn", false, true),
-    THL_OPS_VARIANTS(FAM_F16, "f16", "tt", true, false),
-    THL_OPS_VARIANTS(FAM_F16, "f16", "nt", false, false),
-    THL_TN_VARIANTS(FAM_I8, "i8"),
-    THL_TN_VARIANTS(FAM_FP8, "e4m3"),
-    THL_TN_VARIANTS(FAM_FP4, "e2m1"),
+    THL_VARIANTS(FAM_BF16, "bf16", "tn", true, true),
+    THL_VARIANTS(FAM_BF16, "bf16", "nn", false, true),
+    THL_VARIANTS(FAM_BF16, "bf16", "tt", true, false),
+    THL_VARIANTS(FAM_BF16, "bf16", "nt", false, false),
+    THL_VARIANTS(FAM_F16, "f16", "tn", true, true),
+    THL_VARIANTS(FAM_F16, "f16", "nn", false, true),
+    THL_VARIANTS(FAM_F16, "f16", "tt", true, false),
+    THL_VARIANTS(FAM_F16, "f16", "nt", false, false),
+    THL_VARIANTS(FAM_I8, "i8", "tn", true, true),
+    THL_VARIANTS(FAM_FP8, "e4m3", "tn", true, true),
+    THL_VARIANTS(FAM_FP4, "e2m1", "tn", true, true),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -223,15 +220,18 @@ thl_status thl_gemm(int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
     }
   }
 
-  // Copy offsets inside a 256-row tile are 32-bit.
-  if (k > 0 && (bytes_of(dt->a, lda) > (INT64_C(1) << 24) || bytes_of(dt->b, ldb) > (INT64_C(1) << 24)))
+  // Copy offsets inside a 256-row tile, and scale-row offsets, are 32-bit.
+  if (k > 0 && (bytes_of(dt->a, lda) > (INT64_C(1) << 23) || bytes_of(dt->b, ldb) > (INT64_C(1) << 23)))
+    return THL_ERR_UNSUPPORTED;
+  if (fam == FAM_FP4 && k > 0 && (m * s.ld_sfa > (INT64_C(1) << 31) || n * s.ld_sfb > (INT64_C(1) << 31)))
     return THL_ERR_UNSUPPORTED;
 
   // ---- variant: first fit on family, alignment and shape
   const int64_t lda_bytes = bytes_of(dt->a, lda), ldb_bytes = bytes_of(dt->b, ldb);
   const char* forced = std::getenv("THL_FORCE_VARIANT");
-  const int64_t big_tiles = ((m + 255) / 256) * ((n + 255) / 256);
-  const bool want_small = big_tiles < 256;
+  const int64_t tiles_256 = ((m + 255) / 256) * ((n + 255) / 256);
+  const int64_t tiles_256x128 = ((m + 255) / 256) * ((n + 127) / 128);
+  const int want_tier = tiles_256 >= 256 ? 0 : (tiles_256x128 >= 256 ? 1 : 2);
   const Variant* pick = nullptr;
   bool family_built = false;
   for (int pass = 0; pass < 2 && !pick; ++pass) {
@@ -240,8 +240,8 @@ thl_status thl_gemm(int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
       family_built = true;
       if (forced && *forced) {
         if (std::strcmp(forced, v.name) != 0) continue;
-      } else if (pass == 0 && v.small != want_small) {
-        continue;  // first pass: the variant the shape rule prefers
+      } else if (pass == 0 && v.tier != want_tier) {
+        continue;  // first pass: the tile the shape rule prefers
       }
       bool fits = k == 0 || (aligned(A, lda_bytes, v.loadw) && aligned(B, ldb_bytes, v.loadw));
       if (fam == FAM_FP4 && k > 0) fits = fits && aligned(s.sfa, s.ld_sfa, 4) && aligned(s.sfb, s.ld_sfb, 4);

@@ -5,4 +5,4 @@
 using thl::GemmArgs;
 using thl::FAM_BF16;
 
-THL_INSTANTIATE_TN(FAM_BF16)
+THL_INSTANTIATE_VARIANTS(FAM_BF16, true, true)

@@ -5,4 +5,4 @@
 using thl::GemmArgs;
 using thl::FAM_FP8;
 
-THL_INSTANTIATE_TN(FAM_FP8)
+THL_INSTANTIATE_VARIANTS(FAM_FP8, true, true)

@@ -5,4 +5,4 @@
 using thl::GemmArgs;
 using thl::FAM_F16;
 
-THL_INSTANTIATE_TN(FAM_F16)
+THL_INSTANTIATE_VARIANTS(FAM_F16, true, true)

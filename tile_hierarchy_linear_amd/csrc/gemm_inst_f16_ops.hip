@@ -5,6 +5,6 @@
 using thl::GemmArgs;
 using thl::FAM_F16;
 
-THL_INSTANTIATE_OPS(FAM_F16, false, true)
-THL_INSTANTIATE_OPS(FAM_F16, true, false)
-THL_INSTANTIATE_OPS(FAM_F16, false, false)
+THL_INSTANTIATE_VARIANTS(FAM_F16, false, true)
+THL_INSTANTIATE_VARIANTS(FAM_F16, true, false)
+THL_INSTANTIATE_VARIANTS(FAM_F16, false, false)

@@ -5,4 +5,4 @@
 using thl::GemmArgs;
 using thl::FAM_I8;
 
-THL_INSTANTIATE_TN(FAM_I8)
+THL_INSTANTIATE_VARIANTS(FAM_I8, true, true)

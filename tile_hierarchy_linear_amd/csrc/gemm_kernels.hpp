@@ -6,15 +6,19 @@
 // hierarchy"), built for CDNA4: a workgroup owns a BM x BN tile of D; its
 // WM x WN wavefronts (64 lanes each) own (BM/WM) x (BN/WN) sub-tiles, each a
 // grid of 32x32 MFMA tiles accumulated in registers.  K advances in steps of
-// 128 bytes per operand row (64 fp16/bf16, 128 int8/fp8, 256 fp4 elements),
+// 64 bytes per operand row (32 fp16/bf16, 64 int8/fp8, 128 fp4 elements),
 // so every operand format issues the same number of MFMA cycles per step.
 //
-// Global -> LDS (a3): direct-to-LDS loads (global_load_lds, 16 or 4 bytes a
-// lane) into two swizzled stages; while stage s is consumed by the MFMAs,
-// stage s+1 is in flight.  LDS -> registers (a4): each lane reads its 16-byte
-// fragments from the swizzled rows.  Epilogue (a7): alpha/beta, bias,
-// activation and conversion run on the accumulator registers, with C read
-// and D written once.
+// Global -> LDS (a3): buffer loads that write LDS directly (16 or 4 bytes a
+// lane, no register staging) into a ring of STAGES swizzled buffers, each a
+// separate LDS object so the compiler can tell a copy into one buffer from a
+// read of another; copies run STAGES-1 steps ahead of the MFMAs, and their
+// completion is waited for explicitly (vmcnt) before one workgroup barrier
+// per step.  LDS -> registers (a4): each lane reads its MFMA fragments from
+// the swizzled rows, half a step ahead of their use.  Epilogue (a7): the
+// accumulators leave through LDS so that alpha/beta, bias, activation and
+// conversion run on contiguous 8-row runs of D, with C read and D written
+// once in whole cache lines.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -191,15 +195,109 @@ __device__ __forceinline__ void store4_f(void* d, int type, int64_t off, const f
   }
 }
 
-// Direct global -> LDS load of W bytes per lane (W a literal the builtin accepts).
+// Rows m .. m+rows-1 (rows <= 8) of one column of a float-family matrix, as
+// floats; one or two 16-byte loads when all 8 are wanted and aligned.
+__device__ __forceinline__ void load8_f(const void* base, int type, int64_t off, int rows, float (&v)[8]) {
+  if (type == DT_F32) {
+    const float* q = static_cast<const float*>(base) + off;
+    if (rows == 8 && (reinterpret_cast<uintptr_t>(q) & 15) == 0) {
+      const v4f a = *reinterpret_cast<const v4f*>(q), b = *reinterpret_cast<const v4f*>(q + 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        v[r] = a[r];
+        v[4 + r] = b[r];
+      }
+      return;
+    }
+  } else {
+    const uint16_t* q = static_cast<const uint16_t*>(base) + off;
+    if (rows == 8 && (reinterpret_cast<uintptr_t>(q) & 15) == 0) {
+      const v4i w = *reinterpret_cast<const v4i*>(q);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const uint16_t h = static_cast<uint16_t>(static_cast<unsigned>(w[r / 2]) >> (16 * (r & 1)));
+        v[r] = type == DT_BF16 ? __builtin_bit_cast(float, static_cast<unsigned>(h) << 16)
+                               : static_cast<float>(__builtin_bit_cast(_Float16, h));
+      }
+      return;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 8; ++r) v[r] = r < rows ? load_f(base, type, off + r) : 0.0f;
+}
+
+// Store rows m .. m+rows-1 (rows <= 8) of one column, rounding to nearest
+// even; one or two 16-byte stores when all 8 go out and are aligned.
+__device__ __forceinline__ void store8_f(void* base, int type, int64_t off, const float (&v)[8], int rows) {
+  if (type == DT_F32) {
+    float* q = static_cast<float*>(base) + off;
+    if (rows == 8 && (reinterpret_cast<uintptr_t>(q) & 15) == 0) {
+      *reinterpret_cast<v4f*>(q) = v4f{v[0], v[1], v[2], v[3]};
+      *reinterpret_cast<v4f*>(q + 4) = v4f{v[4], v[5], v[6], v[7]};
+      return;
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+      if (r < rows) q[r] = v[r];
+  } else {
+    uint16_t h[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+      h[r] = type == DT_BF16 ? __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[r]))
+                             : __builtin_bit_cast(uint16_t, static_cast<_Float16>(v[r]));
+    uint16_t* q = static_cast<uint16_t*>(base) + off;
+    if (rows == 8 && (reinterpret_cast<uintptr_t>(q) & 15) == 0) {
+      *reinterpret_cast<v4i*>(q) = __builtin_bit_cast(v4i, h);
+      return;
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+      if (r < rows) q[r] = h[r];
+  }
+}
+
+__device__ __forceinline__ void load8_i(const void* base, int64_t off, int rows, int (&v)[8]) {
+  const int* q = static_cast<const int*>(base) + off;
+  if (rows == 8 && (reinterpret_cast<uintptr_t>(q) & 15) == 0) {
+    const v4i a = *reinterpret_cast<const v4i*>(q), b = *reinterpret_cast<const v4i*>(q + 4);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      v[r] = a[r];
+      v[4 + r] = b[r];
+    }
+    return;
+  }
+#pragma unroll
+  for (int r = 0; r < 8; ++r) v[r] = r < rows ? q[r] : 0;
+}
+
+__device__ __forceinline__ void store8_i(void* base, int64_t off, const int (&v)[8], int rows) {
+  int* q = static_cast<int*>(base) + off;
+  if (rows == 8 && (reinterpret_cast<uintptr_t>(q) & 15) == 0) {
+    *reinterpret_cast<v4i*>(q) = v4i{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<v4i*>(q + 4) = v4i{v[4], v[5], v[6], v[7]};
+    return;
+  }
+#pragma unroll
+  for (int r = 0; r < 8; ++r)
+    if (r < rows) q[r] = v[r];
+}
+
+// Buffer resource over `base` with no range limit (offsets are kept in
+// bounds by the callers); raw dword data, the gfx9 default format word.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), -1, 0x00020000);
+}
+
+// Direct buffer -> LDS load of W bytes per lane at base + voffset.
 template <int W>
-__device__ __forceinline__ void load_lds(const void* src, void* lds) {
+__device__ __forceinline__ void load_lds_buf(__amdgpu_buffer_rsrc_t r, uint32_t voffset, void* lds) {
   auto* l = (__attribute__((address_space(3))) void*)(lds);
   if constexpr (W == 16) {
-    __builtin_amdgcn_global_load_lds(src, l, 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, voffset, 0, 0, 0);
   } else {
     static_assert(W == 4, "16- or 4-byte lanes");
-    __builtin_amdgcn_global_load_lds(src, l, 4, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 4, voffset, 0, 0, 0);
   }
 }
 
@@ -212,26 +310,47 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Workgroup barrier without the memory fence __syncthreads() adds (that
+// fence waits for every outstanding vector-memory operation, including the
+// copies of later stages).  The empty asm statements keep the compiler from
+// moving LDS accesses across it; data waits are explicit.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One LDS buffer of the staging ring per (size, index): separate objects, so
+// the compiler can tell a copy into one slot from a read of another and does
+// not make the read wait for the copy.
+template <int BYTES, int I>
+__device__ __forceinline__ uint8_t* ring_slot() {
+  __shared__ __attribute__((aligned(1024))) uint8_t slot[BYTES];
+  return slot;
+}
+
+
 // ------------------------------------------------------------ the kernel
 //
 // Pipeline (per wavefront, K-steps of 64 bytes per operand row, a ring of
-// STAGES = 4 LDS buffers, copies always issued STAGES-1 steps ahead):
+// STAGES LDS buffers, copies always issued STAGES-1 steps ahead):
 //
 //   step kt, phase A:  first half of step kt's MFMAs; LDS reads of the
 //                      fragments for the second half (from buffer kt).
 //   barrier:           after this wave's copies of stage kt+1 have landed
-//                      (only stage kt+2's may still be in flight); past it,
-//                      stage kt+1 is visible and every wave has finished
+//                      (those of later stages may still be in flight); past
+//                      it, stage kt+1 is visible and every wave has finished
 //                      step kt-1, so buffer kt-1 is free.
-//   step kt, phase B:  second half of step kt's MFMAs; LDS reads of step
-//                      kt+1's first fragments; copies of stage kt+3 into
-//                      the freed buffer.
+//   step kt, phase B:  second half of step kt's MFMAs; copies of stage
+//                      kt+STAGES-1 into the freed buffer; LDS reads of step
+//                      kt+1's first fragments (and fp4 scales).
 //
-// One barrier per step, placed so that the LDS latency of the next step's
-// first fragments hides behind the current step's last MFMAs.  The copies
-// past the last full step re-read the last full step (uniform, in bounds)
-// so every step issues the same number of copies; a partial final K-step is
-// loaded and computed after the loop with bytes past K masked to zero.
+// Each phase is a scheduling region of its own (nothing crosses the
+// barrier), inside which the reads are spread over the MFMAs and finish two
+// MFMAs before the phase ends.  The copies past the last full step re-read
+// the last full step (uniform, in bounds) so every step issues the same
+// number of copies; a partial final K-step is loaded and computed after the
+// loop with bytes past K masked to zero.
 //
 // Operand storage: AK (BK) true when op(A) rows (op(B) columns) are
 // contiguous along K (opA = T, opB = N), staged as rows of 64 bytes of K;
@@ -267,7 +386,7 @@ gemm_kernel(GemmArgs p) {
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole MFMA tiles");
   static_assert(A_LOADS * 64 * LOADW * NW == A_BYTES && B_LOADS * 64 * LOADW * NW == B_BYTES,
                 "copies must split evenly over waves");
-  static_assert(STAGES >= 3 && STAGES <= 5, "three to five stages");
+  static_assert(STAGES >= 3 && STAGES <= 6, "three to six stages");
   static_assert(VM_STAGE * (STAGES - 2) < 64, "vmcnt range");
   // Steps per unrolled loop body: ring slots and fragment-slot parities are
   // compile-time constants inside it.
@@ -278,7 +397,7 @@ gemm_kernel(GemmArgs p) {
   static_assert(AK || PA % 256 == 0, "M-major k-rows are whole 256-byte bank windows");
   static_assert(BK || PB % 256 == 0, "N-major k-rows are whole 256-byte bank windows");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE];
+  auto slot = [](auto i_tag) -> uint8_t* { return ring_slot<STAGE, decltype(i_tag)::value>(); };
 
   const int lane = static_cast<int>(threadIdx.x) & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
@@ -327,8 +446,10 @@ gemm_kernel(GemmArgs p) {
 
   // fp4 scale copies: per lane, the source row base of each copy it issues.
   const int nkb = p.k >> 5;
-  const uint8_t* sc_src[T::SCALED ? SC_LOADS : 1];
+  uint32_t sc_src[T::SCALED ? SC_LOADS : 1];
+  bool sc_a[T::SCALED ? SC_LOADS : 1];
   int sc_dst[T::SCALED ? SC_LOADS : 1];
+  const __amdgpu_buffer_rsrc_t rs_sfa = make_rsrc(p.sfa), rs_sfb = make_rsrc(p.sfb);
   if constexpr (T::SCALED) {
 #pragma unroll
     for (int t = 0; t < SC_LOADS; ++t) {
@@ -336,10 +457,12 @@ gemm_kernel(GemmArgs p) {
       const int row_all = j < SC_INSTR ? j * 64 + lane : 0;
       if (row_all < BM) {
         const int64_t r = m0 + row_all < p.m ? m0 + row_all : p.m - 1;
-        sc_src[t] = p.sfa + r * p.ld_sfa;
+        sc_src[t] = static_cast<uint32_t>(r * p.ld_sfa);
+        sc_a[t] = true;
       } else {
         const int64_t r = n0 + (row_all - BM) < p.n ? n0 + (row_all - BM) : p.n - 1;
-        sc_src[t] = p.sfb + r * p.ld_sfb;
+        sc_src[t] = static_cast<uint32_t>(r * p.ld_sfb);
+        sc_a[t] = false;
       }
       sc_dst[t] = A_BYTES + B_BYTES + (j < SC_INSTR ? j * 64 * SCW : SC_BYTES);
     }
@@ -352,7 +475,7 @@ gemm_kernel(GemmArgs p) {
 #pragma unroll
       for (int t = 0; t < SC_LOADS; ++t) {
         const int o = 4 * kt;
-        load_lds<SCW>(sc_src[t] + (o < nkb ? o : 0), stage + sc_dst[t]);
+        load_lds_buf<SCW>(sc_a[t] ? rs_sfa : rs_sfb, sc_src[t] + (o < nkb ? o : 0), stage + sc_dst[t]);
       }
     }
   };
@@ -360,52 +483,52 @@ gemm_kernel(GemmArgs p) {
   // Copies of one full K-step into ring slot BUF: uniform base + 32-bit offset.
   auto issue_full = [&](int kt, auto buf_tag) {
     constexpr int BUF = decltype(buf_tag)::value;
-    uint8_t* sa = smem + BUF * STAGE;
+    uint8_t* sa = slot(std::integral_constant<int, BUF>{});
     uint8_t* sb = sa + A_BYTES;
     issue_scales(kt, sa);
-    const uint8_t* ak = a_tile + kt * a_step;
-    const uint8_t* bk = b_tile + kt * b_step;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_tile + kt * a_step), rb = make_rsrc(b_tile + kt * b_step);
 #pragma unroll
-    for (int j = 0; j < A_LOADS; ++j) load_lds<LOADW>(ak + a_off[j], sa + (j * NW + wave) * 64 * LOADW);
+    for (int j = 0; j < A_LOADS; ++j) load_lds_buf<LOADW>(ra, a_off[j], sa + (j * NW + wave) * 64 * LOADW);
 #pragma unroll
-    for (int j = 0; j < B_LOADS; ++j) load_lds<LOADW>(bk + b_off[j], sb + (j * NW + wave) * 64 * LOADW);
+    for (int j = 0; j < B_LOADS; ++j) load_lds_buf<LOADW>(rb, b_off[j], sb + (j * NW + wave) * 64 * LOADW);
   };
 
   // The partial last K-step into slot 0: K-major bytes at or past K read the
   // row's first byte instead, M-major k-rows at or past K read the step's
   // first k-row (masked before the MFMAs).
   auto issue_partial = [&](int kt) {
-    uint8_t* sa = smem;
+    uint8_t* sa = slot(std::integral_constant<int, 0>{});
     uint8_t* sb = sa + A_BYTES;
     const int64_t kofs = static_cast<int64_t>(kt) * KB;
     issue_scales(kt, sa);
+    // K-major: offsets from the tile base; M-major: from the step's first k-row.
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(AK ? a_tile : a_tile + kt * a_step);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(BK ? b_tile : b_tile + kt * b_step);
 #pragma unroll
     for (int j = 0; j < A_LOADS; ++j) {
-      int64_t row, byte;
-      const uint8_t* src;
+      int64_t row, byte, off;
       if constexpr (AK) {
         maps::copy_source((j * NW + wave) * 64 * LOADW, lane, LOADW, &row, &byte);
-        src = a_tile + a_off[j] + (kofs + byte < p.kbytes ? kofs : -byte);
+        off = a_off[j] + (kofs + byte < p.kbytes ? kofs : -byte);
       } else {
         maps::mm_copy_source((j * NW + wave) * 64 * LOADW, lane, LOADW, PA, &row, &byte);
         const int64_t k = 32 * static_cast<int64_t>(kt) + row;
-        src = a_tile + kt * a_step + a_off[j] - (k < p.k ? 0 : row * p.lda_bytes);
+        off = a_off[j] - (k < p.k ? 0 : row * p.lda_bytes);
       }
-      load_lds<LOADW>(src, sa + (j * NW + wave) * 64 * LOADW);
+      load_lds_buf<LOADW>(ra, static_cast<uint32_t>(off), sa + (j * NW + wave) * 64 * LOADW);
     }
 #pragma unroll
     for (int j = 0; j < B_LOADS; ++j) {
-      int64_t row, byte;
-      const uint8_t* src;
+      int64_t row, byte, off;
       if constexpr (BK) {
         maps::copy_source((j * NW + wave) * 64 * LOADW, lane, LOADW, &row, &byte);
-        src = b_tile + b_off[j] + (kofs + byte < p.kbytes ? kofs : -byte);
+        off = b_off[j] + (kofs + byte < p.kbytes ? kofs : -byte);
       } else {
         maps::mm_copy_source((j * NW + wave) * 64 * LOADW, lane, LOADW, PB, &row, &byte);
         const int64_t k = 32 * static_cast<int64_t>(kt) + row;
-        src = b_tile + kt * b_step + b_off[j] - (k < p.k ? 0 : row * p.ldb_bytes);
+        off = b_off[j] - (k < p.k ? 0 : row * p.ldb_bytes);
       }
-      load_lds<LOADW>(src, sb + (j * NW + wave) * 64 * LOADW);
+      load_lds_buf<LOADW>(rb, static_cast<uint32_t>(off), sb + (j * NW + wave) * 64 * LOADW);
     }
   };
 
@@ -543,63 +666,85 @@ gemm_kernel(GemmArgs p) {
   using IFM = std::integral_constant<int, FM>;
   using IH = std::integral_constant<int, FM / 2>;
 
+  // Interleave NM MFMAs with NR LDS reads and NV copies in one scheduling
+  // region (issued in that order of preference, reads and copies spread
+  // evenly over the MFMAs).
+  auto interleave = [](auto nm_tag, auto nr_tag, auto nv_tag) {
+    constexpr int NM = decltype(nm_tag)::value, NR = decltype(nr_tag)::value, NV = decltype(nv_tag)::value;
+    // reads go out over the first NM - 2 MFMAs (two MFMAs of slack before
+    // the next phase needs them); copies over all of them
+    constexpr int RM = NM > 2 ? NM - 2 : NM;
+    static_for<NM>([&](auto t) {
+      constexpr int T_ = decltype(t)::value;
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      constexpr int r = T_ < RM ? ((T_ + 1) * NR) / RM - (T_ * NR) / RM : 0;
+      if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
+      constexpr int v = ((T_ + 1) * NV) / NM - (T_ * NV) / NM;
+      if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x020, v, 0);
+    });
+  };
+
   if (nkf > 0) {
-    // Prologue: stages 0 .. STAGES-2, then step 0's first fragments.
+    // Prologue: stages 0 .. STAGES-2, then step 0's first fragments and scales.
     static_for<STAGES - 1>([&](auto sc) {
       constexpr int S = decltype(sc)::value;
       issue_full(S < nkf ? S : nkf - 1, std::integral_constant<int, S>{});
     });
     wait_vm<(STAGES - 2) * VM_STAGE>();
-    __syncthreads();
-    read(smem, I0{}, I0{}, KB);
+    wg_barrier();
+    int scl[2][NSC];
+    scales_of(slot(I0{}), scl[0], false);
+    read(slot(I0{}), I0{}, I0{}, KB);
 
-    for (int kb = 0; kb < nkf; kb += UNROLL) {
-      static_for<UNROLL>([&](auto uc) {
-        constexpr int U = decltype(uc)::value;
-        constexpr int S = U % STAGES;  // ring slot of step kt
-        constexpr int NEXT = (S + 1) % STAGES, ISSUE = (S + STAGES - 1) % STAGES;
-        constexpr int PAR = U & 1;     // parity of kt (kb is even)
-        const int kt = kb + U;
-        if (kt < nkf) {
-          const uint8_t* cur = smem + S * STAGE;
-          int scl[NSC];
-          scales_of(cur, scl, false);
-          // ---- phase A
-          if constexpr (KSUB == 2) {
-            mma(I0{}, I0{}, I0{}, IFM{}, scl);
-            read(cur, I1{}, I1{}, KB);
-            static_for<FM * FN>([&](auto t) {
-              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-              if constexpr (decltype(t)::value % 2 == 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            });
-          } else {
-            mma(I0{}, std::integral_constant<int, PAR>{}, I0{}, IH{}, scl);
-          }
-          // ---- barrier: stage kt+1 visible, buffer kt-1 free
-          wait_vm<(STAGES - 3) * VM_STAGE>();
-          __syncthreads();
-          // ---- phase B
-          const int nxt = kt + STAGES - 1 < nkf ? kt + STAGES - 1 : nkf - 1;
-          issue_full(nxt, std::integral_constant<int, ISSUE>{});
-          if constexpr (KSUB == 2) {
-            mma(I1{}, I1{}, I0{}, IFM{}, scl);
-            read(smem + NEXT * STAGE, I0{}, I0{}, KB);
-          } else {
-            mma(I0{}, std::integral_constant<int, PAR>{}, IH{}, IFM{}, scl);
-            read(smem + NEXT * STAGE, I0{}, std::integral_constant<int, PAR ^ 1>{}, KB);
-          }
-          constexpr int NM = (KSUB == 2) ? FM * FN : FM * FN / 2;
-          constexpr int NR = (FM + FN) * LC;
-          static_for<NM>([&](auto t) {
-            constexpr int T_ = decltype(t)::value;
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if constexpr ((T_ * NR) / NM != ((T_ + 1) * NR) / NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            if constexpr ((T_ * VM_STAGE) / NM != ((T_ + 1) * VM_STAGE) / NM)
-              __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-          });
-        }
-      });
-    }
+    // One K-step; U is its position in the unrolled group, which fixes its
+    // ring slot and fragment-slot parity at compile time.
+    auto step = [&](auto uc, const int kt) {
+      constexpr int U = decltype(uc)::value;
+      constexpr int S = U % STAGES;  // ring slot of step kt
+      constexpr int NEXT = (S + 1) % STAGES, ISSUE = (S + STAGES - 1) % STAGES;
+      constexpr int PAR = U & 1;     // parity of kt (groups start at even kt)
+      const uint8_t* cur = slot(std::integral_constant<int, S>{});
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- phase A: first half of the MFMAs, reads for the second half
+      if constexpr (KSUB == 2) {
+        mma(I0{}, I0{}, I0{}, IFM{}, scl[PAR]);
+        read(cur, I1{}, I1{}, KB);
+        interleave(std::integral_constant<int, FM * FN>{}, std::integral_constant<int, (FM + FN) * LC>{}, I0{});
+      } else {
+        mma(I0{}, std::integral_constant<int, PAR>{}, I0{}, IH{}, scl[PAR]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- barrier: stage kt+1 visible, buffer kt-1 free
+      wait_vm<(STAGES - 3) * VM_STAGE>();
+      wg_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- phase B: second half, copies of stage kt+S-1, next step's first reads
+      const int nxt = kt + STAGES - 1 < nkf ? kt + STAGES - 1 : nkf - 1;
+      issue_full(nxt, std::integral_constant<int, ISSUE>{});
+      const uint8_t* nx = slot(std::integral_constant<int, NEXT>{});
+      if constexpr (KSUB == 2) {
+        mma(I1{}, I1{}, I0{}, IFM{}, scl[PAR]);
+        read(nx, I0{}, I0{}, KB);
+      } else {
+        mma(I0{}, std::integral_constant<int, PAR>{}, IH{}, IFM{}, scl[PAR]);
+        read(nx, I0{}, std::integral_constant<int, PAR ^ 1>{}, KB);
+      }
+      scales_of(nx, scl[PAR ^ 1], false);
+      constexpr int NM = (KSUB == 2) ? FM * FN : FM * FN / 2;
+      constexpr int NR = (FM + FN) * LC + (T::SCALED ? NSC : 0);
+      interleave(std::integral_constant<int, NM>{}, std::integral_constant<int, NR>{},
+                 std::integral_constant<int, VM_STAGE>{});
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Whole unrolled groups without per-step conditions (straight-line code
+    // between loop edges), then the remaining steps.
+    int kb = 0;
+    for (; kb + UNROLL <= nkf; kb += UNROLL)
+      static_for<UNROLL>([&](auto uc) { step(uc, kb + decltype(uc)::value); });
+    static_for<UNROLL - 1>([&](auto uc) {
+      if (kb + decltype(uc)::value < nkf) step(uc, kb + decltype(uc)::value);
+    });
   }
 
   // The partial last K-step, if any: load it alone, then compute masked.
@@ -610,69 +755,107 @@ gemm_kernel(GemmArgs p) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     int scl[NSC];
-    scales_of(smem, scl, true);
+    scales_of(slot(I0{}), scl, true);
     const int kvalid = p.kbytes - nkf * KB;
-    read(smem, I0{}, I0{}, kvalid);
+    read(slot(I0{}), I0{}, I0{}, kvalid);
     mma(I0{}, I0{}, I0{}, IFM{}, scl);
     if constexpr (KSUB == 2) {
-      read(smem, I1{}, I1{}, kvalid);
+      read(slot(I0{}), I1{}, I1{}, kvalid);
       mma(I1{}, I1{}, I0{}, IFM{}, scl);
     }
   }
 
   // ---------------------------------------------------------- epilogue
-  // Straight-line code over every accumulator register (fully unrolled, no
-  // early exits, so the accumulators stay in registers); rows and columns
-  // past M and N are predicated off.
-  static_for<FM>([&](auto ic) {
-    constexpr int i = decltype(ic)::value;
-    static_for<FN>([&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      const int64_t n = n0 + wn * TN + j * 32 + (lane & 31);
-      static_for<4>([&](auto gc) {
-        constexpr int g = decltype(gc)::value;
-        const int64_t m = m0 + wm * TM + i * 32 + 8 * g + 4 * (lane >> 5);
-        if (n < p.n && m < p.m) {
-          const int rows = static_cast<int>(p.m - m < 4 ? p.m - m : 4);
-          if constexpr (T::INT) {
-            int t[4];
-            const int* cp = static_cast<const int*>(p.c) + n * p.ldc + m;
-            const int* bp = static_cast<const int*>(p.bias) + m;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              int v = acc[i][j][4 * g + r];
-              if (r < rows) {
-                if (p.beta != 0.0f) v += cp[r];
-                if (p.flags & EPI_BIAS) v += bp[r];
-              }
-              if ((p.flags & EPI_RELU) && v < 0) v = 0;
-              t[r] = v;
-            }
-            int* dp = static_cast<int*>(p.d) + n * p.ldd + m;
-            if (rows == 4 && (reinterpret_cast<uintptr_t>(dp) & 15) == 0) {
-              *reinterpret_cast<v4i*>(dp) = v4i{t[0], t[1], t[2], t[3]};
-            } else {
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                if (r < rows) dp[r] = t[r];
-            }
-          } else {
-            float t[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              float v = p.alpha * acc[i][j][4 * g + r];
-              if (r < rows) {
-                if (p.beta != 0.0f) v += p.beta * load_f(p.c, p.c_type, n * p.ldc + m + r);
-                if (p.flags & EPI_BIAS) v += load_f(p.bias, p.bias_type, m + r);
-              }
-              t[r] = activate(v, p.flags);
-            }
-            store4_f(p.d, p.d_type, n * p.ldd + m, t, rows);
-          }
-        }
-      });
-    });
+  // The accumulators leave through LDS, one 64-row x 32-column block per wave
+  // at a time, so that every lane then owns 8 consecutive rows of one column:
+  // C is read and D written in contiguous runs along M (whole cache lines),
+  // and the per-element code exists once.
+  __builtin_amdgcn_s_waitcnt(0);
+  wg_barrier();  // every wave is done with the ring
+  constexpr int EPB = 64 * 32 * 4;  // staging bytes per wave
+  static_assert(((NW + STAGES - 1) / STAGES) * EPB <= STAGE, "epilogue staging fits the ring");
+  static_assert(FM % 2 == 0, "64-row passes");
+  constexpr int NPASS = (FM / 2) * FN;
+  uint8_t* ep = slot(I0{});
+  static_for<STAGES>([&](auto sc) {
+    if (wave % STAGES == decltype(sc)::value) ep = slot(sc);
   });
+  ep += (wave / STAGES) * EPB;
+  const int erow = (lane & 7) * 8;  // first of this lane's 8 rows in a block
+  for (int ps = 0; ps < NPASS; ++ps) {
+    // Block ps: rows 64*(ps / FN) .. of the wave tile, column tile ps % FN,
+    // stored column by column (256 bytes each), 16-byte chunks XOR-swizzled
+    // by the column so a write instruction spreads over all banks.
+    static_for<NPASS>([&](auto pc) {
+      constexpr int PS = decltype(pc)::value, IH = PS / FN, J = PS % FN;
+      if (ps == PS) {
+        static_for<2>([&](auto iic) {
+          constexpr int II = decltype(iic)::value;
+          static_for<4>([&](auto gc) {
+            constexpr int G = decltype(gc)::value;
+            const int c = lane & 31, k = II * 8 + 2 * G + (lane >> 5);
+            // (whole-vector bit cast: a bit cast of one vector element reads element 0)
+            const v16i a = __builtin_bit_cast(v16i, acc[2 * IH + II][J]);
+            const v4i val = {a[4 * G], a[4 * G + 1], a[4 * G + 2], a[4 * G + 3]};
+            *reinterpret_cast<v4i*>(ep + c * 256 + ((k ^ (c & 15)) << 4)) = val;
+          });
+        });
+      }
+    });
+    const int64_t m = m0 + wm * TM + (ps / FN) * 64 + erow;
+    for (int it = 0; it < 4; ++it) {
+      const int c = it * 8 + (lane >> 3);
+      const int64_t n = n0 + wn * TN + (ps % FN) * 32 + c;
+      const v4i lo = *reinterpret_cast<const v4i*>(ep + c * 256 + (((2 * (lane & 7)) ^ (c & 15)) << 4));
+      const v4i hi = *reinterpret_cast<const v4i*>(ep + c * 256 + (((2 * (lane & 7) + 1) ^ (c & 15)) << 4));
+      if (n < p.n && m < p.m) {
+        const int rows = static_cast<int>(p.m - m < 8 ? p.m - m : 8);
+        const int v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const v4f lof = __builtin_bit_cast(v4f, lo), hif = __builtin_bit_cast(v4f, hi);
+        if constexpr (T::INT) {
+          int t[8];
+#pragma unroll
+          for (int r = 0; r < 8; ++r) t[r] = v[r];
+          if (p.beta != 0.0f) {
+            int cv[8];
+            load8_i(p.c, n * p.ldc + m, rows, cv);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) t[r] += cv[r];
+          }
+          if (p.flags & EPI_BIAS) {
+            int bv[8];
+            load8_i(p.bias, m, rows, bv);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) t[r] += bv[r];
+          }
+          if (p.flags & EPI_RELU) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) t[r] = t[r] < 0 ? 0 : t[r];
+          }
+          store8_i(p.d, n * p.ldd + m, t, rows);
+        } else {
+          float t[8];
+#pragma unroll
+          for (int r = 0; r < 8; ++r) t[r] = p.alpha * (r < 4 ? lof[r] : hif[r - 4]);
+          if (p.beta != 0.0f) {
+            float cv[8];
+            load8_f(p.c, p.c_type, n * p.ldc + m, rows, cv);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) t[r] += p.beta * cv[r];
+          }
+          if (p.flags & EPI_BIAS) {
+            float bv[8];
+            load8_f(p.bias, p.bias_type, m, rows, bv);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) t[r] += bv[r];
+          }
+#pragma unroll
+          for (int r = 0; r < 8; ++r) t[r] = activate(t[r], p.flags);
+          store8_f(p.d, p.d_type, n * p.ldd + m, t, rows);
+        }
+      }
+    }
+  }
 }
 
 }  // namespace thl

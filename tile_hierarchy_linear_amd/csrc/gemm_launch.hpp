@@ -25,13 +25,8 @@ hipError_t launch_gemm(const GemmArgs& a, dim3 grid, hipStream_t stream) {
 #define THL_INST(FAM, BM, BN, LOADW, ST, OCC, AK, BK) \
   template hipError_t thl::launch_gemm<FAM, BM, BN, 2, 2, LOADW, ST, OCC, 4, AK, BK>(const GemmArgs&, dim3, hipStream_t);
 
-#define THL_INSTANTIATE_TN(FAM)                  \
-  THL_INST(FAM, 256, 128, 16, 3, 2, true, true)  \
-  THL_INST(FAM, 256, 256, 16, 4, 1, true, true)  \
-  THL_INST(FAM, 128, 128, 16, 4, 2, true, true)  \
-  THL_INST(FAM, 128, 128, 4, 4, 2, true, true)
-
-#define THL_INSTANTIATE_OPS(FAM, AK, BK)       \
+#define THL_INSTANTIATE_VARIANTS(FAM, AK, BK) \
+  THL_INST(FAM, 256, 256, 16, 4, 1, AK, BK)    \
   THL_INST(FAM, 256, 128, 16, 3, 2, AK, BK)    \
   THL_INST(FAM, 128, 128, 16, 4, 2, AK, BK)    \
   THL_INST(FAM, 128, 128, 4, 4, 2, AK, BK)
