@@ -102,16 +102,16 @@ struct Fam<FAM_FP4> {
   static constexpr int LANE_CHUNKS = 1, KSUB = 2;
   static constexpr bool INT = false, SCALED = true;
   using Acc = v16f;
-  // The scale register holds this lane's row's four E8M0 bytes for the step
-  // (blocks 4kt .. 4kt+3), shifted right by 8*(lane/32) so that the lane's
-  // block for sub-step KS (2KS + lane/32) sits in byte 2*KS.
+  // Lane group g (lanes 32g .. 32g+31) takes the step's 32-element blocks 2g
+  // (sub-step 0) and 2g+1 (sub-step 1); its scale register holds the two
+  // E8M0 bytes of those blocks in bytes 0 and 1, and opsel picks byte KS.
   template <int KS>
   static __device__ __forceinline__ Acc mma(const v4i* a, const v4i* b, Acc c, int sa, int sb) {
     const v4i z = {0, 0, 0, 0};
     const v8i av = __builtin_shufflevector(a[0], z, 0, 1, 2, 3, 4, 5, 6, 7);
     const v8i bv = __builtin_shufflevector(b[0], z, 0, 1, 2, 3, 4, 5, 6, 7);
-    // Format 4 = E2M1 for both operands; opsel picks byte 0 or byte 2.
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, (KS & 1) * 2, sa, (KS & 1) * 2, sb);
+    // Format 4 = E2M1 for both operands.
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, KS & 1, sa, KS & 1, sb);
   }
 };
 
@@ -376,6 +376,7 @@ gemm_kernel(GemmArgs p) {
   // 4-byte aligned); the per-wave count is padded to a whole number with
   // copies into a dummy area so every wave issues the same.
   static_assert(SCW == 4, "scale copies are dwords");
+  static_assert(BM % 64 == 0, "a scale copy instruction covers 64 rows of one operand");
   constexpr int SC_BYTES = T::SCALED ? (BM + BN) * 4 : 0;
   constexpr int SC_INSTR = T::SCALED ? (BM + BN) * 4 / (64 * SCW) : 0;
   constexpr int SC_LOADS = (SC_INSTR + NW - 1) / NW;
@@ -453,16 +454,18 @@ gemm_kernel(GemmArgs p) {
   if constexpr (T::SCALED) {
 #pragma unroll
     for (int t = 0; t < SC_LOADS; ++t) {
+      // One copy instruction covers 64 rows, all of A or all of B (BM is a
+      // multiple of 64), so the choice is uniform over the wave and the
+      // buffer resource stays scalar.
       const int j = t * NW + wave;
-      const int row_all = j < SC_INSTR ? j * 64 + lane : 0;
-      if (row_all < BM) {
-        const int64_t r = m0 + row_all < p.m ? m0 + row_all : p.m - 1;
+      const int row0 = j < SC_INSTR ? j * 64 : 0;
+      sc_a[t] = row0 < BM;
+      if (sc_a[t]) {
+        const int64_t r = m0 + row0 + lane < p.m ? m0 + row0 + lane : p.m - 1;
         sc_src[t] = static_cast<uint32_t>(r * p.ld_sfa);
-        sc_a[t] = true;
       } else {
-        const int64_t r = n0 + (row_all - BM) < p.n ? n0 + (row_all - BM) : p.n - 1;
+        const int64_t r = n0 + (row0 - BM) + lane < p.n ? n0 + (row0 - BM) + lane : p.n - 1;
         sc_src[t] = static_cast<uint32_t>(r * p.ld_sfb);
-        sc_a[t] = false;
       }
       sc_dst[t] = A_BYTES + B_BYTES + (j < SC_INSTR ? j * 64 * SCW : SC_BYTES);
     }
@@ -481,16 +484,31 @@ gemm_kernel(GemmArgs p) {
   };
 
   // Copies of one full K-step into ring slot BUF: uniform base + 32-bit offset.
-  auto issue_full = [&](int kt, auto buf_tag) {
-    constexpr int BUF = decltype(buf_tag)::value;
+  // Copy V (of VM_STAGE: the scale copies, then A's, then B's) of step kt
+  // into ring slot BUF; ra / rb are the step's operand bases.
+  auto issue_one = [&](auto v_tag, auto buf_tag, int kt, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb) {
+    constexpr int V = decltype(v_tag)::value, BUF = decltype(buf_tag)::value;
     uint8_t* sa = slot(std::integral_constant<int, BUF>{});
-    uint8_t* sb = sa + A_BYTES;
-    issue_scales(kt, sa);
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_tile + kt * a_step), rb = make_rsrc(b_tile + kt * b_step);
-#pragma unroll
-    for (int j = 0; j < A_LOADS; ++j) load_lds_buf<LOADW>(ra, a_off[j], sa + (j * NW + wave) * 64 * LOADW);
-#pragma unroll
-    for (int j = 0; j < B_LOADS; ++j) load_lds_buf<LOADW>(rb, b_off[j], sb + (j * NW + wave) * 64 * LOADW);
+    if constexpr (V < SC_LOADS) {
+      const int o = 4 * kt;
+      load_lds_buf<SCW>(sc_a[V] ? rs_sfa : rs_sfb, sc_src[V] + (o < nkb ? o : 0), sa + sc_dst[V]);
+    } else if constexpr (V < SC_LOADS + A_LOADS) {
+      constexpr int J = V - SC_LOADS;
+      load_lds_buf<LOADW>(ra, a_off[J], sa + (J * NW + wave) * 64 * LOADW);
+    } else {
+      constexpr int J = V - SC_LOADS - A_LOADS;
+      load_lds_buf<LOADW>(rb, b_off[J], sa + A_BYTES + (J * NW + wave) * 64 * LOADW);
+    }
+  };
+  auto step_src = [&](int kt, __amdgpu_buffer_rsrc_t& ra, __amdgpu_buffer_rsrc_t& rb) {
+    ra = make_rsrc(a_tile + kt * a_step);
+    rb = make_rsrc(b_tile + kt * b_step);
+  };
+  // Every copy of one full K-step into ring slot BUF.
+  auto issue_full = [&](int kt, auto buf_tag) {
+    __amdgpu_buffer_rsrc_t ra, rb;
+    step_src(kt, ra, rb);
+    static_for<VM_STAGE>([&](auto vc) { issue_one(vc, buf_tag, kt, ra, rb); });
   };
 
   // The partial last K-step into slot 0: K-major bytes at or past K read the
@@ -542,12 +560,17 @@ gemm_kernel(GemmArgs p) {
   // differ by multiples of 32, which leave the swizzle unchanged, so one
   // offset per sub-step serves every fragment row (plus a constant).
   const int lrow = lane & 31;
+  // The 16-byte chunk of the step's 64 bytes that lane group g (lanes 32g ..)
+  // reads as chunk c of sub-step ks.  A and B use the same assignment, so any
+  // order of K within a step cancels in the dot product; fp4 gives each group
+  // two adjacent 32-element blocks so that its scale bytes are adjacent too.
+  auto chunk_of = [](int ks, int g, int c) { return T::SCALED ? g * KSUB + ks : ks * CPM + g * LC + c; };
   int chunk_off[KSUB][LC];
 #pragma unroll
   for (int ks = 0; ks < KSUB; ++ks)
 #pragma unroll
     for (int c = 0; c < LC; ++c)
-      chunk_off[ks][c] = static_cast<int>(maps::lds_offset(lrow, (ks * CPM + (lane >> 5) * LC + c) * 16));
+      chunk_off[ks][c] = static_cast<int>(maps::lds_offset(lrow, chunk_of(ks, lane >> 5, c) * 16));
   const int a_wave_off = wm * TM * KB, b_wave_off = A_BYTES + wn * TN * KB;
 
   v4i af[2][FM][LC], bf[2][FN][LC];  // fragment slots: (kt*KSUB + ks) & 1
@@ -602,7 +625,7 @@ gemm_kernel(GemmArgs p) {
 #pragma unroll
         for (int c = 0; c < LC; ++c) {
           af[SL][f][c] = *reinterpret_cast<const v4i*>(stage + a_wave_off + f * 32 * KB + chunk_off[KS][c]);
-          if (kvalid < KB) af[SL][f][c] = mask_bytes(af[SL][f][c], kvalid - (KS * CPM + (lane >> 5) * LC + c) * 16);
+          if (kvalid < KB) af[SL][f][c] = mask_bytes(af[SL][f][c], kvalid - chunk_of(KS, lane >> 5, c) * 16);
         }
       } else {
         af[SL][f][0] = read_mm(stage, PA, wm * TM + f * 32, ks_tag, kvalid / 2);
@@ -614,7 +637,7 @@ gemm_kernel(GemmArgs p) {
 #pragma unroll
         for (int c = 0; c < LC; ++c) {
           bf[SL][f][c] = *reinterpret_cast<const v4i*>(stage + b_wave_off + f * 32 * KB + chunk_off[KS][c]);
-          if (kvalid < KB) bf[SL][f][c] = mask_bytes(bf[SL][f][c], kvalid - (KS * CPM + (lane >> 5) * LC + c) * 16);
+          if (kvalid < KB) bf[SL][f][c] = mask_bytes(bf[SL][f][c], kvalid - chunk_of(KS, lane >> 5, c) * 16);
         }
       } else {
         bf[SL][f][0] = read_mm(stage + A_BYTES, PB, wn * TN + f * 32, ks_tag, kvalid / 2);
@@ -639,23 +662,23 @@ gemm_kernel(GemmArgs p) {
       }
   };
 
-  // This lane's scale dword for each fragment row, read from a stage, shifted
-  // right by 8*(lane/32) so sub-step KS finds its block in byte 2*KS.
+  // This lane's two scale bytes for fragment row f (A rows first, then B):
+  // blocks 2g and 2g+1 of the step for lane group g, zero-extended.  In the
+  // tail step, blocks at or past K get scale 1.0 (their data is zero).
+  auto scale_of = [&](const uint8_t* stage, int f, bool tail) -> int {
+    const int row_all = f < FM ? wm * TM + f * 32 + (lane & 31) : BM + wn * TN + (f - FM) * 32 + (lane & 31);
+    int v = *reinterpret_cast<const uint16_t*>(stage + A_BYTES + B_BYTES + row_all * 4 + 2 * (lane >> 5));
+    if (tail) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        if (4 * nkf + 2 * (lane >> 5) + q >= nkb) v = (v & ~(0xff << (8 * q))) | (127 << (8 * q));
+    }
+    return v;
+  };
   auto scales_of = [&](const uint8_t* stage, int (&scl)[NSC], bool tail) {
     if constexpr (T::SCALED) {
-      const int shift = 8 * (lane >> 5);
 #pragma unroll
-      for (int f = 0; f < NSC; ++f) {
-        const int row_all = f < FM ? wm * TM + f * 32 + (lane & 31) : BM + wn * TN + (f - FM) * 32 + (lane & 31);
-        int v = *reinterpret_cast<const int*>(stage + A_BYTES + B_BYTES + row_all * 4);
-        if (tail) {
-          // blocks at or past K get scale 1.0 (their data is zero)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (4 * nkf + q >= nkb) v = (v & ~(0xff << (8 * q))) | (127 << (8 * q));
-        }
-        scl[f] = v >> shift;
-      }
+      for (int f = 0; f < NSC; ++f) scl[f] = scale_of(stage, f, tail);
     } else {
       scl[0] = 0;
     }
@@ -664,24 +687,31 @@ gemm_kernel(GemmArgs p) {
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using IFM = std::integral_constant<int, FM>;
-  using IH = std::integral_constant<int, FM / 2>;
 
-  // Interleave NM MFMAs with NR LDS reads and NV copies in one scheduling
-  // region (issued in that order of preference, reads and copies spread
-  // evenly over the MFMAs).
-  auto interleave = [](auto nm_tag, auto nr_tag, auto nv_tag) {
-    constexpr int NM = decltype(nm_tag)::value, NR = decltype(nr_tag)::value, NV = decltype(nv_tag)::value;
-    // reads go out over the first NM - 2 MFMAs (two MFMAs of slack before
-    // the next phase needs them); copies over all of them
-    constexpr int RM = NM > 2 ? NM - 2 : NM;
-    static_for<NM>([&](auto t) {
-      constexpr int T_ = decltype(t)::value;
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      constexpr int r = T_ < RM ? ((T_ + 1) * NR) / RM - (T_ * NR) / RM : 0;
-      if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
-      constexpr int v = ((T_ + 1) * NV) / NM - (T_ * NV) / NM;
-      if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x020, v, 0);
-    });
+  // One fragment of sub-step KS into fragment slot SL: R = 0 is A's first
+  // row tile, 1 .. FN are B's column tiles, FN+1 .. are A's other row tiles
+  // (the order the MFMAs of a phase consume them).
+  auto read_one = [&](auto r_tag, auto ks_tag, auto slot_tag, const uint8_t* stage) {
+    constexpr int R = decltype(r_tag)::value, KS = decltype(ks_tag)::value, SL = decltype(slot_tag)::value;
+    constexpr bool IS_A = R == 0 || R > FN;
+    constexpr int FI = R == 0 ? 0 : (IS_A ? R - FN : R - 1);
+    if constexpr (IS_A) {
+      if constexpr (AK) {
+#pragma unroll
+        for (int c = 0; c < LC; ++c)
+          af[SL][FI][c] = *reinterpret_cast<const v4i*>(stage + a_wave_off + FI * 32 * KB + chunk_off[KS][c]);
+      } else {
+        af[SL][FI][0] = read_mm(stage, PA, wm * TM + FI * 32, ks_tag, 32);
+      }
+    } else {
+      if constexpr (BK) {
+#pragma unroll
+        for (int c = 0; c < LC; ++c)
+          bf[SL][FI][c] = *reinterpret_cast<const v4i*>(stage + b_wave_off + FI * 32 * KB + chunk_off[KS][c]);
+      } else {
+        bf[SL][FI][0] = read_mm(stage + A_BYTES, PB, wn * TN + FI * 32, ks_tag, 32);
+      }
+    }
   };
 
   if (nkf > 0) {
@@ -696,45 +726,80 @@ gemm_kernel(GemmArgs p) {
     scales_of(slot(I0{}), scl[0], false);
     read(slot(I0{}), I0{}, I0{}, KB);
 
+    // Phase A MFMAs: all of sub-step 0 (two sub-steps per K-step), else the
+    // first quarter of the rows, so that the reads after the barrier spread
+    // over most of the step.
+    constexpr int RA = KSUB == 2 ? FM : (FM >= 4 ? FM / 4 : FM / 2);
     // One K-step; U is its position in the unrolled group, which fixes its
-    // ring slot and fragment-slot parity at compile time.
+    // ring slot and fragment-slot parity at compile time.  Within a phase the
+    // program order interleaves MFMAs, fragment reads and copies, and a hard
+    // scheduling fence after each MFMA keeps that order: reads go out over
+    // the first three quarters of the phase's MFMAs, copies over all of them.
     auto step = [&](auto uc, const int kt) {
       constexpr int U = decltype(uc)::value;
       constexpr int S = U % STAGES;  // ring slot of step kt
       constexpr int NEXT = (S + 1) % STAGES, ISSUE = (S + STAGES - 1) % STAGES;
       constexpr int PAR = U & 1;     // parity of kt (groups start at even kt)
+      constexpr int SA = KSUB == 2 ? 0 : PAR;  // fragment slot used by phase A
+      constexpr int SB = KSUB == 2 ? 1 : PAR;  // ... by phase B
+      constexpr int SN = KSUB == 2 ? 0 : PAR ^ 1;  // ... filled for the next step
       const uint8_t* cur = slot(std::integral_constant<int, S>{});
+      const int* sc = scl[PAR];
       __builtin_amdgcn_sched_barrier(0);
-      // ---- phase A: first half of the MFMAs, reads for the second half
-      if constexpr (KSUB == 2) {
-        mma(I0{}, I0{}, I0{}, IFM{}, scl[PAR]);
-        read(cur, I1{}, I1{}, KB);
-        interleave(std::integral_constant<int, FM * FN>{}, std::integral_constant<int, (FM + FN) * LC>{}, I0{});
-      } else {
-        mma(I0{}, std::integral_constant<int, PAR>{}, I0{}, IH{}, scl[PAR]);
+      // ---- phase A: MFMAs of rows [0, RA) of the first sub-step; reads of the
+      // second sub-step's fragments (two sub-steps per K-step)
+      {
+        constexpr int NM = RA * FN, NR = KSUB == 2 ? FM + FN : 0;
+        constexpr int RM = NM * 3 / 4 > 0 ? NM * 3 / 4 : 1;
+        static_for<NM>([&](auto tc) {
+          constexpr int T_ = decltype(tc)::value, I = T_ / FN, J = T_ % FN;
+          acc[I][J] = T::template mma<0>(af[SA][I], bf[SA][J], acc[I][J], T::SCALED ? sc[I] : 0,
+                                         T::SCALED ? sc[FM + J] : 0);
+          if constexpr (NR > 0 && T_ < RM) {
+            static_for<((T_ + 1) * NR) / RM - (T_ * NR) / RM>([&](auto rc) {
+              constexpr int R = (T_ * NR) / RM + decltype(rc)::value;
+              read_one(std::integral_constant<int, R>{}, I1{}, I1{}, cur);
+            });
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        });
       }
-      __builtin_amdgcn_sched_barrier(0);
       // ---- barrier: stage kt+1 visible, buffer kt-1 free
       wait_vm<(STAGES - 3) * VM_STAGE>();
       wg_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      // ---- phase B: second half, copies of stage kt+S-1, next step's first reads
-      const int nxt = kt + STAGES - 1 < nkf ? kt + STAGES - 1 : nkf - 1;
-      issue_full(nxt, std::integral_constant<int, ISSUE>{});
-      const uint8_t* nx = slot(std::integral_constant<int, NEXT>{});
-      if constexpr (KSUB == 2) {
-        mma(I1{}, I1{}, I0{}, IFM{}, scl[PAR]);
-        read(nx, I0{}, I0{}, KB);
-      } else {
-        mma(I0{}, std::integral_constant<int, PAR>{}, IH{}, IFM{}, scl[PAR]);
-        read(nx, I0{}, std::integral_constant<int, PAR ^ 1>{}, KB);
+      // ---- phase B: the remaining MFMAs; copies of stage kt+STAGES-1 into the
+      // freed buffer; reads of the next step's first fragments and scales
+      {
+        const int nxt = kt + STAGES - 1 < nkf ? kt + STAGES - 1 : nkf - 1;
+        __amdgpu_buffer_rsrc_t ra, rb;
+        step_src(nxt, ra, rb);
+        const uint8_t* nx = slot(std::integral_constant<int, NEXT>{});
+        constexpr int NM = KSUB == 2 ? FM * FN : (FM - RA) * FN;
+        constexpr int NF = FM + FN, NR = NF + (T::SCALED ? NSC : 0);
+        constexpr int RM = NM * 3 / 4 > 0 ? NM * 3 / 4 : 1;
+        static_for<NM>([&](auto tc) {
+          constexpr int T_ = decltype(tc)::value;
+          constexpr int I = KSUB == 2 ? T_ / FN : RA + T_ / FN, J = T_ % FN;
+          acc[I][J] = T::template mma<KSUB - 1>(af[SB][I], bf[SB][J], acc[I][J], T::SCALED ? sc[I] : 0,
+                                                T::SCALED ? sc[FM + J] : 0);
+          if constexpr (T_ < RM) {
+            static_for<((T_ + 1) * NR) / RM - (T_ * NR) / RM>([&](auto rc) {
+              constexpr int R = (T_ * NR) / RM + decltype(rc)::value;
+              if constexpr (R < NF) {
+                read_one(std::integral_constant<int, R>{}, I0{}, std::integral_constant<int, SN>{}, nx);
+              } else if constexpr (T::SCALED) {
+                scl[PAR ^ 1][R - NF] = scale_of(nx, R - NF, false);
+              }
+            });
+          }
+          static_for<((T_ + 1) * VM_STAGE) / NM - (T_ * VM_STAGE) / NM>([&](auto vc) {
+            constexpr int V = (T_ * VM_STAGE) / NM + decltype(vc)::value;
+            issue_one(std::integral_constant<int, V>{}, std::integral_constant<int, ISSUE>{}, nxt, ra, rb);
+          });
+          __builtin_amdgcn_sched_barrier(0);
+        });
       }
-      scales_of(nx, scl[PAR ^ 1], false);
-      constexpr int NM = (KSUB == 2) ? FM * FN : FM * FN / 2;
-      constexpr int NR = (FM + FN) * LC + (T::SCALED ? NSC : 0);
-      interleave(std::integral_constant<int, NM>{}, std::integral_constant<int, NR>{},
-                 std::integral_constant<int, VM_STAGE>{});
-      __builtin_amdgcn_sched_barrier(0);
     };
 
     // Whole unrolled groups without per-step conditions (straight-line code
@@ -766,56 +831,58 @@ gemm_kernel(GemmArgs p) {
   }
 
   // ---------------------------------------------------------- epilogue
-  // The accumulators leave through LDS, one 64-row x 32-column block per wave
-  // at a time, so that every lane then owns 8 consecutive rows of one column:
-  // C is read and D written in contiguous runs along M (whole cache lines),
-  // and the per-element code exists once.
+  // The accumulators leave through LDS, one ER-row x 32-column block of the
+  // wave tile at a time, so that every lane then owns 8 consecutive rows of
+  // one column: C is read and D written in contiguous runs along M (whole
+  // cache lines), and the per-element code is a loop, not one copy per
+  // accumulator register.
   __builtin_amdgcn_s_waitcnt(0);
   wg_barrier();  // every wave is done with the ring
-  constexpr int EPB = 64 * 32 * 4;  // staging bytes per wave
-  static_assert(((NW + STAGES - 1) / STAGES) * EPB <= STAGE, "epilogue staging fits the ring");
-  static_assert(FM % 2 == 0, "64-row passes");
-  constexpr int NPASS = (FM / 2) * FN;
+  // Rows per block: the whole wave-tile height when every wave's block fits
+  // the ring next to the others, else 64.
+  constexpr int ER = ((NW + (STAGE / (TM * 128)) - 1) / (STAGE / (TM * 128) > 0 ? STAGE / (TM * 128) : 1) <= STAGES &&
+                      STAGE / (TM * 128) > 0)
+                         ? TM
+                         : 64;
+  constexpr int EPB = ER * 32 * 4;                 // staging bytes per wave
+  constexpr int WPS = STAGE / EPB;                 // waves per ring slot
+  static_assert(WPS > 0 && (NW + WPS - 1) / WPS <= STAGES, "epilogue staging fits the ring");
+  static_assert(TM % ER == 0 && ER % 64 == 0, "whole 64-row blocks");
+  constexpr int LPC = ER / 8;                      // lanes per column (8 rows each)
+  constexpr int CPI = 64 / LPC;                    // columns per iteration
   uint8_t* ep = slot(I0{});
   static_for<STAGES>([&](auto sc) {
-    if (wave % STAGES == decltype(sc)::value) ep = slot(sc);
+    if (wave / WPS == decltype(sc)::value) ep = slot(sc);
   });
-  ep += (wave / STAGES) * EPB;
-  const int erow = (lane & 7) * 8;  // first of this lane's 8 rows in a block
-  for (int ps = 0; ps < NPASS; ++ps) {
-    // Block ps: rows 64*(ps / FN) .. of the wave tile, column tile ps % FN,
-    // stored column by column (256 bytes each), 16-byte chunks XOR-swizzled
-    // by the column so a write instruction spreads over all banks.
-    static_for<NPASS>([&](auto pc) {
-      constexpr int PS = decltype(pc)::value, IH = PS / FN, J = PS % FN;
-      if (ps == PS) {
-        static_for<2>([&](auto iic) {
-          constexpr int II = decltype(iic)::value;
-          static_for<4>([&](auto gc) {
-            constexpr int G = decltype(gc)::value;
-            const int c = lane & 31, k = II * 8 + 2 * G + (lane >> 5);
-            // (whole-vector bit cast: a bit cast of one vector element reads element 0)
-            const v16i a = __builtin_bit_cast(v16i, acc[2 * IH + II][J]);
-            const v4i val = {a[4 * G], a[4 * G + 1], a[4 * G + 2], a[4 * G + 3]};
-            *reinterpret_cast<v4i*>(ep + c * 256 + ((k ^ (c & 15)) << 4)) = val;
-          });
-        });
-      }
+  ep += (wave % WPS) * EPB;
+  const int erow = (lane % LPC) * 8;  // first of this lane's 8 rows in a block
+  static_for<(TM / ER) * FN>([&](auto pc) {
+    // Block: rows ER*IR .. of the wave tile, column tile J, stored column by
+    // column (ER*4 bytes each), 16-byte chunks XOR-swizzled by the column so
+    // a write instruction spreads over the banks.
+    constexpr int PS = decltype(pc)::value, IR = PS / FN, J = PS % FN;
+    static_for<ER / 32>([&](auto iic) {
+      constexpr int II = decltype(iic)::value;
+      // whole-vector bit cast: a bit cast of one vector element reads element 0
+      const v16i a = __builtin_bit_cast(v16i, acc[IR * (ER / 32) + II][J]);
+      static_for<4>([&](auto gc) {
+        constexpr int G = decltype(gc)::value;
+        const int c = lane & 31, k = II * 8 + 2 * G + (lane >> 5);
+        const v4i val = {a[4 * G], a[4 * G + 1], a[4 * G + 2], a[4 * G + 3]};
+        *reinterpret_cast<v4i*>(ep + c * (ER * 4) + ((k ^ (c & 15)) << 4)) = val;
+      });
     });
-    const int64_t m = m0 + wm * TM + (ps / FN) * 64 + erow;
-    for (int it = 0; it < 4; ++it) {
-      const int c = it * 8 + (lane >> 3);
-      const int64_t n = n0 + wn * TN + (ps % FN) * 32 + c;
-      const v4i lo = *reinterpret_cast<const v4i*>(ep + c * 256 + (((2 * (lane & 7)) ^ (c & 15)) << 4));
-      const v4i hi = *reinterpret_cast<const v4i*>(ep + c * 256 + (((2 * (lane & 7) + 1) ^ (c & 15)) << 4));
+    const int64_t m = m0 + wm * TM + IR * ER + erow;
+    for (int it = 0; it < 32 / CPI; ++it) {
+      const int c = it * CPI + lane / LPC;
+      const int64_t n = n0 + wn * TN + J * 32 + c;
+      const int ch = 2 * (lane % LPC);
+      const v4i lo = *reinterpret_cast<const v4i*>(ep + c * (ER * 4) + ((ch ^ (c & 15)) << 4));
+      const v4i hi = *reinterpret_cast<const v4i*>(ep + c * (ER * 4) + (((ch + 1) ^ (c & 15)) << 4));
       if (n < p.n && m < p.m) {
         const int rows = static_cast<int>(p.m - m < 8 ? p.m - m : 8);
-        const int v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        const v4f lof = __builtin_bit_cast(v4f, lo), hif = __builtin_bit_cast(v4f, hi);
         if constexpr (T::INT) {
-          int t[8];
-#pragma unroll
-          for (int r = 0; r < 8; ++r) t[r] = v[r];
+          int t[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           if (p.beta != 0.0f) {
             int cv[8];
             load8_i(p.c, n * p.ldc + m, rows, cv);
@@ -834,6 +901,7 @@ gemm_kernel(GemmArgs p) {
           }
           store8_i(p.d, n * p.ldd + m, t, rows);
         } else {
+          const v4f lof = __builtin_bit_cast(v4f, lo), hif = __builtin_bit_cast(v4f, hi);
           float t[8];
 #pragma unroll
           for (int r = 0; r < 8; ++r) t[r] = p.alpha * (r < 4 ? lof[r] : hif[r - 4]);
@@ -855,7 +923,7 @@ gemm_kernel(GemmArgs p) {
         }
       }
     }
-  }
+  });
 }
 
 }  // namespace thl
