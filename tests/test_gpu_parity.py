@@ -252,3 +252,32 @@ def test_config_mxfp4_8192_sampled():
     import workloads as wl
 
     _check_sampled(wl.make("mxfp4", 8192, 8192, 8192))
+
+
+@pytest.mark.parametrize("variant", ["bf16_nn_256x256_v16_s4_o1", "bf16_nn_256x128_v16_s3_o2", "bf16_nn_128x128_v16_s4_o2",
+                                     "e2m1_tn_128x128_v16_s4_o2", "e4m3_tn_256x256_v16_s4_o1"])
+def test_persistent_workgroups_walk_several_tiles(variant):
+    # More tiles than the device holds workgroups at once, a ragged K (a
+    # partial last K-step) and ragged M/N: every workgroup runs several tiles,
+    # each with its own prologue, tail step and epilogue.
+    import workloads as wl
+    from oracle import compare
+    from workloads.device import DeviceProblem
+
+    kind = {"bf16": "bf16", "e2m1": "mxfp4", "e4m3": "fp8"}[variant.split("_")[0]]
+    # 16-byte aligned leading dimensions, K with a partial last 64-byte step
+    m, k = {"bf16": (4104, 1032), "fp8": (4100, 1040), "mxfp4": (4100, 1056)}[kind]
+    w = wl.make(kind, m, 4100, k)
+    os.environ["THL_FORCE_VARIANT"] = variant
+    try:
+        _say(f"[persistent] {variant} m={w.m} n={w.n} k={w.k}")
+        dp = DeviceProblem(w)
+        assert dp.run() == 0
+        torch.cuda.synchronize()
+    finally:
+        os.environ.pop("THL_FORCE_VARIANT", None)
+    rows, cols = w.sample(4096)
+    rows = np.concatenate([rows, np.full(w.n, w.m - 1), np.arange(w.m)])
+    cols = np.concatenate([cols, np.arange(w.n), np.full(w.m, w.n - 1)])
+    res = compare.parity_check(w, dp.d_values(rows, cols), rows, cols)
+    assert res["ok"], res

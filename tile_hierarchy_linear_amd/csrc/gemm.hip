@@ -9,6 +9,7 @@
 // CU; then 128x128) is tried first.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
@@ -28,12 +29,13 @@ struct Variant {
   int family;
   bool a_kmajor, b_kmajor;  // opA == T, opB == N
   int bm, bn, threads, loadw;
+  int occ;   // workgroups per CU the kernel is built for
   int tier;  // 0: 256x256, 1: 256x128, 2: 128x128 (the shape rule's preference order)
   LaunchFn launch;
 };
 
 #define THL_V(FAM, NAME, OPS, AK, BK, BM, BN, LOADW, ST, OCC, TIER)                                       \
-  {NAME "_" OPS "_" #BM "x" #BN "_v" #LOADW "_s" #ST "_o" #OCC, FAM, AK, BK, BM, BN, 256, LOADW, TIER,   \
+  {NAME "_" OPS "_" #BM "x" #BN "_v" #LOADW "_s" #ST "_o" #OCC, FAM, AK, BK, BM, BN, 256, LOADW, OCC, TIER, \
    &launch_gemm<FAM, BM, BN, 2, 2, LOADW, ST, OCC, 4, AK, BK>}
 
 // Must list exactly the instantiations of THL_INSTANTIATE_VARIANTS.  Order is
@@ -60,6 +62,20 @@ const Variant kVariants[] = {
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 thread_local const char* t_last_variant = "";
+
+// Compute units of a device, read once per device.
+std::atomic<int> g_cu_count[64];
+
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
+    g_cu_count[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 int family_of(thl_dtype t) {
   switch (t) {
@@ -291,7 +307,14 @@ thl_status thl_gemm(int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
   a.bias_type = static_cast<int32_t>(dt->bias);
   const int64_t tiles = static_cast<int64_t>(a.tiles_m) * a.tiles_n;
   if (tiles > INT32_MAX) return THL_ERR_UNSUPPORTED;
-  if (pick->launch(a, dim3(static_cast<unsigned>(tiles)), reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+  // Persistent workgroups: at most as many as the device holds at once (a
+  // multiple of 8, so each XCD keeps its own range of tiles); each walks
+  // tiles blockIdx.x, + gridDim.x, ...
+  const int ncu = cu_count();
+  if (ncu <= 0) return THL_ERR_HIP;
+  const int64_t resident = static_cast<int64_t>(ncu) * pick->occ;
+  const int64_t grid = tiles < resident ? tiles : resident;
+  if (pick->launch(a, dim3(static_cast<unsigned>(grid)), reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return THL_ERR_HIP;
   t_last_variant = pick->name;
   return THL_OK;

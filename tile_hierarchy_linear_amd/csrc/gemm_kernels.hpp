@@ -330,6 +330,13 @@ __device__ __forceinline__ uint8_t* ring_slot() {
 }
 
 
+// The epilogue's own LDS staging area (separate from the ring).
+template <int BYTES>
+__device__ __forceinline__ uint8_t* ep_area() {
+  __shared__ __attribute__((aligned(1024))) uint8_t area[BYTES];
+  return area;
+}
+
 // ------------------------------------------------------------ the kernel
 //
 // Pipeline (per wavefront, K-steps of 64 bytes per operand row, a ring of
@@ -403,73 +410,84 @@ gemm_kernel(GemmArgs p) {
   const int lane = static_cast<int>(threadIdx.x) & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int wm = wave % WM, wn = wave / WM;
-  int64_t tm, tn;
-  maps::grouped_tile(maps::xcd_remap(blockIdx.x, gridDim.x), p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
-  const int64_t m0 = tm * BM, n0 = tn * BN;
   const int nk = (p.kbytes + KB - 1) / KB;  // K-steps, the last one possibly partial
   const int nkf = p.kbytes / KB;            // full K-steps
-
-  // Per-tile operand bases (uniform), the per-step advance, and per-lane
-  // 32-bit byte offsets of every copy this wave issues.  K-major: rows past M
-  // (N) re-read the last valid row.  M-major: 16-byte chunks wholly past M
-  // (N) re-read the tile's first chunk of that k-row.
-  const uint8_t* a_tile = AK ? p.a + m0 * p.lda_bytes : p.a + m0 * 2;
-  const uint8_t* b_tile = BK ? p.b + n0 * p.ldb_bytes : p.b + n0 * 2;
-  const int64_t a_step = AK ? KB : 32 * p.lda_bytes;
+  const int ntiles = p.tiles_m * p.tiles_n;
+  const int64_t a_step = AK ? KB : 32 * p.lda_bytes;  // operand advance per K-step
   const int64_t b_step = BK ? KB : 32 * p.ldb_bytes;
-  uint32_t a_off[A_LOADS], b_off[B_LOADS];
-#pragma unroll
-  for (int j = 0; j < A_LOADS; ++j) {
-    int64_t row, byte;
-    if constexpr (AK) {
-      maps::copy_source((j * NW + wave) * 64 * LOADW, lane, LOADW, &row, &byte);
-      const int64_t r = (m0 + row < p.m ? m0 + row : p.m - 1) - m0;
-      a_off[j] = static_cast<uint32_t>(r * p.lda_bytes + byte);
-    } else {
-      maps::mm_copy_source((j * NW + wave) * 64 * LOADW, lane, LOADW, PA, &row, &byte);
-      if (m0 + (byte & ~15) / 2 >= p.m) byte &= 15;
-      a_off[j] = static_cast<uint32_t>(row * p.lda_bytes + byte);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < B_LOADS; ++j) {
-    int64_t row, byte;
-    if constexpr (BK) {
-      maps::copy_source((j * NW + wave) * 64 * LOADW, lane, LOADW, &row, &byte);
-      const int64_t r = (n0 + row < p.n ? n0 + row : p.n - 1) - n0;
-      b_off[j] = static_cast<uint32_t>(r * p.ldb_bytes + byte);
-    } else {
-      maps::mm_copy_source((j * NW + wave) * 64 * LOADW, lane, LOADW, PB, &row, &byte);
-      if (n0 + (byte & ~15) / 2 >= p.n) byte &= 15;
-      b_off[j] = static_cast<uint32_t>(row * p.ldb_bytes + byte);
-    }
-  }
-
-  // fp4 scale copies: per lane, the source row base of each copy it issues.
   const int nkb = p.k >> 5;
+  const __amdgpu_buffer_rsrc_t rs_sfa = make_rsrc(p.sfa), rs_sfb = make_rsrc(p.sfb);
+
+  // Per-tile state: the tile's origin, operand bases (uniform) and the
+  // per-lane 32-bit byte offsets of every copy this wave issues.  K-major:
+  // rows past M (N) re-read the last valid row.  M-major: 16-byte chunks
+  // wholly past M (N) re-read the tile's first chunk of that k-row.  fp4:
+  // the source row of each scale copy.
+  int64_t m0 = 0, n0 = 0;
+  const uint8_t* a_tile = p.a;
+  const uint8_t* b_tile = p.b;
+  uint32_t a_off[A_LOADS], b_off[B_LOADS];
   uint32_t sc_src[T::SCALED ? SC_LOADS : 1];
   bool sc_a[T::SCALED ? SC_LOADS : 1];
   int sc_dst[T::SCALED ? SC_LOADS : 1];
-  const __amdgpu_buffer_rsrc_t rs_sfa = make_rsrc(p.sfa), rs_sfb = make_rsrc(p.sfb);
-  if constexpr (T::SCALED) {
+  // Workgroups visit tiles id = blockIdx.x, + gridDim.x, ...; the XCD remap
+  // and grouped raster turn id into (tm, tn) so that the tiles one XCD works
+  // on at a time share A and B panels in its L2 (gridDim.x is a multiple of
+  // 8 whenever the tile count is).
+  auto setup = [&](int id) {
+    int64_t tm, tn;
+    maps::grouped_tile(maps::xcd_remap(id, ntiles), p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
+    m0 = tm * BM;
+    n0 = tn * BN;
+    a_tile = AK ? p.a + m0 * p.lda_bytes : p.a + m0 * 2;
+    b_tile = BK ? p.b + n0 * p.ldb_bytes : p.b + n0 * 2;
 #pragma unroll
-    for (int t = 0; t < SC_LOADS; ++t) {
-      // One copy instruction covers 64 rows, all of A or all of B (BM is a
-      // multiple of 64), so the choice is uniform over the wave and the
-      // buffer resource stays scalar.
-      const int j = t * NW + wave;
-      const int row0 = j < SC_INSTR ? j * 64 : 0;
-      sc_a[t] = row0 < BM;
-      if (sc_a[t]) {
-        const int64_t r = m0 + row0 + lane < p.m ? m0 + row0 + lane : p.m - 1;
-        sc_src[t] = static_cast<uint32_t>(r * p.ld_sfa);
+    for (int j = 0; j < A_LOADS; ++j) {
+      int64_t row, byte;
+      if constexpr (AK) {
+        maps::copy_source((j * NW + wave) * 64 * LOADW, lane, LOADW, &row, &byte);
+        const int64_t r = (m0 + row < p.m ? m0 + row : p.m - 1) - m0;
+        a_off[j] = static_cast<uint32_t>(r * p.lda_bytes + byte);
       } else {
-        const int64_t r = n0 + (row0 - BM) + lane < p.n ? n0 + (row0 - BM) + lane : p.n - 1;
-        sc_src[t] = static_cast<uint32_t>(r * p.ld_sfb);
+        maps::mm_copy_source((j * NW + wave) * 64 * LOADW, lane, LOADW, PA, &row, &byte);
+        if (m0 + (byte & ~15) / 2 >= p.m) byte &= 15;
+        a_off[j] = static_cast<uint32_t>(row * p.lda_bytes + byte);
       }
-      sc_dst[t] = A_BYTES + B_BYTES + (j < SC_INSTR ? j * 64 * SCW : SC_BYTES);
     }
-  }
+#pragma unroll
+    for (int j = 0; j < B_LOADS; ++j) {
+      int64_t row, byte;
+      if constexpr (BK) {
+        maps::copy_source((j * NW + wave) * 64 * LOADW, lane, LOADW, &row, &byte);
+        const int64_t r = (n0 + row < p.n ? n0 + row : p.n - 1) - n0;
+        b_off[j] = static_cast<uint32_t>(r * p.ldb_bytes + byte);
+      } else {
+        maps::mm_copy_source((j * NW + wave) * 64 * LOADW, lane, LOADW, PB, &row, &byte);
+        if (n0 + (byte & ~15) / 2 >= p.n) byte &= 15;
+        b_off[j] = static_cast<uint32_t>(row * p.ldb_bytes + byte);
+      }
+    }
+    if constexpr (T::SCALED) {
+#pragma unroll
+      for (int t = 0; t < SC_LOADS; ++t) {
+        // One copy instruction covers 64 rows, all of A or all of B (BM is a
+        // multiple of 64), so the choice is uniform over the wave and the
+        // buffer resource stays scalar.
+        const int j = t * NW + wave;
+        const int row0 = j < SC_INSTR ? j * 64 : 0;
+        sc_a[t] = row0 < BM;
+        if (sc_a[t]) {
+          const int64_t r = m0 + row0 + lane < p.m ? m0 + row0 + lane : p.m - 1;
+          sc_src[t] = static_cast<uint32_t>(r * p.ld_sfa);
+        } else {
+          const int64_t r = n0 + (row0 - BM) + lane < p.n ? n0 + (row0 - BM) + lane : p.n - 1;
+          sc_src[t] = static_cast<uint32_t>(r * p.ld_sfb);
+        }
+        sc_dst[t] = A_BYTES + B_BYTES + (j < SC_INSTR ? j * 64 * SCW : SC_BYTES);
+      }
+    }
+  };
+
   // Scale copies of step kt into a stage: bytes 4kt .. 4kt+3 of each row; an
   // offset at or past the row's last block reads the row's first dword (those
   // bytes are replaced before use).
@@ -551,10 +569,6 @@ gemm_kernel(GemmArgs p) {
   };
 
   Acc acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = Acc{};
 
   // Per-lane LDS offset of the chunk read for MFMA sub-step ks: fragment rows
   // differ by multiples of 32, which leave the swizzle unchanged, so one
@@ -714,216 +728,268 @@ gemm_kernel(GemmArgs p) {
     }
   };
 
-  if (nkf > 0) {
-    // Prologue: stages 0 .. STAGES-2, then step 0's first fragments and scales.
-    static_for<STAGES - 1>([&](auto sc) {
-      constexpr int S = decltype(sc)::value;
-      issue_full(S < nkf ? S : nkf - 1, std::integral_constant<int, S>{});
-    });
-    wait_vm<(STAGES - 2) * VM_STAGE>();
-    wg_barrier();
-    int scl[2][NSC];
-    scales_of(slot(I0{}), scl[0], false);
-    read(slot(I0{}), I0{}, I0{}, KB);
-
-    // Phase A MFMAs: all of sub-step 0 (two sub-steps per K-step), else the
-    // first quarter of the rows, so that the reads after the barrier spread
-    // over most of the step.
-    constexpr int RA = KSUB == 2 ? FM : (FM >= 4 ? FM / 4 : FM / 2);
-    // One K-step; U is its position in the unrolled group, which fixes its
-    // ring slot and fragment-slot parity at compile time.  Within a phase the
-    // program order interleaves MFMAs, fragment reads and copies, and a hard
-    // scheduling fence after each MFMA keeps that order: reads go out over
-    // the first three quarters of the phase's MFMAs, copies over all of them.
-    auto step = [&](auto uc, const int kt) {
-      constexpr int U = decltype(uc)::value;
-      constexpr int S = U % STAGES;  // ring slot of step kt
-      constexpr int NEXT = (S + 1) % STAGES, ISSUE = (S + STAGES - 1) % STAGES;
-      constexpr int PAR = U & 1;     // parity of kt (groups start at even kt)
-      constexpr int SA = KSUB == 2 ? 0 : PAR;  // fragment slot used by phase A
-      constexpr int SB = KSUB == 2 ? 1 : PAR;  // ... by phase B
-      constexpr int SN = KSUB == 2 ? 0 : PAR ^ 1;  // ... filled for the next step
-      const uint8_t* cur = slot(std::integral_constant<int, S>{});
-      const int* sc = scl[PAR];
-      __builtin_amdgcn_sched_barrier(0);
-      // ---- phase A: MFMAs of rows [0, RA) of the first sub-step; reads of the
-      // second sub-step's fragments (two sub-steps per K-step)
-      {
-        constexpr int NM = RA * FN, NR = KSUB == 2 ? FM + FN : 0;
-        constexpr int RM = NM * 3 / 4 > 0 ? NM * 3 / 4 : 1;
-        static_for<NM>([&](auto tc) {
-          constexpr int T_ = decltype(tc)::value, I = T_ / FN, J = T_ % FN;
-          acc[I][J] = T::template mma<0>(af[SA][I], bf[SA][J], acc[I][J], T::SCALED ? sc[I] : 0,
-                                         T::SCALED ? sc[FM + J] : 0);
-          if constexpr (NR > 0 && T_ < RM) {
-            static_for<((T_ + 1) * NR) / RM - (T_ * NR) / RM>([&](auto rc) {
-              constexpr int R = (T_ * NR) / RM + decltype(rc)::value;
-              read_one(std::integral_constant<int, R>{}, I1{}, I1{}, cur);
-            });
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        });
-      }
-      // ---- barrier: stage kt+1 visible, buffer kt-1 free
-      wait_vm<(STAGES - 3) * VM_STAGE>();
-      wg_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      // ---- phase B: the remaining MFMAs; copies of stage kt+STAGES-1 into the
-      // freed buffer; reads of the next step's first fragments and scales
-      {
-        const int nxt = kt + STAGES - 1 < nkf ? kt + STAGES - 1 : nkf - 1;
-        __amdgpu_buffer_rsrc_t ra, rb;
-        step_src(nxt, ra, rb);
-        const uint8_t* nx = slot(std::integral_constant<int, NEXT>{});
-        constexpr int NM = KSUB == 2 ? FM * FN : (FM - RA) * FN;
-        constexpr int NF = FM + FN, NR = NF + (T::SCALED ? NSC : 0);
-        constexpr int RM = NM * 3 / 4 > 0 ? NM * 3 / 4 : 1;
-        static_for<NM>([&](auto tc) {
-          constexpr int T_ = decltype(tc)::value;
-          constexpr int I = KSUB == 2 ? T_ / FN : RA + T_ / FN, J = T_ % FN;
-          acc[I][J] = T::template mma<KSUB - 1>(af[SB][I], bf[SB][J], acc[I][J], T::SCALED ? sc[I] : 0,
-                                                T::SCALED ? sc[FM + J] : 0);
-          if constexpr (T_ < RM) {
-            static_for<((T_ + 1) * NR) / RM - (T_ * NR) / RM>([&](auto rc) {
-              constexpr int R = (T_ * NR) / RM + decltype(rc)::value;
-              if constexpr (R < NF) {
-                read_one(std::integral_constant<int, R>{}, I0{}, std::integral_constant<int, SN>{}, nx);
-              } else if constexpr (T::SCALED) {
-                scl[PAR ^ 1][R - NF] = scale_of(nx, R - NF, false);
-              }
-            });
-          }
-          static_for<((T_ + 1) * VM_STAGE) / NM - (T_ * VM_STAGE) / NM>([&](auto vc) {
-            constexpr int V = (T_ * VM_STAGE) / NM + decltype(vc)::value;
-            issue_one(std::integral_constant<int, V>{}, std::integral_constant<int, ISSUE>{}, nxt, ra, rb);
+  int scl[2][NSC];
+  // Phase A MFMAs: all of sub-step 0 (two sub-steps per K-step), else the
+  // first quarter of the rows, so that the reads after the barrier spread
+  // over most of the step.
+  constexpr int RA = KSUB == 2 ? FM : (FM >= 4 ? FM / 4 : FM / 2);
+  // One K-step; U is its position in the unrolled group, which fixes its
+  // ring slot and fragment-slot parity at compile time.  Within a phase the
+  // program order interleaves MFMAs, fragment reads and copies, and a hard
+  // scheduling fence after each MFMA keeps that order: reads go out over
+  // the first three quarters of the phase's MFMAs, copies over all of them.
+  auto step = [&](auto uc, const int kt) {
+    constexpr int U = decltype(uc)::value;
+    constexpr int S = U % STAGES;  // ring slot of step kt
+    constexpr int NEXT = (S + 1) % STAGES, ISSUE = (S + STAGES - 1) % STAGES;
+    constexpr int PAR = U & 1;     // parity of kt (groups start at even kt)
+    constexpr int SA = KSUB == 2 ? 0 : PAR;  // fragment slot used by phase A
+    constexpr int SB = KSUB == 2 ? 1 : PAR;  // ... by phase B
+    constexpr int SN = KSUB == 2 ? 0 : PAR ^ 1;  // ... filled for the next step
+    const uint8_t* cur = slot(std::integral_constant<int, S>{});
+    const int* sc = scl[PAR];
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- phase A: MFMAs of rows [0, RA) of the first sub-step; reads of the
+    // second sub-step's fragments (two sub-steps per K-step)
+    {
+      constexpr int NM = RA * FN, NR = KSUB == 2 ? FM + FN : 0;
+      constexpr int RM = NM * 3 / 4 > 0 ? NM * 3 / 4 : 1;
+      static_for<NM>([&](auto tc) {
+        constexpr int T_ = decltype(tc)::value, I = T_ / FN, J = T_ % FN;
+        acc[I][J] = T::template mma<0>(af[SA][I], bf[SA][J], acc[I][J], T::SCALED ? sc[I] : 0,
+                                       T::SCALED ? sc[FM + J] : 0);
+        if constexpr (NR > 0 && T_ < RM) {
+          static_for<((T_ + 1) * NR) / RM - (T_ * NR) / RM>([&](auto rc) {
+            constexpr int R = (T_ * NR) / RM + decltype(rc)::value;
+            read_one(std::integral_constant<int, R>{}, I1{}, I1{}, cur);
           });
-          __builtin_amdgcn_sched_barrier(0);
-        });
-      }
-    };
-
-    // Whole unrolled groups without per-step conditions (straight-line code
-    // between loop edges), then the remaining steps.
-    int kb = 0;
-    for (; kb + UNROLL <= nkf; kb += UNROLL)
-      static_for<UNROLL>([&](auto uc) { step(uc, kb + decltype(uc)::value); });
-    static_for<UNROLL - 1>([&](auto uc) {
-      if (kb + decltype(uc)::value < nkf) step(uc, kb + decltype(uc)::value);
-    });
-  }
-
-  // The partial last K-step, if any: load it alone, then compute masked.
-  if (nk > nkf) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();  // every buffer is free
-    issue_partial(nkf);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    int scl[NSC];
-    scales_of(slot(I0{}), scl, true);
-    const int kvalid = p.kbytes - nkf * KB;
-    read(slot(I0{}), I0{}, I0{}, kvalid);
-    mma(I0{}, I0{}, I0{}, IFM{}, scl);
-    if constexpr (KSUB == 2) {
-      read(slot(I0{}), I1{}, I1{}, kvalid);
-      mma(I1{}, I1{}, I0{}, IFM{}, scl);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
     }
-  }
+    // ---- barrier: stage kt+1 visible, buffer kt-1 free
+    wait_vm<(STAGES - 3) * VM_STAGE>();
+    wg_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- phase B: the remaining MFMAs; copies of stage kt+STAGES-1 into the
+    // freed buffer; reads of the next step's first fragments and scales
+    {
+      const int nxt = kt + STAGES - 1 < nkf ? kt + STAGES - 1 : nkf - 1;
+      __amdgpu_buffer_rsrc_t ra, rb;
+      step_src(nxt, ra, rb);
+      const uint8_t* nx = slot(std::integral_constant<int, NEXT>{});
+      constexpr int NM = KSUB == 2 ? FM * FN : (FM - RA) * FN;
+      constexpr int NF = FM + FN, NR = NF + (T::SCALED ? NSC : 0);
+      constexpr int RM = NM * 3 / 4 > 0 ? NM * 3 / 4 : 1;
+      static_for<NM>([&](auto tc) {
+        constexpr int T_ = decltype(tc)::value;
+        constexpr int I = KSUB == 2 ? T_ / FN : RA + T_ / FN, J = T_ % FN;
+        acc[I][J] = T::template mma<KSUB - 1>(af[SB][I], bf[SB][J], acc[I][J], T::SCALED ? sc[I] : 0,
+                                              T::SCALED ? sc[FM + J] : 0);
+        if constexpr (T_ < RM) {
+          static_for<((T_ + 1) * NR) / RM - (T_ * NR) / RM>([&](auto rc) {
+            constexpr int R = (T_ * NR) / RM + decltype(rc)::value;
+            if constexpr (R < NF) {
+              read_one(std::integral_constant<int, R>{}, I0{}, std::integral_constant<int, SN>{}, nx);
+            } else if constexpr (T::SCALED) {
+              scl[PAR ^ 1][R - NF] = scale_of(nx, R - NF, false);
+            }
+          });
+        }
+        static_for<((T_ + 1) * VM_STAGE) / NM - (T_ * VM_STAGE) / NM>([&](auto vc) {
+          constexpr int V = (T_ * VM_STAGE) / NM + decltype(vc)::value;
+          issue_one(std::integral_constant<int, V>{}, std::integral_constant<int, ISSUE>{}, nxt, ra, rb);
+        });
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    }
+  };
+
 
   // ---------------------------------------------------------- epilogue
   // The accumulators leave through LDS, one ER-row x 32-column block of the
   // wave tile at a time, so that every lane then owns 8 consecutive rows of
   // one column: C is read and D written in contiguous runs along M (whole
   // cache lines), and the per-element code is a loop, not one copy per
-  // accumulator register.
-  __builtin_amdgcn_s_waitcnt(0);
-  wg_barrier();  // every wave is done with the ring
-  // Rows per block: the whole wave-tile height when every wave's block fits
-  // the ring next to the others, else 64.
-  constexpr int ER = ((NW + (STAGE / (TM * 128)) - 1) / (STAGE / (TM * 128) > 0 ? STAGE / (TM * 128) : 1) <= STAGES &&
-                      STAGE / (TM * 128) > 0)
-                         ? TM
-                         : 64;
-  constexpr int EPB = ER * 32 * 4;                 // staging bytes per wave
-  constexpr int WPS = STAGE / EPB;                 // waves per ring slot
-  static_assert(WPS > 0 && (NW + WPS - 1) / WPS <= STAGES, "epilogue staging fits the ring");
-  static_assert(TM % ER == 0 && ER % 64 == 0, "whole 64-row blocks");
-  constexpr int LPC = ER / 8;                      // lanes per column (8 rows each)
-  constexpr int CPI = 64 / LPC;                    // columns per iteration
-  uint8_t* ep = slot(I0{});
-  static_for<STAGES>([&](auto sc) {
-    if (wave / WPS == decltype(sc)::value) ep = slot(sc);
-  });
-  ep += (wave % WPS) * EPB;
-  const int erow = (lane % LPC) * 8;  // first of this lane's 8 rows in a block
-  static_for<(TM / ER) * FN>([&](auto pc) {
-    // Block: rows ER*IR .. of the wave tile, column tile J, stored column by
-    // column (ER*4 bytes each), 16-byte chunks XOR-swizzled by the column so
-    // a write instruction spreads over the banks.
-    constexpr int PS = decltype(pc)::value, IR = PS / FN, J = PS % FN;
-    static_for<ER / 32>([&](auto iic) {
-      constexpr int II = decltype(iic)::value;
-      // whole-vector bit cast: a bit cast of one vector element reads element 0
-      const v16i a = __builtin_bit_cast(v16i, acc[IR * (ER / 32) + II][J]);
-      static_for<4>([&](auto gc) {
-        constexpr int G = decltype(gc)::value;
-        const int c = lane & 31, k = II * 8 + 2 * G + (lane >> 5);
-        const v4i val = {a[4 * G], a[4 * G + 1], a[4 * G + 2], a[4 * G + 3]};
-        *reinterpret_cast<v4i*>(ep + c * (ER * 4) + ((k ^ (c & 15)) << 4)) = val;
-      });
+  // accumulator register.  When a staging area of its own fits next to the
+  // ring, the next tile's first stages are already in flight meanwhile;
+  // otherwise the blocks are staged in the (idle) ring.
+  constexpr int LDS_WG = 163840 / OCC;  // 160 KiB of LDS per CU
+  constexpr int RING = STAGES * STAGE;
+  constexpr int ER_OWN = (TM % 64 == 0 && RING + NW * 64 * 128 <= LDS_WG) ? 64
+                         : (RING + NW * 32 * 128 <= LDS_WG)               ? 32
+                                                                          : 0;
+  constexpr bool EP_OWN = ER_OWN > 0;
+  constexpr int RING_WPS_TM = STAGE / (TM * 128);  // waves per ring slot at the full wave-tile height
+  constexpr int ER = EP_OWN ? ER_OWN : ((RING_WPS_TM > 0 && (NW + RING_WPS_TM - 1) / RING_WPS_TM <= STAGES) ? TM : 64);
+  constexpr int EPB = ER * 32 * 4;  // staging bytes per wave
+  constexpr int WPS = STAGE / EPB;  // waves per ring slot (ring staging)
+  static_assert(EP_OWN || (WPS > 0 && (NW + WPS - 1) / WPS <= STAGES), "epilogue staging fits the ring");
+  static_assert(TM % ER == 0 && ER % 32 == 0, "whole 32-row blocks");
+  constexpr int LPC = ER / 8;                   // lanes per column (8 rows each)
+  constexpr int CPI = 64 / LPC;                 // columns per iteration
+  constexpr int XM = ER / 4 - 1 < 15 ? ER / 4 - 1 : 15;  // chunk swizzle mask (within the column)
+  uint8_t* ep;
+  if constexpr (EP_OWN) {
+    ep = ep_area<NW * EPB>() + wave * EPB;
+  } else {
+    ep = slot(I0{});
+    static_for<STAGES>([&](auto sc) {
+      if (wave / WPS == decltype(sc)::value) ep = slot(sc);
     });
-    const int64_t m = m0 + wm * TM + IR * ER + erow;
-    for (int it = 0; it < 32 / CPI; ++it) {
-      const int c = it * CPI + lane / LPC;
-      const int64_t n = n0 + wn * TN + J * 32 + c;
-      const int ch = 2 * (lane % LPC);
-      const v4i lo = *reinterpret_cast<const v4i*>(ep + c * (ER * 4) + ((ch ^ (c & 15)) << 4));
-      const v4i hi = *reinterpret_cast<const v4i*>(ep + c * (ER * 4) + (((ch + 1) ^ (c & 15)) << 4));
-      if (n < p.n && m < p.m) {
-        const int rows = static_cast<int>(p.m - m < 8 ? p.m - m : 8);
-        if constexpr (T::INT) {
-          int t[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          if (p.beta != 0.0f) {
-            int cv[8];
-            load8_i(p.c, n * p.ldc + m, rows, cv);
-#pragma unroll
-            for (int r = 0; r < 8; ++r) t[r] += cv[r];
+    ep += (wave % WPS) * EPB;
+  }
+  const int erow = (lane % LPC) * 8;  // first of this lane's 8 rows in a block
+  auto epilogue = [&](const int64_t em0, const int64_t en0) {
+    static_for<(TM / ER) * FN>([&](auto pc) {
+      // Block: rows ER*IR .. of the wave tile, column tile J, stored column by
+      // column (ER*4 bytes each), 16-byte chunks XOR-swizzled by the column so
+      // a write instruction spreads over the banks.
+      constexpr int PS = decltype(pc)::value, IR = PS / FN, J = PS % FN;
+      static_for<ER / 32>([&](auto iic) {
+        constexpr int II = decltype(iic)::value;
+        // whole-vector bit cast: a bit cast of one vector element reads element 0
+        const v16i a = __builtin_bit_cast(v16i, acc[IR * (ER / 32) + II][J]);
+        static_for<4>([&](auto gc) {
+          constexpr int G = decltype(gc)::value;
+          const int c = lane & 31, k = II * 8 + 2 * G + (lane >> 5);
+          const v4i val = {a[4 * G], a[4 * G + 1], a[4 * G + 2], a[4 * G + 3]};
+          *reinterpret_cast<v4i*>(ep + c * (ER * 4) + ((k ^ (c & XM)) << 4)) = val;
+        });
+      });
+      const int64_t m = em0 + wm * TM + IR * ER + erow;
+      for (int it = 0; it < 32 / CPI; ++it) {
+        const int c = it * CPI + lane / LPC;
+        const int64_t n = en0 + wn * TN + J * 32 + c;
+        const int ch = 2 * (lane % LPC);
+        const v4i lo = *reinterpret_cast<const v4i*>(ep + c * (ER * 4) + ((ch ^ (c & XM)) << 4));
+        const v4i hi = *reinterpret_cast<const v4i*>(ep + c * (ER * 4) + (((ch + 1) ^ (c & XM)) << 4));
+        if (n < p.n && m < p.m) {
+          const int rows = static_cast<int>(p.m - m < 8 ? p.m - m : 8);
+          if constexpr (T::INT) {
+            int t[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            if (p.beta != 0.0f) {
+              int cv[8];
+              load8_i(p.c, n * p.ldc + m, rows, cv);
+  #pragma unroll
+              for (int r = 0; r < 8; ++r) t[r] += cv[r];
+            }
+            if (p.flags & EPI_BIAS) {
+              int bv[8];
+              load8_i(p.bias, m, rows, bv);
+  #pragma unroll
+              for (int r = 0; r < 8; ++r) t[r] += bv[r];
+            }
+            if (p.flags & EPI_RELU) {
+  #pragma unroll
+              for (int r = 0; r < 8; ++r) t[r] = t[r] < 0 ? 0 : t[r];
+            }
+            store8_i(p.d, n * p.ldd + m, t, rows);
+          } else {
+            const v4f lof = __builtin_bit_cast(v4f, lo), hif = __builtin_bit_cast(v4f, hi);
+            float t[8];
+  #pragma unroll
+            for (int r = 0; r < 8; ++r) t[r] = p.alpha * (r < 4 ? lof[r] : hif[r - 4]);
+            if (p.beta != 0.0f) {
+              float cv[8];
+              load8_f(p.c, p.c_type, n * p.ldc + m, rows, cv);
+  #pragma unroll
+              for (int r = 0; r < 8; ++r) t[r] += p.beta * cv[r];
+            }
+            if (p.flags & EPI_BIAS) {
+              float bv[8];
+              load8_f(p.bias, p.bias_type, m, rows, bv);
+  #pragma unroll
+              for (int r = 0; r < 8; ++r) t[r] += bv[r];
+            }
+  #pragma unroll
+            for (int r = 0; r < 8; ++r) t[r] = activate(t[r], p.flags);
+            store8_f(p.d, p.d_type, n * p.ldd + m, t, rows);
           }
-          if (p.flags & EPI_BIAS) {
-            int bv[8];
-            load8_i(p.bias, m, rows, bv);
-#pragma unroll
-            for (int r = 0; r < 8; ++r) t[r] += bv[r];
-          }
-          if (p.flags & EPI_RELU) {
-#pragma unroll
-            for (int r = 0; r < 8; ++r) t[r] = t[r] < 0 ? 0 : t[r];
-          }
-          store8_i(p.d, n * p.ldd + m, t, rows);
-        } else {
-          const v4f lof = __builtin_bit_cast(v4f, lo), hif = __builtin_bit_cast(v4f, hi);
-          float t[8];
-#pragma unroll
-          for (int r = 0; r < 8; ++r) t[r] = p.alpha * (r < 4 ? lof[r] : hif[r - 4]);
-          if (p.beta != 0.0f) {
-            float cv[8];
-            load8_f(p.c, p.c_type, n * p.ldc + m, rows, cv);
-#pragma unroll
-            for (int r = 0; r < 8; ++r) t[r] += p.beta * cv[r];
-          }
-          if (p.flags & EPI_BIAS) {
-            float bv[8];
-            load8_f(p.bias, p.bias_type, m, rows, bv);
-#pragma unroll
-            for (int r = 0; r < 8; ++r) t[r] += bv[r];
-          }
-#pragma unroll
-          for (int r = 0; r < 8; ++r) t[r] = activate(t[r], p.flags);
-          store8_f(p.d, p.d_type, n * p.ldd + m, t, rows);
         }
       }
+    });
+  };
+
+  // First stages of the current tile.
+  auto prologue = [&]() {
+    static_for<STAGES - 1>([&](auto sc) {
+      constexpr int S = decltype(sc)::value;
+      issue_full(S < nkf ? S : nkf - 1, std::integral_constant<int, S>{});
+    });
+  };
+
+  // ---------------------------------------------------------- tile loop
+  int id = static_cast<int>(blockIdx.x);
+  setup(id);
+  if (nkf > 0) prologue();
+  for (bool first = true;; first = false) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = Acc{};
+
+    if (nkf > 0) {
+      // Stage 0 landed.  After the first tile the previous epilogue's loads
+      // and stores are in the count too, and vector-memory loads and stores
+      // need not complete in order: wait for everything.
+      if (first) {
+        wait_vm<(STAGES - 2) * VM_STAGE>();
+      } else {
+        wait_vm<0>();
+      }
+      wg_barrier();
+      scales_of(slot(I0{}), scl[0], false);
+      read(slot(I0{}), I0{}, I0{}, KB);
+      // Whole unrolled groups without per-step conditions (straight-line code
+      // between loop edges), then the remaining steps.
+      int kb = 0;
+      for (; kb + UNROLL <= nkf; kb += UNROLL)
+        static_for<UNROLL>([&](auto uc) { step(uc, kb + decltype(uc)::value); });
+      static_for<UNROLL - 1>([&](auto uc) {
+        if (kb + decltype(uc)::value < nkf) step(uc, kb + decltype(uc)::value);
+      });
     }
-  });
+
+    // The partial last K-step, if any: load it alone, then compute masked.
+    if (nk > nkf) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();  // every buffer is free
+      issue_partial(nkf);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      int sct[NSC];
+      scales_of(slot(I0{}), sct, true);
+      const int kvalid = p.kbytes - nkf * KB;
+      read(slot(I0{}), I0{}, I0{}, kvalid);
+      mma(I0{}, I0{}, I0{}, IFM{}, sct);
+      if constexpr (KSUB == 2) {
+        read(slot(I0{}), I1{}, I1{}, kvalid);
+        mma(I1{}, I1{}, I0{}, IFM{}, sct);
+      }
+    }
+
+    __builtin_amdgcn_s_waitcnt(0);
+    wg_barrier();  // every wave is done with the ring
+    const int64_t em0 = m0, en0 = n0;
+    const int next = id + static_cast<int>(gridDim.x);
+    if constexpr (EP_OWN) {
+      if (next < ntiles) {
+        setup(next);
+        if (nkf > 0) prologue();
+      }
+      epilogue(em0, en0);
+    } else {
+      epilogue(em0, en0);
+      if (next < ntiles) {
+        wg_barrier();  // the staging blocks in the ring are read
+        setup(next);
+        if (nkf > 0) prologue();
+      }
+    }
+    if (next >= ntiles) break;
+    id = next;
+  }
 }
 
 }  // namespace thl
