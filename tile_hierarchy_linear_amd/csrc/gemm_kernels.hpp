@@ -857,6 +857,10 @@ gemm_kernel(GemmArgs p) {
           *reinterpret_cast<v4i*>(ep + c * (ER * 4) + ((k ^ (c & XM)) << 4)) = val;
         });
       });
+      // Lanes read what other lanes of the wave wrote: the LDS executes a
+      // wave's accesses in order, so only the compiler must keep them in
+      // program order (here and after the reads, before the next block).
+      asm volatile("" ::: "memory");
       const int64_t m = em0 + wm * TM + IR * ER + erow;
       for (int it = 0; it < 32 / CPI; ++it) {
         const int c = it * CPI + lane / LPC;
@@ -908,6 +912,7 @@ gemm_kernel(GemmArgs p) {
           }
         }
       }
+      asm volatile("" ::: "memory");
     });
   };
 
