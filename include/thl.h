@@ -80,10 +80,10 @@ typedef struct {
 typedef struct {
   float a_scale, b_scale; /* per-tensor scales (host values), used for E4M3; 1.0f otherwise */
   const uint8_t* sfa;     /* E2M1X2: E8M0 block scales of A, SFA(i,kb) at sfa[i*ld_sfa + kb], device,
-                             4-byte aligned */
-  int64_t ld_sfa;         /* >= k/32 and a multiple of 4 */
-  const uint8_t* sfb;     /* E2M1X2: SFB(j,kb) at sfb[j*ld_sfb + kb], device, 4-byte aligned */
-  int64_t ld_sfb;         /* >= k/32 and a multiple of 4 */
+                             16-byte aligned */
+  int64_t ld_sfa;         /* >= k/32 and a multiple of 16 */
+  const uint8_t* sfb;     /* E2M1X2: SFB(j,kb) at sfb[j*ld_sfb + kb], device, 16-byte aligned */
+  int64_t ld_sfb;         /* >= k/32 and a multiple of 16 */
 } thl_scales;
 
 /*
@@ -104,7 +104,7 @@ typedef struct {
  *     b_scale folded with alpha into one fp32 factor.
  *   E2M1X2 operands, opA = T, opB = N, k % 32 == 0: F32 accumulate, element
  *     (i,p) of A multiplied by 2^(SFA(i, p/32) - 127), likewise B with SFB(j, p/32);
- *     scale rows 4-byte aligned (THL_ERR_MISALIGNED otherwise).
+ *     scale rows 16-byte aligned (THL_ERR_MISALIGNED otherwise).
  *
  * Ownership: A, B, C, D, bias, sfa, sfb are device pointers owned by the
  * caller; the library allocates nothing and keeps no pointer after return.

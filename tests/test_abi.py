@@ -116,11 +116,13 @@ def test_mxfp4_needs_scales():
     assert call(types=("e2m1", "f32", "bf16", "none"), lda=65, sc=sc) == thl.THL_ERR_INVALID  # odd ld
 
 
-def test_mxfp4_scale_rows_must_be_4_byte_aligned():
-    sc = thl.thl_scales(1.0, 1.0, SFA, 2, SFB, 4)  # ld_sfa = 2: not a multiple of 4
+def test_mxfp4_scale_rows_must_be_16_byte_aligned():
+    sc = thl.thl_scales(1.0, 1.0, SFA, 4, SFB, 16)  # ld_sfa = 4: not a multiple of 16
     assert call(types=("e2m1", "f32", "bf16", "none"), sc=sc) == thl.THL_ERR_MISALIGNED
-    sc = thl.thl_scales(1.0, 1.0, SFA + 1, 4, SFB, 4)
+    sc = thl.thl_scales(1.0, 1.0, SFA + 4, 16, SFB, 16)
     assert call(types=("e2m1", "f32", "bf16", "none"), sc=sc) == thl.THL_ERR_MISALIGNED
+    sc = thl.thl_scales(1.0, 1.0, SFA, 16, SFB, 16)  # accepted (the launch itself needs a GPU)
+    assert call(types=("e2m1", "f32", "bf16", "none"), sc=sc) in (thl.THL_OK, thl.THL_ERR_HIP)
 
 
 def test_misaligned():

@@ -36,7 +36,7 @@ struct Variant {
 
 #define THL_V(FAM, NAME, OPS, AK, BK, BM, BN, LOADW, ST, OCC, TIER)                                       \
   {NAME "_" OPS "_" #BM "x" #BN "_v" #LOADW "_s" #ST "_o" #OCC, FAM, AK, BK, BM, BN, 256, LOADW, OCC, TIER, \
-   &launch_gemm<FAM, BM, BN, 2, 2, LOADW, ST, OCC, 4, AK, BK>}
+   &launch_gemm<FAM, BM, BN, 2, 2, LOADW, ST, OCC, 16, AK, BK>}
 
 // Must list exactly the instantiations of THL_INSTANTIATE_VARIANTS.  Order is
 // the first-fit order within a tier: 16-byte copies before 4-byte ones.
@@ -57,7 +57,9 @@ const Variant kVariants[] = {
     THL_VARIANTS(FAM_F16, "f16", "nt", false, false),
     THL_VARIANTS(FAM_I8, "i8", "tn", true, true),
     THL_VARIANTS(FAM_FP8, "e4m3", "tn", true, true),
-    THL_VARIANTS(FAM_FP4, "e2m1", "tn", true, true),
+    THL_V(FAM_FP4, "e2m1", "tn", true, true, 256, 256, 16, 4, 1, 0),
+    THL_V(FAM_FP4, "e2m1", "tn", true, true, 128, 128, 16, 4, 2, 2),
+    THL_V(FAM_FP4, "e2m1", "tn", true, true, 128, 128, 4, 4, 2, 2),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -250,17 +252,18 @@ thl_status thl_gemm(int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
   const int want_tier = tiles_256 >= 256 ? 0 : (tiles_256x128 >= 256 ? 1 : 2);
   const Variant* pick = nullptr;
   bool family_built = false;
-  for (int pass = 0; pass < 2 && !pick; ++pass) {
+  // Passes: the preferred tier, then each smaller tile, then anything that fits.
+  for (int pass = want_tier; pass <= 3 && !pick; ++pass) {
     for (const Variant& v : kVariants) {
       if (v.family != fam || v.a_kmajor != a_kmajor || v.b_kmajor != b_kmajor) continue;
       family_built = true;
       if (forced && *forced) {
         if (std::strcmp(forced, v.name) != 0) continue;
-      } else if (pass == 0 && v.tier != want_tier) {
-        continue;  // first pass: the tile the shape rule prefers
+      } else if (pass < 3 && v.tier != pass) {
+        continue;
       }
       bool fits = k == 0 || (aligned(A, lda_bytes, v.loadw) && aligned(B, ldb_bytes, v.loadw));
-      if (fam == FAM_FP4 && k > 0) fits = fits && aligned(s.sfa, s.ld_sfa, 4) && aligned(s.sfb, s.ld_sfb, 4);
+      if (fam == FAM_FP4 && k > 0) fits = fits && aligned(s.sfa, s.ld_sfa, 16) && aligned(s.sfb, s.ld_sfb, 16);
       if (fits) {
         pick = &v;
         break;

@@ -5,4 +5,4 @@
 using thl::GemmArgs;
 using thl::FAM_FP4;
 
-THL_INSTANTIATE_VARIANTS(FAM_FP4, true, true)
+THL_INSTANTIATE_VARIANTS_FP4()

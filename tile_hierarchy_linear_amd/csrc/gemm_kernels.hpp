@@ -330,6 +330,13 @@ __device__ __forceinline__ uint8_t* ring_slot() {
 }
 
 
+// The two fp4 scale-group buffers (separate objects, like the ring slots).
+template <int BYTES, int I>
+__device__ __forceinline__ uint8_t* scale_group() {
+  __shared__ __attribute__((aligned(16))) uint8_t buf[BYTES];
+  return buf;
+}
+
 // The epilogue's own LDS staging area (separate from the ring).
 template <int BYTES>
 __device__ __forceinline__ uint8_t* ep_area() {
@@ -378,27 +385,44 @@ gemm_kernel(GemmArgs p) {
   constexpr int A_LOADS = A_BYTES / (64 * LOADW * NW), B_LOADS = B_BYTES / (64 * LOADW * NW);
   constexpr int COPIES = A_LOADS + B_LOADS;  // operand copies per wave per stage
   constexpr int NSC = T::SCALED ? FM + FN : 1;
-  // fp4 block scales travel with their stage: one dword (the 4 E8M0 bytes of
-  // the K-step) per A and B row, copied with 4-byte lanes (scale rows must be
-  // 4-byte aligned); the per-wave count is padded to a whole number with
-  // copies into a dummy area so every wave issues the same.
-  static_assert(SCW == 4, "scale copies are dwords");
+  // fp4 block scales travel in groups of SG = 4 K-steps: one 16-byte lane
+  // per A and B row brings the group's 16 E8M0 bytes (scale rows must be
+  // 16-byte aligned), into one of two group buffers that alternate.  The
+  // copies of group g go out with stage 4g; the per-wave count is padded to
+  // a whole number with copies into a dummy area so every wave issues the
+  // same.  (One 4-byte lane per row per step touched as many cache lines as
+  // all the operand copies of the step.)
+  static_assert(SCW == 16, "scale copies bring 16 bytes (4 K-steps) a row");
   static_assert(BM % 64 == 0, "a scale copy instruction covers 64 rows of one operand");
-  constexpr int SC_BYTES = T::SCALED ? (BM + BN) * 4 : 0;
-  constexpr int SC_INSTR = T::SCALED ? (BM + BN) * 4 / (64 * SCW) : 0;
-  constexpr int SC_LOADS = (SC_INSTR + NW - 1) / NW;
-  constexpr int SC_PAD = T::SCALED ? 64 * SCW : 0;
-  constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES + SC_PAD;
-  constexpr int VM_STAGE = COPIES + SC_LOADS;  // vector-memory instructions per wave per stage
+  constexpr int SG = 4;                                    // K-steps per scale group
+  constexpr int SC_BYTES = T::SCALED ? (BM + BN) * SCW : 0;  // one group buffer
+  constexpr int SC_INSTR = T::SCALED ? (BM + BN) / 64 : 0;
+  constexpr int SC_LOADS = T::SCALED ? (SC_INSTR + NW - 1) / NW : 0;
+  constexpr int SC_PAD = (T::SCALED && SC_INSTR % NW != 0) ? 64 * SCW : 0;
+  constexpr int SC_BUF = SC_BYTES + SC_PAD;  // one group buffer (with the dummy area)
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int VM_STAGE = COPIES;  // operand copies per wave per stage
+  // Copies per wave of the stage at position pos (a multiple of SG carries
+  // its scale group too).
+  auto vm_of = [](int pos) constexpr { return COPIES + (pos % SG == 0 ? SC_LOADS : 0); };
   static_assert(STAGE % 16 == 0, "stages stay 16-byte aligned");
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole MFMA tiles");
   static_assert(A_LOADS * 64 * LOADW * NW == A_BYTES && B_LOADS * 64 * LOADW * NW == B_BYTES,
                 "copies must split evenly over waves");
   static_assert(STAGES >= 3 && STAGES <= 6, "three to six stages");
-  static_assert(VM_STAGE * (STAGES - 2) < 64, "vmcnt range");
-  // Steps per unrolled loop body: ring slots and fragment-slot parities are
-  // compile-time constants inside it.
-  constexpr int UNROLL = (STAGES % 2 == 0) ? STAGES : 2 * STAGES;
+  static_assert((VM_STAGE + SC_LOADS) * (STAGES - 2) < 64, "vmcnt range");
+  // Steps per unrolled loop body: ring slots, fragment-slot parities and (fp4)
+  // the scale-group buffer and position are compile-time constants inside it.
+  constexpr int UNROLL = T::SCALED ? (STAGES % (2 * SG) == 0 ? STAGES : (STAGES % SG == 0 ? 2 * STAGES : 0))
+                                   : ((STAGES % 2 == 0) ? STAGES : 2 * STAGES);
+  static_assert(UNROLL > 0, "scale groups need STAGES to divide into 4 K-step groups");
+  // Copies per wave younger than stage pos+1 when waiting for it at step pos
+  // (stages pos+2 .. pos+STAGES-2 may still be in flight).
+  auto younger = [](int pos) constexpr {
+    int n = 0;
+    for (int q = pos + 2; q <= pos + STAGES - 2; ++q) n += COPIES + (q % SG == 0 ? SC_LOADS : 0);
+    return n;
+  };
   static_assert(KSUB == 2 || (KSUB == 1 && FM % 2 == 0), "a step splits into two halves");
   static_assert((AK && BK) || F == FAM_BF16 || F == FAM_F16, "M/N-major operands are 16-bit only");
   constexpr int PA = BM * 2, PB = BN * 2;  // k-row pitch of M- (N-) major stages
@@ -406,6 +430,8 @@ gemm_kernel(GemmArgs p) {
   static_assert(BK || PB % 256 == 0, "N-major k-rows are whole 256-byte bank windows");
 
   auto slot = [](auto i_tag) -> uint8_t* { return ring_slot<STAGE, decltype(i_tag)::value>(); };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
 
   const int lane = static_cast<int>(threadIdx.x) & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
@@ -478,43 +504,40 @@ gemm_kernel(GemmArgs p) {
         sc_a[t] = row0 < BM;
         if (sc_a[t]) {
           const int64_t r = m0 + row0 + lane < p.m ? m0 + row0 + lane : p.m - 1;
-          sc_src[t] = static_cast<uint32_t>(r * p.ld_sfa);
+          sc_src[t] = static_cast<uint32_t>(r * p.ld_sfa);  // row base; + 16 bytes per group
         } else {
           const int64_t r = n0 + (row0 - BM) + lane < p.n ? n0 + (row0 - BM) + lane : p.n - 1;
           sc_src[t] = static_cast<uint32_t>(r * p.ld_sfb);
         }
-        sc_dst[t] = A_BYTES + B_BYTES + (j < SC_INSTR ? j * 64 * SCW : SC_BYTES);
+        sc_dst[t] = j < SC_INSTR ? j * 64 * SCW : SC_BYTES;
       }
     }
   };
 
-  // Scale copies of step kt into a stage: bytes 4kt .. 4kt+3 of each row; an
-  // offset at or past the row's last block reads the row's first dword (those
-  // bytes are replaced before use).
-  auto issue_scales = [&](int kt, uint8_t* stage) {
-    if constexpr (T::SCALED) {
-#pragma unroll
-      for (int t = 0; t < SC_LOADS; ++t) {
-        const int o = 4 * kt;
-        load_lds_buf<SCW>(sc_a[t] ? rs_sfa : rs_sfb, sc_src[t] + (o < nkb ? o : 0), stage + sc_dst[t]);
-      }
-    }
+  // The scale group buffers (fp4).
+  auto sgbuf = [](auto i_tag) -> uint8_t* { return scale_group<SC_BUF, decltype(i_tag)::value>(); };
+  // The scale copies of group g into group buffer GB: row bytes 16g .. 16g+15;
+  // a group at or past the rows' last block re-reads the row's first group
+  // (never used).
+  auto issue_scale = [&](int t, int g, uint8_t* buf) {
+    const int o = 16 * g;
+    load_lds_buf<SCW>(sc_a[t] ? rs_sfa : rs_sfb, sc_src[t] + (o < nkb ? o : 0), buf + sc_dst[t]);
   };
-
-  // Copies of one full K-step into ring slot BUF: uniform base + 32-bit offset.
-  // Copy V (of VM_STAGE: the scale copies, then A's, then B's) of step kt
-  // into ring slot BUF; ra / rb are the step's operand bases.
-  auto issue_one = [&](auto v_tag, auto buf_tag, int kt, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb) {
-    constexpr int V = decltype(v_tag)::value, BUF = decltype(buf_tag)::value;
+  // Copy V of the stage at position POS (kt is its K-step) into ring slot
+  // BUF: the scale copies first when POS starts a group, then A's, then B's;
+  // ra / rb are the step's operand bases.
+  auto issue_one = [&](auto v_tag, auto buf_tag, auto pos_tag, int kt, __amdgpu_buffer_rsrc_t ra,
+                       __amdgpu_buffer_rsrc_t rb) {
+    constexpr int V = decltype(v_tag)::value, BUF = decltype(buf_tag)::value, POS = decltype(pos_tag)::value;
+    constexpr int NS = vm_of(POS) - COPIES;  // scale copies of this stage
     uint8_t* sa = slot(std::integral_constant<int, BUF>{});
-    if constexpr (V < SC_LOADS) {
-      const int o = 4 * kt;
-      load_lds_buf<SCW>(sc_a[V] ? rs_sfa : rs_sfb, sc_src[V] + (o < nkb ? o : 0), sa + sc_dst[V]);
-    } else if constexpr (V < SC_LOADS + A_LOADS) {
-      constexpr int J = V - SC_LOADS;
+    if constexpr (V < NS) {
+      issue_scale(V, kt / SG, sgbuf(std::integral_constant<int, (POS / SG) % 2>{}));
+    } else if constexpr (V < NS + A_LOADS) {
+      constexpr int J = V - NS;
       load_lds_buf<LOADW>(ra, a_off[J], sa + (J * NW + wave) * 64 * LOADW);
     } else {
-      constexpr int J = V - SC_LOADS - A_LOADS;
+      constexpr int J = V - NS - A_LOADS;
       load_lds_buf<LOADW>(rb, b_off[J], sa + A_BYTES + (J * NW + wave) * 64 * LOADW);
     }
   };
@@ -522,11 +545,11 @@ gemm_kernel(GemmArgs p) {
     ra = make_rsrc(a_tile + kt * a_step);
     rb = make_rsrc(b_tile + kt * b_step);
   };
-  // Every copy of one full K-step into ring slot BUF.
-  auto issue_full = [&](int kt, auto buf_tag) {
+  // Every copy of the stage at position POS (K-step kt) into ring slot BUF.
+  auto issue_full = [&](int kt, auto buf_tag, auto pos_tag) {
     __amdgpu_buffer_rsrc_t ra, rb;
     step_src(kt, ra, rb);
-    static_for<VM_STAGE>([&](auto vc) { issue_one(vc, buf_tag, kt, ra, rb); });
+    static_for<vm_of(decltype(pos_tag)::value)>([&](auto vc) { issue_one(vc, buf_tag, pos_tag, kt, ra, rb); });
   };
 
   // The partial last K-step into slot 0: K-major bytes at or past K read the
@@ -536,7 +559,11 @@ gemm_kernel(GemmArgs p) {
     uint8_t* sa = slot(std::integral_constant<int, 0>{});
     uint8_t* sb = sa + A_BYTES;
     const int64_t kofs = static_cast<int64_t>(kt) * KB;
-    issue_scales(kt, sa);
+    if constexpr (T::SCALED) {
+      uint8_t* gb = ((kt / SG) & 1) ? sgbuf(I1{}) : sgbuf(I0{});
+#pragma unroll
+      for (int t = 0; t < SC_LOADS; ++t) issue_scale(t, kt / SG, gb);
+    }
     // K-major: offsets from the tile base; M-major: from the step's first k-row.
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(AK ? a_tile : a_tile + kt * a_step);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(BK ? b_tile : b_tile + kt * b_step);
@@ -679,9 +706,10 @@ gemm_kernel(GemmArgs p) {
   // This lane's two scale bytes for fragment row f (A rows first, then B):
   // blocks 2g and 2g+1 of the step for lane group g, zero-extended.  In the
   // tail step, blocks at or past K get scale 1.0 (their data is zero).
-  auto scale_of = [&](const uint8_t* stage, int f, bool tail) -> int {
+  // gbuf is the step's group buffer, kq its position in the group.
+  auto scale_of = [&](const uint8_t* gbuf, int kq, int f, bool tail) -> int {
     const int row_all = f < FM ? wm * TM + f * 32 + (lane & 31) : BM + wn * TN + (f - FM) * 32 + (lane & 31);
-    int v = *reinterpret_cast<const uint16_t*>(stage + A_BYTES + B_BYTES + row_all * 4 + 2 * (lane >> 5));
+    int v = *reinterpret_cast<const uint16_t*>(gbuf + row_all * SCW + 4 * kq + 2 * (lane >> 5));
     if (tail) {
 #pragma unroll
       for (int q = 0; q < 2; ++q)
@@ -689,17 +717,15 @@ gemm_kernel(GemmArgs p) {
     }
     return v;
   };
-  auto scales_of = [&](const uint8_t* stage, int (&scl)[NSC], bool tail) {
+  auto scales_of = [&](const uint8_t* gbuf, int kq, int (&scl)[NSC], bool tail) {
     if constexpr (T::SCALED) {
 #pragma unroll
-      for (int f = 0; f < NSC; ++f) scl[f] = scale_of(stage, f, tail);
+      for (int f = 0; f < NSC; ++f) scl[f] = scale_of(gbuf, kq, f, tail);
     } else {
       scl[0] = 0;
     }
   };
 
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
   using IFM = std::integral_constant<int, FM>;
 
   // One fragment of sub-step KS into fragment slot SL: R = 0 is A's first
@@ -768,7 +794,7 @@ gemm_kernel(GemmArgs p) {
       });
     }
     // ---- barrier: stage kt+1 visible, buffer kt-1 free
-    wait_vm<(STAGES - 3) * VM_STAGE>();
+    wait_vm<younger(U)>();
     wg_barrier();
     __builtin_amdgcn_sched_barrier(0);
     // ---- phase B: the remaining MFMAs; copies of stage kt+STAGES-1 into the
@@ -781,6 +807,10 @@ gemm_kernel(GemmArgs p) {
       constexpr int NM = KSUB == 2 ? FM * FN : (FM - RA) * FN;
       constexpr int NF = FM + FN, NR = NF + (T::SCALED ? NSC : 0);
       constexpr int RM = NM * 3 / 4 > 0 ? NM * 3 / 4 : 1;
+      constexpr int P = U + STAGES - 1;  // position of the stage issued here
+      constexpr int NV = vm_of(P);
+      const uint8_t* ng = nullptr;  // the next step's scale group (fp4)
+      if constexpr (T::SCALED) ng = sgbuf(std::integral_constant<int, ((U + 1) / SG) % 2>{});
       static_for<NM>([&](auto tc) {
         constexpr int T_ = decltype(tc)::value;
         constexpr int I = KSUB == 2 ? T_ / FN : RA + T_ / FN, J = T_ % FN;
@@ -792,13 +822,14 @@ gemm_kernel(GemmArgs p) {
             if constexpr (R < NF) {
               read_one(std::integral_constant<int, R>{}, I0{}, std::integral_constant<int, SN>{}, nx);
             } else if constexpr (T::SCALED) {
-              scl[PAR ^ 1][R - NF] = scale_of(nx, R - NF, false);
+              scl[PAR ^ 1][R - NF] = scale_of(ng, (U + 1) % SG, R - NF, false);
             }
           });
         }
-        static_for<((T_ + 1) * VM_STAGE) / NM - (T_ * VM_STAGE) / NM>([&](auto vc) {
-          constexpr int V = (T_ * VM_STAGE) / NM + decltype(vc)::value;
-          issue_one(std::integral_constant<int, V>{}, std::integral_constant<int, ISSUE>{}, nxt, ra, rb);
+        static_for<((T_ + 1) * NV) / NM - (T_ * NV) / NM>([&](auto vc) {
+          constexpr int V = (T_ * NV) / NM + decltype(vc)::value;
+          issue_one(std::integral_constant<int, V>{}, std::integral_constant<int, ISSUE>{},
+                    std::integral_constant<int, P>{}, nxt, ra, rb);
         });
         __builtin_amdgcn_sched_barrier(0);
       });
@@ -815,7 +846,7 @@ gemm_kernel(GemmArgs p) {
   // ring, the next tile's first stages are already in flight meanwhile;
   // otherwise the blocks are staged in the (idle) ring.
   constexpr int LDS_WG = 163840 / OCC;  // 160 KiB of LDS per CU
-  constexpr int RING = STAGES * STAGE;
+  constexpr int RING = STAGES * STAGE + 2 * SC_BUF;  // with the scale group buffers
   constexpr int ER_OWN = (TM % 64 == 0 && RING + NW * 64 * 128 <= LDS_WG) ? 64
                          : (RING + NW * 32 * 128 <= LDS_WG)               ? 32
                                                                           : 0;
@@ -920,7 +951,7 @@ gemm_kernel(GemmArgs p) {
   auto prologue = [&]() {
     static_for<STAGES - 1>([&](auto sc) {
       constexpr int S = decltype(sc)::value;
-      issue_full(S < nkf ? S : nkf - 1, std::integral_constant<int, S>{});
+      issue_full(S < nkf ? S : nkf - 1, std::integral_constant<int, S>{}, std::integral_constant<int, S>{});
     });
   };
 
@@ -939,12 +970,12 @@ gemm_kernel(GemmArgs p) {
       // and stores are in the count too, and vector-memory loads and stores
       // need not complete in order: wait for everything.
       if (first) {
-        wait_vm<(STAGES - 2) * VM_STAGE>();
+        wait_vm<younger(-1) + vm_of(STAGES - 2)>();  // stages 1 .. STAGES-2 may be in flight
       } else {
         wait_vm<0>();
       }
       wg_barrier();
-      scales_of(slot(I0{}), scl[0], false);
+      if constexpr (T::SCALED) scales_of(sgbuf(I0{}), 0, scl[0], false);
       read(slot(I0{}), I0{}, I0{}, KB);
       // Whole unrolled groups without per-step conditions (straight-line code
       // between loop edges), then the remaining steps.
@@ -964,7 +995,11 @@ gemm_kernel(GemmArgs p) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       int sct[NSC];
-      scales_of(slot(I0{}), sct, true);
+      if constexpr (T::SCALED) {
+        scales_of(((nkf / SG) & 1) ? sgbuf(I1{}) : sgbuf(I0{}), nkf % SG, sct, true);
+      } else {
+        sct[0] = 0;
+      }
       const int kvalid = p.kbytes - nkf * KB;
       read(slot(I0{}), I0{}, I0{}, kvalid);
       mma(I0{}, I0{}, I0{}, IFM{}, sct);

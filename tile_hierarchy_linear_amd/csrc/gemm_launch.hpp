@@ -23,7 +23,14 @@ hipError_t launch_gemm(const GemmArgs& a, dim3 grid, hipStream_t stream) {
 // The variants built for one family and operand orientation (used by each
 // instantiation unit; the dispatch table lists the same set).
 #define THL_INST(FAM, BM, BN, LOADW, ST, OCC, AK, BK) \
-  template hipError_t thl::launch_gemm<FAM, BM, BN, 2, 2, LOADW, ST, OCC, 4, AK, BK>(const GemmArgs&, dim3, hipStream_t);
+  template hipError_t thl::launch_gemm<FAM, BM, BN, 2, 2, LOADW, ST, OCC, 16, AK, BK>(const GemmArgs&, dim3, hipStream_t);
+
+// fp4: no 256x128 three-stage variant (its K-step groups of four need a
+// stage count that divides into them).
+#define THL_INSTANTIATE_VARIANTS_FP4()                 \
+  THL_INST(FAM_FP4, 256, 256, 16, 4, 1, true, true)    \
+  THL_INST(FAM_FP4, 128, 128, 16, 4, 2, true, true)    \
+  THL_INST(FAM_FP4, 128, 128, 4, 4, 2, true, true)
 
 #define THL_INSTANTIATE_VARIANTS(FAM, AK, BK) \
   THL_INST(FAM, 256, 256, 16, 4, 1, AK, BK)    \

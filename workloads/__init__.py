@@ -259,8 +259,8 @@ def make(kind: str, m: int, n: int, k: int, seed: int | None = None, *, op_a=Non
         xa, xb = ga.standard_normal((m, k)), gb.standard_normal((n, k))  # B drawn as its stored N x K
         ca_codes, w["sfa"] = mx_quantize(xa) if k else (np.zeros((m, 0), np.uint8), np.zeros((m, 0), np.uint8))
         cb_codes, w["sfb"] = mx_quantize(xb) if k else (np.zeros((n, 0), np.uint8), np.zeros((n, 0), np.uint8))
-        # scale rows padded to a multiple of 4 bytes (the kernels copy dwords)
-        ld_sf = max(4, (k // 32 + 3) // 4 * 4)
+        # scale rows padded to a multiple of 16 bytes (the kernels copy 16-byte groups)
+        ld_sf = max(16, (k // 32 + 15) // 16 * 16)
         w["ld_sfa"] = w["ld_sfb"] = ld_sf
         pad_a = np.full((m, ld_sf), 127, np.uint8)
         pad_a[:, : k // 32] = w["sfa"]
