@@ -127,6 +127,35 @@ def test_epilogue_variants(kind, act):
     _check_full(w)
 
 
+# Interior tiles with 16-byte aligned rows of C, D and bias take the batched
+# vector epilogue; edge tiles of the same call take the general one.  Each case
+# mixes both, over the C / D / bias types and the activations.
+VEC_CASES = [
+    # kind, type_c, type_d, type_bias, act, beta, variant
+    ("fp16", "f16", "f16", "f16", "gelu", 0.5, None),
+    ("fp16", None, "bf16", "bf16", "relu", 0.0, None),
+    ("bf16", "bf16", "f32", "f32", "relu", 1.0, "bf16_nn_256x256_v16_s4_o1"),
+    ("bf16", "f16", "f16", "bf16", "none", -0.25, "bf16_nn_256x128_v16_s3_o2"),
+    ("fp8", "f16", "bf16", "f16", "none", 1.0, "e4m3_tn_256x256_v16_s4_o1"),
+    ("fp8", "bf16", "f32", "bf16", "gelu", 0.75, None),
+    ("mxfp4", "bf16", "f16", None, "none", 1.0, "e2m1_tn_256x256_v16_s4_o1"),
+    ("mxfp4", "f16", "f32", "f32", "relu", 1.0, None),
+]
+
+
+@pytest.mark.parametrize("case", VEC_CASES, ids=lambda c: "-".join(str(x) for x in c[:6]))
+def test_vector_epilogue_types(case):
+    import workloads as wl
+
+    kind, tc, td, tb, act, beta, variant = case
+    m, n, k = 392, 328, 256
+    ld = _pad(m, 16)
+    kw = dict(ldc=ld, ldd=ld, type_d=td, type_c=tc, type_bias=tb, act=act, beta=beta, bias=tb is not None)
+    if kind in ("fp8", "mxfp4"):
+        kw.update(lda=_pad(k, 32), ldb=_pad(k, 32))
+    _check_full(wl.make(kind, m, n, k, **kw), variant=variant)
+
+
 def test_int8_epilogue_bias_beta_relu():
     import workloads as wl
 
@@ -192,6 +221,25 @@ def test_d_aliases_c_in_place():
     got = dp.d_all()
     ii, jj = np.meshgrid(np.arange(w.m), np.arange(w.n), indexing="ij")
     res = compare.parity_check(ref_w, got.ravel(), ii.ravel(), jj.ravel())
+    assert res["ok"], res
+
+
+def test_d_aliases_c_in_place_vector_epilogue():
+    """bf16 C and D in one buffer with 16-byte aligned columns: interior tiles
+    read all of their C before any D of theirs is written."""
+    from oracle import compare
+    import workloads as wl
+    from workloads.device import DeviceProblem
+
+    w = wl.make("bf16", 264, 264, 64, ldc=272, ldd=272, beta=1.0, bias=True, act="relu")
+    dp = DeviceProblem(w)
+    dp.d.view(torch.int16).view(-1).copy_(dp.c.view(torch.int16))
+    st = dp.run(c=dp.d)
+    assert st == 0
+    torch.cuda.synchronize()
+    got = dp.d_all()
+    ii, jj = np.meshgrid(np.arange(w.m), np.arange(w.n), indexing="ij")
+    res = compare.parity_check(w, got.ravel(), ii.ravel(), jj.ravel())
     assert res["ok"], res
 
 

@@ -305,6 +305,17 @@ thl_status thl_gemm(int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
   a.alpha = (fam == FAM_FP8) ? alpha * s.a_scale * s.b_scale : alpha;
   a.beta = beta;
   a.flags = static_cast<int32_t>(flags);
+  // Vector epilogue: D (and C, bias) rows aligned for 16-byte runs along M,
+  // C 16-bit, and a 256-column panel within 32-bit offsets.
+  if (!int_path) {
+    auto vec_ok = [](const void* ptr, int64_t ld_bytes) {
+      return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0 && ld_bytes % 16 == 0 && ld_bytes <= (INT64_C(1) << 23);
+    };
+    bool vec = vec_ok(D, bytes_of(dt->d, ldd));
+    if (beta != 0.0f) vec = vec && (dt->c == THL_F16 || dt->c == THL_BF16) && vec_ok(C, bytes_of(dt->c, ldc));
+    if (has_bias) vec = vec && (reinterpret_cast<uintptr_t>(epi->bias) & 15) == 0;
+    if (vec) a.flags |= EPI_VEC;
+  }
   a.c_type = static_cast<int32_t>(dt->c);
   a.d_type = static_cast<int32_t>(dt->d);
   a.bias_type = static_cast<int32_t>(dt->bias);

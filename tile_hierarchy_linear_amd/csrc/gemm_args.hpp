@@ -13,6 +13,10 @@ enum Family { FAM_F16 = 0, FAM_BF16 = 1, FAM_I8 = 2, FAM_FP8 = 3, FAM_FP4 = 4 };
 // Element-type codes, equal to the public thl_dtype values.
 enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_I8 = 3, DT_I32 = 4 };
 enum : int { EPI_BIAS = 1, EPI_RELU = 2, EPI_GELU = 4 };
+// Set by the host, not part of the public flags: D (and C when beta != 0, and
+// bias) can be moved as aligned 16-byte vectors along M, C is 16-bit, and a
+// 256-column panel of C or D spans less than 2 GiB.
+enum : int { EPI_VEC = 8 };
 
 struct GemmArgs {
   const uint8_t* a;  // A as stored: leading dimension lda_bytes

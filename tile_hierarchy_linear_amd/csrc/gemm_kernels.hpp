@@ -36,6 +36,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
@@ -159,42 +160,6 @@ __device__ __forceinline__ float activate(float t, int flags) {
   return t;
 }
 
-// Store 4 consecutive rows m..m+3 of column n (rows >= `rows` skipped).
-__device__ __forceinline__ void store4_f(void* d, int type, int64_t off, const float (&v)[4], int rows) {
-  if (type == DT_F32) {
-    float* p = static_cast<float*>(d) + off;
-    if (rows >= 4 && (reinterpret_cast<uintptr_t>(p) & 15) == 0) {
-      *reinterpret_cast<v4f*>(p) = v4f{v[0], v[1], v[2], v[3]};
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (i < rows) p[i] = v[i];
-    }
-  } else if (type == DT_BF16) {
-    __bf16* p = static_cast<__bf16*>(d) + off;
-    __bf16 h[4] = {static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1]), static_cast<__bf16>(v[2]),
-                   static_cast<__bf16>(v[3])};
-    if (rows >= 4 && (reinterpret_cast<uintptr_t>(p) & 7) == 0) {
-      *reinterpret_cast<v2i*>(p) = __builtin_bit_cast(v2i, h);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (i < rows) p[i] = h[i];
-    }
-  } else {  // DT_F16
-    _Float16* p = static_cast<_Float16*>(d) + off;
-    _Float16 h[4] = {static_cast<_Float16>(v[0]), static_cast<_Float16>(v[1]), static_cast<_Float16>(v[2]),
-                     static_cast<_Float16>(v[3])};
-    if (rows >= 4 && (reinterpret_cast<uintptr_t>(p) & 7) == 0) {
-      *reinterpret_cast<v2i*>(p) = __builtin_bit_cast(v2i, h);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (i < rows) p[i] = h[i];
-    }
-  }
-}
-
 // Rows m .. m+rows-1 (rows <= 8) of one column of a float-family matrix, as
 // floats; one or two 16-byte loads when all 8 are wanted and aligned.
 __device__ __forceinline__ void load8_f(const void* base, int type, int64_t off, int rows, float (&v)[8]) {
@@ -287,6 +252,66 @@ __device__ __forceinline__ void store8_i(void* base, int64_t off, const int (&v)
 // bounds by the callers); raw dword data, the gfx9 default format word.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), -1, 0x00020000);
+}
+
+// Buffer resource over `num` bytes at `base`: loads at or past the end read
+// zeros without touching memory, stores there are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_n(const void* base, int num) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), num, 0x00020000);
+}
+
+// 16-byte buffer load and store at the resource base + voffset + soffset.
+__device__ __forceinline__ v4i buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t vo, int so) {
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, 0));
+}
+__device__ __forceinline__ void buf_store16(v4i v, __amdgpu_buffer_rsrc_t r, uint32_t vo, int so) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), r, vo, so, 0);
+}
+
+// Bitwise select (a where m is set, else b): keeps a uniform type or flag
+// choice a per-lane select instead of a branch around each element.
+__device__ __forceinline__ unsigned bsel(unsigned m, unsigned a, unsigned b) { return (a & m) | (b & ~m); }
+
+// Eight packed 16-bit values as floats; `bf` is all ones for bf16, zero for
+// f16.
+__device__ __forceinline__ void unpack8(const v4i w, unsigned bf, float (&v)[8]) {
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const unsigned u = static_cast<unsigned>(w[r / 2]);
+    const unsigned hb = __builtin_bit_cast(
+        unsigned, static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(u >> (16 * (r & 1))))));
+    v[r] = __builtin_bit_cast(float, bsel(bf, (r & 1) ? (u & 0xffff0000u) : (u << 16), hb));
+  }
+}
+
+// Eight floats packed to bf16 or f16 (as for unpack8), rounded to nearest even.
+__device__ __forceinline__ v4i pack8(const float (&v)[8], unsigned bf) {
+  v4i w;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const unsigned b = static_cast<unsigned>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v[2 * q]))) |
+                       (static_cast<unsigned>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v[2 * q + 1]))) << 16);
+    const unsigned h = static_cast<unsigned>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(v[2 * q]))) |
+                       (static_cast<unsigned>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(v[2 * q + 1]))) << 16);
+    w[q] = static_cast<int>(bsel(bf, b, h));
+  }
+  return w;
+}
+
+// relu or gelu (EPI_* flags) on eight values: one uniform branch for gelu,
+// a select for relu.
+__device__ __forceinline__ void activate8(float (&t)[8], int flags) {
+  if (flags & EPI_GELU) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) t[r] = 0.5f * t[r] * (1.0f + erff(t[r] * 0.70710678118654752440f));
+  } else {
+    const unsigned m = (flags & EPI_RELU) ? ~0u : 0u;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const float z = t[r] > 0.0f ? t[r] : 0.0f;
+      t[r] = __builtin_bit_cast(float, bsel(m, __builtin_bit_cast(unsigned, z), __builtin_bit_cast(unsigned, t[r])));
+    }
+  }
 }
 
 // Direct buffer -> LDS load of W bytes per lane at base + voffset.
@@ -870,8 +895,10 @@ gemm_kernel(GemmArgs p) {
     });
     ep += (wave % WPS) * EPB;
   }
-  const int erow = (lane % LPC) * 8;  // first of this lane's 8 rows in a block
-  auto epilogue = [&](const int64_t em0, const int64_t en0) {
+  auto epilogue_gen = [&](const int64_t em0, const int64_t en0) {
+    int ln = lane;  // opaque copy, as in epilogue_vec below
+    asm volatile("" : "+v"(ln));
+    const int erow = (ln % LPC) * 8;
     static_for<(TM / ER) * FN>([&](auto pc) {
       // Block: rows ER*IR .. of the wave tile, column tile J, stored column by
       // column (ER*4 bytes each), 16-byte chunks XOR-swizzled by the column so
@@ -883,7 +910,7 @@ gemm_kernel(GemmArgs p) {
         const v16i a = __builtin_bit_cast(v16i, acc[IR * (ER / 32) + II][J]);
         static_for<4>([&](auto gc) {
           constexpr int G = decltype(gc)::value;
-          const int c = lane & 31, k = II * 8 + 2 * G + (lane >> 5);
+          const int c = ln & 31, k = II * 8 + 2 * G + (ln >> 5);
           const v4i val = {a[4 * G], a[4 * G + 1], a[4 * G + 2], a[4 * G + 3]};
           *reinterpret_cast<v4i*>(ep + c * (ER * 4) + ((k ^ (c & XM)) << 4)) = val;
         });
@@ -894,9 +921,9 @@ gemm_kernel(GemmArgs p) {
       asm volatile("" ::: "memory");
       const int64_t m = em0 + wm * TM + IR * ER + erow;
       for (int it = 0; it < 32 / CPI; ++it) {
-        const int c = it * CPI + lane / LPC;
+        const int c = it * CPI + ln / LPC;
         const int64_t n = en0 + wn * TN + J * 32 + c;
-        const int ch = 2 * (lane % LPC);
+        const int ch = 2 * (ln % LPC);
         const v4i lo = *reinterpret_cast<const v4i*>(ep + c * (ER * 4) + ((ch ^ (c & XM)) << 4));
         const v4i hi = *reinterpret_cast<const v4i*>(ep + c * (ER * 4) + (((ch + 1) ^ (c & XM)) << 4));
         if (n < p.n && m < p.m) {
@@ -945,6 +972,128 @@ gemm_kernel(GemmArgs p) {
       }
       asm volatile("" ::: "memory");
     });
+  };
+
+  // Interior tiles whose D (and C, bias) rows allow 16-byte vectors along M
+  // (host flag EPI_VEC, 16-bit C): the C and bias loads of a batch of EB
+  // runs are all issued before the batch's first block is staged, so a wave
+  // waits for memory once per batch rather than once per block.  C and D are
+  // addressed from the wave tile's corner: the lane's part in a VGPR, the
+  // run's part in an SGPR.
+  constexpr int NIT = 32 / CPI;         // iterations per block
+  constexpr int NBLK = (TM / ER) * FN;  // blocks per wave tile
+  constexpr int NU = NBLK * NIT;        // 8-row column runs per lane
+  constexpr int EB = NU < 16 ? NU : 16; // runs per batch (4 VGPRs each)
+  constexpr int BPB = EB / NIT;         // blocks per batch
+  static_assert(NU % EB == 0 && EB % NIT == 0, "whole blocks per batch");
+  auto epilogue_vec = [&](const int64_t em0, const int64_t en0) {
+    // The lane index passes through an opaque copy so that the per-lane
+    // addresses below are computed here rather than hoisted out of the tile
+    // loop and kept live (spilled) through the main loop.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int erow = (ln % LPC) * 8;
+    const int64_t tm0 = em0 + wm * TM, tn0 = en0 + wn * TN;
+    const int cl = ln / LPC;  // the lane's column within an iteration
+    const bool has_c = p.beta != 0.0f, has_bias = (p.flags & EPI_BIAS) != 0;
+    const bool bias32 = p.bias_type == DT_F32, d32 = p.d_type == DT_F32;
+    const unsigned c_bf = p.c_type == DT_BF16 ? ~0u : 0u, b_bf = p.bias_type == DT_BF16 ? ~0u : 0u;
+    const unsigned d_bf = p.d_type == DT_BF16 ? ~0u : 0u, b32 = bias32 ? ~0u : 0u;
+    // An absent C or bias is read through an empty resource: its loads
+    // return zeros, so every path issues the same loads and no wait depends
+    // on a branch.
+    const auto rc = make_rsrc_n(static_cast<const uint16_t*>(p.c) + (has_c ? tn0 * p.ldc + tm0 : 0), has_c ? -1 : 0);
+    const int ldcb = static_cast<int>(p.ldc) * 2;
+    const uint32_t vc = static_cast<uint32_t>(cl * ldcb + erow * 2);
+    const int bs = bias32 ? 4 : 2;
+    const uint8_t* bbase = static_cast<const uint8_t*>(p.bias) + (has_bias ? tm0 * bs : 0);
+    const auto rb = make_rsrc_n(bbase, has_bias ? -1 : 0), rb2 = make_rsrc_n(bbase, has_bias && bias32 ? -1 : 0);
+    const int ds = d32 ? 4 : 2;
+    const auto rd = make_rsrc(static_cast<uint8_t*>(p.d) + (tn0 * p.ldd + tm0) * ds);
+    const int lddb = static_cast<int>(p.ldd) * ds;
+    const uint32_t vd = static_cast<uint32_t>(cl * lddb + erow * ds);
+    static_for<NU / EB>([&](auto bc) {
+      constexpr int B0 = decltype(bc)::value * BPB;  // first block of the batch
+      constexpr int IR0 = B0 / FN, NIR = (B0 + BPB - 1) / FN - IR0 + 1;
+      v4i cv[EB];
+      v4i bv[NIR][2];
+      float bf[NIR][8] = {};
+      static_for<EB>([&](auto uc) {
+        constexpr int U = decltype(uc)::value, PS = B0 + U / NIT, IT = U % NIT, IR = PS / FN, J = PS % FN;
+        cv[U] = buf_load16(rc, vc, (J * 32 + IT * CPI) * ldcb + IR * ER * 2);
+      });
+      static_for<NIR>([&](auto irc) {
+        constexpr int R = decltype(irc)::value;
+        const uint32_t vo = static_cast<uint32_t>(erow * bs);
+        bv[R][0] = buf_load16(rb, vo, (IR0 + R) * ER * bs);
+        bv[R][1] = buf_load16(rb2, vo + 16, (IR0 + R) * ER * bs);
+      });
+      static_for<BPB>([&](auto pc) {
+        constexpr int PS = B0 + decltype(pc)::value, IR = PS / FN, J = PS % FN;
+        if (has_bias && (PS == B0 || J == 0)) {  // this row band's bias run, as floats
+          float b16[8];
+          unpack8(bv[IR - IR0][0], b_bf, b16);
+          const v4f b0 = __builtin_bit_cast(v4f, bv[IR - IR0][0]), b1 = __builtin_bit_cast(v4f, bv[IR - IR0][1]);
+#pragma unroll
+          for (int r = 0; r < 8; ++r)
+            bf[IR - IR0][r] = __builtin_bit_cast(
+                float, bsel(b32, __builtin_bit_cast(unsigned, r < 4 ? b0[r] : b1[r - 4]), __builtin_bit_cast(unsigned, b16[r])));
+        }
+        static_for<ER / 32>([&](auto iic) {
+          constexpr int II = decltype(iic)::value;
+          const v16i a = __builtin_bit_cast(v16i, acc[IR * (ER / 32) + II][J]);
+          static_for<4>([&](auto gc) {
+            constexpr int G = decltype(gc)::value;
+            const int c = ln & 31, k = II * 8 + 2 * G + (ln >> 5);
+            const v4i val = {a[4 * G], a[4 * G + 1], a[4 * G + 2], a[4 * G + 3]};
+            *reinterpret_cast<v4i*>(ep + c * (ER * 4) + ((k ^ (c & XM)) << 4)) = val;
+          });
+        });
+        asm volatile("" ::: "memory");
+        static_for<NIT>([&](auto ic) {
+          constexpr int IT = decltype(ic)::value, U = (PS - B0) * NIT + IT;
+          const int c = IT * CPI + cl, ch = 2 * (ln % LPC);
+          const v4f lo =
+              __builtin_bit_cast(v4f, *reinterpret_cast<const v4i*>(ep + c * (ER * 4) + ((ch ^ (c & XM)) << 4)));
+          const v4f hi = __builtin_bit_cast(
+              v4f, *reinterpret_cast<const v4i*>(ep + c * (ER * 4) + (((ch + 1) ^ (c & XM)) << 4)));
+          float t[8];
+#pragma unroll
+          for (int r = 0; r < 8; ++r) t[r] = p.alpha * (r < 4 ? lo[r] : hi[r - 4]);
+          if (has_c) {
+            float cf[8];
+            unpack8(cv[U], c_bf, cf);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) t[r] += p.beta * cf[r];
+          }
+          if (has_bias) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) t[r] += bf[IR - IR0][r];
+          }
+          activate8(t, p.flags);
+          const int so = (J * 32 + IT * CPI) * lddb + IR * ER * ds;
+          if (d32) {
+            buf_store16(__builtin_bit_cast(v4i, v4f{t[0], t[1], t[2], t[3]}), rd, vd, so);
+            buf_store16(__builtin_bit_cast(v4i, v4f{t[4], t[5], t[6], t[7]}), rd, vd + 16, so);
+          } else {
+            buf_store16(pack8(t, d_bf), rd, vd, so);
+          }
+        });
+        asm volatile("" ::: "memory");
+      });
+    });
+  };
+
+  auto epilogue = [&](const int64_t em0, const int64_t en0) {
+    if constexpr (!T::INT) {
+      // Without C or bias there is nothing to load, and the general path's
+      // stores are as good.
+      if ((p.flags & EPI_VEC) && (p.beta != 0.0f || (p.flags & EPI_BIAS)) && em0 + BM <= p.m && en0 + BN <= p.n) {
+        epilogue_vec(em0, en0);
+        return;
+      }
+    }
+    epilogue_gen(em0, en0);
   };
 
   // First stages of the current tile.

@@ -175,7 +175,7 @@ def _operand(x_logical: np.ndarray, fmt: str, op: str, ld: int):
 
 def make(kind: str, m: int, n: int, k: int, seed: int | None = None, *, op_a=None, op_b=None,
          lda=None, ldb=None, ldd=None, ldc=None, act=None, bias=None, beta=None,
-         type_d=None, alpha=1.0) -> Workload:
+         type_d=None, type_c=None, type_bias=None, alpha=1.0) -> Workload:
     """Build one of the five workload kinds at shape m x n x k.
 
     kinds: 'fp16'  fp16 T/N, U[-1,1], fp32 out, D = A.B
@@ -184,8 +184,8 @@ def make(kind: str, m: int, n: int, k: int, seed: int | None = None, *, op_a=Non
            'fp8'   e4m3 T/N, N(0,1) scaled per tensor to +-448, bf16 out, D = s_a s_b A.B
            'mxfp4' e2m1 T/N, N(0,1) MX-quantized per 32 K-elements, C bf16 N(0,1),
                    bf16 out, D = A.B + C
-    Keyword overrides change ops, leading dimensions and the epilogue for the
-    edge-case sweeps."""
+    Keyword overrides change ops, leading dimensions, the epilogue and the
+    float C, D and bias types for the edge-case sweeps."""
     defaults = {
         "fp16": dict(seed=1001, op_a="T", op_b="N", type_ab="f16", type_d="f32"),
         "bf16": dict(seed=1002, op_a="N", op_b="N", type_ab="bf16", type_d="bf16"),
@@ -215,18 +215,22 @@ def make(kind: str, m: int, n: int, k: int, seed: int | None = None, *, op_a=Non
             w["beta"] = 1.0 if beta is None else beta
             if use_c:
                 ldc = ldc or max(1, m)
-                w["c"], w["ldc"], w["type_c"] = store_colmajor(encode(_uniform(gc, (m, n)), "bf16"), ldc), ldc, "bf16"
+                tc = type_c or "bf16"
+                w["c"], w["ldc"], w["type_c"] = store_colmajor(encode(_uniform(gc, (m, n)), tc), ldc), ldc, tc
             w["act"] = "relu" if act is None else act
             if bias is None or bias:
-                w["bias"], w["type_bias"] = encode(_uniform(gbias, (m,)), "bf16"), "bf16"
+                tb = type_bias or "bf16"
+                w["bias"], w["type_bias"] = encode(_uniform(gbias, (m,)), tb), tb
         else:
             w["beta"] = 0.0 if beta is None else beta
             if w["beta"] != 0.0:
                 ldc = ldc or max(1, m)
-                w["c"], w["ldc"], w["type_c"] = store_colmajor(encode(_uniform(gc, (m, n)), "f32"), ldc), ldc, "f32"
+                tc = type_c or "f32"
+                w["c"], w["ldc"], w["type_c"] = store_colmajor(encode(_uniform(gc, (m, n)), tc), ldc), ldc, tc
             w["act"] = act or "none"
             if bias:
-                w["bias"], w["type_bias"] = encode(_uniform(gbias, (m,)), "f32"), "f32"
+                tb = type_bias or "f32"
+                w["bias"], w["type_bias"] = encode(_uniform(gbias, (m,)), tb), tb
     elif kind == "int8":
         xa = ga.integers(-128, 128, size=(m, k)).astype(np.float64)
         xb = gb.integers(-128, 128, size=(k, n)).astype(np.float64)
@@ -249,10 +253,12 @@ def make(kind: str, m: int, n: int, k: int, seed: int | None = None, *, op_a=Non
         w["beta"] = 0.0 if beta is None else beta
         if w["beta"] != 0.0:
             ldc = ldc or max(1, m)
-            w["c"], w["ldc"], w["type_c"] = store_colmajor(encode(gc.standard_normal((m, n)), "bf16"), ldc), ldc, "bf16"
+            tc = type_c or "bf16"
+            w["c"], w["ldc"], w["type_c"] = store_colmajor(encode(gc.standard_normal((m, n)), tc), ldc), ldc, tc
         w["act"] = act or "none"
         if bias:
-            w["bias"], w["type_bias"] = encode(gbias.standard_normal(m), "bf16"), "bf16"
+            tb = type_bias or "bf16"
+            w["bias"], w["type_bias"] = encode(gbias.standard_normal(m), tb), tb
     elif kind == "mxfp4":
         assert op_a == "T" and op_b == "N", "MX blocks run along the contiguous K"
         assert k % 32 == 0
@@ -275,10 +281,12 @@ def make(kind: str, m: int, n: int, k: int, seed: int | None = None, *, op_a=Non
         w["beta"] = 1.0 if beta is None else beta
         if w["beta"] != 0.0:
             ldc = ldc or max(1, m)
-            w["c"], w["ldc"], w["type_c"] = store_colmajor(encode(gc.standard_normal((m, n)), "bf16"), ldc), ldc, "bf16"
+            tc = type_c or "bf16"
+            w["c"], w["ldc"], w["type_c"] = store_colmajor(encode(gc.standard_normal((m, n)), tc), ldc), ldc, tc
         w["act"] = act or "none"
         if bias:
-            w["bias"], w["type_bias"] = encode(gbias.standard_normal(m), "bf16"), "bf16"
+            tb = type_bias or "bf16"
+            w["bias"], w["type_bias"] = encode(gbias.standard_normal(m), tb), tb
     else:
         raise ValueError(kind)
     return Workload(**w)
