@@ -298,22 +298,6 @@ __device__ __forceinline__ v4i pack8(const float (&v)[8], unsigned bf) {
   return w;
 }
 
-// relu or gelu (EPI_* flags) on eight values: one uniform branch for gelu,
-// a select for relu.
-__device__ __forceinline__ void activate8(float (&t)[8], int flags) {
-  if (flags & EPI_GELU) {
-#pragma unroll
-    for (int r = 0; r < 8; ++r) t[r] = 0.5f * t[r] * (1.0f + erff(t[r] * 0.70710678118654752440f));
-  } else {
-    const unsigned m = (flags & EPI_RELU) ? ~0u : 0u;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const float z = t[r] > 0.0f ? t[r] : 0.0f;
-      t[r] = __builtin_bit_cast(float, bsel(m, __builtin_bit_cast(unsigned, z), __builtin_bit_cast(unsigned, t[r])));
-    }
-  }
-}
-
 // Direct buffer -> LDS load of W bytes per lane at base + voffset.
 template <int W>
 __device__ __forceinline__ void load_lds_buf(__amdgpu_buffer_rsrc_t r, uint32_t voffset, void* lds) {
@@ -976,17 +960,40 @@ gemm_kernel(GemmArgs p) {
 
   // Interior tiles whose D (and C, bias) rows allow 16-byte vectors along M
   // (host flag EPI_VEC, 16-bit C): the C and bias loads of a batch of EB
-  // runs are all issued before the batch's first block is staged, so a wave
+  // runs are all issued before the batch's first block is read, so a wave
   // waits for memory once per batch rather than once per block.  C and D are
   // addressed from the wave tile's corner: the lane's part in a VGPR, the
-  // run's part in an SGPR.
+  // run's part in an SGPR.  The staging is pipelined: a block's runs are read
+  // from LDS all at once, then the next block is written while this one is
+  // computed and stored.
+  //   LD: C or bias is read (else neither is);  BF: C, D and bias are bf16.
+  // GELU takes the general path (its erf, copied into every run here, would
+  // no longer be inlined).
   constexpr int NIT = 32 / CPI;         // iterations per block
   constexpr int NBLK = (TM / ER) * FN;  // blocks per wave tile
   constexpr int NU = NBLK * NIT;        // 8-row column runs per lane
   constexpr int EB = NU < 16 ? NU : 16; // runs per batch (4 VGPRs each)
   constexpr int BPB = EB / NIT;         // blocks per batch
   static_assert(NU % EB == 0 && EB % NIT == 0, "whole blocks per batch");
-  auto epilogue_vec = [&](const int64_t em0, const int64_t en0) {
+  auto stage_block = [&](auto ps_tag, int ln) {
+    constexpr int PS = decltype(ps_tag)::value, IR = PS / FN, J = PS % FN;
+    static_for<ER / 32>([&](auto iic) {
+      constexpr int II = decltype(iic)::value;
+      const v16i a = __builtin_bit_cast(v16i, acc[IR * (ER / 32) + II][J]);
+      static_for<4>([&](auto gc) {
+        constexpr int G = decltype(gc)::value;
+        const int c = ln & 31, k = II * 8 + 2 * G + (ln >> 5);
+        const v4i val = {a[4 * G], a[4 * G + 1], a[4 * G + 2], a[4 * G + 3]};
+        *reinterpret_cast<v4i*>(ep + c * (ER * 4) + ((k ^ (c & XM)) << 4)) = val;
+      });
+    });
+    // Lanes read what other lanes of the wave wrote: the LDS executes a
+    // wave's accesses in order, so only the compiler must keep them in
+    // program order.
+    asm volatile("" ::: "memory");
+  };
+  auto epilogue_vec = [&](const int64_t em0, const int64_t en0, auto ld_tag, auto bf_tag) {
+    constexpr bool LD = decltype(ld_tag)::value, BF = decltype(bf_tag)::value;
     // The lane index passes through an opaque copy so that the per-lane
     // addresses below are computed here rather than hoisted out of the tile
     // loop and kept live (spilled) through the main loop.
@@ -996,12 +1003,12 @@ gemm_kernel(GemmArgs p) {
     const int64_t tm0 = em0 + wm * TM, tn0 = en0 + wn * TN;
     const int cl = ln / LPC;  // the lane's column within an iteration
     const bool has_c = p.beta != 0.0f, has_bias = (p.flags & EPI_BIAS) != 0;
-    const bool bias32 = p.bias_type == DT_F32, d32 = p.d_type == DT_F32;
+    const bool bias32 = p.bias_type == DT_F32, d32 = !BF && p.d_type == DT_F32;
     const unsigned c_bf = p.c_type == DT_BF16 ? ~0u : 0u, b_bf = p.bias_type == DT_BF16 ? ~0u : 0u;
     const unsigned d_bf = p.d_type == DT_BF16 ? ~0u : 0u, b32 = bias32 ? ~0u : 0u;
-    // An absent C or bias is read through an empty resource: its loads
-    // return zeros, so every path issues the same loads and no wait depends
-    // on a branch.
+    // An absent C or bias (with the other present) is read through an empty
+    // resource: its loads return zeros, so the loads do not depend on a
+    // branch and neither does any wait for them.
     const auto rc = make_rsrc_n(static_cast<const uint16_t*>(p.c) + (has_c ? tn0 * p.ldc + tm0 : 0), has_c ? -1 : 0);
     const int ldcb = static_cast<int>(p.ldc) * 2;
     const uint32_t vc = static_cast<uint32_t>(cl * ldcb + erow * 2);
@@ -1012,84 +1019,95 @@ gemm_kernel(GemmArgs p) {
     const auto rd = make_rsrc(static_cast<uint8_t*>(p.d) + (tn0 * p.ldd + tm0) * ds);
     const int lddb = static_cast<int>(p.ldd) * ds;
     const uint32_t vd = static_cast<uint32_t>(cl * lddb + erow * ds);
+    const float alpha = p.alpha, beta = p.beta;
+    const int flags = p.flags;
+    stage_block(std::integral_constant<int, 0>{}, ln);
     static_for<NU / EB>([&](auto bc) {
       constexpr int B0 = decltype(bc)::value * BPB;  // first block of the batch
       constexpr int IR0 = B0 / FN, NIR = (B0 + BPB - 1) / FN - IR0 + 1;
       v4i cv[EB];
       v4i bv[NIR][2];
-      float bf[NIR][8] = {};
-      static_for<EB>([&](auto uc) {
-        constexpr int U = decltype(uc)::value, PS = B0 + U / NIT, IT = U % NIT, IR = PS / FN, J = PS % FN;
-        cv[U] = buf_load16(rc, vc, (J * 32 + IT * CPI) * ldcb + IR * ER * 2);
-      });
-      static_for<NIR>([&](auto irc) {
-        constexpr int R = decltype(irc)::value;
-        const uint32_t vo = static_cast<uint32_t>(erow * bs);
-        bv[R][0] = buf_load16(rb, vo, (IR0 + R) * ER * bs);
-        bv[R][1] = buf_load16(rb2, vo + 16, (IR0 + R) * ER * bs);
-      });
+      float bf[NIR][8];
+      if constexpr (LD) {
+        static_for<EB>([&](auto uc) {
+          constexpr int U = decltype(uc)::value, PS = B0 + U / NIT, IT = U % NIT, IR = PS / FN, J = PS % FN;
+          cv[U] = buf_load16(rc, vc, (J * 32 + IT * CPI) * ldcb + IR * ER * 2);
+        });
+        static_for<NIR>([&](auto irc) {
+          constexpr int R = decltype(irc)::value;
+          const uint32_t vo = static_cast<uint32_t>(erow * bs);
+          bv[R][0] = buf_load16(rb, vo, (IR0 + R) * ER * bs);
+          if constexpr (!BF) bv[R][1] = buf_load16(rb2, vo + 16, (IR0 + R) * ER * bs);
+        });
+      }
       static_for<BPB>([&](auto pc) {
         constexpr int PS = B0 + decltype(pc)::value, IR = PS / FN, J = PS % FN;
-        if (has_bias && (PS == B0 || J == 0)) {  // this row band's bias run, as floats
-          float b16[8];
-          unpack8(bv[IR - IR0][0], b_bf, b16);
-          const v4f b0 = __builtin_bit_cast(v4f, bv[IR - IR0][0]), b1 = __builtin_bit_cast(v4f, bv[IR - IR0][1]);
+        if constexpr (LD) {
+          if (PS == B0 || J == 0) {  // this row band's bias run, as floats (zeros if absent)
+            float b16[8];
+            unpack8(bv[IR - IR0][0], BF ? ~0u : b_bf, b16);
+            if constexpr (BF) {
 #pragma unroll
-          for (int r = 0; r < 8; ++r)
-            bf[IR - IR0][r] = __builtin_bit_cast(
-                float, bsel(b32, __builtin_bit_cast(unsigned, r < 4 ? b0[r] : b1[r - 4]), __builtin_bit_cast(unsigned, b16[r])));
+              for (int r = 0; r < 8; ++r) bf[IR - IR0][r] = b16[r];
+            } else {
+              const v4f b0 = __builtin_bit_cast(v4f, bv[IR - IR0][0]), b1 = __builtin_bit_cast(v4f, bv[IR - IR0][1]);
+#pragma unroll
+              for (int r = 0; r < 8; ++r)
+                bf[IR - IR0][r] = __builtin_bit_cast(float, bsel(b32, __builtin_bit_cast(unsigned, r < 4 ? b0[r] : b1[r - 4]),
+                                                                 __builtin_bit_cast(unsigned, b16[r])));
+            }
+          }
         }
-        static_for<ER / 32>([&](auto iic) {
-          constexpr int II = decltype(iic)::value;
-          const v16i a = __builtin_bit_cast(v16i, acc[IR * (ER / 32) + II][J]);
-          static_for<4>([&](auto gc) {
-            constexpr int G = decltype(gc)::value;
-            const int c = ln & 31, k = II * 8 + 2 * G + (ln >> 5);
-            const v4i val = {a[4 * G], a[4 * G + 1], a[4 * G + 2], a[4 * G + 3]};
-            *reinterpret_cast<v4i*>(ep + c * (ER * 4) + ((k ^ (c & XM)) << 4)) = val;
-          });
+        // this block's runs from LDS, then the next block into LDS
+        v4f lo[NIT], hi[NIT];
+        static_for<NIT>([&](auto ic) {
+          constexpr int IT = decltype(ic)::value;
+          const int c = IT * CPI + cl, ch = 2 * (ln % LPC);
+          lo[IT] = __builtin_bit_cast(v4f, *reinterpret_cast<const v4i*>(ep + c * (ER * 4) + ((ch ^ (c & XM)) << 4)));
+          hi[IT] = __builtin_bit_cast(v4f, *reinterpret_cast<const v4i*>(ep + c * (ER * 4) + (((ch + 1) ^ (c & XM)) << 4)));
         });
         asm volatile("" ::: "memory");
+        if constexpr (PS + 1 < NBLK) stage_block(std::integral_constant<int, PS + 1>{}, ln);
         static_for<NIT>([&](auto ic) {
           constexpr int IT = decltype(ic)::value, U = (PS - B0) * NIT + IT;
-          const int c = IT * CPI + cl, ch = 2 * (ln % LPC);
-          const v4f lo =
-              __builtin_bit_cast(v4f, *reinterpret_cast<const v4i*>(ep + c * (ER * 4) + ((ch ^ (c & XM)) << 4)));
-          const v4f hi = __builtin_bit_cast(
-              v4f, *reinterpret_cast<const v4i*>(ep + c * (ER * 4) + (((ch + 1) ^ (c & XM)) << 4)));
           float t[8];
 #pragma unroll
-          for (int r = 0; r < 8; ++r) t[r] = p.alpha * (r < 4 ? lo[r] : hi[r - 4]);
-          if (has_c) {
+          for (int r = 0; r < 8; ++r) t[r] = alpha * (r < 4 ? lo[IT][r] : hi[IT][r - 4]);
+          if constexpr (LD) {
             float cf[8];
-            unpack8(cv[U], c_bf, cf);
+            unpack8(cv[U], BF ? ~0u : c_bf, cf);
 #pragma unroll
-            for (int r = 0; r < 8; ++r) t[r] += p.beta * cf[r];
+            for (int r = 0; r < 8; ++r) t[r] = (t[r] + beta * cf[r]) + bf[IR - IR0][r];
           }
-          if (has_bias) {
+          if (flags & EPI_RELU) {  // gelu takes the general path
 #pragma unroll
-            for (int r = 0; r < 8; ++r) t[r] += bf[IR - IR0][r];
+            for (int r = 0; r < 8; ++r) t[r] = t[r] > 0.0f ? t[r] : 0.0f;
           }
-          activate8(t, p.flags);
           const int so = (J * 32 + IT * CPI) * lddb + IR * ER * ds;
           if (d32) {
             buf_store16(__builtin_bit_cast(v4i, v4f{t[0], t[1], t[2], t[3]}), rd, vd, so);
             buf_store16(__builtin_bit_cast(v4i, v4f{t[4], t[5], t[6], t[7]}), rd, vd + 16, so);
           } else {
-            buf_store16(pack8(t, d_bf), rd, vd, so);
+            buf_store16(pack8(t, BF ? ~0u : d_bf), rd, vd, so);
           }
         });
-        asm volatile("" ::: "memory");
       });
     });
   };
 
   auto epilogue = [&](const int64_t em0, const int64_t en0) {
     if constexpr (!T::INT) {
-      // Without C or bias there is nothing to load, and the general path's
-      // stores are as good.
-      if ((p.flags & EPI_VEC) && (p.beta != 0.0f || (p.flags & EPI_BIAS)) && em0 + BM <= p.m && en0 + BN <= p.n) {
-        epilogue_vec(em0, en0);
+      if ((p.flags & EPI_VEC) && !(p.flags & EPI_GELU) && em0 + BM <= p.m && en0 + BN <= p.n) {
+        const bool has_c = p.beta != 0.0f, has_bias = (p.flags & EPI_BIAS) != 0;
+        const bool bf = (!has_c || p.c_type == DT_BF16) && p.d_type == DT_BF16 &&
+                        (!has_bias || p.bias_type == DT_BF16);
+        if (!bf) {
+          epilogue_vec(em0, en0, std::true_type{}, std::false_type{});
+        } else if (has_c || has_bias) {
+          epilogue_vec(em0, en0, std::true_type{}, std::true_type{});
+        } else {
+          epilogue_vec(em0, en0, std::false_type{}, std::true_type{});
+        }
         return;
       }
     }
