@@ -18,7 +18,8 @@ def test_map_names_are_all_known():
     for n in names:
         pts = [(0, 0)]
         params = {"xcd_remap": (8,), "grouped_tile": (4, 4, 2), "copy_source": (16,),
-                  "mfma32_operand": (8,), "mm_lds_offset": (256,), "mm_copy_source": (16, 256)}.get(n, ())
+                  "mfma32_operand": (8,), "mm_lds_offset": (256,), "mm_copy_source": (16, 256),
+                  "pair_lds_offset": (0,)}.get(n, ())
         thl.thl_kernel_index_map(n, pts, params)
     with pytest.raises(thl.ThlError):
         thl.thl_kernel_index_map("no_such_map", [(0, 0)])
@@ -193,3 +194,58 @@ def test_transposed_reads_spread_over_banks(pitch):
                         (o, _), = thl.thl_kernel_index_map("mm_lds_offset", [(k + 16 * ks, 2 * (r0 + m))], (pitch,))
                         banks += [(o % 256) // 4, (o % 256) // 4 + 1]
                     assert len(set(banks)) == 32
+
+
+# ------------------------------------------------------------ paired stages
+
+def test_pair_layout_is_a_bijection_of_two_stages():
+    # Stages 2j and 2j+1 of 256 rows x 64 bytes fill one 32 KB pair buffer
+    # exactly once between them.
+    rows = 256
+    offs = []
+    for odd in (0, 1):
+        pts = [(r, b) for r in range(rows) for b in range(ROW)]
+        offs += [o for o, _ in thl.thl_kernel_index_map("pair_lds_offset", pts, (odd,))]
+    assert sorted(offs) == list(range(2 * rows * ROW))
+
+
+def test_pair_rows_keep_the_chunk_swizzle():
+    # Inside a row the bytes sit exactly as in a single stage; rows move by
+    # whole 512-byte halves of a 1 KB group, so the bank of every byte is
+    # unchanged (512 is a multiple of the 256-byte bank window).
+    for odd in (0, 1):
+        pts = [(r, b) for r in range(0, 256, 3) for b in range(0, ROW, 4)]
+        pair = thl.thl_kernel_index_map("pair_lds_offset", pts, (odd,))
+        single = thl.thl_kernel_index_map("lds_offset", pts)
+        for (po, _), (so, _), (r, _b) in zip(pair, single, pts):
+            assert po - so == (r >> 3) * 512 + odd * 512
+            assert po % 256 == so % 256
+
+
+def test_pair_copy_source_inverts_the_pair_layout_with_whole_lines():
+    # Lane l of the copy for 1 KB group g writes LDS bytes 1024 g + 16 l ..;
+    # the (row, byte of the pair's 128) it fetches must be stored exactly
+    # there, and one instruction reads 8 whole 128-byte rows (cache lines).
+    for g in range(32):
+        got = thl.thl_kernel_index_map("pair_copy_source", [(g, lane) for lane in range(64)])
+        back = []
+        for r, b in got:
+            back.append(thl.thl_kernel_index_map("pair_lds_offset", [(r, b % 64)], (b // 64,))[0][0])
+        assert back == [1024 * g + 16 * lane for lane in range(64)]
+        rows = {}
+        for r, b in got:
+            rows.setdefault(r, []).extend(range(b, b + 16))
+        assert sorted(rows) == list(range(8 * g, 8 * g + 8))
+        assert all(sorted(v) == list(range(128)) for v in rows.values())
+
+
+def test_pair_copy_lane_part_is_the_same_for_every_group_of_a_wave():
+    # A wave copies groups wave, wave + 4, wave + 8, ...: the lane's byte in
+    # the pair is the same for all of them (the swizzle repeats every 4
+    # groups), so one per-lane offset plus a uniform row step serves all.
+    for wave in range(4):
+        first = thl.thl_kernel_index_map("pair_copy_source", [(wave, lane) for lane in range(64)])
+        for j in range(1, 8):
+            g = 4 * j + wave
+            got = thl.thl_kernel_index_map("pair_copy_source", [(g, lane) for lane in range(64)])
+            assert [(r - 8 * g, b) for r, b in got] == [(r - 8 * wave, b) for r, b in first]

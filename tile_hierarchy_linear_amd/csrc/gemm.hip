@@ -338,7 +338,7 @@ thl_status thl_gemm(int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
 
 const char* thl_kernel_index_map_names(void) {
   return "xcd_remap,grouped_tile,swz,lds_offset,copy_source,mfma32_operand,mfma32_acc,fp8_32x32_k,tr16_source,"
-         "mm_lds_offset,mm_copy_source,tr16_operand";
+         "mm_lds_offset,mm_copy_source,tr16_operand,pair_lds_offset,pair_copy_source";
 }
 
 int thl_kernel_index_map(const char* map, const int64_t* params, int64_t n, const int64_t* in, int64_t* out) {
@@ -377,6 +377,11 @@ int thl_kernel_index_map(const char* map, const int64_t* params, int64_t n, cons
       maps::mm_copy_source(x, y, param(0), param(1), &r0, &r1);
     } else if (!std::strcmp(map, "tr16_operand")) {
       maps::tr16_operand(x, y, &r0, &r1);
+    } else if (!std::strcmp(map, "pair_lds_offset")) {
+      if (!params || (param(0) != 0 && param(0) != 1)) return THL_ERR_INVALID;
+      r0 = maps::pair_lds_offset(x, y, param(0));
+    } else if (!std::strcmp(map, "pair_copy_source")) {
+      maps::pair_copy_source(x, y, &r0, &r1);
     } else {
       return THL_ERR_INVALID;
     }

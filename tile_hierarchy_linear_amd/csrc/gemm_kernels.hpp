@@ -420,14 +420,31 @@ gemm_kernel(GemmArgs p) {
                 "copies must split evenly over waves");
   static_assert(STAGES >= 3 && STAGES <= 6, "three to six stages");
   static_assert((VM_STAGE + SC_LOADS) * (STAGES - 2) < 64, "vmcnt range");
+  // Paired stages (four buffers, 16-byte copies): stages 2j and 2j+1 share a
+  // buffer pair and go out together, in the step before 2j-1, so that every
+  // copy of a K-major operand reads whole 128-byte lines (maps::pair_*).  The
+  // pair's buffers are free once stage 2j-1 has been read, and stage 2j is
+  // first read two steps later, as with single stages.
+  constexpr bool PAIR = STAGES == 4 && LOADW == 16;
+  static_assert(!PAIR || NW % 4 == 0, "a wave's pair copies keep one chunk swizzle");
+  constexpr int RSTEP = PAIR ? 2 * KB : KB;  // LDS bytes per K-major row of an 8-row group
   // Steps per unrolled loop body: ring slots, fragment-slot parities and (fp4)
   // the scale-group buffer and position are compile-time constants inside it.
   constexpr int UNROLL = T::SCALED ? (STAGES % (2 * SG) == 0 ? STAGES : (STAGES % SG == 0 ? 2 * STAGES : 0))
                                    : ((STAGES % 2 == 0) ? STAGES : 2 * STAGES);
   static_assert(UNROLL > 0, "scale groups need STAGES to divide into 4 K-step groups");
+  // Copies per wave issued in phase B of the step at position pos: paired,
+  // odd steps issue stages pos+3 and pos+4 (with the scale group when pos+3
+  // starts one), even steps none; otherwise every step issues stage pos+3.
+  auto issued_at = [](int pos) constexpr {
+    if constexpr (PAIR) return (pos % 2 != 0) ? 2 * COPIES + ((pos + 3) % SG == 0 ? SC_LOADS : 0) : 0;
+    return COPIES + ((pos + STAGES - 1) % SG == 0 ? SC_LOADS : 0);
+  };
   // Copies per wave younger than stage pos+1 when waiting for it at step pos
-  // (stages pos+2 .. pos+STAGES-2 may still be in flight).
+  // (single: stages pos+2 .. pos+STAGES-2 may still be in flight; paired:
+  // the pair issued at step pos-1 when stage pos+1 is odd).
   auto younger = [](int pos) constexpr {
+    if constexpr (PAIR) return (pos % 2 == 0) ? 2 * COPIES + ((pos + 2) % SG == 0 ? SC_LOADS : 0) : 0;
     int n = 0;
     for (int q = pos + 2; q <= pos + STAGES - 2; ++q) n += COPIES + (q % SG == 0 ? SC_LOADS : 0);
     return n;
@@ -438,7 +455,36 @@ gemm_kernel(GemmArgs p) {
   static_assert(AK || PA % 256 == 0, "M-major k-rows are whole 256-byte bank windows");
   static_assert(BK || PB % 256 == 0, "N-major k-rows are whole 256-byte bank windows");
 
-  auto slot = [](auto i_tag) -> uint8_t* { return ring_slot<STAGE, decltype(i_tag)::value>(); };
+  // Paired: two buffer pairs of 2*STAGE bytes (A's two stages, then B's);
+  // slot(i) is then the i-th STAGE bytes of the ring, for raw staging only.
+  auto pair_buf = [](auto j_tag) -> uint8_t* { return ring_slot<2 * STAGE, decltype(j_tag)::value>(); };
+  auto slot = [&](auto i_tag) -> uint8_t* {
+    constexpr int I = decltype(i_tag)::value;
+    if constexpr (PAIR) {
+      return pair_buf(std::integral_constant<int, I / 2>{}) + (I % 2) * STAGE;
+    } else {
+      return ring_slot<STAGE, I>();
+    }
+  };
+  // Operand bases of the stage held in buffer I: K-major stages of a pair
+  // interleave by 8-row groups (the odd one 512 bytes in), M-major ones
+  // follow each other.
+  auto a_stage = [&](auto i_tag) -> uint8_t* {
+    constexpr int I = decltype(i_tag)::value;
+    if constexpr (PAIR) {
+      return pair_buf(std::integral_constant<int, I / 2>{}) + (I % 2) * (AK ? 512 : A_BYTES);
+    } else {
+      return slot(i_tag);
+    }
+  };
+  auto b_stage = [&](auto i_tag) -> uint8_t* {
+    constexpr int I = decltype(i_tag)::value;
+    if constexpr (PAIR) {
+      return pair_buf(std::integral_constant<int, I / 2>{}) + 2 * A_BYTES + (I % 2) * (BK ? 512 : B_BYTES);
+    } else {
+      return slot(i_tag) + A_BYTES;
+    }
+  };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
 
@@ -462,6 +508,10 @@ gemm_kernel(GemmArgs p) {
   const uint8_t* a_tile = p.a;
   const uint8_t* b_tile = p.b;
   uint32_t a_off[A_LOADS], b_off[B_LOADS];
+  // Paired K-major copies: the lane's offset for instruction 0 (rows of the
+  // wave's first 8-row group); instruction j is 8*NW*j rows further.  Rows
+  // past M (N) are cut off by the buffer resource's size instead of clamped.
+  uint32_t a_lp = 0, b_lp = 0;
   uint32_t sc_src[T::SCALED ? SC_LOADS : 1];
   bool sc_a[T::SCALED ? SC_LOADS : 1];
   int sc_dst[T::SCALED ? SC_LOADS : 1];
@@ -501,6 +551,12 @@ gemm_kernel(GemmArgs p) {
         if (n0 + (byte & ~15) / 2 >= p.n) byte &= 15;
         b_off[j] = static_cast<uint32_t>(row * p.ldb_bytes + byte);
       }
+    }
+    if constexpr (PAIR) {
+      int64_t row, byte;
+      maps::pair_copy_source(wave, lane, &row, &byte);
+      if constexpr (AK) a_lp = static_cast<uint32_t>(row * p.lda_bytes + byte);
+      if constexpr (BK) b_lp = static_cast<uint32_t>(row * p.ldb_bytes + byte);
     }
     if constexpr (T::SCALED) {
 #pragma unroll
@@ -561,12 +617,83 @@ gemm_kernel(GemmArgs p) {
     static_for<vm_of(decltype(pos_tag)::value)>([&](auto vc) { issue_one(vc, buf_tag, pos_tag, kt, ra, rb); });
   };
 
+  // Paired copies.  The K-major sources of the pair whose first stage is s0:
+  // a resource from the pair's first byte of the tile, sized to end at the
+  // operand's last valid byte (rows past M read zeros).
+  auto pair_src = [&](int s0, __amdgpu_buffer_rsrc_t& ra, __amdgpu_buffer_rsrc_t& rb) {
+    const int64_t kb = static_cast<int64_t>(s0) * KB;
+    if constexpr (AK) {
+      int64_t na = (p.m - 1 - m0) * p.lda_bytes + p.kbytes - kb;
+      na = na < BM * p.lda_bytes ? na : BM * p.lda_bytes;
+      ra = make_rsrc_n(a_tile + kb, static_cast<int>(na > 0 ? na : 0));
+    } else {
+      ra = make_rsrc(a_tile);
+    }
+    if constexpr (BK) {
+      int64_t nb = (p.n - 1 - n0) * p.ldb_bytes + p.kbytes - kb;
+      nb = nb < BN * p.ldb_bytes ? nb : BN * p.ldb_bytes;
+      rb = make_rsrc_n(b_tile + kb, static_cast<int>(nb > 0 ? nb : 0));
+    } else {
+      rb = make_rsrc(b_tile);
+    }
+  };
+  // Copies per wave of the pair whose first stage sits at position pos.
+  auto pair_count = [](int pos) constexpr { return 2 * COPIES + (pos % SG == 0 ? SC_LOADS : 0); };
+  // A pair's copies go out over the MFMAs of phase B of the odd step before
+  // it and phase A of the next (even) step, in proportion to their MFMAs:
+  // the first pair_first(pos) in phase B, the rest in phase A.
+  constexpr int NMA = (KSUB == 2 ? FM : (FM >= 4 ? FM / 4 : FM / 2)) * FN;
+  constexpr int NMB = (KSUB == 2 ? FM : FM - (FM >= 4 ? FM / 4 : FM / 2)) * FN;
+  auto pair_first = [](int pos) constexpr {
+    return (2 * COPIES + (pos % SG == 0 ? SC_LOADS : 0)) * NMB / (NMA + NMB);
+  };
+  // Copy V of the pair (stage s0 at position POS, s0+1) into buffer pair BUF:
+  // the scale copies first when POS starts a group, then A's, then B's.
+  // K-major: one 1 KB group of 8 rows x 128 bytes per instruction; M-major:
+  // each stage's copies as for single stages (k-rows of whole lines already).
+  auto issue_pair_one = [&](auto v_tag, auto buf_tag, auto pos_tag, int s0, __amdgpu_buffer_rsrc_t ra,
+                            __amdgpu_buffer_rsrc_t rb) {
+    constexpr int V = decltype(v_tag)::value, BUF = decltype(buf_tag)::value, POS = decltype(pos_tag)::value;
+    constexpr int NS = pair_count(POS) - 2 * COPIES;
+    uint8_t* pa = pair_buf(std::integral_constant<int, BUF>{});
+    uint8_t* pb = pa + 2 * A_BYTES;
+    if constexpr (V < NS) {
+      issue_scale(V, s0 / SG, sgbuf(std::integral_constant<int, (POS / SG) % 2>{}));
+    } else if constexpr (V < NS + 2 * A_LOADS) {
+      constexpr int J = V - NS;
+      if constexpr (AK) {
+        load_lds_buf<16>(ra, a_lp + static_cast<uint32_t>(J * 8 * NW) * static_cast<uint32_t>(p.lda_bytes),
+                         pa + (J * NW + wave) * 1024);
+      } else {
+        constexpr int H = J / A_LOADS, JJ = J % A_LOADS;
+        const int s = s0 + H < nkf ? s0 + H : nkf - 1;
+        load_lds_buf<LOADW>(make_rsrc(a_tile + s * a_step), a_off[JJ], pa + H * A_BYTES + (JJ * NW + wave) * 64 * LOADW);
+      }
+    } else {
+      constexpr int J = V - NS - 2 * A_LOADS;
+      if constexpr (BK) {
+        load_lds_buf<16>(rb, b_lp + static_cast<uint32_t>(J * 8 * NW) * static_cast<uint32_t>(p.ldb_bytes),
+                         pb + (J * NW + wave) * 1024);
+      } else {
+        constexpr int H = J / B_LOADS, JJ = J % B_LOADS;
+        const int s = s0 + H < nkf ? s0 + H : nkf - 1;
+        load_lds_buf<LOADW>(make_rsrc(b_tile + s * b_step), b_off[JJ], pb + H * B_BYTES + (JJ * NW + wave) * 64 * LOADW);
+      }
+    }
+  };
+  // Every copy of the pair whose first stage is s0 (position POS) into BUF.
+  auto issue_pair_full = [&](int s0, auto buf_tag, auto pos_tag) {
+    __amdgpu_buffer_rsrc_t ra, rb;
+    pair_src(s0, ra, rb);
+    static_for<pair_count(decltype(pos_tag)::value)>([&](auto vc) { issue_pair_one(vc, buf_tag, pos_tag, s0, ra, rb); });
+  };
+
   // The partial last K-step into slot 0: K-major bytes at or past K read the
   // row's first byte instead, M-major k-rows at or past K read the step's
   // first k-row (masked before the MFMAs).
   auto issue_partial = [&](int kt) {
-    uint8_t* sa = slot(std::integral_constant<int, 0>{});
-    uint8_t* sb = sa + A_BYTES;
+    uint8_t* sa = a_stage(I0{});
+    uint8_t* sb = b_stage(I0{});
     const int64_t kofs = static_cast<int64_t>(kt) * KB;
     if constexpr (T::SCALED) {
       uint8_t* gb = ((kt / SG) & 1) ? sgbuf(I1{}) : sgbuf(I0{});
@@ -576,8 +703,19 @@ gemm_kernel(GemmArgs p) {
     // K-major: offsets from the tile base; M-major: from the step's first k-row.
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(AK ? a_tile : a_tile + kt * a_step);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(BK ? b_tile : b_tile + kt * b_step);
+    if constexpr (PAIR && AK) {
+      // paired layout: 8-row groups of 128 bytes (the odd half unused)
 #pragma unroll
-    for (int j = 0; j < A_LOADS; ++j) {
+      for (int j = 0; j < 2 * A_LOADS; ++j) {
+        int64_t row, byte;
+        maps::pair_copy_source(j * NW + wave, lane, &row, &byte);
+        const int64_t r = m0 + row < p.m ? row : p.m - 1 - m0;
+        const int64_t off = r * p.lda_bytes + (kofs + byte < p.kbytes ? kofs + byte : 0);
+        load_lds_buf<16>(ra, static_cast<uint32_t>(off), sa + (j * NW + wave) * 1024);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < ((PAIR && AK) ? 0 : A_LOADS); ++j) {
       int64_t row, byte, off;
       if constexpr (AK) {
         maps::copy_source((j * NW + wave) * 64 * LOADW, lane, LOADW, &row, &byte);
@@ -589,8 +727,18 @@ gemm_kernel(GemmArgs p) {
       }
       load_lds_buf<LOADW>(ra, static_cast<uint32_t>(off), sa + (j * NW + wave) * 64 * LOADW);
     }
+    if constexpr (PAIR && BK) {
 #pragma unroll
-    for (int j = 0; j < B_LOADS; ++j) {
+      for (int j = 0; j < 2 * B_LOADS; ++j) {
+        int64_t row, byte;
+        maps::pair_copy_source(j * NW + wave, lane, &row, &byte);
+        const int64_t r = n0 + row < p.n ? row : p.n - 1 - n0;
+        const int64_t off = r * p.ldb_bytes + (kofs + byte < p.kbytes ? kofs + byte : 0);
+        load_lds_buf<16>(rb, static_cast<uint32_t>(off), sb + (j * NW + wave) * 1024);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < ((PAIR && BK) ? 0 : B_LOADS); ++j) {
       int64_t row, byte, off;
       if constexpr (BK) {
         maps::copy_source((j * NW + wave) * 64 * LOADW, lane, LOADW, &row, &byte);
@@ -620,8 +768,11 @@ gemm_kernel(GemmArgs p) {
   for (int ks = 0; ks < KSUB; ++ks)
 #pragma unroll
     for (int c = 0; c < LC; ++c)
-      chunk_off[ks][c] = static_cast<int>(maps::lds_offset(lrow, chunk_of(ks, lane >> 5, c) * 16));
-  const int a_wave_off = wm * TM * KB, b_wave_off = A_BYTES + wn * TN * KB;
+      chunk_off[ks][c] = static_cast<int>(maps::lds_offset(lrow, chunk_of(ks, lane >> 5, c) * 16)) +
+                         (PAIR ? (lrow >> 3) * 512 : 0);
+  // K-major fragment rows start at multiples of 32, where a row's offset is
+  // RSTEP bytes per row (paired stages interleave by 8-row groups).
+  const int a_wave_off = wm * TM * RSTEP, b_wave_off = wn * TN * RSTEP;
 
   v4i af[2][FM][LC], bf[2][FN][LC];  // fragment slots: (kt*KSUB + ks) & 1
 
@@ -667,18 +818,20 @@ gemm_kernel(GemmArgs p) {
     return __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3);
   };
 
-  auto read = [&](const uint8_t* stage, auto ks_tag, auto slot_tag, int kvalid) {
+  auto read = [&](auto stage_tag, auto ks_tag, auto slot_tag, int kvalid) {
     constexpr int KS = decltype(ks_tag)::value, SL = decltype(slot_tag)::value;
+    const uint8_t* sa = a_stage(stage_tag);
+    const uint8_t* sb = b_stage(stage_tag);
 #pragma unroll
     for (int f = 0; f < FM; ++f) {
       if constexpr (AK) {
 #pragma unroll
         for (int c = 0; c < LC; ++c) {
-          af[SL][f][c] = *reinterpret_cast<const v4i*>(stage + a_wave_off + f * 32 * KB + chunk_off[KS][c]);
+          af[SL][f][c] = *reinterpret_cast<const v4i*>(sa + a_wave_off + f * 32 * RSTEP + chunk_off[KS][c]);
           if (kvalid < KB) af[SL][f][c] = mask_bytes(af[SL][f][c], kvalid - chunk_of(KS, lane >> 5, c) * 16);
         }
       } else {
-        af[SL][f][0] = read_mm(stage, PA, wm * TM + f * 32, ks_tag, kvalid / 2);
+        af[SL][f][0] = read_mm(sa, PA, wm * TM + f * 32, ks_tag, kvalid / 2);
       }
     }
 #pragma unroll
@@ -686,11 +839,11 @@ gemm_kernel(GemmArgs p) {
       if constexpr (BK) {
 #pragma unroll
         for (int c = 0; c < LC; ++c) {
-          bf[SL][f][c] = *reinterpret_cast<const v4i*>(stage + b_wave_off + f * 32 * KB + chunk_off[KS][c]);
+          bf[SL][f][c] = *reinterpret_cast<const v4i*>(sb + b_wave_off + f * 32 * RSTEP + chunk_off[KS][c]);
           if (kvalid < KB) bf[SL][f][c] = mask_bytes(bf[SL][f][c], kvalid - chunk_of(KS, lane >> 5, c) * 16);
         }
       } else {
-        bf[SL][f][0] = read_mm(stage + A_BYTES, PB, wn * TN + f * 32, ks_tag, kvalid / 2);
+        bf[SL][f][0] = read_mm(sb, PB, wn * TN + f * 32, ks_tag, kvalid / 2);
       }
     }
   };
@@ -740,7 +893,7 @@ gemm_kernel(GemmArgs p) {
   // One fragment of sub-step KS into fragment slot SL: R = 0 is A's first
   // row tile, 1 .. FN are B's column tiles, FN+1 .. are A's other row tiles
   // (the order the MFMAs of a phase consume them).
-  auto read_one = [&](auto r_tag, auto ks_tag, auto slot_tag, const uint8_t* stage) {
+  auto read_one = [&](auto r_tag, auto ks_tag, auto slot_tag, auto stage_tag) {
     constexpr int R = decltype(r_tag)::value, KS = decltype(ks_tag)::value, SL = decltype(slot_tag)::value;
     constexpr bool IS_A = R == 0 || R > FN;
     constexpr int FI = R == 0 ? 0 : (IS_A ? R - FN : R - 1);
@@ -748,17 +901,19 @@ gemm_kernel(GemmArgs p) {
       if constexpr (AK) {
 #pragma unroll
         for (int c = 0; c < LC; ++c)
-          af[SL][FI][c] = *reinterpret_cast<const v4i*>(stage + a_wave_off + FI * 32 * KB + chunk_off[KS][c]);
+          af[SL][FI][c] =
+              *reinterpret_cast<const v4i*>(a_stage(stage_tag) + a_wave_off + FI * 32 * RSTEP + chunk_off[KS][c]);
       } else {
-        af[SL][FI][0] = read_mm(stage, PA, wm * TM + FI * 32, ks_tag, 32);
+        af[SL][FI][0] = read_mm(a_stage(stage_tag), PA, wm * TM + FI * 32, ks_tag, 32);
       }
     } else {
       if constexpr (BK) {
 #pragma unroll
         for (int c = 0; c < LC; ++c)
-          bf[SL][FI][c] = *reinterpret_cast<const v4i*>(stage + b_wave_off + FI * 32 * KB + chunk_off[KS][c]);
+          bf[SL][FI][c] =
+              *reinterpret_cast<const v4i*>(b_stage(stage_tag) + b_wave_off + FI * 32 * RSTEP + chunk_off[KS][c]);
       } else {
-        bf[SL][FI][0] = read_mm(stage + A_BYTES, PB, wn * TN + FI * 32, ks_tag, 32);
+        bf[SL][FI][0] = read_mm(b_stage(stage_tag), PB, wn * TN + FI * 32, ks_tag, 32);
       }
     }
   };
@@ -781,7 +936,7 @@ gemm_kernel(GemmArgs p) {
     constexpr int SA = KSUB == 2 ? 0 : PAR;  // fragment slot used by phase A
     constexpr int SB = KSUB == 2 ? 1 : PAR;  // ... by phase B
     constexpr int SN = KSUB == 2 ? 0 : PAR ^ 1;  // ... filled for the next step
-    const uint8_t* cur = slot(std::integral_constant<int, S>{});
+    using CUR = std::integral_constant<int, S>;
     const int* sc = scl[PAR];
     __builtin_amdgcn_sched_barrier(0);
     // ---- phase A: MFMAs of rows [0, RA) of the first sub-step; reads of the
@@ -789,6 +944,14 @@ gemm_kernel(GemmArgs p) {
     {
       constexpr int NM = RA * FN, NR = KSUB == 2 ? FM + FN : 0;
       constexpr int RM = NM * 3 / 4 > 0 ? NM * 3 / 4 : 1;
+      // paired, even steps: the rest of the pair begun in the step before
+      // (stages kt+2, kt+3)
+      constexpr int PP = U + 2;
+      constexpr int NV0 = (PAIR && U % 2 == 0) ? pair_first(PP) : 0;
+      constexpr int NVA = (PAIR && U % 2 == 0) ? pair_count(PP) - NV0 : 0;
+      const int s0 = kt + 2 < nkf ? kt + 2 : nkf - 1;
+      __amdgpu_buffer_rsrc_t ra, rb;
+      if constexpr (NVA > 0) pair_src(s0, ra, rb);
       static_for<NM>([&](auto tc) {
         constexpr int T_ = decltype(tc)::value, I = T_ / FN, J = T_ % FN;
         acc[I][J] = T::template mma<0>(af[SA][I], bf[SA][J], acc[I][J], T::SCALED ? sc[I] : 0,
@@ -796,9 +959,14 @@ gemm_kernel(GemmArgs p) {
         if constexpr (NR > 0 && T_ < RM) {
           static_for<((T_ + 1) * NR) / RM - (T_ * NR) / RM>([&](auto rc) {
             constexpr int R = (T_ * NR) / RM + decltype(rc)::value;
-            read_one(std::integral_constant<int, R>{}, I1{}, I1{}, cur);
+            read_one(std::integral_constant<int, R>{}, I1{}, I1{}, CUR{});
           });
         }
+        static_for<((T_ + 1) * NVA) / NM - (T_ * NVA) / NM>([&](auto vc) {
+          constexpr int V = NV0 + (T_ * NVA) / NM + decltype(vc)::value;
+          issue_pair_one(std::integral_constant<int, V>{}, std::integral_constant<int, (PP % STAGES) / 2>{},
+                         std::integral_constant<int, PP>{}, s0, ra, rb);
+        });
         __builtin_amdgcn_sched_barrier(0);
       });
     }
@@ -809,15 +977,20 @@ gemm_kernel(GemmArgs p) {
     // ---- phase B: the remaining MFMAs; copies of stage kt+STAGES-1 into the
     // freed buffer; reads of the next step's first fragments and scales
     {
+      // single: stage kt+STAGES-1; paired (odd steps): stages kt+3, kt+4
       const int nxt = kt + STAGES - 1 < nkf ? kt + STAGES - 1 : nkf - 1;
       __amdgpu_buffer_rsrc_t ra, rb;
-      step_src(nxt, ra, rb);
-      const uint8_t* nx = slot(std::integral_constant<int, NEXT>{});
+      if constexpr (PAIR) {
+        if constexpr (U % 2 != 0) pair_src(nxt, ra, rb);
+      } else {
+        step_src(nxt, ra, rb);
+      }
+      using NX = std::integral_constant<int, NEXT>;
       constexpr int NM = KSUB == 2 ? FM * FN : (FM - RA) * FN;
       constexpr int NF = FM + FN, NR = NF + (T::SCALED ? NSC : 0);
       constexpr int RM = NM * 3 / 4 > 0 ? NM * 3 / 4 : 1;
-      constexpr int P = U + STAGES - 1;  // position of the stage issued here
-      constexpr int NV = vm_of(P);
+      constexpr int P = U + STAGES - 1;  // position of the (first) stage issued here
+      constexpr int NV = PAIR ? (U % 2 != 0 ? pair_first(U + 3) : 0) : issued_at(U);
       const uint8_t* ng = nullptr;  // the next step's scale group (fp4)
       if constexpr (T::SCALED) ng = sgbuf(std::integral_constant<int, ((U + 1) / SG) % 2>{});
       static_for<NM>([&](auto tc) {
@@ -829,7 +1002,7 @@ gemm_kernel(GemmArgs p) {
           static_for<((T_ + 1) * NR) / RM - (T_ * NR) / RM>([&](auto rc) {
             constexpr int R = (T_ * NR) / RM + decltype(rc)::value;
             if constexpr (R < NF) {
-              read_one(std::integral_constant<int, R>{}, I0{}, std::integral_constant<int, SN>{}, nx);
+              read_one(std::integral_constant<int, R>{}, I0{}, std::integral_constant<int, SN>{}, NX{});
             } else if constexpr (T::SCALED) {
               scl[PAR ^ 1][R - NF] = scale_of(ng, (U + 1) % SG, R - NF, false);
             }
@@ -837,8 +1010,13 @@ gemm_kernel(GemmArgs p) {
         }
         static_for<((T_ + 1) * NV) / NM - (T_ * NV) / NM>([&](auto vc) {
           constexpr int V = (T_ * NV) / NM + decltype(vc)::value;
-          issue_one(std::integral_constant<int, V>{}, std::integral_constant<int, ISSUE>{},
-                    std::integral_constant<int, P>{}, nxt, ra, rb);
+          if constexpr (PAIR) {
+            issue_pair_one(std::integral_constant<int, V>{}, std::integral_constant<int, (ISSUE / 2)>{},
+                           std::integral_constant<int, P>{}, nxt, ra, rb);
+          } else {
+            issue_one(std::integral_constant<int, V>{}, std::integral_constant<int, ISSUE>{},
+                      std::integral_constant<int, P>{}, nxt, ra, rb);
+          }
         });
         __builtin_amdgcn_sched_barrier(0);
       });
@@ -1116,10 +1294,19 @@ gemm_kernel(GemmArgs p) {
 
   // First stages of the current tile.
   auto prologue = [&]() {
-    static_for<STAGES - 1>([&](auto sc) {
-      constexpr int S = decltype(sc)::value;
-      issue_full(S < nkf ? S : nkf - 1, std::integral_constant<int, S>{}, std::integral_constant<int, S>{});
-    });
+    if constexpr (PAIR) {  // pairs (0, 1) and (2, 3): the whole ring
+      issue_pair_full(0, I0{}, I0{});
+      // pair (2, 3): its first part, as if issued in phase B of step -1
+      __amdgpu_buffer_rsrc_t ra, rb;
+      const int s2 = 2 < nkf ? 2 : nkf - 1;
+      pair_src(s2, ra, rb);
+      static_for<pair_first(2)>([&](auto vc) { issue_pair_one(vc, I1{}, std::integral_constant<int, 2>{}, s2, ra, rb); });
+    } else {
+      static_for<STAGES - 1>([&](auto sc) {
+        constexpr int S = decltype(sc)::value;
+        issue_full(S < nkf ? S : nkf - 1, std::integral_constant<int, S>{}, std::integral_constant<int, S>{});
+      });
+    }
   };
 
   // ---------------------------------------------------------- tile loop
@@ -1137,13 +1324,17 @@ gemm_kernel(GemmArgs p) {
       // and stores are in the count too, and vector-memory loads and stores
       // need not complete in order: wait for everything.
       if (first) {
-        wait_vm<younger(-1) + vm_of(STAGES - 2)>();  // stages 1 .. STAGES-2 may be in flight
+        if constexpr (PAIR) {
+          wait_vm<pair_first(2)>();  // the first part of pair (2, 3) may be in flight
+        } else {
+          wait_vm<younger(-1) + vm_of(STAGES - 2)>();  // stages 1 .. STAGES-2 may be in flight
+        }
       } else {
         wait_vm<0>();
       }
       wg_barrier();
       if constexpr (T::SCALED) scales_of(sgbuf(I0{}), 0, scl[0], false);
-      read(slot(I0{}), I0{}, I0{}, KB);
+      read(I0{}, I0{}, I0{}, KB);
       // Whole unrolled groups without per-step conditions (straight-line code
       // between loop edges), then the remaining steps.
       int kb = 0;
@@ -1168,10 +1359,10 @@ gemm_kernel(GemmArgs p) {
         sct[0] = 0;
       }
       const int kvalid = p.kbytes - nkf * KB;
-      read(slot(I0{}), I0{}, I0{}, kvalid);
+      read(I0{}, I0{}, I0{}, kvalid);
       mma(I0{}, I0{}, I0{}, IFM{}, sct);
       if constexpr (KSUB == 2) {
-        read(slot(I0{}), I1{}, I1{}, kvalid);
+        read(I0{}, I1{}, I1{}, kvalid);
         mma(I1{}, I1{}, I0{}, IFM{}, sct);
       }
     }

@@ -77,6 +77,31 @@ THL_HD void copy_source(int64_t base, int64_t lane, int64_t loadw, int64_t* row,
   *byte_in_row = (((slot ^ swz(r)) & 3) << 4) | (off & 15);
 }
 
+// Paired stages.  With four stage buffers, stages 2j and 2j+1 share one
+// buffer pair and are copied together, so that every copy instruction reads
+// whole 128-byte lines (the vector L1 line; a 64-byte K-step alone fetches
+// each line twice, once per step).  Rows are grouped by 8: group g is 1 KB,
+// the group's 64 bytes of stage 2j followed by the same rows' 64 bytes of
+// stage 2j+1.  Row r of a stage starts at byte r*64 + (r/8)*512 of the pair
+// (+512 for the odd stage); the chunk swizzle inside a row is the one above.
+THL_HD int64_t pair_row_offset(int64_t row) { return row * kStepBytes + (row >> 3) * 512; }
+
+// Byte offset inside a buffer pair of byte `b` (0..63) of row `row` of the
+// even (odd = 0) or odd (odd = 1) stage.
+THL_HD int64_t pair_lds_offset(int64_t row, int64_t b, int64_t odd) {
+  return pair_row_offset(row) + odd * 512 + (lds_offset(row, b) - row * kStepBytes);
+}
+
+// The 16-byte copy that fills 1 KB group `grp` (rows 8*grp .. 8*grp+7) of a
+// pair: lane l fetches row 8*grp + (l%32)/4 and, within the 128 bytes of K
+// the pair covers, byte 64*(l/32) plus the chunk that slot l%4 of that row
+// holds.  Lanes l and l+32 take the two halves of one line.
+THL_HD void pair_copy_source(int64_t grp, int64_t lane, int64_t* row, int64_t* byte_in_pair) {
+  const int64_t r = 8 * grp + ((lane & 31) >> 2);
+  *row = r;
+  *byte_in_pair = 64 * (lane >> 5) + ((((lane & 3) ^ swz(r)) & 3) << 4);
+}
+
 // ------------------------------------------------------------ a4/a5: MFMA maps
 // 32x32 MFMA operand fragment: lane l holds row l % 32 of the 32-row operand
 // tile and `vals` consecutive K elements starting at (l / 32) * vals, where
