@@ -70,13 +70,13 @@ ROW = 64  # bytes of K staged per operand row (one K-step)
 
 
 def test_lds_swizzle_is_the_xor_composition():
-    # lds_offset(row, b) = Swz<2,4,5>(Swz<2,4,3>(row*64 + b)) over 256 rows.
+    # lds_offset(row, b) = Swz<2,4,4>(Swz<2,4,2>(row*64 + b)) over 256 rows.
     rows = 256
     pts = [(r, b) for r in range(rows) for b in range(ROW)]
     got = [o for o, _ in thl.thl_kernel_index_map("lds_offset", pts)]
     linear = f"{rows * ROW}:1"
-    first = thl.thl_swizzle_eval(2, 4, 3, linear, range(rows * ROW))
-    both = thl.thl_swizzle_eval(2, 4, 5, linear, first)
+    first = thl.thl_swizzle_eval(2, 4, 2, linear, range(rows * ROW))
+    both = thl.thl_swizzle_eval(2, 4, 4, linear, first)
     assert got == both
     assert sorted(got) == list(range(rows * ROW))
 

@@ -50,15 +50,18 @@ THL_HD void grouped_tile(int64_t id, int64_t tiles_m, int64_t tiles_n, int64_t g
 // ------------------------------------------------------------ a3: LDS staging
 // One K-step stages 64 bytes of K per operand row: four 16-byte chunks whose
 // order is XOR-swizzled per row.  Chunk c of row r is stored in slot
-// c ^ swz(r) with swz(r) = ((r >> 1) ^ (r >> 3)) & 3.  Reading one chunk from
-// consecutive rows (what the MFMA fragment reads do), any 8 rows land on 8
-// distinct (row parity, slot) pairs -- all 32 banks of a 128-byte window --
-// and any 16 rows on 16 distinct (row % 4, slot) pairs -- all 64 banks of a
-// 256-byte window.  On the row-major (rows, 64) byte layout it is two XOR
-// swizzles (b=2, m=4, s=3) and (b=2, m=4, s=5) composed on top.
+// c ^ swz(r) with swz(r) = (r ^ (r >> 2)) & 3.  The MFMA fragment reads take
+// one chunk from each of 32 consecutive rows (lane l: row l % 32; the two
+// lane halves read different chunks).  Measured on gfx950 with 16 waves
+// issuing such ds_read_b128, this swizzle streams about 230 B/clk per CU, the
+// same as plain consecutive 16-byte reads; the earlier ((r >> 1) ^ (r >> 3))
+// streamed 126 B/clk (two-way bank conflicts), although both put any 16
+// consecutive rows on 16 distinct (row % 4, slot) pairs.  On the row-major
+// (rows, 64) byte layout it is two XOR swizzles (b=2, m=4, s=2) and (b=2,
+// m=4, s=4) composed on top.
 constexpr int kStepBytes = 64;
 
-THL_HD int swz(int64_t row) { return static_cast<int>(((row >> 1) ^ (row >> 3)) & 3); }
+THL_HD int swz(int64_t row) { return static_cast<int>((row ^ (row >> 2)) & 3); }
 
 // Byte offset, inside one staged operand buffer, of byte `b` (0..63) of row `row`.
 THL_HD int64_t lds_offset(int64_t row, int64_t b) {
@@ -133,11 +136,15 @@ THL_HD int64_t fp8_32x32_k_of(int64_t lane, int64_t j) {
 // ------------------------------------------------------------ M-major operands
 // An operand whose storage is contiguous along M (or N) -- opA = N, opB = T --
 // is staged as k-rows: row k holds the tile's `pitch`/2 consecutive 16-bit
-// elements of that k.  Its 32-byte blocks are XOR-swizzled by k % 8, so the
-// 4 k-rows a transposed read touches land in 4 different 32-byte blocks
-// (distinct banks in a 128- or 256-byte window).  pitch is a multiple of 256.
+// elements of that k.  Its 32-byte blocks are XOR-swizzled by mm_swz(k), a
+// permutation of 0..7 over k % 8: ((k & 3) << 1) | ((k >> 2) & 1).  Measured
+// on gfx950 (16 waves of ds_read_b64_tr_b16 on 512-byte k-rows) it streams
+// about 200 B/clk per CU against 123 B/clk for swizzling by k % 8 itself.
+// pitch is a multiple of 256.
+THL_HD int mm_swz(int64_t k) { return static_cast<int>(((k & 3) << 1) | ((k >> 2) & 1)); }
+
 THL_HD int64_t mm_lds_offset(int64_t k, int64_t b, int64_t pitch) {
-  return k * pitch + ((((b >> 5) ^ (k & 7))) << 5) + (b & 31);
+  return k * pitch + ((((b >> 5) ^ mm_swz(k))) << 5) + (b & 31);
 }
 
 // Inverse for the direct copies: the (k-row, byte within the row) that lane
@@ -148,7 +155,7 @@ THL_HD void mm_copy_source(int64_t base, int64_t lane, int64_t loadw, int64_t pi
   const int64_t r = off / pitch;
   const int64_t pb = off % pitch;
   *k = r;
-  *byte_in_row = ((((pb >> 5) ^ (r & 7))) << 5) | (pb & 31);
+  *byte_in_row = ((((pb >> 5) ^ mm_swz(r))) << 5) | (pb & 31);
 }
 
 // The 8-byte chunk lane `lane` addresses for transposed read h (h = 0, 1) of a
