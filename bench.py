@@ -118,12 +118,18 @@ def cpu_baseline(w, budget_s):
     import oracle
 
     nthreads = oracle.max_threads()
+    # Two pilots: the first includes one-time setup and overestimates the
+    # per-output cost; the second, sized for about a tenth of the budget,
+    # sets the size of the timed sample.
     pilot = 16 * nthreads
-    rows, cols = w.sample(pilot)
-    t0 = time.perf_counter()
-    oracle.gemm_elements(w.oracle_problem(), rows, cols, nthreads)
-    t1 = time.perf_counter() - t0
-    count = int(min(max(pilot, pilot * budget_s / max(t1, 1e-6)), w.m * w.n))
+    for _ in range(2):
+        rows, cols = w.sample(pilot)
+        t0 = time.perf_counter()
+        oracle.gemm_elements(w.oracle_problem(), rows, cols, nthreads)
+        t1 = time.perf_counter() - t0
+        per = max(t1, 1e-6) / pilot
+        pilot = int(min(max(pilot, 0.1 * budget_s / per), w.m * w.n))
+    count = int(min(max(16 * nthreads, budget_s / per), w.m * w.n))
     rows, cols = w.sample(count)
     t0 = time.perf_counter()
     oracle.gemm_elements(w.oracle_problem(), rows, cols, nthreads)
