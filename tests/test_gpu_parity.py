@@ -329,3 +329,31 @@ def test_persistent_workgroups_walk_several_tiles(variant):
     cols = np.concatenate([cols, np.arange(w.n), np.full(w.m, w.n - 1)])
     res = compare.parity_check(w, dp.d_values(rows, cols), rows, cols)
     assert res["ok"], res
+
+
+@pytest.mark.parametrize("variant", ["bf16_nn_256x128_v16_s3_o2", "bf16_nn_128x128_v16_s4_o2"])
+def test_two_workgroups_per_cu_match_the_256x256_kernel(variant):
+    """4096^2 tiles two workgroups onto every CU.  Each output element is the
+    same K-ordered sum in every variant, so the whole D must equal the
+    256x256 kernel's to within one bf16 ulp (the sampled oracle check is in
+    the tests above)."""
+    import workloads as wl
+    from workloads.device import DeviceProblem
+
+    w = wl.make("bf16", 4096, 4096, 1024)
+    outs = []
+    for v in ("bf16_nn_256x256_v16_s4_o1", variant):
+        os.environ["THL_FORCE_VARIANT"] = v
+        try:
+            _say(f"[variants agree] {v} m={w.m} n={w.n} k={w.k}")
+            dp = DeviceProblem(w)
+            assert dp.run() == 0
+            torch.cuda.synchronize()
+        finally:
+            os.environ.pop("THL_FORCE_VARIANT", None)
+        outs.append(dp.d.float().cpu())
+    # same sums; the two epilogue paths may round the last fp32 step apart,
+    # so allow one bf16 ulp
+    a, b = outs
+    bad = (a - b).abs() > 2.0 ** -7 * torch.maximum(a.abs(), b.abs()) + 1e-6
+    assert int(bad.sum()) == 0, f"{int(bad.sum())} elements differ by more than one bf16 ulp"

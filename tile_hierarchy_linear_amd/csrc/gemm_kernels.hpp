@@ -254,6 +254,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), -1, 0x00020000);
 }
 
+// A wave-uniform 64-bit value made visibly uniform (read from lane 0), so
+// that addresses built from it stay scalar: a buffer resource the compiler
+// believes divergent is issued through a loop over its distinct values.
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint64_t u = static_cast<uint64_t>(v);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// beta != 0 as an integer test on its bits (either zero), which stays a
+// scalar value; a float compare is a vector instruction, and everything
+// chosen by its result would be treated as divergent.
+__device__ __forceinline__ bool nonzero_f32(float x) { return (__builtin_bit_cast(uint32_t, x) << 1) != 0; }
+
 // Buffer resource over `num` bytes at `base`: loads at or past the end read
 // zeros without touching memory, stores there are dropped.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_n(const void* base, int num) {
@@ -428,6 +443,9 @@ gemm_kernel(GemmArgs p) {
   constexpr bool PAIR = STAGES == 4 && LOADW == 16;
   static_assert(!PAIR || NW % 4 == 0, "a wave's pair copies keep one chunk swizzle");
   constexpr int RSTEP = PAIR ? 2 * KB : KB;  // LDS bytes per K-major row of an 8-row group
+  // Phase A MFMAs: all of sub-step 0 (two sub-steps per K-step), else the
+  // first half of the rows (measured 2% faster for e4m3 than a quarter).
+  constexpr int RA = KSUB == 2 ? FM : FM / 2;
   // Steps per unrolled loop body: ring slots, fragment-slot parities and (fp4)
   // the scale-group buffer and position are compile-time constants inside it.
   constexpr int UNROLL = T::SCALED ? (STAGES % (2 * SG) == 0 ? STAGES : (STAGES % SG == 0 ? 2 * STAGES : 0))
@@ -642,8 +660,8 @@ gemm_kernel(GemmArgs p) {
   // A pair's copies go out over the MFMAs of phase B of the odd step before
   // it and phase A of the next (even) step, in proportion to their MFMAs:
   // the first pair_first(pos) in phase B, the rest in phase A.
-  constexpr int NMA = (KSUB == 2 ? FM : (FM >= 4 ? FM / 4 : FM / 2)) * FN;
-  constexpr int NMB = (KSUB == 2 ? FM : FM - (FM >= 4 ? FM / 4 : FM / 2)) * FN;
+  constexpr int NMA = RA * FN;
+  constexpr int NMB = (KSUB == 2 ? FM : FM - RA) * FN;
   auto pair_first = [](int pos) constexpr {
     return (2 * COPIES + (pos % SG == 0 ? SC_LOADS : 0)) * NMB / (NMA + NMB);
   };
@@ -919,10 +937,6 @@ gemm_kernel(GemmArgs p) {
   };
 
   int scl[2][NSC];
-  // Phase A MFMAs: all of sub-step 0 (two sub-steps per K-step), else the
-  // first quarter of the rows, so that the reads after the barrier spread
-  // over most of the step.
-  constexpr int RA = KSUB == 2 ? FM : (FM >= 4 ? FM / 4 : FM / 2);
   // One K-step; U is its position in the unrolled group, which fixes its
   // ring slot and fragment-slot parity at compile time.  Within a phase the
   // program order interleaves MFMAs, fragment reads and copies, and a hard
@@ -942,8 +956,15 @@ gemm_kernel(GemmArgs p) {
     // ---- phase A: MFMAs of rows [0, RA) of the first sub-step; reads of the
     // second sub-step's fragments (two sub-steps per K-step)
     {
-      constexpr int NM = RA * FN, NR = KSUB == 2 ? FM + FN : 0;
+      // fp4: unless the next step starts a scale group (whose buffer is
+      // only known to have landed after this step's barrier), its scales
+      // are read here, after this step's own fragments
+      constexpr bool SC_A = T::SCALED && (U + 1) % SG != 0;
+      constexpr int NF_A = KSUB == 2 ? FM + FN : 0;
+      constexpr int NM = RA * FN, NR = NF_A + (SC_A ? NSC : 0);
       constexpr int RM = NM * 3 / 4 > 0 ? NM * 3 / 4 : 1;
+      const uint8_t* ng_a = nullptr;
+      if constexpr (SC_A) ng_a = sgbuf(std::integral_constant<int, ((U + 1) / SG) % 2>{});
       // paired, even steps: the rest of the pair begun in the step before
       // (stages kt+2, kt+3)
       constexpr int PP = U + 2;
@@ -959,7 +980,11 @@ gemm_kernel(GemmArgs p) {
         if constexpr (NR > 0 && T_ < RM) {
           static_for<((T_ + 1) * NR) / RM - (T_ * NR) / RM>([&](auto rc) {
             constexpr int R = (T_ * NR) / RM + decltype(rc)::value;
-            read_one(std::integral_constant<int, R>{}, I1{}, I1{}, CUR{});
+            if constexpr (R < NF_A) {
+              read_one(std::integral_constant<int, R>{}, I1{}, I1{}, CUR{});
+            } else if constexpr (SC_A) {
+              scl[PAR ^ 1][R - NF_A] = scale_of(ng_a, (U + 1) % SG, R - NF_A, false);
+            }
           });
         }
         static_for<((T_ + 1) * NVA) / NM - (T_ * NVA) / NM>([&](auto vc) {
@@ -987,7 +1012,7 @@ gemm_kernel(GemmArgs p) {
       }
       using NX = std::integral_constant<int, NEXT>;
       constexpr int NM = KSUB == 2 ? FM * FN : (FM - RA) * FN;
-      constexpr int NF = FM + FN, NR = NF + (T::SCALED ? NSC : 0);
+      constexpr int NF = FM + FN, NR = NF + ((T::SCALED && (U + 1) % SG == 0) ? NSC : 0);
       constexpr int RM = NM * 3 / 4 > 0 ? NM * 3 / 4 : 1;
       constexpr int P = U + STAGES - 1;  // position of the (first) stage issued here
       constexpr int NV = PAIR ? (U % 2 != 0 ? pair_first(U + 3) : 0) : issued_at(U);
@@ -1000,11 +1025,14 @@ gemm_kernel(GemmArgs p) {
                                               T::SCALED ? sc[FM + J] : 0);
         if constexpr (T_ < RM) {
           static_for<((T_ + 1) * NR) / RM - (T_ * NR) / RM>([&](auto rc) {
+            // fp4, when the next step starts a scale group: its scales
+            // first, then the fragments in the order the MFMAs consume them
             constexpr int R = (T_ * NR) / RM + decltype(rc)::value;
-            if constexpr (R < NF) {
-              read_one(std::integral_constant<int, R>{}, I0{}, std::integral_constant<int, SN>{}, NX{});
-            } else if constexpr (T::SCALED) {
-              scl[PAR ^ 1][R - NF] = scale_of(ng, (U + 1) % SG, R - NF, false);
+            constexpr int NS_ = NR - NF;
+            if constexpr (R < NS_) {
+              scl[PAR ^ 1][R] = scale_of(ng, (U + 1) % SG, R, false);
+            } else {
+              read_one(std::integral_constant<int, R - NS_>{}, I0{}, std::integral_constant<int, SN>{}, NX{});
             }
           });
         }
@@ -1178,9 +1206,9 @@ gemm_kernel(GemmArgs p) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
     const int erow = (ln % LPC) * 8;
-    const int64_t tm0 = em0 + wm * TM, tn0 = en0 + wn * TN;
+    const int64_t tm0 = uniform64(em0 + wm * TM), tn0 = uniform64(en0 + wn * TN);
     const int cl = ln / LPC;  // the lane's column within an iteration
-    const bool has_c = p.beta != 0.0f, has_bias = (p.flags & EPI_BIAS) != 0;
+    const bool has_c = nonzero_f32(p.beta), has_bias = (p.flags & EPI_BIAS) != 0;
     const bool bias32 = p.bias_type == DT_F32, d32 = !BF && p.d_type == DT_F32;
     const unsigned c_bf = p.c_type == DT_BF16 ? ~0u : 0u, b_bf = p.bias_type == DT_BF16 ? ~0u : 0u;
     const unsigned d_bf = p.d_type == DT_BF16 ? ~0u : 0u, b32 = bias32 ? ~0u : 0u;
@@ -1274,9 +1302,14 @@ gemm_kernel(GemmArgs p) {
   };
 
   auto epilogue = [&](const int64_t em0, const int64_t en0) {
-    if constexpr (!T::INT) {
+    // The vector path runs in the one-workgroup-per-CU variants only.  With
+    // two workgroups per CU (256 registers a wave) it spills heavily, and
+    // with C or bias reads it produced wrong values in a few hundredths of a
+    // percent of the outputs (rows 0-1 of some 8-row runs) once two
+    // workgroups shared each CU; the general path is exact there.
+    if constexpr (!T::INT && OCC == 1) {
       if ((p.flags & EPI_VEC) && !(p.flags & EPI_GELU) && em0 + BM <= p.m && en0 + BN <= p.n) {
-        const bool has_c = p.beta != 0.0f, has_bias = (p.flags & EPI_BIAS) != 0;
+        const bool has_c = nonzero_f32(p.beta), has_bias = (p.flags & EPI_BIAS) != 0;
         const bool bf = (!has_c || p.c_type == DT_BF16) && p.d_type == DT_BF16 &&
                         (!has_bias || p.bias_type == DT_BF16);
         if (!bf) {
