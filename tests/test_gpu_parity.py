@@ -357,3 +357,24 @@ def test_two_workgroups_per_cu_match_the_256x256_kernel(variant):
     a, b = outs
     bad = (a - b).abs() > 2.0 ** -7 * torch.maximum(a.abs(), b.abs()) + 1e-6
     assert int(bad.sum()) == 0, f"{int(bad.sum())} elements differ by more than one bf16 ulp"
+
+
+def test_vector_epilogue_matches_general_path_at_8192():
+    """The same bf16 problem with 16-byte aligned C and D columns (vector
+    epilogue) and with ld = 8197 (general epilogue): every element of the two
+    D's agrees to within one bf16 ulp."""
+    import workloads as wl
+    from workloads.device import DeviceProblem
+
+    outs = []
+    for ld in (8192, 8197):
+        w = wl.make("bf16", 8192, 8192, 512, ldc=ld, ldd=ld)
+        _say(f"[vector vs general] m={w.m} n={w.n} k={w.k} ldc=ldd={ld}")
+        dp = DeviceProblem(w)
+        assert dp.run() == 0
+        torch.cuda.synchronize()
+        outs.append(dp.d[:, : w.m].float().cpu())
+        del dp
+    a, b = outs
+    bad = (a - b).abs() > 2.0 ** -7 * torch.maximum(a.abs(), b.abs()) + 1e-6
+    assert int(bad.sum()) == 0, f"{int(bad.sum())} elements differ by more than one bf16 ulp"

@@ -275,6 +275,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_n(const void* base, 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), num, 0x00020000);
 }
 
+// Buffer resource whose base and size are read from lane 0.  Built from
+// values the compiler cannot prove uniform (a select on a flag is a vector
+// select), a resource lands in vector registers and every load through it
+// becomes a loop over the distinct values of the wave.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_u(const void* base, int num) {
+  const int64_t b = uniform64(static_cast<int64_t>(reinterpret_cast<uintptr_t>(base)));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(static_cast<uintptr_t>(b)), static_cast<short>(0),
+                                          __builtin_amdgcn_readfirstlane(num), 0x00020000);
+}
+
 // 16-byte buffer load and store at the resource base + voffset + soffset.
 __device__ __forceinline__ v4i buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t vo, int so) {
   return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, 0));
@@ -1215,14 +1225,14 @@ gemm_kernel(GemmArgs p) {
     // An absent C or bias (with the other present) is read through an empty
     // resource: its loads return zeros, so the loads do not depend on a
     // branch and neither does any wait for them.
-    const auto rc = make_rsrc_n(static_cast<const uint16_t*>(p.c) + (has_c ? tn0 * p.ldc + tm0 : 0), has_c ? -1 : 0);
+    const auto rc = make_rsrc_u(static_cast<const uint16_t*>(p.c) + (has_c ? tn0 * p.ldc + tm0 : 0), has_c ? -1 : 0);
     const int ldcb = static_cast<int>(p.ldc) * 2;
     const uint32_t vc = static_cast<uint32_t>(cl * ldcb + erow * 2);
     const int bs = bias32 ? 4 : 2;
     const uint8_t* bbase = static_cast<const uint8_t*>(p.bias) + (has_bias ? tm0 * bs : 0);
-    const auto rb = make_rsrc_n(bbase, has_bias ? -1 : 0), rb2 = make_rsrc_n(bbase, has_bias && bias32 ? -1 : 0);
+    const auto rb = make_rsrc_u(bbase, has_bias ? -1 : 0), rb2 = make_rsrc_u(bbase, has_bias && bias32 ? -1 : 0);
     const int ds = d32 ? 4 : 2;
-    const auto rd = make_rsrc(static_cast<uint8_t*>(p.d) + (tn0 * p.ldd + tm0) * ds);
+    const auto rd = make_rsrc_u(static_cast<uint8_t*>(p.d) + (tn0 * p.ldd + tm0) * ds, -1);
     const int lddb = static_cast<int>(p.ldd) * ds;
     const uint32_t vd = static_cast<uint32_t>(cl * lddb + erow * ds);
     const float alpha = p.alpha, beta = p.beta;
