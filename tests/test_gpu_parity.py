@@ -116,6 +116,18 @@ def test_small_shapes_mxfp4_full(shape):
     _check_full(wl.make("mxfp4", m, n, k, lda=_pad(k, 32), ldb=_pad(k, 32)))
 
 
+@pytest.mark.parametrize("variant", ["e2m1_tn_256x256_v16_s4_o1", "e2m1_tn_128x128_v16_s4_o2"])
+@pytest.mark.parametrize("k", [384, 640, 768, 896, 1152, 1440, 2048])
+def test_mxfp4_scale_groups_at_every_step_count(variant, k):
+    # fp4 scales travel in groups of four 128-element K-steps, copied two
+    # steps ahead of the pair of stages they ride with: K from 3 to 16 full
+    # steps (one with a partial last step) covers every position of the last
+    # step in its group and in the 8-step unrolled loop body.
+    import workloads as wl
+
+    _check_full(wl.make("mxfp4", 260, 200, k), variant=variant)
+
+
 @pytest.mark.parametrize("act", ["none", "relu", "gelu"])
 @pytest.mark.parametrize("kind", ["fp16", "fp8"])
 def test_epilogue_variants(kind, act):

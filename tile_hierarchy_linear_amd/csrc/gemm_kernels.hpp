@@ -462,17 +462,18 @@ gemm_kernel(GemmArgs p) {
                                    : ((STAGES % 2 == 0) ? STAGES : 2 * STAGES);
   static_assert(UNROLL > 0, "scale groups need STAGES to divide into 4 K-step groups");
   // Copies per wave issued in phase B of the step at position pos: paired,
-  // odd steps issue stages pos+3 and pos+4 (with the scale group when pos+3
-  // starts one), even steps none; otherwise every step issues stage pos+3.
+  // odd steps issue stages pos+3 and pos+4 (with the scale group that starts
+  // at pos+5, when one does), even steps none; otherwise every step issues
+  // stage pos+3.
   auto issued_at = [](int pos) constexpr {
-    if constexpr (PAIR) return (pos % 2 != 0) ? 2 * COPIES + ((pos + 3) % SG == 0 ? SC_LOADS : 0) : 0;
+    if constexpr (PAIR) return (pos % 2 != 0) ? 2 * COPIES + ((pos + 5) % SG == 0 ? SC_LOADS : 0) : 0;
     return COPIES + ((pos + STAGES - 1) % SG == 0 ? SC_LOADS : 0);
   };
   // Copies per wave younger than stage pos+1 when waiting for it at step pos
   // (single: stages pos+2 .. pos+STAGES-2 may still be in flight; paired:
   // the pair issued at step pos-1 when stage pos+1 is odd).
   auto younger = [](int pos) constexpr {
-    if constexpr (PAIR) return (pos % 2 == 0) ? 2 * COPIES + ((pos + 2) % SG == 0 ? SC_LOADS : 0) : 0;
+    if constexpr (PAIR) return (pos % 2 == 0) ? 2 * COPIES + ((pos + 4) % SG == 0 ? SC_LOADS : 0) : 0;
     int n = 0;
     for (int q = pos + 2; q <= pos + STAGES - 2; ++q) n += COPIES + (q % SG == 0 ? SC_LOADS : 0);
     return n;
@@ -665,18 +666,24 @@ gemm_kernel(GemmArgs p) {
       rb = make_rsrc(b_tile);
     }
   };
-  // Copies per wave of the pair whose first stage sits at position pos.
-  auto pair_count = [](int pos) constexpr { return 2 * COPIES + (pos % SG == 0 ? SC_LOADS : 0); };
+  // Copies per wave of the pair whose first stage sits at position pos.  A
+  // pair carries the scale group that starts two stages after it (fp4): the
+  // group of steps 4g+8 .. 4g+11 goes out after step 4g+3's barrier, into the
+  // buffer of group g+0 (last read in phase A of step 4g+2), and has landed
+  // by step 4g+5's barrier, so that every step reads the next step's scales
+  // in its phase A, with no scale read after a barrier.
+  auto pair_count = [](int pos) constexpr { return 2 * COPIES + ((pos + 2) % SG == 0 ? SC_LOADS : 0); };
   // A pair's copies go out over the MFMAs of phase B of the odd step before
   // it and phase A of the next (even) step, in proportion to their MFMAs:
   // the first pair_first(pos) in phase B, the rest in phase A.
   constexpr int NMA = RA * FN;
   constexpr int NMB = (KSUB == 2 ? FM : FM - RA) * FN;
   auto pair_first = [](int pos) constexpr {
-    return (2 * COPIES + (pos % SG == 0 ? SC_LOADS : 0)) * NMB / (NMA + NMB);
+    return (2 * COPIES + ((pos + 2) % SG == 0 ? SC_LOADS : 0)) * NMB / (NMA + NMB);
   };
   // Copy V of the pair (stage s0 at position POS, s0+1) into buffer pair BUF:
-  // the scale copies first when POS starts a group, then A's, then B's.
+  // the scale copies first when POS+2 starts a group, then A's, then B's.  A
+  // pair clamped at the last K-step carries a group that no step uses.
   // K-major: one 1 KB group of 8 rows x 128 bytes per instruction; M-major:
   // each stage's copies as for single stages (k-rows of whole lines already).
   auto issue_pair_one = [&](auto v_tag, auto buf_tag, auto pos_tag, int s0, __amdgpu_buffer_rsrc_t ra,
@@ -686,7 +693,7 @@ gemm_kernel(GemmArgs p) {
     uint8_t* pa = pair_buf(std::integral_constant<int, BUF>{});
     uint8_t* pb = pa + 2 * A_BYTES;
     if constexpr (V < NS) {
-      issue_scale(V, s0 / SG, sgbuf(std::integral_constant<int, (POS / SG) % 2>{}));
+      issue_scale(V, (s0 + 2) / SG, sgbuf(std::integral_constant<int, ((POS + 2) / SG) % 2>{}));
     } else if constexpr (V < NS + 2 * A_LOADS) {
       constexpr int J = V - NS;
       if constexpr (AK) {
@@ -966,10 +973,10 @@ gemm_kernel(GemmArgs p) {
     // ---- phase A: MFMAs of rows [0, RA) of the first sub-step; reads of the
     // second sub-step's fragments (two sub-steps per K-step)
     {
-      // fp4: unless the next step starts a scale group (whose buffer is
-      // only known to have landed after this step's barrier), its scales
-      // are read here, after this step's own fragments
-      constexpr bool SC_A = T::SCALED && (U + 1) % SG != 0;
+      // fp4: the next step's scales are read here, after this step's own
+      // fragments (single stages: unless the next step starts a scale group,
+      // whose buffer is only known to have landed after this step's barrier)
+      constexpr bool SC_A = T::SCALED && (PAIR || (U + 1) % SG != 0);
       constexpr int NF_A = KSUB == 2 ? FM + FN : 0;
       constexpr int NM = RA * FN, NR = NF_A + (SC_A ? NSC : 0);
       constexpr int RM = NM * 3 / 4 > 0 ? NM * 3 / 4 : 1;
@@ -1022,7 +1029,7 @@ gemm_kernel(GemmArgs p) {
       }
       using NX = std::integral_constant<int, NEXT>;
       constexpr int NM = KSUB == 2 ? FM * FN : (FM - RA) * FN;
-      constexpr int NF = FM + FN, NR = NF + ((T::SCALED && (U + 1) % SG == 0) ? NSC : 0);
+      constexpr int NF = FM + FN, NR = NF + ((T::SCALED && !PAIR && (U + 1) % SG == 0) ? NSC : 0);
       constexpr int RM = NM * 3 / 4 > 0 ? NM * 3 / 4 : 1;
       constexpr int P = U + STAGES - 1;  // position of the (first) stage issued here
       constexpr int NV = PAIR ? (U % 2 != 0 ? pair_first(U + 3) : 0) : issued_at(U);
@@ -1035,8 +1042,9 @@ gemm_kernel(GemmArgs p) {
                                               T::SCALED ? sc[FM + J] : 0);
         if constexpr (T_ < RM) {
           static_for<((T_ + 1) * NR) / RM - (T_ * NR) / RM>([&](auto rc) {
-            // fp4, when the next step starts a scale group: its scales
-            // first, then the fragments in the order the MFMAs consume them
+            // fp4 with single stages, when the next step starts a scale
+            // group: its scales first, then the fragments in the order the
+            // MFMAs consume them
             constexpr int R = (T_ * NR) / RM + decltype(rc)::value;
             constexpr int NS_ = NR - NF;
             if constexpr (R < NS_) {
@@ -1338,6 +1346,10 @@ gemm_kernel(GemmArgs p) {
   // First stages of the current tile.
   auto prologue = [&]() {
     if constexpr (PAIR) {  // pairs (0, 1) and (2, 3): the whole ring
+      if constexpr (T::SCALED) {  // scale group 0 (pair (2, 3) brings group 1)
+#pragma unroll
+        for (int t = 0; t < SC_LOADS; ++t) issue_scale(t, 0, sgbuf(I0{}));
+      }
       issue_pair_full(0, I0{}, I0{});
       // pair (2, 3): its first part, as if issued in phase B of step -1
       __amdgpu_buffer_rsrc_t ra, rb;
