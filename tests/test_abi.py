@@ -154,3 +154,32 @@ def test_forced_variant_must_fit():
         assert call(m=0) == thl.THL_ERR_UNSUPPORTED  # bf16 problem, int8 variant
     finally:
         del os.environ["THL_FORCE_VARIANT"]
+
+
+@pytest.mark.parametrize("fam,ta,td", [("bf16", "bf16", "bf16"), ("f16", "f16", "f32"), ("i8", "i8", "i32"),
+                                       ("e4m3", "e4m3", "bf16"), ("e2m1", "e2m1", "bf16")])
+def test_small_m_selection(fam, ta, td):
+    # n == 0 selects a variant without a launch (no GPU needed)
+    tc = "i32" if ta == "i8" else "f32"
+    types = (ta, tc, td, "none")
+    k = 8192
+    for m in (1, 7, 16):
+        assert call(m=m, n=0, k=k, types=types) == thl.THL_OK
+        assert thl.thl_last_variant() == f"{fam}_tn_skinny16_k4"
+    assert call(m=17, n=0, k=k, types=types) == thl.THL_OK
+    assert "skinny" not in thl.thl_last_variant()
+    # k == 0, or operands that are not 16-byte units: the tiled kernels
+    assert call(m=1, n=0, k=0, lda=64, ldb=64, types=types) == thl.THL_OK
+    assert "skinny" not in thl.thl_last_variant()
+    assert call(m=1, n=0, k=k, a=A + 4, types=types) == thl.THL_OK
+    assert "skinny" not in thl.thl_last_variant()
+    if fam in ("bf16", "f16"):  # M-major A: the tiled kernels
+        assert call(m=1, n=0, k=k, opa="N", lda=8, types=types) == thl.THL_OK
+        assert "skinny" not in thl.thl_last_variant()
+    # forcing the small-M kernel on more than 16 rows is refused
+    os.environ["THL_FORCE_VARIANT"] = f"{fam}_tn_skinny16_k4"
+    try:
+        assert call(m=16, n=0, k=k, types=types) == thl.THL_OK
+        assert call(m=17, n=0, k=k, types=types) == thl.THL_ERR_UNSUPPORTED
+    finally:
+        del os.environ["THL_FORCE_VARIANT"]

@@ -128,6 +128,58 @@ def test_mxfp4_scale_groups_at_every_step_count(variant, k):
     _check_full(wl.make("mxfp4", 260, 200, k), variant=variant)
 
 
+SMALL_M_KINDS = [("fp16", "f16", 8), ("bf16", "bf16", 8), ("int8", "i8", 16), ("fp8", "e4m3", 16),
+                 ("mxfp4", "e2m1", 32)]
+
+
+@pytest.mark.parametrize("kind,fam,q", SMALL_M_KINDS)
+@pytest.mark.parametrize("m,n,k", [(1, 1, 64), (1, 1000, 2040), (2, 17, 96), (3, 33, 1000), (16, 64, 4096),
+                                   (16, 300, 160), (5, 16, 8192)])
+def test_small_m_kernel(kind, fam, q, m, n, k):
+    # M <= 16 with K-major operands: the small-M kernel, over ragged N, K
+    # tails inside a 128-byte unit, K split over its wavefronts, and one to
+    # sixteen rows (row blocks past M read as zeros)
+    import tile_hierarchy_linear_amd as thl
+    import workloads as wl
+
+    if kind == "mxfp4":
+        k = _pad(k, 32)
+    kw = dict(op_a="T", op_b="N", lda=_pad(k, q), ldb=_pad(k, q))
+    if kind == "int8":
+        kw.update(bias=True, beta=1.0, act="relu")
+    elif kind in ("fp16", "bf16"):
+        kw.update(bias=True, beta=1.0, act="relu", type_c="bf16", type_bias="f32")
+    _check_full(wl.make(kind, m, n, k, **kw))
+    assert thl.thl_last_variant() == f"{fam}_tn_skinny16_k4"
+
+
+@pytest.mark.parametrize("m", [3, 300])
+def test_mxfp4_nan_codes_in_scale_row_padding_are_never_used(m):
+    # E8M0 0xFF is NaN: scale bytes past K/32 (row padding) must not reach an
+    # MFMA, in the small-M kernel (m = 3) and the tiled kernels (m = 300),
+    # with K = 288 ending inside a K unit / step
+    import workloads as wl
+
+    w = wl.make("mxfp4", m, 40, 288)
+    w.sfa[:, 288 // 32:] = 255
+    w.sfb[:, 288 // 32:] = 255
+    _check_full(w)
+
+
+@pytest.mark.parametrize("act", ["none", "gelu"])
+@pytest.mark.parametrize("kind", ["fp16", "fp8", "mxfp4"])
+def test_small_m_epilogues(kind, act):
+    # alpha, beta with C, bias and the activations on the small-M path
+    import tile_hierarchy_linear_amd as thl
+    import workloads as wl
+
+    q = {"fp16": 8, "fp8": 16, "mxfp4": 32}[kind]
+    w = wl.make(kind, 9, 130, 1024, op_a="T", op_b="N", lda=_pad(1024, q), ldb=_pad(1024, q), act=act, bias=True,
+                beta=0.5, alpha=-1.5, type_d="f16", type_c="f32", type_bias="bf16")
+    _check_full(w)
+    assert "skinny" in thl.thl_last_variant()
+
+
 @pytest.mark.parametrize("act", ["none", "relu", "gelu"])
 @pytest.mark.parametrize("kind", ["fp16", "fp8"])
 def test_epilogue_variants(kind, act):
@@ -185,7 +237,7 @@ def test_every_variant(variant_family):
         if not v.startswith(variant_family + "_"):
             continue
         op_a, op_b = ops[v.split("_")[1]]
-        m, n, k = 300, 260, 520
+        m, n, k = (16 if "skinny" in v else 300), 260, 520
         if kind in ("fp16", "bf16"):
             lda = _pad(m if op_a == "N" else k, 8)  # 16-byte leading dimensions
             ldb = _pad(k if op_b == "N" else n, 8)

@@ -51,6 +51,37 @@ def test_mfma_accumulator_map_is_the_tv_layout():
             assert rows[4 * q:4 * q + 4] == list(range(rows[4 * q], rows[4 * q] + 4))
 
 
+def test_small_m_operand_map_is_the_tv_layout():
+    # the small-M kernel's 128-byte K unit: lane l, byte j -> (row l%16, byte
+    # 64*(j/16) + 16*(l/16) + j%16), the TV layout ((16,4),(16,2)):((128,16),(1,64))
+    # onto the row-major index kbyte + 128*row
+    tv = "((16,4),(16,2)):((128,16),(1,64))"
+    pts = [(l, j) for j in range(32) for l in range(64)]
+    got = thl.thl_kernel_index_map("mfma16_operand", pts)
+    want = _eval(tv, 2048)
+    assert [kb + 128 * r for r, kb in got] == want
+    assert sorted(want) == list(range(2048))  # every byte of 16 rows x 128 bytes once
+    # each 16-byte half is contiguous and 16-byte aligned: one fp4 scale block
+    # (32 elements), block 4*h + l/16 of the unit
+    for l in range(64):
+        for h in range(2):
+            kbs = [got[(16 * h + j) * 64 + l][1] for j in range(16)]
+            assert kbs == list(range(kbs[0], kbs[0] + 16)) and kbs[0] % 16 == 0
+            assert kbs[0] // 16 == 4 * h + l // 16
+
+
+def test_small_m_accumulator_map_is_the_tv_layout():
+    tv = "((16,4),4):((16,4),1)"
+    pts = [(l, v) for v in range(4) for l in range(64)]
+    got = thl.thl_kernel_index_map("mfma16_acc", pts)
+    want = _eval(tv, 256)
+    assert [r + 16 * c for r, c in got] == want
+    assert sorted(want) == list(range(256))
+    for l in range(64):  # four consecutive rows of one column per lane
+        rows = [got[v * 64 + l][0] for v in range(4)]
+        assert rows == list(range(rows[0], rows[0] + 4)) and len({got[v * 64 + l][1] for v in range(4)}) == 1
+
+
 def test_fp8_k_order_covers_each_k_once_per_row():
     for row in range(32):
         ks = sorted(k for lane in (row, row + 32) for (k, _) in

@@ -6,7 +6,8 @@
 // ("Technical Documentation: NVIDIA/cutlass", "CUTLASS Library"), with one
 // shape rule on top: the largest tile whose tile count still fills the 256
 // compute units (256x256 tiles, one workgroup per CU; then 256x128, two per
-// CU; then 128x128) is tried first.
+// CU; then 128x128) is tried first.  Below that, problems with at most 16
+// rows of op(A) go to the small-M kernel, which streams B once.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -30,7 +31,8 @@ struct Variant {
   bool a_kmajor, b_kmajor;  // opA == T, opB == N
   int bm, bn, threads, loadw;
   int occ;   // workgroups per CU the kernel is built for
-  int tier;  // 0: 256x256, 1: 256x128, 2: 128x128 (the shape rule's preference order)
+  int tier;  // 0: 256x256, 1: 256x128, 2: 128x128 (the shape rule's preference order);
+             // -1: the small-M kernel (M <= 16), chosen by its own rule
   LaunchFn launch;
 };
 
@@ -46,6 +48,9 @@ struct Variant {
       THL_V(FAM, NAME, OPS, AK, BK, 128, 128, 16, 4, 2, 2),   \
       THL_V(FAM, NAME, OPS, AK, BK, 128, 128, 4, 4, 2, 2)
 
+// The small-M kernel: 16 columns of D per workgroup, K split over 4 wavefronts.
+#define THL_VS(FAM, NAME) {NAME "_tn_skinny16_k4", FAM, true, true, 16, 16, 256, 16, 2, -1, &launch_skinny<FAM, 4>}
+
 const Variant kVariants[] = {
     THL_VARIANTS(FAM_BF16, "bf16", "tn", true, true),
     THL_VARIANTS(FAM_BF16, "bf16", "nn", false, true),
@@ -60,6 +65,11 @@ const Variant kVariants[] = {
     THL_V(FAM_FP4, "e2m1", "tn", true, true, 256, 256, 16, 4, 1, 0),
     THL_V(FAM_FP4, "e2m1", "tn", true, true, 128, 128, 16, 4, 2, 2),
     THL_V(FAM_FP4, "e2m1", "tn", true, true, 128, 128, 4, 4, 2, 2),
+    THL_VS(FAM_BF16, "bf16"),
+    THL_VS(FAM_F16, "f16"),
+    THL_VS(FAM_I8, "i8"),
+    THL_VS(FAM_FP8, "e4m3"),
+    THL_VS(FAM_FP4, "e2m1"),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -252,19 +262,25 @@ thl_status thl_gemm(int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
   const int want_tier = tiles_256 >= 256 ? 0 : (tiles_256x128 >= 256 ? 1 : 2);
   const Variant* pick = nullptr;
   bool family_built = false;
-  // Passes: the preferred tier, then each smaller tile, then anything that fits.
-  for (int pass = want_tier; pass <= 3 && !pick; ++pass) {
+  auto fits = [&](const Variant& v) {
+    bool ok = k == 0 || (aligned(A, lda_bytes, v.loadw) && aligned(B, ldb_bytes, v.loadw));
+    if (fam == FAM_FP4 && k > 0) ok = ok && aligned(s.sfa, s.ld_sfa, 16) && aligned(s.sfb, s.ld_sfb, 16);
+    return ok;
+  };
+  // The small-M kernel streams B once for at most 16 rows of A (K > 0).
+  const bool small_m = m <= 16 && k > 0;
+  // Passes: the small-M kernel where it applies, then the preferred tier,
+  // then each smaller tile, then any tiled variant that fits.
+  for (int pass = small_m ? -1 : want_tier; pass <= 3 && !pick; pass = pass < 0 ? want_tier : pass + 1) {
     for (const Variant& v : kVariants) {
       if (v.family != fam || v.a_kmajor != a_kmajor || v.b_kmajor != b_kmajor) continue;
       family_built = true;
       if (forced && *forced) {
-        if (std::strcmp(forced, v.name) != 0) continue;
-      } else if (pass < 3 && v.tier != pass) {
+        if (std::strcmp(forced, v.name) != 0 || (v.tier < 0 && !small_m)) continue;
+      } else if ((pass < 3 && v.tier != pass) || (pass == 3 && v.tier < 0)) {
         continue;
       }
-      bool fits = k == 0 || (aligned(A, lda_bytes, v.loadw) && aligned(B, ldb_bytes, v.loadw));
-      if (fam == FAM_FP4 && k > 0) fits = fits && aligned(s.sfa, s.ld_sfa, 16) && aligned(s.sfb, s.ld_sfb, 16);
-      if (fits) {
+      if (fits(v)) {
         pick = &v;
         break;
       }
@@ -319,6 +335,13 @@ thl_status thl_gemm(int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
   a.c_type = static_cast<int32_t>(dt->c);
   a.d_type = static_cast<int32_t>(dt->d);
   a.bias_type = static_cast<int32_t>(dt->bias);
+  if (pick->tier < 0) {  // small M: one workgroup per 16 columns
+    if (pick->launch(a, dim3(static_cast<unsigned>((n + 15) / 16)), reinterpret_cast<hipStream_t>(stream)) !=
+        hipSuccess)
+      return THL_ERR_HIP;
+    t_last_variant = pick->name;
+    return THL_OK;
+  }
   const int64_t tiles = static_cast<int64_t>(a.tiles_m) * a.tiles_n;
   if (tiles > INT32_MAX) return THL_ERR_UNSUPPORTED;
   // Persistent workgroups: at most as many as the device holds at once (a
@@ -338,7 +361,7 @@ thl_status thl_gemm(int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
 
 const char* thl_kernel_index_map_names(void) {
   return "xcd_remap,grouped_tile,swz,lds_offset,copy_source,mfma32_operand,mfma32_acc,fp8_32x32_k,tr16_source,"
-         "mm_lds_offset,mm_copy_source,tr16_operand,pair_lds_offset,pair_copy_source";
+         "mm_lds_offset,mm_copy_source,tr16_operand,pair_lds_offset,pair_copy_source,mfma16_operand,mfma16_acc";
 }
 
 int thl_kernel_index_map(const char* map, const int64_t* params, int64_t n, const int64_t* in, int64_t* out) {
@@ -382,6 +405,10 @@ int thl_kernel_index_map(const char* map, const int64_t* params, int64_t n, cons
       r0 = maps::pair_lds_offset(x, y, param(0));
     } else if (!std::strcmp(map, "pair_copy_source")) {
       maps::pair_copy_source(x, y, &r0, &r1);
+    } else if (!std::strcmp(map, "mfma16_operand")) {
+      maps::mfma16_operand(x, y, &r0, &r1);
+    } else if (!std::strcmp(map, "mfma16_acc")) {
+      maps::mfma16_acc(x, y, &r0, &r1);
     } else {
       return THL_ERR_INVALID;
     }

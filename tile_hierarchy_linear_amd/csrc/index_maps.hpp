@@ -125,6 +125,27 @@ THL_HD void mfma32_acc(int64_t lane, int64_t v, int64_t* row, int64_t* col) {
   *col = lane & 31;
 }
 
+// Small-M kernel, one 128-byte K unit of 16 operand rows (columns of B):
+// byte j (0..31) of lane l is byte 16*(l/16) + j of the unit for j < 16 and
+// 64 + 16*(l/16) + (j - 16) for j >= 16, of row l % 16: the TV layout
+// ((16,4),(16,2)):((128,16),(1,64)) onto the row-major (k_byte + 128*row)
+// index.  Each 16-byte half is one 16x16 MFMA's operand (16-bit, int8 and
+// fp4 families: 16 bytes a lane); fp8 takes all 32 bytes in one 16x16x128.
+// A lane's 16 bytes of fp4 are one 32-element scale block.
+THL_HD void mfma16_operand(int64_t lane, int64_t j, int64_t* row, int64_t* kbyte) {
+  *row = lane & 15;
+  *kbyte = (j >> 4) * 64 + 16 * (lane >> 4) + (j & 15);
+}
+
+// 16x16 MFMA accumulator: register v of lane l is element
+//   (row, col) = (4*(l/16) + v, l % 16)
+// i.e. the TV layout ((16,4),4):((16,4),1) onto the column-major
+// (row + 16*col) tile index: 4 consecutive rows of one column a lane.
+THL_HD void mfma16_acc(int64_t lane, int64_t v, int64_t* row, int64_t* col) {
+  *row = 4 * (lane >> 4) + v;
+  *col = lane & 15;
+}
+
 // fp8 32x32x64 (f8f6f4 with 8-bit data): each lane supplies 32 bytes; the
 // instruction reads them as K = 16*(l/32) + j for j < 16 and 32 + 16*(l/32) +
 // (j - 16) for j >= 16.  The kernels load both operands with the same per-lane
