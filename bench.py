@@ -6,7 +6,8 @@ in HBM.  The headline workload is the bf16 GEMM at M = N = K = 8192, all
 operands column-major (op N/N), with the relu(A.B + C + bias[m]) epilogue
 (bf16 out, fp32 accumulate); the fp8 (e4m3,
 per-tensor scales) and MXFP4 (e2m1 with E8M0 block scales, D = A.B + C)
-GEMMs at 8192^3 are timed the same way and reported in the same line.
+GEMMs at 8192^3 are timed the same way and reported in the same line, and
+so is the single-row fp8 GEMM (M = 1, N = K = 8192), against the HBM peak.
 
 Prints ONE JSON line on stdout (diagnostics go to stderr).
 """
@@ -160,7 +161,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--size", type=int, default=8192)
-    ap.add_argument("--only", default="", help="comma list of bf16,e4m3,e2m1 (default: all)")
+    ap.add_argument("--only", default="", help="comma list of bf16,e4m3,e2m1,m1 (default: all)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0)
@@ -185,7 +186,7 @@ def main():
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
     s = args.size
-    only = set(x for x in args.only.split(",") if x) or {"bf16", "e4m3", "e2m1"}
+    only = set(x for x in args.only.split(",") if x) or {"bf16", "e4m3", "e2m1", "m1"}
 
     results = {}
     headline = None
@@ -215,7 +216,7 @@ def main():
             f"via {variant}; parity {entry['parity_sampled']}")
         if key == "bf16":
             headline = (w, ms, byt, variant)
-        if headline is None and key == sorted(only)[0]:
+        if headline is None and key == min(only - {"m1"}):
             headline = (w, ms, byt, variant)
         if args.sweep_variants:
             fam = {"bf16": "bf16", "e4m3": "e4m3", "e2m1": "e2m1"}[key]
@@ -234,9 +235,38 @@ def main():
         del dp
         torch.cuda.empty_cache()
 
+    # The single-row fp8 configuration (M = 1, N = K = s): HBM-bound, so its
+    # roofline is bytes per second against the HBM peak.  A launch is about
+    # 12 us, so it is timed over ten times as many launches.
+    small_m = None
+    if "m1" in only:
+        w1 = wl.make("fp8", 1, s, s)
+        dp1 = DeviceProblem(w1)
+        ms1 = time_gemm(dp1, 10 * args.steps, 2 * args.warmup, stream)
+        v1 = thl.thl_last_variant()
+        byt1 = compulsory_bytes(w1)
+        gbs = byt1 / (ms1 * 1e-3) / 1e9
+        small_m = {"workload": f"fp8 e4m3 GEMM M=1, N=K={s}, op TN, per-tensor scales, bf16 out",
+                   "us": round(ms1 * 1e3, 2), "variant": v1,
+                   "tflops": round(w1.flops() / (ms1 * 1e-3) / 1e12, 2),
+                   "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": byt1,
+                                "traffic": measured_traffic(v1, w1.m, w1.n, w1.k)}}
+        try:
+            small_m["parity_sampled"] = quick_parity(w1, dp1)
+        except Exception as e:  # noqa: BLE001 -- reported, not fatal for timing
+            small_m["parity_sampled"] = f"error: {e}"
+        log(f"[m1] {ms1 * 1e3:.2f} us  {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of HBM peak) via {v1}; "
+            f"parity {small_m['parity_sampled']}")
+        del dp1
+        torch.cuda.empty_cache()
+
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib)
 
+    if headline is None:
+        print("--only needs one of bf16, e4m3, e2m1 for the headline line", file=sys.stderr)
+        sys.exit(2)
     w, ms, byt, variant = headline
     key = w.type_a
     tflops = w.flops() / (ms * 1e-3) / 1e12
@@ -264,6 +294,7 @@ def main():
                      "traffic": measured_traffic(variant, w.m, w.n, w.k),
                      "algorithmic_bytes": byt, "kernel_sources": kernel_source_hash()},
         "dtypes": results,
+        "small_m": small_m,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

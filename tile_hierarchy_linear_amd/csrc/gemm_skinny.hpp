@@ -101,12 +101,15 @@ constexpr uint32_t kSkinnyOutside = 0x70000000u;
 // every resource (below 2^28 with any lane offset, so no sum wraps).
 constexpr int kSkinnyPast = 0x08000000;
 
-template <int F, int KW>
+// UN: K units per batch of loads (two batches in flight per wavefront).  On
+// fp8 1 x 8192 x 8192, four wavefronts with two-unit batches stream B at
+// about 6.8 TB/s once running; deeper batches were slower (up to 4 units of
+// 8 in flight per wavefront measured).
+template <int F, int KW, int UN = 2>
 __global__ void __launch_bounds__(KW * 64) skinny_kernel(GemmArgs p) {
   using S = Skinny<F>;
   using Acc = typename S::Acc;
   constexpr bool INT = F == FAM_I8, SCALED = F == FAM_FP4;
-  constexpr int UN = 4;  // K units per batch of loads (two batches in flight)
   const int lane = static_cast<int>(threadIdx.x) & 63;
   // The wavefront index read from lane 0, so that the K range and every
   // offset built from it stay scalar.
