@@ -136,6 +136,36 @@ thl_status thl_gemm(int64_t m, int64_t n, int64_t k,
                     const thl_dtypes* dtypes, const thl_epilogue* epilogue,
                     const thl_scales* scales, struct ihipStream_t* stream);
 
+/*
+ * thl_gemm_batched -- `batch` independent problems of one shape in one launch
+ * (the batched GEMM, "L mode", of the "CUTLASS" knowledge-base page and of
+ * "Technical Documentation: NVIDIA/cutlass"):
+ *   D_z = act(alpha*s_a*s_b*op(A_z)*op(B_z) + beta*C_z + bias_z),  z = 0 .. batch-1,
+ * with X_z = X + z*stride_x for X in A, B, C, D, bias (strides in elements of
+ * each array's format; E2M1X2 strides count fp4 elements and must be even)
+ * and SFA_z = sfa + z*stride_sfa, SFB_z likewise (in bytes).  Every other
+ * argument means what it means for thl_gemm and applies to every problem;
+ * the same kernel variant runs all of them.  A stride of 0 shares that array
+ * between problems (not allowed for D when batch > 1).
+ * Extra rules: batch >= 0 (0 returns THL_OK with no launch), batch <= 65535
+ * (else THL_ERR_UNSUPPORTED); strides >= 0 (else THL_ERR_INVALID); with
+ * batch > 1, stride_d >= (n-1)*ldd + m so that no two D matrices overlap.
+ * Overlap checks take each array's whole span over the batch: D may alias C
+ * exactly (also stride_c == stride_d) and may not otherwise overlap the span
+ * of A, B, C, bias or the scales, even where the problems would interleave
+ * without sharing bytes.  Alignment rules apply to every problem's base
+ * (the strides in bytes keep the first base's alignment class).
+ */
+thl_status thl_gemm_batched(int64_t batch, int64_t m, int64_t n, int64_t k,
+                            const void* A, int64_t lda, int64_t stride_a, thl_op opA,
+                            const void* B, int64_t ldb, int64_t stride_b, thl_op opB,
+                            const void* C, int64_t ldc, int64_t stride_c,
+                            void* D, int64_t ldd, int64_t stride_d,
+                            float alpha, float beta,
+                            const thl_dtypes* dtypes, const thl_epilogue* epilogue, int64_t stride_bias,
+                            const thl_scales* scales, int64_t stride_sfa, int64_t stride_sfb,
+                            struct ihipStream_t* stream);
+
 /* Static text for a status code. */
 const char* thl_status_string(int status);
 

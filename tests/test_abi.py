@@ -183,3 +183,41 @@ def test_small_m_selection(fam, ta, td):
         assert call(m=17, n=0, k=k, types=types) == thl.THL_ERR_UNSUPPORTED
     finally:
         del os.environ["THL_FORCE_VARIANT"]
+
+
+def bcall(batch=2, m=64, n=64, k=64, sa=None, sb=None, sc=0, sd=None, sbias=0, d=D, c=None, beta=0.0,
+          types=("bf16", "f32", "f32", "none"), lda=None, ldb=None, opa="T", opb="N", a=A, b=B, bias=None,
+          flags=0, sc_struct=None, ssfa=0, ssfb=0):
+    ta, tc, td, tb = types
+    lda = lda if lda is not None else max(1, k if opa == "T" else m)
+    ldb = ldb if ldb is not None else max(1, k if opb == "N" else n)
+    sa = sa if sa is not None else lda * (m if opa == "T" else k)
+    sb = sb if sb is not None else ldb * (n if opb == "N" else k)
+    sd = sd if sd is not None else m * n
+    dts = thl.make_dtypes(ta, ta, tc, td, tb)
+    epi = thl.thl_epilogue(flags, bias)
+    return thl.thl_gemm_batched(batch, m, n, k, a, lda, sa, opa, b, ldb, sb, opb, c, max(1, m), sc, d, max(1, m), sd,
+                                1.0, beta, dts, epi, sbias, sc_struct, ssfa, ssfb, None)
+
+
+def test_batched_validation():
+    # batch 0 and empty problems return at once (no GPU needed)
+    assert bcall(batch=0) == thl.THL_OK
+    assert bcall(n=0) == thl.THL_OK
+    assert bcall(batch=-1) == thl.THL_ERR_INVALID
+    assert bcall(batch=65536) == thl.THL_ERR_UNSUPPORTED
+    for kw in ({"sa": -1}, {"sb": -64}, {"sd": -4096}, {"sbias": -1}):
+        assert bcall(**kw) == thl.THL_ERR_INVALID
+    # D matrices of two problems overlap
+    assert bcall(sd=64 * 64 - 1) == thl.THL_ERR_INVALID
+    assert bcall(sd=0) == thl.THL_ERR_INVALID
+    # D's span over the batch reaches A's span (A right after the first D)
+    assert bcall(a=D + 4 * 64 * 64, sd=2 * 64 * 64) == thl.THL_ERR_INVALID
+    # C may alias D only with the same stride
+    assert bcall(c=D, beta=1.0, sc=64 * 64 + 64, types=("bf16", "f32", "f32", "none")) == thl.THL_ERR_INVALID
+    # fp4 operand strides count fp4 elements and must be even
+    assert bcall(sa=33, k=64, types=("e2m1", "bf16", "bf16", "none"), lda=64, ldb=64) == thl.THL_ERR_INVALID
+    # a stride that breaks every variant's 4-byte alignment (the second
+    # problem's A would start 2 bytes off)
+    assert bcall(sa=64 * 64 + 1) == thl.THL_ERR_MISALIGNED
+    assert bcall(n=0, sa=64 * 64 + 1) == thl.THL_ERR_MISALIGNED  # selection runs before the quick return

@@ -442,3 +442,66 @@ def test_vector_epilogue_matches_general_path_at_8192():
     a, b = outs
     bad = (a - b).abs() > 2.0 ** -7 * torch.maximum(a.abs(), b.abs()) + 1e-6
     assert int(bad.sum()) == 0, f"{int(bad.sum())} elements differ by more than one bf16 ulp"
+
+
+def _check_batched(ws, shared=(), expect=None):
+    from oracle import compare
+    from workloads.device import BatchedDeviceProblem
+
+    import tile_hierarchy_linear_amd as thl
+
+    w0 = ws[0]
+    _say(f"[batched] {w0.name} L={len(ws)} m={w0.m} n={w0.n} k={w0.k} op={w0.op_a}{w0.op_b} shared={shared}")
+    bp = BatchedDeviceProblem(ws, shared=shared)
+    st = bp.run()
+    assert st == 0, f"thl_gemm_batched status {st}"
+    torch.cuda.synchronize()
+    if expect:
+        assert expect in thl.thl_last_variant()
+    for z, w in enumerate(ws):
+        got = bp.d_all(z)
+        ii, jj = np.meshgrid(np.arange(w.m), np.arange(w.n), indexing="ij")
+        res = compare.parity_check(w, got.ravel(), ii.ravel(), jj.ravel())
+        assert res["ok"], (z, res)
+
+
+@pytest.mark.parametrize("kind,m,n,k,kw,shared,expect", [
+    ("bf16", 260, 200, 136, {}, (), None),                      # N/N, relu(A.B + C + bias), bias per problem
+    ("bf16", 300, 520, 256, {"op_a": "T", "op_b": "T"}, ("bias",), None),
+    ("fp16", 129, 65, 255, {"lda": 256, "ldb": 256}, ("b",), None),  # one B for every problem
+    ("int8", 130, 70, 200, {"lda": 208, "ldb": 208, "bias": True, "beta": 1.0, "act": "relu"}, (), None),
+    ("fp8", 300, 260, 512, {}, (), None),
+    ("mxfp4", 260, 130, 512, {}, (), None),                     # per-problem E8M0 scales
+    ("fp8", 1, 1000, 2048, {}, (), "skinny"),                   # small M, batched
+    ("mxfp4", 5, 70, 1024, {}, ("a", "sfa"), "skinny"),
+])
+def test_batched(kind, m, n, k, kw, shared, expect):
+    import workloads as wl
+
+    base = {"fp16": 1001, "bf16": 1002, "int8": 1003, "fp8": 1004, "mxfp4": 1005}[kind]
+    ws = [wl.make(kind, m, n, k, seed=base + 100 * z, **kw) for z in range(3)]
+    _check_batched(ws, shared=shared, expect=expect)
+
+
+def test_batched_many_tiles_and_d_aliasing_c():
+    # 6 problems of 4 x 4 tiles (more workgroups than one grid row holds at
+    # once), D written in place over C with equal strides
+    import workloads as wl
+    from oracle import compare
+    from workloads.device import BatchedDeviceProblem
+
+    ws = [wl.make("bf16", 1024, 1024, 256, seed=7000 + z) for z in range(6)]
+    bp = BatchedDeviceProblem(ws)
+    # D aliases C: copy C's bits into D's buffer and pass D as C
+    w0 = ws[0]
+    assert bp.strides["c"] == bp.stride_d
+    bp.d.view(torch.uint8)[: bp.bufs["c"].numel()].copy_(bp.bufs["c"])
+    bp.bufs["c"] = bp.d.view(torch.uint8)
+    st = bp.run()
+    assert st == 0, st
+    torch.cuda.synchronize()
+    for z, w in enumerate(ws):
+        got = bp.d_all(z)
+        ii, jj = np.meshgrid(np.arange(w.m), np.arange(w.n), indexing="ij")
+        res = compare.parity_check(w, got.ravel(), ii.ravel(), jj.ravel())
+        assert res["ok"], (z, res)

@@ -61,6 +61,11 @@ def _load():
                              ctypes.c_float, ctypes.c_float, ctypes.POINTER(thl_dtypes),
                              ctypes.POINTER(thl_epilogue), ctypes.POINTER(thl_scales), vp]
     lib.thl_gemm.restype = ctypes.c_int
+    lib.thl_gemm_batched.argtypes = [i64, i64, i64, i64, vp, i64, i64, ctypes.c_int, vp, i64, i64, ctypes.c_int,
+                                     vp, i64, i64, vp, i64, i64, ctypes.c_float, ctypes.c_float,
+                                     ctypes.POINTER(thl_dtypes), ctypes.POINTER(thl_epilogue), i64,
+                                     ctypes.POINTER(thl_scales), i64, i64, vp]
+    lib.thl_gemm_batched.restype = ctypes.c_int
     lib.thl_status_string.argtypes = [ctypes.c_int]
     lib.thl_status_string.restype = cp
     lib.thl_last_variant.restype = cp
@@ -141,6 +146,21 @@ def thl_gemm(m, n, k, A, lda, opA, B, ldb, opB, C, ldc, D, ldd, alpha, beta, dty
                              int(ldd), float(alpha), float(beta), ctypes.byref(dtypes),
                              ctypes.byref(epilogue) if epilogue is not None else None,
                              ctypes.byref(scales) if scales is not None else None, stream))
+
+
+def thl_gemm_batched(batch, m, n, k, A, lda, stride_a, opA, B, ldb, stride_b, opB, C, ldc, stride_c, D, ldd,
+                     stride_d, alpha, beta, dtypes, epilogue=None, stride_bias=0, scales=None, stride_sfa=0,
+                     stride_sfb=0, stream=None) -> int:
+    """Direct call of the batched C entry point (arguments as for thl_gemm,
+    plus the batch count and per-array strides in elements)."""
+    opa = THL_OP_T if opA in ("T", THL_OP_T) else (THL_OP_N if opA in ("N", THL_OP_N) else int(opA))
+    opb = THL_OP_T if opB in ("T", THL_OP_T) else (THL_OP_N if opB in ("N", THL_OP_N) else int(opB))
+    return int(_lib.thl_gemm_batched(int(batch), int(m), int(n), int(k), A, int(lda), int(stride_a), opa, B,
+                                     int(ldb), int(stride_b), opb, C, int(ldc), int(stride_c), D, int(ldd),
+                                     int(stride_d), float(alpha), float(beta), ctypes.byref(dtypes),
+                                     ctypes.byref(epilogue) if epilogue is not None else None, int(stride_bias),
+                                     ctypes.byref(scales) if scales is not None else None, int(stride_sfa),
+                                     int(stride_sfb), stream))
 
 
 def gemm(A, B, D, *, m, n, k, lda, ldb, ldd, op_a="T", op_b="N", C=None, ldc=0, alpha=1.0, beta=0.0,

@@ -144,9 +144,28 @@ Range matrix_range(const void* p, thl_dtype t, int64_t r, int64_t c, int64_t ld)
 
 bool overlaps(const Range& a, const Range& b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
 
+// Batched problems (L mode): `count` problems whose arrays lie at fixed
+// strides, in elements of each array's own format (E8M0 bytes for scales).
+struct Batch {
+  int64_t count = 1;
+  int64_t a = 0, b = 0, c = 0, d = 0, bias = 0, sfa = 0, sfb = 0;
+};
+
+// Byte range spanned by `count` r x c matrices `stride` elements apart.
+Range batch_range(const void* p, thl_dtype t, int64_t r, int64_t c, int64_t ld, int64_t count, int64_t stride) {
+  Range g = matrix_range(p, t, r, c, ld);
+  if (g.lo < g.hi && count > 1) g.hi += static_cast<uintptr_t>(bytes_of(t, (count - 1) * stride));
+  return g;
+}
+
 bool aligned(const void* p, int64_t pitch_bytes, int w) {
   return (reinterpret_cast<uintptr_t>(p) % w) == 0 && (pitch_bytes % w) == 0;
 }
+
+thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const void* A, int64_t lda, thl_op opA,
+                     const void* B, int64_t ldb, thl_op opB, const void* C, int64_t ldc, void* D, int64_t ldd,
+                     float alpha, float beta, const thl_dtypes* dt, const thl_epilogue* epi, const thl_scales* sc,
+                     struct ihipStream_t* stream);
 
 }  // namespace
 }  // namespace thl
@@ -184,8 +203,41 @@ thl_status thl_gemm(int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
                     int64_t ldb, thl_op opB, const void* C, int64_t ldc, void* D, int64_t ldd, float alpha,
                     float beta, const thl_dtypes* dt, const thl_epilogue* epi, const thl_scales* sc,
                     struct ihipStream_t* stream) {
+  return gemm_impl(Batch{}, m, n, k, A, lda, opA, B, ldb, opB, C, ldc, D, ldd, alpha, beta, dt, epi, sc, stream);
+}
+
+thl_status thl_gemm_batched(int64_t batch, int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
+                            int64_t stride_a, thl_op opA, const void* B, int64_t ldb, int64_t stride_b, thl_op opB,
+                            const void* C, int64_t ldc, int64_t stride_c, void* D, int64_t ldd, int64_t stride_d,
+                            float alpha, float beta, const thl_dtypes* dt, const thl_epilogue* epi,
+                            int64_t stride_bias, const thl_scales* sc, int64_t stride_sfa, int64_t stride_sfb,
+                            struct ihipStream_t* stream) {
+  Batch bt;
+  bt.count = batch;
+  bt.a = stride_a;
+  bt.b = stride_b;
+  bt.c = stride_c;
+  bt.d = stride_d;
+  bt.bias = stride_bias;
+  bt.sfa = stride_sfa;
+  bt.sfb = stride_sfb;
+  return gemm_impl(bt, m, n, k, A, lda, opA, B, ldb, opB, C, ldc, D, ldd, alpha, beta, dt, epi, sc, stream);
+}
+
+}  // extern "C"
+
+namespace thl {
+namespace {
+
+thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const void* A, int64_t lda, thl_op opA,
+                     const void* B, int64_t ldb, thl_op opB, const void* C, int64_t ldc, void* D, int64_t ldd,
+                     float alpha, float beta, const thl_dtypes* dt, const thl_epilogue* epi, const thl_scales* sc,
+                     struct ihipStream_t* stream) {
   // ---- arguments
   if (!dt || m < 0 || n < 0 || k < 0) return THL_ERR_INVALID;
+  if (bt.count < 0 || bt.a < 0 || bt.b < 0 || bt.c < 0 || bt.d < 0 || bt.bias < 0 || bt.sfa < 0 || bt.sfb < 0)
+    return THL_ERR_INVALID;
+  if (bt.count > 65535) return THL_ERR_UNSUPPORTED;  // one grid row per problem
   if ((opA != THL_OP_N && opA != THL_OP_T) || (opB != THL_OP_N && opB != THL_OP_T)) return THL_ERR_INVALID;
   if (m > INT32_MAX || n > INT32_MAX || k > INT32_MAX) return THL_ERR_UNSUPPORTED;
   const unsigned flags = epi ? epi->flags : 0u;
@@ -220,7 +272,11 @@ thl_status thl_gemm(int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
   if (ldd < (m > 1 ? m : 1)) return THL_ERR_INVALID;
   if (beta != 0.0f && ldc < (m > 1 ? m : 1)) return THL_ERR_INVALID;
   if (fam == FAM_FP4 && ((lda % 2) != 0 || (ldb % 2) != 0)) return THL_ERR_INVALID;
-  const bool work = m > 0 && n > 0;
+  const bool work = m > 0 && n > 0 && bt.count > 0;
+  // Batched: the D matrices may not overlap one another; fp4 operands move
+  // by whole bytes.
+  if (work && bt.count > 1 && bt.d < (n - 1) * ldd + m) return THL_ERR_INVALID;
+  if (fam == FAM_FP4 && (bt.a % 2 != 0 || bt.b % 2 != 0)) return THL_ERR_INVALID;
   if (work && !D) return THL_ERR_INVALID;
   if (work && k > 0 && (!A || !B)) return THL_ERR_INVALID;
   if (work && beta != 0.0f && !C) return THL_ERR_INVALID;
@@ -233,18 +289,21 @@ thl_status thl_gemm(int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
   }
 
   // ---- overlap: D may alias C exactly; nothing else may overlap D
+  // (Batched: each array's whole span over the batch; a D that only
+  // interleaves with another array is refused too.)
   if (work) {
-    const Range rd = matrix_range(D, dt->d, m, n, ldd);
-    if (overlaps(rd, matrix_range(A, dt->a, rows_a, cols_a, lda))) return THL_ERR_INVALID;
-    if (overlaps(rd, matrix_range(B, dt->b, rows_b, cols_b, ldb))) return THL_ERR_INVALID;
+    const int64_t L = bt.count;
+    const Range rd = batch_range(D, dt->d, m, n, ldd, L, bt.d);
+    if (overlaps(rd, batch_range(A, dt->a, rows_a, cols_a, lda, L, bt.a))) return THL_ERR_INVALID;
+    if (overlaps(rd, batch_range(B, dt->b, rows_b, cols_b, ldb, L, bt.b))) return THL_ERR_INVALID;
     if (beta != 0.0f) {
-      const bool exact_alias = (C == D) && (ldc == ldd) && (dt->c == dt->d);
-      if (!exact_alias && overlaps(rd, matrix_range(C, dt->c, m, n, ldc))) return THL_ERR_INVALID;
+      const bool exact_alias = (C == D) && (ldc == ldd) && (dt->c == dt->d) && (L == 1 || bt.c == bt.d);
+      if (!exact_alias && overlaps(rd, batch_range(C, dt->c, m, n, ldc, L, bt.c))) return THL_ERR_INVALID;
     }
-    if (has_bias && overlaps(rd, matrix_range(epi->bias, dt->bias, m, 1, m))) return THL_ERR_INVALID;
+    if (has_bias && overlaps(rd, batch_range(epi->bias, dt->bias, m, 1, m, L, bt.bias))) return THL_ERR_INVALID;
     if (fam == FAM_FP4 && k > 0) {
-      if (overlaps(rd, matrix_range(s.sfa, THL_E8M0, k / 32, m, s.ld_sfa))) return THL_ERR_INVALID;
-      if (overlaps(rd, matrix_range(s.sfb, THL_E8M0, k / 32, n, s.ld_sfb))) return THL_ERR_INVALID;
+      if (overlaps(rd, batch_range(s.sfa, THL_E8M0, k / 32, m, s.ld_sfa, L, bt.sfa))) return THL_ERR_INVALID;
+      if (overlaps(rd, batch_range(s.sfb, THL_E8M0, k / 32, n, s.ld_sfb, L, bt.sfb))) return THL_ERR_INVALID;
     }
   }
 
@@ -262,9 +321,15 @@ thl_status thl_gemm(int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
   const int want_tier = tiles_256 >= 256 ? 0 : (tiles_256x128 >= 256 ? 1 : 2);
   const Variant* pick = nullptr;
   bool family_built = false;
+  // Batched: every problem's base keeps the alignment of the first.
+  const int64_t sa_bytes = bt.count > 1 ? bytes_of(dt->a, bt.a) : 0;
+  const int64_t sb_bytes = bt.count > 1 ? bytes_of(dt->b, bt.b) : 0;
   auto fits = [&](const Variant& v) {
-    bool ok = k == 0 || (aligned(A, lda_bytes, v.loadw) && aligned(B, ldb_bytes, v.loadw));
-    if (fam == FAM_FP4 && k > 0) ok = ok && aligned(s.sfa, s.ld_sfa, 16) && aligned(s.sfb, s.ld_sfb, 16);
+    bool ok = k == 0 || (aligned(A, lda_bytes, v.loadw) && aligned(B, ldb_bytes, v.loadw) &&
+                         sa_bytes % v.loadw == 0 && sb_bytes % v.loadw == 0);
+    if (fam == FAM_FP4 && k > 0)
+      ok = ok && aligned(s.sfa, s.ld_sfa, 16) && aligned(s.sfb, s.ld_sfb, 16) &&
+           (bt.count == 1 || (bt.sfa % 16 == 0 && bt.sfb % 16 == 0));
     return ok;
   };
   // The small-M kernel streams B once for at most 16 rows of A (K > 0).
@@ -332,12 +397,23 @@ thl_status thl_gemm(int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
     if (has_bias) vec = vec && (reinterpret_cast<uintptr_t>(epi->bias) & 15) == 0;
     if (vec) a.flags |= EPI_VEC;
   }
+  // Batch strides in bytes (zero for a single problem and for absent arrays).
+  if (bt.count > 1) {
+    a.bs_a = sa_bytes;
+    a.bs_b = sb_bytes;
+    a.bs_c = beta != 0.0f ? bytes_of(dt->c, bt.c) : 0;
+    a.bs_d = bytes_of(dt->d, bt.d);
+    a.bs_bias = has_bias ? bytes_of(dt->bias, bt.bias) : 0;
+    a.bs_sfa = fam == FAM_FP4 ? bt.sfa : 0;
+    a.bs_sfb = fam == FAM_FP4 ? bt.sfb : 0;
+    if ((a.bs_c % 16) || (a.bs_d % 16) || (a.bs_bias % 16)) a.flags &= ~EPI_VEC;
+  }
   a.c_type = static_cast<int32_t>(dt->c);
   a.d_type = static_cast<int32_t>(dt->d);
   a.bias_type = static_cast<int32_t>(dt->bias);
   if (pick->tier < 0) {  // small M: one workgroup per 16 columns
-    if (pick->launch(a, dim3(static_cast<unsigned>((n + 15) / 16)), reinterpret_cast<hipStream_t>(stream)) !=
-        hipSuccess)
+    if (pick->launch(a, dim3(static_cast<unsigned>((n + 15) / 16), static_cast<unsigned>(bt.count)),
+                     reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
       return THL_ERR_HIP;
     t_last_variant = pick->name;
     return THL_OK;
@@ -351,11 +427,17 @@ thl_status thl_gemm(int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
   if (ncu <= 0) return THL_ERR_HIP;
   const int64_t resident = static_cast<int64_t>(ncu) * pick->occ;
   const int64_t grid = tiles < resident ? tiles : resident;
-  if (pick->launch(a, dim3(static_cast<unsigned>(grid)), reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+  if (pick->launch(a, dim3(static_cast<unsigned>(grid), static_cast<unsigned>(bt.count)),
+                   reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return THL_ERR_HIP;
   t_last_variant = pick->name;
   return THL_OK;
 }
+
+}  // namespace
+}  // namespace thl
+
+extern "C" {
 
 // ---------------------------------------------------------------- index maps
 

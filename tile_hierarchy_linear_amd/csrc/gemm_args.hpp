@@ -35,6 +35,9 @@ struct GemmArgs {
   float alpha, beta;  // alpha already holds the per-tensor fp8 scales
   int32_t flags;      // EPI_* bits
   int32_t c_type, d_type, bias_type;
+  // Batched problems: problem blockIdx.y's arrays lie these many bytes
+  // further per problem (all zero for a single problem).
+  int64_t bs_a, bs_b, bs_c, bs_d, bs_bias, bs_sfa, bs_sfb;
 };
 
 

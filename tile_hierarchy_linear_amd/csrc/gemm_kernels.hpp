@@ -378,6 +378,20 @@ __device__ __forceinline__ uint8_t* ep_area() {
   return area;
 }
 
+// Batched problems (L mode, the "CUTLASS" knowledge-base page's batched
+// GEMM): grid row blockIdx.y computes problem blockIdx.y, whose operands,
+// scales, C, bias and D sit at fixed byte strides from the first problem's.
+__device__ __forceinline__ void offset_to_problem(GemmArgs& p) {
+  const int64_t z = blockIdx.y;
+  p.a += z * p.bs_a;
+  p.b += z * p.bs_b;
+  p.sfa += z * p.bs_sfa;
+  p.sfb += z * p.bs_sfb;
+  p.c = static_cast<const uint8_t*>(p.c) + z * p.bs_c;
+  p.d = static_cast<uint8_t*>(p.d) + z * p.bs_d;
+  p.bias = static_cast<const uint8_t*>(p.bias) + z * p.bs_bias;
+}
+
 // ------------------------------------------------------------ the kernel
 //
 // Pipeline (per wavefront, K-steps of 64 bytes per operand row, a ring of
@@ -408,6 +422,7 @@ __device__ __forceinline__ uint8_t* ep_area() {
 template <int F, int BM, int BN, int WM, int WN, int LOADW, int STAGES, int OCC, int SCW, bool AK, bool BK>
 __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 gemm_kernel(GemmArgs p) {
+  offset_to_problem(p);
   using T = Fam<F>;
   using Acc = typename T::Acc;
   constexpr int KB = maps::kStepBytes;

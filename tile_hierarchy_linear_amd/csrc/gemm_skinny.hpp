@@ -107,6 +107,7 @@ constexpr int kSkinnyPast = 0x08000000;
 // 8 in flight per wavefront measured).
 template <int F, int KW, int UN = 2>
 __global__ void __launch_bounds__(KW * 64) skinny_kernel(GemmArgs p) {
+  offset_to_problem(p);
   using S = Skinny<F>;
   using Acc = typename S::Acc;
   constexpr bool INT = F == FAM_I8, SCALED = F == FAM_FP4;

@@ -74,3 +74,79 @@ class DeviceProblem:
         if self.w.type_d == "i32":
             return host.to(torch.int64).numpy()
         return host.to(torch.float64).numpy()
+
+
+class BatchedDeviceProblem:
+    """Workloads of one shape and format packed at fixed strides in shared
+    device buffers and run with one thl_gemm_batched call.  Each array's
+    stride is its largest stored size rounded up to `pad` bytes (0 for an
+    array listed in `shared`, which then comes from the first workload).
+    The per-tensor fp8 scales, alpha, beta, activation and types are one set
+    for the whole batch: the first workload's.  The workloads are updated to
+    what runs (shared arrays and the fp8 scales copied from the first), so
+    that each can be checked against the oracle as it stands."""
+
+    def __init__(self, ws, device="cuda", shared=(), pad=256, d_fill=float("nan")):
+        self.ws = ws
+        w0 = ws[0]
+        for w in ws[1:]:
+            w.a_scale, w.b_scale = w0.a_scale, w0.b_scale
+            for name in shared:
+                setattr(w, name, getattr(w0, name))
+        self.L = len(ws)
+        self.strides = {}
+        self.bufs = {}
+        eb = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "i32": 4, "e4m3": 1, "e2m1": 0.5, "e8m0": 1}
+        types = {"a": w0.type_a, "b": w0.type_b, "c": w0.type_c, "bias": w0.type_bias, "sfa": "e8m0",
+                 "sfb": "e8m0"}
+        for name in ("a", "b", "c", "bias", "sfa", "sfb"):
+            arrs = [getattr(w, name) for w in ws]
+            if arrs[0] is None or (name == "c" and w0.beta == 0.0):
+                self.bufs[name], self.strides[name] = None, 0
+                continue
+            raws = [np.ascontiguousarray(x).view(np.uint8).reshape(-1) for x in arrs]
+            if name in shared:
+                raws = raws[:1]
+            sb = (max(len(r) for r in raws) + pad - 1) // pad * pad
+            host = np.zeros(sb * len(raws), np.uint8)
+            for z, r in enumerate(raws):
+                host[z * sb: z * sb + len(r)] = r
+            self.bufs[name] = torch.from_numpy(host).to(device)
+            self.strides[name] = 0 if name in shared else int(sb / eb[types[name]])
+        es_d = eb[w0.type_d]
+        self.stride_d = (w0.ldd * max(1, w0.n) * es_d + pad - 1) // pad * pad // es_d
+        self.d = torch.empty((self.L * self.stride_d,), dtype=_TORCH_D[w0.type_d], device=device)
+        if w0.type_d == "i32":
+            self.d.fill_(-(2 ** 31) + 7)
+        else:
+            self.d.fill_(d_fill)
+
+    def run(self, stream=None):
+        w = self.ws[0]
+        b = self.bufs
+
+        def ptr(name):
+            t = b[name]
+            return t.data_ptr() if t is not None and t.numel() else None
+
+        dt = thl.make_dtypes(w.type_a, w.type_b, w.type_c, w.type_d, w.type_bias if w.bias is not None else "none")
+        flags = (thl.THL_EPI_BIAS if w.bias is not None else 0) | \
+            {"none": 0, "relu": thl.THL_EPI_RELU, "gelu": thl.THL_EPI_GELU}[w.act]
+        epi = thl.thl_epilogue(flags, ptr("bias"))
+        sc = thl.thl_scales(float(w.a_scale), float(w.b_scale), ptr("sfa"), int(w.ld_sfa), ptr("sfb"),
+                            int(w.ld_sfb))
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        s = self.strides
+        return thl.thl_gemm_batched(self.L, w.m, w.n, w.k, ptr("a"), w.lda, s["a"], w.op_a, ptr("b"), w.ldb,
+                                    s["b"], w.op_b, ptr("c"), w.ldc or max(1, w.m), s["c"], self.d.data_ptr(),
+                                    w.ldd, self.stride_d, w.alpha, w.beta, dt, epi, s["bias"], sc, s["sfa"],
+                                    s["sfb"], stream)
+
+    def d_all(self, z) -> np.ndarray:
+        """All of problem z's D as an (m, n) array [i, j]."""
+        w = self.ws[z]
+        host = self.d[z * self.stride_d: z * self.stride_d + w.ldd * w.n].cpu().reshape(w.n, w.ldd)[:, : w.m].T
+        if w.type_d == "i32":
+            return host.to(torch.int64).numpy()
+        return host.to(torch.float64).numpy()
