@@ -7,7 +7,8 @@ operands column-major (op N/N), with the relu(A.B + C + bias[m]) epilogue
 (bf16 out, fp32 accumulate); the fp8 (e4m3,
 per-tensor scales) and MXFP4 (e2m1 with E8M0 block scales, D = A.B + C)
 GEMMs at 8192^3 are timed the same way and reported in the same line, and
-so is the single-row fp8 GEMM (M = 1, N = K = 8192), against the HBM peak.
+so are the single-row fp8 GEMM (M = 1, N = K = 8192), against the HBM peak,
+and a batched bf16 GEMM (16 problems of 2048^3 in one launch).
 
 Prints ONE JSON line on stdout (diagnostics go to stderr).
 """
@@ -161,7 +162,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--size", type=int, default=8192)
-    ap.add_argument("--only", default="", help="comma list of bf16,e4m3,e2m1,m1 (default: all)")
+    ap.add_argument("--only", default="", help="comma list of bf16,e4m3,e2m1,m1,batched (default: all)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0)
@@ -186,7 +187,7 @@ def main():
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
     s = args.size
-    only = set(x for x in args.only.split(",") if x) or {"bf16", "e4m3", "e2m1", "m1"}
+    only = set(x for x in args.only.split(",") if x) or {"bf16", "e4m3", "e2m1", "m1", "batched"}
 
     results = {}
     headline = None
@@ -216,7 +217,7 @@ def main():
             f"via {variant}; parity {entry['parity_sampled']}")
         if key == "bf16":
             headline = (w, ms, byt, variant)
-        if headline is None and key == min(only - {"m1"}):
+        if headline is None and key == min(only - {"m1", "batched"}):
             headline = (w, ms, byt, variant)
         if args.sweep_variants:
             fam = {"bf16": "bf16", "e4m3": "e4m3", "e2m1": "e2m1"}[key]
@@ -261,6 +262,38 @@ def main():
         del dp1
         torch.cuda.empty_cache()
 
+    # Batched (L mode): 16 problems of the headline's layout and epilogue at
+    # M = N = K = s/4, one thl_gemm_batched launch.
+    batched = None
+    if "batched" in only:
+        from oracle import compare
+        from workloads.device import BatchedDeviceProblem
+
+        L, sz = 16, max(256, s // 4)
+        t0 = time.perf_counter()
+        ws = [wl.make("bf16", sz, sz, sz, seed=1002 + 100 * z) for z in range(L)]
+        bp = BatchedDeviceProblem(ws)
+        log(f"[batched] {L} problems generated and uploaded in {time.perf_counter() - t0:.1f} s")
+
+        msb = time_gemm(bp, args.steps, args.warmup, stream)
+        vb = thl.thl_last_variant()
+        tfb = L * ws[0].flops() / (msb * 1e-3) / 1e12
+        status = "ok"
+        for z in (0, L - 1):
+            rows, cols = ws[z].sample(512)
+            got = bp.d_all(z)[rows, cols]
+            res = compare.parity_check(ws[z], got, rows, cols)
+            if not res["ok"]:
+                status = f"FAIL(problem {z}: {res['n_bad']}/{res['n']})"
+        batched = {"workload": f"bf16 GEMM, {L} problems of M=N=K={sz}, op NN, D = relu(A.B + C + bias[m]), "
+                               "bf16 out, one batched launch",
+                   "ms": round(msb, 4), "tflops": round(tfb, 1), "frac_of_peak": round(tfb / PEAK_TFLOPS["bf16"], 4),
+                   "variant": vb, "parity_sampled": status}
+        log(f"[batched] {msb:.3f} ms  {tfb:.1f} TFLOP/s ({100 * tfb / PEAK_TFLOPS['bf16']:.1f}% of peak) via {vb}; "
+            f"parity {status}")
+        del bp
+        torch.cuda.empty_cache()
+
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib)
 
@@ -295,6 +328,7 @@ def main():
                      "algorithmic_bytes": byt, "kernel_sources": kernel_source_hash()},
         "dtypes": results,
         "small_m": small_m,
+        "batched": batched,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

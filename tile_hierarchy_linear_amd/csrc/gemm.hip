@@ -316,8 +316,9 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
   // ---- variant: first fit on family, alignment and shape
   const int64_t lda_bytes = bytes_of(dt->a, lda), ldb_bytes = bytes_of(dt->b, ldb);
   const char* forced = std::getenv("THL_FORCE_VARIANT");
-  const int64_t tiles_256 = ((m + 255) / 256) * ((n + 255) / 256);
-  const int64_t tiles_256x128 = ((m + 255) / 256) * ((n + 127) / 128);
+  // (tile counts over the whole batch: its problems fill the device together)
+  const int64_t tiles_256 = ((m + 255) / 256) * ((n + 255) / 256) * bt.count;
+  const int64_t tiles_256x128 = ((m + 255) / 256) * ((n + 127) / 128) * bt.count;
   const int want_tier = tiles_256 >= 256 ? 0 : (tiles_256x128 >= 256 ? 1 : 2);
   const Variant* pick = nullptr;
   bool family_built = false;
@@ -426,7 +427,13 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
   const int ncu = cu_count();
   if (ncu <= 0) return THL_ERR_HIP;
   const int64_t resident = static_cast<int64_t>(ncu) * pick->occ;
-  const int64_t grid = tiles < resident ? tiles : resident;
+  // Batched: the resident workgroups are shared out over the problems (a
+  // multiple of 8 per problem while that many fit), each grid row walking
+  // its own problem's tiles.
+  int64_t per = resident / bt.count;
+  if (per >= 8) per -= per % 8;
+  if (per < 1) per = 1;
+  const int64_t grid = tiles < per ? tiles : per;
   if (pick->launch(a, dim3(static_cast<unsigned>(grid), static_cast<unsigned>(bt.count)),
                    reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return THL_ERR_HIP;
