@@ -28,7 +28,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 # Test hook: the pins' mutation test points this at a deliberately broken build.
 _LIB_OVERRIDE = os.environ.get("THL_ORACLE_LIB_OVERRIDE")
 
-TYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3, "i32": 4, "e4m3": 5, "e2m1": 6, "e8m0": 7}
+TYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3, "i32": 4, "e4m3": 5, "e2m1": 6, "e8m0": 7, "e5m2": 9}
 ACT_CODES = {"none": 0, "relu": 1, "gelu": 2}
 
 

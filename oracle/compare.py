@@ -58,7 +58,7 @@ def check_exact(got, want) -> dict:
 
 def operand_max_abs(w, which: str) -> float:
     """max |a'| (or |b'|) over the dequantized operand of a workload, decoded
-    by the oracle's own decoders: per-tensor scale for e4m3, per-32-block
+    by the oracle's own decoders: per-tensor scale for fp8, per-32-block
     E8M0 scale for e2m1 (blocks run along the contiguous K)."""
     from . import decode
 
@@ -77,7 +77,7 @@ def operand_max_abs(w, which: str) -> float:
         scales = decode("e8m0", np.ascontiguousarray(sf)).reshape(rows, ld_sf)[:, : w.k // 32]
         vals = vals.reshape(rows, w.k // 32, 32) * scales[:, :, None]
         return float(np.abs(vals).max())
-    scale = (w.a_scale if which == "a" else w.b_scale) if fmt == "e4m3" else 1.0
+    scale = (w.a_scale if which == "a" else w.b_scale) if fmt in ("e4m3", "e5m2") else 1.0
     return float(np.abs(vals).max()) * scale
 
 

@@ -20,7 +20,7 @@
  *   for B with SFB(j, floor(p/32)): same document, "Blackwell SM100 GEMMs",
  *   "Block Scaled GEMMs" (index-notation formula), vector size 32 for the OCP
  *   mx types ("Blackwell Block Scaled Narrow Precision Data Types" table).
- * - The element formats (e4m3, e2m1, ue8m0 bit counts and signedness): same
+ * - The element formats (e4m3, e5m2, e2m1, ue8m0 bit counts and signedness): same
  *   document, "Blackwell Narrow Precision Data Types" table; the bit-level
  *   meaning of each code follows the OCP formats that table points to.
  * - The epilogue (bias, activation) applied to the GEMM result before the
@@ -53,6 +53,7 @@ enum {
     ORC_E4M3 = 5,
     ORC_E2M1 = 6, /* two OCP fp4 codes per byte, even element in the low nibble */
     ORC_E8M0 = 7,
+    ORC_E5M2 = 9,
 };
 
 enum { ORC_ACT_NONE = 0, ORC_ACT_RELU = 1, ORC_ACT_GELU = 2 };
@@ -142,6 +143,22 @@ static double dec_e4m3(uint8_t q)
     return s ? -mag : mag;
 }
 
+/* OCP E5M2: 1 sign, 5 exponent (bias 15), 2 mantissa bits, with the IEEE
+ * conventions: exponent 31 is infinity (mantissa 0) or NaN; largest finite
+ * magnitude 1.75 * 2^15 = 57344, smallest subnormal 2^-16. */
+static double dec_e5m2(uint8_t q)
+{
+    int s = q >> 7, e = (q >> 2) & 0x1f, f = q & 3;
+    double mag;
+    if (e == 31)
+        mag = f == 0 ? INFINITY : NAN;
+    else if (e == 0)
+        mag = ldexp((double)f, -16); /* f/4 * 2^-14 */
+    else
+        mag = ldexp((double)(4 + f), e - 17); /* (1 + f/4) * 2^(e-15) */
+    return s ? -mag : mag;
+}
+
 /* OCP E2M1: 1 sign, 2 exponent (bias 1), 1 mantissa bit; all codes finite. */
 static double dec_e2m1(unsigned nib)
 {
@@ -194,6 +211,8 @@ static double load_real(const void *base, int32_t type, int64_t idx)
     }
     case ORC_E8M0:
         return dec_e8m0(((const uint8_t *)base)[idx]);
+    case ORC_E5M2:
+        return dec_e5m2(((const uint8_t *)base)[idx]);
     }
     return NAN;
 }
@@ -213,7 +232,7 @@ static int64_t load_int(const void *base, int32_t type, int64_t idx)
 /* Public decoder, so that tests can pin each format on every code. */
 int oracle_decode(int32_t type, const void *src, int64_t count, double *out)
 {
-    if (type < ORC_F32 || type > ORC_E8M0)
+    if (type < ORC_F32 || (type > ORC_E8M0 && type != ORC_E5M2))
         return -1;
     for (int64_t t = 0; t < count; ++t)
         out[t] = load_real(src, type, t);

@@ -74,6 +74,20 @@ def test_e4m3_matches_table_bit_counts():
             assert Fraction(got[c]) == _minifloat(c, spec["e"], spec["m"], spec["signed"]), hex(c)
 
 
+def test_e5m2_matches_table_bit_counts():
+    spec = _format_table()["float_e5m2_t"]
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle.decode("e5m2", codes)
+    for c in range(256):
+        if (c & 0x7C) == 0x7C:  # OCP E5M2 keeps the IEEE specials: exponent 31 is inf (mantissa 0) or NaN
+            if c & 3:
+                assert math.isnan(got[c])
+            else:
+                assert got[c] == (-math.inf if c & 0x80 else math.inf)
+        else:
+            assert Fraction(got[c]) == _minifloat(c, spec["e"], spec["m"], spec["signed"]), hex(c)
+
+
 def test_e2m1_matches_table_bit_counts():
     spec = _format_table()["float_e2m1_t"]
     codes = np.arange(256, dtype=np.uint8)  # each byte holds two codes
@@ -125,6 +139,20 @@ def test_e4m3_all_codes_match_torch():
     assert same.all()
 
 
+def test_e5m2_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle.decode("e5m2", codes)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e5m2).double().numpy()
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all()
+
+
+def test_e5m2_hand_points():
+    got = oracle.decode("e5m2", np.array([0x3C, 0xBC, 0x7B, 0x04, 0x01, 0x7C, 0xFC, 0x7D, 0x00], np.uint8))
+    assert list(got[:7]) == [1.0, -1.0, 57344.0, 2.0 ** -14, 2.0 ** -16, math.inf, -math.inf]
+    assert math.isnan(got[7]) and got[8] == 0.0
+
+
 def test_e4m3_hand_points():
     got = oracle.decode("e4m3", np.array([0x38, 0xB8, 0x7E, 0x08, 0x01, 0x7F, 0xFF, 0x00], np.uint8))
     assert list(got[:5]) == [1.0, -1.0, 448.0, 2.0 ** -6, 2.0 ** -9]
@@ -169,6 +197,8 @@ def _values(fmt, x):
         return torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).double().numpy()
     if fmt == "e4m3":
         return torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn).double().numpy()
+    if fmt == "e5m2":
+        return torch.from_numpy(x.astype(np.float32)).to(torch.float8_e5m2).double().numpy()
     if fmt == "i8":
         return x.astype(np.int8).astype(np.float64)
     if fmt == "e2m1":
@@ -184,10 +214,12 @@ def _random_values(fmt, g, shape):
                         size=shape)
     if fmt == "e4m3":
         return _values(fmt, g.standard_normal(shape) * 20)
+    if fmt == "e5m2":
+        return _values(fmt, g.standard_normal(shape) * 1000)
     return _values(fmt, g.uniform(-1, 1, size=shape))
 
 
-FLOAT_FMTS = ["f16", "bf16", "e4m3", "e2m1"]
+FLOAT_FMTS = ["f16", "bf16", "e4m3", "e5m2", "e2m1"]
 ALL_FMTS = FLOAT_FMTS + ["i8"]
 
 
@@ -233,7 +265,7 @@ def test_permutation_a_permutes_rows_of_b(fmt):
     assert np.array_equal(d, b[perm].astype(d.dtype))
 
 
-@pytest.mark.parametrize("fmt", ["f16", "bf16", "e4m3", "i8"])
+@pytest.mark.parametrize("fmt", ["f16", "bf16", "e4m3", "e5m2", "i8"])
 @pytest.mark.parametrize("ops", [("N", "N"), ("N", "T"), ("T", "N"), ("T", "T")])
 def test_storage_op_does_not_change_the_result(fmt, ops):
     g = np.random.default_rng(3)

@@ -21,7 +21,7 @@ import torch
 TENSOR_IDS = {"a": 1, "b": 2, "c": 3, "bias": 4, "sample": 5}
 
 # Bytes per element of each stored format (fp4 packs two per byte).
-ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "i32": 4, "e4m3": 1, "e2m1": 0.5}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "i32": 4, "e4m3": 1, "e5m2": 1, "e2m1": 0.5}
 
 
 def rng(seed: int, tensor: str) -> np.random.Generator:
@@ -32,7 +32,7 @@ def rng(seed: int, tensor: str) -> np.random.Generator:
 
 def encode(x: np.ndarray, fmt: str) -> np.ndarray:
     """Round float64 values to ``fmt`` (round-to-nearest-even) and return the
-    stored bits: uint16 for f16/bf16, uint32 for f32, uint8 for e4m3, int8 and
+    stored bits: uint16 for f16/bf16, uint32 for f32, uint8 for e4m3/e5m2, int8 and
     int32 for the integer formats (values must already be integral)."""
     if fmt == "f32":
         return x.astype(np.float32).view(np.uint32)
@@ -43,6 +43,9 @@ def encode(x: np.ndarray, fmt: str) -> np.ndarray:
         return t.view(torch.int16).numpy().view(np.uint16)
     if fmt == "e4m3":
         t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.float8_e4m3fn)
+        return t.view(torch.uint8).numpy()
+    if fmt == "e5m2":
+        t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.float8_e5m2)
         return t.view(torch.uint8).numpy()
     if fmt == "i8":
         return x.astype(np.int8)
