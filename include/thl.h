@@ -57,7 +57,8 @@ typedef enum {
   THL_E4M3 = 5,   /* OCP fp8 E4M3 ("fn": bias 7, no infinities, S.1111.111 NaN, max 448) */
   THL_E2M1X2 = 6, /* OCP fp4 E2M1, two per byte along the contiguous dimension, even element low nibble */
   THL_E8M0 = 7,   /* OCP E8M0 scale: 2^(code-127), 0xff NaN */
-  THL_NONE = 8    /* "no such operand" (bias dtype when there is no bias) */
+  THL_NONE = 8,   /* "no such operand" (bias dtype when there is no bias) */
+  THL_E5M2 = 9    /* OCP fp8 E5M2 (bias 15, IEEE-style: S.11111.00 infinity, S.11111.xx NaN, max 57344) */
 } thl_dtype;
 
 typedef struct {
@@ -102,6 +103,7 @@ typedef struct {
  *     alpha must be 1 and beta 0 or 1 (the integer epilogue is exact, in int32).
  *   E4M3 operands, opA = T, opB = N: F32 accumulate, s_a, s_b = scales->a_scale,
  *     b_scale folded with alpha into one fp32 factor.
+ *   E5M2 operands (both), opA = T, opB = N: as E4M3.
  *   E2M1X2 operands, opA = T, opB = N, k % 32 == 0: F32 accumulate, element
  *     (i,p) of A multiplied by 2^(SFA(i, p/32) - 127), likewise B with SFB(j, p/32);
  *     scale rows 16-byte aligned (THL_ERR_MISALIGNED otherwise).

@@ -48,7 +48,7 @@ def test_status_strings():
 def test_variants_are_listed():
     vs = thl.variants()
     assert len(vs) == thl.thl_variant_count() > 0
-    for fam in ("bf16", "f16", "i8", "e4m3", "e2m1"):
+    for fam in ("bf16", "f16", "i8", "e4m3", "e5m2", "e2m1"):
         assert any(v.startswith(fam + "_") for v in vs)
     assert thl.thl_variant_name(-1) is None and thl.thl_variant_name(len(vs)) is None
 
@@ -106,6 +106,10 @@ def test_unsupported_combinations():
     sc = thl.thl_scales(1.0, 1.0, SFA, 1, SFB, 1)
     assert call(types=("e2m1", "f32", "bf16", "none"), k=48, sc=sc) == thl.THL_ERR_UNSUPPORTED  # k % 32
     assert call(types=("e4m3", "f32", "bf16", "none"), opb="T") == thl.THL_ERR_UNSUPPORTED
+    assert call(types=("e5m2", "f32", "bf16", "none"), opa="N") == thl.THL_ERR_UNSUPPORTED
+    mixed = thl.make_dtypes("e4m3", "e5m2", "f32", "bf16")  # one format per call
+    assert thl.thl_gemm(64, 64, 64, A, 64, "T", B, 64, "N", None, 64, D, 64, 1.0, 0.0, mixed, None, None,
+                        None) == thl.THL_ERR_UNSUPPORTED
 
 
 def test_mxfp4_needs_scales():
@@ -157,7 +161,8 @@ def test_forced_variant_must_fit():
 
 
 @pytest.mark.parametrize("fam,ta,td", [("bf16", "bf16", "bf16"), ("f16", "f16", "f32"), ("i8", "i8", "i32"),
-                                       ("e4m3", "e4m3", "bf16"), ("e2m1", "e2m1", "bf16")])
+                                       ("e4m3", "e4m3", "bf16"), ("e5m2", "e5m2", "bf16"),
+                                       ("e2m1", "e2m1", "bf16")])
 def test_small_m_selection(fam, ta, td):
     # n == 0 selects a variant without a launch (no GPU needed)
     tc = "i32" if ta == "i8" else "f32"

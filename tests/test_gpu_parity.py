@@ -129,7 +129,7 @@ def test_mxfp4_scale_groups_at_every_step_count(variant, k):
 
 
 SMALL_M_KINDS = [("fp16", "f16", 8), ("bf16", "bf16", 8), ("int8", "i8", 16), ("fp8", "e4m3", 16),
-                 ("mxfp4", "e2m1", 32)]
+                 ("fp8e5m2", "e5m2", 16), ("mxfp4", "e2m1", 32)]
 
 
 @pytest.mark.parametrize("kind,fam,q", SMALL_M_KINDS)
@@ -226,12 +226,13 @@ def test_int8_epilogue_bias_beta_relu():
     _check_full(wl.make("int8", 130, 70, 200, lda=208, ldb=208, act="relu", bias=True, beta=1.0))
 
 
-@pytest.mark.parametrize("variant_family", ["f16", "bf16", "i8", "e4m3", "e2m1"])
+@pytest.mark.parametrize("variant_family", ["f16", "bf16", "i8", "e4m3", "e5m2", "e2m1"])
 def test_every_variant(variant_family):
     import tile_hierarchy_linear_amd as thl
     import workloads as wl
 
-    kind = {"f16": "fp16", "bf16": "bf16", "i8": "int8", "e4m3": "fp8", "e2m1": "mxfp4"}[variant_family]
+    kind = {"f16": "fp16", "bf16": "bf16", "i8": "int8", "e4m3": "fp8", "e5m2": "fp8e5m2",
+            "e2m1": "mxfp4"}[variant_family]
     ops = {"tn": ("T", "N"), "nn": ("N", "N"), "tt": ("T", "T"), "nt": ("N", "T")}
     for v in thl.variants():
         if not v.startswith(variant_family + "_"):
@@ -505,3 +506,20 @@ def test_batched_many_tiles_and_d_aliasing_c():
         ii, jj = np.meshgrid(np.arange(w.m), np.arange(w.n), indexing="ij")
         res = compare.parity_check(w, got.ravel(), ii.ravel(), jj.ravel())
         assert res["ok"], (z, res)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 1, 1), (7, 17, 33), (65, 127, 129), (300, 200, 520), (4097, 1000, 2040)])
+def test_e5m2_shapes(m, n, k):
+    # OCP fp8 E5M2 operands (format code 1 of the f8f6f4 instructions): the
+    # tiled kernels (16- and 4-byte copies), the small-M kernel and ragged
+    # edges, every output checked
+    import workloads as wl
+
+    kw = {} if (m, n, k) == (4097, 1000, 2040) else dict(lda=_pad(k, 16), ldb=_pad(k, 16))
+    _check_full(wl.make("fp8e5m2", m, n, k, act="relu", bias=True, beta=1.0, **kw))
+
+
+def test_e5m2_8192_sampled():
+    import workloads as wl
+
+    _check_sampled(wl.make("fp8e5m2", 8192, 8192, 8192))

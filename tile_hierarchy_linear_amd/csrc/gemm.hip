@@ -62,6 +62,7 @@ const Variant kVariants[] = {
     THL_VARIANTS(FAM_F16, "f16", "nt", false, false),
     THL_VARIANTS(FAM_I8, "i8", "tn", true, true),
     THL_VARIANTS(FAM_FP8, "e4m3", "tn", true, true),
+    THL_VARIANTS(FAM_E5M2, "e5m2", "tn", true, true),
     THL_V(FAM_FP4, "e2m1", "tn", true, true, 256, 256, 16, 4, 1, 0),
     THL_V(FAM_FP4, "e2m1", "tn", true, true, 128, 128, 16, 4, 2, 2),
     THL_V(FAM_FP4, "e2m1", "tn", true, true, 128, 128, 4, 4, 2, 2),
@@ -69,6 +70,7 @@ const Variant kVariants[] = {
     THL_VS(FAM_F16, "f16"),
     THL_VS(FAM_I8, "i8"),
     THL_VS(FAM_FP8, "e4m3"),
+    THL_VS(FAM_E5M2, "e5m2"),
     THL_VS(FAM_FP4, "e2m1"),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
@@ -99,6 +101,8 @@ int family_of(thl_dtype t) {
       return FAM_I8;
     case THL_E4M3:
       return FAM_FP8;
+    case THL_E5M2:
+      return FAM_E5M2;
     case THL_E2M1X2:
       return FAM_FP4;
     default:
@@ -117,6 +121,7 @@ int64_t bytes_of(thl_dtype t, int64_t count) {
       return 2 * count;
     case THL_I8:
     case THL_E4M3:
+    case THL_E5M2:
     case THL_E8M0:
       return count;
     case THL_E2M1X2:
@@ -384,7 +389,7 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
   a.tiles_m = static_cast<int32_t>((m + pick->bm - 1) / pick->bm);
   a.tiles_n = static_cast<int32_t>((n + pick->bn - 1) / pick->bn);
   a.group_m = 8;
-  a.alpha = (fam == FAM_FP8) ? alpha * s.a_scale * s.b_scale : alpha;
+  a.alpha = (fam == FAM_FP8 || fam == FAM_E5M2) ? alpha * s.a_scale * s.b_scale : alpha;
   a.beta = beta;
   a.flags = static_cast<int32_t>(flags);
   // Vector epilogue: D (and C, bias) rows aligned for 16-byte runs along M,

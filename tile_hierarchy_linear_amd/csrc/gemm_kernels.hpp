@@ -83,8 +83,11 @@ struct Fam<FAM_I8> {
   }
 };
 
-template <>
-struct Fam<FAM_FP8> {
+// The two OCP fp8 formats on one instruction: format code 0 = E4M3, 1 = E5M2
+// for both operands; no block scale (constant zero scale operands select
+// the unscaled instruction).
+template <int FMT>
+struct Fam8 {
   static constexpr int LANE_CHUNKS = 2, KSUB = 1;
   static constexpr bool INT = false, SCALED = false;
   using Acc = v16f;
@@ -92,11 +95,13 @@ struct Fam<FAM_FP8> {
   static __device__ __forceinline__ Acc mma(const v4i* a, const v4i* b, Acc c, int, int) {
     const v8i av = __builtin_shufflevector(a[0], a[1], 0, 1, 2, 3, 4, 5, 6, 7);
     const v8i bv = __builtin_shufflevector(b[0], b[1], 0, 1, 2, 3, 4, 5, 6, 7);
-    // Format 0 = E4M3 for both operands; no block scale (constant zero scale
-    // operands select the unscaled instruction).
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 0, 0, 0, 0, 0, 0);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, FMT, FMT, 0, 0, 0, 0);
   }
 };
+template <>
+struct Fam<FAM_FP8> : Fam8<0> {};
+template <>
+struct Fam<FAM_E5M2> : Fam8<1> {};
 
 template <>
 struct Fam<FAM_FP4> {

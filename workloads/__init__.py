@@ -185,6 +185,7 @@ def make(kind: str, m: int, n: int, k: int, seed: int | None = None, *, op_a=Non
            'bf16'  bf16 N/N, U[-1,1] A, B, C, bias, bf16 out, D = relu(A.B + C + bias[m])
            'int8'  int8 T/N, uniform integers in [-128,127], int32 out, D = A.B
            'fp8'   e4m3 T/N, N(0,1) scaled per tensor to +-448, bf16 out, D = s_a s_b A.B
+           'fp8e5m2' e5m2 T/N, N(0,1) scaled per tensor to +-57344, otherwise as 'fp8'
            'mxfp4' e2m1 T/N, N(0,1) MX-quantized per 32 K-elements, C bf16 N(0,1),
                    bf16 out, D = A.B + C
     Keyword overrides change ops, leading dimensions, the epilogue and the
@@ -194,6 +195,7 @@ def make(kind: str, m: int, n: int, k: int, seed: int | None = None, *, op_a=Non
         "bf16": dict(seed=1002, op_a="N", op_b="N", type_ab="bf16", type_d="bf16"),
         "int8": dict(seed=1003, op_a="T", op_b="N", type_ab="i8", type_d="i32"),
         "fp8": dict(seed=1004, op_a="T", op_b="N", type_ab="e4m3", type_d="bf16"),
+        "fp8e5m2": dict(seed=1006, op_a="T", op_b="N", type_ab="e5m2", type_d="bf16"),
         "mxfp4": dict(seed=1005, op_a="T", op_b="N", type_ab="e2m1", type_d="bf16"),
     }[kind]
     seed = defaults["seed"] if seed is None else seed
@@ -246,12 +248,13 @@ def make(kind: str, m: int, n: int, k: int, seed: int | None = None, *, op_a=Non
         w["act"] = act or "none"
         if bias:
             w["bias"], w["type_bias"] = gbias.integers(-1000, 1000, size=(m,)).astype(np.int32), "i32"
-    elif kind == "fp8":
+    elif kind in ("fp8", "fp8e5m2"):
+        top = 448.0 if fmt == "e4m3" else 57344.0  # the format's largest finite magnitude
         xa, xb = ga.standard_normal((m, k)), gb.standard_normal((k, n))
-        sa = float(np.abs(xa).max()) / 448.0 if xa.size else 1.0
-        sb = float(np.abs(xb).max()) / 448.0 if xb.size else 1.0
+        sa = float(np.abs(xa).max()) / top if xa.size else 1.0
+        sb = float(np.abs(xb).max()) / top if xb.size else 1.0
         sa, sb = float(np.float32(sa or 1.0)), float(np.float32(sb or 1.0))
-        w["a"], w["b"] = _operand(xa / sa, "e4m3", op_a, lda), _operand(xb / sb, "e4m3", op_b, ldb)
+        w["a"], w["b"] = _operand(xa / sa, fmt, op_a, lda), _operand(xb / sb, fmt, op_b, ldb)
         w["a_scale"], w["b_scale"] = sa, sb
         w["beta"] = 0.0 if beta is None else beta
         if w["beta"] != 0.0:

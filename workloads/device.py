@@ -96,7 +96,7 @@ class BatchedDeviceProblem:
         self.L = len(ws)
         self.strides = {}
         self.bufs = {}
-        eb = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "i32": 4, "e4m3": 1, "e2m1": 0.5, "e8m0": 1}
+        eb = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "i32": 4, "e4m3": 1, "e5m2": 1, "e2m1": 0.5, "e8m0": 1}
         types = {"a": w0.type_a, "b": w0.type_b, "c": w0.type_c, "bias": w0.type_bias, "sfa": "e8m0",
                  "sfb": "e8m0"}
         for name in ("a", "b", "c", "bias", "sfa", "sfb"):
