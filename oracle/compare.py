@@ -67,7 +67,7 @@ def operand_max_abs(w, which: str) -> float:
     if raw.size == 0:
         return 0.0
     vals = decode(fmt, raw)
-    if fmt == "e2m1":
+    if w.sfa is not None:  # block-scaled (E2M1 or MXFP8 E4M3)
         sf = w.sfa if which == "a" else w.sfb
         ld_sf = w.ld_sfa if which == "a" else w.ld_sfb
         rows = sf.shape[0]
@@ -76,7 +76,8 @@ def operand_max_abs(w, which: str) -> float:
             return 0.0
         scales = decode("e8m0", np.ascontiguousarray(sf)).reshape(rows, ld_sf)[:, : w.k // 32]
         vals = vals.reshape(rows, w.k // 32, 32) * scales[:, :, None]
-        return float(np.abs(vals).max())
+        per_tensor = (w.a_scale if which == "a" else w.b_scale) if fmt == "e4m3" else 1.0
+        return float(np.abs(vals).max()) * per_tensor
     scale = (w.a_scale if which == "a" else w.b_scale) if fmt in ("e4m3", "e5m2") else 1.0
     return float(np.abs(vals).max()) * scale
 

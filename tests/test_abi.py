@@ -48,7 +48,7 @@ def test_status_strings():
 def test_variants_are_listed():
     vs = thl.variants()
     assert len(vs) == thl.thl_variant_count() > 0
-    for fam in ("bf16", "f16", "i8", "e4m3", "e5m2", "e2m1"):
+    for fam in ("bf16", "f16", "i8", "e4m3", "e5m2", "e2m1", "mxe4m3"):
         assert any(v.startswith(fam + "_") for v in vs)
     assert thl.thl_variant_name(-1) is None and thl.thl_variant_name(len(vs)) is None
 

@@ -226,13 +226,13 @@ def test_int8_epilogue_bias_beta_relu():
     _check_full(wl.make("int8", 130, 70, 200, lda=208, ldb=208, act="relu", bias=True, beta=1.0))
 
 
-@pytest.mark.parametrize("variant_family", ["f16", "bf16", "i8", "e4m3", "e5m2", "e2m1"])
+@pytest.mark.parametrize("variant_family", ["f16", "bf16", "i8", "e4m3", "e5m2", "e2m1", "mxe4m3"])
 def test_every_variant(variant_family):
     import tile_hierarchy_linear_amd as thl
     import workloads as wl
 
     kind = {"f16": "fp16", "bf16": "bf16", "i8": "int8", "e4m3": "fp8", "e5m2": "fp8e5m2",
-            "e2m1": "mxfp4"}[variant_family]
+            "e2m1": "mxfp4", "mxe4m3": "mxfp8"}[variant_family]
     ops = {"tn": ("T", "N"), "nn": ("N", "N"), "tt": ("T", "T"), "nt": ("N", "T")}
     for v in thl.variants():
         if not v.startswith(variant_family + "_"):
@@ -523,3 +523,37 @@ def test_e5m2_8192_sampled():
     import workloads as wl
 
     _check_sampled(wl.make("fp8e5m2", 8192, 8192, 8192))
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 1, 32), (7, 17, 64), (65, 127, 288), (300, 200, 1024), (260, 130, 1056),
+                                   (130, 300, 2048)])
+def test_mxfp8_shapes(m, n, k):
+    # MXFP8: e4m3 with one E8M0 scale per 32 K-elements, scale groups of
+    # eight K-steps; K from one block to 64 with partial last steps
+    import tile_hierarchy_linear_amd as thl
+    import workloads as wl
+
+    _check_full(wl.make("mxfp8", m, n, k, lda=_pad(k, 16), ldb=_pad(k, 16), beta=1.0, bias=True, act="relu"))
+    assert thl.thl_last_variant().startswith("mxe4m3_")
+
+
+@pytest.mark.parametrize("variant", ["mxe4m3_tn_256x256_v16_s4_o1", "mxe4m3_tn_128x128_v16_s4_o2"])
+def test_mxfp8_persistent_tiles_every_group_position(variant):
+    # several tiles per workgroup, and K-step counts 13 .. 33 (+ partial)
+    import workloads as wl
+
+    for k in (832, 1056, 1344, 2112):
+        _check_full(wl.make("mxfp8", 600, 520, k), variant=variant)
+
+
+def test_mxfp8_8192_sampled():
+    import workloads as wl
+
+    _check_sampled(wl.make("mxfp8", 8192, 8192, 8192))
+
+
+def test_mxfp8_batched():
+    import workloads as wl
+
+    ws = [wl.make("mxfp8", 300, 260, 512, seed=1007 + 100 * z) for z in range(3)]
+    _check_batched(ws, expect="mxe4m3")

@@ -348,6 +348,24 @@ def test_bruteforce_exact_on_tiny_inputs(fmt, trial):
             assert abs(Fraction(got[i, j]) - want[i, j]) <= Fraction(2) ** -48 * (1 + abs(want[i, j]))
 
 
+@pytest.mark.parametrize("trial", range(3))
+def test_bruteforce_exact_mxfp8(trial):
+    # e4m3 elements with E8M0 block scales (MXFP8): the block-scaled sum is
+    # the same definition as for e2m1, now over 8-bit elements
+    g = np.random.default_rng(300 + trial)
+    m, n, k = int(g.integers(1, 6)), int(g.integers(1, 6)), 96
+    a, b = _random_values("e4m3", g, (m, k)), _random_values("e4m3", g, (k, n))
+    sfa = g.integers(118, 136, size=(m, k // 32)).astype(np.uint8)
+    sfb = g.integers(118, 136, size=(n, k // 32)).astype(np.uint8)
+    p = _problem("e4m3", a, b, "T", "N", alpha=0.75, a_scale=2.0, b_scale=0.5, sfa=sfa, ld_sfa=k // 32,
+                 sfb=sfb, ld_sfb=k // 32)
+    got = _full(p)
+    want = _exact_reference("e4m3", a, b, alpha=0.75, sfa=sfa, sfb=sfb)  # a_scale * b_scale = 1
+    for i in range(m):
+        for j in range(n):
+            assert abs(Fraction(got[i, j]) - want[i, j]) <= Fraction(2) ** -48 * (1 + abs(want[i, j]))
+
+
 def test_bruteforce_int8_exact():
     g = np.random.default_rng(7)
     for _ in range(5):

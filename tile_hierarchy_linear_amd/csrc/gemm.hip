@@ -66,6 +66,9 @@ const Variant kVariants[] = {
     THL_V(FAM_FP4, "e2m1", "tn", true, true, 256, 256, 16, 4, 1, 0),
     THL_V(FAM_FP4, "e2m1", "tn", true, true, 128, 128, 16, 4, 2, 2),
     THL_V(FAM_FP4, "e2m1", "tn", true, true, 128, 128, 4, 4, 2, 2),
+    THL_V(FAM_MX8, "mxe4m3", "tn", true, true, 256, 256, 16, 4, 1, 0),
+    THL_V(FAM_MX8, "mxe4m3", "tn", true, true, 128, 128, 16, 4, 2, 2),
+    THL_V(FAM_MX8, "mxe4m3", "tn", true, true, 128, 128, 4, 4, 2, 2),
     THL_VS(FAM_BF16, "bf16"),
     THL_VS(FAM_F16, "f16"),
     THL_VS(FAM_I8, "i8"),
@@ -251,8 +254,12 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
   const bool has_bias = (flags & THL_EPI_BIAS) != 0;
 
   // ---- supported combinations
-  const int fam = family_of(dt->a);
+  // E4M3 operands with both block-scale arrays given are MXFP8: one E8M0
+  // scale per 32 K-elements, as for E2M1.
+  const int fam0 = family_of(dt->a);
+  const int fam = (fam0 == FAM_FP8 && sc && sc->sfa && sc->sfb) ? FAM_MX8 : fam0;
   if (fam < 0 || dt->b != dt->a) return THL_ERR_UNSUPPORTED;
+  const bool block_scaled = fam == FAM_FP4 || fam == FAM_MX8;
   const bool int_path = fam == FAM_I8;
   if (int_path) {
     if (dt->acc != THL_I32 || dt->d != THL_I32) return THL_ERR_UNSUPPORTED;
@@ -268,7 +275,7 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
   // 8- and 4-bit operands: K-major only (op(A) rows, op(B) columns contiguous along K).
   const bool a_kmajor = opA == THL_OP_T, b_kmajor = opB == THL_OP_N;
   if (fam != FAM_BF16 && fam != FAM_F16 && (!a_kmajor || !b_kmajor)) return THL_ERR_UNSUPPORTED;
-  if (fam == FAM_FP4 && (k % 32 != 0)) return THL_ERR_UNSUPPORTED;
+  if (block_scaled && (k % 32 != 0)) return THL_ERR_UNSUPPORTED;
 
   // ---- leading dimensions and pointers
   const int64_t rows_a = (opA == THL_OP_N) ? m : k, cols_a = (opA == THL_OP_N) ? k : m;
@@ -288,7 +295,7 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
   if (work && has_bias && !epi->bias) return THL_ERR_INVALID;
   const thl_scales unit_scales = {1.0f, 1.0f, nullptr, 0, nullptr, 0};
   const thl_scales& s = sc ? *sc : unit_scales;
-  if (fam == FAM_FP4 && work && k > 0) {
+  if (block_scaled && work && k > 0) {
     if (!s.sfa || !s.sfb) return THL_ERR_INVALID;
     if (s.ld_sfa < k / 32 || s.ld_sfb < k / 32) return THL_ERR_INVALID;
   }
@@ -306,7 +313,7 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
       if (!exact_alias && overlaps(rd, batch_range(C, dt->c, m, n, ldc, L, bt.c))) return THL_ERR_INVALID;
     }
     if (has_bias && overlaps(rd, batch_range(epi->bias, dt->bias, m, 1, m, L, bt.bias))) return THL_ERR_INVALID;
-    if (fam == FAM_FP4 && k > 0) {
+    if (block_scaled && k > 0) {
       if (overlaps(rd, batch_range(s.sfa, THL_E8M0, k / 32, m, s.ld_sfa, L, bt.sfa))) return THL_ERR_INVALID;
       if (overlaps(rd, batch_range(s.sfb, THL_E8M0, k / 32, n, s.ld_sfb, L, bt.sfb))) return THL_ERR_INVALID;
     }
@@ -315,7 +322,7 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
   // Copy offsets inside a 256-row tile, and scale-row offsets, are 32-bit.
   if (k > 0 && (bytes_of(dt->a, lda) > (INT64_C(1) << 23) || bytes_of(dt->b, ldb) > (INT64_C(1) << 23)))
     return THL_ERR_UNSUPPORTED;
-  if (fam == FAM_FP4 && k > 0 && (m * s.ld_sfa > (INT64_C(1) << 31) || n * s.ld_sfb > (INT64_C(1) << 31)))
+  if (block_scaled && k > 0 && (m * s.ld_sfa > (INT64_C(1) << 31) || n * s.ld_sfb > (INT64_C(1) << 31)))
     return THL_ERR_UNSUPPORTED;
 
   // ---- variant: first fit on family, alignment and shape
@@ -333,7 +340,7 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
   auto fits = [&](const Variant& v) {
     bool ok = k == 0 || (aligned(A, lda_bytes, v.loadw) && aligned(B, ldb_bytes, v.loadw) &&
                          sa_bytes % v.loadw == 0 && sb_bytes % v.loadw == 0);
-    if (fam == FAM_FP4 && k > 0)
+    if (block_scaled && k > 0)
       ok = ok && aligned(s.sfa, s.ld_sfa, 16) && aligned(s.sfb, s.ld_sfb, 16) &&
            (bt.count == 1 || (bt.sfa % 16 == 0 && bt.sfb % 16 == 0));
     return ok;
@@ -389,7 +396,7 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
   a.tiles_m = static_cast<int32_t>((m + pick->bm - 1) / pick->bm);
   a.tiles_n = static_cast<int32_t>((n + pick->bn - 1) / pick->bn);
   a.group_m = 8;
-  a.alpha = (fam == FAM_FP8 || fam == FAM_E5M2) ? alpha * s.a_scale * s.b_scale : alpha;
+  a.alpha = (fam == FAM_FP8 || fam == FAM_E5M2 || fam == FAM_MX8) ? alpha * s.a_scale * s.b_scale : alpha;
   a.beta = beta;
   a.flags = static_cast<int32_t>(flags);
   // Vector epilogue: D (and C, bias) rows aligned for 16-byte runs along M,
@@ -410,8 +417,8 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
     a.bs_c = beta != 0.0f ? bytes_of(dt->c, bt.c) : 0;
     a.bs_d = bytes_of(dt->d, bt.d);
     a.bs_bias = has_bias ? bytes_of(dt->bias, bt.bias) : 0;
-    a.bs_sfa = fam == FAM_FP4 ? bt.sfa : 0;
-    a.bs_sfb = fam == FAM_FP4 ? bt.sfb : 0;
+    a.bs_sfa = block_scaled ? bt.sfa : 0;
+    a.bs_sfb = block_scaled ? bt.sfb : 0;
     if ((a.bs_c % 16) || (a.bs_d % 16) || (a.bs_bias % 16)) a.flags &= ~EPI_VEC;
   }
   a.c_type = static_cast<int32_t>(dt->c);

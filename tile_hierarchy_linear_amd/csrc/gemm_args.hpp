@@ -8,7 +8,8 @@
 namespace thl {
 
 // Operand families (one MFMA instruction each).
-enum Family { FAM_F16 = 0, FAM_BF16 = 1, FAM_I8 = 2, FAM_FP8 = 3, FAM_FP4 = 4, FAM_E5M2 = 5 };
+// FAM_MX8: e4m3 elements with one E8M0 scale per 32 K-elements (MXFP8).
+enum Family { FAM_F16 = 0, FAM_BF16 = 1, FAM_I8 = 2, FAM_FP8 = 3, FAM_FP4 = 4, FAM_E5M2 = 5, FAM_MX8 = 6 };
 
 // Element-type codes, equal to the public thl_dtype values.
 enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_I8 = 3, DT_I32 = 4 };

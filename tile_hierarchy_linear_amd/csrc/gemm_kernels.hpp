@@ -103,9 +103,28 @@ struct Fam<FAM_FP8> : Fam8<0> {};
 template <>
 struct Fam<FAM_E5M2> : Fam8<1> {};
 
+// MXFP8: e4m3 with one E8M0 scale per 32 K-elements.  The instruction applies
+// lane l's scale byte to K-block l/32 of row l%32, and reads lane g's 32
+// bytes as K 16g .. 16g+15 and 32+16g .. 32+16g+15 (maps::fp8_32x32_k_of):
+// so lane group g loads the step's 16-byte chunks g and g+2, and block g of
+// the step is exactly the 32 stored elements its scale belongs to.
+template <>
+struct Fam<FAM_MX8> {
+  static constexpr int LANE_CHUNKS = 2, KSUB = 1, SPS = 2;  // SPS: scale blocks per 64-byte step
+  static constexpr bool INT = false, SCALED = true;
+  using Acc = v16f;
+  template <int KS>
+  static __device__ __forceinline__ Acc mma(const v4i* a, const v4i* b, Acc c, int sa, int sb) {
+    const v8i av = __builtin_shufflevector(a[0], a[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    const v8i bv = __builtin_shufflevector(b[0], b[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    // Format 0 = E4M3 for both operands, E8M0 scales in byte 0.
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 0, 0, 0, sa, 0, sb);
+  }
+};
+
 template <>
 struct Fam<FAM_FP4> {
-  static constexpr int LANE_CHUNKS = 1, KSUB = 2;
+  static constexpr int LANE_CHUNKS = 1, KSUB = 2, SPS = 4;  // SPS: scale blocks per 64-byte step
   static constexpr bool INT = false, SCALED = true;
   using Acc = v16f;
   // Lane group g (lanes 32g .. 32g+31) takes the step's 32-element blocks 2g
@@ -120,6 +139,13 @@ struct Fam<FAM_FP4> {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, KS & 1, sa, KS & 1, sb);
   }
 };
+
+// Scale blocks per 64-byte K-step of a block-scaled family (0 without scales).
+template <class T>
+constexpr int sps_of() {
+  if constexpr (T::SCALED) return T::SPS;
+  return 0;
+}
 
 // Compile-time loop: f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>).
 // Guarantees unrolling where a loop body is too large for the unroller, so
@@ -446,9 +472,10 @@ gemm_kernel(GemmArgs p) {
   // a whole number with copies into a dummy area so every wave issues the
   // same.  (One 4-byte lane per row per step touched as many cache lines as
   // all the operand copies of the step.)
-  static_assert(SCW == 16, "scale copies bring 16 bytes (4 K-steps) a row");
+  static_assert(SCW == 16, "scale copies bring 16 bytes (16 blocks) a row");
   static_assert(BM % 64 == 0, "a scale copy instruction covers 64 rows of one operand");
-  constexpr int SG = 4;                                    // K-steps per scale group
+  // K-steps per scale group: 4 for fp4 (4 blocks a step), 8 for MXFP8 (2)
+  constexpr int SG = T::SCALED ? SCW / sps_of<T>() : 4;
   constexpr int SC_BYTES = T::SCALED ? (BM + BN) * SCW : 0;  // one group buffer
   constexpr int SC_INSTR = T::SCALED ? (BM + BN) / 64 : 0;
   constexpr int SC_LOADS = T::SCALED ? (SC_INSTR + NW - 1) / NW : 0;
@@ -478,7 +505,7 @@ gemm_kernel(GemmArgs p) {
   constexpr int RA = KSUB == 2 ? FM : FM / 2;
   // Steps per unrolled loop body: ring slots, fragment-slot parities and (fp4)
   // the scale-group buffer and position are compile-time constants inside it.
-  constexpr int UNROLL = T::SCALED ? (STAGES % (2 * SG) == 0 ? STAGES : (STAGES % SG == 0 ? 2 * STAGES : 0))
+  constexpr int UNROLL = T::SCALED ? (STAGES % (2 * SG) == 0 ? STAGES : ((2 * SG) % STAGES == 0 ? 2 * SG : 0))
                                    : ((STAGES % 2 == 0) ? STAGES : 2 * STAGES);
   static_assert(UNROLL > 0, "scale groups need STAGES to divide into 4 K-step groups");
   // Copies per wave issued in phase B of the step at position pos: paired,
@@ -817,7 +844,10 @@ gemm_kernel(GemmArgs p) {
   // reads as chunk c of sub-step ks.  A and B use the same assignment, so any
   // order of K within a step cancels in the dot product; fp4 gives each group
   // two adjacent 32-element blocks so that its scale bytes are adjacent too.
-  auto chunk_of = [](int ks, int g, int c) { return T::SCALED ? g * KSUB + ks : ks * CPM + g * LC + c; };
+  auto chunk_of = [](int ks, int g, int c) {
+    if constexpr (T::SCALED && LC == 2) return g + 2 * c;  // MXFP8: one scale block per lane group
+    return T::SCALED ? g * KSUB + ks : ks * CPM + g * LC + c;
+  };
   int chunk_off[KSUB][LC];
 #pragma unroll
   for (int ks = 0; ks < KSUB; ++ks)
@@ -920,12 +950,18 @@ gemm_kernel(GemmArgs p) {
       }
   };
 
-  // This lane's two scale bytes for fragment row f (A rows first, then B):
-  // blocks 2g and 2g+1 of the step for lane group g, zero-extended.  In the
-  // tail step, blocks at or past K get scale 1.0 (their data is zero).
-  // gbuf is the step's group buffer, kq its position in the group.
+  // This lane's scale bytes for fragment row f (A rows first, then B),
+  // zero-extended: fp4, blocks 2g and 2g+1 of the step for lane group g (one
+  // per sub-step); MXFP8, block g.  In the tail step, blocks at or past K get
+  // scale 1.0 (their data is zero).  gbuf is the step's group buffer, kq its
+  // position in the group.
   auto scale_of = [&](const uint8_t* gbuf, int kq, int f, bool tail) -> int {
     const int row_all = f < FM ? wm * TM + f * 32 + (lane & 31) : BM + wn * TN + (f - FM) * 32 + (lane & 31);
+    if constexpr (sps_of<T>() == 2) {
+      int v = gbuf[row_all * SCW + 2 * kq + (lane >> 5)];
+      if (tail && 2 * nkf + (lane >> 5) >= nkb) v = 127;
+      return v;
+    }
     int v = *reinterpret_cast<const uint16_t*>(gbuf + row_all * SCW + 4 * kq + 2 * (lane >> 5));
     if (tail) {
 #pragma unroll

@@ -85,6 +85,24 @@ def mx_quantize(x: np.ndarray, block: int = 32):
     return codes.reshape(r, k), (e + 127).astype(np.uint8)
 
 
+def mx_quantize_e4m3(x: np.ndarray, block: int = 32):
+    """OCP MX quantization of rows of ``x`` (R x K, K % block == 0) to E4M3:
+    per block the shared exponent is floor(log2(amax)) - 8 (8 is E4M3's
+    largest exponent), clamped to [-127, 127]; elements are x / 2^X rounded to
+    E4M3 (RNE; the block's largest lands below 512, so values past 448 are
+    clamped to 448 first, the format having no infinity).  Returns (codes
+    R x K uint8, scale codes R x K/block uint8)."""
+    r, k = x.shape
+    xb = x.reshape(r, k // block, block)
+    amax = np.abs(xb).max(axis=2)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 8
+    e = np.clip(e, -127, 127)
+    e = np.where(amax > 0, e, -127)
+    y = np.clip(xb / np.ldexp(1.0, e.astype(np.int64))[:, :, None], -448.0, 448.0)
+    return encode(y.reshape(r, k), "e4m3"), (e + 127).astype(np.uint8)
+
+
 # ----------------------------------------------------------------- storage
 
 def store_colmajor(s: np.ndarray, ld: int) -> np.ndarray:
@@ -188,6 +206,7 @@ def make(kind: str, m: int, n: int, k: int, seed: int | None = None, *, op_a=Non
            'fp8e5m2' e5m2 T/N, N(0,1) scaled per tensor to +-57344, otherwise as 'fp8'
            'mxfp4' e2m1 T/N, N(0,1) MX-quantized per 32 K-elements, C bf16 N(0,1),
                    bf16 out, D = A.B + C
+           'mxfp8' e4m3 T/N, N(0,1) MX-quantized per 32 K-elements, bf16 out, D = A.B
     Keyword overrides change ops, leading dimensions, the epilogue and the
     float C, D and bias types for the edge-case sweeps."""
     defaults = {
@@ -197,6 +216,7 @@ def make(kind: str, m: int, n: int, k: int, seed: int | None = None, *, op_a=Non
         "fp8": dict(seed=1004, op_a="T", op_b="N", type_ab="e4m3", type_d="bf16"),
         "fp8e5m2": dict(seed=1006, op_a="T", op_b="N", type_ab="e5m2", type_d="bf16"),
         "mxfp4": dict(seed=1005, op_a="T", op_b="N", type_ab="e2m1", type_d="bf16"),
+        "mxfp8": dict(seed=1007, op_a="T", op_b="N", type_ab="e4m3", type_d="bf16"),
     }[kind]
     seed = defaults["seed"] if seed is None else seed
     op_a = op_a or defaults["op_a"]
@@ -285,6 +305,33 @@ def make(kind: str, m: int, n: int, k: int, seed: int | None = None, *, op_a=Non
         mem_b[:, :k] = cb_codes
         w["a"], w["b"] = pack_e2m1(mem_a), pack_e2m1(mem_b)
         w["beta"] = 1.0 if beta is None else beta
+        if w["beta"] != 0.0:
+            ldc = ldc or max(1, m)
+            tc = type_c or "bf16"
+            w["c"], w["ldc"], w["type_c"] = store_colmajor(encode(gc.standard_normal((m, n)), tc), ldc), ldc, tc
+        w["act"] = act or "none"
+        if bias:
+            tb = type_bias or "bf16"
+            w["bias"], w["type_bias"] = encode(gbias.standard_normal(m), tb), tb
+    elif kind == "mxfp8":
+        assert op_a == "T" and op_b == "N", "MX blocks run along the contiguous K"
+        assert k % 32 == 0
+        xa, xb = ga.standard_normal((m, k)), gb.standard_normal((n, k))  # B drawn as its stored N x K
+        ca, w["sfa"] = mx_quantize_e4m3(xa) if k else (np.zeros((m, 0), np.uint8), np.zeros((m, 0), np.uint8))
+        cb, w["sfb"] = mx_quantize_e4m3(xb) if k else (np.zeros((n, 0), np.uint8), np.zeros((n, 0), np.uint8))
+        ld_sf = max(16, (k // 32 + 15) // 16 * 16)
+        w["ld_sfa"] = w["ld_sfb"] = ld_sf
+        pad_a = np.full((m, ld_sf), 127, np.uint8)
+        pad_a[:, : k // 32] = w["sfa"]
+        pad_b = np.full((n, ld_sf), 127, np.uint8)
+        pad_b[:, : k // 32] = w["sfb"]
+        w["sfa"], w["sfb"] = pad_a, pad_b
+        mem_a = np.zeros((m, lda), np.uint8)
+        mem_a[:, :k] = ca
+        mem_b = np.zeros((n, ldb), np.uint8)
+        mem_b[:, :k] = cb
+        w["a"], w["b"] = mem_a, mem_b
+        w["beta"] = 0.0 if beta is None else beta
         if w["beta"] != 0.0:
             ldc = ldc or max(1, m)
             tc = type_c or "bf16"
