@@ -4,8 +4,9 @@ A step is one pass of the hot path: one thl_gemm call (validation, dispatch,
 the tiled MFMA kernel with its fused epilogue) over inputs already resident
 in HBM.  The headline workload is the bf16 GEMM at M = N = K = 8192, all
 operands column-major (op N/N), with the relu(A.B + C + bias[m]) epilogue
-(bf16 out, fp32 accumulate); the fp8 (e4m3 and e5m2,
-per-tensor scales) and MXFP4 (e2m1 with E8M0 block scales, D = A.B + C)
+(bf16 out, fp32 accumulate); the fp8 (e4m3 and e5m2, per-tensor scales),
+MXFP8 (e4m3 with E8M0 block scales) and MXFP4 (e2m1 with E8M0 block scales,
+D = A.B + C)
 GEMMs at 8192^3 are timed the same way and reported in the same line, and
 so are the single-row fp8 GEMM (M = 1, N = K = 8192), against the HBM peak,
 and a batched bf16 GEMM (16 problems of 2048^3 in one launch).
@@ -25,7 +26,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 # MI355X published dense peaks (TFLOP/s, TOP/s for int8) and HBM bandwidth.
-PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2, "e5m2": 5033.2, "e2m1": 10066.3, "i8": 5033.2}
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2, "e5m2": 5033.2, "mxe4m3": 5033.2, "e2m1": 10066.3,
+               "i8": 5033.2}
 HBM_PEAK_GBS = 8000.0
 
 CSRC = os.path.join(ROOT, "tile_hierarchy_linear_amd", "csrc")
@@ -162,7 +164,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--size", type=int, default=8192)
-    ap.add_argument("--only", default="", help="comma list of bf16,e4m3,e5m2,e2m1,m1,batched (default: all)")
+    ap.add_argument("--only", default="", help="comma list of bf16,e4m3,e5m2,mxe4m3,e2m1,m1,batched (default: all)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0)
@@ -187,11 +189,12 @@ def main():
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
     s = args.size
-    only = set(x for x in args.only.split(",") if x) or {"bf16", "e4m3", "e5m2", "e2m1", "m1", "batched"}
+    only = set(x for x in args.only.split(",") if x) or {"bf16", "e4m3", "e5m2", "mxe4m3", "e2m1", "m1", "batched"}
 
     results = {}
     headline = None
-    for key, kind, kw in (("bf16", "bf16", {}), ("e4m3", "fp8", {}), ("e5m2", "fp8e5m2", {}), ("e2m1", "mxfp4", {})):
+    for key, kind, kw in (("bf16", "bf16", {}), ("e4m3", "fp8", {}), ("e5m2", "fp8e5m2", {}), ("mxe4m3", "mxfp8", {}),
+                          ("e2m1", "mxfp4", {})):
         if key not in only:
             continue
         t0 = time.perf_counter()
@@ -298,7 +301,7 @@ def main():
         copy_calibration(args.copy_calibration_mib)
 
     if headline is None:
-        print("--only needs one of bf16, e4m3, e5m2, e2m1 for the headline line", file=sys.stderr)
+        print("--only needs one of bf16, e4m3, e5m2, mxe4m3, e2m1 for the headline line", file=sys.stderr)
         sys.exit(2)
     w, ms, byt, variant = headline
     key = w.type_a
