@@ -366,6 +366,22 @@ def test_bruteforce_exact_mxfp8(trial):
             assert abs(Fraction(got[i, j]) - want[i, j]) <= Fraction(2) ** -48 * (1 + abs(want[i, j]))
 
 
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e5m2"), ("e5m2", "e4m3")])
+def test_mixed_fp8_bruteforce_exact(fa, fb):
+    # A and B in different fp8 formats: each operand decoded by its own format
+    g = np.random.default_rng(500)
+    m, n, k = 4, 5, 7
+    a, b = _random_values(fa, g, (m, k)), _random_values(fb, g, (k, n))
+    p = dict(m=m, n=n, k=k, a=wl.store_colmajor(wl.encode(a.T, fa), k), lda=k, op_a="T", type_a=fa,
+             b=wl.store_colmajor(wl.encode(b, fb), k), ldb=k, op_b="N", type_b=fb, alpha=1.25, a_scale=0.5,
+             b_scale=4.0)
+    got = _full(p)
+    want = _exact_reference(fa, a, b, alpha=2.5)  # 1.25 * 0.5 * 4
+    for i in range(m):
+        for j in range(n):
+            assert abs(Fraction(got[i, j]) - want[i, j]) <= Fraction(2) ** -48 * (1 + abs(want[i, j]))
+
+
 def test_bruteforce_int8_exact():
     g = np.random.default_rng(7)
     for _ in range(5):
