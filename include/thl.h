@@ -104,6 +104,10 @@ typedef struct {
  *   E4M3 operands, opA = T, opB = N: F32 accumulate, s_a, s_b = scales->a_scale,
  *     b_scale folded with alpha into one fp32 factor.
  *   E5M2 operands (both), opA = T, opB = N: as E4M3.
+ *   E4M3 A with E5M2 B, or E5M2 A with E4M3 B, opA = T, opB = N: as E4M3.
+ *   E4M3 operands with both scales->sfa and scales->sfb given (MXFP8), opA = T,
+ *     opB = N, k % 32 == 0: as E2M1X2's block scales (on top of the per-tensor
+ *     scales), with the same scale-row rules.
  *   E2M1X2 operands, opA = T, opB = N, k % 32 == 0: F32 accumulate, element
  *     (i,p) of A multiplied by 2^(SFA(i, p/32) - 127), likewise B with SFB(j, p/32);
  *     scale rows 16-byte aligned (THL_ERR_MISALIGNED otherwise).

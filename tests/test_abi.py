@@ -48,7 +48,7 @@ def test_status_strings():
 def test_variants_are_listed():
     vs = thl.variants()
     assert len(vs) == thl.thl_variant_count() > 0
-    for fam in ("bf16", "f16", "i8", "e4m3", "e5m2", "e2m1", "mxe4m3"):
+    for fam in ("bf16", "f16", "i8", "e4m3", "e5m2", "e2m1", "mxe4m3", "e4m3e5m2", "e5m2e4m3"):
         assert any(v.startswith(fam + "_") for v in vs)
     assert thl.thl_variant_name(-1) is None and thl.thl_variant_name(len(vs)) is None
 
@@ -107,9 +107,16 @@ def test_unsupported_combinations():
     assert call(types=("e2m1", "f32", "bf16", "none"), k=48, sc=sc) == thl.THL_ERR_UNSUPPORTED  # k % 32
     assert call(types=("e4m3", "f32", "bf16", "none"), opb="T") == thl.THL_ERR_UNSUPPORTED
     assert call(types=("e5m2", "f32", "bf16", "none"), opa="N") == thl.THL_ERR_UNSUPPORTED
-    mixed = thl.make_dtypes("e4m3", "e5m2", "f32", "bf16")  # one format per call
+    mixed = thl.make_dtypes("e4m3", "bf16", "f32", "bf16")  # mixed only within fp8
     assert thl.thl_gemm(64, 64, 64, A, 64, "T", B, 64, "N", None, 64, D, 64, 1.0, 0.0, mixed, None, None,
                         None) == thl.THL_ERR_UNSUPPORTED
+    mixed8 = thl.make_dtypes("e4m3", "e5m2", "f32", "bf16")  # e4m3 x e5m2: built, but not block-scaled
+    sc8 = thl.thl_scales(1.0, 1.0, SFA, 16, SFB, 16)
+    assert thl.thl_gemm(64, 64, 64, A, 64, "T", B, 64, "N", None, 64, D, 64, 1.0, 0.0, mixed8, None, sc8,
+                        None) == thl.THL_ERR_UNSUPPORTED
+    assert thl.thl_gemm(64, 0, 64, A, 64, "T", B, 64, "N", None, 64, D, 64, 1.0, 0.0, mixed8, None, None,
+                        None) == thl.THL_OK
+    assert thl.thl_last_variant().startswith("e4m3e5m2_")
 
 
 def test_mxfp4_needs_scales():

@@ -129,7 +129,8 @@ def test_mxfp4_scale_groups_at_every_step_count(variant, k):
 
 
 SMALL_M_KINDS = [("fp16", "f16", 8), ("bf16", "bf16", 8), ("int8", "i8", 16), ("fp8", "e4m3", 16),
-                 ("fp8e5m2", "e5m2", 16), ("mxfp4", "e2m1", 32)]
+                 ("fp8e5m2", "e5m2", 16), ("fp8e4e5", "e4m3e5m2", 16), ("fp8e5e4", "e5m2e4m3", 16),
+                 ("mxfp4", "e2m1", 32)]
 
 
 @pytest.mark.parametrize("kind,fam,q", SMALL_M_KINDS)
@@ -226,13 +227,14 @@ def test_int8_epilogue_bias_beta_relu():
     _check_full(wl.make("int8", 130, 70, 200, lda=208, ldb=208, act="relu", bias=True, beta=1.0))
 
 
-@pytest.mark.parametrize("variant_family", ["f16", "bf16", "i8", "e4m3", "e5m2", "e2m1", "mxe4m3"])
+@pytest.mark.parametrize("variant_family", ["f16", "bf16", "i8", "e4m3", "e5m2", "e2m1", "mxe4m3", "e4m3e5m2",
+                                            "e5m2e4m3"])
 def test_every_variant(variant_family):
     import tile_hierarchy_linear_amd as thl
     import workloads as wl
 
     kind = {"f16": "fp16", "bf16": "bf16", "i8": "int8", "e4m3": "fp8", "e5m2": "fp8e5m2",
-            "e2m1": "mxfp4", "mxe4m3": "mxfp8"}[variant_family]
+            "e2m1": "mxfp4", "mxe4m3": "mxfp8", "e4m3e5m2": "fp8e4e5", "e5m2e4m3": "fp8e5e4"}[variant_family]
     ops = {"tn": ("T", "N"), "nn": ("N", "N"), "tt": ("T", "T"), "nt": ("N", "T")}
     for v in thl.variants():
         if not v.startswith(variant_family + "_"):
@@ -557,3 +559,13 @@ def test_mxfp8_batched():
 
     ws = [wl.make("mxfp8", 300, 260, 512, seed=1007 + 100 * z) for z in range(3)]
     _check_batched(ws, expect="mxe4m3")
+
+
+@pytest.mark.parametrize("kind", ["fp8e4e5", "fp8e5e4"])
+@pytest.mark.parametrize("m,n,k", [(65, 127, 129), (300, 200, 520), (4097, 1000, 2040)])
+def test_mixed_fp8_shapes(kind, m, n, k):
+    # e4m3 A with e5m2 B and the other way round (one format code per operand)
+    import workloads as wl
+
+    kw = {} if (m, n, k) == (4097, 1000, 2040) else dict(lda=_pad(k, 16), ldb=_pad(k, 16))
+    _check_full(wl.make(kind, m, n, k, act="gelu", bias=True, beta=0.5, **kw))

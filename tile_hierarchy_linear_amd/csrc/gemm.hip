@@ -63,6 +63,8 @@ const Variant kVariants[] = {
     THL_VARIANTS(FAM_I8, "i8", "tn", true, true),
     THL_VARIANTS(FAM_FP8, "e4m3", "tn", true, true),
     THL_VARIANTS(FAM_E5M2, "e5m2", "tn", true, true),
+    THL_VARIANTS(FAM_E4E5, "e4m3e5m2", "tn", true, true),
+    THL_VARIANTS(FAM_E5E4, "e5m2e4m3", "tn", true, true),
     THL_V(FAM_FP4, "e2m1", "tn", true, true, 256, 256, 16, 4, 1, 0),
     THL_V(FAM_FP4, "e2m1", "tn", true, true, 128, 128, 16, 4, 2, 2),
     THL_V(FAM_FP4, "e2m1", "tn", true, true, 128, 128, 4, 4, 2, 2),
@@ -74,6 +76,8 @@ const Variant kVariants[] = {
     THL_VS(FAM_I8, "i8"),
     THL_VS(FAM_FP8, "e4m3"),
     THL_VS(FAM_E5M2, "e5m2"),
+    THL_VS(FAM_E4E5, "e4m3e5m2"),
+    THL_VS(FAM_E5E4, "e5m2e4m3"),
     THL_VS(FAM_FP4, "e2m1"),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
@@ -256,9 +260,14 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
   // ---- supported combinations
   // E4M3 operands with both block-scale arrays given are MXFP8: one E8M0
   // scale per 32 K-elements, as for E2M1.
+  // One fp8 format for A and the other for B is the mixed family of that order.
   const int fam0 = family_of(dt->a);
-  const int fam = (fam0 == FAM_FP8 && sc && sc->sfa && sc->sfb) ? FAM_MX8 : fam0;
-  if (fam < 0 || dt->b != dt->a) return THL_ERR_UNSUPPORTED;
+  const bool f8a = dt->a == THL_E4M3 || dt->a == THL_E5M2, f8b = dt->b == THL_E4M3 || dt->b == THL_E5M2;
+  const bool mixed = f8a && f8b && dt->a != dt->b;
+  const int fam = mixed ? (dt->a == THL_E4M3 ? FAM_E4E5 : FAM_E5E4)
+                        : ((fam0 == FAM_FP8 && sc && sc->sfa && sc->sfb) ? FAM_MX8 : fam0);
+  if (fam < 0 || (dt->b != dt->a && !mixed)) return THL_ERR_UNSUPPORTED;
+  if (mixed && sc && (sc->sfa || sc->sfb)) return THL_ERR_UNSUPPORTED;  // block scales: E4M3 only
   const bool block_scaled = fam == FAM_FP4 || fam == FAM_MX8;
   const bool int_path = fam == FAM_I8;
   if (int_path) {
@@ -396,7 +405,8 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
   a.tiles_m = static_cast<int32_t>((m + pick->bm - 1) / pick->bm);
   a.tiles_n = static_cast<int32_t>((n + pick->bn - 1) / pick->bn);
   a.group_m = 8;
-  a.alpha = (fam == FAM_FP8 || fam == FAM_E5M2 || fam == FAM_MX8) ? alpha * s.a_scale * s.b_scale : alpha;
+  const bool tensor_scaled = fam == FAM_FP8 || fam == FAM_E5M2 || fam == FAM_MX8 || fam == FAM_E4E5 || fam == FAM_E5E4;
+  a.alpha = tensor_scaled ? alpha * s.a_scale * s.b_scale : alpha;
   a.beta = beta;
   a.flags = static_cast<int32_t>(flags);
   // Vector epilogue: D (and C, bias) rows aligned for 16-byte runs along M,

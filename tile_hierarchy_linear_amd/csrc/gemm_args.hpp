@@ -8,8 +8,12 @@
 namespace thl {
 
 // Operand families (one MFMA instruction each).
-// FAM_MX8: e4m3 elements with one E8M0 scale per 32 K-elements (MXFP8).
-enum Family { FAM_F16 = 0, FAM_BF16 = 1, FAM_I8 = 2, FAM_FP8 = 3, FAM_FP4 = 4, FAM_E5M2 = 5, FAM_MX8 = 6 };
+// FAM_MX8: e4m3 elements with one E8M0 scale per 32 K-elements (MXFP8);
+// FAM_E4E5 / FAM_E5E4: e4m3 A with e5m2 B, and the other way round.
+enum Family {
+  FAM_F16 = 0, FAM_BF16 = 1, FAM_I8 = 2, FAM_FP8 = 3, FAM_FP4 = 4, FAM_E5M2 = 5, FAM_MX8 = 6,
+  FAM_E4E5 = 7, FAM_E5E4 = 8
+};
 
 // Element-type codes, equal to the public thl_dtype values.
 enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_I8 = 3, DT_I32 = 4 };

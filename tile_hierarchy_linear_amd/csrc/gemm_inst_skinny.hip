@@ -17,6 +17,8 @@ template hipError_t launch_skinny<FAM_F16, 4>(const GemmArgs&, dim3, hipStream_t
 template hipError_t launch_skinny<FAM_I8, 4>(const GemmArgs&, dim3, hipStream_t);
 template hipError_t launch_skinny<FAM_FP8, 4>(const GemmArgs&, dim3, hipStream_t);
 template hipError_t launch_skinny<FAM_E5M2, 4>(const GemmArgs&, dim3, hipStream_t);
+template hipError_t launch_skinny<FAM_E4E5, 4>(const GemmArgs&, dim3, hipStream_t);
+template hipError_t launch_skinny<FAM_E5E4, 4>(const GemmArgs&, dim3, hipStream_t);
 template hipError_t launch_skinny<FAM_FP4, 4>(const GemmArgs&, dim3, hipStream_t);
 
 }  // namespace thl

@@ -83,10 +83,10 @@ struct Fam<FAM_I8> {
   }
 };
 
-// The two OCP fp8 formats on one instruction: format code 0 = E4M3, 1 = E5M2
-// for both operands; no block scale (constant zero scale operands select
-// the unscaled instruction).
-template <int FMT>
+// The two OCP fp8 formats on one instruction: format code 0 = E4M3, 1 = E5M2,
+// one code for A (FA) and one for B (FB); no block scale (constant zero scale
+// operands select the unscaled instruction).
+template <int FA, int FB>
 struct Fam8 {
   static constexpr int LANE_CHUNKS = 2, KSUB = 1;
   static constexpr bool INT = false, SCALED = false;
@@ -95,13 +95,17 @@ struct Fam8 {
   static __device__ __forceinline__ Acc mma(const v4i* a, const v4i* b, Acc c, int, int) {
     const v8i av = __builtin_shufflevector(a[0], a[1], 0, 1, 2, 3, 4, 5, 6, 7);
     const v8i bv = __builtin_shufflevector(b[0], b[1], 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, FMT, FMT, 0, 0, 0, 0);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, FA, FB, 0, 0, 0, 0);
   }
 };
 template <>
-struct Fam<FAM_FP8> : Fam8<0> {};
+struct Fam<FAM_FP8> : Fam8<0, 0> {};
 template <>
-struct Fam<FAM_E5M2> : Fam8<1> {};
+struct Fam<FAM_E5M2> : Fam8<1, 1> {};
+template <>
+struct Fam<FAM_E4E5> : Fam8<0, 1> {};
+template <>
+struct Fam<FAM_E5E4> : Fam8<1, 0> {};
 
 // MXFP8: e4m3 with one E8M0 scale per 32 K-elements.  The instruction applies
 // lane l's scale byte to K-block l/32 of row l%32, and reads lane g's 32

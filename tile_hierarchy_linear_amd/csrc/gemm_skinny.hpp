@@ -62,20 +62,24 @@ struct Skinny<FAM_I8> {
 
 // fp8: one 16x16x128 instruction takes a lane's 32 bytes; A and B arrive in
 // the same per-lane byte order, so the order in which it reads K cancels.
-// Format code 0 = E4M3, 1 = E5M2.
-template <int FMT>
+// Format code 0 = E4M3, 1 = E5M2 (FA for A, FB for B).
+template <int FA, int FB>
 struct Skinny8 {
   using Acc = v4f;
   static __device__ __forceinline__ Acc unit(const v4i (&a)[2], const v4i (&b)[2], Acc c, unsigned, unsigned) {
     const v8i av = __builtin_shufflevector(a[0], a[1], 0, 1, 2, 3, 4, 5, 6, 7);
     const v8i bv = __builtin_shufflevector(b[0], b[1], 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, FMT, FMT, 0, 0, 0, 0);
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, FA, FB, 0, 0, 0, 0);
   }
 };
 template <>
-struct Skinny<FAM_FP8> : Skinny8<0> {};
+struct Skinny<FAM_FP8> : Skinny8<0, 0> {};
 template <>
-struct Skinny<FAM_E5M2> : Skinny8<1> {};
+struct Skinny<FAM_E5M2> : Skinny8<1, 1> {};
+template <>
+struct Skinny<FAM_E4E5> : Skinny8<0, 1> {};
+template <>
+struct Skinny<FAM_E5E4> : Skinny8<1, 0> {};
 
 template <>
 struct Skinny<FAM_FP4> {

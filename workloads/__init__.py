@@ -204,6 +204,7 @@ def make(kind: str, m: int, n: int, k: int, seed: int | None = None, *, op_a=Non
            'int8'  int8 T/N, uniform integers in [-128,127], int32 out, D = A.B
            'fp8'   e4m3 T/N, N(0,1) scaled per tensor to +-448, bf16 out, D = s_a s_b A.B
            'fp8e5m2' e5m2 T/N, N(0,1) scaled per tensor to +-57344, otherwise as 'fp8'
+           'fp8e4e5', 'fp8e5e4'  e4m3 A with e5m2 B, and the other way round
            'mxfp4' e2m1 T/N, N(0,1) MX-quantized per 32 K-elements, C bf16 N(0,1),
                    bf16 out, D = A.B + C
            'mxfp8' e4m3 T/N, N(0,1) MX-quantized per 32 K-elements, bf16 out, D = A.B
@@ -215,6 +216,8 @@ def make(kind: str, m: int, n: int, k: int, seed: int | None = None, *, op_a=Non
         "int8": dict(seed=1003, op_a="T", op_b="N", type_ab="i8", type_d="i32"),
         "fp8": dict(seed=1004, op_a="T", op_b="N", type_ab="e4m3", type_d="bf16"),
         "fp8e5m2": dict(seed=1006, op_a="T", op_b="N", type_ab="e5m2", type_d="bf16"),
+        "fp8e4e5": dict(seed=1008, op_a="T", op_b="N", type_ab="e4m3", type_b="e5m2", type_d="bf16"),
+        "fp8e5e4": dict(seed=1009, op_a="T", op_b="N", type_ab="e5m2", type_b="e4m3", type_d="bf16"),
         "mxfp4": dict(seed=1005, op_a="T", op_b="N", type_ab="e2m1", type_d="bf16"),
         "mxfp8": dict(seed=1007, op_a="T", op_b="N", type_ab="e4m3", type_d="bf16"),
     }[kind]
@@ -222,6 +225,7 @@ def make(kind: str, m: int, n: int, k: int, seed: int | None = None, *, op_a=Non
     op_a = op_a or defaults["op_a"]
     op_b = op_b or defaults["op_b"]
     fmt = defaults["type_ab"]
+    fmt_b = defaults.get("type_b", fmt)
     type_d = type_d or defaults["type_d"]
     ra, ca = stored_shape(m, k, op_a, "a")
     rb, cb = stored_shape(k, n, op_b, "b")
@@ -229,7 +233,7 @@ def make(kind: str, m: int, n: int, k: int, seed: int | None = None, *, op_a=Non
     ldb = ldb or max(1, rb)
     ldd = ldd or max(1, m)
     ga, gb, gc, gbias = rng(seed, "a"), rng(seed, "b"), rng(seed, "c"), rng(seed, "bias")
-    w = dict(name=kind, m=m, n=n, k=k, type_a=fmt, type_b=fmt, type_d=type_d, op_a=op_a,
+    w = dict(name=kind, m=m, n=n, k=k, type_a=fmt, type_b=fmt_b, type_d=type_d, op_a=op_a,
              op_b=op_b, lda=lda, ldb=ldb, ldd=ldd, seed=seed, alpha=alpha)
 
     if kind in ("fp16", "bf16"):
@@ -268,13 +272,13 @@ def make(kind: str, m: int, n: int, k: int, seed: int | None = None, *, op_a=Non
         w["act"] = act or "none"
         if bias:
             w["bias"], w["type_bias"] = gbias.integers(-1000, 1000, size=(m,)).astype(np.int32), "i32"
-    elif kind in ("fp8", "fp8e5m2"):
-        top = 448.0 if fmt == "e4m3" else 57344.0  # the format's largest finite magnitude
+    elif kind in ("fp8", "fp8e5m2", "fp8e4e5", "fp8e5e4"):
+        top = {"e4m3": 448.0, "e5m2": 57344.0}  # each format's largest finite magnitude
         xa, xb = ga.standard_normal((m, k)), gb.standard_normal((k, n))
-        sa = float(np.abs(xa).max()) / top if xa.size else 1.0
-        sb = float(np.abs(xb).max()) / top if xb.size else 1.0
+        sa = float(np.abs(xa).max()) / top[fmt] if xa.size else 1.0
+        sb = float(np.abs(xb).max()) / top[fmt_b] if xb.size else 1.0
         sa, sb = float(np.float32(sa or 1.0)), float(np.float32(sb or 1.0))
-        w["a"], w["b"] = _operand(xa / sa, fmt, op_a, lda), _operand(xb / sb, fmt, op_b, ldb)
+        w["a"], w["b"] = _operand(xa / sa, fmt, op_a, lda), _operand(xb / sb, fmt_b, op_b, ldb)
         w["a_scale"], w["b_scale"] = sa, sb
         w["beta"] = 0.0 if beta is None else beta
         if w["beta"] != 0.0:
