@@ -126,7 +126,9 @@ typedef struct {
  * D may alias C exactly (same pointer, ldc == ldd, c and d the same format);
  * any other overlap of D with A, B, C, bias or the scales is THL_ERR_INVALID.
  * m == 0 or n == 0 returns THL_OK with no launch; k == 0 gives
- * D = act(beta*C + bias).
+ * D = act(beta*C + bias).  m, n, k and every leading dimension above
+ * INT32_MAX, and byte leading dimensions of A or B above 2^23, return
+ * THL_ERR_UNSUPPORTED.
  *
  * Errors: every check runs before any HIP call; on an error nothing is
  * enqueued and D is untouched.  The call is asynchronous: it returns once
@@ -154,7 +156,8 @@ thl_status thl_gemm(int64_t m, int64_t n, int64_t k,
  * the same kernel variant runs all of them.  A stride of 0 shares that array
  * between problems (not allowed for D when batch > 1).
  * Extra rules: batch >= 0 (0 returns THL_OK with no launch), batch <= 65535
- * (else THL_ERR_UNSUPPORTED); strides >= 0 (else THL_ERR_INVALID); with
+ * and strides <= 2^40 (else THL_ERR_UNSUPPORTED); strides >= 0 (else
+ * THL_ERR_INVALID); with
  * batch > 1, stride_d >= (n-1)*ldd + m so that no two D matrices overlap.
  * Overlap checks take each array's whole span over the batch: D may alias C
  * exactly (also stride_c == stride_d) and may not otherwise overlap the span

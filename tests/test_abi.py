@@ -212,6 +212,15 @@ def bcall(batch=2, m=64, n=64, k=64, sa=None, sb=None, sc=0, sd=None, sbias=0, d
                                 1.0, beta, dts, epi, sbias, sc_struct, ssfa, ssfb, None)
 
 
+def test_huge_leading_dimensions_and_strides_are_refused():
+    # spans are computed in int64: ld above INT32_MAX and batch strides
+    # above 2^40 are refused before any arithmetic could overflow
+    assert call(ldd=2 ** 31) == thl.THL_ERR_UNSUPPORTED
+    assert call(c=C, beta=1.0, ldc=2 ** 40) == thl.THL_ERR_UNSUPPORTED
+    assert bcall(sd=2 ** 41) == thl.THL_ERR_UNSUPPORTED
+    assert bcall(sa=2 ** 62) == thl.THL_ERR_UNSUPPORTED
+
+
 def test_batched_validation():
     # batch 0 and empty problems return at once (no GPU needed)
     assert bcall(batch=0) == thl.THL_OK

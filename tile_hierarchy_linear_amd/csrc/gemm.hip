@@ -250,6 +250,13 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
   if (bt.count < 0 || bt.a < 0 || bt.b < 0 || bt.c < 0 || bt.d < 0 || bt.bias < 0 || bt.sfa < 0 || bt.sfb < 0)
     return THL_ERR_INVALID;
   if (bt.count > 65535) return THL_ERR_UNSUPPORTED;  // one grid row per problem
+  // Byte spans below are computed in int64: leading dimensions up to 2^31 and
+  // batch strides up to 2^40 elements keep every product in range.
+  if (lda > INT32_MAX || ldb > INT32_MAX || ldc > INT32_MAX || ldd > INT32_MAX) return THL_ERR_UNSUPPORTED;
+  constexpr int64_t kMaxStride = INT64_C(1) << 40;
+  if (bt.a > kMaxStride || bt.b > kMaxStride || bt.c > kMaxStride || bt.d > kMaxStride || bt.bias > kMaxStride ||
+      bt.sfa > kMaxStride || bt.sfb > kMaxStride)
+    return THL_ERR_UNSUPPORTED;
   if ((opA != THL_OP_N && opA != THL_OP_T) || (opB != THL_OP_N && opB != THL_OP_T)) return THL_ERR_INVALID;
   if (m > INT32_MAX || n > INT32_MAX || k > INT32_MAX) return THL_ERR_UNSUPPORTED;
   const unsigned flags = epi ? epi->flags : 0u;
