@@ -1,13 +1,16 @@
-// gemm.hip -- the thl_gemm C ABI: validation, first-fit variant selection,
-// launch, and host evaluation of the kernels' index maps.
+// gemm.hip -- the thl_gemm and thl_gemm_batched C ABI: validation, first-fit
+// variant selection, launch, and host evaluation of the kernels' index maps.
 //
-// Selection follows the page's rule for the library's host API: the first
-// built kernel whose data types, layouts and alignment fit the problem
-// ("Technical Documentation: NVIDIA/cutlass", "CUTLASS Library"), with one
-// shape rule on top: the largest tile whose tile count still fills the 256
-// compute units (256x256 tiles, one workgroup per CU; then 256x128, two per
-// CU; then 128x128) is tried first.  Below that, problems with at most 16
-// rows of op(A) go to the small-M kernel, which streams B once.
+// The operand family follows the dtypes: one per format, the two mixed fp8
+// orders, and MXFP8 for E4M3 operands given block scales.  Selection follows
+// the page's rule for the library's host API: the first built kernel whose
+// data types, layouts and alignment fit the problem ("Technical
+// Documentation: NVIDIA/cutlass", "CUTLASS Library"), with two shape rules on
+// top.  Problems with at most 16 rows of op(A) first try the small-M kernel,
+// which streams B once.  Otherwise the largest tile whose tile count (over
+// the whole batch) still fills the 256 compute units is tried first: 256x256
+// tiles with one workgroup per CU, then 256x128 with two per CU, then
+// 128x128.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
