@@ -42,6 +42,10 @@ MUTANTS = [
     ("alpha dropped", "double t = p->alpha * (", "double t = 1.0 * ("),
     ("last k dropped", "for (int64_t q = 0; q < p->k; ++q) {", "for (int64_t q = 0; q + 1 < p->k; ++q) {"),
     ("e2m1 subnormal", "mag = 0.5 * f;", "mag = 1.0 * f;"),
+    ("e5m2 exponent bias", "ldexp((double)(4 + f), e - 17)", "ldexp((double)(4 + f), e - 16)"),
+    ("e5m2 top exponent taken as finite", "if (e == 31)\n        mag = f == 0 ? INFINITY : NAN;",
+     "if (e == 32)\n        mag = f == 0 ? INFINITY : NAN;"),
+    ("e5m2 subnormal scale", "ldexp((double)f, -16); /* f/4 * 2^-14 */", "ldexp((double)f, -14); /* f/4 * 2^-14 */"),
 ]
 
 
