@@ -175,10 +175,10 @@ def test_small_m_selection(fam, ta, td):
     tc = "i32" if ta == "i8" else "f32"
     types = (ta, tc, td, "none")
     k = 8192
-    for m in (1, 7, 16):
+    for m, rows in ((1, 16), (7, 16), (16, 16), (17, 32), (32, 32), (33, 64), (64, 64)):
         assert call(m=m, n=0, k=k, types=types) == thl.THL_OK
-        assert thl.thl_last_variant() == f"{fam}_tn_skinny16_k4"
-    assert call(m=17, n=0, k=k, types=types) == thl.THL_OK
+        assert thl.thl_last_variant() == f"{fam}_tn_skinny{rows}_k4"
+    assert call(m=65, n=0, k=k, types=types) == thl.THL_OK
     assert "skinny" not in thl.thl_last_variant()
     # k == 0, or operands that are not 16-byte units: the tiled kernels
     assert call(m=1, n=0, k=0, lda=64, ldb=64, types=types) == thl.THL_OK
@@ -188,13 +188,14 @@ def test_small_m_selection(fam, ta, td):
     if fam in ("bf16", "f16"):  # M-major A: the tiled kernels
         assert call(m=1, n=0, k=k, opa="N", lda=8, types=types) == thl.THL_OK
         assert "skinny" not in thl.thl_last_variant()
-    # forcing the small-M kernel on more than 16 rows is refused
-    os.environ["THL_FORCE_VARIANT"] = f"{fam}_tn_skinny16_k4"
-    try:
-        assert call(m=16, n=0, k=k, types=types) == thl.THL_OK
-        assert call(m=17, n=0, k=k, types=types) == thl.THL_ERR_UNSUPPORTED
-    finally:
-        del os.environ["THL_FORCE_VARIANT"]
+    # forcing a small-M variant on more rows than it covers is refused
+    for rows in (16, 64):
+        os.environ["THL_FORCE_VARIANT"] = f"{fam}_tn_skinny{rows}_k4"
+        try:
+            assert call(m=rows, n=0, k=k, types=types) == thl.THL_OK
+            assert call(m=rows + 1, n=0, k=k, types=types) == thl.THL_ERR_UNSUPPORTED
+        finally:
+            del os.environ["THL_FORCE_VARIANT"]
 
 
 def bcall(batch=2, m=64, n=64, k=64, sa=None, sb=None, sc=0, sd=None, sbias=0, d=D, c=None, beta=0.0,

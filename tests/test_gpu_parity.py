@@ -135,11 +135,12 @@ SMALL_M_KINDS = [("fp16", "f16", 8), ("bf16", "bf16", 8), ("int8", "i8", 16), ("
 
 @pytest.mark.parametrize("kind,fam,q", SMALL_M_KINDS)
 @pytest.mark.parametrize("m,n,k", [(1, 1, 64), (1, 1000, 2040), (2, 17, 96), (3, 33, 1000), (16, 64, 4096),
-                                   (16, 300, 160), (5, 16, 8192)])
+                                   (16, 300, 160), (5, 16, 8192), (17, 100, 1000), (32, 64, 4096),
+                                   (40, 130, 2040), (64, 50, 512)])
 def test_small_m_kernel(kind, fam, q, m, n, k):
-    # M <= 16 with K-major operands: the small-M kernel, over ragged N, K
-    # tails inside a 128-byte unit, K split over its wavefronts, and one to
-    # sixteen rows (row blocks past M read as zeros)
+    # M <= 64 with K-major operands: the small-M kernel (16-, 32- and 64-row
+    # variants), over ragged N, K tails inside a 128-byte unit, K split over
+    # its wavefronts, and rows past M read as zeros
     import tile_hierarchy_linear_amd as thl
     import workloads as wl
 
@@ -151,7 +152,8 @@ def test_small_m_kernel(kind, fam, q, m, n, k):
     elif kind in ("fp16", "bf16"):
         kw.update(bias=True, beta=1.0, act="relu", type_c="bf16", type_bias="f32")
     _check_full(wl.make(kind, m, n, k, **kw))
-    assert thl.thl_last_variant() == f"{fam}_tn_skinny16_k4"
+    rows = 16 if m <= 16 else (32 if m <= 32 else 64)
+    assert thl.thl_last_variant() == f"{fam}_tn_skinny{rows}_k4"
 
 
 @pytest.mark.parametrize("m", [3, 300])

@@ -6,7 +6,7 @@
 // the page's rule for the library's host API: the first built kernel whose
 // data types, layouts and alignment fit the problem ("Technical
 // Documentation: NVIDIA/cutlass", "CUTLASS Library"), with two shape rules on
-// top.  Problems with at most 16 rows of op(A) first try the small-M kernel,
+// top.  Problems with at most 64 rows of op(A) first try the small-M kernel,
 // which streams B once.  Otherwise the largest tile whose tile count (over
 // the whole batch) still fills the 256 compute units is tried first: 256x256
 // tiles with one workgroup per CU, then 256x128 with two per CU, then
@@ -51,8 +51,11 @@ struct Variant {
       THL_V(FAM, NAME, OPS, AK, BK, 128, 128, 16, 4, 2, 2),   \
       THL_V(FAM, NAME, OPS, AK, BK, 128, 128, 4, 4, 2, 2)
 
-// The small-M kernel: 16 columns of D per workgroup, K split over 4 wavefronts.
-#define THL_VS(FAM, NAME) {NAME "_tn_skinny16_k4", FAM, true, true, 16, 16, 256, 16, 2, -1, &launch_skinny<FAM, 4>}
+// The small-M kernel: 16 columns and 16, 32 or 64 rows of D per workgroup, K
+// split over 4 wavefronts (the first whose rows cover M is chosen).
+#define THL_VS1(FAM, NAME, MT, ROWS) \
+  {NAME "_tn_skinny" #ROWS "_k4", FAM, true, true, ROWS, 16, 256, 16, 2, -1, &launch_skinny<FAM, 4, MT>}
+#define THL_VS(FAM, NAME) THL_VS1(FAM, NAME, 1, 16), THL_VS1(FAM, NAME, 2, 32), THL_VS1(FAM, NAME, 4, 64)
 
 const Variant kVariants[] = {
     THL_VARIANTS(FAM_BF16, "bf16", "tn", true, true),
@@ -364,8 +367,9 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
            (bt.count == 1 || (bt.sfa % 16 == 0 && bt.sfb % 16 == 0));
     return ok;
   };
-  // The small-M kernel streams B once for at most 16 rows of A (K > 0).
-  const bool small_m = m <= 16 && k > 0;
+  // The small-M kernel streams B once for at most 64 rows of A (K > 0); its
+  // variants are listed by rows, and the first whose rows cover M is taken.
+  const bool small_m = m <= 64 && k > 0;
   // Passes: the small-M kernel where it applies, then the preferred tier,
   // then each smaller tile, then any tiled variant that fits.
   for (int pass = small_m ? -1 : want_tier; pass <= 3 && !pick; pass = pass < 0 ? want_tier : pass + 1) {
@@ -373,8 +377,8 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
       if (v.family != fam || v.a_kmajor != a_kmajor || v.b_kmajor != b_kmajor) continue;
       family_built = true;
       if (forced && *forced) {
-        if (std::strcmp(forced, v.name) != 0 || (v.tier < 0 && !small_m)) continue;
-      } else if ((pass < 3 && v.tier != pass) || (pass == 3 && v.tier < 0)) {
+        if (std::strcmp(forced, v.name) != 0 || (v.tier < 0 && (!small_m || v.bm < m))) continue;
+      } else if ((pass < 3 && v.tier != pass) || (pass == 3 && v.tier < 0) || (v.tier < 0 && v.bm < m)) {
         continue;
       }
       if (fits(v)) {

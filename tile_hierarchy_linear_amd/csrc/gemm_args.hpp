@@ -50,9 +50,9 @@ struct GemmArgs {
 template <int F, int BM, int BN, int WM, int WN, int LOADW, int STAGES, int OCC, int SCW, bool AK, bool BK>
 hipError_t launch_gemm(const GemmArgs& a, dim3 grid, hipStream_t stream);
 
-// Launches the small-M kernel (M <= 16, K-major A and B; KW wavefronts split
-// K), one workgroup per 16 columns of D.
-template <int F, int KW>
+// Launches the small-M kernel (M <= 16 * MT, K-major A and B; KW wavefronts
+// split K), one workgroup per 16 columns of D.
+template <int F, int KW, int MT>
 hipError_t launch_skinny(const GemmArgs& a, dim3 grid, hipStream_t stream);
 
 }  // namespace thl

@@ -103,23 +103,29 @@ struct Skinny<FAM_FP4> {
 
 // Lanes for rows past M and columns past N read at this offset, past the end
 // of every operand resource: the buffer unit returns zeros for them without
-// touching memory.  (Resources here span at most 16 rows or columns of at most
-// 2^23 bytes, and per-unit offsets stay below 2^23, so no sum wraps.)
+// touching memory.  (Operand resources here span at most 64 rows or 16
+// columns of at most 2^23 bytes, below 2^29, and per-unit offsets stay below
+// 2^23, so no sum wraps.)
 constexpr uint32_t kSkinnyOutside = 0x70000000u;
 // Scalar offset of a K unit past a wavefront's range: also past the end of
-// every resource (below 2^28 with any lane offset, so no sum wraps).
-constexpr int kSkinnyPast = 0x08000000;
+// every operand resource (and below 2^32 with any lane offset).
+constexpr int kSkinnyPast = 0x40000000;
+
+template <class Acc>
+__device__ __forceinline__ void store_tile(const GemmArgs& p, Acc sum, int64_t n0, int r_base);
 
 // UN: K units per batch of loads (two batches in flight per wavefront).  On
 // fp8 1 x 8192 x 8192, four wavefronts with two-unit batches stream B at
 // about 6.8 TB/s once running; deeper batches were slower (up to 4 units of
-// 8 in flight per wavefront measured).
-template <int F, int KW, int UN = 2>
+// 8 in flight per wavefront measured).  MT: 16-row tiles of D per workgroup
+// (M <= 16 * MT); every B operand register serves all MT of them, so B is
+// still read once.
+template <int F, int KW, int UN = 2, int MT = 1>
 __global__ void __launch_bounds__(KW * 64) skinny_kernel(GemmArgs p) {
   offset_to_problem(p);
   using S = Skinny<F>;
   using Acc = typename S::Acc;
-  constexpr bool INT = F == FAM_I8, SCALED = F == FAM_FP4;
+  constexpr bool SCALED = F == FAM_FP4;
   const int lane = static_cast<int>(threadIdx.x) & 63;
   // The wavefront index read from lane 0, so that the K range and every
   // offset built from it stay scalar.
@@ -141,26 +147,31 @@ __global__ void __launch_bounds__(KW * 64) skinny_kernel(GemmArgs p) {
   const int kb16 = (kb + 15) & ~15;
   const auto ra = make_rsrc_n(p.a, static_cast<int>((p.m - 1) * p.lda_bytes + kb16));
   const auto rb = make_rsrc_n(p.b + n0 * p.ldb_bytes, static_cast<int>((ncols - 1) * p.ldb_bytes + kb16));
-  const uint32_t va = row < p.m ? static_cast<uint32_t>(row * p.lda_bytes + kbyte) : kSkinnyOutside;
+  uint32_t va[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+    va[t] = row + 16 * t < p.m ? static_cast<uint32_t>((row + 16 * t) * p.lda_bytes + kbyte) : kSkinnyOutside;
   const uint32_t vb = row < ncols ? static_cast<uint32_t>(row * p.ldb_bytes + kbyte) : kSkinnyOutside;
   // fp4 scales: the row's (column's) 8 E8M0 bytes of the unit, blocks 8u ..
   // 8u+7 (rows start 16-byte aligned with lengths a multiple of 16, so an
   // 8-byte read at 8u < K/32 stays in the row).
   const int nkb = p.k >> 5;
   __amdgpu_buffer_rsrc_t rsa = ra, rsb = rb;
-  uint32_t vsa = 0, vsb = 0;
+  uint32_t vsa[MT] = {}, vsb = 0;
   if constexpr (SCALED) {
     rsa = make_rsrc_n(p.sfa, static_cast<int>((p.m - 1) * p.ld_sfa + ((nkb + 15) & ~15)));
     rsb = make_rsrc_n(p.sfb + n0 * p.ld_sfb, static_cast<int>((ncols - 1) * p.ld_sfb + ((nkb + 15) & ~15)));
-    vsa = row < p.m ? static_cast<uint32_t>(row * p.ld_sfa) : kSkinnyOutside;
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+      vsa[t] = row + 16 * t < p.m ? static_cast<uint32_t>((row + 16 * t) * p.ld_sfa) : kSkinnyOutside;
     vsb = row < ncols ? static_cast<uint32_t>(row * p.ld_sfb) : kSkinnyOutside;
   }
   const int g = lane >> 4;
-  Acc acc = {};
+  Acc acc[MT] = {};
 
   struct Unit {
-    v4i a[2], b[2];
-    v2i sa, sb;  // fp4: the 8 E8M0 bytes of the unit's blocks
+    v4i a[MT][2], b[2];
+    v2i sa[MT], sb;  // fp4: the 8 E8M0 bytes of the unit's blocks
   };
   // Unit u's loads; a unit at or past the wave's end reads zeros (offset past
   // every resource) and adds nothing.  No loaded value is touched here, so
@@ -169,48 +180,53 @@ __global__ void __launch_bounds__(KW * 64) skinny_kernel(GemmArgs p) {
     const int so = u < u_end ? (u << 7) : kSkinnyPast;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      x.a[h] = buf_load16(ra, va + 64 * h, so);
       x.b[h] = buf_load16(rb, vb + 64 * h, so);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) x.a[t][h] = buf_load16(ra, va[t] + 64 * h, so);
     }
     if constexpr (SCALED) {
       const int ss = u < u_end ? (u << 3) : kSkinnyPast;
-      x.sa = __builtin_bit_cast(v2i, __builtin_amdgcn_raw_buffer_load_b64(rsa, vsa, ss, 0));
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+        x.sa[t] = __builtin_bit_cast(v2i, __builtin_amdgcn_raw_buffer_load_b64(rsa, vsa[t], ss, 0));
       x.sb = __builtin_bit_cast(v2i, __builtin_amdgcn_raw_buffer_load_b64(rsb, vsb, ss, 0));
     }
   };
   // Unit u's MFMAs.  In a unit that runs past K the bytes past K are zeroed
   // and scale blocks past K/32 read as 2^0 (their data is zero; a NaN code
   // in row padding would otherwise poison the sum).
+  // byte 0: block 8u + g (half 0), byte 1: block 8u + 4 + g (half 1)
+  auto scale_pair = [&](v2i w) -> unsigned {
+    const unsigned sh = 8u * static_cast<unsigned>(g);
+    return ((static_cast<unsigned>(w[0]) >> sh) & 0xffu) | (((static_cast<unsigned>(w[1]) >> sh) & 0xffu) << 8);
+  };
   auto use = [&](int u, Unit& x) {
     const int so = u << 7;
-    unsigned sa = 0, sb = 0;
+    unsigned sa[MT] = {}, sb = 0;
     if constexpr (SCALED) {
-      // byte 0: block 8u + g (half 0), byte 1: block 8u + 4 + g (half 1)
-      const unsigned sh = 8u * static_cast<unsigned>(g);
-      sa = ((static_cast<unsigned>(x.sa[0]) >> sh) & 0xffu) | (((static_cast<unsigned>(x.sa[1]) >> sh) & 0xffu) << 8);
-      sb = ((static_cast<unsigned>(x.sb[0]) >> sh) & 0xffu) | (((static_cast<unsigned>(x.sb[1]) >> sh) & 0xffu) << 8);
-      if (u >= u_end) sa = sb = 0x7f7fu;  // zero data past the range: unit scales
+#pragma unroll
+      for (int t = 0; t < MT; ++t) sa[t] = u < u_end ? scale_pair(x.sa[t]) : 0x7f7fu;
+      sb = u < u_end ? scale_pair(x.sb) : 0x7f7fu;  // zero data past the range: unit scales
     }
     if (u < u_end && so + 128 > kb) {  // the last, partial unit (uniform branch)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int valid = kb - (so + 64 * h + 16 * g);
-        x.a[h] = mask_bytes(x.a[h], valid);
         x.b[h] = mask_bytes(x.b[h], valid);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) x.a[t][h] = mask_bytes(x.a[t][h], valid);
       }
       if constexpr (SCALED) {
         const int blk = 8 * u + g;
-        if (blk >= nkb) {
-          sa = (sa & 0xff00u) | 127u;
-          sb = (sb & 0xff00u) | 127u;
-        }
-        if (blk + 4 >= nkb) {
-          sa = (sa & 0x00ffu) | (127u << 8);
-          sb = (sb & 0x00ffu) | (127u << 8);
-        }
+        const unsigned keep = (blk >= nkb ? 0u : 0xffu) | (blk + 4 >= nkb ? 0u : 0xff00u);
+        const unsigned unit1 = (blk >= nkb ? 127u : 0u) | (blk + 4 >= nkb ? 127u << 8 : 0u);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) sa[t] = (sa[t] & keep) | unit1;
+        sb = (sb & keep) | unit1;
       }
     }
-    acc = S::unit(x.a, x.b, acc, sa, sb);
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = S::unit(x.a[t], x.b, acc[t], sa[t], sb);
   };
 
   // Two batches of UN units in flight: batch j+1's loads go out before batch
@@ -233,17 +249,29 @@ __global__ void __launch_bounds__(KW * 64) skinny_kernel(GemmArgs p) {
 
   // Sum the KW partial tiles in wavefront order (the same order for every
   // element, so the result does not depend on timing).
-  __shared__ __attribute__((aligned(16))) v4i part[KW][64];
-  part[wave][lane] = __builtin_bit_cast(v4i, acc);
+  __shared__ __attribute__((aligned(16))) v4i part[KW][MT][64];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) part[wave][t][lane] = __builtin_bit_cast(v4i, acc[t]);
   __syncthreads();
   if (wave != 0) return;
-  Acc sum = __builtin_bit_cast(Acc, part[0][lane]);
 #pragma unroll
-  for (int w = 1; w < KW; ++w) sum += __builtin_bit_cast(Acc, part[w][lane]);
+  for (int t = 0; t < MT; ++t) {
+    Acc sum = __builtin_bit_cast(Acc, part[0][t][lane]);
+#pragma unroll
+    for (int w = 1; w < KW; ++w) sum += __builtin_bit_cast(Acc, part[w][t][lane]);
+    store_tile(p, sum, n0, 16 * t);
+  }
+}
 
-  // Epilogue: lane l holds rows 4*(l/16) .. +3 of column l % 16.
+// Epilogue of one 16 x 16 tile whose first row is r_base: lane l holds rows
+// r_base + 4*(l/16) .. +3 of column n0 + l % 16.
+template <class Acc>
+__device__ __forceinline__ void store_tile(const GemmArgs& p, Acc sum, int64_t n0, int r_base) {
+  constexpr bool INT = std::is_same<Acc, v4i>::value;
+  const int lane = static_cast<int>(threadIdx.x) & 63;
   int64_t r0, c0;
   maps::mfma16_acc(lane, 0, &r0, &c0);
+  r0 += r_base;
   const int64_t n = n0 + c0;
   if (n >= p.n || r0 >= p.m) return;
   const int rows = p.m - r0 < 4 ? static_cast<int>(p.m - r0) : 4;
