@@ -111,10 +111,11 @@ typedef struct {
  *   E2M1X2 operands, opA = T, opB = N, k % 32 == 0: F32 accumulate, element
  *     (i,p) of A multiplied by 2^(SFA(i, p/32) - 127), likewise B with SFB(j, p/32);
  *     scale rows 16-byte aligned (THL_ERR_MISALIGNED otherwise).
- * With m <= 16, k > 0, opA = T and opB = N (any operand family), A and B
+ * With m <= 64, k > 0, opA = T and opB = N (any operand family but MXFP8), A and B
  * 16-byte aligned with leading dimensions of whole 16-byte units, the small-M
- * kernel runs (variants "<family>_tn_skinny16_k4"): it streams B once from
- * memory and sums K in a fixed order, so results do not depend on timing.
+ * kernel runs (variants "<family>_tn_skinny{16,32,64}_k4", the first whose
+ * rows cover m): it streams B once from memory and sums K in a fixed order,
+ * so results do not depend on timing.
  * It reads each scale row (E2M1X2) in 8-byte units up to its next 16-byte
  * boundary, as the tiled kernels read it in 16-byte groups.
  *

@@ -35,7 +35,7 @@ struct Variant {
   int bm, bn, threads, loadw;
   int occ;   // workgroups per CU the kernel is built for
   int tier;  // 0: 256x256, 1: 256x128, 2: 128x128 (the shape rule's preference order);
-             // -1: the small-M kernel (M <= 16), chosen by its own rule
+             // -1: the small-M kernel (M <= bm <= 64), chosen by its own rule
   LaunchFn launch;
 };
 

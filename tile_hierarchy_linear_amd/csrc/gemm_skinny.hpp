@@ -1,4 +1,4 @@
-// gemm_skinny.hpp -- the small-M GEMM kernel: M <= 16, K-major A and B.
+// gemm_skinny.hpp -- the small-M GEMM kernel: M <= 64, K-major A and B.
 //
 // With one or a few rows of op(A), the product is a stream over B: every byte
 // of B is used once, against a handful of A rows that every workgroup shares
@@ -7,12 +7,12 @@
 // MFMA operand registers, one whole 128-byte line per column per K unit, and
 // spreads K over the wavefronts of a workgroup so that enough lines are in
 // flight to cover HBM latency on every CU.  (The "CUTLASS" knowledge-base
-// page's tile hierarchy still holds: workgroup tile 16 x 16 of D,
+// page's tile hierarchy still holds: workgroup tile (16 MT) x 16 of D,
 // wavefront = one K slice of it, MFMA tile 16 x 16; the tiled kernels'
 // smallest tile, 128 x 128, would run 127 rows of zeros through the matrix
 // cores for M = 1 and give each workgroup 128 columns of B to stream.)
 //
-//   workgroup:  16 columns of D (all M <= 16 rows), KW wavefronts
+//   workgroup:  16 columns and MT sixteen-row tiles of D, KW wavefronts
 //   wavefront:  K units [w*U/KW, (w+1)*U/KW) of U = ceil(K bytes / 128)
 //   lane l:     row / column l % 16, bytes 16*(l/16) and 64 + 16*(l/16) of
 //               each 128-byte unit (maps::mfma16_operand)
