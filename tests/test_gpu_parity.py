@@ -571,3 +571,14 @@ def test_mixed_fp8_shapes(kind, m, n, k):
 
     kw = {} if (m, n, k) == (4097, 1000, 2040) else dict(lda=_pad(k, 16), ldb=_pad(k, 16))
     _check_full(wl.make(kind, m, n, k, act="gelu", bias=True, beta=0.5, **kw))
+
+
+@pytest.mark.parametrize("kind,m,n,k,L", [("bf16", 300, 260, 136, 8), ("fp8", 520, 300, 512, 16),
+                                           ("mxfp4", 130, 130, 256, 16)])
+def test_batched_many_problems(kind, m, n, k, L):
+    # 8 and 16 problems (the persistent workgroups shared out over them)
+    import workloads as wl
+
+    base = {"bf16": 1002, "fp8": 1004, "mxfp4": 1005}[kind]
+    ws = [wl.make(kind, m, n, k, seed=base + 10 * z) for z in range(L)]
+    _check_batched(ws)
