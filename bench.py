@@ -173,8 +173,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the GEMM shards by output "
-              "tiles with no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (the GEMM would shard by "
+              "output tiles with no exchange). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -1,0 +1,48 @@
+"""The seeded input generators (host only, no GEMM arithmetic) and the
+benchmark's command line."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_mxfp8_blocks_follow_the_shared_exponent_rule():
+    # OCP MX: X = floor(log2(amax)) - 8 for E4M3 (largest exponent 8), so each
+    # block's largest element lands in [256, 512) before rounding, at most 448
+    # after it; dequantized values are within E4M3's half-ulp of x
+    g = np.random.default_rng(5)
+    x = g.standard_normal((6, 128)) * np.exp(g.uniform(-8, 8, size=(6, 1)))
+    codes, sc = wl.mx_quantize_e4m3(x)
+    vals = oracle.decode("e4m3", np.ascontiguousarray(codes)).reshape(6, 128)
+    scale = np.ldexp(1.0, sc.astype(np.int64) - 127)
+    blk = np.abs(vals.reshape(6, 4, 32)).max(axis=2)
+    assert ((blk >= 256) & (blk <= 448)).all()
+    deq = (vals.reshape(6, 4, 32) * scale[:, :, None]).reshape(6, 128)
+    ref = torch.from_numpy((x / np.repeat(scale, 32, axis=1)).astype(np.float32)).clamp(-448, 448)
+    want = ref.to(torch.float8_e4m3fn).double().numpy() * np.repeat(scale, 32, axis=1)
+    assert np.array_equal(deq, want)
+
+
+def test_fp8_kinds_scale_each_operand_to_its_format():
+    for kind, (ta, tb) in (("fp8", ("e4m3", "e4m3")), ("fp8e5m2", ("e5m2", "e5m2")),
+                           ("fp8e4e5", ("e4m3", "e5m2")), ("fp8e5e4", ("e5m2", "e4m3"))):
+        w = wl.make(kind, 9, 7, 64)
+        assert (w.type_a, w.type_b) == (ta, tb)
+        top = {"e4m3": 448.0, "e5m2": 57344.0}
+        a = np.abs(oracle.decode(ta, np.ascontiguousarray(w.a))).max()
+        b = np.abs(oracle.decode(tb, np.ascontiguousarray(w.b))).max()
+        assert a <= top[ta] and b <= top[tb]
+        assert a >= top[ta] / 2 and b >= top[tb] / 2  # the per-tensor scale fills the range
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
