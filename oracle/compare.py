@@ -45,7 +45,8 @@ def check_float(got, want, tol) -> dict:
     bad = ~(err <= tol)  # NaN counts as bad
     worst = int(np.argmax(np.where(np.isfinite(err), err - tol, np.inf))) if err.size else 0
     return {"ok": not bool(bad.any()), "n_bad": int(bad.sum()), "n": int(err.size),
-            "max_err": float(np.nanmax(err)) if err.size else 0.0,
+            "max_err": float(err[np.isfinite(err)].max()) if np.isfinite(err).any() else
+            (float("nan") if err.size else 0.0),
             "worst_index": worst}
 
 

@@ -395,6 +395,32 @@ def test_bruteforce_int8_exact():
         assert np.array_equal(_full(p), want)
 
 
+def test_bruteforce_int8_relu_exact():
+    # The integer epilogue with relu: sums of both signs, C and bias, against
+    # exact int64 arithmetic and max(t, 0).  C and bias are drawn so that
+    # about half of the outputs are negative before the activation.
+    g = np.random.default_rng(11)
+    for _ in range(5):
+        m, n, k = (int(x) for x in g.integers(2, 9, size=3))
+        a, b = _random_values("i8", g, (m, k)), _random_values("i8", g, (k, n))
+        c = g.integers(-30000, 30000, size=(m, n)).astype(np.int32)
+        bias = g.integers(-30000, 30000, size=m).astype(np.int32)
+        p = _problem("i8", a, b, "T", "N", beta=1.0, c=wl.store_colmajor(c, m), ldc=m,
+                     type_c="i32", bias=bias, type_bias="i32", act="relu")
+        t = a.astype(np.int64) @ b.astype(np.int64) + c + bias[:, None]
+        assert (t < 0).any() and (t > 0).any()
+        assert np.array_equal(_full(p), np.maximum(t, 0))
+
+
+def test_int8_relu_boundary_points():
+    # t = -1, 0, +1 exactly (A = 0): relu gives 0, 0, 1
+    m, n, k = 3, 1, 4
+    c = np.array([[-1], [0], [1]], np.int32)
+    p = _problem("i8", np.zeros((m, k)), np.zeros((k, n)), beta=1.0,
+                 c=wl.store_colmajor(c, m), ldc=m, type_c="i32", act="relu")
+    assert np.array_equal(_full(p)[:, 0], np.array([0, 0, 1]))
+
+
 def test_block_scale_closed_form():
     # A = B = all 1.0 (code 0x2), SFA(i,kb) = 2^((i+kb) mod 3), SFB(j,kb) = 2^(j mod 2):
     # D(i,j) = 32 * 2^(j mod 2) * sum_kb 2^((i+kb) mod 3).  A block boundary off by
@@ -463,6 +489,51 @@ def test_gelu_special_points():
                  type_c="f32", act="gelu")
     got = _full(p)[:, 0]
     assert got[0] == 0.0 and got[1] == 20.0 and abs(got[2]) < 1e-80
+
+
+def _normal_cdf_table():
+    rows = []
+    for line in open(os.path.join(GOLDEN, "normal_cdf.txt")):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            x, phi = line.split()
+            rows.append((float(x), float(phi)))
+    return rows
+
+
+def test_normal_cdf_table_matches_an_independent_implementation():
+    from scipy.special import ndtr
+
+    for x, phi in _normal_cdf_table():
+        assert abs(float(ndtr(x)) - phi) <= 1e-15
+
+
+def test_gelu_is_x_times_the_normal_cdf():
+    # GELU (erf form) at mid-range points: D = x * Phi(x) with Phi from the
+    # tabulated standard normal distribution, to 1e-14 absolute.  The tanh
+    # approximation misses these by 2e-5 or more; a wrong argument scale
+    # (erf(x/2)) or a missing factor 1/2 by far more.
+    tab = _normal_cdf_table()
+    m, n, k = len(tab), 1, 1
+    c = np.array([[x] for x, _ in tab])
+    p = _problem("bf16", np.zeros((m, k)), np.zeros((k, n)), beta=1.0,
+                 c=wl.store_colmajor(c.astype(np.float32).view(np.uint32), m), ldc=m,
+                 type_c="f32", act="gelu")
+    got = _full(p)[:, 0]
+    for (x, phi), d in zip(tab, got):
+        assert abs(d - x * phi) <= 1e-14, (x, d, x * phi)
+
+
+def test_gelu_matches_torch_exact_gelu():
+    # torch's own erf-form GELU (approximate='none') in float64 on the CPU, an
+    # implementation independent of the oracle's, at 64 points over [-6, 6].
+    x = np.linspace(-6.0, 6.0, 64).astype(np.float32).astype(np.float64)
+    m, n, k = x.size, 1, 1
+    p = _problem("bf16", np.zeros((m, k)), np.zeros((k, n)), beta=1.0,
+                 c=wl.store_colmajor(x[:, None].astype(np.float32).view(np.uint32), m), ldc=m,
+                 type_c="f32", act="gelu")
+    ref = torch.nn.functional.gelu(torch.from_numpy(x), approximate="none").numpy()
+    assert np.allclose(_full(p)[:, 0], ref, rtol=1e-14, atol=1e-300)
 
 
 def test_relu_boundary_points():

@@ -4,6 +4,7 @@ Each case plants one mistake in a copy of oracle.c (on the CPU, in a temporary
 directory), builds it, and runs the pin suite against it; the suite must fail.
 """
 import os
+import shutil
 import subprocess
 import sys
 import tempfile
@@ -46,6 +47,30 @@ MUTANTS = [
     ("e5m2 top exponent taken as finite", "if (e == 31)\n        mag = f == 0 ? INFINITY : NAN;",
      "if (e == 32)\n        mag = f == 0 ? INFINITY : NAN;"),
     ("e5m2 subnormal scale", "ldexp((double)f, -16); /* f/4 * 2^-14 */", "ldexp((double)f, -14); /* f/4 * 2^-14 */"),
+    ("integer relu keeps negatives, zeroes positives", "if (p->act == ORC_ACT_RELU && t < 0)",
+     "if (p->act == ORC_ACT_RELU && t > 0)"),
+    ("gelu by the tanh approximation", "return 0.5 * t * (1.0 + erf(t / sqrt(2.0))); /* erf form of GELU */",
+     "return 0.5 * t * (1.0 + tanh(sqrt(2.0 / 3.141592653589793) * (t + 0.044715 * t * t * t)));"),
+    ("gelu without the factor one half", "return 0.5 * t * (1.0 + erf(t / sqrt(2.0))); /* erf form of GELU */",
+     "return t * (1.0 + erf(t / sqrt(2.0)));"),
+]
+
+# Mistakes planted in the comparison (oracle/compare.py), caught by
+# tests/test_compare.py: (description, text, replacement).
+COMPARE_MUTANTS = [
+    ("per-tensor scale applied twice on a block-scaled operand",
+     "return float(np.abs(vals).max()) * per_tensor", "return float(np.abs(vals).max()) * per_tensor * per_tensor"),
+    ("block scales not applied", "vals = vals.reshape(rows, w.k // 32, 32) * scales[:, :, None]",
+     "vals = vals.reshape(rows, w.k // 32, 32) * 1.0"),
+    ("per-tensor fp8 scale ignored",
+     'scale = (w.a_scale if which == "a" else w.b_scale) if fmt in ("e4m3", "e5m2") else 1.0', "scale = 1.0"),
+    ("operand B's maximum taken from A", 'raw = w.a if which == "a" else w.b', "raw = w.a"),
+    ("scale padding read as blocks", "[:, : w.k // 32]", "[:, : w.k // 32 + 1][:, 1:]"),
+    ("gelu factor dropped", 'g = 1.13 if act == "gelu" else 1.0', "g = 1.0"),
+    ("alpha dropped", "* k * abs(alpha) *", "* k *"),
+    ("K dropped", "term = 2.0 ** -20 * k *", "term = 2.0 ** -20 *"),
+    ("ulp one bit too fine", "(e - (p - 1))", "(e - p)"),
+    ("subnormal spacing ignored", "e = np.maximum(np.where(a > 0, e, emin), emin)", "e = np.where(a > 0, e, emin)"),
 ]
 
 
@@ -66,8 +91,47 @@ def _run_mutant(case):
         return desc, r.returncode
 
 
+def _run_compare_mutant(case):
+    """Copy the oracle package, the generators and the comparison pins into a
+    temporary tree, plant the mistake in its compare.py, and run the pins
+    there (the built oracle library is reused)."""
+    desc, old, new = case
+    src = os.path.join(ROOT, "oracle", "compare.py")
+    text = open(src).read()
+    assert text.count(old) == 1, f"mutation anchor not unique: {desc}"
+    with tempfile.TemporaryDirectory() as tmp:
+        shutil.copytree(os.path.join(ROOT, "oracle"), os.path.join(tmp, "oracle"),
+                        ignore=shutil.ignore_patterns("*.so", "__pycache__"))
+        shutil.copytree(os.path.join(ROOT, "workloads"), os.path.join(tmp, "workloads"),
+                        ignore=shutil.ignore_patterns("__pycache__"))
+        os.makedirs(os.path.join(tmp, "tests"))
+        for name in ("conftest.py", "test_compare.py"):
+            shutil.copy(os.path.join(ROOT, "tests", name), os.path.join(tmp, "tests", name))
+        with open(os.path.join(tmp, "oracle", "compare.py"), "w") as f:
+            f.write(text.replace(old, new))
+        env = dict(os.environ, THL_ORACLE_LIB_OVERRIDE=oracle.build(force=False))
+        r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                            os.path.join(tmp, "tests", "test_compare.py")],
+                           cwd=tmp, env=env, capture_output=True, text=True, timeout=600)
+        return desc, r.returncode
+
+
+def test_unmutated_copies_pass_the_pins():
+    # Control: the same machinery with the anchor replaced by itself must
+    # pass, so that a mutant's failure means a pin caught it.
+    assert _run_mutant(("control", MUTANTS[0][1], MUTANTS[0][1]))[1] == 0
+    assert _run_compare_mutant(("control", COMPARE_MUTANTS[0][1], COMPARE_MUTANTS[0][1]))[1] == 0
+
+
 def test_every_planted_mistake_fails_a_pin():
     with ThreadPoolExecutor(max_workers=4) as ex:
         results = list(ex.map(_run_mutant, MUTANTS))
+    survivors = [desc for desc, rc in results if rc == 0]
+    assert not survivors, f"mutants that pass every pin: {survivors}"
+
+
+def test_every_planted_comparison_mistake_fails_a_pin():
+    with ThreadPoolExecutor(max_workers=4) as ex:
+        results = list(ex.map(_run_compare_mutant, COMPARE_MUTANTS))
     survivors = [desc for desc, rc in results if rc == 0]
     assert not survivors, f"mutants that pass every pin: {survivors}"
