@@ -62,7 +62,8 @@ typedef enum {
 } thl_dtype;
 
 typedef struct {
-  thl_dtype a, b; /* operand formats; a == b is required (F16, BF16, I8, E4M3, E2M1X2) */
+  thl_dtype a, b; /* operand formats: a == b (F16, BF16, I8, E4M3, E5M2, E2M1X2), or one of
+                     E4M3 / E5M2 for a and the other for b (mixed fp8) */
   thl_dtype c;    /* format of C: F32, F16 or BF16 for float paths, I32 for the int8 path */
   thl_dtype d;    /* format of D: F32, F16 or BF16 (float paths), I32 (int8 path) */
   thl_dtype bias; /* format of the bias vector: F32, F16, BF16, or I32 (int8 path) */
@@ -79,11 +80,12 @@ typedef struct {
 } thl_epilogue;
 
 typedef struct {
-  float a_scale, b_scale; /* per-tensor scales (host values), used for E4M3; 1.0f otherwise */
-  const uint8_t* sfa;     /* E2M1X2: E8M0 block scales of A, SFA(i,kb) at sfa[i*ld_sfa + kb], device,
-                             16-byte aligned */
+  float a_scale, b_scale; /* per-tensor scales (host values), used for E4M3 and E5M2 (also mixed and
+                             MXFP8); ignored (taken as 1) for the other formats */
+  const uint8_t* sfa;     /* E8M0 block scales of A for E2M1X2 (required) and E4M3 (MXFP8, with sfb):
+                             SFA(i,kb) at sfa[i*ld_sfa + kb], device, 16-byte aligned; NULL otherwise */
   int64_t ld_sfa;         /* >= k/32 and a multiple of 16 */
-  const uint8_t* sfb;     /* E2M1X2: SFB(j,kb) at sfb[j*ld_sfb + kb], device, 16-byte aligned */
+  const uint8_t* sfb;     /* SFB(j,kb) at sfb[j*ld_sfb + kb], device, 16-byte aligned; as sfa */
   int64_t ld_sfb;         /* >= k/32 and a multiple of 16 */
 } thl_scales;
 
@@ -122,6 +124,10 @@ typedef struct {
  * Ownership: A, B, C, D, bias, sfa, sfb are device pointers owned by the
  * caller; the library allocates nothing and keeps no pointer after return.
  * alpha, beta and the per-tensor scales are host values.
+ *
+ * Block scales: sfa or sfb given with operands other than E2M1X2 and E4M3
+ * (F16, BF16, I8, E5M2, mixed fp8) is THL_ERR_UNSUPPORTED; E4M3 with only
+ * one of the two is THL_ERR_INVALID; E2M1X2 without both is THL_ERR_INVALID.
  *
  * Semantics: beta == 0 means C is not read (it may be NULL and may hold NaN).
  * D may alias C exactly (same pointer, ldc == ldd, c and d the same format);

@@ -119,6 +119,29 @@ def test_unsupported_combinations():
     assert thl.thl_last_variant().startswith("e4m3e5m2_")
 
 
+@pytest.mark.parametrize("fmt,td", [("bf16", "f32"), ("f16", "f32"), ("i8", "i32"), ("e5m2", "bf16")])
+def test_block_scales_with_formats_that_take_none_are_refused(fmt, td):
+    # A block-scale array given with a format that has no block-scaled kernel
+    # is refused, not dropped (the result would ignore the caller's scales).
+    tc = "i32" if fmt == "i8" else "f32"
+    for sc in (thl.thl_scales(1.0, 1.0, SFA, 16, SFB, 16), thl.thl_scales(1.0, 1.0, SFA, 16, None, 0),
+               thl.thl_scales(1.0, 1.0, None, 0, SFB, 16)):
+        assert call(types=(fmt, tc, td, "none"), sc=sc) == thl.THL_ERR_UNSUPPORTED
+        assert call(m=0, types=(fmt, tc, td, "none"), sc=sc) == thl.THL_ERR_UNSUPPORTED
+
+
+def test_e4m3_with_one_scale_array_is_invalid():
+    # E4M3 with both arrays is MXFP8, with neither plain fp8; one alone is an error.
+    for sc in (thl.thl_scales(1.0, 1.0, SFA, 16, None, 0), thl.thl_scales(1.0, 1.0, None, 0, SFB, 16)):
+        assert call(types=("e4m3", "f32", "bf16", "none"), sc=sc) == thl.THL_ERR_INVALID
+        assert call(m=0, types=("e4m3", "f32", "bf16", "none"), sc=sc) == thl.THL_ERR_INVALID
+    both = thl.thl_scales(1.0, 1.0, SFA, 16, SFB, 16)
+    assert call(m=0, types=("e4m3", "f32", "bf16", "none"), sc=both) == thl.THL_OK
+    assert thl.thl_last_variant().startswith("mxe4m3_")
+    assert call(m=0, types=("e4m3", "f32", "bf16", "none"), sc=None) == thl.THL_OK
+    assert thl.thl_last_variant().startswith("e4m3_")
+
+
 def test_mxfp4_needs_scales():
     assert call(types=("e2m1", "f32", "bf16", "none"), sc=None) == thl.THL_ERR_INVALID
     sc = thl.thl_scales(1.0, 1.0, SFA, 1, SFB, 2)  # ld_sfa < k/32

@@ -280,7 +280,13 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
   const int fam = mixed ? (dt->a == THL_E4M3 ? FAM_E4E5 : FAM_E5E4)
                         : ((fam0 == FAM_FP8 && sc && sc->sfa && sc->sfb) ? FAM_MX8 : fam0);
   if (fam < 0 || (dt->b != dt->a && !mixed)) return THL_ERR_UNSUPPORTED;
-  if (mixed && sc && (sc->sfa || sc->sfb)) return THL_ERR_UNSUPPORTED;  // block scales: E4M3 only
+  // Block scales come with E2M1 and E4M3 operands only; E4M3 needs both
+  // arrays or neither (one alone is neither MXFP8 nor plain fp8).
+  const bool any_sf = sc && (sc->sfa || sc->sfb);
+  if (any_sf && fam != FAM_FP4 && fam != FAM_MX8) {
+    if (fam0 == FAM_FP8 && !mixed) return THL_ERR_INVALID;
+    return THL_ERR_UNSUPPORTED;
+  }
   const bool block_scaled = fam == FAM_FP4 || fam == FAM_MX8;
   const bool int_path = fam == FAM_I8;
   if (int_path) {
