@@ -334,6 +334,16 @@ def test_config_bf16_nn_4096_relu_bias_residual():
     _check_sampled(w)
 
 
+def test_config_bf16_nn_8192_headline_sampled():
+    # The benchmark's headline workload itself: bf16 N/N at 8192^3,
+    # D = relu(A.B + C + bias[m]), bf16 out, on the seeded 4096-output sample.
+    import workloads as wl
+
+    w = wl.make("bf16", 8192, 8192, 8192)
+    assert (w.op_a, w.op_b, w.act, w.beta, w.bias is not None) == ("N", "N", "relu", 1.0, True)
+    _check_sampled(w)
+
+
 def test_config_bf16_nn_ragged():
     import workloads as wl
 
@@ -418,6 +428,13 @@ def test_two_workgroups_per_cu_match_the_256x256_kernel(variant):
             dp = DeviceProblem(w)
             assert dp.run() == 0
             torch.cuda.synchronize()
+            first = dp.d.clone()
+            # the kernel is deterministic: two more runs give the same bits
+            for _ in range(2):
+                dp.d.fill_(float("nan"))
+                assert dp.run() == 0
+                torch.cuda.synchronize()
+                assert torch.equal(dp.d.view(torch.int16), first.view(torch.int16)), f"{v} differs between runs"
         finally:
             os.environ.pop("THL_FORCE_VARIANT", None)
         outs.append(dp.d.float().cpu())
@@ -426,6 +443,54 @@ def test_two_workgroups_per_cu_match_the_256x256_kernel(variant):
     a, b = outs
     bad = (a - b).abs() > 2.0 ** -7 * torch.maximum(a.abs(), b.abs()) + 1e-6
     assert int(bad.sum()) == 0, f"{int(bad.sum())} elements differ by more than one bf16 ulp"
+
+
+@pytest.mark.parametrize("kind,variant", [("bf16", "bf16_nn_128x128_v16_s4_o2"), ("fp8", "e4m3_tn_128x128_v16_s4_o2"),
+                                          ("mxfp4", "e2m1_tn_128x128_v16_s4_o2")])
+def test_two_workgroup_vector_epilogue_against_the_oracle(kind, variant):
+    # The vector epilogue in a two-workgroups-per-CU variant, with C (and
+    # bias for bf16) read, several tiles per workgroup (4096^2 in 128^2
+    # tiles is 1024 tiles on 512 workgroups): sampled against the oracle,
+    # plus the whole first tile row and column.
+    import workloads as wl
+    from oracle import compare
+    from workloads.device import DeviceProblem
+
+    w = wl.make(kind, 4096, 4096, 2048, beta=1.0)
+    os.environ["THL_FORCE_VARIANT"] = variant
+    try:
+        _say(f"[two-workgroup vector epilogue] {variant} m={w.m} n={w.n} k={w.k}")
+        dp = DeviceProblem(w)
+        assert dp.run() == 0
+        torch.cuda.synchronize()
+    finally:
+        os.environ.pop("THL_FORCE_VARIANT", None)
+    rows, cols = w.sample(4096)
+    r0, c0 = np.meshgrid(np.arange(128), np.arange(0, 4096, 37), indexing="ij")
+    rows = np.concatenate([rows, r0.ravel(), c0.ravel()])
+    cols = np.concatenate([cols, c0.ravel(), r0.ravel()])
+    res = compare.parity_check(w, dp.d_values(rows, cols), rows, cols)
+    assert res["ok"], res
+
+
+def test_headline_kernel_is_deterministic_at_8192():
+    # The 256x256 kernel with the vector epilogue at the headline shape:
+    # three runs give bit-identical D (a race between a wave's loads, stores
+    # and LDS staging would show up as differing bits).
+    import workloads as wl
+    from workloads.device import DeviceProblem
+
+    w = wl.make("bf16", 8192, 8192, 1024)
+    _say(f"[deterministic] m={w.m} n={w.n} k={w.k}")
+    dp = DeviceProblem(w)
+    assert dp.run() == 0
+    torch.cuda.synchronize()
+    first = dp.d.clone()
+    for _ in range(2):
+        dp.d.fill_(float("nan"))
+        assert dp.run() == 0
+        torch.cuda.synchronize()
+        assert torch.equal(dp.d.view(torch.int16), first.view(torch.int16))
 
 
 def test_vector_epilogue_matches_general_path_at_8192():
@@ -582,3 +647,101 @@ def test_batched_many_problems(kind, m, n, k, L):
     base = {"bf16": 1002, "fp8": 1004, "mxfp4": 1005}[kind]
     ws = [wl.make(kind, m, n, k, seed=base + 10 * z) for z in range(L)]
     _check_batched(ws)
+
+
+# ------------------------------------------------------------ edge-value operands
+
+def _codes_workload(name, type_ab, a_codes, b_codes, type_d="bf16", a_scale=1.0, b_scale=1.0, sfa=None, sfb=None):
+    """A T/N workload from stored codes: a_codes is op(A) as M x K rows, b_codes
+    op(B) as N x K rows (both K-contiguous, e2m1 already packed)."""
+    import workloads as wl
+
+    m, n = a_codes.shape[0], b_codes.shape[0]
+    k = a_codes.shape[1] * (2 if type_ab == "e2m1" else 1)
+    kw = {}
+    if sfa is not None:
+        kw = dict(sfa=sfa, ld_sfa=sfa.shape[1], sfb=sfb, ld_sfb=sfb.shape[1])
+    return wl.Workload(name=name, m=m, n=n, k=k, type_a=type_ab, type_b=type_ab, type_d=type_d, op_a="T",
+                       op_b="N", lda=k, ldb=k, ldd=m, a=np.ascontiguousarray(a_codes),
+                       b=np.ascontiguousarray(b_codes), a_scale=a_scale, b_scale=b_scale, **kw)
+
+
+def _fp8_extreme_codes(g, rows, k, top_code, small_codes, shift):
+    """Each 64-element K block of each row holds one +-top element (at a
+    position that moves with the row and block) among random small codes of
+    either sign."""
+    codes = g.choice(small_codes, size=(rows, k)).astype(np.uint8)
+    codes |= (g.integers(0, 2, size=(rows, k)) << 7).astype(np.uint8)
+    for r in range(rows):
+        for blk in range(k // 64):
+            pos = blk * 64 + (shift * r + blk) % 64
+            codes[r, pos] = top_code | (int(g.integers(0, 2)) << 7)
+    return codes
+
+
+@pytest.mark.parametrize("fmt,type_d", [("e4m3", "f32"), ("e4m3", "bf16"), ("e5m2", "f32"), ("e5m2", "bf16")])
+def test_fp8_largest_codes_among_small_ones(fmt, type_d):
+    # +-448 (e4m3 0x7E) or +-57344 (e5m2 0x7B) once in every 64-element K
+    # block, the rest small codes of both signs (e4m3 exponents 1..6, i.e.
+    # 2^-6 .. 0.94; e5m2 exponents 1..14, i.e. 2^-14 .. 0.875), K = 8192.
+    # Where the large elements of a row and a column meet in one block the
+    # product is 448^2 (57344^2) beside products many binades smaller; every
+    # output is checked against the oracle at the bar.
+    g = np.random.default_rng(71 if fmt == "e4m3" else 72)
+    k, m, n = 8192, 256, 256
+    if fmt == "e4m3":
+        top, small = 0x7E, np.arange(0x08, 0x38)
+    else:
+        top, small = 0x7B, np.arange(0x04, 0x3C)
+    a = _fp8_extreme_codes(g, m, k, top, small, 1)
+    b = _fp8_extreme_codes(g, n, k, top, small, 3)
+    _check_full(_codes_workload(f"{fmt}-extremes", fmt, a, b, type_d=type_d))
+
+
+@pytest.mark.parametrize("va,vb", [(127, 127), (-128, -128), (127, -128)])
+def test_int8_extremes_4096_exact(va, vb):
+    # All of A = va and all of B = vb at 4096^3: every output is exactly
+    # 4096 * va * vb (66,064,384, 67,108,864 and -66,584,576), checked on the
+    # whole of D, and the oracle's sample agrees.
+    import workloads as wl
+    from workloads.device import DeviceProblem
+
+    m = n = k = 4096
+    w = wl.Workload(name="int8-extremes", m=m, n=n, k=k, type_a="i8", type_b="i8", type_d="i32", op_a="T",
+                    op_b="N", lda=k, ldb=k, ldd=m, a=np.full((m, k), va, np.int8), b=np.full((n, k), vb, np.int8))
+    _say(f"[int8 extremes] {va} x {vb} at {m}^3")
+    dp = DeviceProblem(w)
+    assert dp.run() == 0
+    torch.cuda.synchronize()
+    assert bool((dp.d[:, :m] == k * va * vb).all())
+    _check_sampled_existing(w, dp)
+
+
+def _check_sampled_existing(w, dp):
+    from oracle import compare
+
+    rows, cols = w.sample(4096)
+    res = compare.parity_check(w, dp.d_values(rows, cols), rows, cols)
+    assert res["ok"], res
+
+
+@pytest.mark.parametrize("type_d", ["f32", "bf16"])
+def test_mxfp4_largest_codes_under_spread_scales(type_d):
+    # e2m1 +-6 (codes 0x7 / 0xF) in every 32-element block among random
+    # codes, with E8M0 scales drawn over 2^-20 .. 2^20 (codes 107 .. 147):
+    # products span about 2^-83 .. 2^45.  K = 8192, every output checked.
+    import workloads as wl
+
+    g = np.random.default_rng(73)
+    m, n, k = 256, 192, 8192
+    def operand(rows):
+        codes = g.integers(0, 16, size=(rows, k)).astype(np.uint8)
+        for r in range(rows):
+            for blk in range(k // 32):
+                codes[r, blk * 32 + (5 * r + blk) % 32] = 0x7 | (int(g.integers(0, 2)) << 3)
+        sf = np.full((rows, k // 32), 127, np.uint8)
+        sf[:, :] = g.integers(107, 148, size=(rows, k // 32))
+        return wl.pack_e2m1(codes), sf
+    a, sfa = operand(m)
+    b, sfb = operand(n)
+    _check_full(_codes_workload("e2m1-spread", "e2m1", a, b, type_d=type_d, sfa=sfa, sfb=sfb))

@@ -320,12 +320,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_u(const void* base, 
                                           __builtin_amdgcn_readfirstlane(num), 0x00020000);
 }
 
-// 16-byte buffer load and store at the resource base + voffset + soffset.
+// 16-byte buffer load at the resource base + voffset + soffset.
 __device__ __forceinline__ v4i buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t vo, int so) {
   return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, 0));
 }
+// 16-byte buffer store at the resource base + voffset + so, with the whole
+// offset in the vector operand and a zero soffset.  A store of more than 8
+// bytes reads its data registers over the cycles after it issues, so a VALU
+// write of those registers must wait a few cycles.  The compiler inserts
+// that wait for buffer stores with a zero soffset (and for global stores),
+// but not for ones whose soffset is a scalar register: there, a register
+// reused at once for the next run's arithmetic was stored instead of the
+// packed outputs (first dword of some lanes' 16-byte runs).
 __device__ __forceinline__ void buf_store16(v4i v, __amdgpu_buffer_rsrc_t r, uint32_t vo, int so) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), r, vo, so, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), r, vo + static_cast<uint32_t>(so), 0, 0);
 }
 
 // Bitwise select (a where m is set, else b): keeps a uniform type or flag
@@ -1379,13 +1387,12 @@ gemm_kernel(GemmArgs p) {
     });
   };
 
+  // The vector path needs registers for a batch of C runs next to the
+  // staging: it is built where that fits without spilling (one workgroup per
+  // CU, or the 128x128 two-workgroup variant with 16-byte copies).
+  constexpr bool VEC_EPI = !T::INT && (OCC == 1 || (BM * BN <= 128 * 128 && LOADW == 16));
   auto epilogue = [&](const int64_t em0, const int64_t en0) {
-    // The vector path runs in the one-workgroup-per-CU variants only.  With
-    // two workgroups per CU (256 registers a wave) it spills heavily, and
-    // with C or bias reads it produced wrong values in a few hundredths of a
-    // percent of the outputs (rows 0-1 of some 8-row runs) once two
-    // workgroups shared each CU; the general path is exact there.
-    if constexpr (!T::INT && OCC == 1) {
+    if constexpr (VEC_EPI) {
       if ((p.flags & EPI_VEC) && !(p.flags & EPI_GELU) && em0 + BM <= p.m && en0 + BN <= p.n) {
         const bool has_c = nonzero_f32(p.beta), has_bias = (p.flags & EPI_BIAS) != 0;
         const bool bf = (!has_c || p.c_type == DT_BF16) && p.d_type == DT_BF16 &&
