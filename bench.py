@@ -4,12 +4,24 @@ A step is one pass of the hot path: one thl_gemm call (validation, dispatch,
 the tiled MFMA kernel with its fused epilogue) over inputs already resident
 in HBM.  The headline workload is the bf16 GEMM at M = N = K = 8192, all
 operands column-major (op N/N), with the relu(A.B + C + bias[m]) epilogue
-(bf16 out, fp32 accumulate); the fp8 (e4m3 and e5m2, per-tensor scales),
-MXFP8 (e4m3 with E8M0 block scales) and MXFP4 (e2m1 with E8M0 block scales,
-D = A.B + C)
-GEMMs at 8192^3 are timed the same way and reported in the same line, and
-so are the single-row fp8 GEMM (M = 1, N = K = 8192), against the HBM peak,
-and a batched bf16 GEMM (16 problems of 2048^3 in one launch).
+(bf16 out, fp32 accumulate).
+
+Every configuration of the benchmark set is timed the same way and reported
+in the same line under "configs", each with its own bound (MFMA, HBM or
+launch latency), fraction of that bound's peak, a parity check against the
+oracle (all outputs at 256^3, else a seeded sample of 4096 outputs, plus the
+whole last row and column of the ragged shapes) and the oracle's own time
+for the outputs it checked:
+
+  fp16 256^3 (T/N, fp32 out), bf16 4096^3 and 8192^3 (N/N, relu(A.B + C +
+  bias)), int8 4096^3 (T/N, int32 out, exact), fp8 e4m3 8192^3,
+  4097x1000x2040 and 1x8192x8192 (T/N, per-tensor scales, bf16 out), MXFP4
+  8192^3 (T/N, D = A.B + C); and, beside them, e5m2 and MXFP8 at 8192^3 and a
+  batched bf16 GEMM (16 problems of 2048^3 in one launch).
+
+Each launch is bracketed by HIP events on the stream it runs on: the mean
+over the timed launches is the throughput; the median and minimum of the
+per-launch times are reported with it.
 
 Prints ONE JSON line on stdout (diagnostics go to stderr).
 """
@@ -19,13 +31,14 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-# MI355X published dense peaks (TFLOP/s, TOP/s for int8) and HBM bandwidth.
+# MI355X published dense peaks (TFLOP/s; TOP/s for int8) and HBM bandwidth.
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2, "e5m2": 5033.2, "mxe4m3": 5033.2, "e2m1": 10066.3,
                "i8": 5033.2}
 HBM_PEAK_GBS = 8000.0
@@ -34,14 +47,34 @@ CSRC = os.path.join(ROOT, "tile_hierarchy_linear_amd", "csrc")
 # Summary of the FETCH_SIZE / WRITE_SIZE counter runs over this script.
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_8192_hbm_traffic.md")
 
+METRIC = "GEMM TFLOP/s and % of MFMA peak (bf16, fp8, MXFP4 at M=N=K=8192)"
+
+# (key, workload kind, m, n, k, bound, launches per timed step)
+CONFIGS = [
+    ("fp16_256", "fp16", 256, 256, 256, "latency", 10),
+    ("bf16_4096", "bf16", 4096, 4096, 4096, "mfma", 2),
+    ("bf16_8192", "bf16", 8192, 8192, 8192, "mfma", 1),
+    ("int8_4096", "int8", 4096, 4096, 4096, "mfma", 2),
+    ("fp8_8192", "fp8", 8192, 8192, 8192, "mfma", 1),
+    ("fp8_4097x1000x2040", "fp8", 4097, 1000, 2040, "mfma", 5),
+    ("fp8_1x8192x8192", "fp8", 1, 8192, 8192, "hbm", 10),
+    ("mxfp4_8192", "mxfp4", 8192, 8192, 8192, "mfma", 1),
+    ("e5m2_8192", "fp8e5m2", 8192, 8192, 8192, "mfma", 1),
+    ("mxfp8_8192", "mxfp8", 8192, 8192, 8192, "mfma", 1),
+]
+HEADLINE = "bf16_8192"
+PEAK_KEY = {"f16": "f16", "bf16": "bf16", "i8": "i8", "e4m3": "e4m3", "e5m2": "e5m2", "e2m1": "e2m1"}
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
 def page_flops_bytes(m, n, k, a_bytes, b_bytes, d_bytes, c_bytes=0):
-    """The profiler's bookkeeping on the pages: FLOPs = 2MNK + 2MN and
-    Bytes = |A| + |B| + |D| (+|C| when beta != 0)."""
+    """The profiler's bookkeeping on the pages ("Technical Documentation:
+    NVIDIA/cutlass", "Performance Profiling", its sample output): FLOPs =
+    2MNK + 2MN and Bytes = |A| + |B| + |D| (+|C| when beta != 0), with
+    elements of a_bytes, b_bytes, c_bytes, d_bytes bytes."""
     return 2 * m * n * k + 2 * m * n, m * k * a_bytes + k * n * b_bytes + m * n * d_bytes + m * n * c_bytes
 
 
@@ -57,7 +90,7 @@ def compulsory_bytes(w):
         total += w.m * eb[w.type_bias]
     if w.sfa is not None:
         total += (w.m + w.n) * (w.k // 32)
-    return total
+    return int(total)
 
 
 def kernel_source_hash():
@@ -89,60 +122,225 @@ def measured_traffic(variant, m, n, k):
     return None
 
 
-def time_gemm(dp, steps, warmup, stream):
-    """Average duration of one thl_gemm launch, with HIP events recorded on
-    the stream the kernel runs on."""
+def time_launches(run, steps, warmup, stream):
+    """Launch `run` warmup times untimed, then `steps` times with a HIP event
+    before and after each launch on `stream` (the stream the kernels run on).
+    Returns (mean, median, min) per launch in ms; the mean is over the whole
+    timed region (first event to last)."""
     import torch
 
     for _ in range(warmup):
-        st = dp.run(stream=stream.cuda_stream)
+        st = run()
         assert st == 0, st
     torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(steps):
-        dp.run(stream=stream.cuda_stream)
-    stop.record(stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        run()
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    return start.elapsed_time(stop) / steps  # ms
+    each = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    mean = ev[0].elapsed_time(ev[steps]) / steps
+    return mean, each[len(each) // 2], each[0]
 
 
-def quick_parity(w, dp, count=512):
-    from oracle import compare
-
-    rows, cols = w.sample(count)
-    res = compare.parity_check(w, dp.d_values(rows, cols), rows, cols)
-    return "ok" if res["ok"] else f"FAIL({res['n_bad']}/{res['n']})"
-
-
-def cpu_baseline(w, budget_s):
-    """The oracle timed on this host's cores over a bounded sample of D."""
+def parity_and_oracle_time(w, dp, full=False, edges=False):
+    """Compare D with the oracle (every output when `full`, else the seeded
+    4096-output sample; `edges` adds the whole last row and column) and time
+    the oracle's evaluation of the outputs it checked (all host threads)."""
     import numpy as np
 
     import oracle
+    from oracle import compare
 
-    nthreads = oracle.max_threads()
-    # Two pilots: the first includes one-time setup and overestimates the
-    # per-output cost; the second, sized for about a tenth of the budget,
-    # sets the size of the timed sample.
-    pilot = 16 * nthreads
-    for _ in range(2):
-        rows, cols = w.sample(pilot)
+    if full:
+        ii, jj = np.meshgrid(np.arange(w.m), np.arange(w.n), indexing="ij")
+        rows, cols = ii.ravel(), jj.ravel()
+        kind = f"all {w.m * w.n} outputs"
+    else:
+        rows, cols = w.sample(4096)
+        kind = f"{rows.size} seeded outputs"
+        if edges:
+            rows = np.concatenate([rows, np.full(w.n, w.m - 1), np.arange(w.m)])
+            cols = np.concatenate([cols, np.arange(w.n), np.full(w.m, w.n - 1)])
+            kind += f" + last row ({w.n}) and last column ({w.m})"
+    t0 = time.perf_counter()
+    ref = oracle.gemm_elements(w.oracle_problem(), rows, cols)
+    dt = time.perf_counter() - t0
+    res = compare.parity_check(w, dp.d_values(rows, cols), rows, cols, ref=ref)
+    bar = "bit-exact" if w.type_a == "i8" else "2^-20*K*max|a'|*max|b'| + 1 ulp"
+    out = {"ok": bool(res["ok"]), "checked": kind, "n_bad": res["n_bad"], "bar": bar}
+    if "max_err" in res:
+        out["max_err"] = res["max_err"]
+    oracle_t = {"outputs": int(rows.size), "seconds": round(dt, 3), "threads": oracle.max_threads(),
+                "extrapolated_full_d_s": round(dt * w.m * w.n / rows.size, 1)}
+    return out, oracle_t
+
+
+def run_config(key, kind, m, n, k, bound, mult, args, stream):
+    import torch
+
+    import tile_hierarchy_linear_amd as thl
+    import workloads as wl
+    from workloads.device import DeviceProblem
+
+    t0 = time.perf_counter()
+    w = wl.make(kind, m, n, k)
+    dp = DeviceProblem(w)
+    log(f"[{key}] inputs generated and uploaded in {time.perf_counter() - t0:.1f} s")
+    steps, warmup = args.steps * mult, args.warmup * mult
+    mean, med, mn = time_launches(lambda: dp.run(stream=stream.cuda_stream), steps, warmup, stream)
+    variant = thl.thl_last_variant()
+    flops = w.flops()
+    peak_key = "mxe4m3" if kind == "mxfp8" else PEAK_KEY[w.type_a]
+    peak = PEAK_TFLOPS[peak_key]
+    tflops = flops / (mean * 1e-3) / 1e12
+    byt = compulsory_bytes(w)
+    gbs = byt / (mean * 1e-3) / 1e9
+    eb = wl.ELEM_BYTES
+    pf, pb = page_flops_bytes(m, n, k, eb[w.type_a], eb[w.type_b], eb[w.type_d],
+                              eb[w.type_c] if w.beta != 0.0 else 0)
+    entry = {
+        "workload": describe(w), "variant": variant, "launches": steps,
+        "ms_mean": round(mean, 5), "ms_median": round(med, 5), "ms_min": round(mn, 5),
+        "tflops": round(tflops, 2), "bound": bound,
+        "algorithmic_bytes": byt, "hbm_gbs_algorithmic": round(gbs, 1),
+        "page_convention": {"flops": int(pf), "bytes": int(pb)},
+        "traffic": measured_traffic(variant, m, n, k),
+    }
+    if bound == "hbm":
+        entry["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    else:
+        entry["roofline"] = {"bound": "mfma" if bound == "mfma" else "latency", "achieved": round(tflops, 2),
+                             "peak": peak, "unit": "TOP/s" if w.type_a == "i8" else "TFLOP/s",
+                             "frac": round(tflops / peak, 4)}
+    try:
+        entry["parity"], entry["oracle"] = parity_and_oracle_time(w, dp, full=m * n <= 65536,
+                                                                  edges=(m % 256 != 0 or n % 256 != 0))
+    except Exception as e:  # noqa: BLE001 -- reported in the line, not fatal for timing
+        entry["parity"] = {"ok": False, "error": str(e)}
+    log(f"[{key}] mean {mean * 1e3:.1f} us (median {med * 1e3:.1f}, min {mn * 1e3:.1f}) {tflops:.1f} TFLOP/s "
+        f"frac {entry['roofline']['frac']:.3f} of the {entry['roofline']['bound']} peak via {variant}; "
+        f"parity {entry['parity'].get('ok')}")
+    if args.sweep_variants:
+        ops = (w.op_a + w.op_b).lower()
+        fam = variant.split("_")[0]
+        for v in thl.variants():
+            if not v.startswith(f"{fam}_{ops}_"):
+                continue
+            os.environ["THL_FORCE_VARIANT"] = v
+            try:
+                vm, _, _ = time_launches(lambda: dp.run(stream=stream.cuda_stream), max(3, steps // 2), 2, stream)
+                log(f"   sweep {v}: {vm * 1e3:.1f} us {flops / (vm * 1e-3) / 1e12:.1f} TFLOP/s")
+            except AssertionError as e:
+                log(f"   sweep {v}: not applicable ({e})")
+            finally:
+                os.environ.pop("THL_FORCE_VARIANT", None)
+    del dp
+    torch.cuda.empty_cache()
+    return w, entry
+
+
+def describe(w):
+    epi = []
+    if w.beta != 0.0:
+        epi.append("C")
+    if w.bias is not None:
+        epi.append("bias[m]")
+    body = "A.B" + "".join(" + " + e for e in epi)
+    if w.act != "none":
+        body = f"{w.act}({body})"
+    scales = ""
+    if w.sfa is not None:
+        scales = ", E8M0 scale per 32 K-elements"
+    elif w.type_a in ("e4m3", "e5m2"):
+        scales = ", per-tensor scales"
+    return (f"{w.type_a} GEMM M={w.m} N={w.n} K={w.k}, op {w.op_a}{w.op_b}{scales}, D = {body}, "
+            f"{w.type_d} out")
+
+
+def run_batched(args, stream):
+    import torch
+
+    import tile_hierarchy_linear_amd as thl
+    import workloads as wl
+    from oracle import compare
+    from workloads.device import BatchedDeviceProblem
+
+    L, sz = 16, 2048
+    t0 = time.perf_counter()
+    ws = [wl.make("bf16", sz, sz, sz, seed=1002 + 100 * z) for z in range(L)]
+    bp = BatchedDeviceProblem(ws)
+    log(f"[batched] {L} problems generated and uploaded in {time.perf_counter() - t0:.1f} s")
+    mean, med, mn = time_launches(lambda: bp.run(stream=stream.cuda_stream), args.steps, args.warmup, stream)
+    vb = thl.thl_last_variant()
+    tfb = L * ws[0].flops() / (mean * 1e-3) / 1e12
+    ok = True
+    for z in (0, L - 1):
+        rows, cols = ws[z].sample(4096)
+        got = bp.d_all(z)[rows, cols]
+        ok = ok and compare.parity_check(ws[z], got, rows, cols)["ok"]
+    out = {"workload": f"bf16 GEMM, {L} problems of M=N=K={sz}, op NN, D = relu(A.B + C + bias[m]), bf16 out, "
+                       "one batched launch",
+           "variant": vb, "ms_mean": round(mean, 5), "ms_median": round(med, 5), "ms_min": round(mn, 5),
+           "tflops": round(tfb, 1),
+           "roofline": {"bound": "mfma", "achieved": round(tfb, 1), "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
+                        "frac": round(tfb / PEAK_TFLOPS["bf16"], 4)},
+           "parity": {"ok": bool(ok), "checked": "4096 seeded outputs of problems 0 and 15"}}
+    log(f"[batched] {mean:.3f} ms {tfb:.1f} TFLOP/s via {vb}; parity {ok}")
+    del bp
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(w, budget_s, budget_1t_s):
+    """The oracle timed on this host's cores over a bounded sample of the
+    headline D: all OpenMP threads for about budget_s seconds, then one thread
+    for about budget_1t_s."""
+    import oracle
+
+    def timed(nthreads, budget):
+        # Two pilots: the first includes one-time setup and overestimates the
+        # per-output cost; the second, sized for about a tenth of the budget,
+        # sets the size of the timed sample.
+        pilot = 16 * nthreads
+        per = 1.0
+        for _ in range(2):
+            rows, cols = w.sample(pilot)
+            t0 = time.perf_counter()
+            oracle.gemm_elements(w.oracle_problem(), rows, cols, nthreads)
+            per = max(time.perf_counter() - t0, 1e-6) / pilot
+            pilot = int(min(max(pilot, 0.1 * budget / per), w.m * w.n))
+        count = int(min(max(16 * nthreads, budget / per), w.m * w.n))
+        rows, cols = w.sample(count)
         t0 = time.perf_counter()
         oracle.gemm_elements(w.oracle_problem(), rows, cols, nthreads)
-        t1 = time.perf_counter() - t0
-        per = max(t1, 1e-6) / pilot
-        pilot = int(min(max(pilot, 0.1 * budget_s / per), w.m * w.n))
-    count = int(min(max(16 * nthreads, budget_s / per), w.m * w.n))
-    rows, cols = w.sample(count)
-    t0 = time.perf_counter()
-    oracle.gemm_elements(w.oracle_problem(), rows, cols, nthreads)
-    dt = time.perf_counter() - t0
-    flops = 2.0 * w.k * count
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": nthreads, "kind": "oracle",
-            "sample": f"{count} seeded outputs of the {w.m}x{w.n}x{w.k} {w.type_a} GEMM "
-                      f"({2 * w.k} flops each) in {dt:.1f} s; full D extrapolated "
-                      f"{dt * w.m * w.n / count / 3600:.1f} h"}
+        return count, time.perf_counter() - t0
+
+    nthreads = oracle.max_threads()
+    count, dt = timed(nthreads, budget_s)
+    count1, dt1 = timed(1, budget_1t_s)
+    flops = 2.0 * w.k
+    return {"value": round(flops * count / dt / 1e12, 6), "unit": "TFLOP/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"{count} seeded outputs of the {w.m}x{w.n}x{w.k} {w.type_a} GEMM ({2 * w.k} flops each) "
+                      f"in {dt:.1f} s on {nthreads} threads; full D extrapolated "
+                      f"{dt * w.m * w.n / count / 3600:.1f} h",
+            "one_thread": {"value": round(flops * count1 / dt1 / 1e12, 6), "unit": "TFLOP/s",
+                           "sample": f"{count1} seeded outputs in {dt1:.1f} s; full D extrapolated "
+                                     f"{dt1 * w.m * w.n / count1 / 3600:.1f} h"},
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
 
 
 def copy_calibration(mib):
@@ -163,13 +361,15 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--size", type=int, default=8192)
-    ap.add_argument("--only", default="", help="comma list of bf16,e4m3,e5m2,mxe4m3,e2m1,m1,batched (default: all)")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--only", default="",
+                    help="comma list of configuration keys (" + ",".join(c[0] for c in CONFIGS) +
+                         ",batched); default: all")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work on all threads")
+    ap.add_argument("--cpu-budget-1t", type=float, default=4.0, help="seconds of oracle work on one thread")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0)
     ap.add_argument("--sweep-variants", action="store_true",
-                    help="also time every built variant of each dtype (stderr)")
+                    help="also time every built variant of each configuration's family (stderr)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -179,159 +379,57 @@ def main():
 
     import torch
 
-    import tile_hierarchy_linear_amd as thl
-    import workloads as wl
-    from workloads.device import DeviceProblem
-
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
-    s = args.size
-    only = set(x for x in args.only.split(",") if x) or {"bf16", "e4m3", "e5m2", "mxe4m3", "e2m1", "m1", "batched"}
+    keys = [c[0] for c in CONFIGS] + ["batched"]
+    only = [x for x in args.only.split(",") if x] or keys
+    unknown = set(only) - set(keys)
+    if unknown:
+        print(f"unknown configuration keys {sorted(unknown)}", file=sys.stderr)
+        sys.exit(2)
 
-    results = {}
-    headline = None
-    for key, kind, kw in (("bf16", "bf16", {}), ("e4m3", "fp8", {}), ("e5m2", "fp8e5m2", {}), ("mxe4m3", "mxfp8", {}),
-                          ("e2m1", "mxfp4", {})):
-        if key not in only:
-            continue
-        t0 = time.perf_counter()
-        w = wl.make(kind, s, s, s, **kw)
-        dp = DeviceProblem(w)
-        log(f"[{key}] inputs generated and uploaded in {time.perf_counter() - t0:.1f} s")
-        ms = time_gemm(dp, args.steps, args.warmup, stream)
-        variant = thl.thl_last_variant()
-        flops = w.flops()
-        tflops = flops / (ms * 1e-3) / 1e12
-        byt = compulsory_bytes(w)
-        entry = {"tflops": round(tflops, 1), "frac_of_peak": round(tflops / PEAK_TFLOPS[key], 4),
-                 "peak_tflops": PEAK_TFLOPS[key], "ms": round(ms, 4), "variant": variant,
-                 "op": w.op_a + w.op_b, "epilogue": {"act": w.act, "beta": w.beta, "bias": w.bias is not None},
-                 "hbm_gbs_compulsory": round(byt / (ms * 1e-3) / 1e9, 1), "algorithmic_bytes": byt,
-                 "traffic": measured_traffic(variant, w.m, w.n, w.k)}
-        try:
-            entry["parity_sampled"] = quick_parity(w, dp)
-        except Exception as e:  # noqa: BLE001 -- reported, not fatal for timing
-            entry["parity_sampled"] = f"error: {e}"
-        results[key] = entry
-        log(f"[{key}] {ms:.3f} ms  {tflops:.1f} TFLOP/s  ({100 * tflops / PEAK_TFLOPS[key]:.1f}% of peak) "
-            f"via {variant}; parity {entry['parity_sampled']}")
-        if key == "bf16":
-            headline = (w, ms, byt, variant)
-        if headline is None and key == min(only - {"m1", "batched"}):
-            headline = (w, ms, byt, variant)
-        if args.sweep_variants:
-            fam = key
-            ops = (w.op_a + w.op_b).lower()
-            for v in thl.variants():
-                if not v.startswith(f"{fam}_{ops}_"):
-                    continue
-                os.environ["THL_FORCE_VARIANT"] = v
-                try:
-                    vms = time_gemm(dp, max(3, args.steps // 2), 2, stream)
-                    log(f"   sweep {v}: {vms:.3f} ms {flops / (vms * 1e-3) / 1e12:.1f} TFLOP/s")
-                except AssertionError as e:
-                    log(f"   sweep {v}: not applicable ({e})")
-                finally:
-                    os.environ.pop("THL_FORCE_VARIANT", None)
-        del dp
-        torch.cuda.empty_cache()
-
-    # The single-row fp8 configuration (M = 1, N = K = s): HBM-bound, so its
-    # roofline is bytes per second against the HBM peak.  A launch is about
-    # 12 us, so it is timed over ten times as many launches.
-    small_m = None
-    if "m1" in only:
-        w1 = wl.make("fp8", 1, s, s)
-        dp1 = DeviceProblem(w1)
-        ms1 = time_gemm(dp1, 10 * args.steps, 2 * args.warmup, stream)
-        v1 = thl.thl_last_variant()
-        byt1 = compulsory_bytes(w1)
-        gbs = byt1 / (ms1 * 1e-3) / 1e9
-        small_m = {"workload": f"fp8 e4m3 GEMM M=1, N=K={s}, op TN, per-tensor scales, bf16 out",
-                   "us": round(ms1 * 1e3, 2), "variant": v1,
-                   "tflops": round(w1.flops() / (ms1 * 1e-3) / 1e12, 2),
-                   "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": byt1,
-                                "traffic": measured_traffic(v1, w1.m, w1.n, w1.k)}}
-        try:
-            small_m["parity_sampled"] = quick_parity(w1, dp1)
-        except Exception as e:  # noqa: BLE001 -- reported, not fatal for timing
-            small_m["parity_sampled"] = f"error: {e}"
-        log(f"[m1] {ms1 * 1e3:.2f} us  {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of HBM peak) via {v1}; "
-            f"parity {small_m['parity_sampled']}")
-        del dp1
-        torch.cuda.empty_cache()
-
-    # Batched (L mode): 16 problems of the headline's layout and epilogue at
-    # M = N = K = s/4, one thl_gemm_batched launch.
-    batched = None
+    configs = {}
+    workloads = {}
+    for key, kind, m, n, k, bound, mult in CONFIGS:
+        if key in only:
+            workloads[key], configs[key] = run_config(key, kind, m, n, k, bound, mult, args, stream)
     if "batched" in only:
-        from oracle import compare
-        from workloads.device import BatchedDeviceProblem
-
-        L, sz = 16, max(256, s // 4)
-        t0 = time.perf_counter()
-        ws = [wl.make("bf16", sz, sz, sz, seed=1002 + 100 * z) for z in range(L)]
-        bp = BatchedDeviceProblem(ws)
-        log(f"[batched] {L} problems generated and uploaded in {time.perf_counter() - t0:.1f} s")
-
-        msb = time_gemm(bp, args.steps, args.warmup, stream)
-        vb = thl.thl_last_variant()
-        tfb = L * ws[0].flops() / (msb * 1e-3) / 1e12
-        status = "ok"
-        for z in (0, L - 1):
-            rows, cols = ws[z].sample(512)
-            got = bp.d_all(z)[rows, cols]
-            res = compare.parity_check(ws[z], got, rows, cols)
-            if not res["ok"]:
-                status = f"FAIL(problem {z}: {res['n_bad']}/{res['n']})"
-        batched = {"workload": f"bf16 GEMM, {L} problems of M=N=K={sz}, op NN, D = relu(A.B + C + bias[m]), "
-                               "bf16 out, one batched launch",
-                   "ms": round(msb, 4), "tflops": round(tfb, 1), "frac_of_peak": round(tfb / PEAK_TFLOPS["bf16"], 4),
-                   "variant": vb, "parity_sampled": status}
-        log(f"[batched] {msb:.3f} ms  {tfb:.1f} TFLOP/s ({100 * tfb / PEAK_TFLOPS['bf16']:.1f}% of peak) via {vb}; "
-            f"parity {status}")
-        del bp
-        torch.cuda.empty_cache()
-
+        configs["batched"] = run_batched(args, stream)
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib)
 
-    if headline is None:
-        print("--only needs one of bf16, e4m3, e5m2, mxe4m3, e2m1 for the headline line", file=sys.stderr)
+    head = HEADLINE if HEADLINE in configs else next((k for k in configs if k != "batched"), None)
+    if head is None:
+        print("--only needs one GEMM configuration for the headline line", file=sys.stderr)
         sys.exit(2)
-    w, ms, byt, variant = headline
-    key = w.type_a
-    tflops = w.flops() / (ms * 1e-3) / 1e12
+    w, h = workloads[head], configs[head]
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, args.cpu_budget)
+        cpu = cpu_baseline(w, args.cpu_budget, args.cpu_budget_1t)
+    roof = dict(h["roofline"])
+    roof.update({"traffic": h["traffic"], "algorithmic_bytes": h["algorithmic_bytes"],
+                 "kernel_sources": kernel_source_hash()})
     line = {
-        "metric": "GEMM TFLOP/s and % of MFMA peak (bf16, fp8, MXFP4 at M=N=K=8192)",
-        "value": round(tflops, 1),
+        "metric": METRIC,
+        "value": h["tflops"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": h["ms_mean"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.type_a,
-        "data": "synthetic (seeded PCG64; U[-1,1] bf16 A, B, C, bias)",
-        "config": {"workload": f"{key} GEMM M=N=K={s} op {w.op_a}{w.op_b}, D = relu(A.B + C + bias[m]), "
-                               f"fp32 accumulate, {w.type_d} out", "m": w.m, "n": w.n, "k": w.k,
-                   "kernel_variant": variant},
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_TFLOPS[key], "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_TFLOPS[key], 4),
-                     "traffic": measured_traffic(variant, w.m, w.n, w.k),
-                     "algorithmic_bytes": byt, "kernel_sources": kernel_source_hash()},
-        "dtypes": results,
-        "small_m": small_m,
-        "batched": batched,
+        "data": "synthetic (seeded PCG64 streams per tensor; see each configuration's workload)",
+        "config": {"workload": h["workload"] + ", fp32 accumulate", "m": w.m, "n": w.n, "k": w.k,
+                   "kernel_variant": h["variant"], "ms_median": h["ms_median"], "ms_min": h["ms_min"],
+                   "parity": h.get("parity")},
+        "roofline": roof,
+        "configs": configs,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

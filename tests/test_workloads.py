@@ -46,3 +46,40 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_bench_bookkeeping_reproduces_the_profiler_sample():
+    # The profiler's sample output on the pages ("Technical Documentation:
+    # NVIDIA/cutlass", "Performance Profiling"): an f16 x f16 -> f32 GEMM with
+    # M=3456, N=4096, K=4096 and beta = 0 prints FLOPs 115992428544 and Bytes
+    # 118489088 (A and B at 2 bytes, D at 4).
+    sys.path.insert(0, ROOT)
+    import bench
+
+    flops, byts = bench.page_flops_bytes(3456, 4096, 4096, 2, 2, 4)
+    assert flops == 115992428544
+    assert byts == 118489088
+
+
+def test_bench_compulsory_bytes_of_the_headline_workload():
+    # bf16 8192^3 with C and bias: A, B, C, D at 2 bytes plus an 8192-row bf16 bias
+    sys.path.insert(0, ROOT)
+    import bench
+
+    w = wl.make("bf16", 64, 48, 32)
+    assert bench.compulsory_bytes(w) == 2 * (64 * 32 + 32 * 48 + 64 * 48 + 64 * 48 + 64)
+    w4 = wl.make("mxfp4", 64, 48, 64)
+    # packed fp4 operands, one scale byte per 32 K-elements per row and column, C and D bf16
+    assert bench.compulsory_bytes(w4) == 64 * 32 + 48 * 32 + (64 + 48) * 2 + 2 * 2 * 64 * 48
+
+
+def test_bench_lists_every_configuration():
+    sys.path.insert(0, ROOT)
+    import bench
+
+    shapes = {(c[1], c[2], c[3], c[4]) for c in bench.CONFIGS}
+    for need in (("fp16", 256, 256, 256), ("bf16", 4096, 4096, 4096), ("bf16", 8192, 8192, 8192),
+                 ("int8", 4096, 4096, 4096), ("fp8", 8192, 8192, 8192), ("fp8", 4097, 1000, 2040),
+                 ("fp8", 1, 8192, 8192), ("mxfp4", 8192, 8192, 8192)):
+        assert need in shapes
+    assert bench.HEADLINE == "bf16_8192"
