@@ -77,7 +77,7 @@ def operand_max_abs(w, which: str) -> float:
             return 0.0
         scales = decode("e8m0", np.ascontiguousarray(sf)).reshape(rows, ld_sf)[:, : w.k // 32]
         vals = vals.reshape(rows, w.k // 32, 32) * scales[:, :, None]
-        per_tensor = (w.a_scale if which == "a" else w.b_scale) if fmt == "e4m3" else 1.0
+        per_tensor = (w.a_scale if which == "a" else w.b_scale) if fmt in ("e4m3", "e5m2") else 1.0
         return float(np.abs(vals).max()) * per_tensor
     scale = (w.a_scale if which == "a" else w.b_scale) if fmt in ("e4m3", "e5m2") else 1.0
     return float(np.abs(vals).max()) * scale

@@ -48,7 +48,8 @@ def test_status_strings():
 def test_variants_are_listed():
     vs = thl.variants()
     assert len(vs) == thl.thl_variant_count() > 0
-    for fam in ("bf16", "f16", "i8", "e4m3", "e5m2", "e2m1", "mxe4m3", "e4m3e5m2", "e5m2e4m3"):
+    for fam in ("bf16", "f16", "i8", "e4m3", "e5m2", "e2m1", "mxe4m3", "e4m3e5m2", "e5m2e4m3", "mxe5m2",
+                "mxe4m3e5m2", "mxe5m2e4m3"):
         assert any(v.startswith(fam + "_") for v in vs)
     assert thl.thl_variant_name(-1) is None and thl.thl_variant_name(len(vs)) is None
 
@@ -110,16 +111,13 @@ def test_unsupported_combinations():
     mixed = thl.make_dtypes("e4m3", "bf16", "f32", "bf16")  # mixed only within fp8
     assert thl.thl_gemm(64, 64, 64, A, 64, "T", B, 64, "N", None, 64, D, 64, 1.0, 0.0, mixed, None, None,
                         None) == thl.THL_ERR_UNSUPPORTED
-    mixed8 = thl.make_dtypes("e4m3", "e5m2", "f32", "bf16")  # e4m3 x e5m2: built, but not block-scaled
-    sc8 = thl.thl_scales(1.0, 1.0, SFA, 16, SFB, 16)
-    assert thl.thl_gemm(64, 64, 64, A, 64, "T", B, 64, "N", None, 64, D, 64, 1.0, 0.0, mixed8, None, sc8,
-                        None) == thl.THL_ERR_UNSUPPORTED
+    mixed8 = thl.make_dtypes("e4m3", "e5m2", "f32", "bf16")
     assert thl.thl_gemm(64, 0, 64, A, 64, "T", B, 64, "N", None, 64, D, 64, 1.0, 0.0, mixed8, None, None,
                         None) == thl.THL_OK
     assert thl.thl_last_variant().startswith("e4m3e5m2_")
 
 
-@pytest.mark.parametrize("fmt,td", [("bf16", "f32"), ("f16", "f32"), ("i8", "i32"), ("e5m2", "bf16")])
+@pytest.mark.parametrize("fmt,td", [("bf16", "f32"), ("f16", "f32"), ("i8", "i32")])
 def test_block_scales_with_formats_that_take_none_are_refused(fmt, td):
     # A block-scale array given with a format that has no block-scaled kernel
     # is refused, not dropped (the result would ignore the caller's scales).
@@ -130,16 +128,24 @@ def test_block_scales_with_formats_that_take_none_are_refused(fmt, td):
         assert call(m=0, types=(fmt, tc, td, "none"), sc=sc) == thl.THL_ERR_UNSUPPORTED
 
 
-def test_e4m3_with_one_scale_array_is_invalid():
-    # E4M3 with both arrays is MXFP8, with neither plain fp8; one alone is an error.
+@pytest.mark.parametrize("fa,fb,mx,plain", [("e4m3", "e4m3", "mxe4m3_", "e4m3_"), ("e5m2", "e5m2", "mxe5m2_", "e5m2_"),
+                                             ("e4m3", "e5m2", "mxe4m3e5m2_", "e4m3e5m2_"),
+                                             ("e5m2", "e4m3", "mxe5m2e4m3_", "e5m2e4m3_")])
+def test_fp8_block_scales_both_or_neither(fa, fb, mx, plain):
+    # fp8 operands with both arrays are MX fp8 (one scale per 32 K-elements),
+    # with neither plain fp8; one alone is an error.
+    dts = thl.make_dtypes(fa, fb, "f32", "bf16")
+
+    def go(sc, m=64):
+        return thl.thl_gemm(m, 64, 64, A, 64, "T", B, 64, "N", None, 64, D, 64, 1.0, 0.0, dts, None, sc, None)
+
     for sc in (thl.thl_scales(1.0, 1.0, SFA, 16, None, 0), thl.thl_scales(1.0, 1.0, None, 0, SFB, 16)):
-        assert call(types=("e4m3", "f32", "bf16", "none"), sc=sc) == thl.THL_ERR_INVALID
-        assert call(m=0, types=("e4m3", "f32", "bf16", "none"), sc=sc) == thl.THL_ERR_INVALID
-    both = thl.thl_scales(1.0, 1.0, SFA, 16, SFB, 16)
-    assert call(m=0, types=("e4m3", "f32", "bf16", "none"), sc=both) == thl.THL_OK
-    assert thl.thl_last_variant().startswith("mxe4m3_")
-    assert call(m=0, types=("e4m3", "f32", "bf16", "none"), sc=None) == thl.THL_OK
-    assert thl.thl_last_variant().startswith("e4m3_")
+        assert go(sc) == thl.THL_ERR_INVALID
+        assert go(sc, m=0) == thl.THL_ERR_INVALID
+    assert go(thl.thl_scales(1.0, 1.0, SFA, 16, SFB, 16), m=0) == thl.THL_OK
+    assert thl.thl_last_variant().startswith(mx)
+    assert go(None, m=0) == thl.THL_OK
+    assert thl.thl_last_variant().startswith(plain)
 
 
 def test_mxfp4_needs_scales():

@@ -137,3 +137,16 @@ def test_exact_check_for_integers():
     assert compare.check_exact(np.array([3, -4]), np.array([3, -4]))["ok"]
     r = compare.check_exact(np.array([3, -4]), np.array([3, -5]))
     assert not r["ok"] and r["n_bad"] == 1
+
+
+def test_operand_max_mx_e5m2_keeps_the_per_tensor_scale():
+    # MX fp8 with E5M2 elements: 0x7B = 57344 at block scale 2^-10 -> 56, times
+    # the per-tensor scale 1/4 -> 14 (the per-tensor scales multiply every fp8
+    # family, block-scaled or not)
+    a = np.zeros((1, 32), np.uint8)
+    a[0, 9] = 0x7B
+    sfa = _mx_scales(1, [[117]], 0xFF)
+    w = _w(k=32, lda=32, ldb=32, type_a="e5m2", type_b="e5m2", a=a, b=a.copy(), sfa=sfa, ld_sfa=16,
+           sfb=sfa.copy(), ld_sfb=16, a_scale=0.25, b_scale=1.0)
+    assert compare.operand_max_abs(w, "a") == 14.0
+    assert compare.operand_max_abs(w, "b") == 56.0

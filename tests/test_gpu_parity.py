@@ -230,13 +230,14 @@ def test_int8_epilogue_bias_beta_relu():
 
 
 @pytest.mark.parametrize("variant_family", ["f16", "bf16", "i8", "e4m3", "e5m2", "e2m1", "mxe4m3", "e4m3e5m2",
-                                            "e5m2e4m3"])
+                                            "e5m2e4m3", "mxe5m2", "mxe4m3e5m2", "mxe5m2e4m3"])
 def test_every_variant(variant_family):
     import tile_hierarchy_linear_amd as thl
     import workloads as wl
 
     kind = {"f16": "fp16", "bf16": "bf16", "i8": "int8", "e4m3": "fp8", "e5m2": "fp8e5m2",
-            "e2m1": "mxfp4", "mxe4m3": "mxfp8", "e4m3e5m2": "fp8e4e5", "e5m2e4m3": "fp8e5e4"}[variant_family]
+            "e2m1": "mxfp4", "mxe4m3": "mxfp8", "e4m3e5m2": "fp8e4e5", "e5m2e4m3": "fp8e5e4",
+            "mxe5m2": "mxfp8e5m2", "mxe4m3e5m2": "mxfp8e4e5", "mxe5m2e4m3": "mxfp8e5e4"}[variant_family]
     ops = {"tn": ("T", "N"), "nn": ("N", "N"), "tt": ("T", "T"), "nt": ("N", "T")}
     for v in thl.variants():
         if not v.startswith(variant_family + "_"):
@@ -594,16 +595,35 @@ def test_e5m2_8192_sampled():
     _check_sampled(wl.make("fp8e5m2", 8192, 8192, 8192))
 
 
+@pytest.mark.parametrize("kind,fam", [("mxfp8", "mxe4m3_"), ("mxfp8e5m2", "mxe5m2_"), ("mxfp8e4e5", "mxe4m3e5m2_"),
+                                      ("mxfp8e5e4", "mxe5m2e4m3_")])
 @pytest.mark.parametrize("m,n,k", [(1, 1, 32), (7, 17, 64), (65, 127, 288), (300, 200, 1024), (260, 130, 1056),
                                    (130, 300, 2048)])
-def test_mxfp8_shapes(m, n, k):
-    # MXFP8: e4m3 with one E8M0 scale per 32 K-elements, scale groups of
-    # eight K-steps; K from one block to 64 with partial last steps
+def test_mxfp8_shapes(m, n, k, kind, fam):
+    # MX fp8: E4M3 or E5M2 elements (or one of each) with one E8M0 scale per
+    # 32 K-elements, scale groups of eight K-steps; K from one block to 64
+    # with partial last steps
     import tile_hierarchy_linear_amd as thl
     import workloads as wl
 
-    _check_full(wl.make("mxfp8", m, n, k, lda=_pad(k, 16), ldb=_pad(k, 16), beta=1.0, bias=True, act="relu"))
-    assert thl.thl_last_variant().startswith("mxe4m3_")
+    _check_full(wl.make(kind, m, n, k, lda=_pad(k, 16), ldb=_pad(k, 16), beta=1.0, bias=True, act="relu"))
+    assert thl.thl_last_variant().startswith(fam)
+
+
+@pytest.mark.parametrize("kind", ["mxfp8e5m2", "mxfp8e4e5", "mxfp8e5e4"])
+def test_mx_fp8_pairs_8192_sampled(kind):
+    import workloads as wl
+
+    _check_sampled(wl.make(kind, 8192, 8192, 8192))
+
+
+@pytest.mark.parametrize("variant,kind", [("mxe5m2_tn_256x256_v16_s4_o1", "mxfp8e5m2"),
+                                          ("mxe4m3e5m2_tn_128x128_v16_s4_o2", "mxfp8e4e5"),
+                                          ("mxe5m2e4m3_tn_128x128_v4_s4_o2", "mxfp8e5e4")])
+def test_mx_fp8_pairs_every_variant(variant, kind):
+    import workloads as wl
+
+    _check_full(wl.make(kind, 600, 520, 1056), variant=variant)
 
 
 @pytest.mark.parametrize("variant", ["mxe4m3_tn_256x256_v16_s4_o1", "mxe4m3_tn_128x128_v16_s4_o2"])

@@ -348,19 +348,22 @@ def test_bruteforce_exact_on_tiny_inputs(fmt, trial):
             assert abs(Fraction(got[i, j]) - want[i, j]) <= Fraction(2) ** -48 * (1 + abs(want[i, j]))
 
 
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e5m2"), ("e4m3", "e5m2"), ("e5m2", "e4m3")])
 @pytest.mark.parametrize("trial", range(3))
-def test_bruteforce_exact_mxfp8(trial):
-    # e4m3 elements with E8M0 block scales (MXFP8): the block-scaled sum is
-    # the same definition as for e2m1, now over 8-bit elements
+def test_bruteforce_exact_mxfp8(trial, fa, fb):
+    # fp8 elements (E4M3, E5M2, or one of each) with E8M0 block scales (MX
+    # fp8): the block-scaled sum is the same definition as for e2m1, now over
+    # 8-bit elements, each operand decoded by its own format
     g = np.random.default_rng(300 + trial)
     m, n, k = int(g.integers(1, 6)), int(g.integers(1, 6)), 96
-    a, b = _random_values("e4m3", g, (m, k)), _random_values("e4m3", g, (k, n))
+    a, b = _random_values(fa, g, (m, k)), _random_values(fb, g, (k, n))
     sfa = g.integers(118, 136, size=(m, k // 32)).astype(np.uint8)
     sfb = g.integers(118, 136, size=(n, k // 32)).astype(np.uint8)
-    p = _problem("e4m3", a, b, "T", "N", alpha=0.75, a_scale=2.0, b_scale=0.5, sfa=sfa, ld_sfa=k // 32,
-                 sfb=sfb, ld_sfb=k // 32)
+    p = dict(m=m, n=n, k=k, a=wl.store_colmajor(wl.encode(a.T, fa), k), lda=k, op_a="T", type_a=fa,
+             b=wl.store_colmajor(wl.encode(b, fb), k), ldb=k, op_b="N", type_b=fb, alpha=0.75, a_scale=2.0,
+             b_scale=0.5, sfa=sfa, ld_sfa=k // 32, sfb=sfb, ld_sfb=k // 32)
     got = _full(p)
-    want = _exact_reference("e4m3", a, b, alpha=0.75, sfa=sfa, sfb=sfb)  # a_scale * b_scale = 1
+    want = _exact_reference(fa, a, b, alpha=0.75, sfa=sfa, sfb=sfb)  # a_scale * b_scale = 1
     for i in range(m):
         for j in range(n):
             assert abs(Fraction(got[i, j]) - want[i, j]) <= Fraction(2) ** -48 * (1 + abs(want[i, j]))

@@ -83,3 +83,17 @@ def test_bench_lists_every_configuration():
                  ("fp8", 1, 8192, 8192), ("mxfp4", 8192, 8192, 8192)):
         assert need in shapes
     assert bench.HEADLINE == "bf16_8192"
+
+
+def test_mx_e5m2_blocks_follow_the_shared_exponent_rule():
+    # E5M2's largest exponent is 15: each block's largest element lands in
+    # [2^15, 57344] after scaling, and mixed kinds give each operand its format
+    g = np.random.default_rng(6)
+    x = g.standard_normal((4, 96)) * np.exp(g.uniform(-8, 8, size=(4, 1)))
+    codes, sc = wl.mx_quantize_fp8(x, "e5m2")
+    vals = oracle.decode("e5m2", np.ascontiguousarray(codes)).reshape(4, 96)
+    blk = np.abs(vals.reshape(4, 3, 32)).max(axis=2)
+    assert ((blk >= 2.0 ** 15) & (blk <= 57344)).all()
+    for kind, ta, tb in (("mxfp8e5m2", "e5m2", "e5m2"), ("mxfp8e4e5", "e4m3", "e5m2"), ("mxfp8e5e4", "e5m2", "e4m3")):
+        w = wl.make(kind, 5, 7, 64)
+        assert (w.type_a, w.type_b) == (ta, tb) and w.sfa is not None and w.sfb is not None

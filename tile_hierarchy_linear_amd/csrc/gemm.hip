@@ -51,6 +51,13 @@ struct Variant {
       THL_V(FAM, NAME, OPS, AK, BK, 128, 128, 16, 4, 2, 2),   \
       THL_V(FAM, NAME, OPS, AK, BK, 128, 128, 4, 4, 2, 2)
 
+// The MX fp8 families (no 256x128 variant: their scale groups of eight
+// K-steps need a stage count that divides into them).
+#define THL_VMX8(FAM, NAME)                                      \
+  THL_V(FAM, NAME, "tn", true, true, 256, 256, 16, 4, 1, 0),     \
+      THL_V(FAM, NAME, "tn", true, true, 128, 128, 16, 4, 2, 2), \
+      THL_V(FAM, NAME, "tn", true, true, 128, 128, 4, 4, 2, 2)
+
 // The small-M kernel: 16 columns and 16, 32 or 64 rows of D per workgroup, K
 // split over 4 wavefronts (the first whose rows cover M is chosen).
 #define THL_VS1(FAM, NAME, MT, ROWS) \
@@ -74,9 +81,10 @@ const Variant kVariants[] = {
     THL_V(FAM_FP4, "e2m1", "tn", true, true, 256, 256, 16, 4, 1, 0),
     THL_V(FAM_FP4, "e2m1", "tn", true, true, 128, 128, 16, 4, 2, 2),
     THL_V(FAM_FP4, "e2m1", "tn", true, true, 128, 128, 4, 4, 2, 2),
-    THL_V(FAM_MX8, "mxe4m3", "tn", true, true, 256, 256, 16, 4, 1, 0),
-    THL_V(FAM_MX8, "mxe4m3", "tn", true, true, 128, 128, 16, 4, 2, 2),
-    THL_V(FAM_MX8, "mxe4m3", "tn", true, true, 128, 128, 4, 4, 2, 2),
+    THL_VMX8(FAM_MX8, "mxe4m3"),
+    THL_VMX8(FAM_MX8_E5M2, "mxe5m2"),
+    THL_VMX8(FAM_MX8_E4E5, "mxe4m3e5m2"),
+    THL_VMX8(FAM_MX8_E5E4, "mxe5m2e4m3"),
     THL_VS(FAM_BF16, "bf16"),
     THL_VS(FAM_F16, "f16"),
     THL_VS(FAM_I8, "i8"),
@@ -277,17 +285,25 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
   const int fam0 = family_of(dt->a);
   const bool f8a = dt->a == THL_E4M3 || dt->a == THL_E5M2, f8b = dt->b == THL_E4M3 || dt->b == THL_E5M2;
   const bool mixed = f8a && f8b && dt->a != dt->b;
-  const int fam = mixed ? (dt->a == THL_E4M3 ? FAM_E4E5 : FAM_E5E4)
-                        : ((fam0 == FAM_FP8 && sc && sc->sfa && sc->sfb) ? FAM_MX8 : fam0);
+  // fp8 operands with both block-scale arrays are MX fp8 (MXFP8 with E4M3 or
+  // E5M2 elements, or one of each).
+  const bool mx8 = f8a && f8b && sc && sc->sfa && sc->sfb;
+  int fam = fam0;
+  if (mx8) {
+    fam = !mixed ? (dt->a == THL_E4M3 ? FAM_MX8 : FAM_MX8_E5M2) : (dt->a == THL_E4M3 ? FAM_MX8_E4E5 : FAM_MX8_E5E4);
+  } else if (mixed) {
+    fam = dt->a == THL_E4M3 ? FAM_E4E5 : FAM_E5E4;
+  }
   if (fam < 0 || (dt->b != dt->a && !mixed)) return THL_ERR_UNSUPPORTED;
-  // Block scales come with E2M1 and E4M3 operands only; E4M3 needs both
-  // arrays or neither (one alone is neither MXFP8 nor plain fp8).
+  // Block scales come with E2M1 and fp8 operands only; fp8 operands need
+  // both arrays or neither (one alone is neither MXFP8 nor plain fp8).
   const bool any_sf = sc && (sc->sfa || sc->sfb);
-  if (any_sf && fam != FAM_FP4 && fam != FAM_MX8) {
-    if (fam0 == FAM_FP8 && !mixed) return THL_ERR_INVALID;
+  if (any_sf && fam != FAM_FP4 && fam != FAM_MX8 && fam != FAM_MX8_E5M2 && fam != FAM_MX8_E4E5 &&
+      fam != FAM_MX8_E5E4) {
+    if (f8a && f8b) return THL_ERR_INVALID;
     return THL_ERR_UNSUPPORTED;
   }
-  const bool block_scaled = fam == FAM_FP4 || fam == FAM_MX8;
+  const bool block_scaled = fam == FAM_FP4 || mx8;
   const bool int_path = fam == FAM_I8;
   if (int_path) {
     if (dt->acc != THL_I32 || dt->d != THL_I32) return THL_ERR_UNSUPPORTED;
@@ -425,7 +441,7 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
   a.tiles_m = static_cast<int32_t>((m + pick->bm - 1) / pick->bm);
   a.tiles_n = static_cast<int32_t>((n + pick->bn - 1) / pick->bn);
   a.group_m = 8;
-  const bool tensor_scaled = fam == FAM_FP8 || fam == FAM_E5M2 || fam == FAM_MX8 || fam == FAM_E4E5 || fam == FAM_E5E4;
+  const bool tensor_scaled = f8a && f8b;  // every fp8 family, block-scaled or not
   a.alpha = tensor_scaled ? alpha * s.a_scale * s.b_scale : alpha;
   a.beta = beta;
   a.flags = static_cast<int32_t>(flags);

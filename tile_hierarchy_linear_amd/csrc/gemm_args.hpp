@@ -9,10 +9,12 @@ namespace thl {
 
 // Operand families (one MFMA instruction each).
 // FAM_MX8: e4m3 elements with one E8M0 scale per 32 K-elements (MXFP8);
+// FAM_MX8_E5M2 the same with e5m2 elements, FAM_MX8_E4E5 / FAM_MX8_E5E4 with
+// e4m3 A and e5m2 B and the other way round;
 // FAM_E4E5 / FAM_E5E4: e4m3 A with e5m2 B, and the other way round.
 enum Family {
   FAM_F16 = 0, FAM_BF16 = 1, FAM_I8 = 2, FAM_FP8 = 3, FAM_FP4 = 4, FAM_E5M2 = 5, FAM_MX8 = 6,
-  FAM_E4E5 = 7, FAM_E5E4 = 8
+  FAM_E4E5 = 7, FAM_E5E4 = 8, FAM_MX8_E5M2 = 9, FAM_MX8_E4E5 = 10, FAM_MX8_E5E4 = 11
 };
 
 // Element-type codes, equal to the public thl_dtype values.

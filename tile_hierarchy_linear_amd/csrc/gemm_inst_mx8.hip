@@ -5,4 +5,4 @@
 using thl::GemmArgs;
 using thl::FAM_MX8;
 
-THL_INSTANTIATE_VARIANTS_MX8()
+THL_INSTANTIATE_VARIANTS_MX8(FAM_MX8)

@@ -107,13 +107,14 @@ struct Fam<FAM_E4E5> : Fam8<0, 1> {};
 template <>
 struct Fam<FAM_E5E4> : Fam8<1, 0> {};
 
-// MXFP8: e4m3 with one E8M0 scale per 32 K-elements.  The instruction applies
-// lane l's scale byte to K-block l/32 of row l%32, and reads lane g's 32
-// bytes as K 16g .. 16g+15 and 32+16g .. 32+16g+15 (maps::fp8_32x32_k_of):
-// so lane group g loads the step's 16-byte chunks g and g+2, and block g of
-// the step is exactly the 32 stored elements its scale belongs to.
-template <>
-struct Fam<FAM_MX8> {
+// MXFP8: fp8 elements with one E8M0 scale per 32 K-elements, format code FA
+// for A and FB for B (0 = E4M3, 1 = E5M2).  The instruction applies lane l's
+// scale byte to K-block l/32 of row l%32, and reads lane g's 32 bytes as K
+// 16g .. 16g+15 and 32+16g .. 32+16g+15 (maps::fp8_32x32_k_of): so lane
+// group g loads the step's 16-byte chunks g and g+2, and block g of the step
+// is exactly the 32 stored elements its scale belongs to.
+template <int FA, int FB>
+struct FamMX8 {
   static constexpr int LANE_CHUNKS = 2, KSUB = 1, SPS = 2;  // SPS: scale blocks per 64-byte step
   static constexpr bool INT = false, SCALED = true;
   using Acc = v16f;
@@ -121,10 +122,18 @@ struct Fam<FAM_MX8> {
   static __device__ __forceinline__ Acc mma(const v4i* a, const v4i* b, Acc c, int sa, int sb) {
     const v8i av = __builtin_shufflevector(a[0], a[1], 0, 1, 2, 3, 4, 5, 6, 7);
     const v8i bv = __builtin_shufflevector(b[0], b[1], 0, 1, 2, 3, 4, 5, 6, 7);
-    // Format 0 = E4M3 for both operands, E8M0 scales in byte 0.
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 0, 0, 0, sa, 0, sb);
+    // E8M0 scales in byte 0 of each lane's scale operand.
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, FA, FB, 0, sa, 0, sb);
   }
 };
+template <>
+struct Fam<FAM_MX8> : FamMX8<0, 0> {};
+template <>
+struct Fam<FAM_MX8_E5M2> : FamMX8<1, 1> {};
+template <>
+struct Fam<FAM_MX8_E4E5> : FamMX8<0, 1> {};
+template <>
+struct Fam<FAM_MX8_E5E4> : FamMX8<1, 0> {};
 
 template <>
 struct Fam<FAM_FP4> {

@@ -32,11 +32,11 @@ hipError_t launch_gemm(const GemmArgs& a, dim3 grid, hipStream_t stream) {
   THL_INST(FAM_FP4, 128, 128, 16, 4, 2, true, true)    \
   THL_INST(FAM_FP4, 128, 128, 4, 4, 2, true, true)
 
-// MXFP8: as fp4 (scale groups of eight K-steps).
-#define THL_INSTANTIATE_VARIANTS_MX8()              \
-  THL_INST(FAM_MX8, 256, 256, 16, 4, 1, true, true) \
-  THL_INST(FAM_MX8, 128, 128, 16, 4, 2, true, true) \
-  THL_INST(FAM_MX8, 128, 128, 4, 4, 2, true, true)
+// MX fp8 families: as fp4 (scale groups of eight K-steps).
+#define THL_INSTANTIATE_VARIANTS_MX8(FAM)       \
+  THL_INST(FAM, 256, 256, 16, 4, 1, true, true) \
+  THL_INST(FAM, 128, 128, 16, 4, 2, true, true) \
+  THL_INST(FAM, 128, 128, 4, 4, 2, true, true)
 
 #define THL_INSTANTIATE_VARIANTS(FAM, AK, BK) \
   THL_INST(FAM, 256, 256, 16, 4, 1, AK, BK)    \

@@ -85,22 +85,33 @@ def mx_quantize(x: np.ndarray, block: int = 32):
     return codes.reshape(r, k), (e + 127).astype(np.uint8)
 
 
-def mx_quantize_e4m3(x: np.ndarray, block: int = 32):
-    """OCP MX quantization of rows of ``x`` (R x K, K % block == 0) to E4M3:
-    per block the shared exponent is floor(log2(amax)) - 8 (8 is E4M3's
-    largest exponent), clamped to [-127, 127]; elements are x / 2^X rounded to
-    E4M3 (RNE; the block's largest lands below 512, so values past 448 are
-    clamped to 448 first, the format having no infinity).  Returns (codes
-    R x K uint8, scale codes R x K/block uint8)."""
+# Largest exponent and largest finite magnitude of the OCP fp8 formats.
+_FP8_EMAX = {"e4m3": (8, 448.0), "e5m2": (15, 57344.0)}
+
+
+def mx_quantize_fp8(x: np.ndarray, fmt: str = "e4m3", block: int = 32):
+    """OCP MX quantization of rows of ``x`` (R x K, K % block == 0) to an fp8
+    format: per block the shared exponent is floor(log2(amax)) - emax (emax
+    is the format's largest exponent: 8 for E4M3, 15 for E5M2), clamped to
+    [-127, 127]; elements are x / 2^X rounded to the format (RNE; the block's
+    largest lands below 2^(emax+1), so values past the largest finite
+    magnitude are clamped to it first).  Returns (codes R x K uint8, scale
+    codes R x K/block uint8)."""
+    emax, top = _FP8_EMAX[fmt]
     r, k = x.shape
     xb = x.reshape(r, k // block, block)
     amax = np.abs(xb).max(axis=2)
     with np.errstate(divide="ignore"):
-        e = np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 8
+        e = np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - emax
     e = np.clip(e, -127, 127)
     e = np.where(amax > 0, e, -127)
-    y = np.clip(xb / np.ldexp(1.0, e.astype(np.int64))[:, :, None], -448.0, 448.0)
-    return encode(y.reshape(r, k), "e4m3"), (e + 127).astype(np.uint8)
+    y = np.clip(xb / np.ldexp(1.0, e.astype(np.int64))[:, :, None], -top, top)
+    return encode(y.reshape(r, k), fmt), (e + 127).astype(np.uint8)
+
+
+def mx_quantize_e4m3(x: np.ndarray, block: int = 32):
+    """mx_quantize_fp8 with E4M3 elements."""
+    return mx_quantize_fp8(x, "e4m3", block)
 
 
 # ----------------------------------------------------------------- storage
@@ -208,6 +219,8 @@ def make(kind: str, m: int, n: int, k: int, seed: int | None = None, *, op_a=Non
            'mxfp4' e2m1 T/N, N(0,1) MX-quantized per 32 K-elements, C bf16 N(0,1),
                    bf16 out, D = A.B + C
            'mxfp8' e4m3 T/N, N(0,1) MX-quantized per 32 K-elements, bf16 out, D = A.B
+           'mxfp8e5m2' the same with e5m2 elements; 'mxfp8e4e5', 'mxfp8e5e4' e4m3 A with
+                   e5m2 B, and the other way round
     Keyword overrides change ops, leading dimensions, the epilogue and the
     float C, D and bias types for the edge-case sweeps."""
     defaults = {
@@ -220,6 +233,9 @@ def make(kind: str, m: int, n: int, k: int, seed: int | None = None, *, op_a=Non
         "fp8e5e4": dict(seed=1009, op_a="T", op_b="N", type_ab="e5m2", type_b="e4m3", type_d="bf16"),
         "mxfp4": dict(seed=1005, op_a="T", op_b="N", type_ab="e2m1", type_d="bf16"),
         "mxfp8": dict(seed=1007, op_a="T", op_b="N", type_ab="e4m3", type_d="bf16"),
+        "mxfp8e5m2": dict(seed=1010, op_a="T", op_b="N", type_ab="e5m2", type_d="bf16"),
+        "mxfp8e4e5": dict(seed=1011, op_a="T", op_b="N", type_ab="e4m3", type_b="e5m2", type_d="bf16"),
+        "mxfp8e5e4": dict(seed=1012, op_a="T", op_b="N", type_ab="e5m2", type_b="e4m3", type_d="bf16"),
     }[kind]
     seed = defaults["seed"] if seed is None else seed
     op_a = op_a or defaults["op_a"]
@@ -317,12 +333,12 @@ def make(kind: str, m: int, n: int, k: int, seed: int | None = None, *, op_a=Non
         if bias:
             tb = type_bias or "bf16"
             w["bias"], w["type_bias"] = encode(gbias.standard_normal(m), tb), tb
-    elif kind == "mxfp8":
+    elif kind in ("mxfp8", "mxfp8e5m2", "mxfp8e4e5", "mxfp8e5e4"):
         assert op_a == "T" and op_b == "N", "MX blocks run along the contiguous K"
         assert k % 32 == 0
         xa, xb = ga.standard_normal((m, k)), gb.standard_normal((n, k))  # B drawn as its stored N x K
-        ca, w["sfa"] = mx_quantize_e4m3(xa) if k else (np.zeros((m, 0), np.uint8), np.zeros((m, 0), np.uint8))
-        cb, w["sfb"] = mx_quantize_e4m3(xb) if k else (np.zeros((n, 0), np.uint8), np.zeros((n, 0), np.uint8))
+        ca, w["sfa"] = mx_quantize_fp8(xa, fmt) if k else (np.zeros((m, 0), np.uint8), np.zeros((m, 0), np.uint8))
+        cb, w["sfb"] = mx_quantize_fp8(xb, fmt_b) if k else (np.zeros((n, 0), np.uint8), np.zeros((n, 0), np.uint8))
         ld_sf = max(16, (k // 32 + 15) // 16 * 16)
         w["ld_sfa"] = w["ld_sfb"] = ld_sf
         pad_a = np.full((m, ld_sf), 127, np.uint8)
