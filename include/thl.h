@@ -107,9 +107,10 @@ typedef struct {
  *     b_scale folded with alpha into one fp32 factor.
  *   E5M2 operands (both), opA = T, opB = N: as E4M3.
  *   E4M3 A with E5M2 B, or E5M2 A with E4M3 B, opA = T, opB = N: as E4M3.
- *   E4M3 operands with both scales->sfa and scales->sfb given (MXFP8), opA = T,
- *     opB = N, k % 32 == 0: as E2M1X2's block scales (on top of the per-tensor
- *     scales), with the same scale-row rules.
+ *   fp8 operands (E4M3, E5M2, or one of each) with scales->sfa and
+ *     scales->sfb given (MX fp8), opA = T, opB = N, k % 32 == 0: as E2M1X2's
+ *     block scales (on top of the per-tensor scales), with the same scale-row
+ *     rules.
  *   E2M1X2 operands, opA = T, opB = N, k % 32 == 0: F32 accumulate, element
  *     (i,p) of A multiplied by 2^(SFA(i, p/32) - 127), likewise B with SFB(j, p/32);
  *     scale rows 16-byte aligned (THL_ERR_MISALIGNED otherwise).
@@ -125,9 +126,10 @@ typedef struct {
  * caller; the library allocates nothing and keeps no pointer after return.
  * alpha, beta and the per-tensor scales are host values.
  *
- * Block scales: sfa or sfb given with operands other than E2M1X2 and E4M3
- * (F16, BF16, I8, E5M2, mixed fp8) is THL_ERR_UNSUPPORTED; E4M3 with only
- * one of the two is THL_ERR_INVALID; E2M1X2 without both is THL_ERR_INVALID.
+ * Block scales: sfa or sfb given with F16, BF16 or I8 operands is
+ * THL_ERR_UNSUPPORTED.  fp8 operands with either array given are MX fp8;
+ * E2M1X2 always is.  Both arrays are then required (THL_ERR_INVALID
+ * otherwise) whenever m > 0, n > 0 and k > 0.
  *
  * Semantics: beta == 0 means C is not read (it may be NULL and may hold NaN).
  * D may alias C exactly (same pointer, ldc == ldd, c and d the same format);
@@ -180,6 +182,59 @@ thl_status thl_gemm_batched(int64_t batch, int64_t m, int64_t n, int64_t k,
                             float alpha, float beta,
                             const thl_dtypes* dtypes, const thl_epilogue* epilogue, int64_t stride_bias,
                             const thl_scales* scales, int64_t stride_sfa, int64_t stride_sfb,
+                            struct ihipStream_t* stream);
+
+/*
+ * thl_gemm_grouped -- `count` independent problems of different shapes in one
+ * launch (the grouped GEMM of "What's New in CUTLASS 4.8", "CUTLASS Operator
+ * API": per-problem sizes, pointers and leading dimensions, as its
+ * IndexPtrGroupedGemmArguments carry them):
+ *   D_z = act(alpha*s_a*s_b*op(A_z)*op(B_z) + beta*C_z + bias_z),  z = 0 .. count-1,
+ * with problem z's m, n, k, arrays and leading dimensions in problems[z].
+ * Formats, opA/opB, alpha, beta, the activation flags and the per-tensor
+ * scales are one set for the whole group; epilogue->bias is ignored (each
+ * problem brings its bias in problems[z].bias, read when THL_EPI_BIAS is
+ * set).  Every problem follows the rules of thl_gemm (leading dimensions,
+ * alignment, block scales, C == D aliasing), and in addition no problem's D
+ * may overlap another problem's D or any array another problem reads.  The
+ * problems with outputs (m > 0 and n > 0) must resolve to one operand
+ * family: block scales on all of them or on none (THL_ERR_INVALID
+ * otherwise); every problem's operands must suit one kernel variant.
+ *
+ *   problems      host array of `count` descriptors: validated here, and
+ *                 used to choose the kernel and the grid.
+ *   problems_dev  device array holding the same `count` descriptors (the
+ *                 kernel reads each problem's sizes and pointers from it);
+ *                 the caller keeps it unchanged until the launch completes.
+ *
+ * One kernel variant (the tiled kernels; the small-M kernel is not used)
+ * runs every problem; grid row z computes problem z with its share of
+ * persistent workgroups.  count == 0, or every problem with m == 0 or
+ * n == 0, returns THL_OK with no launch; count above 65535 returns
+ * THL_ERR_UNSUPPORTED; a NULL problems_dev with work to do is
+ * THL_ERR_INVALID.  Errors as for thl_gemm (nothing is enqueued).
+ */
+typedef struct {
+  int64_t m, n, k;
+  const void* A;
+  int64_t lda;
+  const void* B;
+  int64_t ldb;
+  const void* C; /* read when beta != 0 */
+  int64_t ldc;
+  void* D;
+  int64_t ldd;
+  const void* bias; /* length m, read when THL_EPI_BIAS is set */
+  const uint8_t* sfa; /* E8M0 block scales (E2M1X2, MX fp8), as for thl_gemm */
+  int64_t ld_sfa;
+  const uint8_t* sfb;
+  int64_t ld_sfb;
+} thl_group_problem;
+
+thl_status thl_gemm_grouped(int64_t count, const thl_group_problem* problems,
+                            const thl_group_problem* problems_dev, thl_op opA, thl_op opB,
+                            float alpha, float beta, const thl_dtypes* dtypes,
+                            const thl_epilogue* epilogue, const thl_scales* scales,
                             struct ihipStream_t* stream);
 
 /* Static text for a status code. */

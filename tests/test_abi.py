@@ -132,8 +132,8 @@ def test_block_scales_with_formats_that_take_none_are_refused(fmt, td):
                                              ("e4m3", "e5m2", "mxe4m3e5m2_", "e4m3e5m2_"),
                                              ("e5m2", "e4m3", "mxe5m2e4m3_", "e5m2e4m3_")])
 def test_fp8_block_scales_both_or_neither(fa, fb, mx, plain):
-    # fp8 operands with both arrays are MX fp8 (one scale per 32 K-elements),
-    # with neither plain fp8; one alone is an error.
+    # fp8 operands with scale arrays are MX fp8 (one scale per 32 K-elements),
+    # with neither plain fp8; one alone is an error when there is work to do.
     dts = thl.make_dtypes(fa, fb, "f32", "bf16")
 
     def go(sc, m=64):
@@ -141,7 +141,9 @@ def test_fp8_block_scales_both_or_neither(fa, fb, mx, plain):
 
     for sc in (thl.thl_scales(1.0, 1.0, SFA, 16, None, 0), thl.thl_scales(1.0, 1.0, None, 0, SFB, 16)):
         assert go(sc) == thl.THL_ERR_INVALID
-        assert go(sc, m=0) == thl.THL_ERR_INVALID
+        # with no outputs nothing is read: one array (for the non-empty operand) is enough
+        assert go(sc, m=0) == thl.THL_OK
+        assert thl.thl_last_variant().startswith(mx)
     assert go(thl.thl_scales(1.0, 1.0, SFA, 16, SFB, 16), m=0) == thl.THL_OK
     assert thl.thl_last_variant().startswith(mx)
     assert go(None, m=0) == thl.THL_OK
@@ -272,3 +274,58 @@ def test_batched_validation():
     # problem's A would start 2 bytes off)
     assert bcall(sa=64 * 64 + 1) == thl.THL_ERR_MISALIGNED
     assert bcall(n=0, sa=64 * 64 + 1) == thl.THL_ERR_MISALIGNED  # selection runs before the quick return
+
+
+# ------------------------------------------------------------ grouped problems
+
+def _gp(m=64, n=64, k=64, a=A, lda=None, b=B, ldb=None, c=None, ldc=None, d=D, ldd=None, bias=None, sfa=None,
+        ld_sfa=0, sfb=None, ld_sfb=0):
+    return thl.thl_group_problem(m, n, k, a, lda if lda is not None else max(1, k), b,
+                                 ldb if ldb is not None else max(1, k), c, ldc if ldc is not None else max(1, m), d,
+                                 ldd if ldd is not None else max(1, m), bias, sfa, ld_sfa, sfb, ld_sfb)
+
+
+def gcall(problems, dev=0x70000000, opa="T", opb="N", alpha=1.0, beta=0.0, types=("bf16", "f32", "f32", "none"),
+          flags=0, sc=None):
+    ta, tc, td, tb = types
+    arr = (thl.thl_group_problem * max(1, len(problems)))(*problems)
+    dts = thl.make_dtypes(ta, ta, tc, td, tb)
+    return thl.thl_gemm_grouped(len(problems), arr, dev, opa, opb, alpha, beta, dts, thl.thl_epilogue(flags, None),
+                                sc, None)
+
+
+def test_grouped_validation():
+    assert gcall([]) == thl.THL_OK
+    dts = thl.make_dtypes("bf16", "bf16", "f32", "f32")
+    assert thl.thl_gemm_grouped(-1, None, None, "T", "N", 1.0, 0.0, dts, None, None, None) == thl.THL_ERR_INVALID
+    assert thl.thl_gemm_grouped(2, None, None, "T", "N", 1.0, 0.0, dts, None, None, None) == thl.THL_ERR_INVALID
+    assert thl.thl_gemm_grouped(70000, None, None, "T", "N", 1.0, 0.0, dts, None, None, None) == \
+        thl.THL_ERR_UNSUPPORTED
+    # one bad problem fails the group
+    assert gcall([_gp(), _gp(lda=10, d=D + 0x100000)]) == thl.THL_ERR_INVALID
+    # no launch when no problem has outputs; the variant is still chosen
+    assert gcall([_gp(m=0), _gp(n=0, d=D + 0x100000)]) == thl.THL_OK
+    assert thl.thl_last_variant().startswith("bf16_tn_")
+    # work to do needs the device copy of the descriptors
+    assert gcall([_gp()], dev=None) == thl.THL_ERR_INVALID
+    # accepted (the launch itself needs a GPU)
+    assert gcall([_gp(), _gp(m=100, n=37, d=D + 0x100000)]) in (thl.THL_OK, thl.THL_ERR_HIP)
+
+
+def test_grouped_outputs_may_not_overlap_across_problems():
+    # D of problem 1 inside D of problem 0
+    assert gcall([_gp(), _gp(d=D + 64)]) == thl.THL_ERR_INVALID
+    # D of problem 1 over A of problem 0
+    assert gcall([_gp(), _gp(d=A)]) == thl.THL_ERR_INVALID
+    # D of problem 0 over problem 1's C (beta != 0)
+    assert gcall([_gp(c=C), _gp(c=D, d=D + 0x100000)], beta=1.0) == thl.THL_ERR_INVALID
+    # each problem may read its own C in place (C == D), and problems may share inputs
+    assert gcall([_gp(c=D), _gp(c=D + 0x100000, d=D + 0x100000)], beta=1.0) in (thl.THL_OK, thl.THL_ERR_HIP)
+
+
+def test_grouped_needs_one_family():
+    # fp8 problems with block scales and without them would be two families
+    sc = [_gp(sfa=SFA, ld_sfa=16, sfb=SFB, ld_sfb=16), _gp(d=D + 0x100000)]
+    assert gcall(sc, types=("e4m3", "f32", "bf16", "none")) == thl.THL_ERR_INVALID
+    assert gcall([sc[0], _gp(d=D + 0x100000, sfa=SFA, ld_sfa=16, sfb=SFB + 0x10000, ld_sfb=16)],
+                 types=("e4m3", "f32", "bf16", "none")) in (thl.THL_OK, thl.THL_ERR_HIP)

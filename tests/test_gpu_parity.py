@@ -765,3 +765,72 @@ def test_mxfp4_largest_codes_under_spread_scales(type_d):
     a, sfa = operand(m)
     b, sfb = operand(n)
     _check_full(_codes_workload("e2m1-spread", "e2m1", a, b, type_d=type_d, sfa=sfa, sfb=sfb))
+
+
+# ------------------------------------------------------------ grouped problems
+
+def _check_grouped(ws, expect=None):
+    from oracle import compare
+    from workloads.device import GroupedDeviceProblem
+
+    import tile_hierarchy_linear_amd as thl
+
+    shapes = [(w.m, w.n, w.k) for w in ws]
+    _say(f"[grouped] {ws[0].name} count={len(ws)} shapes={shapes}")
+    gp = GroupedDeviceProblem(ws)
+    st = gp.run()
+    assert st == 0, f"thl_gemm_grouped status {st}"
+    torch.cuda.synchronize()
+    if expect:
+        assert thl.thl_last_variant().startswith(expect)
+    for z, w in enumerate(ws):
+        if w.m == 0 or w.n == 0:
+            continue
+        got = gp.d_all(z)
+        ii, jj = np.meshgrid(np.arange(w.m), np.arange(w.n), indexing="ij")
+        res = compare.parity_check(w, got.ravel(), ii.ravel(), jj.ravel())
+        assert res["ok"], (z, shapes[z], res)
+    # outputs of empty problems are not touched
+    for z, w in enumerate(ws):
+        if (w.m == 0 or w.n == 0) and w.type_d != "i32":
+            assert torch.isnan(gp.probs[z].d.float()).all()
+
+
+GROUPED_SHAPES = [(300, 200, 136), (64, 520, 256), (1000, 33, 64), (1, 1, 32), (0, 10, 64), (257, 129, 0),
+                  (129, 640, 512)]
+
+
+@pytest.mark.parametrize("kind,kw", [("bf16", {}), ("bf16", {"op_a": "T", "op_b": "T", "act": "gelu"}),
+                                     ("fp16", {}), ("int8", {"beta": 1.0, "bias": True, "act": "relu"}),
+                                     ("fp8", {}), ("fp8e5m2", {"beta": 1.0}), ("mxfp4", {}), ("mxfp8", {})])
+def test_grouped(kind, kw):
+    # problems of different shapes (ragged, single element, empty, k = 0) in one launch
+    import workloads as wl
+
+    shapes = GROUPED_SHAPES
+    if kind in ("mxfp4", "mxfp8"):
+        shapes = [(m, n, (k + 31) // 32 * 32) for m, n, k in shapes]
+    pad = 32 if kind == "mxfp4" else 16
+    ws = []
+    for z, (m, n, k) in enumerate(shapes):
+        extra = dict(kw)
+        if kind in ("fp16", "bf16") and extra.get("op_a", "N" if kind == "bf16" else "T") == "N":
+            extra["lda"] = _pad(max(1, m), 8)
+        elif kind in ("fp16", "bf16"):
+            extra["lda"] = _pad(max(1, k), 8)
+        if kind in ("fp16", "bf16") and extra.get("op_b", "N") == "T":
+            extra["ldb"] = _pad(max(1, n), 8)
+        elif kind in ("fp16", "bf16"):
+            extra["ldb"] = _pad(max(1, k), 8)
+        else:
+            extra["lda"] = extra["ldb"] = _pad(max(1, k), pad)
+        ws.append(wl.make(kind, m, n, k, seed=4000 + 10 * z, **extra))
+    _check_grouped(ws)
+
+
+def test_grouped_many_tiles_per_problem():
+    # 6 problems of 1000 .. 2304 rows, each with many tiles per workgroup
+    import workloads as wl
+
+    ws = [wl.make("bf16", 1000 + 256 * z, 2304 - 256 * z, 512, seed=4100 + z) for z in range(6)]
+    _check_grouped(ws, expect="bf16_nn_")

@@ -41,6 +41,14 @@ class thl_scales(ctypes.Structure):
                 ("ld_sfa", ctypes.c_int64), ("sfb", ctypes.c_void_p), ("ld_sfb", ctypes.c_int64)]
 
 
+class thl_group_problem(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_int64), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("A", ctypes.c_void_p), ("lda", ctypes.c_int64), ("B", ctypes.c_void_p), ("ldb", ctypes.c_int64),
+                ("C", ctypes.c_void_p), ("ldc", ctypes.c_int64), ("D", ctypes.c_void_p), ("ldd", ctypes.c_int64),
+                ("bias", ctypes.c_void_p), ("sfa", ctypes.c_void_p), ("ld_sfa", ctypes.c_int64),
+                ("sfb", ctypes.c_void_p), ("ld_sfb", ctypes.c_int64)]
+
+
 def _load():
     # One HIP runtime per process.  torch ships its own libamdhip64 and asks
     # for it by its unversioned name, so loading libthl first (which pulls in
@@ -66,6 +74,10 @@ def _load():
                                      ctypes.POINTER(thl_dtypes), ctypes.POINTER(thl_epilogue), i64,
                                      ctypes.POINTER(thl_scales), i64, i64, vp]
     lib.thl_gemm_batched.restype = ctypes.c_int
+    lib.thl_gemm_grouped.argtypes = [i64, ctypes.POINTER(thl_group_problem), vp, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_float, ctypes.c_float, ctypes.POINTER(thl_dtypes),
+                                     ctypes.POINTER(thl_epilogue), ctypes.POINTER(thl_scales), vp]
+    lib.thl_gemm_grouped.restype = ctypes.c_int
     lib.thl_status_string.argtypes = [ctypes.c_int]
     lib.thl_status_string.restype = cp
     lib.thl_last_variant.restype = cp
@@ -161,6 +173,18 @@ def thl_gemm_batched(batch, m, n, k, A, lda, stride_a, opA, B, ldb, stride_b, op
                                      ctypes.byref(epilogue) if epilogue is not None else None, int(stride_bias),
                                      ctypes.byref(scales) if scales is not None else None, int(stride_sfa),
                                      int(stride_sfb), stream))
+
+
+def thl_gemm_grouped(count, problems, problems_dev, opA, opB, alpha, beta, dtypes, epilogue=None, scales=None,
+                     stream=None) -> int:
+    """Direct call of the grouped C entry point: `problems` is a ctypes array
+    of thl_group_problem (host), `problems_dev` the device address of a copy
+    of the same bytes."""
+    opa = THL_OP_T if opA in ("T", THL_OP_T) else THL_OP_N
+    opb = THL_OP_T if opB in ("T", THL_OP_T) else THL_OP_N
+    return int(_lib.thl_gemm_grouped(int(count), problems, problems_dev, opa, opb, float(alpha), float(beta),
+                                     ctypes.byref(dtypes), ctypes.byref(epilogue) if epilogue is not None else None,
+                                     ctypes.byref(scales) if scales is not None else None, stream))
 
 
 def gemm(A, B, D, *, m, n, k, lda, ldb, ldd, op_a="T", op_b="N", C=None, ldc=0, alpha=1.0, beta=0.0,

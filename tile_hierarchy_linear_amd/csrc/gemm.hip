@@ -13,17 +13,24 @@
 // 128x128.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
+#include <cstddef>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
 #include <type_traits>
+#include <vector>
 
 #include "../../include/thl.h"
 #include "gemm_args.hpp"
 #include "index_maps.hpp"
 
 namespace thl {
+
+static_assert(sizeof(GroupProblem) == sizeof(thl_group_problem), "device descriptors are the public ones");
+static_assert(offsetof(GroupProblem, ld_sfb) == offsetof(thl_group_problem, ld_sfb), "same layout");
+
 namespace {
 
 using LaunchFn = hipError_t (*)(const GemmArgs&, dim3, hipStream_t);
@@ -192,6 +199,9 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
                      const void* B, int64_t ldb, thl_op opB, const void* C, int64_t ldc, void* D, int64_t ldd,
                      float alpha, float beta, const thl_dtypes* dt, const thl_epilogue* epi, const thl_scales* sc,
                      struct ihipStream_t* stream);
+thl_status grouped_impl(int64_t count, const thl_group_problem* pb, const thl_group_problem* pb_dev, thl_op opA,
+                        thl_op opB, float alpha, float beta, const thl_dtypes* dt, const thl_epilogue* epi,
+                        const thl_scales* sc, struct ihipStream_t* stream);
 
 }  // namespace
 }  // namespace thl
@@ -250,15 +260,35 @@ thl_status thl_gemm_batched(int64_t batch, int64_t m, int64_t n, int64_t k, cons
   return gemm_impl(bt, m, n, k, A, lda, opA, B, ldb, opB, C, ldc, D, ldd, alpha, beta, dt, epi, sc, stream);
 }
 
+thl_status thl_gemm_grouped(int64_t count, const thl_group_problem* problems, const thl_group_problem* problems_dev,
+                            thl_op opA, thl_op opB, float alpha, float beta, const thl_dtypes* dtypes,
+                            const thl_epilogue* epilogue, const thl_scales* scales, struct ihipStream_t* stream) {
+  return grouped_impl(count, problems, problems_dev, opA, opB, alpha, beta, dtypes, epilogue, scales, stream);
+}
+
 }  // extern "C"
 
 namespace thl {
 namespace {
 
-thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const void* A, int64_t lda, thl_op opA,
-                     const void* B, int64_t ldb, thl_op opB, const void* C, int64_t ldc, void* D, int64_t ldd,
-                     float alpha, float beta, const thl_dtypes* dt, const thl_epilogue* epi, const thl_scales* sc,
-                     struct ihipStream_t* stream) {
+// Everything the validation of one problem establishes: its family, flags,
+// byte leading dimensions and scales, and the conditions the variant choice
+// and the kernel arguments depend on.
+struct Prep {
+  int fam = -1;
+  bool a_kmajor = false, b_kmajor = false, block_scaled = false, int_path = false, has_bias = false;
+  bool small_m = false, work = false, vec = false;
+  unsigned flags = 0;
+  int64_t lda_bytes = 0, ldb_bytes = 0, sa_bytes = 0, sb_bytes = 0;
+  thl_scales s{1.0f, 1.0f, nullptr, 0, nullptr, 0};
+};
+
+// Validate one problem (all of thl_gemm's rules, for `bt.count` problems at
+// the batch strides); nothing touches the device.
+thl_status prepare(const Batch& bt, int64_t m, int64_t n, int64_t k, const void* A, int64_t lda, thl_op opA,
+                   const void* B, int64_t ldb, thl_op opB, const void* C, int64_t ldc, void* D, int64_t ldd,
+                   float alpha, float beta, const thl_dtypes* dt, unsigned flags, const void* bias,
+                   const thl_scales* sc, Prep* out) {
   // ---- arguments
   if (!dt || m < 0 || n < 0 || k < 0) return THL_ERR_INVALID;
   if (bt.count < 0 || bt.a < 0 || bt.b < 0 || bt.c < 0 || bt.d < 0 || bt.bias < 0 || bt.sfa < 0 || bt.sfb < 0)
@@ -273,21 +303,20 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
     return THL_ERR_UNSUPPORTED;
   if ((opA != THL_OP_N && opA != THL_OP_T) || (opB != THL_OP_N && opB != THL_OP_T)) return THL_ERR_INVALID;
   if (m > INT32_MAX || n > INT32_MAX || k > INT32_MAX) return THL_ERR_UNSUPPORTED;
-  const unsigned flags = epi ? epi->flags : 0u;
   if (flags & ~static_cast<unsigned>(THL_EPI_BIAS | THL_EPI_RELU | THL_EPI_GELU)) return THL_ERR_INVALID;
   if ((flags & THL_EPI_RELU) && (flags & THL_EPI_GELU)) return THL_ERR_INVALID;
   const bool has_bias = (flags & THL_EPI_BIAS) != 0;
 
   // ---- supported combinations
-  // E4M3 operands with both block-scale arrays given are MXFP8: one E8M0
-  // scale per 32 K-elements, as for E2M1.
   // One fp8 format for A and the other for B is the mixed family of that order.
   const int fam0 = family_of(dt->a);
   const bool f8a = dt->a == THL_E4M3 || dt->a == THL_E5M2, f8b = dt->b == THL_E4M3 || dt->b == THL_E5M2;
   const bool mixed = f8a && f8b && dt->a != dt->b;
-  // fp8 operands with both block-scale arrays are MX fp8 (MXFP8 with E4M3 or
-  // E5M2 elements, or one of each).
-  const bool mx8 = f8a && f8b && sc && sc->sfa && sc->sfb;
+  // fp8 operands with block-scale arrays are MX fp8 (MXFP8 with E4M3 or E5M2
+  // elements, or one of each); both arrays are then required once the
+  // problem has outputs and k > 0 (an empty operand may come without one).
+  const bool any_sf = sc && (sc->sfa || sc->sfb);
+  const bool mx8 = f8a && f8b && any_sf;
   int fam = fam0;
   if (mx8) {
     fam = !mixed ? (dt->a == THL_E4M3 ? FAM_MX8 : FAM_MX8_E5M2) : (dt->a == THL_E4M3 ? FAM_MX8_E4E5 : FAM_MX8_E5E4);
@@ -295,14 +324,8 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
     fam = dt->a == THL_E4M3 ? FAM_E4E5 : FAM_E5E4;
   }
   if (fam < 0 || (dt->b != dt->a && !mixed)) return THL_ERR_UNSUPPORTED;
-  // Block scales come with E2M1 and fp8 operands only; fp8 operands need
-  // both arrays or neither (one alone is neither MXFP8 nor plain fp8).
-  const bool any_sf = sc && (sc->sfa || sc->sfb);
-  if (any_sf && fam != FAM_FP4 && fam != FAM_MX8 && fam != FAM_MX8_E5M2 && fam != FAM_MX8_E4E5 &&
-      fam != FAM_MX8_E5E4) {
-    if (f8a && f8b) return THL_ERR_INVALID;
-    return THL_ERR_UNSUPPORTED;
-  }
+  // Block scales come with E2M1 and fp8 operands only.
+  if (any_sf && fam != FAM_FP4 && !mx8) return THL_ERR_UNSUPPORTED;
   const bool block_scaled = fam == FAM_FP4 || mx8;
   const bool int_path = fam == FAM_I8;
   if (int_path) {
@@ -336,7 +359,7 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
   if (work && !D) return THL_ERR_INVALID;
   if (work && k > 0 && (!A || !B)) return THL_ERR_INVALID;
   if (work && beta != 0.0f && !C) return THL_ERR_INVALID;
-  if (work && has_bias && !epi->bias) return THL_ERR_INVALID;
+  if (work && has_bias && !bias) return THL_ERR_INVALID;
   const thl_scales unit_scales = {1.0f, 1.0f, nullptr, 0, nullptr, 0};
   const thl_scales& s = sc ? *sc : unit_scales;
   if (block_scaled && work && k > 0) {
@@ -356,7 +379,7 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
       const bool exact_alias = (C == D) && (ldc == ldd) && (dt->c == dt->d) && (L == 1 || bt.c == bt.d);
       if (!exact_alias && overlaps(rd, batch_range(C, dt->c, m, n, ldc, L, bt.c))) return THL_ERR_INVALID;
     }
-    if (has_bias && overlaps(rd, batch_range(epi->bias, dt->bias, m, 1, m, L, bt.bias))) return THL_ERR_INVALID;
+    if (has_bias && overlaps(rd, batch_range(bias, dt->bias, m, 1, m, L, bt.bias))) return THL_ERR_INVALID;
     if (block_scaled && k > 0) {
       if (overlaps(rd, batch_range(s.sfa, THL_E8M0, k / 32, m, s.ld_sfa, L, bt.sfa))) return THL_ERR_INVALID;
       if (overlaps(rd, batch_range(s.sfb, THL_E8M0, k / 32, n, s.ld_sfb, L, bt.sfb))) return THL_ERR_INVALID;
@@ -369,107 +392,173 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
   if (block_scaled && k > 0 && (m * s.ld_sfa > (INT64_C(1) << 31) || n * s.ld_sfb > (INT64_C(1) << 31)))
     return THL_ERR_UNSUPPORTED;
 
-  // ---- variant: first fit on family, alignment and shape
-  const int64_t lda_bytes = bytes_of(dt->a, lda), ldb_bytes = bytes_of(dt->b, ldb);
-  const char* forced = std::getenv("THL_FORCE_VARIANT");
-  // (tile counts over the whole batch: its problems fill the device together)
-  const int64_t tiles_256 = ((m + 255) / 256) * ((n + 255) / 256) * bt.count;
-  const int64_t tiles_256x128 = ((m + 255) / 256) * ((n + 127) / 128) * bt.count;
-  const int want_tier = tiles_256 >= 256 ? 0 : (tiles_256x128 >= 256 ? 1 : 2);
-  const Variant* pick = nullptr;
-  bool family_built = false;
+  Prep& o = *out;
+  o.fam = fam;
+  o.a_kmajor = a_kmajor;
+  o.b_kmajor = b_kmajor;
+  o.block_scaled = block_scaled;
+  o.int_path = int_path;
+  o.has_bias = has_bias;
+  o.small_m = m <= 64 && k > 0;
+  o.work = work;
+  o.flags = flags;
+  o.lda_bytes = bytes_of(dt->a, lda);
+  o.ldb_bytes = bytes_of(dt->b, ldb);
   // Batched: every problem's base keeps the alignment of the first.
-  const int64_t sa_bytes = bt.count > 1 ? bytes_of(dt->a, bt.a) : 0;
-  const int64_t sb_bytes = bt.count > 1 ? bytes_of(dt->b, bt.b) : 0;
-  auto fits = [&](const Variant& v) {
-    bool ok = k == 0 || (aligned(A, lda_bytes, v.loadw) && aligned(B, ldb_bytes, v.loadw) &&
-                         sa_bytes % v.loadw == 0 && sb_bytes % v.loadw == 0);
-    if (block_scaled && k > 0)
-      ok = ok && aligned(s.sfa, s.ld_sfa, 16) && aligned(s.sfb, s.ld_sfb, 16) &&
-           (bt.count == 1 || (bt.sfa % 16 == 0 && bt.sfb % 16 == 0));
-    return ok;
-  };
-  // The small-M kernel streams B once for at most 64 rows of A (K > 0); its
-  // variants are listed by rows, and the first whose rows cover M is taken.
-  const bool small_m = m <= 64 && k > 0;
-  // Passes: the small-M kernel where it applies, then the preferred tier,
-  // then each smaller tile, then any tiled variant that fits.
-  for (int pass = small_m ? -1 : want_tier; pass <= 3 && !pick; pass = pass < 0 ? want_tier : pass + 1) {
-    for (const Variant& v : kVariants) {
-      if (v.family != fam || v.a_kmajor != a_kmajor || v.b_kmajor != b_kmajor) continue;
-      family_built = true;
-      if (forced && *forced) {
-        if (std::strcmp(forced, v.name) != 0 || (v.tier < 0 && (!small_m || v.bm < m))) continue;
-      } else if ((pass < 3 && v.tier != pass) || (pass == 3 && v.tier < 0) || (v.tier < 0 && v.bm < m)) {
-        continue;
-      }
-      if (fits(v)) {
-        pick = &v;
-        break;
-      }
-    }
-    if (forced && *forced) break;
-  }
-  if (!pick) {
-    if (forced && *forced) return THL_ERR_UNSUPPORTED;
-    return family_built ? THL_ERR_MISALIGNED : THL_ERR_UNSUPPORTED;
-  }
-  if (!work) {
-    t_last_variant = pick->name;
-    return THL_OK;
-  }
-
-  // ---- launch
-  GemmArgs a{};
-  a.a = static_cast<const uint8_t*>(A);
-  a.b = static_cast<const uint8_t*>(B);
-  a.c = C;
-  a.d = D;
-  a.bias = has_bias ? epi->bias : nullptr;
-  a.sfa = s.sfa;
-  a.sfb = s.sfb;
-  a.lda_bytes = lda_bytes;
-  a.ldb_bytes = ldb_bytes;
-  a.ldc = ldc;
-  a.ldd = ldd;
-  a.ld_sfa = s.ld_sfa;
-  a.ld_sfb = s.ld_sfb;
-  a.m = static_cast<int32_t>(m);
-  a.n = static_cast<int32_t>(n);
-  a.k = static_cast<int32_t>(k);
-  a.kbytes = static_cast<int32_t>(bytes_of(dt->a, k));
-  a.tiles_m = static_cast<int32_t>((m + pick->bm - 1) / pick->bm);
-  a.tiles_n = static_cast<int32_t>((n + pick->bn - 1) / pick->bn);
-  a.group_m = 8;
-  const bool tensor_scaled = f8a && f8b;  // every fp8 family, block-scaled or not
-  a.alpha = tensor_scaled ? alpha * s.a_scale * s.b_scale : alpha;
-  a.beta = beta;
-  a.flags = static_cast<int32_t>(flags);
+  o.sa_bytes = bt.count > 1 ? bytes_of(dt->a, bt.a) : 0;
+  o.sb_bytes = bt.count > 1 ? bytes_of(dt->b, bt.b) : 0;
+  o.s = s;
   // Vector epilogue: D (and C, bias) rows aligned for 16-byte runs along M,
   // C 16-bit, and a 256-column panel within 32-bit offsets.
+  o.vec = false;
   if (!int_path) {
     auto vec_ok = [](const void* ptr, int64_t ld_bytes) {
       return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0 && ld_bytes % 16 == 0 && ld_bytes <= (INT64_C(1) << 23);
     };
     bool vec = vec_ok(D, bytes_of(dt->d, ldd));
     if (beta != 0.0f) vec = vec && (dt->c == THL_F16 || dt->c == THL_BF16) && vec_ok(C, bytes_of(dt->c, ldc));
-    if (has_bias) vec = vec && (reinterpret_cast<uintptr_t>(epi->bias) & 15) == 0;
-    if (vec) a.flags |= EPI_VEC;
+    if (has_bias) vec = vec && (reinterpret_cast<uintptr_t>(bias) & 15) == 0;
+    if (bt.count > 1) {
+      const int64_t bs_c = beta != 0.0f ? bytes_of(dt->c, bt.c) : 0, bs_d = bytes_of(dt->d, bt.d);
+      const int64_t bs_bias = has_bias ? bytes_of(dt->bias, bt.bias) : 0;
+      if ((bs_c % 16) || (bs_d % 16) || (bs_bias % 16)) vec = false;
+    }
+    o.vec = vec;
   }
-  // Batch strides in bytes (zero for a single problem and for absent arrays).
-  if (bt.count > 1) {
-    a.bs_a = sa_bytes;
-    a.bs_b = sb_bytes;
-    a.bs_c = beta != 0.0f ? bytes_of(dt->c, bt.c) : 0;
-    a.bs_d = bytes_of(dt->d, bt.d);
-    a.bs_bias = has_bias ? bytes_of(dt->bias, bt.bias) : 0;
-    a.bs_sfa = block_scaled ? bt.sfa : 0;
-    a.bs_sfb = block_scaled ? bt.sfb : 0;
-    if ((a.bs_c % 16) || (a.bs_d % 16) || (a.bs_bias % 16)) a.flags &= ~EPI_VEC;
+  return THL_OK;
+}
+
+// Does variant v take this problem's operands (alignment class, scale rows)?
+bool fits(const Variant& v, const Prep& pr, const Batch& bt, const void* A, const void* B, int64_t k) {
+  bool ok = k == 0 || (aligned(A, pr.lda_bytes, v.loadw) && aligned(B, pr.ldb_bytes, v.loadw) &&
+                       pr.sa_bytes % v.loadw == 0 && pr.sb_bytes % v.loadw == 0);
+  if (pr.block_scaled && k > 0)
+    ok = ok && aligned(pr.s.sfa, pr.s.ld_sfa, 16) && aligned(pr.s.sfb, pr.s.ld_sfb, 16) &&
+         (bt.count == 1 || (bt.sfa % 16 == 0 && bt.sfb % 16 == 0));
+  return ok;
+}
+
+// The tile tier the shape rule prefers for this many tiles of each size.
+int want_tier_of(int64_t tiles_256, int64_t tiles_256x128) {
+  return tiles_256 >= 256 ? 0 : (tiles_256x128 >= 256 ? 1 : 2);
+}
+
+// First fit over the built variants of the problem's family, in the order
+// of the shape rule: the small-M kernel where it applies (allow_small),
+// then the preferred tier, then each smaller tile, then any tiled variant;
+// `fit` decides alignment.  THL_FORCE_VARIANT=<name> restricts the choice to
+// that variant.  Returns nullptr with *status set when none fits.
+template <class Fit>
+const Variant* choose_variant(const Prep& pr, bool allow_small, int64_t rows, int want_tier, Fit&& fit,
+                              thl_status* status) {
+  const char* forced = std::getenv("THL_FORCE_VARIANT");
+  const bool small_m = allow_small && pr.small_m;
+  const Variant* pick = nullptr;
+  bool family_built = false;
+  for (int pass = small_m ? -1 : want_tier; pass <= 3 && !pick; pass = pass < 0 ? want_tier : pass + 1) {
+    for (const Variant& v : kVariants) {
+      if (v.family != pr.fam || v.a_kmajor != pr.a_kmajor || v.b_kmajor != pr.b_kmajor) continue;
+      family_built = true;
+      if (forced && *forced) {
+        if (std::strcmp(forced, v.name) != 0 || (v.tier < 0 && (!small_m || v.bm < rows))) continue;
+      } else if ((pass < 3 && v.tier != pass) || (pass == 3 && v.tier < 0) || (v.tier < 0 && v.bm < rows)) {
+        continue;
+      }
+      if (fit(v)) {
+        pick = &v;
+        break;
+      }
+    }
+    if (forced && *forced) break;
   }
+  if (!pick) *status = (forced && *forced) ? THL_ERR_UNSUPPORTED : (family_built ? THL_ERR_MISALIGNED : THL_ERR_UNSUPPORTED);
+  return pick;
+}
+
+// Kernel arguments of one problem for variant v.
+GemmArgs make_args(const Prep& pr, const Variant& v, int64_t m, int64_t n, int64_t k, const void* A, const void* B,
+                   const void* C, int64_t ldc, void* D, int64_t ldd, float alpha, float beta, const thl_dtypes* dt,
+                   const void* bias) {
+  GemmArgs a{};
+  a.a = static_cast<const uint8_t*>(A);
+  a.b = static_cast<const uint8_t*>(B);
+  a.c = C;
+  a.d = D;
+  a.bias = pr.has_bias ? bias : nullptr;
+  a.sfa = pr.s.sfa;
+  a.sfb = pr.s.sfb;
+  a.lda_bytes = pr.lda_bytes;
+  a.ldb_bytes = pr.ldb_bytes;
+  a.ldc = ldc;
+  a.ldd = ldd;
+  a.ld_sfa = pr.s.ld_sfa;
+  a.ld_sfb = pr.s.ld_sfb;
+  a.m = static_cast<int32_t>(m);
+  a.n = static_cast<int32_t>(n);
+  a.k = static_cast<int32_t>(k);
+  a.kbytes = static_cast<int32_t>(bytes_of(dt->a, k));
+  a.tiles_m = static_cast<int32_t>((m + v.bm - 1) / v.bm);
+  a.tiles_n = static_cast<int32_t>((n + v.bn - 1) / v.bn);
+  a.group_m = 8;
+  const bool tensor_scaled = (dt->a == THL_E4M3 || dt->a == THL_E5M2) && (dt->b == THL_E4M3 || dt->b == THL_E5M2);
+  a.alpha = tensor_scaled ? alpha * pr.s.a_scale * pr.s.b_scale : alpha;
+  a.beta = beta;
+  a.flags = static_cast<int32_t>(pr.flags) | (pr.vec ? EPI_VEC : 0);
   a.c_type = static_cast<int32_t>(dt->c);
   a.d_type = static_cast<int32_t>(dt->d);
   a.bias_type = static_cast<int32_t>(dt->bias);
+  return a;
+}
+
+// Persistent workgroups for `problems` grid rows: at most as many as the
+// device holds at once, shared out over the rows (a multiple of 8 per row
+// while that many fit, so each XCD keeps its own range of tiles), and no
+// more than the largest row's tile count.  0 when the device cannot be
+// queried.
+int64_t persistent_grid(const Variant& v, int64_t problems, int64_t max_tiles) {
+  const int ncu = cu_count();
+  if (ncu <= 0) return 0;
+  const int64_t resident = static_cast<int64_t>(ncu) * v.occ;
+  int64_t per = resident / problems;
+  if (per >= 8) per -= per % 8;
+  if (per < 1) per = 1;
+  return max_tiles < per ? max_tiles : per;
+}
+
+thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const void* A, int64_t lda, thl_op opA,
+                     const void* B, int64_t ldb, thl_op opB, const void* C, int64_t ldc, void* D, int64_t ldd,
+                     float alpha, float beta, const thl_dtypes* dt, const thl_epilogue* epi, const thl_scales* sc,
+                     struct ihipStream_t* stream) {
+  Prep pr;
+  const unsigned flags = epi ? epi->flags : 0u;
+  thl_status st = prepare(bt, m, n, k, A, lda, opA, B, ldb, opB, C, ldc, D, ldd, alpha, beta, dt, flags,
+                          epi ? epi->bias : nullptr, sc, &pr);
+  if (st != THL_OK) return st;
+
+  // ---- variant: first fit on family, alignment and shape
+  // (tile counts over the whole batch: its problems fill the device together)
+  const int64_t tiles_256 = ((m + 255) / 256) * ((n + 255) / 256) * bt.count;
+  const int64_t tiles_256x128 = ((m + 255) / 256) * ((n + 127) / 128) * bt.count;
+  const Variant* pick = choose_variant(pr, true, m, want_tier_of(tiles_256, tiles_256x128),
+                                       [&](const Variant& v) { return fits(v, pr, bt, A, B, k); }, &st);
+  if (!pick) return st;
+  if (!pr.work) {
+    t_last_variant = pick->name;
+    return THL_OK;
+  }
+
+  // ---- launch
+  GemmArgs a = make_args(pr, *pick, m, n, k, A, B, C, ldc, D, ldd, alpha, beta, dt, epi ? epi->bias : nullptr);
+  // Batch strides in bytes (zero for a single problem and for absent arrays).
+  if (bt.count > 1) {
+    a.bs_a = pr.sa_bytes;
+    a.bs_b = pr.sb_bytes;
+    a.bs_c = beta != 0.0f ? bytes_of(dt->c, bt.c) : 0;
+    a.bs_d = bytes_of(dt->d, bt.d);
+    a.bs_bias = pr.has_bias ? bytes_of(dt->bias, bt.bias) : 0;
+    a.bs_sfa = pr.block_scaled ? bt.sfa : 0;
+    a.bs_sfb = pr.block_scaled ? bt.sfb : 0;
+  }
   if (pick->tier < 0) {  // small M: one workgroup per 16 columns
     if (pick->launch(a, dim3(static_cast<unsigned>((n + 15) / 16), static_cast<unsigned>(bt.count)),
                      reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
@@ -479,20 +568,133 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
   }
   const int64_t tiles = static_cast<int64_t>(a.tiles_m) * a.tiles_n;
   if (tiles > INT32_MAX) return THL_ERR_UNSUPPORTED;
-  // Persistent workgroups: at most as many as the device holds at once (a
-  // multiple of 8, so each XCD keeps its own range of tiles); each walks
-  // tiles blockIdx.x, + gridDim.x, ...
-  const int ncu = cu_count();
-  if (ncu <= 0) return THL_ERR_HIP;
-  const int64_t resident = static_cast<int64_t>(ncu) * pick->occ;
-  // Batched: the resident workgroups are shared out over the problems (a
-  // multiple of 8 per problem while that many fit), each grid row walking
-  // its own problem's tiles.
-  int64_t per = resident / bt.count;
-  if (per >= 8) per -= per % 8;
-  if (per < 1) per = 1;
-  const int64_t grid = tiles < per ? tiles : per;
+  // Persistent workgroups; each walks tiles blockIdx.x, + gridDim.x, ...
+  const int64_t grid = persistent_grid(*pick, bt.count, tiles);
+  if (grid <= 0) return THL_ERR_HIP;
   if (pick->launch(a, dim3(static_cast<unsigned>(grid), static_cast<unsigned>(bt.count)),
+                   reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return THL_ERR_HIP;
+  t_last_variant = pick->name;
+  return THL_OK;
+}
+
+// Grouped problems: each validated as by thl_gemm, then checked against each
+// other, and run with one variant, grid row z computing problem z from the
+// device copy of the descriptors.
+thl_status grouped_impl(int64_t count, const thl_group_problem* pb, const thl_group_problem* pb_dev, thl_op opA,
+                        thl_op opB, float alpha, float beta, const thl_dtypes* dt, const thl_epilogue* epi,
+                        const thl_scales* sc, struct ihipStream_t* stream) {
+  if (count < 0 || !dt) return THL_ERR_INVALID;
+  if (count > 65535) return THL_ERR_UNSUPPORTED;  // one grid row per problem
+  if (count > 0 && !pb) return THL_ERR_INVALID;
+  const unsigned flags = epi ? epi->flags : 0u;
+  const Batch one{};
+  std::vector<Prep> preps(static_cast<size_t>(count));
+  int64_t tiles_256 = 0, tiles_256x128 = 0;
+  bool any_work = false, all_vec = true;
+  int64_t ref = -1;  // the first problem with outputs: its family is the group's
+  for (int64_t z = 0; z < count; ++z) {
+    const thl_group_problem& q = pb[z];
+    thl_scales s = sc ? *sc : thl_scales{1.0f, 1.0f, nullptr, 0, nullptr, 0};
+    s.sfa = q.sfa;
+    s.ld_sfa = q.ld_sfa;
+    s.sfb = q.sfb;
+    s.ld_sfb = q.ld_sfb;
+    const thl_status st = prepare(one, q.m, q.n, q.k, q.A, q.lda, opA, q.B, q.ldb, opB, q.C, q.ldc, q.D, q.ldd,
+                                  alpha, beta, dt, flags, q.bias, &s, &preps[z]);
+    if (st != THL_OK) return st;
+    if (preps[z].work) {
+      // one family for the problems with outputs: block scales on every one
+      // of them or on none
+      if (ref < 0) ref = z;
+      if (preps[z].fam != preps[ref].fam) return THL_ERR_INVALID;
+      any_work = true;
+      all_vec = all_vec && preps[z].vec;
+      tiles_256 += ((q.m + 255) / 256) * ((q.n + 255) / 256);
+      tiles_256x128 += ((q.m + 255) / 256) * ((q.n + 127) / 128);
+    }
+  }
+  if (count == 0) return THL_OK;
+  if (any_work && !pb_dev) return THL_ERR_INVALID;
+
+  // ---- no problem's D overlaps another problem's D or anything it reads
+  if (any_work) {
+    struct Span {
+      Range r;
+      int64_t z;
+      bool is_d;
+    };
+    std::vector<Span> spans;
+    for (int64_t z = 0; z < count; ++z) {
+      const thl_group_problem& q = pb[z];
+      const Prep& pr = preps[z];
+      if (!pr.work) continue;
+      const int64_t ra = opA == THL_OP_N ? q.m : q.k, ca = opA == THL_OP_N ? q.k : q.m;
+      const int64_t rb = opB == THL_OP_N ? q.k : q.n, cb = opB == THL_OP_N ? q.n : q.k;
+      spans.push_back({matrix_range(q.D, dt->d, q.m, q.n, q.ldd), z, true});
+      if (q.k > 0) {
+        spans.push_back({matrix_range(q.A, dt->a, ra, ca, q.lda), z, false});
+        spans.push_back({matrix_range(q.B, dt->b, rb, cb, q.ldb), z, false});
+      }
+      if (beta != 0.0f) spans.push_back({matrix_range(q.C, dt->c, q.m, q.n, q.ldc), z, false});
+      if (pr.has_bias) spans.push_back({matrix_range(q.bias, dt->bias, q.m, 1, q.m), z, false});
+      if (pr.block_scaled && q.k > 0) {
+        spans.push_back({matrix_range(q.sfa, THL_E8M0, q.k / 32, q.m, q.ld_sfa), z, false});
+        spans.push_back({matrix_range(q.sfb, THL_E8M0, q.k / 32, q.n, q.ld_sfb), z, false});
+      }
+    }
+    // D spans sorted by start: neighbours must not overlap, and every other
+    // span of another problem must miss them all (its own problem's spans
+    // were checked by prepare; C == D of one problem is its exact alias).
+    std::vector<Span> ds;
+    for (const Span& sp : spans)
+      if (sp.is_d && sp.r.lo < sp.r.hi) ds.push_back(sp);
+    std::sort(ds.begin(), ds.end(), [](const Span& a, const Span& b) { return a.r.lo < b.r.lo; });
+    for (size_t i = 1; i < ds.size(); ++i)
+      if (ds[i].r.lo < ds[i - 1].r.hi) return THL_ERR_INVALID;
+    for (const Span& sp : spans) {
+      if (sp.is_d || sp.r.lo >= sp.r.hi) continue;
+      // first D span ending after sp starts
+      auto it = std::upper_bound(ds.begin(), ds.end(), sp.r.lo,
+                                 [](uintptr_t v, const Span& d) { return v < d.r.hi; });
+      for (; it != ds.end() && it->r.lo < sp.r.hi; ++it)
+        if (it->z != sp.z) return THL_ERR_INVALID;
+    }
+  }
+
+  // ---- one variant for every problem (tiled kernels only)
+  thl_status st = THL_OK;
+  const Prep& pref = preps[ref < 0 ? 0 : ref];
+  const Variant* pick = choose_variant(pref, false, 0, want_tier_of(tiles_256, tiles_256x128),
+                                       [&](const Variant& v) {
+                                         for (int64_t z = 0; z < count; ++z)
+                                           if (preps[z].work && !fits(v, preps[z], one, pb[z].A, pb[z].B, pb[z].k))
+                                             return false;
+                                         return true;
+                                       },
+                                       &st);
+  if (!pick) return st;
+  if (!any_work) {
+    t_last_variant = pick->name;
+    return THL_OK;
+  }
+  int64_t max_tiles = 0;
+  for (int64_t z = 0; z < count; ++z) {
+    const int64_t t = preps[z].work ? ((pb[z].m + pick->bm - 1) / pick->bm) * ((pb[z].n + pick->bn - 1) / pick->bn) : 0;
+    if (t > INT32_MAX) return THL_ERR_UNSUPPORTED;
+    max_tiles = t > max_tiles ? t : max_tiles;
+  }
+  // Group-wide arguments; the kernel fills in each row's problem from the
+  // device descriptors.
+  Prep p0 = pref;
+  p0.vec = all_vec;
+  GemmArgs a = make_args(p0, *pick, 0, 0, 0, nullptr, nullptr, nullptr, 0, nullptr, 0, alpha, beta, dt, nullptr);
+  a.group = reinterpret_cast<const GroupProblem*>(pb_dev);
+  a.elem_bits_a = static_cast<int32_t>(dt->a == THL_E2M1X2 ? 4 : 8 * bytes_of(dt->a, 1));
+  a.elem_bits_b = static_cast<int32_t>(dt->b == THL_E2M1X2 ? 4 : 8 * bytes_of(dt->b, 1));
+  const int64_t grid = persistent_grid(*pick, count, max_tiles);
+  if (grid <= 0) return THL_ERR_HIP;
+  if (pick->launch(a, dim3(static_cast<unsigned>(grid), static_cast<unsigned>(count)),
                    reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return THL_ERR_HIP;
   t_last_variant = pick->name;

@@ -25,6 +25,25 @@ enum : int { EPI_BIAS = 1, EPI_RELU = 2, EPI_GELU = 4 };
 // 256-column panel of C or D spans less than 2 GiB.
 enum : int { EPI_VEC = 8 };
 
+// One problem of a grouped launch, as the caller's device array holds it
+// (the same layout as the public thl_group_problem).
+struct GroupProblem {
+  int64_t m, n, k;
+  const void* a;
+  int64_t lda;  // elements
+  const void* b;
+  int64_t ldb;
+  const void* c;
+  int64_t ldc;
+  void* d;
+  int64_t ldd;
+  const void* bias;
+  const uint8_t* sfa;
+  int64_t ld_sfa;
+  const uint8_t* sfb;
+  int64_t ld_sfb;
+};
+
 struct GemmArgs {
   const uint8_t* a;  // A as stored: leading dimension lda_bytes
   const uint8_t* b;  // B as stored: leading dimension ldb_bytes
@@ -45,6 +64,11 @@ struct GemmArgs {
   // Batched problems: problem blockIdx.y's arrays lie these many bytes
   // further per problem (all zero for a single problem).
   int64_t bs_a, bs_b, bs_c, bs_d, bs_bias, bs_sfa, bs_sfb;
+  // Grouped problems: grid row blockIdx.y computes group[blockIdx.y] (sizes,
+  // pointers and leading dimensions replace the fields above); operand
+  // elements are elem_bits_a / elem_bits_b bits wide.  NULL otherwise.
+  const GroupProblem* group;
+  int32_t elem_bits_a, elem_bits_b;
 };
 
 

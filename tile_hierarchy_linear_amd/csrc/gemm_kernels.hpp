@@ -444,6 +444,36 @@ __device__ __forceinline__ void offset_to_problem(GemmArgs& p) {
   p.bias = static_cast<const uint8_t*>(p.bias) + z * p.bs_bias;
 }
 
+// Grouped problems (the grouped GEMM of "What's New in CUTLASS 4.8"): grid
+// row blockIdx.y computes problem group[blockIdx.y], whose sizes, pointers
+// and leading dimensions replace the launch-wide ones.  Returns false when
+// this workgroup has no tile of that problem (the whole workgroup leaves).
+template <int BM, int BN>
+__device__ __forceinline__ bool select_group_problem(GemmArgs& p) {
+  const GroupProblem& g = p.group[blockIdx.y];
+  const int64_t m = g.m, n = g.n, k = g.k;
+  p.m = static_cast<int32_t>(m);
+  p.n = static_cast<int32_t>(n);
+  p.k = static_cast<int32_t>(k);
+  p.kbytes = static_cast<int32_t>(k * p.elem_bits_a / 8);
+  p.a = static_cast<const uint8_t*>(g.a);
+  p.b = static_cast<const uint8_t*>(g.b);
+  p.c = g.c;
+  p.d = g.d;
+  p.bias = (p.flags & EPI_BIAS) ? g.bias : nullptr;
+  p.sfa = g.sfa;
+  p.sfb = g.sfb;
+  p.lda_bytes = g.lda * p.elem_bits_a / 8;
+  p.ldb_bytes = g.ldb * p.elem_bits_b / 8;
+  p.ldc = g.ldc;
+  p.ldd = g.ldd;
+  p.ld_sfa = g.ld_sfa;
+  p.ld_sfb = g.ld_sfb;
+  p.tiles_m = static_cast<int32_t>((m + BM - 1) / BM);
+  p.tiles_n = static_cast<int32_t>((n + BN - 1) / BN);
+  return m > 0 && n > 0 && static_cast<int64_t>(blockIdx.x) < static_cast<int64_t>(p.tiles_m) * p.tiles_n;
+}
+
 // ------------------------------------------------------------ the kernel
 //
 // Pipeline (per wavefront, K-steps of 64 bytes per operand row, a ring of
@@ -474,7 +504,11 @@ __device__ __forceinline__ void offset_to_problem(GemmArgs& p) {
 template <int F, int BM, int BN, int WM, int WN, int LOADW, int STAGES, int OCC, int SCW, bool AK, bool BK>
 __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 gemm_kernel(GemmArgs p) {
-  offset_to_problem(p);
+  if (p.group) {
+    if (!select_group_problem<BM, BN>(p)) return;
+  } else {
+    offset_to_problem(p);
+  }
   using T = Fam<F>;
   using Acc = typename T::Acc;
   constexpr int KB = maps::kStepBytes;

@@ -150,3 +150,46 @@ class BatchedDeviceProblem:
         if w.type_d == "i32":
             return host.to(torch.int64).numpy()
         return host.to(torch.float64).numpy()
+
+
+class GroupedDeviceProblem:
+    """Workloads of different shapes, one format and one epilogue, each
+    uploaded to buffers of its own, run with one thl_gemm_grouped call.  The
+    descriptor array is built on the host and copied to the device; the
+    per-tensor fp8 scales, alpha, beta, activation and types are the first
+    workload's (the others are updated to match, so that each can be checked
+    against the oracle as it stands)."""
+
+    def __init__(self, ws, device="cuda", d_fill=float("nan")):
+        self.ws = ws
+        w0 = ws[0]
+        for w in ws[1:]:
+            w.a_scale, w.b_scale = w0.a_scale, w0.b_scale
+        self.probs = [DeviceProblem(w, device=device, d_fill=d_fill) for w in ws]
+        arr = (thl.thl_group_problem * len(ws))()
+
+        def ptr(t):
+            return t.data_ptr() if t is not None and t.numel() else None
+
+        for z, (w, dp) in enumerate(zip(ws, self.probs)):
+            arr[z] = thl.thl_group_problem(w.m, w.n, w.k, ptr(dp.a), w.lda, ptr(dp.b), w.ldb, ptr(dp.c),
+                                           w.ldc or max(1, w.m), dp.d.data_ptr(), dp.ldd, ptr(dp.bias), ptr(dp.sfa),
+                                           int(w.ld_sfa), ptr(dp.sfb), int(w.ld_sfb))
+        self.host = arr
+        raw = np.frombuffer(bytes(arr), dtype=np.uint8).copy() if len(ws) else np.zeros(0, np.uint8)
+        self.dev = torch.from_numpy(raw).to(device)
+
+    def run(self, stream=None):
+        w = self.ws[0]
+        dt = thl.make_dtypes(w.type_a, w.type_b, w.type_c, w.type_d, w.type_bias if w.bias is not None else "none")
+        flags = (thl.THL_EPI_BIAS if w.bias is not None else 0) | \
+            {"none": 0, "relu": thl.THL_EPI_RELU, "gelu": thl.THL_EPI_GELU}[w.act]
+        epi = thl.thl_epilogue(flags, None)
+        sc = thl.thl_scales(float(w.a_scale), float(w.b_scale), None, 0, None, 0)
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        return thl.thl_gemm_grouped(len(self.ws), self.host, self.dev.data_ptr() if self.dev.numel() else None,
+                                    w.op_a, w.op_b, w.alpha, w.beta, dt, epi, sc, stream)
+
+    def d_all(self, z) -> np.ndarray:
+        return self.probs[z].d_all()
