@@ -122,9 +122,23 @@ typedef struct {
  * It reads each scale row (E2M1X2) in 8-byte units up to its next 16-byte
  * boundary, as the tiled kernels read it in 16-byte groups.
  *
+ * Split K: when a single problem's tiles fill at most half of the device's
+ * resident workgroups (128x128 tiles, F16/BF16/I8 and the unscaled fp8
+ * families, k spanning at least 16 K-steps), the K range of each tile is
+ * split over 2 to 16 workgroups.  Each writes its partial fp32 (int32)
+ * accumulators to a workspace; the last to finish a tile adds them in split
+ * order 0, 1, 2, ... (so results do not depend on timing) and runs the
+ * epilogue.  The workspace, splits * tiles * 64 KiB plus one counter per
+ * tile, comes from a stream-ordered memory pool the library creates once per
+ * device; it is taken and returned on `stream` around the launch, and its
+ * counters are cleared by a small kernel on `stream` first.  If the pool
+ * cannot provide it the problem runs unsplit.  thl_last_splits reports what
+ * ran.
+ *
  * Ownership: A, B, C, D, bias, sfa, sfb are device pointers owned by the
- * caller; the library allocates nothing and keeps no pointer after return.
- * alpha, beta and the per-tensor scales are host values.
+ * caller; apart from the split-K workspace above the library allocates
+ * nothing, and it keeps no pointer after return.  alpha, beta and the
+ * per-tensor scales are host values.
  *
  * Block scales: sfa or sfb given with F16, BF16 or I8 operands is
  * THL_ERR_UNSUPPORTED.  fp8 operands with either array given are MX fp8;
@@ -244,6 +258,11 @@ const char* thl_status_string(int status);
  * launched ("" before any); the storage is thread-local and stays valid until
  * the thread's next thl_gemm call. */
 const char* thl_last_variant(void);
+
+/* Number of K splits (workgroups sharing each output tile) of the calling
+ * thread's last successful launch: 1 unless thl_gemm split K (see thl_gemm,
+ * "Split K"). */
+int thl_last_splits(void);
 
 /* Number of kernel variants built into the library, and the name of each
  * (static strings).  Setting THL_FORCE_VARIANT=<name> in the environment makes

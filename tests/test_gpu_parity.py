@@ -834,3 +834,73 @@ def test_grouped_many_tiles_per_problem():
 
     ws = [wl.make("bf16", 1000 + 256 * z, 2304 - 256 * z, 512, seed=4100 + z) for z in range(6)]
     _check_grouped(ws, expect="bf16_nn_")
+
+
+# ------------------------------------------------------------ split K
+
+SPLITK_CASES = [
+    # kind, variant, shape (ragged M/N, K with a partial last K-step), extra workload arguments
+    ("bf16", "bf16_nn_128x128_v16_s4_o2", (300, 200, 1000), {"lda": 304, "ldb": 1000}),
+    ("bf16", "bf16_tt_128x128_v16_s4_o2", (260, 130, 520), {"op_a": "T", "op_b": "T", "lda": 520, "ldb": 136,
+                                                            "act": "gelu"}),
+    ("fp16", "f16_tn_128x128_v16_s4_o2", (129, 257, 1032), {"lda": 1032, "ldb": 1032, "beta": 0.5, "type_c": "f32"}),
+    ("int8", "i8_tn_128x128_v16_s4_o2", (260, 130, 2032), {"beta": 1.0, "bias": True, "act": "relu"}),
+    ("fp8", "e4m3_tn_128x128_v16_s4_o2", (300, 260, 2032), {"beta": 1.0, "bias": True}),
+    ("fp8e5m2", "e5m2_tn_128x128_v16_s4_o2", (140, 300, 1040), {}),
+    ("fp8e4e5", "e4m3e5m2_tn_128x128_v16_s4_o2", (200, 200, 1024), {}),
+    ("fp8", "e4m3_tn_128x128_v4_s4_o2", (300, 260, 2040), {}),
+]
+
+
+@pytest.mark.parametrize("splits", [2, 3, 5])
+@pytest.mark.parametrize("case", SPLITK_CASES, ids=lambda c: c[1])
+def test_split_k_forced(case, splits):
+    # K split over `splits` workgroups per tile, the last split with the
+    # partial K-step; every output against the oracle
+    import tile_hierarchy_linear_amd as thl
+    import workloads as wl
+
+    kind, variant, (m, n, k), kw = case
+    w = wl.make(kind, m, n, k, **kw)
+    # splits of ceil(nk / splits) K-steps each, dropping a split left empty
+    nk = -(-k * {"e4m3": 1, "e5m2": 1, "i8": 1}.get(w.type_a, 2) // 64)
+    want = -(-nk // -(-nk // splits))
+    os.environ["THL_FORCE_SPLITS"] = str(splits)
+    try:
+        _check_full(w, variant=variant)
+        assert thl.thl_last_splits() == want
+    finally:
+        os.environ.pop("THL_FORCE_SPLITS", None)
+
+
+@pytest.mark.parametrize("kind,shape,want", [("bf16", (2048, 2048, 8192), 2), ("fp8", (1024, 1024, 8192), 8),
+                                             ("int8", (1024, 512, 4096), 8), ("fp16", (640, 384, 8192), 16)])
+def test_split_k_automatic(kind, shape, want):
+    # few tiles and a long K: thl_gemm splits K on its own
+    import tile_hierarchy_linear_amd as thl
+    import workloads as wl
+
+    m, n, k = shape
+    w = wl.make(kind, m, n, k)
+    dp = _check_sampled(w, extra_edges=True)
+    assert thl.thl_last_splits() == want, (thl.thl_last_variant(), thl.thl_last_splits())
+    del dp
+
+
+def test_split_k_is_deterministic():
+    # the partials are added in split order whichever split finishes last
+    import tile_hierarchy_linear_amd as thl
+    import workloads as wl
+    from workloads.device import DeviceProblem
+
+    w = wl.make("bf16", 1024, 1024, 8192)
+    dp = DeviceProblem(w)
+    assert dp.run() == 0
+    torch.cuda.synchronize()
+    assert thl.thl_last_splits() > 1
+    first = dp.d.clone()
+    for _ in range(3):
+        dp.d.fill_(float("nan"))
+        assert dp.run() == 0
+        torch.cuda.synchronize()
+        assert torch.equal(dp.d.view(torch.int16), first.view(torch.int16))

@@ -81,6 +81,7 @@ def _load():
     lib.thl_status_string.argtypes = [ctypes.c_int]
     lib.thl_status_string.restype = cp
     lib.thl_last_variant.restype = cp
+    lib.thl_last_splits.restype = ctypes.c_int
     lib.thl_variant_count.restype = ctypes.c_int
     lib.thl_variant_name.argtypes = [ctypes.c_int]
     lib.thl_variant_name.restype = cp
@@ -118,6 +119,10 @@ def thl_status_string(status: int) -> str:
 
 def thl_last_variant() -> str:
     return _lib.thl_last_variant().decode()
+
+
+def thl_last_splits() -> int:
+    return int(_lib.thl_last_splits())
 
 
 def thl_variant_count() -> int:

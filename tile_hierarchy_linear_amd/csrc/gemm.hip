@@ -19,6 +19,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 #include <vector>
 
@@ -104,6 +105,7 @@ const Variant kVariants[] = {
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 thread_local const char* t_last_variant = "";
+thread_local int last_splits = 1;
 
 // Compute units of a device, read once per device.
 std::atomic<int> g_cu_count[64];
@@ -117,6 +119,44 @@ int cu_count() {
     g_cu_count[dev].store(n, std::memory_order_relaxed);
   }
   return n;
+}
+
+// ---- split-K workspace
+// Split K needs device memory for the partial tiles and one arrival counter
+// per tile.  thl_gemm draws it per call from a stream-ordered pool the
+// library creates once per device (memory stays in the pool between calls),
+// clears the counters with a small kernel on the stream, and returns the
+// block to the pool on the stream after the GEMM.
+
+__global__ void clear_counters(uint32_t* c, int n) {
+  for (int i = static_cast<int>(blockIdx.x * blockDim.x + threadIdx.x); i < n; i += gridDim.x * blockDim.x) c[i] = 0u;
+}
+
+std::mutex g_pool_mutex;
+hipMemPool_t g_pools[64];
+
+hipMemPool_t pool_for_device(int dev) {
+  if (dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(g_pool_mutex);
+  if (!g_pools[dev]) {
+    hipMemPoolProps props{};
+    props.allocType = hipMemAllocationTypePinned;
+    props.handleTypes = hipMemHandleTypeNone;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t pool = nullptr;
+    if (hipMemPoolCreate(&pool, &props) != hipSuccess) return nullptr;
+    uint64_t keep = UINT64_MAX;  // keep freed blocks for the next call
+    (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+    g_pools[dev] = pool;
+  }
+  return g_pools[dev];
+}
+
+// Bytes of workspace for `tiles` tiles of bm x bn split `splits` ways: the
+// partial tiles (fp32 or int32), then the counters from a 256-byte boundary.
+int64_t splitk_bytes(int64_t tiles, int splits, int bm, int bn) {
+  return tiles * splits * bm * bn * 4 + (tiles * 4 + 255) / 256 * 256;
 }
 
 int family_of(thl_dtype t) {
@@ -195,10 +235,15 @@ bool aligned(const void* p, int64_t pitch_bytes, int w) {
   return (reinterpret_cast<uintptr_t>(p) % w) == 0 && (pitch_bytes % w) == 0;
 }
 
+// Where a split-K workspace comes from: a stream-ordered pool allocation
+// (thl_gemm), or the library's static scratch array (the no-allocation
+// entry point).
+enum { WS_POOL = 0, WS_STATIC = 1 };
+
 thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const void* A, int64_t lda, thl_op opA,
                      const void* B, int64_t ldb, thl_op opB, const void* C, int64_t ldc, void* D, int64_t ldd,
                      float alpha, float beta, const thl_dtypes* dt, const thl_epilogue* epi, const thl_scales* sc,
-                     struct ihipStream_t* stream);
+                     struct ihipStream_t* stream, int ws_mode);
 thl_status grouped_impl(int64_t count, const thl_group_problem* pb, const thl_group_problem* pb_dev, thl_op opA,
                         thl_op opB, float alpha, float beta, const thl_dtypes* dt, const thl_epilogue* epi,
                         const thl_scales* sc, struct ihipStream_t* stream);
@@ -231,6 +276,8 @@ const char* thl_status_string(int s) {
 
 const char* thl_last_variant(void) { return t_last_variant; }
 
+int thl_last_splits(void) { return last_splits; }
+
 int thl_variant_count(void) { return kNumVariants; }
 
 const char* thl_variant_name(int i) { return (i >= 0 && i < kNumVariants) ? kVariants[i].name : nullptr; }
@@ -239,7 +286,7 @@ thl_status thl_gemm(int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
                     int64_t ldb, thl_op opB, const void* C, int64_t ldc, void* D, int64_t ldd, float alpha,
                     float beta, const thl_dtypes* dt, const thl_epilogue* epi, const thl_scales* sc,
                     struct ihipStream_t* stream) {
-  return gemm_impl(Batch{}, m, n, k, A, lda, opA, B, ldb, opB, C, ldc, D, ldd, alpha, beta, dt, epi, sc, stream);
+  return gemm_impl(Batch{}, m, n, k, A, lda, opA, B, ldb, opB, C, ldc, D, ldd, alpha, beta, dt, epi, sc, stream, WS_POOL);
 }
 
 thl_status thl_gemm_batched(int64_t batch, int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
@@ -257,7 +304,7 @@ thl_status thl_gemm_batched(int64_t batch, int64_t m, int64_t n, int64_t k, cons
   bt.bias = stride_bias;
   bt.sfa = stride_sfa;
   bt.sfb = stride_sfb;
-  return gemm_impl(bt, m, n, k, A, lda, opA, B, ldb, opB, C, ldc, D, ldd, alpha, beta, dt, epi, sc, stream);
+  return gemm_impl(bt, m, n, k, A, lda, opA, B, ldb, opB, C, ldc, D, ldd, alpha, beta, dt, epi, sc, stream, WS_POOL);
 }
 
 thl_status thl_gemm_grouped(int64_t count, const thl_group_problem* problems, const thl_group_problem* problems_dev,
@@ -525,10 +572,36 @@ int64_t persistent_grid(const Variant& v, int64_t problems, int64_t max_tiles) {
   return max_tiles < per ? max_tiles : per;
 }
 
+// Splits for one problem on variant v: only the variants built with split K
+// (128x128, two workgroups per CU, unscaled families), a single problem, and
+// tiles that fill at most half the resident workgroups; as many splits as
+// fill them, at most 16, with at least 8 K-steps each.  THL_FORCE_SPLITS=<s>
+// asks for s splits on any eligible variant (tests use it to cover the path
+// at small sizes).
+int choose_splits(const Prep& pr, const Variant& v, const Batch& bt, int64_t tiles, int64_t kbytes) {
+  if (bt.count != 1 || v.tier < 0 || pr.block_scaled || v.occ != 2 || v.bm * v.bn > 128 * 128 || kbytes <= 0)
+    return 1;
+  const int64_t nk_all = (kbytes + 63) / 64;
+  const char* forced = std::getenv("THL_FORCE_SPLITS");
+  if (forced && *forced) {
+    const int64_t f = std::atoll(forced);
+    return static_cast<int>(f < 1 ? 1 : (f > nk_all ? nk_all : (f > 64 ? 64 : f)));
+  }
+  const int ncu = cu_count();
+  const int64_t resident = static_cast<int64_t>(ncu) * v.occ;
+  if (ncu <= 0 || tiles * 2 > resident) return 1;
+  int64_t sp = resident / tiles;
+  if (sp > nk_all / 8) sp = nk_all / 8;
+  if (sp > 16) sp = 16;
+  return sp >= 2 ? static_cast<int>(sp) : 1;
+}
+
+thl_status static_scratch(hipStream_t stream, int64_t bytes, uint8_t** out);
+
 thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const void* A, int64_t lda, thl_op opA,
                      const void* B, int64_t ldb, thl_op opB, const void* C, int64_t ldc, void* D, int64_t ldd,
                      float alpha, float beta, const thl_dtypes* dt, const thl_epilogue* epi, const thl_scales* sc,
-                     struct ihipStream_t* stream) {
+                     struct ihipStream_t* stream, int ws_mode) {
   Prep pr;
   const unsigned flags = epi ? epi->flags : 0u;
   thl_status st = prepare(bt, m, n, k, A, lda, opA, B, ldb, opB, C, ldc, D, ldd, alpha, beta, dt, flags,
@@ -544,6 +617,7 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
   if (!pick) return st;
   if (!pr.work) {
     t_last_variant = pick->name;
+    last_splits = 1;
     return THL_OK;
   }
 
@@ -564,17 +638,62 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
                      reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
       return THL_ERR_HIP;
     t_last_variant = pick->name;
+    last_splits = 1;
     return THL_OK;
   }
   const int64_t tiles = static_cast<int64_t>(a.tiles_m) * a.tiles_n;
   if (tiles > INT32_MAX) return THL_ERR_UNSUPPORTED;
-  // Persistent workgroups; each walks tiles blockIdx.x, + gridDim.x, ...
-  const int64_t grid = persistent_grid(*pick, bt.count, tiles);
+  const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  // Split K over workgroups when the tiles fill at most half the resident
+  // workgroups: each tile's K-steps go to `splits` consecutive units.
+  const int splits = choose_splits(pr, *pick, bt, tiles, a.kbytes);
+  int64_t units = tiles;
+  uint8_t* pool_ws = nullptr;
+  if (splits > 1) {
+    const int64_t nk_all = (a.kbytes + 63) / 64;
+    a.ksteps = static_cast<int32_t>((nk_all + splits - 1) / splits);
+    a.splits = static_cast<int32_t>((nk_all + a.ksteps - 1) / a.ksteps);  // no empty split
+    units = tiles * a.splits;
+    const int64_t bytes = splitk_bytes(tiles, a.splits, pick->bm, pick->bn);
+    uint8_t* ws = nullptr;
+    if (ws_mode == WS_STATIC) {
+      st = static_scratch(hs, bytes, &ws);
+      if (st != THL_OK) return st;
+    } else {
+      int dev = 0;
+      hipMemPool_t pool = hipGetDevice(&dev) == hipSuccess ? pool_for_device(dev) : nullptr;
+      if (!pool || hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws), static_cast<size_t>(bytes), pool, hs) !=
+                       hipSuccess) {
+        (void)hipGetLastError();
+        ws = nullptr;  // no workspace: run unsplit
+      }
+      pool_ws = ws;
+    }
+    if (ws) {
+      a.ws = ws;
+      a.counters = reinterpret_cast<uint32_t*>(ws + tiles * a.splits * pick->bm * pick->bn * 4);
+      if (pool_ws) {
+        const int nt = static_cast<int>(tiles);
+        hipLaunchKernelGGL(clear_counters, dim3((nt + 255) / 256), dim3(256), 0, hs, a.counters, nt);
+        if (hipGetLastError() != hipSuccess) {
+          (void)hipFreeAsync(pool_ws, hs);
+          return THL_ERR_HIP;
+        }
+      }
+    } else {
+      a.splits = 1;
+      a.ksteps = 0;
+      units = tiles;
+    }
+  }
+  // Persistent workgroups; each walks units blockIdx.x, + gridDim.x, ...
+  const int64_t grid = persistent_grid(*pick, bt.count, units);
   if (grid <= 0) return THL_ERR_HIP;
-  if (pick->launch(a, dim3(static_cast<unsigned>(grid), static_cast<unsigned>(bt.count)),
-                   reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
-    return THL_ERR_HIP;
+  const hipError_t le = pick->launch(a, dim3(static_cast<unsigned>(grid), static_cast<unsigned>(bt.count)), hs);
+  if (pool_ws) (void)hipFreeAsync(pool_ws, hs);  // back to the pool once the GEMM has run
+  if (le != hipSuccess) return THL_ERR_HIP;
   t_last_variant = pick->name;
+  last_splits = a.splits > 1 ? a.splits : 1;
   return THL_OK;
 }
 
@@ -698,8 +817,11 @@ thl_status grouped_impl(int64_t count, const thl_group_problem* pb, const thl_gr
                    reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return THL_ERR_HIP;
   t_last_variant = pick->name;
+  last_splits = 1;
   return THL_OK;
 }
+
+thl_status static_scratch(hipStream_t, int64_t, uint8_t**) { return THL_ERR_UNSUPPORTED; }
 
 }  // namespace
 }  // namespace thl

@@ -69,6 +69,13 @@ struct GemmArgs {
   // elements are elem_bits_a / elem_bits_b bits wide.  NULL otherwise.
   const GroupProblem* group;
   int32_t elem_bits_a, elem_bits_b;
+  // Split K across workgroups: `splits` units per tile (1: none), each over
+  // `ksteps` 64-byte K-steps from its split's first; partial accumulators in
+  // `ws` (splits slots of BM*BN*4 bytes per tile), one arrival counter per
+  // tile in `counters` (zero before the launch, left zero after it).
+  int32_t splits, ksteps;
+  uint8_t* ws;
+  uint32_t* counters;
 };
 
 

@@ -622,9 +622,22 @@ gemm_kernel(GemmArgs p) {
   const int lane = static_cast<int>(threadIdx.x) & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int wm = wave % WM, wn = wave / WM;
-  const int nk = (p.kbytes + KB - 1) / KB;  // K-steps, the last one possibly partial
-  const int nkf = p.kbytes / KB;            // full K-steps
   const int ntiles = p.tiles_m * p.tiles_n;
+  // Split K: work unit u is split u % splits of tile u / splits and covers
+  // p.ksteps K-steps from the split's first (the last split keeps the
+  // partial step); without it, one unit per tile.  nk, nkf, kbytes_u and
+  // kel_u describe the current unit's K range.
+  // Split K is built into the 128x128 two-workgroup variants of the unscaled
+  // families (the tiles chosen when a problem has few); elsewhere splits is 1.
+  constexpr bool SPLITK = OCC == 2 && BM * BN <= 128 * 128 && !T::SCALED;
+  const int splits = (SPLITK && p.splits > 1) ? p.splits : 1;
+  const int nk_all = (p.kbytes + KB - 1) / KB;
+  const int nunits = ntiles * splits;
+  int nk = nk_all;         // K-steps of the unit, the last one possibly partial
+  int nkf = p.kbytes / KB; // full K-steps of the unit
+  int kbytes_u = p.kbytes; // bytes of K per operand row in the unit
+  int kel_u = p.k;         // elements of K in the unit
+  int unit_tile = 0, unit_split = 0;
   const int64_t a_step = AK ? KB : 32 * p.lda_bytes;  // operand advance per K-step
   const int64_t b_step = BK ? KB : 32 * p.ldb_bytes;
   const int nkb = p.k >> 5;
@@ -652,11 +665,29 @@ gemm_kernel(GemmArgs p) {
   // 8 whenever the tile count is).
   auto setup = [&](int id) {
     int64_t tm, tn;
-    maps::grouped_tile(maps::xcd_remap(id, ntiles), p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
+    if (SPLITK && splits > 1) {
+      // the splits of one tile are consecutive units (consecutive workgroups)
+      unit_tile = id / splits;
+      unit_split = id - unit_tile * splits;
+      maps::grouped_tile(unit_tile, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
+    } else {
+      maps::grouped_tile(maps::xcd_remap(id, ntiles), p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
+    }
     m0 = tm * BM;
     n0 = tn * BN;
     a_tile = AK ? p.a + m0 * p.lda_bytes : p.a + m0 * 2;
     b_tile = BK ? p.b + n0 * p.ldb_bytes : p.b + n0 * 2;
+    if (SPLITK && splits > 1) {
+      const int kbeg = unit_split * p.ksteps;
+      const int kend = kbeg + p.ksteps < nk_all ? kbeg + p.ksteps : nk_all;
+      const int bend = kend * KB < p.kbytes ? kend * KB : p.kbytes;
+      kbytes_u = bend - kbeg * KB;
+      kel_u = p.k - kbeg * (KB / 2);  // M-major operands are 16-bit: 32 elements a step
+      nk = kend - kbeg;
+      nkf = kbytes_u / KB;
+      a_tile += kbeg * a_step;
+      b_tile += kbeg * b_step;
+    }
 #pragma unroll
     for (int j = 0; j < A_LOADS; ++j) {
       int64_t row, byte;
@@ -754,14 +785,14 @@ gemm_kernel(GemmArgs p) {
   auto pair_src = [&](int s0, __amdgpu_buffer_rsrc_t& ra, __amdgpu_buffer_rsrc_t& rb) {
     const int64_t kb = static_cast<int64_t>(s0) * KB;
     if constexpr (AK) {
-      int64_t na = (p.m - 1 - m0) * p.lda_bytes + p.kbytes - kb;
+      int64_t na = (p.m - 1 - m0) * p.lda_bytes + kbytes_u - kb;
       na = na < BM * p.lda_bytes ? na : BM * p.lda_bytes;
       ra = make_rsrc_n(a_tile + kb, static_cast<int>(na > 0 ? na : 0));
     } else {
       ra = make_rsrc(a_tile);
     }
     if constexpr (BK) {
-      int64_t nb = (p.n - 1 - n0) * p.ldb_bytes + p.kbytes - kb;
+      int64_t nb = (p.n - 1 - n0) * p.ldb_bytes + kbytes_u - kb;
       nb = nb < BN * p.ldb_bytes ? nb : BN * p.ldb_bytes;
       rb = make_rsrc_n(b_tile + kb, static_cast<int>(nb > 0 ? nb : 0));
     } else {
@@ -847,7 +878,7 @@ gemm_kernel(GemmArgs p) {
         int64_t row, byte;
         maps::pair_copy_source(j * NW + wave, lane, &row, &byte);
         const int64_t r = m0 + row < p.m ? row : p.m - 1 - m0;
-        const int64_t off = r * p.lda_bytes + (kofs + byte < p.kbytes ? kofs + byte : 0);
+        const int64_t off = r * p.lda_bytes + (kofs + byte < kbytes_u ? kofs + byte : 0);
         load_lds_buf<16>(ra, static_cast<uint32_t>(off), sa + (j * NW + wave) * 1024);
       }
     }
@@ -856,11 +887,11 @@ gemm_kernel(GemmArgs p) {
       int64_t row, byte, off;
       if constexpr (AK) {
         maps::copy_source((j * NW + wave) * 64 * LOADW, lane, LOADW, &row, &byte);
-        off = a_off[j] + (kofs + byte < p.kbytes ? kofs : -byte);
+        off = a_off[j] + (kofs + byte < kbytes_u ? kofs : -byte);
       } else {
         maps::mm_copy_source((j * NW + wave) * 64 * LOADW, lane, LOADW, PA, &row, &byte);
         const int64_t k = 32 * static_cast<int64_t>(kt) + row;
-        off = a_off[j] - (k < p.k ? 0 : row * p.lda_bytes);
+        off = a_off[j] - (k < kel_u ? 0 : row * p.lda_bytes);
       }
       load_lds_buf<LOADW>(ra, static_cast<uint32_t>(off), sa + (j * NW + wave) * 64 * LOADW);
     }
@@ -870,7 +901,7 @@ gemm_kernel(GemmArgs p) {
         int64_t row, byte;
         maps::pair_copy_source(j * NW + wave, lane, &row, &byte);
         const int64_t r = n0 + row < p.n ? row : p.n - 1 - n0;
-        const int64_t off = r * p.ldb_bytes + (kofs + byte < p.kbytes ? kofs + byte : 0);
+        const int64_t off = r * p.ldb_bytes + (kofs + byte < kbytes_u ? kofs + byte : 0);
         load_lds_buf<16>(rb, static_cast<uint32_t>(off), sb + (j * NW + wave) * 1024);
       }
     }
@@ -879,11 +910,11 @@ gemm_kernel(GemmArgs p) {
       int64_t row, byte, off;
       if constexpr (BK) {
         maps::copy_source((j * NW + wave) * 64 * LOADW, lane, LOADW, &row, &byte);
-        off = b_off[j] + (kofs + byte < p.kbytes ? kofs : -byte);
+        off = b_off[j] + (kofs + byte < kbytes_u ? kofs : -byte);
       } else {
         maps::mm_copy_source((j * NW + wave) * 64 * LOADW, lane, LOADW, PB, &row, &byte);
         const int64_t k = 32 * static_cast<int64_t>(kt) + row;
-        off = b_off[j] - (k < p.k ? 0 : row * p.ldb_bytes);
+        off = b_off[j] - (k < kel_u ? 0 : row * p.ldb_bytes);
       }
       load_lds_buf<LOADW>(rb, static_cast<uint32_t>(off), sb + (j * NW + wave) * 64 * LOADW);
     }
@@ -1474,6 +1505,67 @@ gemm_kernel(GemmArgs p) {
     }
   };
 
+  // ---------------------------------------------------------- split K
+  // Unit (t, s) stores its partial accumulators in slot s of tile t's
+  // workspace (each lane its own 16-byte pieces, so every store instruction
+  // covers 1 KB), makes them visible device-wide, and counts its arrival on
+  // the tile's counter.  The split that arrives last (old count splits-1)
+  // reads the partials back and adds them in split order 0, 1, ...,
+  // splits-1, so the sum does not depend on which split came last; it resets
+  // the counter for the next launch and runs the epilogue.  No split waits
+  // for another, so nothing can stall.
+  __shared__ int arrival;
+  constexpr int64_t SLOT = static_cast<int64_t>(BM) * BN * 4;  // bytes of one split's partial tile
+  auto split_fixup = [&](int t, int s) -> bool {
+    uint8_t* tile_ws = p.ws + static_cast<int64_t>(t) * splits * SLOT;
+    const int64_t wave_off = static_cast<int64_t>(wave) * (TM * TN * 4) + lane * 16;
+    static_for<FM * FN>([&](auto fc) {
+      constexpr int FR = decltype(fc)::value, I = FR / FN, J = FR % FN;
+      const v16i a = __builtin_bit_cast(v16i, acc[I][J]);
+      static_for<4>([&](auto qc) {
+        constexpr int Q = decltype(qc)::value;
+        *reinterpret_cast<v4i*>(tile_ws + s * SLOT + wave_off + (FR * 4 + Q) * 1024) =
+            v4i{a[4 * Q], a[4 * Q + 1], a[4 * Q + 2], a[4 * Q + 3]};
+      });
+    });
+    __threadfence();  // release: the partial is visible device-wide before the arrival
+    __syncthreads();
+    if (threadIdx.x == 0)
+      arrival = __hip_atomic_fetch_add(p.counters + t, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int old = __builtin_amdgcn_readfirstlane(arrival);
+    if (old != splits - 1) return false;
+    __threadfence();  // acquire: the other splits' partials
+    if (threadIdx.x == 0) __hip_atomic_store(p.counters + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    static_for<FM * FN>([&](auto fc) {
+      constexpr int FR = decltype(fc)::value, I = FR / FN, J = FR % FN;
+      auto part = [&](int q) {
+        v16i v;
+        static_for<4>([&](auto qc) {
+          constexpr int Q = decltype(qc)::value;
+          const v4i w = *reinterpret_cast<const v4i*>(tile_ws + q * SLOT + wave_off + (FR * 4 + Q) * 1024);
+          v[4 * Q] = w[0];
+          v[4 * Q + 1] = w[1];
+          v[4 * Q + 2] = w[2];
+          v[4 * Q + 3] = w[3];
+        });
+        return v;
+      };
+      v16i tot = part(0);
+      for (int q = 1; q < splits; ++q) {
+        const v16i v = part(q);
+        if constexpr (T::INT) {
+          tot = tot + v;
+        } else {
+          tot = __builtin_bit_cast(v16i, __builtin_bit_cast(v16f, tot) + __builtin_bit_cast(v16f, v));
+        }
+      }
+      acc[I][J] = __builtin_bit_cast(Acc, tot);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    return true;
+  };
+
   // ---------------------------------------------------------- tile loop
   int id = static_cast<int>(blockIdx.x);
   setup(id);
@@ -1523,7 +1615,7 @@ gemm_kernel(GemmArgs p) {
       } else {
         sct[0] = 0;
       }
-      const int kvalid = p.kbytes - nkf * KB;
+      const int kvalid = kbytes_u - nkf * KB;
       read(I0{}, I0{}, I0{}, kvalid);
       mma(I0{}, I0{}, I0{}, IFM{}, sct);
       if constexpr (KSUB == 2) {
@@ -1534,23 +1626,29 @@ gemm_kernel(GemmArgs p) {
 
     __builtin_amdgcn_s_waitcnt(0);
     wg_barrier();  // every wave is done with the ring
+    // Split K: only the tile's last arriving split runs the epilogue, on the
+    // sum of every split's partial accumulators.
+    bool do_epi = true;
+    if constexpr (SPLITK) {
+      if (splits > 1) do_epi = split_fixup(unit_tile, unit_split);
+    }
     const int64_t em0 = m0, en0 = n0;
     const int next = id + static_cast<int>(gridDim.x);
     if constexpr (EP_OWN) {
-      if (next < ntiles) {
+      if (next < nunits) {
         setup(next);
         if (nkf > 0) prologue();
       }
-      epilogue(em0, en0);
+      if (do_epi) epilogue(em0, en0);
     } else {
-      epilogue(em0, en0);
-      if (next < ntiles) {
+      if (do_epi) epilogue(em0, en0);
+      if (next < nunits) {
         wg_barrier();  // the staging blocks in the ring are read
         setup(next);
         if (nkf > 0) prologue();
       }
     }
-    if (next >= ntiles) break;
+    if (next >= nunits) break;
     id = next;
   }
 }
