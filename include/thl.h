@@ -122,18 +122,17 @@ typedef struct {
  * It reads each scale row (E2M1X2) in 8-byte units up to its next 16-byte
  * boundary, as the tiled kernels read it in 16-byte groups.
  *
- * Split K: when a single problem's tiles fill at most half of the device's
- * resident workgroups (128x128 tiles, F16/BF16/I8 and the unscaled fp8
- * families, k spanning at least 16 K-steps), the K range of each tile is
- * split over 2 to 16 workgroups.  Each writes its partial fp32 (int32)
- * accumulators to a workspace; the last to finish a tile adds them in split
- * order 0, 1, 2, ... (so results do not depend on timing) and runs the
- * epilogue.  The workspace, splits * tiles * 64 KiB plus one counter per
- * tile, comes from a stream-ordered memory pool the library creates once per
- * device; it is taken and returned on `stream` around the launch, and its
- * counters are cleared by a small kernel on `stream` first.  If the pool
- * cannot provide it the problem runs unsplit.  thl_last_splits reports what
- * ran.
+ * Split K: when a single problem's tiles fill at most a quarter of the
+ * device's resident workgroups (128x128 tiles; F16, BF16, I8 and the
+ * unscaled fp8 families) and K spans at least 128 steps of 64 bytes, the K
+ * range of each tile is split over 2 to 16 workgroups.  Each split writes its
+ * partial product (fp32, or int32 for I8) to a matrix of its own, and a
+ * second kernel adds the splits' matrices in split order 0, 1, 2, ... (so
+ * results do not depend on timing) and applies the epilogue.  The matrices,
+ * splits * round_up(m, 4) * n * 4 bytes, come from a stream-ordered memory
+ * pool the library creates once per device; they are taken and returned on
+ * `stream` around the two kernels.  If the pool cannot provide them the
+ * problem runs unsplit.  thl_last_splits reports what ran.
  *
  * Ownership: A, B, C, D, bias, sfa, sfb are device pointers owned by the
  * caller; apart from the split-K workspace above the library allocates

@@ -873,10 +873,12 @@ def test_split_k_forced(case, splits):
         os.environ.pop("THL_FORCE_SPLITS", None)
 
 
-@pytest.mark.parametrize("kind,shape,want", [("bf16", (2048, 2048, 8192), 2), ("fp8", (1024, 1024, 8192), 8),
-                                             ("int8", (1024, 512, 4096), 8), ("fp16", (640, 384, 8192), 16)])
+@pytest.mark.parametrize("kind,shape,want", [("bf16", (1024, 1024, 8192), 8), ("fp8", (1024, 1024, 8192), 8),
+                                             ("int8", (1024, 512, 8192), 8), ("fp16", (640, 384, 8192), 16),
+                                             ("bf16", (2048, 2048, 8192), 1), ("int8", (1024, 512, 4096), 1)])
 def test_split_k_automatic(kind, shape, want):
-    # few tiles and a long K: thl_gemm splits K on its own
+    # few tiles and a long K: thl_gemm splits K on its own (not at 256 tiles,
+    # nor with K of 64 steps)
     import tile_hierarchy_linear_amd as thl
     import workloads as wl
 

@@ -121,15 +121,95 @@ int cu_count() {
   return n;
 }
 
-// ---- split-K workspace
-// Split K needs device memory for the partial tiles and one arrival counter
-// per tile.  thl_gemm draws it per call from a stream-ordered pool the
-// library creates once per device (memory stays in the pool between calls),
-// clears the counters with a small kernel on the stream, and returns the
-// block to the pool on the stream after the GEMM.
+// ---- split K
+// With split K each work unit writes its partial product, unscaled, to an
+// fp32 (int32) matrix of its own split; splitk_reduce then adds the splits'
+// matrices in split order 0, 1, 2, ... and applies the epilogue proper
+// (alpha and the per-tensor scales, beta*C, bias, activation, rounding to
+// D's format).  thl_gemm draws the matrices per call from a stream-ordered
+// pool the library creates once per device (memory stays in the pool
+// between calls) and returns them on the stream after the two kernels.
 
-__global__ void clear_counters(uint32_t* c, int n) {
-  for (int i = static_cast<int>(blockIdx.x * blockDim.x + threadIdx.x); i < n; i += gridDim.x * blockDim.x) c[i] = 0u;
+struct ReduceArgs {
+  const uint8_t* ws;     // the splits' matrices: column j of split s at ws + s*stride + j*ld_ws*4
+  int64_t ld_ws, stride; // elements per column, bytes per split
+  int32_t splits, m, n, int_path;
+  const void* c;
+  int64_t ldc;
+  int32_t c_type;
+  const void* bias;
+  int32_t bias_type;
+  void* d;
+  int64_t ldd;
+  int32_t d_type;
+  float alpha, beta;  // alpha holds the per-tensor fp8 scales
+  int32_t flags;
+};
+
+__device__ __forceinline__ float ld_float(const void* p, int t, int64_t i) {
+  if (t == THL_F32) return static_cast<const float*>(p)[i];
+  if (t == THL_F16) return static_cast<float>(static_cast<const _Float16*>(p)[i]);
+  return static_cast<float>(static_cast<const __bf16*>(p)[i]);
+}
+
+__device__ __forceinline__ void st_float(void* p, int t, int64_t i, float v) {
+  if (t == THL_F32) {
+    static_cast<float*>(p)[i] = v;
+  } else if (t == THL_F16) {
+    static_cast<_Float16*>(p)[i] = static_cast<_Float16>(v);
+  } else {
+    static_cast<__bf16*>(p)[i] = static_cast<__bf16>(v);
+  }
+}
+
+// One thread per 4 rows of a column, consecutive threads down the column.
+__global__ void __launch_bounds__(256) splitk_reduce(ReduceArgs r) {
+  const int64_t chunks_per_col = (r.m + 3) / 4;
+  const int64_t total = chunks_per_col * r.n;
+  for (int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; q < total;
+       q += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t j = q / chunks_per_col, i0 = (q - j * chunks_per_col) * 4;
+    const uint8_t* col = r.ws + j * r.ld_ws * 4 + i0 * 4;
+    const int rows = r.m - i0 < 4 ? static_cast<int>(r.m - i0) : 4;
+    if (r.int_path) {
+      int4 acc = *reinterpret_cast<const int4*>(col);
+      for (int s = 1; s < r.splits; ++s) {
+        const int4 v = *reinterpret_cast<const int4*>(col + s * r.stride);
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+      }
+      const int sum[4] = {acc.x, acc.y, acc.z, acc.w};
+      for (int e = 0; e < rows; ++e) {
+        const int64_t i = i0 + e;
+        int t = sum[e];
+        if (r.beta != 0.0f) t += static_cast<const int*>(r.c)[j * r.ldc + i];
+        if (r.flags & THL_EPI_BIAS) t += static_cast<const int*>(r.bias)[i];
+        if ((r.flags & THL_EPI_RELU) && t < 0) t = 0;
+        static_cast<int*>(r.d)[j * r.ldd + i] = t;
+      }
+    } else {
+      float4 acc = *reinterpret_cast<const float4*>(col);
+      for (int s = 1; s < r.splits; ++s) {
+        const float4 v = *reinterpret_cast<const float4*>(col + s * r.stride);
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+      }
+      const float sum[4] = {acc.x, acc.y, acc.z, acc.w};
+      for (int e = 0; e < rows; ++e) {
+        const int64_t i = i0 + e;
+        float t = r.alpha * sum[e];
+        if (r.beta != 0.0f) t += r.beta * ld_float(r.c, r.c_type, j * r.ldc + i);
+        if (r.flags & THL_EPI_BIAS) t += ld_float(r.bias, r.bias_type, i);
+        if (r.flags & THL_EPI_RELU) t = t > 0.0f ? t : 0.0f;
+        if (r.flags & THL_EPI_GELU) t = 0.5f * t * (1.0f + erff(t * 0.70710678118654752440f));
+        st_float(r.d, r.d_type, j * r.ldd + i, t);
+      }
+    }
+  }
 }
 
 std::mutex g_pool_mutex;
@@ -151,12 +231,6 @@ hipMemPool_t pool_for_device(int dev) {
     g_pools[dev] = pool;
   }
   return g_pools[dev];
-}
-
-// Bytes of workspace for `tiles` tiles of bm x bn split `splits` ways: the
-// partial tiles (fp32 or int32), then the counters from a 256-byte boundary.
-int64_t splitk_bytes(int64_t tiles, int splits, int bm, int bn) {
-  return tiles * splits * bm * bn * 4 + (tiles * 4 + 255) / 256 * 256;
 }
 
 int family_of(thl_dtype t) {
@@ -573,11 +647,15 @@ int64_t persistent_grid(const Variant& v, int64_t problems, int64_t max_tiles) {
 }
 
 // Splits for one problem on variant v: only the variants built with split K
-// (128x128, two workgroups per CU, unscaled families), a single problem, and
-// tiles that fill at most half the resident workgroups; as many splits as
-// fill them, at most 16, with at least 8 K-steps each.  THL_FORCE_SPLITS=<s>
-// asks for s splits on any eligible variant (tests use it to cover the path
-// at small sizes).
+// (128x128, two workgroups per CU, unscaled families) and a single problem.
+// Splitting pays when the tiles fill at most a quarter of the resident
+// workgroups and K is long (at least 128 K-steps): then as many splits as
+// fill them, at most 16, with at least 16 K-steps each.  Measured on bf16
+// and fp8 with K = 8192: 64 tiles went from 79 to 41 us (bf16) and 44 to
+// 32 us (fp8), 15 tiles from 81 to 30 us (fp16); at 256 tiles, or K of 64
+// steps, the partial matrices' traffic and the second kernel cost more than
+// the split gains.  THL_FORCE_SPLITS=<s> asks for s splits on any eligible
+// variant (tests use it to cover the path at small sizes).
 int choose_splits(const Prep& pr, const Variant& v, const Batch& bt, int64_t tiles, int64_t kbytes) {
   if (bt.count != 1 || v.tier < 0 || pr.block_scaled || v.occ != 2 || v.bm * v.bn > 128 * 128 || kbytes <= 0)
     return 1;
@@ -589,9 +667,9 @@ int choose_splits(const Prep& pr, const Variant& v, const Batch& bt, int64_t til
   }
   const int ncu = cu_count();
   const int64_t resident = static_cast<int64_t>(ncu) * v.occ;
-  if (ncu <= 0 || tiles * 2 > resident) return 1;
+  if (ncu <= 0 || tiles * 4 > resident || nk_all < 128) return 1;
   int64_t sp = resident / tiles;
-  if (sp > nk_all / 8) sp = nk_all / 8;
+  if (sp > nk_all / 16) sp = nk_all / 16;
   if (sp > 16) sp = 16;
   return sp >= 2 ? static_cast<int>(sp) : 1;
 }
@@ -646,54 +724,88 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
   const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   // Split K over workgroups when the tiles fill at most half the resident
   // workgroups: each tile's K-steps go to `splits` consecutive units.
-  const int splits = choose_splits(pr, *pick, bt, tiles, a.kbytes);
-  int64_t units = tiles;
-  uint8_t* pool_ws = nullptr;
+  int splits = choose_splits(pr, *pick, bt, tiles, a.kbytes);
+  uint8_t* ws = nullptr;
+  bool pooled = false;
+  const int64_t ld_ws = (m + 3) / 4 * 4;                      // 16-byte columns
+  const int64_t stride = (ld_ws * n * 4 + 255) / 256 * 256;  // bytes per split
   if (splits > 1) {
     const int64_t nk_all = (a.kbytes + 63) / 64;
-    a.ksteps = static_cast<int32_t>((nk_all + splits - 1) / splits);
-    a.splits = static_cast<int32_t>((nk_all + a.ksteps - 1) / a.ksteps);  // no empty split
-    units = tiles * a.splits;
-    const int64_t bytes = splitk_bytes(tiles, a.splits, pick->bm, pick->bn);
-    uint8_t* ws = nullptr;
+    const int64_t ksteps = (nk_all + splits - 1) / splits;
+    splits = static_cast<int>((nk_all + ksteps - 1) / ksteps);  // no empty split
+    a.ksteps = static_cast<int32_t>(ksteps);
+    const int64_t bytes = splits * stride;
     if (ws_mode == WS_STATIC) {
       st = static_scratch(hs, bytes, &ws);
       if (st != THL_OK) return st;
     } else {
       int dev = 0;
       hipMemPool_t pool = hipGetDevice(&dev) == hipSuccess ? pool_for_device(dev) : nullptr;
-      if (!pool || hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws), static_cast<size_t>(bytes), pool, hs) !=
-                       hipSuccess) {
+      if (pool && hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws), static_cast<size_t>(bytes), pool, hs) ==
+                      hipSuccess) {
+        pooled = true;
+      } else {
         (void)hipGetLastError();
         ws = nullptr;  // no workspace: run unsplit
       }
-      pool_ws = ws;
     }
-    if (ws) {
-      a.ws = ws;
-      a.counters = reinterpret_cast<uint32_t*>(ws + tiles * a.splits * pick->bm * pick->bn * 4);
-      if (pool_ws) {
-        const int nt = static_cast<int>(tiles);
-        hipLaunchKernelGGL(clear_counters, dim3((nt + 255) / 256), dim3(256), 0, hs, a.counters, nt);
-        if (hipGetLastError() != hipSuccess) {
-          (void)hipFreeAsync(pool_ws, hs);
-          return THL_ERR_HIP;
-        }
-      }
-    } else {
-      a.splits = 1;
-      a.ksteps = 0;
-      units = tiles;
-    }
+    if (!ws) splits = 1;
   }
+  const int64_t units = tiles * splits;
   // Persistent workgroups; each walks units blockIdx.x, + gridDim.x, ...
   const int64_t grid = persistent_grid(*pick, bt.count, units);
-  if (grid <= 0) return THL_ERR_HIP;
-  const hipError_t le = pick->launch(a, dim3(static_cast<unsigned>(grid), static_cast<unsigned>(bt.count)), hs);
-  if (pool_ws) (void)hipFreeAsync(pool_ws, hs);  // back to the pool once the GEMM has run
+  if (grid <= 0) {
+    if (pooled) (void)hipFreeAsync(ws, hs);
+    return THL_ERR_HIP;
+  }
+  hipError_t le;
+  if (splits > 1) {
+    // the splits' partial products, unscaled, to the workspace ...
+    GemmArgs ap = a;
+    ap.splits = splits;
+    ap.split_stride = stride;
+    ap.d = ws;
+    ap.ldd = ld_ws;
+    ap.d_type = pr.int_path ? THL_I32 : THL_F32;
+    ap.c = nullptr;
+    ap.bias = nullptr;
+    ap.alpha = 1.0f;
+    ap.beta = 0.0f;
+    ap.flags = pr.int_path ? 0 : EPI_VEC;
+    le = pick->launch(ap, dim3(static_cast<unsigned>(grid), 1u), hs);
+    // ... then their sum in split order through the epilogue
+    if (le == hipSuccess) {
+      ReduceArgs r{};
+      r.ws = ws;
+      r.ld_ws = ld_ws;
+      r.stride = stride;
+      r.splits = splits;
+      r.m = a.m;
+      r.n = a.n;
+      r.int_path = pr.int_path ? 1 : 0;
+      r.c = a.c;
+      r.ldc = a.ldc;
+      r.c_type = a.c_type;
+      r.bias = a.bias;
+      r.bias_type = a.bias_type;
+      r.d = a.d;
+      r.ldd = a.ldd;
+      r.d_type = a.d_type;
+      r.alpha = a.alpha;
+      r.beta = a.beta;
+      r.flags = static_cast<int32_t>(pr.flags);
+      const int64_t chunks = (m + 3) / 4 * n;
+      const int64_t blocks = (chunks + 255) / 256 < 4096 ? (chunks + 255) / 256 : 4096;
+      hipLaunchKernelGGL(splitk_reduce, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, hs, r);
+      le = hipGetLastError();
+    }
+  } else {
+    le = pick->launch(a, dim3(static_cast<unsigned>(grid), static_cast<unsigned>(bt.count)), hs);
+  }
+  if (pooled) (void)hipFreeAsync(ws, hs);  // back to the pool once the kernels have run
   if (le != hipSuccess) return THL_ERR_HIP;
   t_last_variant = pick->name;
-  last_splits = a.splits > 1 ? a.splits : 1;
+  last_splits = splits;
   return THL_OK;
 }
 

@@ -70,12 +70,10 @@ struct GemmArgs {
   const GroupProblem* group;
   int32_t elem_bits_a, elem_bits_b;
   // Split K across workgroups: `splits` units per tile (1: none), each over
-  // `ksteps` 64-byte K-steps from its split's first; partial accumulators in
-  // `ws` (splits slots of BM*BN*4 bytes per tile), one arrival counter per
-  // tile in `counters` (zero before the launch, left zero after it).
+  // `ksteps` 64-byte K-steps from its split's first, writing its partial
+  // product to D + split * split_stride bytes.
   int32_t splits, ksteps;
-  uint8_t* ws;
-  uint32_t* counters;
+  int64_t split_stride;
 };
 
 

@@ -626,7 +626,10 @@ gemm_kernel(GemmArgs p) {
   // Split K: work unit u is split u % splits of tile u / splits and covers
   // p.ksteps K-steps from the split's first (the last split keeps the
   // partial step); without it, one unit per tile.  nk, nkf, kbytes_u and
-  // kel_u describe the current unit's K range.
+  // kel_u describe the current unit's K range.  Each split writes its
+  // partial product, unscaled, to a matrix of its own: D here is the first
+  // of `splits` fp32 (int32) matrices p.split_stride bytes apart, which a
+  // second kernel adds in split order before the epilogue proper.
   // Split K is built into the 128x128 two-workgroup variants of the unscaled
   // families (the tiles chosen when a problem has few); elsewhere splits is 1.
   constexpr bool SPLITK = OCC == 2 && BM * BN <= 128 * 128 && !T::SCALED;
@@ -638,6 +641,7 @@ gemm_kernel(GemmArgs p) {
   int kbytes_u = p.kbytes; // bytes of K per operand row in the unit
   int kel_u = p.k;         // elements of K in the unit
   int unit_tile = 0, unit_split = 0;
+  void* d_unit = p.d;  // the current unit's output matrix
   const int64_t a_step = AK ? KB : 32 * p.lda_bytes;  // operand advance per K-step
   const int64_t b_step = BK ? KB : 32 * p.ldb_bytes;
   const int nkb = p.k >> 5;
@@ -687,6 +691,7 @@ gemm_kernel(GemmArgs p) {
       nkf = kbytes_u / KB;
       a_tile += kbeg * a_step;
       b_tile += kbeg * b_step;
+      d_unit = static_cast<uint8_t*>(p.d) + unit_split * p.split_stride;
     }
 #pragma unroll
     for (int j = 0; j < A_LOADS; ++j) {
@@ -1245,7 +1250,7 @@ gemm_kernel(GemmArgs p) {
     });
     ep += (wave % WPS) * EPB;
   }
-  auto epilogue_gen = [&](const int64_t em0, const int64_t en0) {
+  auto epilogue_gen = [&](const int64_t em0, const int64_t en0, void* const dst) {
     int ln = lane;  // opaque copy, as in epilogue_vec below
     asm volatile("" : "+v"(ln));
     const int erow = (ln % LPC) * 8;
@@ -1296,7 +1301,7 @@ gemm_kernel(GemmArgs p) {
   #pragma unroll
               for (int r = 0; r < 8; ++r) t[r] = t[r] < 0 ? 0 : t[r];
             }
-            store8_i(p.d, n * p.ldd + m, t, rows);
+            store8_i(dst, n * p.ldd + m, t, rows);
           } else {
             const v4f lof = __builtin_bit_cast(v4f, lo), hif = __builtin_bit_cast(v4f, hi);
             float t[8];
@@ -1316,7 +1321,7 @@ gemm_kernel(GemmArgs p) {
             }
   #pragma unroll
             for (int r = 0; r < 8; ++r) t[r] = activate(t[r], p.flags);
-            store8_f(p.d, p.d_type, n * p.ldd + m, t, rows);
+            store8_f(dst, p.d_type, n * p.ldd + m, t, rows);
           }
         }
       }
@@ -1358,7 +1363,7 @@ gemm_kernel(GemmArgs p) {
     // program order.
     asm volatile("" ::: "memory");
   };
-  auto epilogue_vec = [&](const int64_t em0, const int64_t en0, auto ld_tag, auto bf_tag) {
+  auto epilogue_vec = [&](const int64_t em0, const int64_t en0, void* const dst, auto ld_tag, auto bf_tag) {
     constexpr bool LD = decltype(ld_tag)::value, BF = decltype(bf_tag)::value;
     // The lane index passes through an opaque copy so that the per-lane
     // addresses below are computed here rather than hoisted out of the tile
@@ -1382,7 +1387,7 @@ gemm_kernel(GemmArgs p) {
     const uint8_t* bbase = static_cast<const uint8_t*>(p.bias) + (has_bias ? tm0 * bs : 0);
     const auto rb = make_rsrc_u(bbase, has_bias ? -1 : 0), rb2 = make_rsrc_u(bbase, has_bias && bias32 ? -1 : 0);
     const int ds = d32 ? 4 : 2;
-    const auto rd = make_rsrc_u(static_cast<uint8_t*>(p.d) + (tn0 * p.ldd + tm0) * ds, -1);
+    const auto rd = make_rsrc_u(static_cast<uint8_t*>(dst) + (tn0 * p.ldd + tm0) * ds, -1);
     const int lddb = static_cast<int>(p.ldd) * ds;
     const uint32_t vd = static_cast<uint32_t>(cl * lddb + erow * ds);
     const float alpha = p.alpha, beta = p.beta;
@@ -1465,23 +1470,23 @@ gemm_kernel(GemmArgs p) {
   // staging: it is built where that fits without spilling (one workgroup per
   // CU, or the 128x128 two-workgroup variant with 16-byte copies).
   constexpr bool VEC_EPI = !T::INT && (OCC == 1 || (BM * BN <= 128 * 128 && LOADW == 16));
-  auto epilogue = [&](const int64_t em0, const int64_t en0) {
+  auto epilogue = [&](const int64_t em0, const int64_t en0, void* const dst) {
     if constexpr (VEC_EPI) {
       if ((p.flags & EPI_VEC) && !(p.flags & EPI_GELU) && em0 + BM <= p.m && en0 + BN <= p.n) {
         const bool has_c = nonzero_f32(p.beta), has_bias = (p.flags & EPI_BIAS) != 0;
         const bool bf = (!has_c || p.c_type == DT_BF16) && p.d_type == DT_BF16 &&
                         (!has_bias || p.bias_type == DT_BF16);
         if (!bf) {
-          epilogue_vec(em0, en0, std::true_type{}, std::false_type{});
+          epilogue_vec(em0, en0, dst, std::true_type{}, std::false_type{});
         } else if (has_c || has_bias) {
-          epilogue_vec(em0, en0, std::true_type{}, std::true_type{});
+          epilogue_vec(em0, en0, dst, std::true_type{}, std::true_type{});
         } else {
-          epilogue_vec(em0, en0, std::false_type{}, std::true_type{});
+          epilogue_vec(em0, en0, dst, std::false_type{}, std::true_type{});
         }
         return;
       }
     }
-    epilogue_gen(em0, en0);
+    epilogue_gen(em0, en0, dst);
   };
 
   // First stages of the current tile.
@@ -1503,67 +1508,6 @@ gemm_kernel(GemmArgs p) {
         issue_full(S < nkf ? S : nkf - 1, std::integral_constant<int, S>{}, std::integral_constant<int, S>{});
       });
     }
-  };
-
-  // ---------------------------------------------------------- split K
-  // Unit (t, s) stores its partial accumulators in slot s of tile t's
-  // workspace (each lane its own 16-byte pieces, so every store instruction
-  // covers 1 KB), makes them visible device-wide, and counts its arrival on
-  // the tile's counter.  The split that arrives last (old count splits-1)
-  // reads the partials back and adds them in split order 0, 1, ...,
-  // splits-1, so the sum does not depend on which split came last; it resets
-  // the counter for the next launch and runs the epilogue.  No split waits
-  // for another, so nothing can stall.
-  __shared__ int arrival;
-  constexpr int64_t SLOT = static_cast<int64_t>(BM) * BN * 4;  // bytes of one split's partial tile
-  auto split_fixup = [&](int t, int s) -> bool {
-    uint8_t* tile_ws = p.ws + static_cast<int64_t>(t) * splits * SLOT;
-    const int64_t wave_off = static_cast<int64_t>(wave) * (TM * TN * 4) + lane * 16;
-    static_for<FM * FN>([&](auto fc) {
-      constexpr int FR = decltype(fc)::value, I = FR / FN, J = FR % FN;
-      const v16i a = __builtin_bit_cast(v16i, acc[I][J]);
-      static_for<4>([&](auto qc) {
-        constexpr int Q = decltype(qc)::value;
-        *reinterpret_cast<v4i*>(tile_ws + s * SLOT + wave_off + (FR * 4 + Q) * 1024) =
-            v4i{a[4 * Q], a[4 * Q + 1], a[4 * Q + 2], a[4 * Q + 3]};
-      });
-    });
-    __threadfence();  // release: the partial is visible device-wide before the arrival
-    __syncthreads();
-    if (threadIdx.x == 0)
-      arrival = __hip_atomic_fetch_add(p.counters + t, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    const int old = __builtin_amdgcn_readfirstlane(arrival);
-    if (old != splits - 1) return false;
-    __threadfence();  // acquire: the other splits' partials
-    if (threadIdx.x == 0) __hip_atomic_store(p.counters + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    static_for<FM * FN>([&](auto fc) {
-      constexpr int FR = decltype(fc)::value, I = FR / FN, J = FR % FN;
-      auto part = [&](int q) {
-        v16i v;
-        static_for<4>([&](auto qc) {
-          constexpr int Q = decltype(qc)::value;
-          const v4i w = *reinterpret_cast<const v4i*>(tile_ws + q * SLOT + wave_off + (FR * 4 + Q) * 1024);
-          v[4 * Q] = w[0];
-          v[4 * Q + 1] = w[1];
-          v[4 * Q + 2] = w[2];
-          v[4 * Q + 3] = w[3];
-        });
-        return v;
-      };
-      v16i tot = part(0);
-      for (int q = 1; q < splits; ++q) {
-        const v16i v = part(q);
-        if constexpr (T::INT) {
-          tot = tot + v;
-        } else {
-          tot = __builtin_bit_cast(v16i, __builtin_bit_cast(v16f, tot) + __builtin_bit_cast(v16f, v));
-        }
-      }
-      acc[I][J] = __builtin_bit_cast(Acc, tot);
-      __builtin_amdgcn_sched_barrier(0);
-    });
-    return true;
   };
 
   // ---------------------------------------------------------- tile loop
@@ -1626,22 +1570,17 @@ gemm_kernel(GemmArgs p) {
 
     __builtin_amdgcn_s_waitcnt(0);
     wg_barrier();  // every wave is done with the ring
-    // Split K: only the tile's last arriving split runs the epilogue, on the
-    // sum of every split's partial accumulators.
-    bool do_epi = true;
-    if constexpr (SPLITK) {
-      if (splits > 1) do_epi = split_fixup(unit_tile, unit_split);
-    }
     const int64_t em0 = m0, en0 = n0;
+    void* const d_ep = d_unit;  // (setup of the next unit moves d_unit)
     const int next = id + static_cast<int>(gridDim.x);
     if constexpr (EP_OWN) {
       if (next < nunits) {
         setup(next);
         if (nkf > 0) prologue();
       }
-      if (do_epi) epilogue(em0, en0);
+      epilogue(em0, en0, d_ep);
     } else {
-      if (do_epi) epilogue(em0, en0);
+      epilogue(em0, en0, d_ep);
       if (next < nunits) {
         wg_barrier();  // the staging blocks in the ring are read
         setup(next);
