@@ -42,7 +42,8 @@ typedef enum {
   THL_ERR_UNSUPPORTED = -2, /* a dtype / op / epilogue / scale combination that is not built */
   THL_ERR_MISALIGNED = -3,  /* a pointer or leading dimension breaks every kernel's alignment */
   THL_ERR_HIP = -4,         /* the HIP runtime reported an error while launching */
-  THL_ERR_UNDEFINED = -5    /* layout algebra: the operation is undefined (divisibility, overlap) */
+  THL_ERR_UNDEFINED = -5,   /* layout algebra: the operation is undefined (divisibility, overlap) */
+  THL_ERR_SCRATCH = -6      /* thl_gemm_noalloc: the call needs more than its static scratch */
 } thl_status;
 
 /* op(X): N = X as stored, T = its transpose (BLAS convention). */
@@ -165,6 +166,32 @@ thl_status thl_gemm(int64_t m, int64_t n, int64_t k,
                     float alpha, float beta,
                     const thl_dtypes* dtypes, const thl_epilogue* epilogue,
                     const thl_scales* scales, struct ihipStream_t* stream);
+
+/*
+ * thl_gemm_noalloc -- thl_gemm for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same arguments, rules and results as thl_gemm; it calls
+ * no allocating routine.  Where thl_gemm would split K, the partial matrices
+ * go to a static device array of the library (40 MiB, one per GPU, held
+ * until the process ends) instead of a pool allocation.  Its address is read
+ * once per device, with that device current, at the first call on it.
+ * Nothing in the array needs to start at any value: each call writes every
+ * partial element it reads.
+ * Limit: a call whose split needs more than 40 MiB returns THL_ERR_SCRATCH
+ * with nothing enqueued (the splits thl_gemm chooses by itself always fit;
+ * only a split count forced through THL_FORCE_SPLITS can exceed it).
+ * Concurrency: every call on one GPU uses that GPU's one array, so calls that
+ * overlap in time on that GPU (on different streams, or from different
+ * threads) race; calls ordered on one stream do not.
+ */
+thl_status thl_gemm_noalloc(int64_t m, int64_t n, int64_t k,
+                            const void* A, int64_t lda, thl_op opA,
+                            const void* B, int64_t ldb, thl_op opB,
+                            const void* C, int64_t ldc,
+                            void* D, int64_t ldd,
+                            float alpha, float beta,
+                            const thl_dtypes* dtypes, const thl_epilogue* epilogue,
+                            const thl_scales* scales, struct ihipStream_t* stream);
 
 /*
  * thl_gemm_batched -- `batch` independent problems of one shape in one launch

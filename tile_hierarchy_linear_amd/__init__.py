@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libthl.so")
 
 THL_OK, THL_ERR_INVALID, THL_ERR_UNSUPPORTED, THL_ERR_MISALIGNED, THL_ERR_HIP, THL_ERR_UNDEFINED = (
     0, -1, -2, -3, -4, -5)
+THL_ERR_SCRATCH = -6
 THL_OP_N, THL_OP_T = 0, 1
 DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3, "i32": 4, "e4m3": 5, "e2m1": 6, "e8m0": 7, "none": 8, "e5m2": 9}
 THL_EPI_NONE, THL_EPI_BIAS, THL_EPI_RELU, THL_EPI_GELU = 0, 1, 2, 4
@@ -69,6 +70,8 @@ def _load():
                              ctypes.c_float, ctypes.c_float, ctypes.POINTER(thl_dtypes),
                              ctypes.POINTER(thl_epilogue), ctypes.POINTER(thl_scales), vp]
     lib.thl_gemm.restype = ctypes.c_int
+    lib.thl_gemm_noalloc.argtypes = lib.thl_gemm.argtypes
+    lib.thl_gemm_noalloc.restype = ctypes.c_int
     lib.thl_gemm_batched.argtypes = [i64, i64, i64, i64, vp, i64, i64, ctypes.c_int, vp, i64, i64, ctypes.c_int,
                                      vp, i64, i64, vp, i64, i64, ctypes.c_float, ctypes.c_float,
                                      ctypes.POINTER(thl_dtypes), ctypes.POINTER(thl_epilogue), i64,
@@ -163,6 +166,17 @@ def thl_gemm(m, n, k, A, lda, opA, B, ldb, opB, C, ldc, D, ldd, alpha, beta, dty
                              int(ldd), float(alpha), float(beta), ctypes.byref(dtypes),
                              ctypes.byref(epilogue) if epilogue is not None else None,
                              ctypes.byref(scales) if scales is not None else None, stream))
+
+
+def thl_gemm_noalloc(m, n, k, A, lda, opA, B, ldb, opB, C, ldc, D, ldd, alpha, beta, dtypes, epilogue=None,
+                     scales=None, stream=None) -> int:
+    """Direct call of the no-allocation C entry point (arguments as for thl_gemm)."""
+    opa = THL_OP_T if opA in ("T", THL_OP_T) else (THL_OP_N if opA in ("N", THL_OP_N) else int(opA))
+    opb = THL_OP_T if opB in ("T", THL_OP_T) else (THL_OP_N if opB in ("N", THL_OP_N) else int(opB))
+    return int(_lib.thl_gemm_noalloc(int(m), int(n), int(k), A, int(lda), opa, B, int(ldb), opb, C, int(ldc), D,
+                                     int(ldd), float(alpha), float(beta), ctypes.byref(dtypes),
+                                     ctypes.byref(epilogue) if epilogue is not None else None,
+                                     ctypes.byref(scales) if scales is not None else None, stream))
 
 
 def thl_gemm_batched(batch, m, n, k, A, lda, stride_a, opA, B, ldb, stride_b, opB, C, ldc, stride_c, D, ldd,

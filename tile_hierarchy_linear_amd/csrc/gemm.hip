@@ -343,6 +343,8 @@ const char* thl_status_string(int s) {
       return "THL_ERR_HIP: the HIP runtime reported a launch error";
     case THL_ERR_UNDEFINED:
       return "THL_ERR_UNDEFINED: layout operation undefined (divisibility or overlap)";
+    case THL_ERR_SCRATCH:
+      return "THL_ERR_SCRATCH: the call needs more than the no-allocation entry point's 40 MiB of scratch";
     default:
       return "unknown status";
   }
@@ -361,6 +363,14 @@ thl_status thl_gemm(int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
                     float beta, const thl_dtypes* dt, const thl_epilogue* epi, const thl_scales* sc,
                     struct ihipStream_t* stream) {
   return gemm_impl(Batch{}, m, n, k, A, lda, opA, B, ldb, opB, C, ldc, D, ldd, alpha, beta, dt, epi, sc, stream, WS_POOL);
+}
+
+thl_status thl_gemm_noalloc(int64_t m, int64_t n, int64_t k, const void* A, int64_t lda, thl_op opA, const void* B,
+                            int64_t ldb, thl_op opB, const void* C, int64_t ldc, void* D, int64_t ldd, float alpha,
+                            float beta, const thl_dtypes* dt, const thl_epilogue* epi, const thl_scales* sc,
+                            struct ihipStream_t* stream) {
+  return gemm_impl(Batch{}, m, n, k, A, lda, opA, B, ldb, opB, C, ldc, D, ldd, alpha, beta, dt, epi, sc, stream,
+                   WS_STATIC);
 }
 
 thl_status thl_gemm_batched(int64_t batch, int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
@@ -933,7 +943,43 @@ thl_status grouped_impl(int64_t count, const thl_group_problem* pb, const thl_gr
   return THL_OK;
 }
 
-thl_status static_scratch(hipStream_t, int64_t, uint8_t**) { return THL_ERR_UNSUPPORTED; }
+}  // namespace
+}  // namespace thl
+
+// The no-allocation entry point's scratch: the split-K partial matrices.  The
+// split rule bounds them by splits * tiles * 128 * 128 * 4 bytes with
+// splits * tiles at most the 512 resident 128x128 workgroups, i.e. 32 MiB plus
+// the rounding of m to 4 rows and of each split to 256 bytes; 40 MiB holds
+// every split thl_gemm would choose.  Each GPU keeps its copy until the
+// process ends.
+static constexpr int64_t kScratchBytes = INT64_C(40) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace thl {
+namespace {
+
+// The scratch array's device address on each device, read once per device
+// (with that device current) at its first no-allocation call.  In host code
+// the array's name is only a stand-in: kernels get this address.
+std::mutex g_scratch_mutex;
+uint8_t* g_scratch_ptr[64];
+
+thl_status static_scratch(hipStream_t, int64_t bytes, uint8_t** out) {
+  if (bytes > kScratchBytes) return THL_ERR_SCRATCH;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return THL_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return THL_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = static_cast<uint8_t*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return THL_OK;
+}
 
 }  // namespace
 }  // namespace thl

@@ -36,7 +36,9 @@ class DeviceProblem:
         else:
             self.d.fill_(d_fill)
 
-    def run(self, stream=None, d=None, c=None, ldc=None):
+    def run(self, stream=None, d=None, c=None, ldc=None, entry=None):
+        """Run through thl_gemm (or `entry`, an entry point of the same
+        arguments, e.g. thl.thl_gemm_noalloc)."""
         w = self.w
         dt = thl.make_dtypes(w.type_a, w.type_b, w.type_c, w.type_d,
                              w.type_bias if w.bias is not None else "none")
@@ -50,12 +52,11 @@ class DeviceProblem:
             stream = torch.cuda.current_stream().cuda_stream
         dd = self.d if d is None else d
         cc = self.c if c is None else c
-        status = thl.thl_gemm(w.m, w.n, w.k, self.a.data_ptr() if self.a is not None and self.a.numel() else None,
-                              w.lda, w.op_a,
-                              self.b.data_ptr() if self.b is not None and self.b.numel() else None, w.ldb,
-                              w.op_b, cc.data_ptr() if cc is not None else None,
-                              ldc or w.ldc or max(1, w.m), dd.data_ptr(), self.ldd, w.alpha, w.beta, dt, epi,
-                              sc, stream)
+        a_ptr = self.a.data_ptr() if self.a is not None and self.a.numel() else None
+        b_ptr = self.b.data_ptr() if self.b is not None and self.b.numel() else None
+        status = (entry or thl.thl_gemm)(w.m, w.n, w.k, a_ptr, w.lda, w.op_a, b_ptr, w.ldb, w.op_b,
+                                         cc.data_ptr() if cc is not None else None, ldc or w.ldc or max(1, w.m),
+                                         dd.data_ptr(), self.ldd, w.alpha, w.beta, dt, epi, sc, stream)
         return status
 
     def d_values(self, rows, cols) -> np.ndarray:
