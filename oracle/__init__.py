@@ -80,6 +80,9 @@ def _load():
                                       ctypes.c_void_p]
         lib.oracle_decode.restype = ctypes.c_int
         lib.oracle_max_threads.restype = ctypes.c_int
+        lib.oracle_mx_quantize.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                           ctypes.c_void_p]
+        lib.oracle_mx_quantize.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -167,3 +170,34 @@ def gemm_full(prob: dict, nthreads: int = 0) -> np.ndarray:
     m, n = int(prob["m"]), int(prob["n"])
     jj, ii = np.meshgrid(np.arange(n), np.arange(m))
     return gemm_elements(prob, ii.ravel(), jj.ravel(), nthreads).reshape(m, n)
+
+
+def mx_quantize_block(values, fmt: str):
+    """OCP MX quantization of one block (1 .. 32 values) to ``fmt`` ('e2m1',
+    'e4m3' or 'e5m2'): returns (element codes as a uint8 array, E8M0 scale
+    code)."""
+    vals = np.ascontiguousarray(np.asarray(values, dtype=np.float64))
+    codes = np.zeros(vals.size, dtype=np.uint8)
+    scale = np.zeros(1, dtype=np.uint8)
+    rc = _load().oracle_mx_quantize(TYPE_CODES[fmt], _ptr(vals), vals.size, _ptr(codes), _ptr(scale))
+    if rc != 0:
+        raise ValueError("oracle rejected the block")
+    return codes, int(scale[0])
+
+
+def mx_quantize_columns(y, fmt: str, block: int = 32):
+    """MX output of an (m, n) array of values: each column cut into blocks of
+    ``block`` consecutive rows (the last possibly shorter), each block
+    quantized by mx_quantize_block.  Returns (codes (m, n) uint8, scales
+    (ceil(m/block), n) uint8)."""
+    y = np.asarray(y, dtype=np.float64)
+    m, n = y.shape
+    nb = (m + block - 1) // block
+    codes = np.zeros((m, n), dtype=np.uint8)
+    scales = np.zeros((nb, n), dtype=np.uint8)
+    for j in range(n):
+        for b in range(nb):
+            c, s = mx_quantize_block(y[b * block: (b + 1) * block, j], fmt)
+            codes[b * block: b * block + c.size, j] = c
+            scales[b, j] = s
+    return codes, scales

@@ -334,6 +334,88 @@ int oracle_gemm_elements(const oracle_problem *p, int64_t count, const int64_t *
     return 0;
 }
 
+/* ------------------------------------------------------- MX output blocks */
+
+/*
+ * OCP MX quantization of one block of values (the output side of a
+ * block-scaled GEMM: "Technical Documentation: NVIDIA/cutlass", "Blackwell
+ * SM100 GEMMs", "Building a Block Scaled Kernel", where the epilogue writes
+ * elements plus one scale factor per SFDVectorSize outputs; the rule that
+ * turns a block into a scale and elements is the OCP MX format's, which the
+ * pages' block-scaled type table points to):
+ *
+ *   amax = max |v|;  X = floor(log2(amax)) - emax   (emax: the element
+ *   format's largest exponent: 2 for E2M1, 8 for E4M3, 15 for E5M2),
+ *   clamped to [-127, 127];  scale code = X + 127 (E8M0);
+ *   element = the representable value nearest to v / 2^X, ties to the even
+ *   code, magnitudes above the largest finite value clamped to it.
+ *   A block of zeros gets scale code 0 and zero elements.  Every element
+ *   keeps the sign of its value, also when it rounds to zero.
+ *
+ * fmt is ORC_E2M1, ORC_E4M3 or ORC_E5M2; codes[t] receives element t's code
+ * (4 bits for E2M1, sign in bit 3; 8 bits otherwise).  Returns 0, or -1 for
+ * an unknown format or count outside 1..32.
+ */
+int oracle_mx_quantize(int32_t fmt, const double *vals, int64_t count, uint8_t *codes, uint8_t *scale)
+{
+    int emax, ncodes, sign_bit;
+    if (fmt == ORC_E2M1) {
+        emax = 2; ncodes = 8; sign_bit = 3;
+    } else if (fmt == ORC_E4M3) {
+        emax = 8; ncodes = 127; sign_bit = 7; /* 0x7f is NaN */
+    } else if (fmt == ORC_E5M2) {
+        emax = 15; ncodes = 124; sign_bit = 7; /* 0x7c.. are Inf/NaN */
+    } else {
+        return -1;
+    }
+    if (count < 1 || count > 32)
+        return -1;
+    double amax = 0.0;
+    for (int64_t t = 0; t < count; ++t)
+        if (fabs(vals[t]) > amax)
+            amax = fabs(vals[t]);
+    if (amax == 0.0) {
+        *scale = 0;
+        for (int64_t t = 0; t < count; ++t)
+            codes[t] = (uint8_t)(signbit(vals[t]) ? (1 << sign_bit) : 0);
+        return 0;
+    }
+    int x = (int)floor(log2(amax)) - emax;
+    /* log2 of an exact power of two is exact; guard the floor against a
+     * result just below an integer for values just below a power of two */
+    if (ldexp(1.0, x + emax + 1) <= amax)
+        x += 1;
+    else if (ldexp(1.0, x + emax) > amax)
+        x -= 1;
+    if (x < -127)
+        x = -127;
+    if (x > 127)
+        x = 127;
+    *scale = (uint8_t)(x + 127);
+    for (int64_t t = 0; t < count; ++t) {
+        double a = fabs(vals[t]) / ldexp(1.0, x);
+        /* nearest non-negative code by magnitude; the codes 0 .. ncodes-1
+         * are in increasing order of value, and ncodes-1 is the largest
+         * finite one, which every larger magnitude clamps to */
+        int best = ncodes - 1;
+        double top = fmt == ORC_E2M1 ? dec_e2m1((unsigned)best) : (fmt == ORC_E4M3 ? dec_e4m3((uint8_t)best)
+                                                                                   : dec_e5m2((uint8_t)best));
+        double best_err = INFINITY;
+        for (int c = 0; c < ncodes && a < top; ++c) {
+            double v = fmt == ORC_E2M1 ? dec_e2m1((unsigned)c) : (fmt == ORC_E4M3 ? dec_e4m3((uint8_t)c)
+                                                                                  : dec_e5m2((uint8_t)c));
+            double err = fabs(v - a);
+            if (err < best_err || (err == best_err && (c & 1) == 0)) {
+                best = c;
+                best_err = err;
+            }
+        }
+        /* the sign is kept, also when the magnitude rounds to zero */
+        codes[t] = (uint8_t)(best | (signbit(vals[t]) ? (1 << sign_bit) : 0));
+    }
+    return 0;
+}
+
 /* Number of threads an OpenMP region would use here (for reporting). */
 int oracle_max_threads(void)
 {

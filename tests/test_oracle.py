@@ -604,3 +604,104 @@ def test_fp32_accumulation_stays_well_inside_the_bound():
     f32 = (a.astype(np.float32) @ b.astype(np.float32)).astype(np.float64)
     bound = 2.0 ** -20 * w.k * np.abs(a).max() * np.abs(b).max()
     assert np.abs(f32 - ref).max() < bound / 8
+
+
+# ------------------------------------------------------------- MX output blocks
+
+def test_mx_all_equal_block():
+    # 32 x 1.0: amax 1, X = 0 - emax; every element is 2^emax in the format
+    for fmt, emax, code in (("e2m1", 2, 0x6), ("e4m3", 8, 0x78), ("e5m2", 15, 0x78)):
+        codes, sc = oracle.mx_quantize_block([1.0] * 32, fmt)
+        assert sc == 127 - emax and (codes == code).all(), (fmt, sc, codes)
+
+
+def test_mx_e2m1_ties_go_to_the_even_code_and_large_values_saturate():
+    # amax 7 -> X = floor(log2 7) - 2 = 0: values are quantized as they are.
+    vals = [7.0, 5.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, -3.5, 6.0, -0.5, 0.1]
+    codes, sc = oracle.mx_quantize_block(vals, "e2m1")
+    assert sc == 127
+    # 7 -> 6 (clamped); 5 -> 4; 0.25 -> 0; 0.75 -> 1; 1.25 -> 1; 1.75 -> 2; 2.5 -> 2;
+    # 3.5 -> 4; -3.5 -> -4; 6 -> 6; -0.5 -> -0.5; 0.1 -> 0
+    assert codes.tolist() == [0x7, 0x6, 0x0, 0x2, 0x2, 0x4, 0x4, 0x6, 0xE, 0x7, 0x9, 0x0]
+
+
+def test_mx_scale_follows_the_binade_of_amax():
+    # just below a power of two stays in the lower binade; the power itself moves up
+    _, s1 = oracle.mx_quantize_block([8.0 - 2.0 ** -20, 1.0], "e2m1")
+    _, s2 = oracle.mx_quantize_block([8.0, 1.0], "e2m1")
+    _, s3 = oracle.mx_quantize_block([-8.0, 1.0], "e2m1")
+    assert (s1, s2, s3) == (127, 128, 128)
+    # the scale code saturates at both ends of E8M0
+    c_hi, s_hi = oracle.mx_quantize_block([2.0 ** 200, -(2.0 ** 199)], "e2m1")
+    c_lo, s_lo = oracle.mx_quantize_block([2.0 ** -200, -(2.0 ** -201)], "e2m1")
+    assert s_hi == 254 and c_hi.tolist() == [0x7, 0xF]  # 2^73 and -2^72 clamp to +-6
+    assert s_lo == 0 and c_lo.tolist() == [0x0, 0x8]    # far below the smallest element: signed zeros
+
+
+def test_mx_zero_block():
+    codes, sc = oracle.mx_quantize_block([0.0, -0.0, 0.0], "e4m3")
+    assert sc == 0 and codes.tolist() == [0x00, 0x80, 0x00]
+
+
+def test_mx_e4m3_subnormal_elements():
+    # amax 1 -> X = -8; 2^-17 / 2^-8 = 2^-9 is E4M3's smallest subnormal (code 1);
+    # 1.5 * 2^-9 is a tie between codes 1 and 2 -> 2; 448.5 * 2^-8 clamps to 448 (0x7E)
+    codes, sc = oracle.mx_quantize_block([1.0, 2.0 ** -17, 1.5 * 2.0 ** -17, 2.0 ** -30], "e4m3")
+    assert sc == 119 and codes.tolist() == [0x78, 0x01, 0x02, 0x00]
+    codes, sc = oracle.mx_quantize_block([511.0 * 2.0 ** -8, 1.0], "e4m3")
+    assert sc == 119 and codes.tolist() == [0x7E, 0x78]
+
+
+def test_mx_e5m2_saturates_below_its_infinity():
+    # amax 65535 -> X = 15 - 15 = 0: 65535 clamps to 57344 (0x7B), never to the Inf code 0x7C
+    codes, sc = oracle.mx_quantize_block([65535.0, -40000.0, 1.0], "e5m2")
+    assert sc == 127 and codes.tolist() == [0x7B, 0xF9, 0x3C]
+
+
+@pytest.mark.parametrize("fmt", ["e2m1", "e4m3", "e5m2"])
+def test_mx_blocks_dequantize_within_half_a_step(fmt):
+    # every element dequantizes to within half the element grid's spacing at
+    # its magnitude (times 2^X), except values above the largest element,
+    # which clamp to it; and the scale puts amax in the top binade
+    top = {"e2m1": 6.0, "e4m3": 448.0, "e5m2": 57344.0}[fmt]
+    emax = {"e2m1": 2, "e4m3": 8, "e5m2": 15}[fmt]
+    dec = {"e2m1": lambda c: oracle.decode("e2m1", np.array([c | (c << 4)], np.uint8))[0],
+           "e4m3": lambda c: oracle.decode("e4m3", np.array([c], np.uint8))[0],
+           "e5m2": lambda c: oracle.decode("e5m2", np.array([c], np.uint8))[0]}[fmt]
+    mags = [abs(dec(c)) for c in range(8 if fmt == "e2m1" else 256)]
+    grid = np.array(sorted({v for v in mags if np.isfinite(v)}))
+    g = np.random.default_rng(17)
+    for trial in range(50):
+        vals = g.standard_normal(32) * np.exp(g.uniform(-30, 30))
+        codes, sc = oracle.mx_quantize_block(vals, fmt)
+        x = sc - 127
+        amax = np.abs(vals).max()
+        assert 2.0 ** (x + emax) <= amax < 2.0 ** (x + emax + 1)
+        for v, c in zip(vals, codes):
+            a = abs(v) / 2.0 ** x
+            got = abs(dec(int(c) & (0x7 if fmt == "e2m1" else 0x7F)))
+            assert (c >> (3 if fmt == "e2m1" else 7)) == (v < 0)
+            if a >= top:
+                assert got == top
+            else:
+                i = np.searchsorted(grid, a)
+                lo, hi = grid[max(i - 1, 0)], grid[min(i, grid.size - 1)]
+                assert got in (lo, hi) and abs(got - a) <= (hi - lo) / 2 + 1e-300
+
+
+@pytest.mark.parametrize("fmt", ["e2m1", "e4m3", "e5m2"])
+def test_mx_blocks_agree_with_the_input_generators_quantizer(fmt):
+    # the generators' numpy quantizer (an independent implementation of the
+    # same OCP rule, used to make the MX operands) gives the same scales and
+    # elements on random blocks
+    g = np.random.default_rng(18)
+    x = g.standard_normal((8, 64)) * np.exp(g.uniform(-10, 10, size=(8, 1)))
+    if fmt == "e2m1":
+        want_codes, want_sc = wl.mx_quantize(x)
+    else:
+        want_codes, want_sc = wl.mx_quantize_fp8(x, fmt)
+    for r in range(8):
+        for b in range(2):
+            codes, sc = oracle.mx_quantize_block(x[r, 32 * b: 32 * b + 32], fmt)
+            assert sc == want_sc[r, b]
+            assert codes.tolist() == want_codes[r, 32 * b: 32 * b + 32].tolist()

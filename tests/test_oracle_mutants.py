@@ -53,6 +53,14 @@ MUTANTS = [
      "return 0.5 * t * (1.0 + tanh(sqrt(2.0 / 3.141592653589793) * (t + 0.044715 * t * t * t)));"),
     ("gelu without the factor one half", "return 0.5 * t * (1.0 + erf(t / sqrt(2.0))); /* erf form of GELU */",
      "return t * (1.0 + erf(t / sqrt(2.0)));"),
+    ("MX output: E2M1's largest exponent off by one", "emax = 2; ncodes = 8;", "emax = 1; ncodes = 8;"),
+    ("MX output: ties to the odd code", "(err == best_err && (c & 1) == 0)", "(err == best_err && (c & 1) == 1)"),
+    ("MX output: large magnitudes not clamped", "for (int c = 0; c < ncodes && a < top; ++c)",
+     "for (int c = 0; c < ncodes; ++c)"),
+    ("MX output: scale bias", "*scale = (uint8_t)(x + 127);", "*scale = (uint8_t)(x + 126);"),
+    ("MX output: element sign dropped", "codes[t] = (uint8_t)(best | (signbit(vals[t]) ? (1 << sign_bit) : 0));",
+     "codes[t] = (uint8_t)best;"),
+    ("MX output: E5M2 clamps one code short", "emax = 15; ncodes = 124;", "emax = 15; ncodes = 123;"),
 ]
 
 # Mistakes planted in the comparison (oracle/compare.py), caught by
