@@ -78,6 +78,10 @@ enum { THL_EPI_NONE = 0, THL_EPI_BIAS = 1, THL_EPI_RELU = 2, THL_EPI_GELU = 4 };
 typedef struct {
   unsigned flags;   /* THL_EPI_* bits */
   const void* bias; /* device pointer, length m (bias[i] is added to row i), when THL_EPI_BIAS */
+  uint8_t* sfd;     /* MX output (D in E2M1X2, E4M3 or E5M2): the generated E8M0 scales,
+                       SFD(b, j) for rows 32b .. 32b+31 of column j at sfd[j*ld_sfd + b], device;
+                       unused otherwise */
+  int64_t ld_sfd;   /* >= ceil(m/32) */
 } thl_epilogue;
 
 typedef struct {
@@ -139,6 +143,24 @@ typedef struct {
  * caller; apart from the split-K workspace above the library allocates
  * nothing, and it keeps no pointer after return.  alpha, beta and the
  * per-tensor scales are host values.
+ *
+ * MX output ("Technical Documentation: NVIDIA/cutlass", "Building a Block
+ * Scaled Kernel": the epilogue writes elements plus one scale factor per
+ * block of outputs, blocks along D's contiguous dimension): with the float
+ * operand families, dtypes->d may be E2M1X2 (two codes a byte along M, the
+ * even row in the low nibble, ldd even), E4M3 or E5M2.  Each run of 32
+ * consecutive rows of a column of act(alpha*acc + beta*C + bias), computed in
+ * fp32 (the last run of a column may be shorter), becomes one block by the
+ * OCP MX rule: scale X = floor(log2 max|v|) - emax (2 for E2M1, 8 for E4M3,
+ * 15 for E5M2), clamped to [-127, 127], stored as the E8M0 code X + 127 in
+ * epilogue->sfd; elements v / 2^X rounded to nearest even in the element
+ * format, magnitudes past its largest finite value clamped to it, signs kept;
+ * a block of zeros gets scale code 0.  The tiled kernels' general epilogue
+ * writes it (no small-M kernel, no split K), built with 16-byte operand
+ * loads only: A and B need 16-byte aligned bases and leading dimensions
+ * (THL_ERR_MISALIGNED otherwise); single problems only (batched and grouped
+ * launches return THL_ERR_UNSUPPORTED); sfd must not overlap any other array
+ * (THL_ERR_INVALID, as a NULL sfd or a short ld_sfd is).
  *
  * Block scales: sfa or sfb given with F16, BF16 or I8 operands is
  * THL_ERR_UNSUPPORTED.  fp8 operands with either array given are MX fp8;

@@ -59,14 +59,15 @@ A, B, C, D, BIAS, SFA, SFB = (0x10000000 * i for i in range(1, 8))
 
 
 def call(m=64, n=64, k=64, a=A, lda=None, opa="T", b=B, ldb=None, opb="N", c=None, ldc=None, d=D, ldd=None,
-         alpha=1.0, beta=0.0, types=("bf16", "f32", "f32", "none"), flags=0, bias=None, sc=None):
+         alpha=1.0, beta=0.0, types=("bf16", "f32", "f32", "none"), flags=0, bias=None, sc=None, sfd=None,
+         ld_sfd=0):
     ta, tc, td, tb = types
     lda = lda if lda is not None else max(1, k if opa == "T" else m)
     ldb = ldb if ldb is not None else max(1, k if opb == "N" else n)
     ldc = ldc if ldc is not None else max(1, m)
     ldd = ldd if ldd is not None else max(1, m)
     dts = thl.make_dtypes(ta, ta, tc, td, tb)
-    epi = thl.thl_epilogue(flags, bias)
+    epi = thl.thl_epilogue(flags, bias, sfd, ld_sfd)
     return thl.thl_gemm(m, n, k, a, lda, opa, b, ldb, opb, c, ldc, d, ldd, alpha, beta, dts, epi, sc, None)
 
 
@@ -329,3 +330,49 @@ def test_grouped_needs_one_family():
     assert gcall(sc, types=("e4m3", "f32", "bf16", "none")) == thl.THL_ERR_INVALID
     assert gcall([sc[0], _gp(d=D + 0x100000, sfa=SFA, ld_sfa=16, sfb=SFB + 0x10000, ld_sfb=16)],
                  types=("e4m3", "f32", "bf16", "none")) in (thl.THL_OK, thl.THL_ERR_HIP)
+
+
+# ------------------------------------------------------------ MX-format D
+
+SFD = 0x80000000
+
+
+@pytest.mark.parametrize("td", ["e2m1", "e4m3", "e5m2"])
+def test_mx_output_needs_its_scale_array(td):
+    mx = dict(types=("bf16", "f32", td, "none"), ldd=64)
+    assert call(**mx) == thl.THL_ERR_INVALID                       # no scale array
+    assert call(m=100, ldd=100, sfd=SFD, ld_sfd=3, types=mx["types"]) == thl.THL_ERR_INVALID  # < ceil(100/32)
+    # no rows or no columns: nothing is written, no scale array needed;
+    # the selection still names an MX-output variant
+    assert call(m=0, **mx) == thl.THL_OK
+    assert thl.thl_last_variant().endswith("_mxout")
+    assert call(n=0, **mx) == thl.THL_OK
+
+
+def test_mx_output_e2m1_column_starts_on_whole_bytes():
+    # two E2M1 codes a byte along M: an odd ldd would start every other column mid-byte
+    assert call(m=63, ldd=63, sfd=SFD, ld_sfd=2, types=("bf16", "f32", "e2m1", "none")) == thl.THL_ERR_INVALID
+
+
+def test_mx_output_scales_overlap_nothing():
+    types = ("bf16", "f32", "e4m3", "none")
+    # D spans 64 x 64 bytes from D; scales 2 x 64 bytes
+    assert call(sfd=D + 64 * 63, ld_sfd=2, types=types) == thl.THL_ERR_INVALID
+    assert call(sfd=A + 16, ld_sfd=2, types=types) == thl.THL_ERR_INVALID
+    assert call(sfd=BIAS, ld_sfd=2, bias=BIAS + 8, flags=thl.THL_EPI_BIAS, types=("bf16", "f32", "e4m3", "f32")) \
+        == thl.THL_ERR_INVALID
+
+
+def test_mx_output_is_for_single_float_problems():
+    types = ("bf16", "f32", "e4m3", "none")
+    assert bcall(types=types, sd=64 * 64) == thl.THL_ERR_UNSUPPORTED
+    assert gcall([_gp()], types=types) == thl.THL_ERR_UNSUPPORTED
+    # integer GEMMs write int32
+    assert call(types=("i8", "i32", "e4m3", "none"), sfd=SFD, ld_sfd=2) == thl.THL_ERR_UNSUPPORTED
+
+
+def test_mx_output_needs_16_byte_operand_rows():
+    # bf16 B rows of 130 elements (260 bytes): no MX-output variant loads them
+    types = ("bf16", "f32", "e4m3", "none")
+    assert call(n=130, opb="T", ldb=130, sfd=SFD, ld_sfd=2, types=types) == thl.THL_ERR_MISALIGNED
+    assert call(n=130, opb="T", ldb=136, sfd=SFD, ld_sfd=2, types=types, m=0) == thl.THL_OK

@@ -9,6 +9,7 @@ shapes, the full last row and column.
 """
 import os
 import sys
+import zlib
 
 import numpy as np
 import pytest
@@ -243,6 +244,10 @@ def test_every_variant(variant_family):
         if not v.startswith(variant_family + "_"):
             continue
         op_a, op_b = ops[v.split("_")[1]]
+        if v.endswith("_mxout"):
+            # MX-format D: exact inputs, codes and scales bit for bit
+            _check_mx_exact(kind, op_a, op_b, "e4m3", variant=v)
+            continue
         m, n, k = (16 if "skinny" in v else 300), 260, 520
         if kind in ("fp16", "bf16"):
             lda = _pad(m if op_a == "N" else k, 8)  # 16-byte leading dimensions
@@ -906,3 +911,142 @@ def test_split_k_is_deterministic():
         assert dp.run() == 0
         torch.cuda.synchronize()
         assert torch.equal(dp.d.view(torch.int16), first.view(torch.int16))
+
+
+# ------------------------------------------------------------ MX output (D as MX blocks)
+
+def _exact_mx_workload(kind, m, n, k, fmt, op_a=None, op_b=None, seed=0):
+    """Operands, C and bias with small integer values (e2m1 values for fp4)
+    and alpha = 1/2: every fp32 epilogue value on the GPU is exact, so its MX
+    blocks must be the oracle's bit for bit."""
+    import workloads as wl
+
+    g = np.random.default_rng(seed)
+    kw = {}
+    if op_a:
+        kw["op_a"] = op_a
+    if op_b:
+        kw["op_b"] = op_b
+    # MX output runs with 16-byte operand loads: rows of A and B padded to 8 elements
+    pad8 = lambda v: (v + 7) // 8 * 8
+    lds = {}
+    if kind in ("bf16", "fp16"):
+        lds = dict(lda=pad8(m if (op_a or "N") == "N" else k), ldb=pad8(k if (op_b or "N") == "N" else n))
+    w = wl.make(kind, m, n, k, type_d=fmt, ldd=m + 8 + m % 2, **kw, **lds)
+    if kind == "mxfp4":
+        vals = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.5, -1, -1.5, -2, -3, -4, -6])
+        av, bv = g.choice(vals, size=(m, k)), g.choice(vals, size=(n, k))
+        ma, mb = np.zeros((m, w.lda), np.uint8), np.zeros((n, w.ldb), np.uint8)
+        ma[:, :k], mb[:, :k] = wl.encode_e2m1_codes(av), wl.encode_e2m1_codes(bv)
+        w.a, w.b = wl.pack_e2m1(ma), wl.pack_e2m1(mb)
+        w.sfa[:], w.sfb[:] = 127, 127
+    else:
+        av = g.integers(-4, 5, size=(m, k)).astype(float)
+        bv = g.integers(-4, 5, size=(k, n)).astype(float)
+        w.a = wl.store_colmajor(wl.encode(av if w.op_a == "N" else av.T, w.type_a), w.lda)
+        w.b = wl.store_colmajor(wl.encode(bv if w.op_b == "N" else bv.T, w.type_b), w.ldb)
+        w.a_scale = w.b_scale = 1.0
+        if w.sfa is not None:
+            w.sfa[:], w.sfb[:] = 127, 127
+    if w.c is not None and w.beta != 0.0:
+        w.c = wl.store_colmajor(wl.encode(g.integers(-64, 65, size=(m, n)).astype(float), w.type_c), w.ldc)
+    if w.bias is not None:
+        w.bias = wl.encode(g.integers(-32, 33, size=m).astype(float), w.type_bias)
+    w.alpha = 0.5
+    return w
+
+
+def _run_mx(w, variant=None):
+    from workloads.device import DeviceProblem
+
+    import tile_hierarchy_linear_amd as thl
+
+    _say(f"[mx output] {w.name} {w.m}x{w.n}x{w.k} op={w.op_a}{w.op_b} D={w.type_d} act={w.act} variant={variant}")
+    if variant:
+        os.environ["THL_FORCE_VARIANT"] = variant
+    try:
+        dp = DeviceProblem(w)
+        assert dp.run() == 0
+        torch.cuda.synchronize()
+    finally:
+        os.environ.pop("THL_FORCE_VARIANT", None)
+    assert thl.thl_last_variant() == variant if variant else thl.thl_last_variant().endswith("_mxout")
+    return dp
+
+
+def _check_mx_exact(kind, op_a, op_b, fmt, variant=None):
+    import oracle
+
+    k = 64 if kind.startswith("mx") else 48
+    seed = zlib.crc32(f"{kind}{op_a}{op_b}{fmt}".encode()) % 1000
+    w = _exact_mx_workload(kind, 200, 130, k, fmt, op_a, op_b, seed=seed)
+    dp = _run_mx(w, variant)
+    codes, scales = dp.mx_all()
+    y = oracle.gemm_full(w.oracle_problem())
+    want_codes, want_scales = oracle.mx_quantize_columns(y, fmt)
+    assert np.array_equal(scales, want_scales), np.argwhere(scales != want_scales)[:5]
+    bad = np.argwhere(codes != want_codes)
+    assert bad.size == 0, (bad[:5], codes[tuple(bad[0])], want_codes[tuple(bad[0])], y[tuple(bad[0])])
+    # the 8 padding rows of each D column (ldd = m + 8) are untouched
+    raw = dp.d.cpu().numpy()
+    pad = raw[:, 100:104] if fmt == "e2m1" else raw[:, 200:208]
+    assert (pad == 0xEE).all()
+
+
+@pytest.mark.parametrize("fmt", ["e2m1", "e4m3", "e5m2"])
+@pytest.mark.parametrize("kind,ops", [("bf16", ("N", "N")), ("bf16", ("T", "T")), ("fp16", ("T", "N")),
+                                      ("bf16", ("N", "T")), ("fp8", ("T", "N")), ("mxfp4", ("T", "N")),
+                                      ("mxfp8", ("T", "N"))])
+def test_mx_output_bit_exact(kind, ops, fmt):
+    # 200 rows (six whole 32-row blocks and one of 8), 130 columns, several tiles
+    _check_mx_exact(kind, ops[0], ops[1], fmt)
+
+
+def _mx_grid(fmt):
+    import oracle
+
+    # the magnitude of each non-negative code (NaN / Inf where the format has them)
+    if fmt == "e2m1":
+        return oracle.decode(fmt, np.array([0x10, 0x32, 0x54, 0x76], np.uint8), 8)
+    return oracle.decode(fmt, np.arange(128, dtype=np.uint8))
+
+
+@pytest.mark.parametrize("fmt", ["e2m1", "e4m3"])
+@pytest.mark.parametrize("kind", ["fp8", "bf16"])
+def test_mx_output_random_within_rounding(kind, fmt):
+    # random operands: each block's scale is the oracle's (or one binade off
+    # where the block maximum lies within the GEMM tolerance of a power of
+    # two), and each element is a grid value the rounding of some value
+    # within the tolerance of the exact result can give
+    import oracle
+    from oracle import compare
+    import workloads as wl
+
+    w = wl.make(kind, 1000, 520, 2048, type_d=fmt)
+    dp = _run_mx(w)
+    codes, scales = dp.mx_all()
+    y = oracle.gemm_full(w.oracle_problem())
+    tol = compare.float_tolerance(w.k, w.alpha, compare.operand_max_abs(w, "a"), compare.operand_max_abs(w, "b"),
+                                  "f32", y, w.act)
+    emax = {"e2m1": 2, "e4m3": 8}[fmt]
+    mags = _mx_grid(fmt)
+    grid = np.array(sorted({v for v in mags if np.isfinite(v)}))
+    _, ref_scales = oracle.mx_quantize_columns(y, fmt)
+    x_gpu, x_ref = scales.astype(np.int64) - 127, ref_scales.astype(np.int64) - 127
+    m, n = y.shape
+    nb = (m + 31) // 32
+    amax = np.array([[np.abs(y[32 * b: 32 * b + 32, j]).max() for j in range(n)] for b in range(nb)])
+    tmax = np.array([[tol[32 * b: 32 * b + 32, j].max() for j in range(n)] for b in range(nb)])
+    near = (np.abs(amax - 2.0 ** (x_ref + emax)) <= tmax) | (np.abs(amax - 2.0 ** (x_ref + emax + 1)) <= tmax)
+    assert ((x_gpu == x_ref) | ((np.abs(x_gpu - x_ref) == 1) & near)).all()
+    xe = np.repeat(x_gpu, 32, axis=0)[:m]
+    sign_bit = 3 if fmt == "e2m1" else 7
+    mag = mags[(codes & ((1 << sign_bit) - 1)).astype(np.int64)]
+    lo = np.maximum(np.abs(y) - tol, 0.0) / 2.0 ** xe
+    hi = (np.abs(y) + tol) / 2.0 ** xe
+    fl = grid[np.maximum(np.searchsorted(grid, lo, side="right") - 1, 0)]
+    ce = grid[np.minimum(np.searchsorted(grid, hi, side="left"), grid.size - 1)]
+    ok = (mag >= fl) & (mag <= ce)
+    neg = (codes >> sign_bit) == 1
+    ok &= (neg == (y < 0)) | (np.abs(y) <= tol) | (mag == 0)
+    assert ok.all(), (np.argwhere(~ok)[:5], int((~ok).sum()))

@@ -34,7 +34,8 @@ class thl_dtypes(ctypes.Structure):
 
 
 class thl_epilogue(ctypes.Structure):
-    _fields_ = [("flags", ctypes.c_uint), ("bias", ctypes.c_void_p)]
+    _fields_ = [("flags", ctypes.c_uint), ("bias", ctypes.c_void_p), ("sfd", ctypes.c_void_p),
+                ("ld_sfd", ctypes.c_int64)]
 
 
 class thl_scales(ctypes.Structure):

@@ -45,11 +45,17 @@ struct Variant {
   int tier;  // 0: 256x256, 1: 256x128, 2: 128x128 (the shape rule's preference order);
              // -1: the small-M kernel (M <= bm <= 64), chosen by its own rule
   LaunchFn launch;
+  bool mxout = false;  // writes MX-format D (elements plus generated scales); chosen only for such D
 };
 
 #define THL_V(FAM, NAME, OPS, AK, BK, BM, BN, LOADW, ST, OCC, TIER)                                       \
   {NAME "_" OPS "_" #BM "x" #BN "_v" #LOADW "_s" #ST "_o" #OCC, FAM, AK, BK, BM, BN, 256, LOADW, OCC, TIER, \
-   &launch_gemm<FAM, BM, BN, 2, 2, LOADW, ST, OCC, 16, AK, BK>}
+   &launch_gemm<FAM, BM, BN, 2, 2, LOADW, ST, OCC, 16, AK, BK, false>}
+
+// The MX-output variant (must match THL_INST_MXOUT).
+#define THL_VMXO(FAM, NAME, OPS, AK, BK)                                                         \
+  {NAME "_" OPS "_128x128_v16_s4_o2_mxout", FAM, AK, BK, 128, 128, 256, 16, 2, 2,              \
+   &launch_gemm<FAM, 128, 128, 2, 2, 16, 4, 2, 16, AK, BK, true>, true}
 
 // Must list exactly the instantiations of THL_INSTANTIATE_VARIANTS.  Order is
 // the first-fit order within a tier: 16-byte copies before 4-byte ones.
@@ -93,6 +99,23 @@ const Variant kVariants[] = {
     THL_VMX8(FAM_MX8_E5M2, "mxe5m2"),
     THL_VMX8(FAM_MX8_E4E5, "mxe4m3e5m2"),
     THL_VMX8(FAM_MX8_E5E4, "mxe5m2e4m3"),
+    THL_VMXO(FAM_BF16, "bf16", "tn", true, true),
+    THL_VMXO(FAM_BF16, "bf16", "nn", false, true),
+    THL_VMXO(FAM_BF16, "bf16", "tt", true, false),
+    THL_VMXO(FAM_BF16, "bf16", "nt", false, false),
+    THL_VMXO(FAM_F16, "f16", "tn", true, true),
+    THL_VMXO(FAM_F16, "f16", "nn", false, true),
+    THL_VMXO(FAM_F16, "f16", "tt", true, false),
+    THL_VMXO(FAM_F16, "f16", "nt", false, false),
+    THL_VMXO(FAM_FP8, "e4m3", "tn", true, true),
+    THL_VMXO(FAM_E5M2, "e5m2", "tn", true, true),
+    THL_VMXO(FAM_E4E5, "e4m3e5m2", "tn", true, true),
+    THL_VMXO(FAM_E5E4, "e5m2e4m3", "tn", true, true),
+    THL_VMXO(FAM_MX8, "mxe4m3", "tn", true, true),
+    THL_VMXO(FAM_MX8_E5M2, "mxe5m2", "tn", true, true),
+    THL_VMXO(FAM_MX8_E4E5, "mxe4m3e5m2", "tn", true, true),
+    THL_VMXO(FAM_MX8_E5E4, "mxe5m2e4m3", "tn", true, true),
+    THL_VMXO(FAM_FP4, "e2m1", "tn", true, true),
     THL_VS(FAM_BF16, "bf16"),
     THL_VS(FAM_F16, "f16"),
     THL_VS(FAM_I8, "i8"),
@@ -275,6 +298,12 @@ int64_t bytes_of(thl_dtype t, int64_t count) {
 
 bool is_float_io(thl_dtype t) { return t == THL_F32 || t == THL_F16 || t == THL_BF16; }
 
+// D formats written as MX blocks (elements plus generated E8M0 scales).
+int mx_out_of(thl_dtype t) {
+  return t == THL_E4M3 ? MX_E4M3 : (t == THL_E5M2 ? MX_E5M2 : (t == THL_E2M1X2 ? MX_E2M1 : MX_NONE));
+}
+bool is_mx_out(thl_dtype t) { return mx_out_of(t) != MX_NONE; }
+
 struct Range {
   uintptr_t lo = 0, hi = 0;  // [lo, hi), empty when lo == hi
 };
@@ -409,6 +438,7 @@ struct Prep {
   int fam = -1;
   bool a_kmajor = false, b_kmajor = false, block_scaled = false, int_path = false, has_bias = false;
   bool small_m = false, work = false, vec = false;
+  int mx_out = MX_NONE;  // D in an MX element format, with generated scales
   unsigned flags = 0;
   int64_t lda_bytes = 0, ldb_bytes = 0, sa_bytes = 0, sb_bytes = 0;
   thl_scales s{1.0f, 1.0f, nullptr, 0, nullptr, 0};
@@ -419,7 +449,7 @@ struct Prep {
 thl_status prepare(const Batch& bt, int64_t m, int64_t n, int64_t k, const void* A, int64_t lda, thl_op opA,
                    const void* B, int64_t ldb, thl_op opB, const void* C, int64_t ldc, void* D, int64_t ldd,
                    float alpha, float beta, const thl_dtypes* dt, unsigned flags, const void* bias,
-                   const thl_scales* sc, Prep* out) {
+                   const thl_scales* sc, const uint8_t* sfd, int64_t ld_sfd, Prep* out) {
   // ---- arguments
   if (!dt || m < 0 || n < 0 || k < 0) return THL_ERR_INVALID;
   if (bt.count < 0 || bt.a < 0 || bt.b < 0 || bt.c < 0 || bt.d < 0 || bt.bias < 0 || bt.sfa < 0 || bt.sfb < 0)
@@ -466,10 +496,14 @@ thl_status prepare(const Batch& bt, int64_t m, int64_t n, int64_t k, const void*
     if (alpha != 1.0f || (beta != 0.0f && beta != 1.0f)) return THL_ERR_UNSUPPORTED;
     if (flags & THL_EPI_GELU) return THL_ERR_UNSUPPORTED;
   } else {
-    if (dt->acc != THL_F32 || !is_float_io(dt->d)) return THL_ERR_UNSUPPORTED;
+    if (dt->acc != THL_F32 || !(is_float_io(dt->d) || is_mx_out(dt->d))) return THL_ERR_UNSUPPORTED;
     if (beta != 0.0f && !is_float_io(dt->c)) return THL_ERR_UNSUPPORTED;
     if (has_bias && !is_float_io(dt->bias)) return THL_ERR_UNSUPPORTED;
   }
+  // MX output: D in E2M1 (two a byte along M), E4M3 or E5M2 with one E8M0
+  // scale per 32 consecutive rows of a column, for one problem at a time.
+  const int mx_out = int_path ? MX_NONE : mx_out_of(dt->d);
+  if (mx_out != MX_NONE && bt.count > 1) return THL_ERR_UNSUPPORTED;
   // 8- and 4-bit operands: K-major only (op(A) rows, op(B) columns contiguous along K).
   const bool a_kmajor = opA == THL_OP_T, b_kmajor = opB == THL_OP_N;
   if (fam != FAM_BF16 && fam != FAM_F16 && (!a_kmajor || !b_kmajor)) return THL_ERR_UNSUPPORTED;
@@ -482,7 +516,9 @@ thl_status prepare(const Batch& bt, int64_t m, int64_t n, int64_t k, const void*
   if (ldd < (m > 1 ? m : 1)) return THL_ERR_INVALID;
   if (beta != 0.0f && ldc < (m > 1 ? m : 1)) return THL_ERR_INVALID;
   if (fam == FAM_FP4 && ((lda % 2) != 0 || (ldb % 2) != 0)) return THL_ERR_INVALID;
+  if (mx_out == MX_E2M1 && ldd % 2 != 0) return THL_ERR_INVALID;
   const bool work = m > 0 && n > 0 && bt.count > 0;
+  if (work && mx_out != MX_NONE && (!sfd || ld_sfd < (m + 31) / 32)) return THL_ERR_INVALID;
   // Batched: the D matrices may not overlap one another; fp4 operands move
   // by whole bytes.
   if (work && bt.count > 1 && bt.d < (n - 1) * ldd + m) return THL_ERR_INVALID;
@@ -515,6 +551,19 @@ thl_status prepare(const Batch& bt, int64_t m, int64_t n, int64_t k, const void*
       if (overlaps(rd, batch_range(s.sfa, THL_E8M0, k / 32, m, s.ld_sfa, L, bt.sfa))) return THL_ERR_INVALID;
       if (overlaps(rd, batch_range(s.sfb, THL_E8M0, k / 32, n, s.ld_sfb, L, bt.sfb))) return THL_ERR_INVALID;
     }
+    if (mx_out != MX_NONE) {
+      // the generated scales overlap nothing else either
+      const Range rs = matrix_range(sfd, THL_E8M0, (m + 31) / 32, n, ld_sfd);
+      const Range others[] = {rd,
+                              matrix_range(A, dt->a, rows_a, cols_a, lda),
+                              matrix_range(B, dt->b, rows_b, cols_b, ldb),
+                              beta != 0.0f ? matrix_range(C, dt->c, m, n, ldc) : Range{},
+                              has_bias ? matrix_range(bias, dt->bias, m, 1, m) : Range{},
+                              block_scaled && k > 0 ? matrix_range(s.sfa, THL_E8M0, k / 32, m, s.ld_sfa) : Range{},
+                              block_scaled && k > 0 ? matrix_range(s.sfb, THL_E8M0, k / 32, n, s.ld_sfb) : Range{}};
+      for (const Range& o : others)
+        if (overlaps(rs, o)) return THL_ERR_INVALID;
+    }
   }
 
   // Copy offsets inside a 256-row tile, and scale-row offsets, are 32-bit.
@@ -530,7 +579,8 @@ thl_status prepare(const Batch& bt, int64_t m, int64_t n, int64_t k, const void*
   o.block_scaled = block_scaled;
   o.int_path = int_path;
   o.has_bias = has_bias;
-  o.small_m = m <= 64 && k > 0;
+  o.small_m = m <= 64 && k > 0 && mx_out == MX_NONE;  // MX output: the tiled kernels' epilogue
+  o.mx_out = mx_out;
   o.work = work;
   o.flags = flags;
   o.lda_bytes = bytes_of(dt->a, lda);
@@ -542,7 +592,7 @@ thl_status prepare(const Batch& bt, int64_t m, int64_t n, int64_t k, const void*
   // Vector epilogue: D (and C, bias) rows aligned for 16-byte runs along M,
   // C 16-bit, and a 256-column panel within 32-bit offsets.
   o.vec = false;
-  if (!int_path) {
+  if (!int_path && mx_out == MX_NONE) {
     auto vec_ok = [](const void* ptr, int64_t ld_bytes) {
       return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0 && ld_bytes % 16 == 0 && ld_bytes <= (INT64_C(1) << 23);
     };
@@ -595,6 +645,8 @@ const Variant* choose_variant(const Prep& pr, bool allow_small, int64_t rows, in
       } else if ((pass < 3 && v.tier != pass) || (pass == 3 && v.tier < 0) || (v.tier < 0 && v.bm < rows)) {
         continue;
       }
+      // MX-format D runs on the MX-output variants, and only it does
+      if ((pr.mx_out != MX_NONE) != v.mxout) continue;
       if (fit(v)) {
         pick = &v;
         break;
@@ -638,6 +690,7 @@ GemmArgs make_args(const Prep& pr, const Variant& v, int64_t m, int64_t n, int64
   a.c_type = static_cast<int32_t>(dt->c);
   a.d_type = static_cast<int32_t>(dt->d);
   a.bias_type = static_cast<int32_t>(dt->bias);
+  a.mx_out = pr.mx_out;
   return a;
 }
 
@@ -667,7 +720,8 @@ int64_t persistent_grid(const Variant& v, int64_t problems, int64_t max_tiles) {
 // the split gains.  THL_FORCE_SPLITS=<s> asks for s splits on any eligible
 // variant (tests use it to cover the path at small sizes).
 int choose_splits(const Prep& pr, const Variant& v, const Batch& bt, int64_t tiles, int64_t kbytes) {
-  if (bt.count != 1 || v.tier < 0 || pr.block_scaled || v.occ != 2 || v.bm * v.bn > 128 * 128 || kbytes <= 0)
+  if (bt.count != 1 || v.tier < 0 || pr.block_scaled || v.occ != 2 || v.bm * v.bn > 128 * 128 || kbytes <= 0 ||
+      pr.mx_out != MX_NONE)
     return 1;
   const int64_t nk_all = (kbytes + 63) / 64;
   const char* forced = std::getenv("THL_FORCE_SPLITS");
@@ -693,7 +747,7 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
   Prep pr;
   const unsigned flags = epi ? epi->flags : 0u;
   thl_status st = prepare(bt, m, n, k, A, lda, opA, B, ldb, opB, C, ldc, D, ldd, alpha, beta, dt, flags,
-                          epi ? epi->bias : nullptr, sc, &pr);
+                          epi ? epi->bias : nullptr, sc, epi ? epi->sfd : nullptr, epi ? epi->ld_sfd : 0, &pr);
   if (st != THL_OK) return st;
 
   // ---- variant: first fit on family, alignment and shape
@@ -711,6 +765,10 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
 
   // ---- launch
   GemmArgs a = make_args(pr, *pick, m, n, k, A, B, C, ldc, D, ldd, alpha, beta, dt, epi ? epi->bias : nullptr);
+  if (pr.mx_out != MX_NONE) {
+    a.sfd = epi->sfd;
+    a.ld_sfd = epi->ld_sfd;
+  }
   // Batch strides in bytes (zero for a single problem and for absent arrays).
   if (bt.count > 1) {
     a.bs_a = pr.sa_bytes;
@@ -828,6 +886,7 @@ thl_status grouped_impl(int64_t count, const thl_group_problem* pb, const thl_gr
   if (count < 0 || !dt) return THL_ERR_INVALID;
   if (count > 65535) return THL_ERR_UNSUPPORTED;  // one grid row per problem
   if (count > 0 && !pb) return THL_ERR_INVALID;
+  if (is_mx_out(dt->d)) return THL_ERR_UNSUPPORTED;  // MX output: single problems only
   const unsigned flags = epi ? epi->flags : 0u;
   const Batch one{};
   std::vector<Prep> preps(static_cast<size_t>(count));
@@ -842,7 +901,7 @@ thl_status grouped_impl(int64_t count, const thl_group_problem* pb, const thl_gr
     s.sfb = q.sfb;
     s.ld_sfb = q.ld_sfb;
     const thl_status st = prepare(one, q.m, q.n, q.k, q.A, q.lda, opA, q.B, q.ldb, opB, q.C, q.ldc, q.D, q.ldd,
-                                  alpha, beta, dt, flags, q.bias, &s, &preps[z]);
+                                  alpha, beta, dt, flags, q.bias, &s, nullptr, 0, &preps[z]);
     if (st != THL_OK) return st;
     if (preps[z].work) {
       // one family for the problems with outputs: block scales on every one

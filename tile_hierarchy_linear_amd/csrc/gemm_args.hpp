@@ -74,11 +74,20 @@ struct GemmArgs {
   // product to D + split * split_stride bytes.
   int32_t splits, ksteps;
   int64_t split_stride;
+  // MX output (D in an MX element format with one E8M0 scale per 32
+  // consecutive rows of a column): mx_out is MX_* (0: none); SFD(b, j) at
+  // sfd[j * ld_sfd + b].
+  int32_t mx_out;
+  uint8_t* sfd;
+  int64_t ld_sfd;
 };
+
+// MX output element formats.
+enum : int { MX_NONE = 0, MX_E4M3 = 1, MX_E5M2 = 2, MX_E2M1 = 3 };
 
 
 // Launches one kernel variant on `stream`; returns the launch status.
-template <int F, int BM, int BN, int WM, int WN, int LOADW, int STAGES, int OCC, int SCW, bool AK, bool BK>
+template <int F, int BM, int BN, int WM, int WN, int LOADW, int STAGES, int OCC, int SCW, bool AK, bool BK, bool MXO>
 hipError_t launch_gemm(const GemmArgs& a, dim3 grid, hipStream_t stream);
 
 // Launches the small-M kernel (M <= 16 * MT, K-major A and B; KW wavefronts

@@ -345,6 +345,44 @@ __device__ __forceinline__ void buf_store16(v4i v, __amdgpu_buffer_rsrc_t r, uin
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), r, vo + static_cast<uint32_t>(so), 0, 0);
 }
 
+// ------------------------------------------------------------ MX output
+// One block of an MX output: the OCP MX rule applied to the fp32 epilogue
+// values (shared exponent floor(log2 amax) - emax, clamped to E8M0's range;
+// elements rounded to nearest even, larger magnitudes clamped to the largest
+// finite element, signs kept).
+
+// floor(log2(x)) of a finite x > 0 from its bits (subnormals included).
+__device__ __forceinline__ int floor_log2_f32(float x) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, x) & 0x7fffffffu;
+  const int e = static_cast<int>(b >> 23);
+  if (e != 0) return e - 127;
+  return -149 + (31 - __builtin_clz(b));  // subnormal: the top set mantissa bit
+}
+
+// E8M0 code of the block whose largest magnitude is amax (>= 0), for an
+// element format whose largest exponent is emax; 0 for a block of zeros.
+__device__ __forceinline__ int mx_scale_code(float amax, int emax) {
+  if (!(amax > 0.0f)) return 0;
+  int x = floor_log2_f32(amax) - emax;
+  x = x < -127 ? -127 : (x > 127 ? 127 : x);
+  return x + 127;
+}
+
+// E2M1 code of v (already divided by the block scale): the nearest of
+// 0, 0.5, 1, 1.5, 2, 3, 4, 6, ties to the even code, above 6 clamped to 6.
+__device__ __forceinline__ unsigned e2m1_code(float v) {
+  const float a = __builtin_fabsf(v);
+  unsigned c = 0;
+  c += (a > 0.25f) ? 1u : 0u;
+  c += (a >= 0.75f) ? 1u : 0u;  // tie at 0.75 goes up to the even code 2
+  c += (a > 1.25f) ? 1u : 0u;
+  c += (a >= 1.75f) ? 1u : 0u;  // tie at 1.75 -> code 4
+  c += (a > 2.5f) ? 1u : 0u;
+  c += (a >= 3.5f) ? 1u : 0u;   // tie at 3.5 -> code 6
+  c += (a > 5.0f) ? 1u : 0u;
+  return c | ((__builtin_bit_cast(uint32_t, v) >> 28) & 8u);
+}
+
 // Bitwise select (a where m is set, else b): keeps a uniform type or flag
 // choice a per-lane select instead of a branch around each element.
 __device__ __forceinline__ unsigned bsel(unsigned m, unsigned a, unsigned b) { return (a & m) | (b & ~m); }
@@ -501,7 +539,12 @@ __device__ __forceinline__ bool select_group_problem(GemmArgs& p) {
 // false when they are contiguous along M (N) -- 16-bit types only -- staged
 // as 32 k-rows of the tile's M (N) extent and turned into K-contiguous
 // fragments by two transposed 16-bit LDS reads each.
-template <int F, int BM, int BN, int WM, int WN, int LOADW, int STAGES, int OCC, int SCW, bool AK, bool BK>
+//
+// MXO: the variant writes MX-format D (elements plus generated E8M0 scales,
+// GemmArgs::mx_out); built as variants of their own so that no other kernel
+// carries its code.
+template <int F, int BM, int BN, int WM, int WN, int LOADW, int STAGES, int OCC, int SCW, bool AK, bool BK,
+          bool MXO = false>
 __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 gemm_kernel(GemmArgs p) {
   if (p.group) {
@@ -1250,6 +1293,90 @@ gemm_kernel(GemmArgs p) {
     });
     ep += (wave % WPS) * EPB;
   }
+  constexpr bool MXOUT = MXO && !T::INT;
+  // MX output of one lane's 8-row run (rows m .. m+7 of column n; lo, hi
+  // the staged accumulators): the epilogue values, the block's largest
+  // magnitude over the 4 lanes that hold its 32 rows (consecutive lanes, the
+  // first at a multiple of 4), then the element codes and, from the block's
+  // first lane, its scale.  Called by every lane of the wave; lanes past M
+  // or N take part in the maximum with nothing.
+  auto mx_run = [&](const v4i lo, const v4i hi, const int64_t m, const int64_t n, void* const dst) {
+    const bool valid = n < p.n && m < p.m;
+    const int rows = valid ? static_cast<int>(p.m - m < 8 ? p.m - m : 8) : 0;
+    const v4f lof = __builtin_bit_cast(v4f, lo), hif = __builtin_bit_cast(v4f, hi);
+    float t[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) t[r] = p.alpha * (r < 4 ? lof[r] : hif[r - 4]);
+    if (valid) {
+      if (p.beta != 0.0f) {
+        float cv[8];
+        load8_f(p.c, p.c_type, n * p.ldc + m, rows, cv);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) t[r] += p.beta * cv[r];
+      }
+      if (p.flags & EPI_BIAS) {
+        float bv[8];
+        load8_f(p.bias, p.bias_type, m, rows, bv);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) t[r] += bv[r];
+      }
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      t[r] = activate(t[r], p.flags);
+      if (r < rows) amax = __builtin_fmaxf(amax, __builtin_fabsf(t[r]));
+    }
+    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1));
+    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 2));
+    if (!valid) return;
+    const int emax = p.mx_out == MX_E2M1 ? 2 : (p.mx_out == MX_E4M3 ? 8 : 15);
+    const int code = mx_scale_code(amax, emax);
+    const float inv = __builtin_ldexpf(1.0f, 127 - code);  // 1 / 2^X, exact
+    uint8_t* d8 = static_cast<uint8_t*>(dst);
+    if (p.mx_out == MX_E2M1) {
+      // two codes a byte along M, the even row in the low nibble
+      uint32_t w = 0;
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        if (r < rows) w |= e2m1_code(t[r] * inv) << (4 * r);
+      const int64_t off = (n * p.ldd + m) / 2;
+      if (rows == 8 && (reinterpret_cast<uintptr_t>(d8 + off) & 3) == 0) {
+        *reinterpret_cast<uint32_t*>(d8 + off) = w;
+      } else {
+        for (int q = 0; q < (rows + 1) / 2; ++q) d8[off + q] = static_cast<uint8_t>(w >> (8 * q));
+      }
+    } else {
+      const float top = p.mx_out == MX_E4M3 ? 448.0f : 57344.0f;
+      uint32_t w[2] = {0, 0};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float s = t[4 * h + r] * inv;
+          v[r] = __builtin_fabsf(s) > top ? __builtin_copysignf(top, s) : s;
+        }
+        int lo2, hi2;
+        if (p.mx_out == MX_E4M3) {
+          lo2 = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+          hi2 = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], lo2, true);
+        } else {
+          lo2 = __builtin_amdgcn_cvt_pk_bf8_f32(v[0], v[1], 0, false);
+          hi2 = __builtin_amdgcn_cvt_pk_bf8_f32(v[2], v[3], lo2, true);
+        }
+        w[h] = static_cast<uint32_t>(hi2);
+      }
+      const int64_t off = n * p.ldd + m;
+      if (rows == 8 && (reinterpret_cast<uintptr_t>(d8 + off) & 7) == 0) {
+        *reinterpret_cast<uint64_t*>(d8 + off) = (static_cast<uint64_t>(w[1]) << 32) | w[0];
+      } else {
+        for (int r = 0; r < rows; ++r) d8[off + r] = static_cast<uint8_t>(w[r / 4] >> (8 * (r % 4)));
+      }
+    }
+    if ((m & 31) == 0) p.sfd[n * p.ld_sfd + (m >> 5)] = static_cast<uint8_t>(code);
+  };
+
   auto epilogue_gen = [&](const int64_t em0, const int64_t en0, void* const dst) {
     int ln = lane;  // opaque copy, as in epilogue_vec below
     asm volatile("" : "+v"(ln));
@@ -1302,7 +1429,7 @@ gemm_kernel(GemmArgs p) {
               for (int r = 0; r < 8; ++r) t[r] = t[r] < 0 ? 0 : t[r];
             }
             store8_i(dst, n * p.ldd + m, t, rows);
-          } else {
+          } else if (!MXOUT || p.mx_out == MX_NONE) {
             const v4f lof = __builtin_bit_cast(v4f, lo), hif = __builtin_bit_cast(v4f, hi);
             float t[8];
   #pragma unroll
@@ -1323,6 +1450,9 @@ gemm_kernel(GemmArgs p) {
             for (int r = 0; r < 8; ++r) t[r] = activate(t[r], p.flags);
             store8_f(dst, p.d_type, n * p.ldd + m, t, rows);
           }
+        }
+        if constexpr (MXOUT) {
+          if (p.mx_out != MX_NONE) mx_run(lo, hi, m, n, dst);
         }
       }
       asm volatile("" ::: "memory");

@@ -9,6 +9,8 @@ import torch
 import tile_hierarchy_linear_amd as thl
 
 _TORCH_D = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "i32": torch.int32}
+# D formats written as MX blocks (element codes plus one E8M0 scale per 32 rows)
+MX_D = ("e2m1", "e4m3", "e5m2")
 
 
 def upload(arr, device="cuda"):
@@ -30,11 +32,19 @@ class DeviceProblem:
         self.sfa = upload(w.sfa, device)
         self.sfb = upload(w.sfb, device)
         self.ldd = ldd or w.ldd
-        self.d = torch.empty((max(1, w.n), self.ldd), dtype=_TORCH_D[w.type_d], device=device)
-        if w.type_d == "i32":
-            self.d.fill_(-(2 ** 31) + 7)
+        self.sfd, self.ld_sfd = None, 0
+        if w.type_d in MX_D:
+            # codes as bytes (two a byte for e2m1), the scales beside them; 0xEE marks unwritten bytes
+            ld_bytes = self.ldd // 2 if w.type_d == "e2m1" else self.ldd
+            self.d = torch.full((max(1, w.n), ld_bytes), 0xEE, dtype=torch.uint8, device=device)
+            self.ld_sfd = max(1, (w.m + 31) // 32)
+            self.sfd = torch.full((max(1, w.n), self.ld_sfd), 0xEE, dtype=torch.uint8, device=device)
         else:
-            self.d.fill_(d_fill)
+            self.d = torch.empty((max(1, w.n), self.ldd), dtype=_TORCH_D[w.type_d], device=device)
+            if w.type_d == "i32":
+                self.d.fill_(-(2 ** 31) + 7)
+            else:
+                self.d.fill_(d_fill)
 
     def run(self, stream=None, d=None, c=None, ldc=None, entry=None):
         """Run through thl_gemm (or `entry`, an entry point of the same
@@ -44,7 +54,8 @@ class DeviceProblem:
                              w.type_bias if w.bias is not None else "none")
         flags = (thl.THL_EPI_BIAS if w.bias is not None else 0) | \
             {"none": 0, "relu": thl.THL_EPI_RELU, "gelu": thl.THL_EPI_GELU}[w.act]
-        epi = thl.thl_epilogue(flags, self.bias.data_ptr() if self.bias is not None else None)
+        epi = thl.thl_epilogue(flags, self.bias.data_ptr() if self.bias is not None else None,
+                               self.sfd.data_ptr() if self.sfd is not None else None, self.ld_sfd)
         sc = thl.thl_scales(float(w.a_scale), float(w.b_scale),
                             self.sfa.data_ptr() if self.sfa is not None else None, int(w.ld_sfa),
                             self.sfb.data_ptr() if self.sfb is not None else None, int(w.ld_sfb))
@@ -68,6 +79,17 @@ class DeviceProblem:
         if self.w.type_d == "i32":
             return vals.to(torch.int64).numpy()
         return vals.to(torch.float64).numpy()
+
+    def mx_all(self):
+        """MX-format D: (element codes (m, n) uint8, scale codes (ceil(m/32), n) uint8)."""
+        w = self.w
+        raw = self.d.cpu().numpy()[: w.n]
+        if w.type_d == "e2m1":
+            codes = np.empty((w.n, raw.shape[1] * 2), np.uint8)
+            codes[:, 0::2], codes[:, 1::2] = raw & 0xF, raw >> 4
+        else:
+            codes = raw
+        return codes[:, : w.m].T.copy(), self.sfd.cpu().numpy()[: w.n, : (w.m + 31) // 32].T.copy()
 
     def d_all(self) -> np.ndarray:
         """All of D as an (m, n) array [i, j]."""
