@@ -28,7 +28,8 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 # Test hook: the pins' mutation test points this at a deliberately broken build.
 _LIB_OVERRIDE = os.environ.get("THL_ORACLE_LIB_OVERRIDE")
 
-TYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3, "i32": 4, "e4m3": 5, "e2m1": 6, "e8m0": 7, "e5m2": 9}
+TYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3, "i32": 4, "e4m3": 5, "e2m1": 6, "e8m0": 7, "e5m2": 9,
+              "e2m3": 10, "e3m2": 11}
 ACT_CODES = {"none": 0, "relu": 1, "gelu": 2}
 
 
@@ -98,7 +99,12 @@ def decode(type_name: str, raw: np.ndarray, count: int | None = None) -> np.ndar
     """Decode ``count`` stored elements of ``raw`` (its bytes) to exact float64."""
     raw = np.ascontiguousarray(raw)
     if count is None:
-        count = raw.nbytes * 2 if type_name == "e2m1" else raw.size
+        if type_name == "e2m1":
+            count = raw.nbytes * 2
+        elif type_name in ("e2m3", "e3m2"):
+            count = raw.nbytes * 8 // 6
+        else:
+            count = raw.size
     out = np.empty(count, dtype=np.float64)
     rc = _load().oracle_decode(TYPE_CODES[type_name], _ptr(raw), count, _ptr(out))
     if rc != 0:

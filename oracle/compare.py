@@ -57,30 +57,42 @@ def check_exact(got, want) -> dict:
     return {"ok": not bool(bad.any()), "n_bad": int(bad.sum()), "n": int(got.size)}
 
 
-def operand_max_abs(w, which: str) -> float:
-    """max |a'| (or |b'|) over the dequantized operand of a workload, decoded
-    by the oracle's own decoders: per-tensor scale for fp8, per-32-block
-    E8M0 scale for e2m1 (blocks run along the contiguous K)."""
+def logical_operand(w, which: str) -> np.ndarray:
+    """The operand as its logical rows x K matrix (A: m x k; B: n x k, one
+    row per column of op(B)) of decoded element values, read from its storage
+    (lines of ld elements along K, or along the rows, by op), before any
+    scale."""
     from . import decode
 
     raw = w.a if which == "a" else w.b
     fmt = w.type_a if which == "a" else w.type_b
-    if raw.size == 0:
+    ld = w.lda if which == "a" else w.ldb
+    rows = w.m if which == "a" else w.n
+    kmajor = (w.op_a == "T") if which == "a" else (w.op_b == "N")
+    if raw.size == 0 or rows == 0 or w.k == 0:
+        return np.zeros((rows, w.k))
+    vals = decode(fmt, raw).reshape(-1, ld)
+    return vals[:rows, : w.k] if kmajor else vals[: w.k, :rows].T
+
+
+def operand_max_abs(w, which: str) -> float:
+    """max |a'| (or |b'|) over the dequantized operand of a workload, decoded
+    by the oracle's own decoders: per-tensor scale for fp8, per-32-block E8M0
+    scale along K for the block-scaled formats, whatever the storage."""
+    from . import decode
+
+    fmt = w.type_a if which == "a" else w.type_b
+    vals = logical_operand(w, which)
+    if vals.size == 0:
         return 0.0
-    vals = decode(fmt, raw)
-    if w.sfa is not None:  # block-scaled (E2M1 or MXFP8 E4M3)
+    per_tensor = (w.a_scale if which == "a" else w.b_scale) if fmt in ("e4m3", "e5m2") else 1.0
+    if w.sfa is not None:  # block-scaled
         sf = w.sfa if which == "a" else w.sfb
         ld_sf = w.ld_sfa if which == "a" else w.ld_sfb
-        rows = sf.shape[0]
-        vals = vals.reshape(rows, -1)[:, : w.k]
-        if w.k == 0:
-            return 0.0
-        scales = decode("e8m0", np.ascontiguousarray(sf)).reshape(rows, ld_sf)[:, : w.k // 32]
+        rows = vals.shape[0]
+        scales = decode("e8m0", np.ascontiguousarray(sf)).reshape(-1, ld_sf)[:rows, : w.k // 32]
         vals = vals.reshape(rows, w.k // 32, 32) * scales[:, :, None]
-        per_tensor = (w.a_scale if which == "a" else w.b_scale) if fmt in ("e4m3", "e5m2") else 1.0
-        return float(np.abs(vals).max()) * per_tensor
-    scale = (w.a_scale if which == "a" else w.b_scale) if fmt in ("e4m3", "e5m2") else 1.0
-    return float(np.abs(vals).max()) * scale
+    return float(np.abs(vals).max()) * per_tensor
 
 
 def parity_check(w, d_values, rows, cols, ref=None) -> dict:

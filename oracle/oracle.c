@@ -20,9 +20,12 @@
  *   for B with SFB(j, floor(p/32)): same document, "Blackwell SM100 GEMMs",
  *   "Block Scaled GEMMs" (index-notation formula), vector size 32 for the OCP
  *   mx types ("Blackwell Block Scaled Narrow Precision Data Types" table).
- * - The element formats (e4m3, e5m2, e2m1, ue8m0 bit counts and signedness): same
- *   document, "Blackwell Narrow Precision Data Types" table; the bit-level
- *   meaning of each code follows the OCP formats that table points to.
+ * - The element formats (e4m3, e5m2, e2m1, e2m3, e3m2, ue8m0 bit counts and
+ *   signedness): same document, "Blackwell Narrow Precision Data Types" table;
+ *   the bit-level meaning of each code follows the OCP formats that table
+ *   points to.  The pages fix no byte packing for the 6-bit types; the reading
+ *   taken is the plainest one, the same as for the 4-bit type: consecutive
+ *   elements fill a little-endian bit stream, lowest bits first.
  * - The epilogue (bias, activation) applied to the GEMM result before the
  *   store: knowledge-base page, "Epilogues".
  *
@@ -54,6 +57,8 @@ enum {
     ORC_E2M1 = 6, /* two OCP fp4 codes per byte, even element in the low nibble */
     ORC_E8M0 = 7,
     ORC_E5M2 = 9,
+    ORC_E2M3 = 10, /* OCP fp6 E2M3, bit-packed: element t in bits 6t .. 6t+5 of the little-endian stream */
+    ORC_E3M2 = 11, /* OCP fp6 E3M2, packed the same way */
 };
 
 enum { ORC_ACT_NONE = 0, ORC_ACT_RELU = 1, ORC_ACT_GELU = 2 };
@@ -171,6 +176,46 @@ static double dec_e2m1(unsigned nib)
     return s ? -mag : mag;
 }
 
+/* OCP E2M3 (fp6): 1 sign, 2 exponent (bias 1), 3 mantissa bits; all codes
+ * finite, largest magnitude 1.875 * 2^2 = 7.5, smallest subnormal 2^-3. */
+static double dec_e2m3(unsigned c)
+{
+    int s = (c >> 5) & 1, e = (c >> 3) & 3, f = c & 7;
+    double mag;
+    if (e == 0)
+        mag = ldexp((double)f, -3); /* f/8 * 2^0 */
+    else
+        mag = ldexp((double)(8 + f), e - 4); /* (1 + f/8) * 2^(e-1) */
+    return s ? -mag : mag;
+}
+
+/* OCP E3M2 (fp6): 1 sign, 3 exponent (bias 3), 2 mantissa bits; all codes
+ * finite, largest magnitude 1.75 * 2^4 = 28, smallest subnormal 2^-4. */
+static double dec_e3m2(unsigned c)
+{
+    int s = (c >> 5) & 1, e = (c >> 2) & 7, f = c & 3;
+    double mag;
+    if (e == 0)
+        mag = ldexp((double)f, -4); /* f/4 * 2^-2 */
+    else
+        mag = ldexp((double)(4 + f), e - 5); /* (1 + f/4) * 2^(e-3) */
+    return s ? -mag : mag;
+}
+
+/* The 6-bit code of element idx of a bit-packed fp6 buffer: bits 6*idx ..
+ * 6*idx+5 of the buffer read as one little-endian bit stream (element 0 in
+ * the low six bits of byte 0; four elements fill three bytes). */
+static unsigned fp6_code(const uint8_t *base, int64_t idx)
+{
+    int64_t bit = 6 * idx;
+    int64_t byte = bit >> 3;
+    int shift = (int)(bit & 7);
+    unsigned w = base[byte];
+    if (shift > 2)
+        w |= (unsigned)base[byte + 1] << 8;
+    return (w >> shift) & 63u;
+}
+
 /* OCP E8M0 scale: 8 exponent bits, bias 127, no sign or mantissa; 0xff NaN. */
 static double dec_e8m0(uint8_t x)
 {
@@ -213,6 +258,10 @@ static double load_real(const void *base, int32_t type, int64_t idx)
         return dec_e8m0(((const uint8_t *)base)[idx]);
     case ORC_E5M2:
         return dec_e5m2(((const uint8_t *)base)[idx]);
+    case ORC_E2M3:
+        return dec_e2m3(fp6_code((const uint8_t *)base, idx));
+    case ORC_E3M2:
+        return dec_e3m2(fp6_code((const uint8_t *)base, idx));
     }
     return NAN;
 }
@@ -232,7 +281,7 @@ static int64_t load_int(const void *base, int32_t type, int64_t idx)
 /* Public decoder, so that tests can pin each format on every code. */
 int oracle_decode(int32_t type, const void *src, int64_t count, double *out)
 {
-    if (type < ORC_F32 || (type > ORC_E8M0 && type != ORC_E5M2))
+    if (type < ORC_F32 || type > ORC_E3M2 || type == 8)
         return -1;
     for (int64_t t = 0; t < count; ++t)
         out[t] = load_real(src, type, t);

@@ -150,3 +150,33 @@ def test_operand_max_mx_e5m2_keeps_the_per_tensor_scale():
            sfb=sfa.copy(), ld_sfb=16, a_scale=0.25, b_scale=1.0)
     assert compare.operand_max_abs(w, "a") == 14.0
     assert compare.operand_max_abs(w, "b") == 56.0
+
+
+def test_operand_max_m_major_block_scaled():
+    # A stored along M (op N): 64 k-lines of lda = 2 e4m3 codes.  A(0, 5) = 448
+    # (0x7E) at SFA(0, 0) = 2^-3 -> 56; A(1, 40) = 2 (0x40) at SFA(1, 1) = 2^4
+    # -> 32; A(0, 40) = 1 (0x38) at SFA(0, 1) = 2^-8.  max |a'| = 56.  Read as
+    # K-major rows (the wrong way) the same bytes give 448 * 2^-3 in no place
+    # and 2 at scale 2^4 in row 0 (32), so the maximum would differ.
+    a = np.zeros((64, 2), np.uint8)
+    a[5, 0], a[40, 1], a[40, 0] = 0x7E, 0x40, 0x38
+    sfa = _mx_scales(2, [[124, 119], [127, 131]], 0xFF)
+    b = np.zeros((1, 64), np.uint8)
+    b[0, 0] = 0x38
+    sfb = _mx_scales(1, [[127, 127]], 0xFF)
+    w = _w(m=2, n=1, k=64, lda=2, ldb=64, op_a="N", type_a="e4m3", type_b="e4m3", a=a, b=b, sfa=sfa, ld_sfa=16,
+           sfb=sfb, ld_sfb=16)
+    assert compare.operand_max_abs(w, "a") == 56.0
+    assert compare.operand_max_abs(w, "b") == 1.0
+
+
+def test_operand_max_fp6_packed():
+    # B: one row of 64 E3M2 codes, bit-packed; code 0b011111 (28) at K 9 and
+    # 0b000001 (0.0625) at K 40; no scales (plain fp6 takes no per-tensor
+    # scale either: b_scale = 8 is ignored) -> 28
+    acc = (0b011111 << (6 * 9)) | (0b000001 << (6 * 40))
+    b = np.frombuffer(acc.to_bytes(48, "little"), np.uint8).reshape(1, 48).copy()
+    a = np.zeros((1, 48), np.uint8)
+    w = _w(k=64, lda=64, ldb=64, type_a="e3m2", type_b="e3m2", a=a, b=b, b_scale=8.0)
+    assert compare.operand_max_abs(w, "b") == 28.0
+    assert compare.operand_max_abs(w, "a") == 0.0

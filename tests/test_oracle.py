@@ -9,6 +9,7 @@ cases.
 """
 import math
 import os
+import zlib
 from fractions import Fraction
 
 import numpy as np
@@ -705,3 +706,109 @@ def test_mx_blocks_agree_with_the_input_generators_quantizer(fmt):
             codes, sc = oracle.mx_quantize_block(x[r, 32 * b: 32 * b + 32], fmt)
             assert sc == want_sc[r, b]
             assert codes.tolist() == want_codes[r, 32 * b: 32 * b + 32].tolist()
+
+
+# ------------------------------------------------------------- fp6 and mixed narrow formats
+
+def _fp6_stream(codes):
+    """Bytes of 6-bit codes laid out as one little-endian bit stream (element
+    t in bits 6t .. 6t+5), built with Python integers."""
+    acc = 0
+    for t, c in enumerate(codes):
+        acc |= int(c) << (6 * t)
+    nbytes = (6 * len(codes) + 7) // 8
+    return np.frombuffer(acc.to_bytes(nbytes, "little"), dtype=np.uint8).copy()
+
+
+@pytest.mark.parametrize("fmt,table", [("e2m3", "float_e2m3_t"), ("e3m2", "float_e3m2_t")])
+def test_fp6_matches_table_bit_counts(fmt, table):
+    # every one of the 64 codes: the table's exponent and mantissa widths,
+    # bias 2^(e-1) - 1, gradual underflow, no special encodings (OCP fp6)
+    spec = _format_table()[table]
+    assert spec["bits"] == 6 and spec["signed"]
+    got = oracle.decode(fmt, _fp6_stream(range(64)), 64)
+    for c in range(64):
+        assert Fraction(got[c]) == _minifloat(c, spec["e"], spec["m"], True), (fmt, c)
+
+
+@pytest.mark.parametrize("fmt,extremes", [
+    # OCP MX specification, fp6 format table: max normal, min normal, max subnormal, min subnormal
+    ("e2m3", (7.5, 1.0, 0.875, 0.125)),
+    ("e3m2", (28.0, 0.25, 0.1875, 0.0625)),
+])
+def test_fp6_published_extremes(fmt, extremes):
+    e_bits = 2 if fmt == "e2m3" else 3
+    m_bits = 5 - e_bits
+    max_norm = 0b011111
+    min_norm = 1 << m_bits
+    max_sub = (1 << m_bits) - 1
+    got = oracle.decode(fmt, _fp6_stream([max_norm, min_norm, max_sub, 1]), 4)
+    assert tuple(got) == extremes
+    neg = oracle.decode(fmt, _fp6_stream([32 | max_norm]), 1)
+    assert neg[0] == -extremes[0]
+
+
+def test_fp6_packing_by_hand():
+    # E2M3 codes 0b000001 (0.125), 0b011111 (7.5), 0b100000 (-0), 0b111111 (-7.5)
+    # in one 24-bit little-endian word: 0xFE07C1 -> bytes C1 07 FE
+    got = oracle.decode("e2m3", np.array([0xC1, 0x07, 0xFE], np.uint8), 4)
+    assert list(got) == [0.125, 7.5, 0.0, -7.5] and math.copysign(1, got[2]) == -1
+    # an element straddling a byte: element 1 of E3M2 occupies bits 6 .. 11
+    got = oracle.decode("e3m2", np.array([0b11000000, 0b00000111, 0], np.uint8), 4)
+    assert list(got) == [0.0, 28.0, 0.0, 0.0]
+
+
+def _narrow_values(fmt, g, shape):
+    """Random exact values of a narrow format and their stored codes, from
+    the format table's bit counts (codes first, values by _minifloat)."""
+    spec = {"e4m3": (4, 3, 8), "e5m2": (5, 2, 8), "e2m3": (2, 3, 6), "e3m2": (3, 2, 6), "e2m1": (2, 1, 4)}[fmt]
+    e_bits, m_bits, bits = spec
+    codes = g.integers(0, 1 << bits, size=shape)
+    if fmt == "e4m3":  # skip the NaN codes
+        codes = np.where((codes & 0x7F) == 0x7F, codes ^ 1, codes)
+    if fmt == "e5m2":  # and the infinities / NaNs
+        codes = np.where((codes & 0x7C) == 0x7C, codes & 0x83, codes)
+    vals = np.vectorize(lambda c: _minifloat(int(c), e_bits, m_bits, True), otypes=[object])(codes)
+    return codes.astype(np.uint8), vals
+
+
+def _stored(codes_rows, fmt, kmajor, ld):
+    lines = codes_rows if kmajor else codes_rows.T
+    mem = np.zeros((lines.shape[0], ld), np.uint8)
+    mem[:, : lines.shape[1]] = lines
+    if fmt == "e2m1":
+        return wl.pack_e2m1(mem)
+    if fmt in ("e2m3", "e3m2"):
+        return np.concatenate([_fp6_stream(row) for row in mem]).reshape(mem.shape[0], -1)
+    return mem
+
+
+@pytest.mark.parametrize("fa,fb", [("e2m3", "e2m3"), ("e3m2", "e3m2"), ("e2m3", "e3m2"), ("e4m3", "e2m1"),
+                                   ("e2m1", "e5m2"), ("e3m2", "e4m3"), ("e2m1", "e2m3")])
+@pytest.mark.parametrize("ops", [("T", "N"), ("N", "N"), ("T", "T"), ("N", "T")])
+@pytest.mark.parametrize("mx", [False, True])
+def test_bruteforce_exact_narrow_pairs_in_every_layout(fa, fb, ops, mx):
+    # random codes of each format, stored in the given layout (fp6 packed into
+    # a bit stream, fp4 two a byte), against exact rational arithmetic on the
+    # values the format table defines; block scales (MX) per 32 K-elements of
+    # each logical row whatever the storage
+    g = np.random.default_rng(zlib.crc32(f"{fa}{fb}{ops}{mx}".encode()))
+    m, n, k = 5, 3, 64
+    ca, va = _narrow_values(fa, g, (m, k))
+    cb, vb = _narrow_values(fb, g, (n, k))
+    a_km, b_km = ops[0] == "T", ops[1] == "N"
+    lda = 68 if a_km else 8
+    ldb = 68 if b_km else 4
+    p = dict(m=m, n=n, k=k, a=_stored(ca, fa, a_km, lda), lda=lda, op_a=ops[0], type_a=fa,
+             b=_stored(cb, fb, b_km, ldb), ldb=ldb, op_b=ops[1], type_b=fb, alpha=0.5)
+    ex = {}
+    if mx:
+        sfa = g.integers(120, 134, size=(m, k // 32)).astype(np.uint8)
+        sfb = g.integers(120, 134, size=(n, k // 32)).astype(np.uint8)
+        p.update(sfa=sfa, ld_sfa=k // 32, sfb=sfb, ld_sfb=k // 32)
+        ex = dict(sfa=sfa, sfb=sfb)
+    got = _full(p)
+    want = _exact_reference(fa, va, vb.T, alpha=0.5, **ex)
+    for i in range(m):
+        for j in range(n):
+            assert abs(Fraction(got[i, j]) - want[i, j]) <= Fraction(2) ** -48 * (1 + abs(want[i, j])), (i, j)

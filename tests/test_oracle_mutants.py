@@ -61,6 +61,12 @@ MUTANTS = [
     ("MX output: element sign dropped", "codes[t] = (uint8_t)(best | (signbit(vals[t]) ? (1 << sign_bit) : 0));",
      "codes[t] = (uint8_t)best;"),
     ("MX output: E5M2 clamps one code short", "emax = 15; ncodes = 124;", "emax = 15; ncodes = 123;"),
+    ("e2m3 exponent bias", "ldexp((double)(8 + f), e - 4)", "ldexp((double)(8 + f), e - 3)"),
+    ("e3m2 mantissa width", "ldexp((double)(4 + f), e - 5)", "ldexp((double)(4 + f), e - 4)"),
+    ("e3m2 subnormal scale", "ldexp((double)f, -4); /* f/4 * 2^-2 */", "ldexp((double)f, -3); /* f/4 * 2^-2 */"),
+    ("fp6 bits straddling a byte dropped at shift 4", "if (shift > 2)", "if (shift > 4)"),
+    ("fp6 elements a byte apart", "int64_t bit = 6 * idx;", "int64_t bit = 8 * idx;"),
+    ("fp6 sign bit taken from the exponent", "int s = (c >> 5) & 1, e = (c >> 2) & 7", "int s = (c >> 4) & 1, e = (c >> 2) & 7"),
 ]
 
 # Mistakes planted in the comparison (oracle/compare.py), caught by
@@ -71,9 +77,12 @@ COMPARE_MUTANTS = [
     ("block scales not applied", "vals = vals.reshape(rows, w.k // 32, 32) * scales[:, :, None]",
      "vals = vals.reshape(rows, w.k // 32, 32) * 1.0"),
     ("per-tensor fp8 scale ignored",
-     'scale = (w.a_scale if which == "a" else w.b_scale) if fmt in ("e4m3", "e5m2") else 1.0', "scale = 1.0"),
+     'per_tensor = (w.a_scale if which == "a" else w.b_scale) if fmt in ("e4m3", "e5m2") else 1.0',
+     "per_tensor = 1.0"),
+    ("M-major operand read as if K-major", "return vals[:rows, : w.k] if kmajor else vals[: w.k, :rows].T",
+     "return vals[:rows, : w.k] if True else vals"),
     ("operand B's maximum taken from A", 'raw = w.a if which == "a" else w.b', "raw = w.a"),
-    ("scale padding read as blocks", "[:, : w.k // 32]", "[:, : w.k // 32 + 1][:, 1:]"),
+    ("scale padding read as blocks", "[:rows, : w.k // 32]", "[:rows, : w.k // 32 + 1][:, 1:]"),
     ("gelu factor dropped", 'g = 1.13 if act == "gelu" else 1.0', "g = 1.0"),
     ("alpha dropped", "* k * abs(alpha) *", "* k *"),
     ("K dropped", "term = 2.0 ** -20 * k *", "term = 2.0 ** -20 *"),

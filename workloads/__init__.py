@@ -21,7 +21,8 @@ import torch
 TENSOR_IDS = {"a": 1, "b": 2, "c": 3, "bias": 4, "sample": 5}
 
 # Bytes per element of each stored format (fp4 packs two per byte).
-ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "i32": 4, "e4m3": 1, "e5m2": 1, "e2m1": 0.5}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "i32": 4, "e4m3": 1, "e5m2": 1, "e2m1": 0.5, "e2m3": 0.75,
+              "e3m2": 0.75}
 
 
 def rng(seed: int, tensor: str) -> np.random.Generator:
@@ -114,6 +115,53 @@ def mx_quantize_e4m3(x: np.ndarray, block: int = 32):
     return mx_quantize_fp8(x, "e4m3", block)
 
 
+# OCP fp6 formats: (exponent bits, mantissa bits, largest exponent); bias
+# 2^(e-1) - 1, every code finite.
+_FP6 = {"e2m3": (2, 3, 2), "e3m2": (3, 2, 4)}
+
+
+def _fp6_magnitudes(fmt: str) -> np.ndarray:
+    """Magnitude of each non-negative fp6 code 0 .. 31, in code order."""
+    e_bits, m_bits, _ = _FP6[fmt]
+    bias = 2 ** (e_bits - 1) - 1
+    out = []
+    for c in range(32):
+        e, f = c >> m_bits, c & ((1 << m_bits) - 1)
+        frac = f / 2 ** m_bits
+        out.append(frac * 2.0 ** (1 - bias) if e == 0 else (1 + frac) * 2.0 ** (e - bias))
+    return np.array(out)
+
+
+def encode_fp6_codes(v: np.ndarray, fmt: str) -> np.ndarray:
+    """Round to the nearest value of an fp6 format (E2M3 or E3M2), ties to the
+    even code, saturating at the largest magnitude; one 6-bit code per
+    element (uint8, sign in bit 5)."""
+    mags = _fp6_magnitudes(fmt)
+    mid = (mags[1:] + mags[:-1]) / 2
+    a = np.abs(v)
+    idx = np.searchsorted(mid, a, side="left")
+    at = np.minimum(idx, mid.size - 1)
+    idx = idx + ((idx < mid.size) & (a == mid[at]) & (idx % 2 == 1))
+    return (idx.astype(np.uint8) | (np.signbit(v).astype(np.uint8) << 5)).astype(np.uint8)
+
+
+def mx_quantize_fp6(x: np.ndarray, fmt: str, block: int = 32):
+    """OCP MX quantization of rows of ``x`` (R x K, K % block == 0) to an fp6
+    format: shared exponent floor(log2(amax)) - emax (2 for E2M3, 4 for E3M2),
+    clamped to [-127, 127]; elements x / 2^X rounded to the format.  Returns
+    (codes R x K uint8, scale codes R x K/block uint8)."""
+    emax = _FP6[fmt][2]
+    r, k = x.shape
+    xb = x.reshape(r, k // block, block)
+    amax = np.abs(xb).max(axis=2)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - emax
+    e = np.clip(e, -127, 127)
+    e = np.where(amax > 0, e, -127)
+    codes = encode_fp6_codes(xb / np.ldexp(1.0, e.astype(np.int64))[:, :, None], fmt)
+    return codes.reshape(r, k), (e + 127).astype(np.uint8)
+
+
 # ----------------------------------------------------------------- storage
 
 def store_colmajor(s: np.ndarray, ld: int) -> np.ndarray:
@@ -131,6 +179,17 @@ def pack_e2m1(mem_codes: np.ndarray) -> np.ndarray:
     the low nibble."""
     assert mem_codes.shape[-1] % 2 == 0
     return (mem_codes[..., 0::2] | (mem_codes[..., 1::2] << 4)).astype(np.uint8)
+
+
+def pack_fp6(mem_codes: np.ndarray) -> np.ndarray:
+    """Four 6-bit codes in three bytes along the contiguous dimension: element
+    t in bits 6t .. 6t+5 of the little-endian bit stream."""
+    n = mem_codes.shape[-1]
+    assert n % 4 == 0
+    c = mem_codes.astype(np.uint32).reshape(*mem_codes.shape[:-1], n // 4, 4)
+    w = c[..., 0] | (c[..., 1] << 6) | (c[..., 2] << 12) | (c[..., 3] << 18)
+    out = np.stack([w & 255, (w >> 8) & 255, (w >> 16) & 255], axis=-1)
+    return out.reshape(*mem_codes.shape[:-1], n // 4 * 3).astype(np.uint8)
 
 
 def stored_shape(rows: int, cols: int, op: str, which: str):
@@ -362,4 +421,76 @@ def make(kind: str, m: int, n: int, k: int, seed: int | None = None, *, op_a=Non
             w["bias"], w["type_bias"] = encode(gbias.standard_normal(m), tb), tb
     else:
         raise ValueError(kind)
+    return Workload(**w)
+
+
+# ------------------------------------------------------ narrow-format pairs
+
+_LD_QUANTUM = {"e2m1": 2, "e2m3": 4, "e3m2": 4}  # elements a stored line is padded to (whole bytes)
+_TOP = {"e4m3": 448.0, "e5m2": 57344.0}
+
+
+def _narrow_codes(g, rows: int, k: int, fmt: str, mx: bool):
+    """Codes (rows x k, uint8) of N(0,1) draws in ``fmt``: MX-quantized per 32
+    K-elements (returns the scale codes too), or, without block scales, fp8
+    scaled per tensor to its largest magnitude and fp4 / fp6 drawn in range."""
+    x = g.standard_normal((rows, k))
+    if mx:
+        if fmt == "e2m1":
+            return mx_quantize(x) + (1.0,)
+        if fmt in _FP6:
+            return mx_quantize_fp6(x, fmt) + (1.0,)
+        return mx_quantize_fp8(x, fmt) + (1.0,)
+    if fmt == "e2m1":
+        return encode_e2m1_codes(2.0 * x), None, 1.0
+    if fmt in _FP6:
+        return encode_fp6_codes(2.0 * x if fmt == "e2m3" else 6.0 * x, fmt), None, 1.0
+    s = float(np.float32((float(np.abs(x).max()) / _TOP[fmt]) or 1.0)) if x.size else 1.0
+    return encode(x / s, fmt), None, s
+
+
+def _store_lines(codes_rows: np.ndarray, kmajor: bool, ld: int, fmt: str) -> np.ndarray:
+    """Stored bytes of an operand given as logical rows x K codes: K-major
+    lines are the rows, otherwise the K-indices; packed for fp4 / fp6."""
+    lines = codes_rows if kmajor else codes_rows.T
+    mem = np.zeros((lines.shape[0], ld), np.uint8)
+    mem[:, : lines.shape[1]] = lines
+    if fmt == "e2m1":
+        return pack_e2m1(mem)
+    if fmt in _FP6:
+        return pack_fp6(mem)
+    return mem
+
+
+def make_narrow(type_a: str, type_b: str, m: int, n: int, k: int, *, mx: bool, op_a: str = "T", op_b: str = "N",
+                lda=None, ldb=None, seed: int = 1020, type_d: str = "bf16", beta: float = 0.0, act: str = "none",
+                bias: bool = False, alpha: float = 1.0, ldd=None) -> Workload:
+    """A GEMM over any pair of the 8-, 6- and 4-bit float formats (e4m3, e5m2,
+    e2m3, e3m2, e2m1) in any layout: N(0,1) operands, MX-quantized per 32
+    K-elements when ``mx`` (scale rows padded to 16 bytes with 127), else fp8
+    per-tensor scaled and fp4 / fp6 in range; C (when beta != 0) and bias
+    bf16 N(0,1)."""
+    ga, gb, gc, gbias = rng(seed, "a"), rng(seed, "b"), rng(seed, "c"), rng(seed, "bias")
+    ca, sfa, sa = _narrow_codes(ga, m, k, type_a, mx)
+    cb, sfb, sb = _narrow_codes(gb, n, k, type_b, mx)
+    a_km, b_km = op_a == "T", op_b == "N"
+    qa, qb = _LD_QUANTUM.get(type_a, 1), _LD_QUANTUM.get(type_b, 1)
+    lda = lda or max(qa, -(-(k if a_km else m) // qa) * qa)
+    ldb = ldb or max(qb, -(-(k if b_km else n) // qb) * qb)
+    w = dict(name=f"{'mx' if mx else ''}{type_a}x{type_b}", m=m, n=n, k=k, type_a=type_a, type_b=type_b,
+             type_d=type_d, op_a=op_a, op_b=op_b, lda=lda, ldb=ldb, ldd=ldd or max(1, m), seed=seed, alpha=alpha,
+             a=_store_lines(ca, a_km, lda, type_a), b=_store_lines(cb, b_km, ldb, type_b), a_scale=sa, b_scale=sb,
+             beta=beta, act=act)
+    if mx:
+        ld_sf = max(16, (k // 32 + 15) // 16 * 16)
+        pa = np.full((m, ld_sf), 127, np.uint8)
+        pa[:, : k // 32] = sfa
+        pb = np.full((n, ld_sf), 127, np.uint8)
+        pb[:, : k // 32] = sfb
+        w.update(sfa=pa, sfb=pb, ld_sfa=ld_sf, ld_sfb=ld_sf)
+    if beta != 0.0:
+        w.update(c=store_colmajor(encode(gc.standard_normal((m, n)), "bf16"), max(1, m)), ldc=max(1, m),
+                 type_c="bf16")
+    if bias:
+        w.update(bias=encode(gbias.standard_normal(m), "bf16"), type_bias="bf16")
     return Workload(**w)
