@@ -59,12 +59,16 @@ typedef enum {
   THL_E2M1X2 = 6, /* OCP fp4 E2M1, two per byte along the contiguous dimension, even element low nibble */
   THL_E8M0 = 7,   /* OCP E8M0 scale: 2^(code-127), 0xff NaN */
   THL_NONE = 8,   /* "no such operand" (bias dtype when there is no bias) */
-  THL_E5M2 = 9    /* OCP fp8 E5M2 (bias 15, IEEE-style: S.11111.00 infinity, S.11111.xx NaN, max 57344) */
+  THL_E5M2 = 9,   /* OCP fp8 E5M2 (bias 15, IEEE-style: S.11111.00 infinity, S.11111.xx NaN, max 57344) */
+  THL_E2M3 = 10,  /* OCP fp6 E2M3 (bias 1, all codes finite, max 7.5), bit-packed along the contiguous
+                     dimension: element t in bits 6t .. 6t+5 of the little-endian bit stream (four in
+                     three bytes) */
+  THL_E3M2 = 11   /* OCP fp6 E3M2 (bias 3, all codes finite, max 28), packed as THL_E2M3 */
 } thl_dtype;
 
 typedef struct {
-  thl_dtype a, b; /* operand formats: a == b (F16, BF16, I8, E4M3, E5M2, E2M1X2), or one of
-                     E4M3 / E5M2 for a and the other for b (mixed fp8) */
+  thl_dtype a, b; /* operand formats: a == b (F16, BF16, I8), or any two of E4M3, E5M2, E2M3,
+                     E3M2, E2M1X2 (the 8-, 6- and 4-bit float formats, mixed freely) */
   thl_dtype c;    /* format of C: F32, F16 or BF16 for float paths, I32 for the int8 path */
   thl_dtype d;    /* format of D: F32, F16 or BF16 (float paths), I32 (int8 path) */
   thl_dtype bias; /* format of the bias vector: F32, F16, BF16, or I32 (int8 path) */
@@ -87,8 +91,10 @@ typedef struct {
 typedef struct {
   float a_scale, b_scale; /* per-tensor scales (host values), used for E4M3 and E5M2 (also mixed and
                              MXFP8); ignored (taken as 1) for the other formats */
-  const uint8_t* sfa;     /* E8M0 block scales of A for E2M1X2 (required) and E4M3 (MXFP8, with sfb):
-                             SFA(i,kb) at sfa[i*ld_sfa + kb], device, 16-byte aligned; NULL otherwise */
+  const uint8_t* sfa;     /* E8M0 block scales of A for the MX formats (8-, 6- or 4-bit elements, with
+                             sfb): SFA(i,kb) for row i of op(A) and K-elements 32kb .. 32kb+31 at
+                             sfa[i*ld_sfa + kb], whatever A's storage, device, 16-byte aligned; NULL
+                             for plain formats */
   int64_t ld_sfa;         /* >= k/32 and a multiple of 16 */
   const uint8_t* sfb;     /* SFB(j,kb) at sfb[j*ld_sfb + kb], device, 16-byte aligned; as sfa */
   int64_t ld_sfb;         /* >= k/32 and a multiple of 16 */
@@ -102,7 +108,9 @@ typedef struct {
  *   opA = N: A(i,p) at A[i + p*lda], lda >= max(1,m);   opA = T: at A[p + i*lda], lda >= max(1,k)
  *   opB = N: B(p,j) at B[p + j*ldb], ldb >= max(1,k);   opB = T: at B[j + p*ldb], ldb >= max(1,n)
  *   C(i,j) at C[i + j*ldc], ldc >= max(1,m);  D(i,j) at D[i + j*ldd], ldd >= max(1,m).
- * For E2M1X2 the leading dimension counts fp4 elements and must be even.
+ * For E2M1X2 the leading dimension counts fp4 elements and must be even; for
+ * E2M3 and E3M2 it counts fp6 elements and must be a multiple of 4 (so that
+ * every stored line starts on a whole byte); batch strides likewise.
  *
  * Built combinations (first fitting kernel is launched):
  *   F16 or BF16 operands, opA/opB in {N,T}: F32 accumulate; C, D in F32/F16/BF16.
@@ -119,6 +127,26 @@ typedef struct {
  *   E2M1X2 operands, opA = T, opB = N, k % 32 == 0: F32 accumulate, element
  *     (i,p) of A multiplied by 2^(SFA(i, p/32) - 127), likewise B with SFB(j, p/32);
  *     scale rows 16-byte aligned (THL_ERR_MISALIGNED otherwise).
+ *   Every other layout and pairing of the 8-, 6- and 4-bit formats ("Technical
+ *   Documentation: NVIDIA/cutlass", "Layouts, Tensor Alignment Requirements to
+ *   Target tcgen05.mma Instructions", Tables 2 and 3: TN, NN, NT, TT, dense or
+ *   with E8M0 block scales per 32 K-elements), and I8 in NN, NT, TT: each
+ *   operand the tiled kernels cannot stage directly (stored along M or N,
+ *   6-bit, or 4-bit beside another format or without block scales) is first
+ *   rewritten by a conversion pass into a workspace as K-major rows (variant
+ *   name suffix "+cvt_a", "+cvt_b" or "+cvt_ab"): 8-bit formats as they are,
+ *   E2M1X2 as E2M1X2 when both operands are block-scaled fp4, and E2M1X2, E2M3
+ *   and E3M2 otherwise widened to E4M3, which holds each of their values
+ *   exactly; then the TN kernels above run.  Block scales, when given (both
+ *   sfa and sfb, k % 32 == 0), apply per logical row and 32 K-elements
+ *   whatever the storage; the per-tensor scales apply to E4M3 and E5M2
+ *   operands only.  The workspace is
+ *   taken from a stream-ordered pool (THL_ERR_HIP if none can be had) and
+ *   returned after the launch; thl_gemm_noalloc takes it from its static
+ *   scratch (THL_ERR_SCRATCH when it does not fit).  The pass costs one read
+ *   of the operand and one write of its K-major copy (HBM-bound); 6-bit and
+ *   widened 4-bit operands then run at the fp8 MFMA rate.  Grouped launches
+ *   take only what the kernels stage directly (THL_ERR_UNSUPPORTED otherwise).
  * With m <= 64, k > 0, opA = T and opB = N (any operand family but MXFP8), A and B
  * 16-byte aligned with leading dimensions of whole 16-byte units, the small-M
  * kernel runs (variants "<family>_tn_skinny{16,32,64}_k4", the first whose
@@ -163,9 +191,10 @@ typedef struct {
  * (THL_ERR_INVALID, as a NULL sfd or a short ld_sfd is).
  *
  * Block scales: sfa or sfb given with F16, BF16 or I8 operands is
- * THL_ERR_UNSUPPORTED.  fp8 operands with either array given are MX fp8;
- * E2M1X2 always is.  Both arrays are then required (THL_ERR_INVALID
- * otherwise) whenever m > 0, n > 0 and k > 0.
+ * THL_ERR_UNSUPPORTED.  8-, 6- and 4-bit operands with either array given are
+ * MX (MXFP8, MXFP6, MXFP4 or a mix); without either they are plain (dense)
+ * formats.  Both arrays are then required (THL_ERR_INVALID otherwise)
+ * whenever m > 0, n > 0 and k > 0.
  *
  * Semantics: beta == 0 means C is not read (it may be NULL and may hold NaN).
  * D may alias C exactly (same pointer, ldc == ldd, c and d the same format);

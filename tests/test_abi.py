@@ -104,11 +104,8 @@ def test_unsupported_combinations():
     assert call(types=("i8", "f32", "f32", "none")) == thl.THL_ERR_UNSUPPORTED  # int8 needs int32 out
     assert call(types=("i8", "i32", "i32", "none"), alpha=2.0) == thl.THL_ERR_UNSUPPORTED
     assert call(types=("i8", "i32", "i32", "none"), beta=0.5, c=C) == thl.THL_ERR_UNSUPPORTED
-    assert call(types=("i8", "i32", "i32", "none"), opa="N") == thl.THL_ERR_UNSUPPORTED
     sc = thl.thl_scales(1.0, 1.0, SFA, 1, SFB, 1)
     assert call(types=("e2m1", "f32", "bf16", "none"), k=48, sc=sc) == thl.THL_ERR_UNSUPPORTED  # k % 32
-    assert call(types=("e4m3", "f32", "bf16", "none"), opb="T") == thl.THL_ERR_UNSUPPORTED
-    assert call(types=("e5m2", "f32", "bf16", "none"), opa="N") == thl.THL_ERR_UNSUPPORTED
     mixed = thl.make_dtypes("e4m3", "bf16", "f32", "bf16")  # mixed only within fp8
     assert thl.thl_gemm(64, 64, 64, A, 64, "T", B, 64, "N", None, 64, D, 64, 1.0, 0.0, mixed, None, None,
                         None) == thl.THL_ERR_UNSUPPORTED
@@ -151,8 +148,13 @@ def test_fp8_block_scales_both_or_neither(fa, fb, mx, plain):
     assert thl.thl_last_variant().startswith(plain)
 
 
-def test_mxfp4_needs_scales():
-    assert call(types=("e2m1", "f32", "bf16", "none"), sc=None) == thl.THL_ERR_INVALID
+def test_mxfp4_needs_both_scale_arrays():
+    # one array without the other is refused; none at all is plain fp4 (run
+    # by way of the conversion pass, so only the quick return works here)
+    assert call(types=("e2m1", "f32", "bf16", "none"), sc=thl.thl_scales(1.0, 1.0, SFA, 16, None, 0)) == \
+        thl.THL_ERR_INVALID
+    assert call(types=("e2m1", "f32", "bf16", "none"), sc=None, m=0) == thl.THL_OK
+    assert thl.thl_last_variant().endswith("+cvt_ab")
     sc = thl.thl_scales(1.0, 1.0, SFA, 1, SFB, 2)  # ld_sfa < k/32
     assert call(types=("e2m1", "f32", "bf16", "none"), sc=sc) == thl.THL_ERR_INVALID
     sc = thl.thl_scales(1.0, 1.0, SFA, 4, SFB, 4)
@@ -207,25 +209,31 @@ def test_small_m_selection(fam, ta, td):
     tc = "i32" if ta == "i8" else "f32"
     types = (ta, tc, td, "none")
     k = 8192
+    # MXFP4 with its block scales (E2M1 without them is plain fp4, run by way of fp8)
+    sc = thl.thl_scales(1.0, 1.0, SFA, 256, SFB, 256) if ta == "e2m1" else None
+
+    def go(**kw):
+        return call(sc=sc, **kw)
+
     for m, rows in ((1, 16), (7, 16), (16, 16), (17, 32), (32, 32), (33, 64), (64, 64)):
-        assert call(m=m, n=0, k=k, types=types) == thl.THL_OK
+        assert go(m=m, n=0, k=k, types=types) == thl.THL_OK
         assert thl.thl_last_variant() == f"{fam}_tn_skinny{rows}_k4"
-    assert call(m=65, n=0, k=k, types=types) == thl.THL_OK
+    assert go(m=65, n=0, k=k, types=types) == thl.THL_OK
     assert "skinny" not in thl.thl_last_variant()
     # k == 0, or operands that are not 16-byte units: the tiled kernels
-    assert call(m=1, n=0, k=0, lda=64, ldb=64, types=types) == thl.THL_OK
+    assert go(m=1, n=0, k=0, lda=64, ldb=64, types=types) == thl.THL_OK
     assert "skinny" not in thl.thl_last_variant()
-    assert call(m=1, n=0, k=k, a=A + 4, types=types) == thl.THL_OK
+    assert go(m=1, n=0, k=k, a=A + 4, types=types) == thl.THL_OK
     assert "skinny" not in thl.thl_last_variant()
     if fam in ("bf16", "f16"):  # M-major A: the tiled kernels
-        assert call(m=1, n=0, k=k, opa="N", lda=8, types=types) == thl.THL_OK
+        assert go(m=1, n=0, k=k, opa="N", lda=8, types=types) == thl.THL_OK
         assert "skinny" not in thl.thl_last_variant()
     # forcing a small-M variant on more rows than it covers is refused
     for rows in (16, 64):
         os.environ["THL_FORCE_VARIANT"] = f"{fam}_tn_skinny{rows}_k4"
         try:
-            assert call(m=rows, n=0, k=k, types=types) == thl.THL_OK
-            assert call(m=rows + 1, n=0, k=k, types=types) == thl.THL_ERR_UNSUPPORTED
+            assert go(m=rows, n=0, k=k, types=types) == thl.THL_OK
+            assert go(m=rows + 1, n=0, k=k, types=types) == thl.THL_ERR_UNSUPPORTED
         finally:
             del os.environ["THL_FORCE_VARIANT"]
 
@@ -376,3 +384,47 @@ def test_mx_output_needs_16_byte_operand_rows():
     types = ("bf16", "f32", "e4m3", "none")
     assert call(n=130, opb="T", ldb=130, sfd=SFD, ld_sfd=2, types=types) == thl.THL_ERR_MISALIGNED
     assert call(n=130, opb="T", ldb=136, sfd=SFD, ld_sfd=2, types=types, m=0) == thl.THL_OK
+
+
+# ------------------------------------------------------------ the conversion pass
+
+@pytest.mark.parametrize("types,ops,which", [
+    (("i8", "i32", "i32", "none"), ("N", "N"), "a"),
+    (("e4m3", "f32", "bf16", "none"), ("T", "T"), "b"),
+    (("e5m2", "f32", "bf16", "none"), ("N", "T"), "ab"),
+    (("e2m3", "f32", "bf16", "none"), ("T", "N"), "ab"),
+    (("e3m2", "f32", "bf16", "none"), ("N", "N"), "ab"),
+])
+def test_layouts_and_formats_the_tiles_cannot_stage_take_the_pass(types, ops, which):
+    # m = 0: the quick return still picks the K-major run and names the pass
+    assert call(m=0, types=types, opa=ops[0], opb=ops[1], lda=64, ldb=64) == thl.THL_OK
+    v = thl.thl_last_variant()
+    assert v.endswith("+cvt_" + which), v
+    inner = {"i8": "i8_", "e4m3": "e4m3_", "e5m2": "e5m2_", "e2m3": "e4m3_", "e3m2": "e4m3_"}[types[0]]
+    assert v.startswith(inner) and "_tn_" in v, v
+
+
+def test_conversion_pass_validation():
+    f6 = ("e2m3", "f32", "bf16", "none")
+    # fp6 lines start on whole bytes: leading dimensions a multiple of 4 elements
+    assert call(types=f6, lda=66) == thl.THL_ERR_INVALID
+    assert call(types=f6, opa="N", lda=66) == thl.THL_ERR_INVALID
+    # block-scaled fp6: k % 32 and both scale arrays, as for the other MX formats
+    assert call(types=f6, k=48, sc=thl.thl_scales(1.0, 1.0, SFA, 16, SFB, 16)) == thl.THL_ERR_UNSUPPORTED
+    assert call(types=f6, sc=thl.thl_scales(1.0, 1.0, SFA, 16, None, 0)) == thl.THL_ERR_INVALID
+    # fp6 beside a 16-bit operand: no path
+    dts = thl.make_dtypes("e2m3", "bf16", "f32", "bf16")
+    assert thl.thl_gemm(64, 64, 64, A, 64, "T", B, 64, "N", None, 64, D, 64, 1.0, 0.0, dts, None, None,
+                        None) == thl.THL_ERR_UNSUPPORTED
+    # D overlapping the caller's operand stored along M
+    assert call(types=("e4m3", "f32", "bf16", "none"), opa="N", d=A + 64) == thl.THL_ERR_INVALID
+    # the K-major run's own rules (int8: alpha 1) are checked before anything runs
+    assert call(types=("i8", "i32", "i32", "none"), opa="N", alpha=2.0) == thl.THL_ERR_UNSUPPORTED
+
+
+def test_no_alloc_entry_point_bounds_the_converted_operands():
+    # two 8192 x 8192 fp8 operands rewritten: 128 MiB, past the 40 MiB scratch;
+    # refused before any device call
+    dts = thl.make_dtypes("e4m3", "e4m3", "f32", "bf16")
+    assert thl.thl_gemm_noalloc(8192, 8192, 8192, A, 8192, "N", B, 8192, "T", None, 8192, D, 8192, 1.0, 0.0, dts,
+                                None, None, None) == thl.THL_ERR_SCRATCH

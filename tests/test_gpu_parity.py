@@ -528,7 +528,8 @@ def _check_batched(ws, shared=(), expect=None):
 
     w0 = ws[0]
     _say(f"[batched] {w0.name} L={len(ws)} m={w0.m} n={w0.n} k={w0.k} op={w0.op_a}{w0.op_b} shared={shared}")
-    bp = BatchedDeviceProblem(ws, shared=shared)
+    pad = 768 if any(t in ("e2m3", "e3m2") for t in (w0.type_a, w0.type_b)) else 256
+    bp = BatchedDeviceProblem(ws, shared=shared, pad=pad)
     st = bp.run()
     assert st == 0, f"thl_gemm_batched status {st}"
     torch.cuda.synchronize()
@@ -1050,3 +1051,80 @@ def test_mx_output_random_within_rounding(kind, fmt):
     neg = (codes >> sign_bit) == 1
     ok &= (neg == (y < 0)) | (np.abs(y) <= tol) | (mag == 0)
     assert ok.all(), (np.argwhere(~ok)[:5], int((~ok).sum()))
+
+
+
+# ------------------------------------------------------------ the conversion pass
+
+FP8 = ("e4m3", "e5m2")
+NARROW_PAIRS = [("e2m3", "e2m3"), ("e3m2", "e3m2"), ("e2m3", "e3m2"), ("e4m3", "e2m1"), ("e2m1", "e5m2"),
+                ("e3m2", "e4m3"), ("e2m1", "e2m1"), ("e4m3", "e4m3"), ("e5m2", "e4m3")]
+
+
+@pytest.mark.parametrize("mx", [False, True])
+@pytest.mark.parametrize("ops", [("T", "N"), ("N", "N"), ("T", "T"), ("N", "T")])
+@pytest.mark.parametrize("fa,fb", NARROW_PAIRS)
+def test_narrow_pairs_in_every_layout(fa, fb, ops, mx):
+    # 8-, 6- and 4-bit pairs, dense and block-scaled, in all four layouts:
+    # operands the tiled kernels cannot stage directly are rewritten as
+    # K-major rows first (variant name "+cvt_a", "+cvt_b" or "+cvt_ab")
+    import tile_hierarchy_linear_amd as thl
+    import workloads as wl
+
+    k = 256 if mx else 200  # block scaling needs k % 32; the dense cases end K inside a step
+    w = wl.make_narrow(fa, fb, 200, 136, k, mx=mx, op_a=ops[0], op_b=ops[1], beta=0.5 if mx else 0.0,
+                       act="relu" if mx else "none", bias=mx, alpha=1.5)
+    _check_full(w)
+    v = thl.thl_last_variant()
+    tn = ops == ("T", "N")
+    native = tn and ((fa in FP8 and fb in FP8) or (fa == fb == "e2m1" and mx))
+    assert ("+cvt" in v) == (not native), v
+    if fa == fb == "e2m1" and mx:
+        assert v.startswith("e2m1_"), v  # fp4 pairs keep the fp4 rate
+
+
+@pytest.mark.parametrize("ops", [("N", "N"), ("T", "T"), ("N", "T")])
+def test_int8_in_every_layout(ops):
+    import tile_hierarchy_linear_amd as thl
+    import workloads as wl
+
+    w = wl.make("int8", 190, 130, 300, op_a=ops[0], op_b=ops[1], bias=True, beta=1.0, act="relu")
+    _check_full(w)
+    assert thl.thl_last_variant().startswith("i8_tn_") and "+cvt" in thl.thl_last_variant()
+
+
+def test_conversion_pass_at_a_large_shape():
+    # MXFP6 (E2M3) N/T at 2048 x 1536 x 4096 with ragged-free tiles: a
+    # sampled check plus the full last row and column
+    import workloads as wl
+
+    w = wl.make_narrow("e2m3", "e3m2", 2048, 1536, 4096, mx=True, op_a="N", op_b="T")
+    _check_sampled(w, extra_edges=True)
+
+
+@pytest.mark.parametrize("fa,fb,ops,mx", [("e2m3", "e2m3", ("N", "N"), True), ("e4m3", "e4m3", ("N", "T"), False),
+                                          ("e2m1", "e2m1", ("T", "T"), True)])
+def test_conversion_pass_batched(fa, fb, ops, mx):
+    # three problems at fixed strides, each operand rewritten per problem
+    import workloads as wl
+
+    ws = [wl.make_narrow(fa, fb, 130, 70, 192, mx=mx, op_a=ops[0], op_b=ops[1], seed=40 + z) for z in range(3)]
+    _check_batched(ws, expect="+cvt")
+
+
+def test_conversion_pass_through_the_no_alloc_entry_point():
+    # the rewritten operands live in the static scratch; the result is the
+    # allocating entry point's, bit for bit, twice in a row (second smaller)
+    import tile_hierarchy_linear_amd as thl
+    import workloads as wl
+    from workloads.device import DeviceProblem
+
+    for m, n, k in ((300, 200, 512), (100, 70, 256)):
+        w = wl.make_narrow("e3m2", "e2m1", m, n, k, mx=True, op_a="N", op_b="N")
+        _say(f"[no-alloc pass] {m}x{n}x{k}")
+        ref, got = DeviceProblem(w), DeviceProblem(w)
+        assert ref.run() == 0
+        assert got.run(entry=thl.thl_gemm_noalloc) == 0
+        torch.cuda.synchronize()
+        assert "+cvt_ab" in thl.thl_last_variant()
+        assert torch.equal(ref.d.view(torch.int16), got.d.view(torch.int16))

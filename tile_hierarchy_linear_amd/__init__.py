@@ -18,7 +18,8 @@ THL_OK, THL_ERR_INVALID, THL_ERR_UNSUPPORTED, THL_ERR_MISALIGNED, THL_ERR_HIP, T
     0, -1, -2, -3, -4, -5)
 THL_ERR_SCRATCH = -6
 THL_OP_N, THL_OP_T = 0, 1
-DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3, "i32": 4, "e4m3": 5, "e2m1": 6, "e8m0": 7, "none": 8, "e5m2": 9}
+DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3, "i32": 4, "e4m3": 5, "e2m1": 6, "e8m0": 7, "none": 8, "e5m2": 9,
+          "e2m3": 10, "e3m2": 11}
 THL_EPI_NONE, THL_EPI_BIAS, THL_EPI_RELU, THL_EPI_GELU = 0, 1, 2, 4
 
 

@@ -13,8 +13,8 @@ SOURCES = ["gemm.hip", "layout.cpp", "gemm_inst_bf16.hip", "gemm_inst_f16.hip", 
            "gemm_inst_e4m3.hip", "gemm_inst_e2m1.hip", "gemm_inst_bf16_ops.hip", "gemm_inst_f16_ops.hip",
            "gemm_inst_skinny.hip", "gemm_inst_e5m2.hip",
            "gemm_inst_mx8.hip", "gemm_inst_mx8e5.hip", "gemm_inst_mx8mix.hip", "gemm_inst_e4e5.hip",
-           "gemm_inst_e5e4.hip", "gemm_inst_mxout16.hip", "gemm_inst_mxout8.hip"]
-HEADERS = ["gemm_args.hpp", "gemm_kernels.hpp", "gemm_launch.hpp", "gemm_skinny.hpp", "index_maps.hpp", "layout.hpp"]
+           "gemm_inst_e5e4.hip", "gemm_inst_mxout16.hip", "gemm_inst_mxout8.hip", "convert.hip"]
+HEADERS = ["convert.hpp", "gemm_args.hpp", "gemm_kernels.hpp", "gemm_launch.hpp", "gemm_skinny.hpp", "index_maps.hpp", "layout.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU instructions are switched off for every HIP compile.

@@ -18,12 +18,14 @@
 #include <cstddef>
 #include <cstdint>
 #include <cstdlib>
+#include <cstdio>
 #include <cstring>
 #include <mutex>
 #include <type_traits>
 #include <vector>
 
 #include "../../include/thl.h"
+#include "convert.hpp"
 #include "gemm_args.hpp"
 #include "index_maps.hpp"
 
@@ -291,9 +293,17 @@ int64_t bytes_of(thl_dtype t, int64_t count) {
       return count;
     case THL_E2M1X2:
       return (count + 1) / 2;
+    case THL_E2M3:
+    case THL_E3M2:
+      return (6 * count + 7) / 8;
     default:
       return 0;
   }
+}
+
+// Bits of one element of an operand format.
+int bits_of(thl_dtype t) {
+  return t == THL_E2M1X2 ? 4 : ((t == THL_E2M3 || t == THL_E3M2) ? 6 : 8 * static_cast<int>(bytes_of(t, 1)));
 }
 
 bool is_float_io(thl_dtype t) { return t == THL_F32 || t == THL_F16 || t == THL_BF16; }
@@ -314,7 +324,6 @@ Range matrix_range(const void* p, thl_dtype t, int64_t r, int64_t c, int64_t ld)
   if (!p || r <= 0 || c <= 0) return g;
   g.lo = reinterpret_cast<uintptr_t>(p);
   g.hi = g.lo + static_cast<uintptr_t>(bytes_of(t, (c - 1) * ld + r));
-  if (t == THL_E2M1X2) g.hi = g.lo + static_cast<uintptr_t>(((c - 1) * ld + r + 1) / 2);
   return g;
 }
 
@@ -346,7 +355,7 @@ enum { WS_POOL = 0, WS_STATIC = 1 };
 thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const void* A, int64_t lda, thl_op opA,
                      const void* B, int64_t ldb, thl_op opB, const void* C, int64_t ldc, void* D, int64_t ldd,
                      float alpha, float beta, const thl_dtypes* dt, const thl_epilogue* epi, const thl_scales* sc,
-                     struct ihipStream_t* stream, int ws_mode);
+                     struct ihipStream_t* stream, int ws_mode, int64_t ws_offset = 0);
 thl_status grouped_impl(int64_t count, const thl_group_problem* pb, const thl_group_problem* pb_dev, thl_op opA,
                         thl_op opB, float alpha, float beta, const thl_dtypes* dt, const thl_epilogue* epi,
                         const thl_scales* sc, struct ihipStream_t* stream);
@@ -738,12 +747,66 @@ int choose_splits(const Prep& pr, const Variant& v, const Batch& bt, int64_t til
   return sp >= 2 ? static_cast<int>(sp) : 1;
 }
 
+// Operands the tiled kernels cannot stage directly are first rewritten as
+// K-major rows (convert.hip): 8-bit operands stored along M (N), 6-bit
+// operands, 4-bit operands beside another format or without block scales.
+// Stage says which operand is rewritten and into which format.
+struct Stage {
+  bool a = false, b = false;
+  thl_dtype ta = THL_NONE, tb = THL_NONE;  // formats after the rewrite
+};
+
+bool is_fp8(thl_dtype t) { return t == THL_E4M3 || t == THL_E5M2; }
+bool is_narrow_float(thl_dtype t) { return is_fp8(t) || t == THL_E2M1X2 || t == THL_E2M3 || t == THL_E3M2; }
+
+// True when the problem takes the conversion pass (and fills *sg); false
+// for every combination the kernels stage directly and for the ones no path
+// builds (validation then reports those).
+bool plan_stage(const thl_dtypes* dt, thl_op opA, thl_op opB, const thl_scales* sc, Stage* sg) {
+  if (!dt) return false;
+  const bool a_km = opA == THL_OP_T, b_km = opB == THL_OP_N;
+  Stage g;
+  if (dt->a == THL_I8 && dt->b == THL_I8) {
+    g.a = !a_km;
+    g.b = !b_km;
+    g.ta = g.tb = THL_I8;
+  } else if (is_narrow_float(dt->a) && is_narrow_float(dt->b)) {
+    const bool any_sf = sc && (sc->sfa || sc->sfb);
+    if (dt->a == THL_E2M1X2 && dt->b == THL_E2M1X2 && any_sf) {
+      // MXFP4 both sides: fp4 rows (nibbles moved, not widened)
+      g.a = !a_km;
+      g.b = !b_km;
+      g.ta = g.tb = THL_E2M1X2;
+    } else {
+      // fp8 rows for the fp8 kernels: fp8 stays itself, the others widen to E4M3
+      g.a = !(is_fp8(dt->a) && a_km);
+      g.b = !(is_fp8(dt->b) && b_km);
+      g.ta = is_fp8(dt->a) ? dt->a : THL_E4M3;
+      g.tb = is_fp8(dt->b) ? dt->b : THL_E4M3;
+    }
+  } else {
+    return false;
+  }
+  if (!g.a && !g.b) return false;
+  *sg = g;
+  return true;
+}
+
 thl_status static_scratch(hipStream_t stream, int64_t bytes, uint8_t** out);
+thl_status staged_gemm(const Batch& bt, int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
+                       thl_op opA, const void* B, int64_t ldb, thl_op opB, const void* C, int64_t ldc, void* D,
+                       int64_t ldd, float alpha, float beta, const thl_dtypes* dt, const thl_epilogue* epi,
+                       const thl_scales* sc, struct ihipStream_t* stream, int ws_mode, int64_t ws_offset,
+                       const struct Stage& sg);
 
 thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const void* A, int64_t lda, thl_op opA,
                      const void* B, int64_t ldb, thl_op opB, const void* C, int64_t ldc, void* D, int64_t ldd,
                      float alpha, float beta, const thl_dtypes* dt, const thl_epilogue* epi, const thl_scales* sc,
-                     struct ihipStream_t* stream, int ws_mode) {
+                     struct ihipStream_t* stream, int ws_mode, int64_t ws_offset) {
+  Stage sg;
+  if (plan_stage(dt, opA, opB, sc, &sg))
+    return staged_gemm(bt, m, n, k, A, lda, opA, B, ldb, opB, C, ldc, D, ldd, alpha, beta, dt, epi, sc, stream, ws_mode,
+                       ws_offset, sg);
   Prep pr;
   const unsigned flags = epi ? epi->flags : 0u;
   thl_status st = prepare(bt, m, n, k, A, lda, opA, B, ldb, opB, C, ldc, D, ldd, alpha, beta, dt, flags,
@@ -804,8 +867,9 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
     a.ksteps = static_cast<int32_t>(ksteps);
     const int64_t bytes = splits * stride;
     if (ws_mode == WS_STATIC) {
-      st = static_scratch(hs, bytes, &ws);
+      st = static_scratch(hs, ws_offset + bytes, &ws);
       if (st != THL_OK) return st;
+      ws += ws_offset;  // past what the caller holds
     } else {
       int dev = 0;
       hipMemPool_t pool = hipGetDevice(&dev) == hipSuccess ? pool_for_device(dev) : nullptr;
@@ -874,6 +938,147 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
   if (le != hipSuccess) return THL_ERR_HIP;
   t_last_variant = pick->name;
   last_splits = splits;
+  return THL_OK;
+}
+
+// Bytes of one rewritten operand row: whole 64-byte K-steps of the target format.
+int64_t staged_ld_bytes(thl_dtype t, int64_t k) {
+  const int64_t b = bytes_of(t, k);
+  return b <= 0 ? 64 : (b + 63) / 64 * 64;
+}
+
+thread_local char t_staged_name[96];
+
+// The problem with the operands in sg rewritten (convert.hip) into a
+// workspace and then run as a K-major problem of the rewritten formats.  The
+// caller's operands are validated here (what the K-major run cannot see:
+// their shapes, leading dimensions, pointers and overlap with D); everything
+// else is validated by the K-major run.  Per-tensor scales stay with fp8
+// operands; E2M1, E2M3 and E3M2 operands take none (as 1).
+thl_status staged_gemm(const Batch& bt, int64_t m, int64_t n, int64_t k, const void* A, int64_t lda, thl_op opA,
+                       const void* B, int64_t ldb, thl_op opB, const void* C, int64_t ldc, void* D, int64_t ldd,
+                       float alpha, float beta, const thl_dtypes* dt, const thl_epilogue* epi, const thl_scales* sc,
+                       struct ihipStream_t* stream, int ws_mode, int64_t ws_offset, const Stage& sg) {
+  if (m < 0 || n < 0 || k < 0 || bt.count < 0 || bt.a < 0 || bt.b < 0) return THL_ERR_INVALID;
+  if (m > INT32_MAX || n > INT32_MAX || k > INT32_MAX || lda > INT32_MAX || ldb > INT32_MAX) return THL_ERR_UNSUPPORTED;
+  if (bt.count > 65535 || bt.a > (INT64_C(1) << 40) || bt.b > (INT64_C(1) << 40)) return THL_ERR_UNSUPPORTED;
+  const int64_t rows_a = (opA == THL_OP_N) ? m : k, cols_a = (opA == THL_OP_N) ? k : m;
+  const int64_t rows_b = (opB == THL_OP_N) ? k : n, cols_b = (opB == THL_OP_N) ? n : k;
+  if (lda < (rows_a > 1 ? rows_a : 1) || ldb < (rows_b > 1 ? rows_b : 1)) return THL_ERR_INVALID;
+  // a stored line (and each problem of a batch) starts on a whole byte
+  auto whole_bytes = [](thl_dtype t, int64_t elems) { return (elems * bits_of(t)) % 8 == 0; };
+  if (!whole_bytes(dt->a, lda) || !whole_bytes(dt->b, ldb) || !whole_bytes(dt->a, bt.a) || !whole_bytes(dt->b, bt.b))
+    return THL_ERR_INVALID;
+  const bool work = m > 0 && n > 0 && bt.count > 0;
+  if (work && k > 0 && (!A || !B)) return THL_ERR_INVALID;
+  if (work && D) {
+    const Range rd = batch_range(D, dt->d, m, n, ldd, bt.count, bt.d);
+    if (overlaps(rd, batch_range(A, dt->a, rows_a, cols_a, lda, bt.count, bt.a)) ||
+        overlaps(rd, batch_range(B, dt->b, rows_b, cols_b, ldb, bt.count, bt.b)))
+      return THL_ERR_INVALID;
+    if (epi && epi->sfd && is_mx_out(dt->d) && m > 0) {
+      const Range rs = matrix_range(epi->sfd, THL_E8M0, (m + 31) / 32, n, epi->ld_sfd);
+      if (overlaps(rs, matrix_range(A, dt->a, rows_a, cols_a, lda)) ||
+          overlaps(rs, matrix_range(B, dt->b, rows_b, cols_b, ldb)))
+        return THL_ERR_INVALID;
+    }
+  }
+  if (sg.a && (m + 63) / 64 > 65535) return THL_ERR_UNSUPPORTED;  // the pass's grid
+  if (sg.b && (n + 63) / 64 > 65535) return THL_ERR_UNSUPPORTED;
+
+  // ---- the rewritten operands: K-major rows of 64-byte steps
+  const int64_t lda_b = staged_ld_bytes(sg.ta, k), ldb_b = staged_ld_bytes(sg.tb, k);
+  const int64_t elems_per_byte_a = sg.ta == THL_E2M1X2 ? 2 : 1, elems_per_byte_b = sg.tb == THL_E2M1X2 ? 2 : 1;
+  const int64_t size_a = sg.a ? (m * lda_b + 255) / 256 * 256 : 0;
+  const int64_t size_b = sg.b ? (n * ldb_b + 255) / 256 * 256 : 0;
+  const int64_t count = bt.count > 0 ? bt.count : 0;
+  const int64_t total = count * (size_a + size_b);
+  const bool run_pass = work && k > 0 && total > 0;
+  // ---- the K-major problem, validated before the pass runs
+  thl_dtypes d2 = *dt;
+  if (sg.a) d2.a = sg.ta;
+  if (sg.b) d2.b = sg.tb;
+  thl_scales s2 = sc ? *sc : thl_scales{1.0f, 1.0f, nullptr, 0, nullptr, 0};
+  if (!is_fp8(dt->a)) s2.a_scale = 1.0f;
+  if (!is_fp8(dt->b)) s2.b_scale = 1.0f;
+  Batch b2 = bt;
+  if (sg.a) b2.a = count > 1 ? size_a * elems_per_byte_a : 0;
+  if (sg.b) b2.b = count > 1 ? size_b * elems_per_byte_b : 0;
+  // The rewritten operands are fresh memory: validated at stand-in addresses
+  // (256-byte aligned, far above any allocation, never dereferenced) so that
+  // every argument error is reported before anything is allocated or run.
+  const uintptr_t stand_in = static_cast<uintptr_t>(1) << 62;
+  const void* A2 = sg.a ? (run_pass ? reinterpret_cast<const void*>(stand_in) : nullptr) : A;
+  const void* B2 = sg.b ? (run_pass ? reinterpret_cast<const void*>(stand_in + count * size_a) : nullptr) : B;
+  const int64_t lda2 = sg.a ? lda_b * elems_per_byte_a : lda, ldb2 = sg.b ? ldb_b * elems_per_byte_b : ldb;
+  const thl_op opA2 = sg.a ? THL_OP_T : opA, opB2 = sg.b ? THL_OP_N : opB;
+  {
+    Prep check;
+    const thl_status st = prepare(b2, m, n, k, A2, lda2, opA2, B2, ldb2, opB2, C, ldc, D, ldd, alpha, beta, &d2,
+                                  epi ? epi->flags : 0u, epi ? epi->bias : nullptr, sc ? &s2 : nullptr,
+                                  epi ? epi->sfd : nullptr, epi ? epi->ld_sfd : 0, &check);
+    if (st != THL_OK) return st;
+  }
+
+  const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  uint8_t* ws = nullptr;
+  bool pooled = false;
+  if (run_pass) {
+    if (ws_mode == WS_STATIC) {
+      const thl_status st = static_scratch(hs, ws_offset + total, &ws);
+      if (st != THL_OK) return st;
+      ws += ws_offset;
+    } else {
+      int dev = 0;
+      hipMemPool_t pool = hipGetDevice(&dev) == hipSuccess ? pool_for_device(dev) : nullptr;
+      if (!pool || hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws), static_cast<size_t>(total), pool, hs) !=
+                       hipSuccess) {
+        (void)hipGetLastError();
+        return THL_ERR_HIP;
+      }
+      pooled = true;
+    }
+  }
+  uint8_t* wa = ws;
+  uint8_t* wb = ws ? ws + count * size_a : nullptr;
+  if (run_pass && sg.a) A2 = wa;
+  if (run_pass && sg.b) B2 = wb;
+
+  // ---- the pass
+  auto pass = [&](const void* src, thl_dtype from, thl_dtype to, int64_t ld, int64_t stride, bool kmajor, int64_t rows,
+                  uint8_t* dst, int64_t dst_ld, int64_t dst_batch) -> hipError_t {
+    CvtArgs c{};
+    c.src = static_cast<const uint8_t*>(src);
+    c.ld_bytes = bytes_of(from, ld);
+    c.line_bytes = bytes_of(from, kmajor ? k : rows);
+    c.src_batch = bytes_of(from, stride);
+    c.src_fmt = from;
+    c.dst_fmt = to;
+    c.kmajor = kmajor ? 1 : 0;
+    c.aligned4 = (reinterpret_cast<uintptr_t>(src) % 4 == 0 && c.ld_bytes % 4 == 0 && c.src_batch % 4 == 0) ? 1 : 0;
+    c.rows = rows;
+    c.k = k;
+    c.dst = dst;
+    c.dst_ld_bytes = dst_ld;
+    c.dst_batch = dst_batch;
+    return launch_convert(c, count, hs);
+  };
+  hipError_t le = hipSuccess;
+  if (run_pass && sg.a) le = pass(A, dt->a, sg.ta, lda, bt.a, opA == THL_OP_T, m, wa, lda_b, size_a);
+  if (run_pass && sg.b && le == hipSuccess) le = pass(B, dt->b, sg.tb, ldb, bt.b, opB == THL_OP_N, n, wb, ldb_b, size_b);
+  if (le != hipSuccess) {
+    if (pooled) (void)hipFreeAsync(ws, hs);
+    return THL_ERR_HIP;
+  }
+
+  // ---- the K-major run
+  const thl_status st = gemm_impl(b2, m, n, k, A2, lda2, opA2, B2, ldb2, opB2, C, ldc, D, ldd, alpha, beta, &d2, epi,
+                                  sc ? &s2 : nullptr, stream, ws_mode, ws_offset + (ws_mode == WS_STATIC ? total : 0));
+  if (pooled) (void)hipFreeAsync(ws, hs);  // back to the pool once the kernels have run
+  if (st != THL_OK) return st;
+  std::snprintf(t_staged_name, sizeof(t_staged_name), "%s+cvt_%s", t_last_variant,
+                sg.a && sg.b ? "ab" : (sg.a ? "a" : "b"));
+  t_last_variant = t_staged_name;
   return THL_OK;
 }
 

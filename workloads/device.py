@@ -119,7 +119,8 @@ class BatchedDeviceProblem:
         self.L = len(ws)
         self.strides = {}
         self.bufs = {}
-        eb = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "i32": 4, "e4m3": 1, "e5m2": 1, "e2m1": 0.5, "e8m0": 1}
+        eb = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "i32": 4, "e4m3": 1, "e5m2": 1, "e2m1": 0.5, "e8m0": 1,
+              "e2m3": 0.75, "e3m2": 0.75}
         types = {"a": w0.type_a, "b": w0.type_b, "c": w0.type_c, "bias": w0.type_bias, "sfa": "e8m0",
                  "sfb": "e8m0"}
         for name in ("a", "b", "c", "bias", "sfa", "sfb"):
@@ -135,6 +136,7 @@ class BatchedDeviceProblem:
             for z, r in enumerate(raws):
                 host[z * sb: z * sb + len(r)] = r
             self.bufs[name] = torch.from_numpy(host).to(device)
+            assert (sb / eb[types[name]]).is_integer(), "pad must hold whole elements (768 bytes for fp6)"
             self.strides[name] = 0 if name in shared else int(sb / eb[types[name]])
         es_d = eb[w0.type_d]
         self.stride_d = (w0.ldd * max(1, w0.n) * es_d + pad - 1) // pad * pad // es_d
