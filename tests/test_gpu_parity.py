@@ -1128,3 +1128,29 @@ def test_conversion_pass_through_the_no_alloc_entry_point():
         torch.cuda.synchronize()
         assert "+cvt_ab" in thl.thl_last_variant()
         assert torch.equal(ref.d.view(torch.int16), got.d.view(torch.int16))
+
+
+@pytest.mark.parametrize("kind", ["fp8", "int8", "mxfp4"])
+def test_misaligned_rows_repitched_only_for_large_problems(kind):
+    # K-major rows that are not whole 16-byte units: with D below 2^23
+    # elements the 4-byte-copy kernels read them where they are; from 2^23 on
+    # the pass copies them to 64-byte rows for the 16-byte kernels (sampled
+    # check there)
+    import tile_hierarchy_linear_amd as thl
+    import workloads as wl
+
+    small = (300, 200, 520) if kind != "mxfp4" else (300, 200, 544)
+    large = (4096, 2048, 200) if kind != "mxfp4" else (4096, 2048, 224)
+    q = 8 if kind != "mxfp4" else 16  # a leading dimension 8 bytes past a 16-byte unit
+    for (m, n, k), want in ((small, False), (large, True)):
+        kb = k if kind != "mxfp4" else k // 2
+        ld = k + q if kb % 16 == 0 else k
+        w = wl.make(kind, m, n, k, lda=ld, ldb=ld)
+        if want:
+            _check_sampled(w, extra_edges=True)
+        else:
+            _check_full(w)
+        v = thl.thl_last_variant()
+        assert ("+cvt_ab" in v) == want, v
+        if not want:
+            assert "_v4_" in v, v

@@ -761,8 +761,17 @@ bool is_narrow_float(thl_dtype t) { return is_fp8(t) || t == THL_E2M1X2 || t == 
 
 // True when the problem takes the conversion pass (and fills *sg); false
 // for every combination the kernels stage directly and for the ones no path
-// builds (validation then reports those).
-bool plan_stage(const thl_dtypes* dt, thl_op opA, thl_op opB, const thl_scales* sc, Stage* sg) {
+// builds (validation then reports those).  A K-major 8- or 4-bit operand
+// whose rows are not 16-byte aligned is rewritten too (into 64-byte rows)
+// when D has 2^23 elements or more: only the 4-byte-copy kernels could
+// stage it as it is, and with many tiles they run at half the 16-byte
+// kernels' rate.  Measured on fp8 rows 8 bytes past a 16-byte unit: 8192^3
+// 1007 us on the 4-byte kernel against 488 us rewritten, 4096^3 144 against
+// 96 us; with few tiles the 16-byte kernel is bound by load latency as well
+// and the pass does not pay (4097 x 1000 x 2040: 51 against 59 us;
+// 2048 x 2048 x 8192: 76 against 83 us).
+bool plan_stage(const thl_dtypes* dt, thl_op opA, thl_op opB, const thl_scales* sc, int64_t m, int64_t n, int64_t k,
+                const void* A, int64_t lda, const void* B, int64_t ldb, const Batch& bt, Stage* sg) {
   if (!dt) return false;
   const bool a_km = opA == THL_OP_T, b_km = opB == THL_OP_N;
   Stage g;
@@ -787,6 +796,23 @@ bool plan_stage(const thl_dtypes* dt, thl_op opA, thl_op opB, const thl_scales* 
   } else {
     return false;
   }
+  // re-pitch misaligned K-major rows of a large problem (not when a variant
+  // is forced: THL_FORCE_VARIANT keeps the caller's operands as they are)
+  const char* forced = std::getenv("THL_FORCE_VARIANT");
+  const bool large = k > 0 && m * n >= (INT64_C(1) << 23) && !(forced && *forced);
+  auto rows16 = [&](const void* p, thl_dtype t, int64_t ld, int64_t stride) {
+    return reinterpret_cast<uintptr_t>(p) % 16 == 0 && bytes_of(t, ld) % 16 == 0 &&
+           (bt.count <= 1 || bytes_of(t, stride) % 16 == 0);
+  };
+  auto repitchable = [](thl_dtype t) { return t == THL_I8 || is_fp8(t) || t == THL_E2M1X2; };
+  if (large && !g.a && a_km && repitchable(dt->a) && !rows16(A, dt->a, lda, bt.a)) {
+    g.a = true;
+    g.ta = dt->a;
+  }
+  if (large && !g.b && b_km && repitchable(dt->b) && !rows16(B, dt->b, ldb, bt.b)) {
+    g.b = true;
+    g.tb = dt->b;
+  }
   if (!g.a && !g.b) return false;
   *sg = g;
   return true;
@@ -804,7 +830,7 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
                      float alpha, float beta, const thl_dtypes* dt, const thl_epilogue* epi, const thl_scales* sc,
                      struct ihipStream_t* stream, int ws_mode, int64_t ws_offset) {
   Stage sg;
-  if (plan_stage(dt, opA, opB, sc, &sg))
+  if (plan_stage(dt, opA, opB, sc, m, n, k, A, lda, B, ldb, bt, &sg))
     return staged_gemm(bt, m, n, k, A, lda, opA, B, ldb, opB, C, ldc, D, ldd, alpha, beta, dt, epi, sc, stream, ws_mode,
                        ws_offset, sg);
   Prep pr;
