@@ -137,7 +137,11 @@ typedef struct {
  *   name suffix "+cvt_a", "+cvt_b" or "+cvt_ab"): 8-bit formats as they are,
  *   E2M1X2 as E2M1X2 when both operands are block-scaled fp4, and E2M1X2, E2M3
  *   and E3M2 otherwise widened to E4M3, which holds each of their values
- *   exactly; then the TN kernels above run.  Block scales, when given (both
+ *   exactly; then the TN kernels above run.  K-major 8- and 4-bit rows are
+ *   rewritten too (as they are, into 64-byte rows) when they are not whole
+ *   4-byte units (no kernel reads them), or not whole 16-byte units and D
+ *   has 2^23 elements or more (the 16-byte kernels then win by far more than
+ *   the pass costs); not while THL_FORCE_VARIANT is set.  Block scales, when given (both
  *   sfa and sfb, k % 32 == 0), apply per logical row and 32 K-elements
  *   whatever the storage; the per-tensor scales apply to E4M3 and E5M2
  *   operands only.  The workspace is
@@ -298,6 +302,10 @@ thl_status thl_gemm_batched(int64_t batch, int64_t m, int64_t n, int64_t k,
  *                 kernel reads each problem's sizes and pointers from it);
  *                 the caller keeps it unchanged until the launch completes.
  *
+ * Only what the tiled kernels stage directly is built grouped: operands
+ * that thl_gemm would first rewrite (see "Every other layout and pairing"
+ * above: 8-bit formats stored along M or N, fp6, fp4 beside another format
+ * or without block scales) and MX-format D return THL_ERR_UNSUPPORTED.
  * One kernel variant (the tiled kernels; the small-M kernel is not used)
  * runs every problem; grid row z computes problem z with its share of
  * persistent workgroups.  count == 0, or every problem with m == 0 or

@@ -428,3 +428,13 @@ def test_no_alloc_entry_point_bounds_the_converted_operands():
     dts = thl.make_dtypes("e4m3", "e4m3", "f32", "bf16")
     assert thl.thl_gemm_noalloc(8192, 8192, 8192, A, 8192, "N", B, 8192, "T", None, 8192, D, 8192, 1.0, 0.0, dts,
                                 None, None, None) == thl.THL_ERR_SCRATCH
+
+
+def test_rows_off_every_kernel_alignment_take_the_pass():
+    # fp8 rows of 2041 bytes fit no kernel (they need 4-byte units): rewritten
+    # whatever the size; bf16 rows of odd length have no such path
+    assert call(m=0, types=("e4m3", "f32", "bf16", "none"), k=2041, lda=2041, ldb=2041) == thl.THL_OK
+    assert thl.thl_last_variant().endswith("+cvt_ab")
+    assert call(m=0, types=("e4m3", "f32", "bf16", "none"), k=2040, lda=2040, ldb=2040) == thl.THL_OK
+    assert "+cvt" not in thl.thl_last_variant() and "_v4_" in thl.thl_last_variant()
+    assert call(m=8, types=("bf16", "f32", "f32", "none"), k=63, lda=63, ldb=63) == thl.THL_ERR_MISALIGNED

@@ -1154,3 +1154,14 @@ def test_misaligned_rows_repitched_only_for_large_problems(kind):
         assert ("+cvt_ab" in v) == want, v
         if not want:
             assert "_v4_" in v, v
+
+
+def test_rows_of_odd_bytes_through_the_pass():
+    # fp8 and int8 rows of 1021 bytes (no kernel takes them as they are)
+    import tile_hierarchy_linear_amd as thl
+    import workloads as wl
+
+    for kind in ("fp8", "int8"):
+        w = wl.make(kind, 130, 70, 1021, lda=1021, ldb=1021)
+        _check_full(w)
+        assert thl.thl_last_variant().endswith("+cvt_ab"), thl.thl_last_variant()

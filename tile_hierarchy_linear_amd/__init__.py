@@ -210,10 +210,13 @@ def thl_gemm_grouped(count, problems, problems_dev, opA, opB, alpha, beta, dtype
 
 def gemm(A, B, D, *, m, n, k, lda, ldb, ldd, op_a="T", op_b="N", C=None, ldc=0, alpha=1.0, beta=0.0,
          type_ab="bf16", type_c="f32", type_d="f32", bias=None, type_bias="none", act="none",
-         a_scale=1.0, b_scale=1.0, sfa=None, ld_sfa=0, sfb=None, ld_sfb=0, stream=None) -> str:
+         a_scale=1.0, b_scale=1.0, sfa=None, ld_sfa=0, sfb=None, ld_sfb=0, stream=None, type_b=None,
+         sfd=None, ld_sfd=0) -> str:
     """Torch-tensor convenience around thl_gemm: takes device tensors holding
     the stored bits, issues on the current stream, raises ThlError on a
-    non-OK status and returns the name of the kernel variant launched."""
+    non-OK status and returns the name of the kernel variant launched.
+    type_ab is A's format and B's unless type_b is given; sfd / ld_sfd take
+    the generated scales of an MX-format D."""
     import torch
 
     def ptr(t):
@@ -221,9 +224,9 @@ def gemm(A, B, D, *, m, n, k, lda, ldb, ldd, op_a="T", op_b="N", C=None, ldc=0, 
 
     flags = (THL_EPI_BIAS if bias is not None else 0) | {"none": 0, "relu": THL_EPI_RELU,
                                                          "gelu": THL_EPI_GELU}[act]
-    epi = thl_epilogue(flags, ptr(bias))
+    epi = thl_epilogue(flags, ptr(bias), ptr(sfd), int(ld_sfd))
     sc = thl_scales(float(a_scale), float(b_scale), ptr(sfa), int(ld_sfa), ptr(sfb), int(ld_sfb))
-    dts = make_dtypes(type_ab, type_ab, type_c, type_d, type_bias)
+    dts = make_dtypes(type_ab, type_b or type_ab, type_c, type_d, type_bias)
     if stream is None:
         stream = torch.cuda.current_stream().cuda_stream
     st = thl_gemm(m, n, k, ptr(A), lda, op_a, ptr(B), ldb, op_b, ptr(C), ldc or max(1, m), ptr(D), ldd,

@@ -804,12 +804,21 @@ bool plan_stage(const thl_dtypes* dt, thl_op opA, thl_op opB, const thl_scales* 
     return reinterpret_cast<uintptr_t>(p) % 16 == 0 && bytes_of(t, ld) % 16 == 0 &&
            (bt.count <= 1 || bytes_of(t, stride) % 16 == 0);
   };
+  // rows that are not even whole 4-byte units fit no kernel at all: rewritten
+  // whatever the size
+  auto rows4 = [&](const void* p, thl_dtype t, int64_t ld, int64_t stride) {
+    return reinterpret_cast<uintptr_t>(p) % 4 == 0 && bytes_of(t, ld) % 4 == 0 &&
+           (bt.count <= 1 || bytes_of(t, stride) % 4 == 0);
+  };
   auto repitchable = [](thl_dtype t) { return t == THL_I8 || is_fp8(t) || t == THL_E2M1X2; };
-  if (large && !g.a && a_km && repitchable(dt->a) && !rows16(A, dt->a, lda, bt.a)) {
+  const bool keep = forced && *forced;
+  if (!g.a && a_km && repitchable(dt->a) &&
+      ((large && !rows16(A, dt->a, lda, bt.a)) || (!keep && !rows4(A, dt->a, lda, bt.a)))) {
     g.a = true;
     g.ta = dt->a;
   }
-  if (large && !g.b && b_km && repitchable(dt->b) && !rows16(B, dt->b, ldb, bt.b)) {
+  if (!g.b && b_km && repitchable(dt->b) &&
+      ((large && !rows16(B, dt->b, ldb, bt.b)) || (!keep && !rows4(B, dt->b, ldb, bt.b)))) {
     g.b = true;
     g.tb = dt->b;
   }
