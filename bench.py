@@ -362,6 +362,36 @@ def cpu_baseline(w, budget_s, budget_1t_s):
             "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
 
 
+def mfma_ceiling(stream):
+    """The matrix cores alone (csrc/mfma_probe.hip): TFLOP/s of a loop of
+    independent MFMAs on every SIMD, at the clock the chip holds under that
+    load, for bf16, e4m3 and e2m1 (scaled).  HIP events around 50 launches of
+    about 0.9 ms each after 50 warm-up launches (the clock's ramp from idle,
+    as for the GEMMs)."""
+    import ctypes
+
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "tile_hierarchy_linear_amd", "libthl_probe.so"))
+    lib.thl_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.thl_probe_mfma.restype = ctypes.c_int
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(cus * 256, dtype=torch.float32, device="cuda")
+    res = {}
+    for fmt, name, flops_each, iters in ((0, "bf16", 32768, 8000), (1, "e4m3", 131072, 4000),
+                                         (2, "e2m1", 131072, 8000)):
+        def run():
+            return lib.thl_probe_mfma(fmt, iters, cus, ctypes.c_void_p(out.data_ptr()),
+                                      ctypes.c_void_p(stream.cuda_stream))
+        mean, med, mn = time_launches(run, 50, 50, stream)
+        tf = cus * 4 * iters * 8 * flops_each / (mean * 1e-3) / 1e12
+        peak = PEAK_TFLOPS[name]
+        res[name] = {"tflops": round(tf, 1), "frac_of_peak": round(tf / peak, 4), "ms_per_launch": round(mean, 4),
+                     "mfma_per_wave": iters * 8}
+        log(f"[mfma only] {name}: {tf:.1f} TFLOP/s, {tf / peak:.3f} of the dense peak")
+    return res
+
+
 def copy_calibration(mib):
     """A plain device copy of known size, for scaling HBM byte counters."""
     import torch
@@ -378,14 +408,20 @@ def copy_calibration(mib):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # The chip takes about 50 launches of the 8192^3 GEMM (some 40 ms of load)
+    # to reach its steady clock from idle: bf16 measured 1,073 TFLOP/s at the
+    # 5th launch, 1,305 at the 20th and 1,390-1,400 from the 50th to the
+    # 1,000th.  The default warm-up covers that ramp.
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--only", default="",
                     help="comma list of configuration keys (" + ",".join(c[0] for c in CONFIGS) +
                          ",batched); default: all")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work on all threads")
     ap.add_argument("--cpu-budget-1t", type=float, default=4.0, help="seconds of oracle work on one thread")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mfma-ceiling", action="store_true",
+                    help="skip the matrix-core-only loop (the ceiling at the chip's loaded clock)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0)
     ap.add_argument("--sweep-variants", action="store_true",
                     help="also time every built variant of each configuration's family (stderr)")
@@ -419,6 +455,7 @@ def main():
         configs["batched"] = run_batched(args, stream)
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib)
+    ceiling = None if args.no_mfma_ceiling else mfma_ceiling(stream)
 
     head = HEADLINE if HEADLINE in configs else next((k for k in configs if k != "batched"), None)
     if head is None:
@@ -431,6 +468,10 @@ def main():
     roof = dict(h["roofline"])
     roof.update({"traffic": h["traffic"], "algorithmic_bytes": h["algorithmic_bytes"],
                  "kernel_sources": kernel_source_hash()})
+    if ceiling and w.type_a in ceiling:
+        c = ceiling[w.type_a]
+        roof["mfma_only_ceiling"] = {"achieved": c["tflops"], "frac_of_peak": c["frac_of_peak"],
+                                     "gemm_frac_of_ceiling": round(h["tflops"] / c["tflops"], 4)}
     line = {
         "metric": METRIC,
         "value": h["tflops"],
@@ -449,6 +490,7 @@ def main():
                    "parity": h.get("parity")},
         "roofline": roof,
         "configs": configs,
+        "mfma_only_ceiling": ceiling,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -9,6 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(os.path.dirname(HERE), "_build")
 LIB = os.path.join(HERE, "libthl.so")
+PROBE_LIB = os.path.join(HERE, "libthl_probe.so")
 SOURCES = ["gemm.hip", "layout.cpp", "gemm_inst_bf16.hip", "gemm_inst_f16.hip", "gemm_inst_i8.hip",
            "gemm_inst_e4m3.hip", "gemm_inst_e2m1.hip", "gemm_inst_bf16_ops.hip", "gemm_inst_f16_ops.hip",
            "gemm_inst_skinny.hip", "gemm_inst_e5m2.hip",
@@ -48,6 +49,11 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp])
     os.replace(tmp, LIB)
+    # the measurement probe, a library of its own outside the GEMM boundary
+    tmp = PROBE_LIB + ".tmp"
+    subprocess.check_call([HIPCC] + FLAGS + ["-shared", "-x", "hip", os.path.join(CSRC, "mfma_probe.hip"), "-o", tmp],
+                          stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

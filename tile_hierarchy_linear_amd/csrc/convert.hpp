@@ -24,7 +24,8 @@ struct CvtArgs {
 
 // Launches the pass over `batch` problems on stream s.  hipErrorInvalidValue
 // for a combination it does not build or a grid beyond its limits (rows up
-// to 65535 tiles of 64, batch up to 65535).
+// to 65535 tiles of 64 for K-major sources, of 256 otherwise; batch up to
+// 65535).
 hipError_t launch_convert(const CvtArgs& a, int64_t batch, hipStream_t s);
 
 }  // namespace thl
