@@ -438,3 +438,4 @@ def test_rows_off_every_kernel_alignment_take_the_pass():
     assert call(m=0, types=("e4m3", "f32", "bf16", "none"), k=2040, lda=2040, ldb=2040) == thl.THL_OK
     assert "+cvt" not in thl.thl_last_variant() and "_v4_" in thl.thl_last_variant()
     assert call(m=8, types=("bf16", "f32", "f32", "none"), k=63, lda=63, ldb=63) == thl.THL_ERR_MISALIGNED
+

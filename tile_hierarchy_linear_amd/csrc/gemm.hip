@@ -446,7 +446,7 @@ namespace {
 struct Prep {
   int fam = -1;
   bool a_kmajor = false, b_kmajor = false, block_scaled = false, int_path = false, has_bias = false;
-  bool small_m = false, work = false, vec = false;
+  bool small_m = false, work = false, vec = false, rows16 = true;
   int mx_out = MX_NONE;  // D in an MX element format, with generated scales
   unsigned flags = 0;
   int64_t lda_bytes = 0, ldb_bytes = 0, sa_bytes = 0, sb_bytes = 0;
@@ -606,8 +606,10 @@ thl_status prepare(const Batch& bt, int64_t m, int64_t n, int64_t k, const void*
       return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0 && ld_bytes % 16 == 0 && ld_bytes <= (INT64_C(1) << 23);
     };
     bool vec = vec_ok(D, bytes_of(dt->d, ldd));
-    if (beta != 0.0f) vec = vec && (dt->c == THL_F16 || dt->c == THL_BF16) && vec_ok(C, bytes_of(dt->c, ldc));
+    if (beta != 0.0f) vec = vec && vec_ok(C, bytes_of(dt->c, ldc));
     if (has_bias) vec = vec && (reinterpret_cast<uintptr_t>(bias) & 15) == 0;
+    o.rows16 = vec;  // every column run of D, C and bias a whole 16-byte unit
+    if (beta != 0.0f) vec = vec && (dt->c == THL_F16 || dt->c == THL_BF16);
     if (bt.count > 1) {
       const int64_t bs_c = beta != 0.0f ? bytes_of(dt->c, bt.c) : 0, bs_d = bytes_of(dt->d, bt.d);
       const int64_t bs_bias = has_bias ? bytes_of(dt->bias, bt.bias) : 0;
@@ -629,8 +631,15 @@ bool fits(const Variant& v, const Prep& pr, const Batch& bt, const void* A, cons
 }
 
 // The tile tier the shape rule prefers for this many tiles of each size.
-int want_tier_of(int64_t tiles_256, int64_t tiles_256x128) {
-  return tiles_256 >= 256 ? 0 : (tiles_256x128 >= 256 ? 1 : 2);
+// A float problem whose D, C or bias column runs are not 16-byte units (an
+// odd leading dimension, say) takes the general epilogue with element-wise
+// accesses on every tile, and with one workgroup per CU nothing hides it: it
+// then starts at the two-workgroup tiers.  Measured at 4097^2 x 4096 (bf16 D, ldd = 4097): e4m3 192 us on
+// 256x256 against 124 us on 256x128 and 137 us on 128x128; bf16 390, 270
+// and 293 us.
+int want_tier_of(int64_t tiles_256, int64_t tiles_256x128, bool general_epilogue = false) {
+  const int t = tiles_256 >= 256 ? 0 : (tiles_256x128 >= 256 ? 1 : 2);
+  return general_epilogue && t == 0 ? 1 : t;
 }
 
 // First fit over the built variants of the problem's family, in the order
@@ -852,7 +861,8 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
   // (tile counts over the whole batch: its problems fill the device together)
   const int64_t tiles_256 = ((m + 255) / 256) * ((n + 255) / 256) * bt.count;
   const int64_t tiles_256x128 = ((m + 255) / 256) * ((n + 127) / 128) * bt.count;
-  const Variant* pick = choose_variant(pr, true, m, want_tier_of(tiles_256, tiles_256x128),
+  const Variant* pick = choose_variant(pr, true, m,
+                                       want_tier_of(tiles_256, tiles_256x128, !pr.int_path && !pr.rows16 && pr.mx_out == MX_NONE),
                                        [&](const Variant& v) { return fits(v, pr, bt, A, B, k); }, &st);
   if (!pick) return st;
   if (!pr.work) {
@@ -982,7 +992,7 @@ int64_t staged_ld_bytes(thl_dtype t, int64_t k) {
   return b <= 0 ? 64 : (b + 63) / 64 * 64;
 }
 
-thread_local char t_staged_name[96];
+thread_local char t_staged_name[192];
 
 // The problem with the operands in sg rewritten (convert.hip) into a
 // workspace and then run as a K-major problem of the rewritten formats.  The
