@@ -112,10 +112,12 @@ def compulsory_bytes(w):
 
 
 def kernel_source_hash():
-    """Hash of every source the GEMM kernels and their launch are built from."""
+    """Hash of the device code of the GEMM kernels: the kernel templates, their
+    arguments, launch wrappers and instantiations, and the index maps (not
+    the host-side dispatch in gemm.hip, which chooses among them)."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
-        if name.startswith("gemm") or name == "index_maps.hpp":
+        if (name.startswith("gemm") and name != "gemm.hip") or name == "index_maps.hpp":
             h.update(name.encode())
             with open(os.path.join(CSRC, name), "rb") as f:
                 h.update(f.read())
