@@ -1180,3 +1180,51 @@ def test_odd_leading_dimension_of_d_starts_at_the_two_workgroup_tiers():
     w = wl.make("bf16", 4096, 4096, 64, ldd=4097, ldc=4097)
     _check_sampled(w, extra_edges=True)
     assert "_256x128_" in thl.thl_last_variant(), thl.thl_last_variant()
+
+
+def test_conversion_pass_with_k_zero_is_the_epilogue():
+    # fp6 operands with K = 0: nothing to convert, D = act(beta*C + bias)
+    import workloads as wl
+
+    w = wl.make_narrow("e2m3", "e3m2", 70, 40, 0, mx=False, op_a="N", op_b="T", beta=0.75, act="relu", bias=True)
+    _check_full(w)
+
+
+def test_conversion_pass_batched_with_a_shared_operand():
+    # three problems sharing A (stride 0) stored along M; B per problem
+    import workloads as wl
+
+    ws = [wl.make_narrow("e4m3", "e2m1", 130, 70, 192, mx=True, op_a="N", op_b="N", seed=60 + z) for z in range(3)]
+    _check_batched(ws, shared=("a", "sfa"), expect="+cvt_")
+
+
+@pytest.mark.parametrize("m,n", [(5, 1), (31, 3), (33, 1)])
+@pytest.mark.parametrize("fmt", ["e2m1", "e4m3"])
+def test_mx_output_short_columns(m, n, fmt):
+    # fewer rows than one block, one block and one row, a single column
+    _check_mx_exact_shape("bf16", "N", "N", fmt, m, n)
+
+
+def _check_mx_exact_shape(kind, op_a, op_b, fmt, m, n):
+    import oracle
+
+    w = _exact_mx_workload(kind, m, n, 48, fmt, op_a, op_b, seed=m * 7 + n)
+    dp = _run_mx(w)
+    codes, scales = dp.mx_all()
+    y = oracle.gemm_full(w.oracle_problem())
+    want_codes, want_scales = oracle.mx_quantize_columns(y, fmt)
+    assert np.array_equal(scales, want_scales)
+    assert np.array_equal(codes, want_codes)
+
+
+def test_mx_output_through_the_no_alloc_entry_point():
+    # the MX-output kernels take no workspace: the no-allocation entry point
+    # writes the same codes and scales as thl_gemm
+    import tile_hierarchy_linear_amd as thl
+    from workloads.device import DeviceProblem
+
+    w = _exact_mx_workload("fp8", 200, 130, 64, "e2m1", "T", "N", seed=5)
+    ref, got = DeviceProblem(w), DeviceProblem(w)
+    assert ref.run() == 0 and got.run(entry=thl.thl_gemm_noalloc) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(ref.d, got.d) and torch.equal(ref.sfd, got.sfd)
