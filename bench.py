@@ -19,9 +19,10 @@ for the outputs it checked:
   8192^3 (T/N, D = A.B + C); and, beside them, e5m2 and MXFP8 at 8192^3 and a
   batched bf16 GEMM (16 problems of 2048^3 in one launch).
 
-Each launch is bracketed by HIP events on the stream it runs on: the mean
-over the timed launches is the throughput; the median and minimum of the
-per-launch times are reported with it.
+The timed launches run back to back between two HIP events on the stream
+they run on: their mean is the throughput.  A second pass with an event
+around each launch gives the median and minimum per-launch times reported
+with it.  Each call's arguments are marshalled once, before timing.
 
 Prints ONE JSON line on stdout (diagnostics go to stderr).
 """
@@ -143,16 +144,25 @@ def measured_traffic(variant, m, n, k):
 
 
 def time_launches(run, steps, warmup, stream):
-    """Launch `run` warmup times untimed, then `steps` times with a HIP event
-    before and after each launch on `stream` (the stream the kernels run on).
-    Returns (mean, median, min) per launch in ms; the mean is over the whole
-    timed region (first event to last)."""
+    """Launch `run` warmup times untimed, then time `steps` launches back to
+    back on `stream` (the stream the kernels run on) between two HIP events:
+    the mean per launch.  A second pass of `steps` launches, each between
+    events of its own, gives the median and the minimum (an event between
+    launches adds a few microseconds of queue work, so it stays out of the
+    mean).  Returns (mean, median, min) per launch in ms."""
     import torch
 
     for _ in range(warmup):
         st = run()
         assert st == 0, st
     torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        run()
+    end.record(stream)
+    torch.cuda.synchronize()
+    mean = start.elapsed_time(end) / steps
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     ev[0].record(stream)
     for i in range(steps):
@@ -160,7 +170,6 @@ def time_launches(run, steps, warmup, stream):
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
     each = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
-    mean = ev[0].elapsed_time(ev[steps]) / steps
     return mean, each[len(each) // 2], each[0]
 
 
@@ -209,7 +218,8 @@ def run_config(key, kind, m, n, k, bound, mult, args, stream):
     dp = DeviceProblem(w)
     log(f"[{key}] inputs generated and uploaded in {time.perf_counter() - t0:.1f} s")
     steps, warmup = args.steps * mult, args.warmup * mult
-    mean, med, mn = time_launches(lambda: dp.run(stream=stream.cuda_stream), steps, warmup, stream)
+    call = dp.bind(stream=stream.cuda_stream)  # arguments marshalled once, outside the timed region
+    mean, med, mn = time_launches(call, steps, warmup, stream)
     variant = thl.thl_last_variant()
     flops = w.flops()
     peak_key = "mxe4m3" if kind == "mxfp8" else PEAK_KEY[w.type_a]  # fp6: the fp6 MFMA peak

@@ -76,6 +76,19 @@ def test_negative_dimensions():
     assert call(k=-5) == thl.THL_ERR_INVALID
 
 
+def test_bound_call_validates_like_the_direct_call():
+    # bind_thl_gemm marshals once and repeats the same call: same statuses as thl_gemm
+    dts, epi = thl.make_dtypes("bf16", "bf16", "f32", "f32"), thl.thl_epilogue(0, None, None, 0)
+    for entry in ("thl_gemm", "thl_gemm_noalloc"):
+        bad_m = thl.bind_thl_gemm(-1, 64, 64, A, 64, "T", B, 64, "N", None, 64, D, 64, 1.0, 0.0, dts, epi, None,
+                                  None, entry)
+        assert bad_m() == bad_m() == thl.THL_ERR_INVALID
+        bad_ld = thl.bind_thl_gemm(64, 64, 64, A, 63, "T", B, 64, "N", None, 64, D, 64, 1.0, 0.0, dts, epi, None,
+                                   None, entry)
+        assert bad_ld() == thl.THL_ERR_INVALID
+    assert call(lda=63) == thl.THL_ERR_INVALID
+
+
 def test_leading_dimension_too_small():
     assert call(lda=63) == thl.THL_ERR_INVALID
     assert call(ldb=10) == thl.THL_ERR_INVALID

@@ -170,6 +170,30 @@ def thl_gemm(m, n, k, A, lda, opA, B, ldb, opB, C, ldc, D, ldd, alpha, beta, dty
                              ctypes.byref(scales) if scales is not None else None, stream))
 
 
+def bind_thl_gemm(m, n, k, A, lda, opA, B, ldb, opB, C, ldc, D, ldd, alpha, beta, dtypes, epilogue=None,
+                  scales=None, stream=None, entry="thl_gemm"):
+    """The arguments of one thl_gemm (or thl_gemm_noalloc) call, marshalled
+    once: returns a callable that issues exactly that call and returns its
+    status.  For loops that repeat one call (timing), where rebuilding the
+    ctypes arguments each time would cost more host time than a small
+    kernel runs."""
+    opa = THL_OP_T if opA in ("T", THL_OP_T) else (THL_OP_N if opA in ("N", THL_OP_N) else int(opA))
+    opb = THL_OP_T if opB in ("T", THL_OP_T) else (THL_OP_N if opB in ("N", THL_OP_N) else int(opB))
+    fn = getattr(_lib, entry)
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    args = (i64(m), i64(n), i64(k), vp(A), i64(lda), ctypes.c_int(opa), vp(B), i64(ldb), ctypes.c_int(opb), vp(C),
+            i64(ldc), vp(D), i64(ldd), ctypes.c_float(alpha), ctypes.c_float(beta), ctypes.byref(dtypes),
+            ctypes.byref(epilogue) if epilogue is not None else None,
+            ctypes.byref(scales) if scales is not None else None, vp(stream))
+    keep = (dtypes, epilogue, scales)
+
+    def call() -> int:
+        return fn(*args)
+
+    call.keep = keep  # the structures the byref arguments point into
+    return call
+
+
 def thl_gemm_noalloc(m, n, k, A, lda, opA, B, ldb, opB, C, ldc, D, ldd, alpha, beta, dtypes, epilogue=None,
                      scales=None, stream=None) -> int:
     """Direct call of the no-allocation C entry point (arguments as for thl_gemm)."""

@@ -46,9 +46,7 @@ class DeviceProblem:
             else:
                 self.d.fill_(d_fill)
 
-    def run(self, stream=None, d=None, c=None, ldc=None, entry=None):
-        """Run through thl_gemm (or `entry`, an entry point of the same
-        arguments, e.g. thl.thl_gemm_noalloc)."""
+    def _structs(self):
         w = self.w
         dt = thl.make_dtypes(w.type_a, w.type_b, w.type_c, w.type_d,
                              w.type_bias if w.bias is not None else "none")
@@ -59,16 +57,32 @@ class DeviceProblem:
         sc = thl.thl_scales(float(w.a_scale), float(w.b_scale),
                             self.sfa.data_ptr() if self.sfa is not None else None, int(w.ld_sfa),
                             self.sfb.data_ptr() if self.sfb is not None else None, int(w.ld_sfb))
-        if stream is None:
-            stream = torch.cuda.current_stream().cuda_stream
+        return dt, epi, sc
+
+    def _args(self, d=None, c=None, ldc=None):
+        w = self.w
         dd = self.d if d is None else d
         cc = self.c if c is None else c
         a_ptr = self.a.data_ptr() if self.a is not None and self.a.numel() else None
         b_ptr = self.b.data_ptr() if self.b is not None and self.b.numel() else None
-        status = (entry or thl.thl_gemm)(w.m, w.n, w.k, a_ptr, w.lda, w.op_a, b_ptr, w.ldb, w.op_b,
-                                         cc.data_ptr() if cc is not None else None, ldc or w.ldc or max(1, w.m),
-                                         dd.data_ptr(), self.ldd, w.alpha, w.beta, dt, epi, sc, stream)
-        return status
+        return (w.m, w.n, w.k, a_ptr, w.lda, w.op_a, b_ptr, w.ldb, w.op_b,
+                cc.data_ptr() if cc is not None else None, ldc or w.ldc or max(1, w.m),
+                dd.data_ptr(), self.ldd, w.alpha, w.beta)
+
+    def run(self, stream=None, d=None, c=None, ldc=None, entry=None):
+        """Run through thl_gemm (or `entry`, an entry point of the same
+        arguments, e.g. thl.thl_gemm_noalloc)."""
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        return (entry or thl.thl_gemm)(*self._args(d, c, ldc), *self._structs(), stream)
+
+    def bind(self, stream=None, entry="thl_gemm"):
+        """run()'s call with its arguments marshalled once: a callable that
+        issues it (for timing loops, where marshalling per call would cost
+        more host time than a small kernel runs)."""
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        return thl.bind_thl_gemm(*self._args(), *self._structs(), stream, entry)
 
     def d_values(self, rows, cols) -> np.ndarray:
         """D at (rows[t], cols[t]) as float64 (int64 for int32 outputs)."""
