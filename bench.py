@@ -48,6 +48,11 @@ CSRC = os.path.join(ROOT, "tile_hierarchy_linear_amd", "csrc")
 # Summary of the FETCH_SIZE / WRITE_SIZE counter runs over this script.
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_8192_hbm_traffic.md")
 
+# Least wall time of each configuration's untimed warm-up (seconds): the
+# chip takes about 40 ms of GEMM load to reach its steady clock from idle,
+# and it idles between configurations while the oracle checks parity.
+WARM_S = 0.1
+
 METRIC = "GEMM TFLOP/s and % of MFMA peak (bf16, fp8, MXFP4 at M=N=K=8192)"
 
 # (key, workload kind, m, n, k, bound, launches per timed step)
@@ -143,19 +148,26 @@ def measured_traffic(variant, m, n, k):
     return None
 
 
-def time_launches(run, steps, warmup, stream):
-    """Launch `run` warmup times untimed, then time `steps` launches back to
-    back on `stream` (the stream the kernels run on) between two HIP events:
-    the mean per launch.  A second pass of `steps` launches, each between
-    events of its own, gives the median and the minimum (an event between
-    launches adds a few microseconds of queue work, so it stays out of the
-    mean).  Returns (mean, median, min) per launch in ms."""
+def time_launches(run, steps, warmup, stream, min_warm_s=WARM_S):
+    """Launch `run` untimed: `warmup` times, and more until at least
+    `min_warm_s` seconds have passed (the clock ramp from idle takes some
+    40 ms of load).  Then time `steps` launches back to back on `stream` (the
+    stream the kernels run on) between two HIP events: the mean per launch.
+    A second pass of `steps` launches, each between events of its own, gives
+    the median and the minimum (an event between launches adds a few
+    microseconds of queue work, so it stays out of the mean).  Returns
+    (mean, median, min) per launch in ms."""
     import torch
 
+    t0 = time.perf_counter()
     for _ in range(warmup):
         st = run()
         assert st == 0, st
     torch.cuda.synchronize()
+    while time.perf_counter() - t0 < min_warm_s:
+        for _ in range(max(1, warmup)):
+            run()
+        torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for _ in range(steps):
@@ -423,7 +435,9 @@ def main():
     # The chip takes about 50 launches of the 8192^3 GEMM (some 40 ms of load)
     # to reach its steady clock from idle: bf16 measured 1,073 TFLOP/s at the
     # 5th launch, 1,305 at the 20th and 1,390-1,400 from the 50th to the
-    # 1,000th.  The default warm-up covers that ramp.
+    # 1,000th.  Each configuration's warm-up is W launches (times its
+    # multiplier) and at least WARM_S seconds, which covers that ramp also
+    # for the short kernels.
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--only", default="",
@@ -491,6 +505,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_min_s": WARM_S,
         "ms_per_step": h["ms_mean"],
         "higher_is_better": True,
         "scaling": "weak",
