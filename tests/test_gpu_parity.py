@@ -1228,3 +1228,24 @@ def test_mx_output_through_the_no_alloc_entry_point():
     assert ref.run() == 0 and got.run(entry=thl.thl_gemm_noalloc) == 0
     torch.cuda.synchronize()
     assert torch.equal(ref.d, got.d) and torch.equal(ref.sfd, got.sfd)
+
+
+def test_bound_call_repeats_the_call():
+    # DeviceProblem.bind (the benchmark's timed call: arguments marshalled
+    # once) writes what run() writes, through either entry point, and a
+    # second call writes the same again
+    import tile_hierarchy_linear_amd as thl
+    import workloads as wl
+    from workloads.device import DeviceProblem
+
+    w = wl.make("bf16", 300, 260, 520, act="relu", bias=True, beta=1.0)
+    ref = _check_full(w).d_all()
+    stream = torch.cuda.current_stream().cuda_stream
+    for entry in ("thl_gemm", "thl_gemm_noalloc"):
+        dp = DeviceProblem(w)
+        call = dp.bind(stream=stream, entry=entry)
+        for _ in range(2):
+            dp.d.fill_(float("nan"))
+            assert call() == thl.THL_OK
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(dp.d_all(), ref)
