@@ -1249,3 +1249,99 @@ def test_bound_call_repeats_the_call():
             assert call() == thl.THL_OK
             torch.cuda.synchronize()
             np.testing.assert_array_equal(dp.d_all(), ref)
+
+
+def _fuzz_case(i):
+    """Seeded random problem i: a family, layout, ragged shape, leading
+    dimensions (tight or padded, aligned or not where the format allows) and
+    epilogue, each drawn within the documented rules."""
+    import workloads as wl
+
+    g = np.random.default_rng(7000 + i)
+    pick = lambda xs: xs[int(g.integers(len(xs)))]  # noqa: E731
+    ops = pick([("T", "N"), ("N", "N"), ("T", "T"), ("N", "T")])
+    m, n = int(g.integers(1, 520)), int(g.integers(1, 330))
+    kind = pick(["fp16", "bf16", "int8", "fp8", "fp8e5m2", "fp8e4e5", "mxfp8", "mxfp4", "narrow"])
+    k = int(g.integers(0, 600))
+    if kind not in ("fp16", "bf16", "int8") and 0 < k < 256:
+        # the 8-, 6- and 4-bit formats with four or more MFMA steps per output:
+        # with one or two, the matrix cores' own accumulation error can pass
+        # the K-proportional bar (test_fp8_matrix_core_error_at_small_k)
+        k = 256 + k
+    act = pick(["none", "relu", "gelu"])
+    beta = pick([0.0, 1.0, -0.5])
+    bias = bool(g.integers(2))
+    ftypes = ["f32", "f16", "bf16"]
+
+    def ld(rows, quantum=1):
+        pad = pick([0, 0, 1, 8, 13])
+        return max(quantum, -(-(rows + pad) // quantum) * quantum)
+
+    if kind == "narrow":
+        fa, fb = pick(wl.NARROW if hasattr(wl, "NARROW") else ["e4m3", "e5m2", "e2m3", "e3m2", "e2m1"]), \
+            pick(["e4m3", "e5m2", "e2m3", "e3m2", "e2m1"])
+        mx = bool(g.integers(2))
+        if mx:
+            k -= k % 32
+        return wl.make_narrow(fa, fb, m, n, k, mx=mx, op_a=ops[0], op_b=ops[1], beta=beta, act=act, bias=bias,
+                              alpha=pick([1.0, 0.5]), ldd=ld(m), seed=7000 + i)
+    kw = dict(ldd=ld(m), act=act, bias=bias)
+    if kind in ("mxfp8", "mxfp4"):
+        ops = ("T", "N")
+        k -= k % 32
+    if kind == "int8":
+        kw.update(act=pick(["none", "relu"]), beta=pick([0.0, 1.0]))
+    else:
+        kw.update(beta=beta, type_d=pick(ftypes))
+        if beta != 0.0:
+            kw["type_c"] = pick(ftypes)
+        if bias:
+            kw["type_bias"] = pick(ftypes)
+    if beta != 0.0 or kw.get("beta"):
+        kw["ldc"] = ld(m)
+    q = 2 if kind in ("fp16", "bf16", "mxfp4") else 1  # 16-bit rows in whole 4-byte units; fp4 in whole bytes
+    a_rows = k if ops[0] == "T" else m
+    b_rows = k if ops[1] == "N" else n
+    kw.update(lda=ld(a_rows, q), ldb=ld(b_rows, q), op_a=ops[0], op_b=ops[1])
+    return wl.make(kind, m, n, k, seed=7000 + i, **kw)
+
+
+@pytest.mark.parametrize("i", range(64))
+def test_random_problems(i):
+    # sixty-four seeded random problems over every family, layout, alignment
+    # class and epilogue, each checked in full against the oracle
+    _check_full(_fuzz_case(i))
+
+
+def test_fp8_matrix_core_error_at_small_k():
+    # gfx950's fp8 MFMA does not sum in exact fp32: its error is about 2^-13 of
+    # the largest product in one instruction.  The parity bar's operand term,
+    # 2^-20 * K * max|a'| * max|b'|, grows with K and covers it from a few
+    # instructions on; with K = 32 (one instruction, half of it zeros) it can
+    # be smaller.  Measured here: MXFP8 291 x 12 x 32, where the bar's term is
+    # 4.3e-4 and a product reaches 10.5.  Every output stays within the bar
+    # plus 2^-12 of its own largest product; how many exceed the bar alone is
+    # printed, not asserted.
+    import workloads as wl
+    from oracle import compare
+    from workloads.device import DeviceProblem
+
+    w = wl.make("mxfp8", 291, 12, 32, lda=33, ldb=40, ldd=292, ldc=292, beta=1.0, act="relu", type_d="f32",
+                type_c="f32", seed=7012)
+    dp = DeviceProblem(w)
+    assert dp.run() == 0
+    torch.cuda.synchronize()
+    got = dp.d_all()
+    ii, jj = np.meshgrid(np.arange(w.m), np.arange(w.n), indexing="ij")
+    import oracle
+
+    want = oracle.gemm_elements(w.oracle_problem(), ii.ravel(), jj.ravel()).reshape(w.m, w.n)
+    a = compare.logical_operand(w, "a") * np.exp2(w.sfa[: w.m, :1].astype(np.float64) - 127) * w.a_scale
+    b = compare.logical_operand(w, "b") * np.exp2(w.sfb[: w.n, :1].astype(np.float64) - 127) * w.b_scale
+    largest = (np.abs(a)[:, None, :] * np.abs(b)[None, :, :]).max(axis=2)
+    tol = compare.float_tolerance(w.k, w.alpha, compare.operand_max_abs(w, "a"), compare.operand_max_abs(w, "b"),
+                                  w.type_d, want, w.act)
+    err = np.abs(got - want)
+    _say(f"[small K] {int((err > tol).sum())} of {err.size} outputs past the bar alone (largest error "
+         f"{err.max():.3g}, bar term {tol.min():.3g})")
+    assert np.all(err <= tol + 2.0 ** -12 * largest)
