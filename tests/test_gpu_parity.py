@@ -1345,3 +1345,77 @@ def test_fp8_matrix_core_error_at_small_k():
     _say(f"[small K] {int((err > tol).sum())} of {err.size} outputs past the bar alone (largest error "
          f"{err.max():.3g}, bar term {tol.min():.3g})")
     assert np.all(err <= tol + 2.0 ** -12 * largest)
+
+
+def _fuzz_special(i):
+    """Seeded random problem i for the paths the general draw rarely takes:
+    the small-M kernel (m <= 64, T/N, 16-byte rows), split K (a few 128x128
+    tiles over a long K) and batched launches (2 to 4 problems, sometimes
+    one operand shared).  Returns (category, workloads, shared)."""
+    import workloads as wl
+
+    g = np.random.default_rng(9000 + i)
+    pick = lambda xs: xs[int(g.integers(len(xs)))]  # noqa: E731
+    cat = ("small_m", "split_k", "batched")[i % 3]
+    ftypes = ["f32", "f16", "bf16"]
+    act = pick(["none", "relu", "gelu"])
+
+    def epi(kind, m):
+        if kind == "int8":
+            return dict(act=pick(["none", "relu"]), beta=pick([0.0, 1.0]), bias=bool(g.integers(2)), ldc=m)
+        beta = pick([0.0, 1.0, 0.5])
+        kw = dict(act=act, beta=beta, bias=bool(g.integers(2)), type_d=pick(ftypes), ldc=m)
+        if beta:
+            kw["type_c"] = pick(ftypes)
+        if kw["bias"]:
+            kw["type_bias"] = pick(ftypes)
+        return kw
+
+    if cat == "small_m":
+        kind = pick(["fp16", "bf16", "int8", "fp8", "fp8e5m2", "mxfp4"])
+        m, n, k = int(g.integers(1, 65)), int(g.integers(1, 1200)), int(g.integers(1, 3000))
+        q = {"fp16": 8, "bf16": 8, "int8": 16, "fp8": 16, "fp8e5m2": 16, "mxfp4": 32}[kind]
+        if kind == "mxfp4":
+            k = max(32, k - k % 32)
+        ld = -(-k // q) * q
+        w = wl.make(kind, m, n, k, seed=9000 + i, op_a="T", op_b="N", lda=ld, ldb=ld, **epi(kind, m))
+        return cat, [w], ()
+    if cat == "split_k":
+        kind = pick(["fp16", "bf16", "int8", "fp8"])
+        m, n = int(g.integers(1, 257)), int(g.integers(1, 257))
+        k = int(g.integers(4096, 6000)) * (1 if kind in ("fp16", "bf16") else 2)
+        ops = pick([("T", "N"), ("N", "N")]) if kind in ("fp16", "bf16") else ("T", "N")
+        lds = {}
+        if kind in ("fp16", "bf16"):  # 16-bit rows in whole 4-byte units
+            lds = dict(lda=-(-(k if ops[0] == "T" else m) // 2) * 2, ldb=-(-k // 2) * 2)
+        w = wl.make(kind, m, n, k, seed=9000 + i, op_a=ops[0], op_b=ops[1], **lds, **epi(kind, m))
+        return cat, [w], ()
+    kind = pick(["fp16", "bf16", "int8", "fp8", "mxfp4"])
+    m, n, k = int(g.integers(1, 300)), int(g.integers(1, 300)), int(g.integers(0, 700))
+    if kind == "mxfp4":
+        k = max(32, k - k % 32)
+    kw = epi(kind, m)
+    if kind in ("fp16", "bf16"):
+        ops = pick([("T", "N"), ("N", "N"), ("T", "T"), ("N", "T")])
+        kw.update(op_a=ops[0], op_b=ops[1], lda=-(-(k if ops[0] == "T" else m) // 8) * 8 or 8,
+                  ldb=-(-(k if ops[1] == "N" else n) // 8) * 8 or 8)
+    count = int(g.integers(2, 5))
+    ws = [wl.make(kind, m, n, k, seed=9000 + 17 * i + z, **kw) for z in range(count)]
+    shared = pick([(), (), ("b",), ("bias",)])
+    if shared == ("bias",) and ws[0].bias is None:
+        shared = ()
+    return cat, ws, shared
+
+
+@pytest.mark.parametrize("i", range(36))
+def test_random_special_paths(i):
+    # thirty-six seeded random problems on the small-M kernel, split K and
+    # batched launches, each problem's whole D against the oracle
+    import tile_hierarchy_linear_amd as thl
+
+    cat, ws, shared = _fuzz_special(i)
+    if cat == "batched":
+        _check_batched(ws, shared=shared)
+    else:
+        _check_full(ws[0])
+        _say(f"   ran {thl.thl_last_variant()} splits={thl.thl_last_splits()}")
