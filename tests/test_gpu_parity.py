@@ -1419,3 +1419,44 @@ def test_random_special_paths(i):
     else:
         _check_full(ws[0])
         _say(f"   ran {thl.thl_last_variant()} splits={thl.thl_last_splits()}")
+
+
+def _fuzz_grouped(i):
+    """Seeded random grouped launch i: 2 to 7 problems of one family and
+    epilogue with independent shapes (empty ones and K = 0 included) and
+    16-byte rows, as grouped launches take them."""
+    import workloads as wl
+
+    g = np.random.default_rng(9500 + i)
+    pick = lambda xs: xs[int(g.integers(len(xs)))]  # noqa: E731
+    kind = pick(["fp16", "bf16", "int8", "fp8", "mxfp8", "mxfp4"])
+    ops = pick([("T", "N"), ("N", "N"), ("T", "T"), ("N", "T")]) if kind in ("fp16", "bf16") else ("T", "N")
+    ftypes = ["f32", "f16", "bf16"]
+    if kind == "int8":
+        kw = dict(act=pick(["none", "relu"]), beta=pick([0.0, 1.0]), bias=bool(g.integers(2)))
+    else:
+        beta = pick([0.0, 1.0, -0.5])
+        kw = dict(act=pick(["none", "relu", "gelu"]), beta=beta, bias=bool(g.integers(2)), type_d=pick(ftypes))
+        if beta:
+            kw["type_c"] = pick(ftypes)
+        if kw["bias"]:
+            kw["type_bias"] = pick(ftypes)
+    q = {"fp16": 8, "bf16": 8, "int8": 16, "fp8": 16, "mxfp8": 16, "mxfp4": 32}[kind]
+    ws = []
+    for z in range(int(g.integers(2, 8))):
+        m, n, k = int(g.integers(0, 400)), int(g.integers(0, 300)), int(g.integers(0, 600))
+        if kind in ("fp8", "mxfp8", "mxfp4") and 0 < k < 256:
+            k += 256  # four or more MFMA steps per output (as in test_random_problems)
+        if kind in ("mxfp8", "mxfp4"):
+            k -= k % 32
+        a_rows = k if ops[0] == "T" else m
+        b_rows = k if ops[1] == "N" else n
+        lds = dict(lda=max(q, -(-a_rows // q) * q), ldb=max(q, -(-b_rows // q) * q))
+        ws.append(wl.make(kind, m, n, k, seed=9500 + 37 * i + z, op_a=ops[0], op_b=ops[1], **lds, **kw))
+    return ws
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_grouped(i):
+    # twelve seeded random grouped launches, every problem's D against the oracle
+    _check_grouped(_fuzz_grouped(i))
