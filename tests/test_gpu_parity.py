@@ -1460,3 +1460,27 @@ def _fuzz_grouped(i):
 def test_random_grouped(i):
     # twelve seeded random grouped launches, every problem's D against the oracle
     _check_grouped(_fuzz_grouped(i))
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_mx_output(i):
+    # sixteen seeded random MX-output problems (family, layout, shape with
+    # ragged 32-row blocks, element format) on exact inputs: codes and E8M0
+    # scales bit for bit against the oracle's quantisation
+    import oracle
+
+    g = np.random.default_rng(9800 + i)
+    pick = lambda xs: xs[int(g.integers(len(xs)))]  # noqa: E731
+    kind = pick(["bf16", "fp16", "fp8", "mxfp8", "mxfp4"])
+    ops = pick([("T", "N"), ("N", "N"), ("T", "T"), ("N", "T")]) if kind in ("bf16", "fp16") else ("T", "N")
+    fmt = pick(["e2m1", "e4m3", "e5m2"])
+    m, n = int(g.integers(1, 400)), int(g.integers(1, 300))
+    k = int(g.integers(1, 9)) * 32
+    w = _exact_mx_workload(kind, m, n, k, fmt, ops[0], ops[1], seed=9800 + i)
+    dp = _run_mx(w)
+    codes, scales = dp.mx_all()
+    y = oracle.gemm_full(w.oracle_problem())
+    want_codes, want_scales = oracle.mx_quantize_columns(y, fmt)
+    assert np.array_equal(scales, want_scales), np.argwhere(scales != want_scales)[:5]
+    bad = np.argwhere(codes != want_codes)
+    assert bad.size == 0, (bad[:5], codes[tuple(bad[0])], want_codes[tuple(bad[0])], y[tuple(bad[0])])
