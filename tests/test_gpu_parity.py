@@ -1417,8 +1417,16 @@ def test_random_special_paths(i):
     if cat == "batched":
         _check_batched(ws, shared=shared)
     else:
-        _check_full(ws[0])
+        dp = _check_full(ws[0])
         _say(f"   ran {thl.thl_last_variant()} splits={thl.thl_last_splits()}")
+        # the no-allocation entry point (its workspace in static scratch)
+        # writes the same bits
+        w = ws[0]
+        ref = dp.d[: w.n, : w.m].clone()
+        dp.d.fill_(-7)
+        assert dp.run(entry=thl.thl_gemm_noalloc) == 0
+        torch.cuda.synchronize()
+        assert torch.equal(dp.d[: w.n, : w.m], ref), thl.thl_last_variant()
 
 
 def _fuzz_grouped(i):
