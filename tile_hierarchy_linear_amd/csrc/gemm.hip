@@ -929,7 +929,7 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
     if (!ws) splits = 1;
   }
   const int64_t units = tiles * splits;
-  // Persistent workgroups; each walks units blockIdx.x, + gridDim.x, ...
+  // Persistent workgroups; each walks units blockIdx.y, + gridDim.y, ...
   const int64_t grid = persistent_grid(*pick, bt.count, units);
   if (grid <= 0) {
     if (pooled) (void)hipFreeAsync(ws, hs);
@@ -949,7 +949,7 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
     ap.alpha = 1.0f;
     ap.beta = 0.0f;
     ap.flags = pr.int_path ? 0 : EPI_VEC;
-    le = pick->launch(ap, dim3(static_cast<unsigned>(grid), 1u), hs);
+    le = pick->launch(ap, dim3(1u, static_cast<unsigned>(grid)), hs);
     // ... then their sum in split order through the epilogue
     if (le == hipSuccess) {
       ReduceArgs r{};
@@ -977,7 +977,8 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
       le = hipGetLastError();
     }
   } else {
-    le = pick->launch(a, dim3(static_cast<unsigned>(grid), static_cast<unsigned>(bt.count)), hs);
+    a.xcd_local = bt.count % 8 == 0 ? 1 : 0;
+    le = pick->launch(a, dim3(static_cast<unsigned>(bt.count), static_cast<unsigned>(grid)), hs);
   }
   if (pooled) (void)hipFreeAsync(ws, hs);  // back to the pool once the kernels have run
   if (le != hipSuccess) return THL_ERR_HIP;
@@ -1244,7 +1245,8 @@ thl_status grouped_impl(int64_t count, const thl_group_problem* pb, const thl_gr
   a.elem_bits_b = static_cast<int32_t>(dt->b == THL_E2M1X2 ? 4 : 8 * bytes_of(dt->b, 1));
   const int64_t grid = persistent_grid(*pick, count, max_tiles);
   if (grid <= 0) return THL_ERR_HIP;
-  if (pick->launch(a, dim3(static_cast<unsigned>(grid), static_cast<unsigned>(count)),
+  a.xcd_local = count % 8 == 0 ? 1 : 0;
+  if (pick->launch(a, dim3(static_cast<unsigned>(count), static_cast<unsigned>(grid)),
                    reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return THL_ERR_HIP;
   t_last_variant = pick->name;

@@ -58,13 +58,15 @@ struct GemmArgs {
   int32_t m, n, k;  // k in elements
   int32_t kbytes;   // bytes of K per operand row
   int32_t tiles_m, tiles_n, group_m;
+  int32_t xcd_local;  // a multiple of 8 problems: each problem's workgroups share one XCD
   float alpha, beta;  // alpha already holds the per-tensor fp8 scales
   int32_t flags;      // EPI_* bits
   int32_t c_type, d_type, bias_type;
-  // Batched problems: problem blockIdx.y's arrays lie these many bytes
-  // further per problem (all zero for a single problem).
+  // Batched problems: problem z's arrays (grid column blockIdx.x of the
+  // tiled kernels, row blockIdx.y of the small-M kernel) lie z times these
+  // many bytes further (all zero for a single problem).
   int64_t bs_a, bs_b, bs_c, bs_d, bs_bias, bs_sfa, bs_sfb;
-  // Grouped problems: grid row blockIdx.y computes group[blockIdx.y] (sizes,
+  // Grouped problems: grid column blockIdx.x computes group[blockIdx.x] (sizes,
   // pointers and leading dimensions replace the fields above); operand
   // elements are elem_bits_a / elem_bits_b bits wide.  NULL otherwise.
   const GroupProblem* group;

@@ -469,10 +469,9 @@ __device__ __forceinline__ uint8_t* ep_area() {
 }
 
 // Batched problems (L mode, the "CUTLASS" knowledge-base page's batched
-// GEMM): grid row blockIdx.y computes problem blockIdx.y, whose operands,
-// scales, C, bias and D sit at fixed byte strides from the first problem's.
-__device__ __forceinline__ void offset_to_problem(GemmArgs& p) {
-  const int64_t z = blockIdx.y;
+// GEMM): problem z's operands, scales, C, bias and D sit at fixed byte
+// strides from the first problem's.
+__device__ __forceinline__ void offset_to_problem(GemmArgs& p, const int64_t z) {
   p.a += z * p.bs_a;
   p.b += z * p.bs_b;
   p.sfa += z * p.bs_sfa;
@@ -483,12 +482,12 @@ __device__ __forceinline__ void offset_to_problem(GemmArgs& p) {
 }
 
 // Grouped problems (the grouped GEMM of "What's New in CUTLASS 4.8"): grid
-// row blockIdx.y computes problem group[blockIdx.y], whose sizes, pointers
+// column blockIdx.x computes problem group[blockIdx.x], whose sizes, pointers
 // and leading dimensions replace the launch-wide ones.  Returns false when
 // this workgroup has no tile of that problem (the whole workgroup leaves).
 template <int BM, int BN>
 __device__ __forceinline__ bool select_group_problem(GemmArgs& p) {
-  const GroupProblem& g = p.group[blockIdx.y];
+  const GroupProblem& g = p.group[blockIdx.x];
   const int64_t m = g.m, n = g.n, k = g.k;
   p.m = static_cast<int32_t>(m);
   p.n = static_cast<int32_t>(n);
@@ -509,7 +508,7 @@ __device__ __forceinline__ bool select_group_problem(GemmArgs& p) {
   p.ld_sfb = g.ld_sfb;
   p.tiles_m = static_cast<int32_t>((m + BM - 1) / BM);
   p.tiles_n = static_cast<int32_t>((n + BN - 1) / BN);
-  return m > 0 && n > 0 && static_cast<int64_t>(blockIdx.x) < static_cast<int64_t>(p.tiles_m) * p.tiles_n;
+  return m > 0 && n > 0 && static_cast<int64_t>(blockIdx.y) < static_cast<int64_t>(p.tiles_m) * p.tiles_n;
 }
 
 // ------------------------------------------------------------ the kernel
@@ -547,10 +546,12 @@ template <int F, int BM, int BN, int WM, int WN, int LOADW, int STAGES, int OCC,
           bool MXO = false>
 __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 gemm_kernel(GemmArgs p) {
+  // Grid: problem blockIdx.x (one for a single problem), persistent
+  // workgroup blockIdx.y of gridDim.y per problem.
   if (p.group) {
     if (!select_group_problem<BM, BN>(p)) return;
   } else {
-    offset_to_problem(p);
+    offset_to_problem(p, blockIdx.x);
   }
   using T = Fam<F>;
   using Acc = typename T::Acc;
@@ -706,10 +707,13 @@ gemm_kernel(GemmArgs p) {
   uint32_t sc_src[T::SCALED ? SC_LOADS : 1];
   bool sc_a[T::SCALED ? SC_LOADS : 1];
   int sc_dst[T::SCALED ? SC_LOADS : 1];
-  // Workgroups visit tiles id = blockIdx.x, + gridDim.x, ...; the XCD remap
+  // Workgroups visit tiles id = blockIdx.y, + gridDim.y, ...; the XCD remap
   // and grouped raster turn id into (tm, tn) so that the tiles one XCD works
-  // on at a time share A and B panels in its L2 (gridDim.x is a multiple of
-  // 8 whenever the tile count is).
+  // on at a time share A and B panels in its L2 (gridDim.y is a multiple of
+  // 8 whenever the tile count is).  The hardware deals workgroups to the 8
+  // XCDs by their linear id x + y * gridDim.x: with a multiple of 8
+  // problems every workgroup of a problem runs on one XCD (p.xcd_local), and
+  // the raster alone keeps its concurrent tiles together.
   auto setup = [&](int id) {
     int64_t tm, tn;
     if (SPLITK && splits > 1) {
@@ -718,7 +722,7 @@ gemm_kernel(GemmArgs p) {
       unit_split = id - unit_tile * splits;
       maps::grouped_tile(unit_tile, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
     } else {
-      maps::grouped_tile(maps::xcd_remap(id, ntiles), p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
+      maps::grouped_tile(p.xcd_local ? id : maps::xcd_remap(id, ntiles), p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
     }
     m0 = tm * BM;
     n0 = tn * BN;
@@ -1641,7 +1645,7 @@ gemm_kernel(GemmArgs p) {
   };
 
   // ---------------------------------------------------------- tile loop
-  int id = static_cast<int>(blockIdx.x);
+  int id = static_cast<int>(blockIdx.y);
   setup(id);
   if (nkf > 0) prologue();
   for (bool first = true;; first = false) {
@@ -1702,7 +1706,7 @@ gemm_kernel(GemmArgs p) {
     wg_barrier();  // every wave is done with the ring
     const int64_t em0 = m0, en0 = n0;
     void* const d_ep = d_unit;  // (setup of the next unit moves d_unit)
-    const int next = id + static_cast<int>(gridDim.x);
+    const int next = id + static_cast<int>(gridDim.y);
     if constexpr (EP_OWN) {
       if (next < nunits) {
         setup(next);

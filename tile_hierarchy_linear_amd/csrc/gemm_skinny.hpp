@@ -122,7 +122,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, Acc sum, int64_t n
 // still read once.
 template <int F, int KW, int UN = 2, int MT = 1>
 __global__ void __launch_bounds__(KW * 64) skinny_kernel(GemmArgs p) {
-  offset_to_problem(p);
+  offset_to_problem(p, blockIdx.y);
   using S = Skinny<F>;
   using Acc = typename S::Acc;
   constexpr bool SCALED = F == FAM_FP4;
