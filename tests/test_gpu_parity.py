@@ -1492,3 +1492,29 @@ def test_random_mx_output(i):
     assert np.array_equal(scales, want_scales), np.argwhere(scales != want_scales)[:5]
     bad = np.argwhere(codes != want_codes)
     assert bad.size == 0, (bad[:5], codes[tuple(bad[0])], want_codes[tuple(bad[0])], y[tuple(bad[0])])
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_batched_narrow(i):
+    # sixteen seeded random batched launches of 8-, 6- and 4-bit pairings in
+    # any layout (the conversion pass per problem when needed), 2 to 16
+    # problems (multiples of 8 among them: each problem on one XCD),
+    # sometimes one operand shared; every problem's D against the oracle
+    import workloads as wl
+
+    g = np.random.default_rng(9900 + i)
+    pick = lambda xs: xs[int(g.integers(len(xs)))]  # noqa: E731
+    fmts = ["e4m3", "e5m2", "e2m3", "e3m2", "e2m1"]
+    fa, fb = pick(fmts), pick(fmts)
+    mx = bool(g.integers(2))
+    ops = pick([("T", "N"), ("N", "N"), ("T", "T"), ("N", "T")])
+    m, n = int(g.integers(1, 260)), int(g.integers(1, 200))
+    k = 256 + int(g.integers(0, 300))
+    if mx:
+        k -= k % 32
+    count = pick([2, 3, 5, 8, 16])
+    beta, act, bias = pick([0.0, 1.0]), pick(["none", "relu"]), bool(g.integers(2))  # one epilogue per batch
+    ws = [wl.make_narrow(fa, fb, m, n, k, mx=mx, op_a=ops[0], op_b=ops[1], beta=beta, act=act, bias=bias,
+                         seed=9900 + 31 * i + z) for z in range(count)]
+    shared = pick([(), (), ("a",) + (("sfa",) if mx else ()), ("b",) + (("sfb",) if mx else ())])
+    _check_batched(ws, shared=shared)
