@@ -114,6 +114,13 @@ typedef struct {
  *
  * Built combinations (first fitting kernel is launched):
  *   F16 or BF16 operands, opA/opB in {N,T}: F32 accumulate; C, D in F32/F16/BF16.
+ *     An operand whose stored lines (rows along K, or k-lines along M or N)
+ *     are not whole 4-byte units (an odd leading dimension, batch stride or
+ *     base offset), or, with D of 2^23 elements or more, not whole 16-byte
+ *     units, is first copied by the conversion pass below into a workspace
+ *     at a pitch of whole 64-byte units, in the same layout (variant name
+ *     suffix "+cvt_a", "+cvt_b" or "+cvt_ab"); not while THL_FORCE_VARIANT
+ *     is set.
  *   I8 operands, opA = T, opB = N: I32 accumulate, C and D I32, bias I32;
  *     alpha must be 1 and beta 0 or 1 (the integer epilogue is exact, in int32).
  *   E4M3 operands, opA = T, opB = N: F32 accumulate, s_a, s_b = scales->a_scale,

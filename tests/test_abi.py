@@ -183,10 +183,25 @@ def test_mxfp4_scale_rows_must_be_16_byte_aligned():
     assert call(types=("e2m1", "f32", "bf16", "none"), sc=sc) in (thl.THL_OK, thl.THL_ERR_HIP)
 
 
-def test_misaligned():
-    # bf16 rows of 63 elements = 126 bytes: not 4-byte aligned for any variant
-    assert call(k=63, lda=63, ldb=64) == thl.THL_ERR_MISALIGNED
-    assert call(a=A + 2) == thl.THL_ERR_MISALIGNED
+def test_misaligned_16bit_lines_take_the_pass():
+    # bf16 rows of 63 elements = 126 bytes, or a base 2 bytes off, fit no
+    # kernel: the pass re-pitches them in their own layout (m = 0 runs the
+    # choice and validation without touching a device)
+    assert call(m=0, k=63, lda=63, ldb=64) == thl.THL_OK
+    assert thl.thl_last_variant().endswith("+cvt_a") and "_tn_" in thl.thl_last_variant()
+    assert call(m=0, a=A + 2) == thl.THL_OK
+    assert thl.thl_last_variant().endswith("+cvt_a")
+    assert call(m=0, opa="N", lda=8, opb="T", ldb=65) == thl.THL_OK
+    assert thl.thl_last_variant().endswith("+cvt_b") and "_nt_" in thl.thl_last_variant()
+    # 4-byte lines that are not 16-byte units stay on the 4-byte-copy kernels
+    assert call(m=0, k=64, lda=66, ldb=64) == thl.THL_OK
+    assert "+cvt" not in thl.thl_last_variant() and "_v4_" in thl.thl_last_variant()
+    # a forced variant keeps the caller's lines, which it cannot read
+    os.environ["THL_FORCE_VARIANT"] = "bf16_tn_128x128_v4_s4_o2"
+    try:
+        assert call(m=0, k=63, lda=63, ldb=64) == thl.THL_ERR_UNSUPPORTED
+    finally:
+        del os.environ["THL_FORCE_VARIANT"]
 
 
 def test_overlaps():
@@ -293,9 +308,9 @@ def test_batched_validation():
     # fp4 operand strides count fp4 elements and must be even
     assert bcall(sa=33, k=64, types=("e2m1", "bf16", "bf16", "none"), lda=64, ldb=64) == thl.THL_ERR_INVALID
     # a stride that breaks every variant's 4-byte alignment (the second
-    # problem's A would start 2 bytes off)
-    assert bcall(sa=64 * 64 + 1) == thl.THL_ERR_MISALIGNED
-    assert bcall(n=0, sa=64 * 64 + 1) == thl.THL_ERR_MISALIGNED  # selection runs before the quick return
+    # problem's A would start 2 bytes off): re-pitched by the pass
+    assert bcall(n=0, sa=64 * 64 + 1) == thl.THL_OK  # selection runs before the quick return
+    assert thl.thl_last_variant().endswith("+cvt_a")
 
 
 # ------------------------------------------------------------ grouped problems
@@ -445,10 +460,11 @@ def test_no_alloc_entry_point_bounds_the_converted_operands():
 
 def test_rows_off_every_kernel_alignment_take_the_pass():
     # fp8 rows of 2041 bytes fit no kernel (they need 4-byte units): rewritten
-    # whatever the size; bf16 rows of odd length have no such path
+    # whatever the size; bf16 rows of odd length are re-pitched as bf16
     assert call(m=0, types=("e4m3", "f32", "bf16", "none"), k=2041, lda=2041, ldb=2041) == thl.THL_OK
     assert thl.thl_last_variant().endswith("+cvt_ab")
     assert call(m=0, types=("e4m3", "f32", "bf16", "none"), k=2040, lda=2040, ldb=2040) == thl.THL_OK
     assert "+cvt" not in thl.thl_last_variant() and "_v4_" in thl.thl_last_variant()
-    assert call(m=8, types=("bf16", "f32", "f32", "none"), k=63, lda=63, ldb=63) == thl.THL_ERR_MISALIGNED
+    assert call(m=0, types=("bf16", "f32", "f32", "none"), k=63, lda=63, ldb=63) == thl.THL_OK
+    assert thl.thl_last_variant().endswith("+cvt_ab")
 

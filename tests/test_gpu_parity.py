@@ -1518,3 +1518,69 @@ def test_random_batched_narrow(i):
                          seed=9900 + 31 * i + z) for z in range(count)]
     shared = pick([(), (), ("a",) + (("sfa",) if mx else ()), ("b",) + (("sfb",) if mx else ())])
     _check_batched(ws, shared=shared)
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp16"])
+@pytest.mark.parametrize("ops", [("N", "N"), ("T", "N"), ("N", "T"), ("T", "T")])
+def test_16bit_lines_off_4_byte_units_take_the_pass(kind, ops):
+    # odd leading dimensions: 16-bit lines that no kernel reads, re-pitched
+    # by the pass in their own layout ("+cvt_a", "+cvt_b", "+cvt_ab")
+    import tile_hierarchy_linear_amd as thl
+    import workloads as wl
+
+    m, n, k = 203, 141, 317  # odd: tight leading dimensions are odd
+    lda = m if ops[0] == "N" else k
+    ldb = (k if ops[1] == "N" else n) if ops != ("N", "T") else n + 7  # 296-byte lines: 4-byte units
+    w = wl.make(kind, m, n, k, op_a=ops[0], op_b=ops[1], lda=lda, ldb=ldb, beta=1.0, bias=True, act="relu",
+                type_c="bf16", type_bias="f32", ldc=m + 3, ldd=m + 1)
+    _check_full(w)
+    v = thl.thl_last_variant()
+    want = "+cvt_a" if ops == ("N", "T") else "+cvt_ab"
+    assert v.endswith(want) and f"_{(ops[0] + ops[1]).lower()}_" in v, v
+
+
+def test_16bit_base_off_4_bytes_and_no_alloc():
+    # A's base 2 bytes past a 4-byte unit: re-pitched; the no-allocation
+    # entry point (the re-pitched copy in static scratch) writes the same bits
+    import tile_hierarchy_linear_amd as thl
+    import workloads as wl
+    from oracle import compare
+    from workloads.device import DeviceProblem
+
+    w = wl.make("bf16", 150, 90, 200, op_a="T", op_b="N", lda=200, ldb=200)
+    dp = DeviceProblem(w)
+    buf = torch.zeros(dp.a.numel() + 2, dtype=torch.uint8, device="cuda")
+    buf[2:] = dp.a
+    dp.a = buf[2:]
+    assert dp.a.data_ptr() % 4 == 2
+    assert dp.run() == 0
+    torch.cuda.synchronize()
+    assert thl.thl_last_variant().endswith("+cvt_a"), thl.thl_last_variant()
+    got = dp.d_all()
+    ii, jj = np.meshgrid(np.arange(w.m), np.arange(w.n), indexing="ij")
+    assert compare.parity_check(w, got.ravel(), ii.ravel(), jj.ravel())["ok"]
+    ref = dp.d[: w.n, : w.m].clone()
+    dp.d.fill_(-7)
+    assert dp.run(entry=thl.thl_gemm_noalloc) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(dp.d[: w.n, : w.m], ref)
+
+
+def test_16bit_batched_odd_leading_dimension():
+    # three problems whose A lines (M-major, odd lda) fit no kernel: each
+    # problem re-pitched at the batch stride of the copies
+    import workloads as wl
+
+    ws = [wl.make("bf16", 130, 70, 96, lda=131, seed=77 + z) for z in range(3)]
+    _check_batched(ws, expect="+cvt_a")
+
+
+def test_16bit_lines_off_16_byte_units_at_a_large_shape():
+    # lines of whole 4-byte but not 16-byte units with D of 2^23 elements or
+    # more: re-pitched for the 16-byte kernels
+    import tile_hierarchy_linear_amd as thl
+    import workloads as wl
+
+    w = wl.make("bf16", 4096, 2048, 512, lda=4098)
+    _check_sampled(w, extra_edges=True)
+    assert thl.thl_last_variant().endswith("+cvt_a") and "_v16_" in thl.thl_last_variant(), thl.thl_last_variant()

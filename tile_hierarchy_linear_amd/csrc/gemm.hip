@@ -763,6 +763,9 @@ int choose_splits(const Prep& pr, const Variant& v, const Batch& bt, int64_t til
 struct Stage {
   bool a = false, b = false;
   thl_dtype ta = THL_NONE, tb = THL_NONE;  // formats after the rewrite
+  // 16-bit operands: lines re-pitched byte for byte in their own layout
+  // (M- or K-major kept) rather than rewritten as K-major rows
+  bool keep_a = false, keep_b = false;
 };
 
 bool is_fp8(thl_dtype t) { return t == THL_E4M3 || t == THL_E5M2; }
@@ -802,7 +805,7 @@ bool plan_stage(const thl_dtypes* dt, thl_op opA, thl_op opB, const thl_scales* 
       g.ta = is_fp8(dt->a) ? dt->a : THL_E4M3;
       g.tb = is_fp8(dt->b) ? dt->b : THL_E4M3;
     }
-  } else {
+  } else if (!((dt->a == THL_F16 || dt->a == THL_BF16) && dt->b == dt->a)) {
     return false;
   }
   // re-pitch misaligned K-major rows of a large problem (not when a variant
@@ -821,6 +824,20 @@ bool plan_stage(const thl_dtypes* dt, thl_op opA, thl_op opB, const thl_scales* 
   };
   auto repitchable = [](thl_dtype t) { return t == THL_I8 || is_fp8(t) || t == THL_E2M1X2; };
   const bool keep = forced && *forced;
+  if (dt->a == THL_F16 || dt->a == THL_BF16) {
+    // 16-bit lines (rows along K, or k-lines along M) in either layout, by
+    // the same rules: not whole 4-byte units (no kernel reads them), or not
+    // whole 16-byte units with D of 2^23 elements or more
+    g.a = (large && !rows16(A, dt->a, lda, bt.a)) || (!keep && !rows4(A, dt->a, lda, bt.a));
+    g.b = (large && !rows16(B, dt->b, ldb, bt.b)) || (!keep && !rows4(B, dt->b, ldb, bt.b));
+    g.ta = dt->a;
+    g.tb = dt->b;
+    g.keep_a = g.a;
+    g.keep_b = g.b;
+    if (!g.a && !g.b) return false;
+    *sg = g;
+    return true;
+  }
   if (!g.a && a_km && repitchable(dt->a) &&
       ((large && !rows16(A, dt->a, lda, bt.a)) || (!keep && !rows4(A, dt->a, lda, bt.a)))) {
     g.a = true;
@@ -1029,14 +1046,21 @@ thl_status staged_gemm(const Batch& bt, int64_t m, int64_t n, int64_t k, const v
         return THL_ERR_INVALID;
     }
   }
-  if (sg.a && (m + 63) / 64 > 65535) return THL_ERR_UNSUPPORTED;  // the pass's grid
-  if (sg.b && (n + 63) / 64 > 65535) return THL_ERR_UNSUPPORTED;
-
-  // ---- the rewritten operands: K-major rows of 64-byte steps
-  const int64_t lda_b = staged_ld_bytes(sg.ta, k), ldb_b = staged_ld_bytes(sg.tb, k);
+  // ---- the rewritten operands: K-major rows of 64-byte steps, or (16-bit,
+  // keep_*) the caller's lines, in the caller's layout, at a pitch of whole
+  // 64-byte units.  lines_* lines of line_*: A's are rows (opA = T) or
+  // k-lines along M (opA = N), B's columns (opB = N) or k-lines along N.
+  const int64_t lines_a = sg.keep_a && opA == THL_OP_N ? k : m;
+  const int64_t lines_b = sg.keep_b && opB == THL_OP_T ? k : n;
+  const int64_t line_a = sg.keep_a && opA == THL_OP_N ? m : k;
+  const int64_t line_b = sg.keep_b && opB == THL_OP_T ? n : k;
+  if (sg.a && (lines_a + 63) / 64 > 65535) return THL_ERR_UNSUPPORTED;  // the pass's grid
+  if (sg.b && (lines_b + 63) / 64 > 65535) return THL_ERR_UNSUPPORTED;
+  const int64_t lda_b = staged_ld_bytes(sg.ta, line_a), ldb_b = staged_ld_bytes(sg.tb, line_b);
   const int64_t elems_per_byte_a = sg.ta == THL_E2M1X2 ? 2 : 1, elems_per_byte_b = sg.tb == THL_E2M1X2 ? 2 : 1;
-  const int64_t size_a = sg.a ? (m * lda_b + 255) / 256 * 256 : 0;
-  const int64_t size_b = sg.b ? (n * ldb_b + 255) / 256 * 256 : 0;
+  const int64_t elem_bytes_a = sg.keep_a ? 2 : 1, elem_bytes_b = sg.keep_b ? 2 : 1;  // kept 16-bit elements
+  const int64_t size_a = sg.a ? (lines_a * lda_b + 255) / 256 * 256 : 0;
+  const int64_t size_b = sg.b ? (lines_b * ldb_b + 255) / 256 * 256 : 0;
   const int64_t count = bt.count > 0 ? bt.count : 0;
   const int64_t total = count * (size_a + size_b);
   const bool run_pass = work && k > 0 && total > 0;
@@ -1048,16 +1072,17 @@ thl_status staged_gemm(const Batch& bt, int64_t m, int64_t n, int64_t k, const v
   if (!is_fp8(dt->a)) s2.a_scale = 1.0f;
   if (!is_fp8(dt->b)) s2.b_scale = 1.0f;
   Batch b2 = bt;
-  if (sg.a) b2.a = count > 1 ? size_a * elems_per_byte_a : 0;
-  if (sg.b) b2.b = count > 1 ? size_b * elems_per_byte_b : 0;
+  if (sg.a) b2.a = count > 1 ? size_a * elems_per_byte_a / elem_bytes_a : 0;
+  if (sg.b) b2.b = count > 1 ? size_b * elems_per_byte_b / elem_bytes_b : 0;
   // The rewritten operands are fresh memory: validated at stand-in addresses
   // (256-byte aligned, far above any allocation, never dereferenced) so that
   // every argument error is reported before anything is allocated or run.
   const uintptr_t stand_in = static_cast<uintptr_t>(1) << 62;
   const void* A2 = sg.a ? (run_pass ? reinterpret_cast<const void*>(stand_in) : nullptr) : A;
   const void* B2 = sg.b ? (run_pass ? reinterpret_cast<const void*>(stand_in + count * size_a) : nullptr) : B;
-  const int64_t lda2 = sg.a ? lda_b * elems_per_byte_a : lda, ldb2 = sg.b ? ldb_b * elems_per_byte_b : ldb;
-  const thl_op opA2 = sg.a ? THL_OP_T : opA, opB2 = sg.b ? THL_OP_N : opB;
+  const int64_t lda2 = sg.a ? lda_b * elems_per_byte_a / elem_bytes_a : lda;
+  const int64_t ldb2 = sg.b ? ldb_b * elems_per_byte_b / elem_bytes_b : ldb;
+  const thl_op opA2 = sg.a && !sg.keep_a ? THL_OP_T : opA, opB2 = sg.b && !sg.keep_b ? THL_OP_N : opB;
   {
     Prep check;
     const thl_status st = prepare(b2, m, n, k, A2, lda2, opA2, B2, ldb2, opB2, C, ldc, D, ldd, alpha, beta, &d2,
@@ -1109,9 +1134,33 @@ thl_status staged_gemm(const Batch& bt, int64_t m, int64_t n, int64_t k, const v
     c.dst_batch = dst_batch;
     return launch_convert(c, count, hs);
   };
+  // 16-bit lines moved byte for byte: the pass's 8-bit K-major path over
+  // lines of 2 * line bytes
+  auto repitch = [&](const void* src, int64_t ld, int64_t stride, int64_t lines, int64_t line, uint8_t* dst,
+                     int64_t dst_ld, int64_t dst_batch) -> hipError_t {
+    CvtArgs c{};
+    c.src = static_cast<const uint8_t*>(src);
+    c.ld_bytes = 2 * ld;
+    c.line_bytes = 2 * line;
+    c.src_batch = 2 * stride;
+    c.src_fmt = THL_I8;
+    c.dst_fmt = THL_I8;
+    c.kmajor = 1;
+    c.aligned4 = (reinterpret_cast<uintptr_t>(src) % 4 == 0 && c.ld_bytes % 4 == 0 && c.src_batch % 4 == 0) ? 1 : 0;
+    c.rows = lines;
+    c.k = 2 * line;
+    c.dst = dst;
+    c.dst_ld_bytes = dst_ld;
+    c.dst_batch = dst_batch;
+    return launch_convert(c, count, hs);
+  };
   hipError_t le = hipSuccess;
-  if (run_pass && sg.a) le = pass(A, dt->a, sg.ta, lda, bt.a, opA == THL_OP_T, m, wa, lda_b, size_a);
-  if (run_pass && sg.b && le == hipSuccess) le = pass(B, dt->b, sg.tb, ldb, bt.b, opB == THL_OP_N, n, wb, ldb_b, size_b);
+  if (run_pass && sg.a)
+    le = sg.keep_a ? repitch(A, lda, bt.a, lines_a, line_a, wa, lda_b, size_a)
+                   : pass(A, dt->a, sg.ta, lda, bt.a, opA == THL_OP_T, m, wa, lda_b, size_a);
+  if (run_pass && sg.b && le == hipSuccess)
+    le = sg.keep_b ? repitch(B, ldb, bt.b, lines_b, line_b, wb, ldb_b, size_b)
+                   : pass(B, dt->b, sg.tb, ldb, bt.b, opB == THL_OP_N, n, wb, ldb_b, size_b);
   if (le != hipSuccess) {
     if (pooled) (void)hipFreeAsync(ws, hs);
     return THL_ERR_HIP;
