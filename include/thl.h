@@ -196,8 +196,10 @@ typedef struct {
  * format, magnitudes past its largest finite value clamped to it, signs kept;
  * a block of zeros gets scale code 0.  The tiled kernels' general epilogue
  * writes it (no small-M kernel, no split K), built with 16-byte operand
- * loads only: A and B need 16-byte aligned bases and leading dimensions
- * (THL_ERR_MISALIGNED otherwise); single problems only (batched and grouped
+ * loads only: operand lines that are not whole 16-byte units (base or
+ * leading dimension) are first re-pitched by the conversion pass (fp16,
+ * bf16 in their own layout; 8- and 4-bit as K-major rows), whatever the
+ * size; single problems only (batched and grouped
  * launches return THL_ERR_UNSUPPORTED); sfd must not overlap any other array
  * (THL_ERR_INVALID, as a NULL sfd or a short ld_sfd is).
  *

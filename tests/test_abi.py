@@ -407,11 +407,18 @@ def test_mx_output_is_for_single_float_problems():
     assert call(types=("i8", "i32", "e4m3", "none"), sfd=SFD, ld_sfd=2) == thl.THL_ERR_UNSUPPORTED
 
 
-def test_mx_output_needs_16_byte_operand_rows():
-    # bf16 B rows of 130 elements (260 bytes): no MX-output variant loads them
+def test_mx_output_re_pitches_operand_lines_off_16_byte_units():
+    # bf16 B lines of 130 elements (260 bytes): the MX-output kernels load
+    # 16-byte units only, so the pass re-pitches them (m = 0: choice and
+    # validation only)
     types = ("bf16", "f32", "e4m3", "none")
-    assert call(n=130, opb="T", ldb=130, sfd=SFD, ld_sfd=2, types=types) == thl.THL_ERR_MISALIGNED
+    assert call(n=130, opb="T", ldb=130, sfd=SFD, ld_sfd=2, types=types, m=0) == thl.THL_OK
+    assert thl.thl_last_variant().endswith("_mxout+cvt_b"), thl.thl_last_variant()
     assert call(n=130, opb="T", ldb=136, sfd=SFD, ld_sfd=2, types=types, m=0) == thl.THL_OK
+    assert "+cvt" not in thl.thl_last_variant()
+    # fp8 rows of 68 bytes: the same
+    assert call(types=("e4m3", "f32", "e4m3", "none"), k=64, lda=68, ldb=64, sfd=SFD, ld_sfd=2, m=0) == thl.THL_OK
+    assert thl.thl_last_variant().endswith("_mxout+cvt_a"), thl.thl_last_variant()
 
 
 # ------------------------------------------------------------ the conversion pass

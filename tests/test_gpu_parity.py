@@ -916,7 +916,7 @@ def test_split_k_is_deterministic():
 
 # ------------------------------------------------------------ MX output (D as MX blocks)
 
-def _exact_mx_workload(kind, m, n, k, fmt, op_a=None, op_b=None, seed=0):
+def _exact_mx_workload(kind, m, n, k, fmt, op_a=None, op_b=None, seed=0, lds=None):
     """Operands, C and bias with small integer values (e2m1 values for fp4)
     and alpha = 1/2: every fp32 epilogue value on the GPU is exact, so its MX
     blocks must be the oracle's bit for bit."""
@@ -930,9 +930,10 @@ def _exact_mx_workload(kind, m, n, k, fmt, op_a=None, op_b=None, seed=0):
         kw["op_b"] = op_b
     # MX output runs with 16-byte operand loads: rows of A and B padded to 8 elements
     pad8 = lambda v: (v + 7) // 8 * 8
-    lds = {}
-    if kind in ("bf16", "fp16"):
-        lds = dict(lda=pad8(m if (op_a or "N") == "N" else k), ldb=pad8(k if (op_b or "N") == "N" else n))
+    if lds is None:
+        lds = {}
+        if kind in ("bf16", "fp16"):
+            lds = dict(lda=pad8(m if (op_a or "N") == "N" else k), ldb=pad8(k if (op_b or "N") == "N" else n))
     w = wl.make(kind, m, n, k, type_d=fmt, ldd=m + 8 + m % 2, **kw, **lds)
     if kind == "mxfp4":
         vals = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.5, -1, -1.5, -2, -3, -4, -6])
@@ -971,7 +972,7 @@ def _run_mx(w, variant=None):
         torch.cuda.synchronize()
     finally:
         os.environ.pop("THL_FORCE_VARIANT", None)
-    assert thl.thl_last_variant() == variant if variant else thl.thl_last_variant().endswith("_mxout")
+    assert thl.thl_last_variant() == variant if variant else "_mxout" in thl.thl_last_variant()
     return dp
 
 
@@ -1584,3 +1585,24 @@ def test_16bit_lines_off_16_byte_units_at_a_large_shape():
     w = wl.make("bf16", 4096, 2048, 512, lda=4098)
     _check_sampled(w, extra_edges=True)
     assert thl.thl_last_variant().endswith("+cvt_a") and "_v16_" in thl.thl_last_variant(), thl.thl_last_variant()
+
+
+@pytest.mark.parametrize("kind,ops,lds,want", [
+    ("bf16", ("N", "T"), {"lda": 208, "ldb": 130}, "+cvt_b"),   # B k-lines of 260 bytes
+    ("bf16", ("T", "N"), {"lda": 97, "ldb": 97}, "+cvt_ab"),    # odd: no kernel at all
+    ("fp8", ("T", "N"), {"lda": 100, "ldb": 96}, "+cvt_a"),     # A rows of 100 bytes
+])
+def test_mx_output_with_operand_lines_off_16_byte_units(kind, ops, lds, want):
+    # the MX-output kernels load 16-byte units: such operands are re-pitched
+    # first; codes and scales still bit for bit on exact inputs
+    import oracle
+    import tile_hierarchy_linear_amd as thl
+
+    w = _exact_mx_workload(kind, 200, 130, 96, "e4m3", ops[0], ops[1], seed=91, lds=lds)
+    dp = _run_mx(w)
+    assert thl.thl_last_variant().endswith("_mxout" + want), thl.thl_last_variant()
+    codes, scales = dp.mx_all()
+    y = oracle.gemm_full(w.oracle_problem())
+    want_codes, want_scales = oracle.mx_quantize_columns(y, "e4m3")
+    assert np.array_equal(scales, want_scales)
+    assert np.array_equal(codes, want_codes)

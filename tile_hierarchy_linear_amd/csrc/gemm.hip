@@ -824,12 +824,18 @@ bool plan_stage(const thl_dtypes* dt, thl_op opA, thl_op opB, const thl_scales* 
   };
   auto repitchable = [](thl_dtype t) { return t == THL_I8 || is_fp8(t) || t == THL_E2M1X2; };
   const bool keep = forced && *forced;
+  // lines no kernel reads: not whole 4-byte units, or for MX-format D (whose
+  // kernels load 16-byte units only) not whole 16-byte units
+  const bool mx_d = is_mx_out(dt->d);
+  auto unreadable = [&](const void* p, thl_dtype t, int64_t ld, int64_t stride) {
+    return mx_d ? !rows16(p, t, ld, stride) : !rows4(p, t, ld, stride);
+  };
   if (dt->a == THL_F16 || dt->a == THL_BF16) {
     // 16-bit lines (rows along K, or k-lines along M) in either layout, by
-    // the same rules: not whole 4-byte units (no kernel reads them), or not
-    // whole 16-byte units with D of 2^23 elements or more
-    g.a = (large && !rows16(A, dt->a, lda, bt.a)) || (!keep && !rows4(A, dt->a, lda, bt.a));
-    g.b = (large && !rows16(B, dt->b, ldb, bt.b)) || (!keep && !rows4(B, dt->b, ldb, bt.b));
+    // the same rules: lines no kernel reads, or not whole 16-byte units with
+    // D of 2^23 elements or more
+    g.a = (large && !rows16(A, dt->a, lda, bt.a)) || (!keep && unreadable(A, dt->a, lda, bt.a));
+    g.b = (large && !rows16(B, dt->b, ldb, bt.b)) || (!keep && unreadable(B, dt->b, ldb, bt.b));
     g.ta = dt->a;
     g.tb = dt->b;
     g.keep_a = g.a;
@@ -839,12 +845,12 @@ bool plan_stage(const thl_dtypes* dt, thl_op opA, thl_op opB, const thl_scales* 
     return true;
   }
   if (!g.a && a_km && repitchable(dt->a) &&
-      ((large && !rows16(A, dt->a, lda, bt.a)) || (!keep && !rows4(A, dt->a, lda, bt.a)))) {
+      ((large && !rows16(A, dt->a, lda, bt.a)) || (!keep && unreadable(A, dt->a, lda, bt.a)))) {
     g.a = true;
     g.ta = dt->a;
   }
   if (!g.b && b_km && repitchable(dt->b) &&
-      ((large && !rows16(B, dt->b, ldb, bt.b)) || (!keep && !rows4(B, dt->b, ldb, bt.b)))) {
+      ((large && !rows16(B, dt->b, ldb, bt.b)) || (!keep && unreadable(B, dt->b, ldb, bt.b)))) {
     g.b = true;
     g.tb = dt->b;
   }
