@@ -1431,7 +1431,7 @@ def test_random_special_paths(i):
 
 
 def _fuzz_grouped(i):
-    """Seeded random grouped launch i: 2 to 7 problems of one family and
+    """Seeded random grouped launch i: 2 to 16 problems of one family and
     epilogue with independent shapes (empty ones and K = 0 included) and
     16-byte rows, as grouped launches take them."""
     import workloads as wl
@@ -1452,7 +1452,7 @@ def _fuzz_grouped(i):
             kw["type_bias"] = pick(ftypes)
     q = {"fp16": 8, "bf16": 8, "int8": 16, "fp8": 16, "mxfp8": 16, "mxfp4": 32}[kind]
     ws = []
-    for z in range(int(g.integers(2, 8))):
+    for z in range(pick([2, 3, 5, 7, 8, 16])):
         m, n, k = int(g.integers(0, 400)), int(g.integers(0, 300)), int(g.integers(0, 600))
         if kind in ("fp8", "mxfp8", "mxfp4") and 0 < k < 256:
             k += 256  # four or more MFMA steps per output (as in test_random_problems)
@@ -1465,9 +1465,10 @@ def _fuzz_grouped(i):
     return ws
 
 
-@pytest.mark.parametrize("i", range(12))
+@pytest.mark.parametrize("i", range(16))
 def test_random_grouped(i):
-    # twelve seeded random grouped launches, every problem's D against the oracle
+    # sixteen seeded random grouped launches (8 or 16 problems among them:
+    # each problem on one XCD), every problem's D against the oracle
     _check_grouped(_fuzz_grouped(i))
 
 
