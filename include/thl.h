@@ -350,7 +350,11 @@ const char* thl_status_string(int status);
 
 /* Name of the kernel variant the calling thread's last successful thl_gemm
  * launched ("" before any); the storage is thread-local and stays valid until
- * the thread's next thl_gemm call. */
+ * the thread's next thl_gemm call.  "<variant>+cvt_a" (b, ab): the operands
+ * named went through the conversion pass first.  "<first>|<rest>": a single
+ * problem whose 256x256 tiles would fill at most half of a last round of the
+ * device's CUs ran as two launches, the rows of whole rounds on <first> and
+ * the remaining rows as a problem of their own on <rest>. */
 const char* thl_last_variant(void);
 
 /* Number of K splits (workgroups sharing each output tile) of the calling

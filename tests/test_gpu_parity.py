@@ -1607,3 +1607,36 @@ def test_mx_output_with_operand_lines_off_16_byte_units(kind, ops, lds, want):
     want_codes, want_scales = oracle.mx_quantize_columns(y, "e4m3")
     assert np.array_equal(scales, want_scales)
     assert np.array_equal(codes, want_codes)
+
+
+@pytest.mark.parametrize("kind,kw", [
+    ("bf16", {}),                                               # relu(A.B + C + bias), N/N
+    ("bf16", {"op_a": "T", "op_b": "N", "lda": 256, "ldb": 256}),
+    ("mxfp4", {}),                                              # A's block scales offset with its rows
+    ("int8", {"beta": 1.0, "bias": True, "act": "relu"}),
+    ("fp8", {"bias": True, "beta": 0.5, "type_c": "f32"}),
+])
+def test_rows_of_a_poorly_filled_last_round_run_apart(kind, kw):
+    # 4352 x 4096 makes 272 tiles of 256x256, 16 past a whole round of the
+    # 256 CUs: the first 4096 rows run on 256x256 tiles, the last 256 as a
+    # problem of their own ("<first>|<rest>"); every output of the rows on
+    # both sides of the split and a sample of the rest against the oracle
+    import tile_hierarchy_linear_amd as thl
+    import workloads as wl
+    from oracle import compare
+    from workloads.device import DeviceProblem
+
+    w = wl.make(kind, 4352, 4096, 256, **kw)
+    _say(f"[row split] {kind} {kw}")
+    dp = DeviceProblem(w)
+    assert dp.run() == 0
+    torch.cuda.synchronize()
+    v = thl.thl_last_variant()
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert "|" in v and "_256x256_" in v.split("|")[0], v
+    rows, cols = w.sample(2048)
+    b = np.repeat(np.array([4094, 4095, 4096, 4097, 4351]), w.n)
+    c = np.tile(np.arange(w.n), 5)
+    rr, cc = np.concatenate([rows, b]), np.concatenate([cols, c])
+    res = compare.parity_check(w, dp.d_values(rr, cc), rr, cc)
+    assert res["ok"], res

@@ -130,6 +130,7 @@ const Variant kVariants[] = {
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 thread_local const char* t_last_variant = "";
+thread_local char t_rows_name[256];  // a problem run as two row ranges: "<first>|<rest>"
 thread_local int last_splits = 1;
 
 // Compute units of a device, read once per device.
@@ -884,8 +885,43 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
   // (tile counts over the whole batch: its problems fill the device together)
   const int64_t tiles_256 = ((m + 255) / 256) * ((n + 255) / 256) * bt.count;
   const int64_t tiles_256x128 = ((m + 255) / 256) * ((n + 127) / 128) * bt.count;
-  const Variant* pick = choose_variant(pr, true, m,
-                                       want_tier_of(tiles_256, tiles_256x128, !pr.int_path && !pr.rows16 && pr.mx_out == MX_NONE),
+  const int want = want_tier_of(tiles_256, tiles_256x128, !pr.int_path && !pr.rows16 && pr.mx_out == MX_NONE);
+
+  // ---- a last round of 256x256 tiles that would leave most CUs idle: the
+  // rows of whole rounds run first, the remaining rows as a problem of their
+  // own (smaller tiles, the whole chip).  6144^3 makes 576 tiles, 2.25 rounds
+  // of 256 CUs: run as 504 tiles, then 768 rows on 128x128 tiles.
+  if (want == 0 && bt.count == 1 && pr.work && !pr.small_m && pr.mx_out == MX_NONE) {
+    const char* forced = std::getenv("THL_FORCE_VARIANT");
+    const int64_t ncu = cu_count();
+    const int64_t tn = (n + 255) / 256;
+    if (!(forced && *forced) && ncu > 0 && tiles_256 >= ncu && (tiles_256 % ncu) * 2 <= ncu &&
+        tiles_256 % ncu != 0) {
+      const int64_t rows = (tiles_256 / ncu) * ncu / tn * 256;  // whole tile rows within the full rounds
+      if (rows > 0 && rows < m) {
+        const int64_t off_a = opA == THL_OP_N ? bytes_of(dt->a, rows) : bytes_of(dt->a, rows * lda);
+        const uint8_t* a_rest = static_cast<const uint8_t*>(A) + off_a;
+        const uint8_t* c_rest = C ? static_cast<const uint8_t*>(C) + bytes_of(dt->c, rows) : nullptr;
+        uint8_t* d_rest = static_cast<uint8_t*>(D) + bytes_of(dt->d, rows);
+        thl_epilogue e2 = epi ? *epi : thl_epilogue{0u, nullptr, nullptr, 0};
+        if (e2.bias) e2.bias = static_cast<const uint8_t*>(e2.bias) + bytes_of(dt->bias, rows);
+        thl_scales s2 = sc ? *sc : thl_scales{1.0f, 1.0f, nullptr, 0, nullptr, 0};
+        if (s2.sfa) s2.sfa += rows * s2.ld_sfa;
+        st = gemm_impl(bt, rows, n, k, A, lda, opA, B, ldb, opB, C, ldc, D, ldd, alpha, beta, dt, epi, sc, stream,
+                       ws_mode, ws_offset);
+        if (st != THL_OK) return st;
+        char first[128];
+        std::snprintf(first, sizeof(first), "%s", t_last_variant);
+        st = gemm_impl(bt, m - rows, n, k, a_rest, lda, opA, B, ldb, opB, c_rest, ldc, d_rest, ldd, alpha, beta, dt,
+                       epi ? &e2 : nullptr, sc ? &s2 : nullptr, stream, ws_mode, ws_offset);
+        if (st != THL_OK) return st;
+        std::snprintf(t_rows_name, sizeof(t_rows_name), "%s|%s", first, t_last_variant);
+        t_last_variant = t_rows_name;
+        return THL_OK;
+      }
+    }
+  }
+  const Variant* pick = choose_variant(pr, true, m, want,
                                        [&](const Variant& v) { return fits(v, pr, bt, A, B, k); }, &st);
   if (!pick) return st;
   if (!pr.work) {
