@@ -895,6 +895,75 @@ def test_split_k_automatic(kind, shape, want):
     del dp
 
 
+# ------------------------------------------------------------ one round of 128x128 tiles
+
+ONE_ROUND_CASES = [
+    # kind, shape (ragged M/N, K with a partial last K-step), extra workload arguments, family and layout
+    ("bf16", (300, 200, 1000), {"lda": 304, "ldb": 1000}, "bf16_nn"),
+    ("bf16", (260, 130, 520), {"op_a": "T", "op_b": "T", "lda": 520, "ldb": 136, "act": "gelu"}, "bf16_tt"),
+    ("bf16", (257, 300, 776), {"op_a": "T", "op_b": "N", "lda": 776, "ldb": 776, "beta": 1.0, "bias": True},
+     "bf16_tn"),
+    ("bf16", (200, 136, 264), {"op_a": "N", "op_b": "T", "lda": 200, "ldb": 136}, "bf16_nt"),
+    ("fp16", (129, 257, 1032), {"lda": 1032, "ldb": 1032, "beta": 0.5, "type_c": "f32"}, "f16_tn"),
+    ("int8", (260, 130, 2032), {"beta": 1.0, "bias": True, "act": "relu"}, "i8_tn"),
+    ("fp8", (300, 260, 2032), {"beta": 1.0, "bias": True}, "e4m3_tn"),
+    ("fp8e5m2", (140, 300, 1040), {}, "e5m2_tn"),
+    ("fp8e4e5", (200, 200, 1024), {}, "e4m3e5m2_tn"),
+]
+
+
+@pytest.mark.parametrize("case", ONE_ROUND_CASES, ids=lambda c: c[3])
+def test_one_round_of_tiles_takes_the_six_stage_variant(case):
+    # a launch whose 128x128 tiles all run at once (one per CU) and whose K
+    # is not split takes the one-workgroup, six-stage variant; every output
+    # against the oracle
+    import tile_hierarchy_linear_amd as thl
+    import workloads as wl
+
+    kind, (m, n, k), kw, fam = case
+    _check_full(wl.make(kind, m, n, k, **kw))
+    assert thl.thl_last_variant() == f"{fam}_128x128_v16_s6_o1", thl.thl_last_variant()
+    assert thl.thl_last_splits() == 1
+
+
+@pytest.mark.parametrize("kind,shape", [("bf16", (2048, 2048, 2048)), ("bf16", (4096, 1024, 4096)),
+                                        ("fp8", (2048, 2048, 2048)), ("int8", (2048, 2048, 1024)),
+                                        ("fp16", (1920, 2048, 520))])
+def test_one_round_of_tiles_at_the_full_chip(kind, shape):
+    # 240 or 256 tiles of 128x128, one per CU of a 256-CU device: sampled
+    # outputs plus the last row and column against the oracle
+    import tile_hierarchy_linear_amd as thl
+    import workloads as wl
+
+    m, n, k = shape
+    _check_sampled(wl.make(kind, m, n, k, beta=1.0), extra_edges=True)
+    if torch.cuda.get_device_properties(0).multi_processor_count >= 256:
+        assert "_128x128_v16_s6_o1" in thl.thl_last_variant(), thl.thl_last_variant()
+
+
+def test_more_tiles_than_cus_keep_two_workgroups_per_cu():
+    # 400 tiles of 128x128: the two-workgroup variant, not two rounds of the
+    # one-workgroup one
+    import tile_hierarchy_linear_amd as thl
+    import workloads as wl
+
+    _check_sampled(wl.make("bf16", 2560, 2560, 256), extra_edges=True)
+    if torch.cuda.get_device_properties(0).multi_processor_count <= 256:
+        assert thl.thl_last_variant() == "bf16_nn_128x128_v16_s4_o2", thl.thl_last_variant()
+
+
+def test_one_round_batched_and_grouped():
+    # four problems of 15 tiles each share one round; the batched and the
+    # grouped launch both take the six-stage variant
+    import tile_hierarchy_linear_amd as thl
+    import workloads as wl
+
+    ws = [wl.make("bf16", 300, 520, 256, op_a="T", op_b="T", seed=70 + z) for z in range(4)]
+    _check_batched(ws, expect="_128x128_v16_s6_o1")
+    ws = [wl.make("bf16", 304 - 40 * z, 520 + 8 * z, 256 + 40 * z, seed=80 + z) for z in range(4)]
+    _check_grouped(ws, expect="bf16_nn_128x128_v16_s6_o1")
+
+
 def test_split_k_is_deterministic():
     # the partials are added in split order whichever split finishes last
     import tile_hierarchy_linear_amd as thl

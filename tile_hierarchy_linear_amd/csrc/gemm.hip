@@ -60,10 +60,13 @@ struct Variant {
    &launch_gemm<FAM, 128, 128, 2, 2, 16, 4, 2, 16, AK, BK, true>, true}
 
 // Must list exactly the instantiations of THL_INSTANTIATE_VARIANTS.  Order is
-// the first-fit order within a tier: 16-byte copies before 4-byte ones.
+// the first-fit order within a tier: 16-byte copies before 4-byte ones.  The
+// 128x128 variant with one workgroup per CU and six stages is taken only for
+// a launch whose tiles fit one round of the CUs (choose_variant).
 #define THL_VARIANTS(FAM, NAME, OPS, AK, BK)                  \
   THL_V(FAM, NAME, OPS, AK, BK, 256, 256, 16, 4, 1, 0),       \
       THL_V(FAM, NAME, OPS, AK, BK, 256, 128, 16, 3, 2, 1),   \
+      THL_V(FAM, NAME, OPS, AK, BK, 128, 128, 16, 6, 1, 2),   \
       THL_V(FAM, NAME, OPS, AK, BK, 128, 128, 16, 4, 2, 2),   \
       THL_V(FAM, NAME, OPS, AK, BK, 128, 128, 4, 4, 2, 2)
 
@@ -646,11 +649,19 @@ int want_tier_of(int64_t tiles_256, int64_t tiles_256x128, bool general_epilogue
 // First fit over the built variants of the problem's family, in the order
 // of the shape rule: the small-M kernel where it applies (allow_small),
 // then the preferred tier, then each smaller tile, then any tiled variant;
-// `fit` decides alignment.  THL_FORCE_VARIANT=<name> restricts the choice to
-// that variant.  Returns nullptr with *status set when none fits.
+// `fit` decides alignment.  The one-workgroup 128x128 variants only where
+// `one_round` says the launch's 128x128 tiles all run at once, one per CU:
+// then no second workgroup is there to hide a tile's load latency, and their
+// deeper ring (six stages instead of four) does instead.  Measured (bf16 N/N
+// relu(A B + C + bias), steady clock, three rounds in fresh processes):
+// 2048^3 28.2 -> 23.6 us, 1536^3 20.7 -> 19.0, 4096 x 1024 x 4096 46.8 ->
+// 40.1; e4m3 T/N 2048^3 13.1 -> 12.1; int8 equal.  With more tiles than CUs
+// the two-workgroup variants win (2560^3, 400 tiles: 39 against 53 us).
+// THL_FORCE_VARIANT=<name> restricts the choice to that variant.  Returns
+// nullptr with *status set when none fits.
 template <class Fit>
-const Variant* choose_variant(const Prep& pr, bool allow_small, int64_t rows, int want_tier, Fit&& fit,
-                              thl_status* status) {
+const Variant* choose_variant(const Prep& pr, bool allow_small, int64_t rows, int want_tier, bool one_round,
+                              Fit&& fit, thl_status* status) {
   const char* forced = std::getenv("THL_FORCE_VARIANT");
   const bool small_m = allow_small && pr.small_m;
   const Variant* pick = nullptr;
@@ -661,7 +672,8 @@ const Variant* choose_variant(const Prep& pr, bool allow_small, int64_t rows, in
       family_built = true;
       if (forced && *forced) {
         if (std::strcmp(forced, v.name) != 0 || (v.tier < 0 && (!small_m || v.bm < rows))) continue;
-      } else if ((pass < 3 && v.tier != pass) || (pass == 3 && v.tier < 0) || (v.tier < 0 && v.bm < rows)) {
+      } else if ((pass < 3 && v.tier != pass) || (pass == 3 && v.tier < 0) || (v.tier < 0 && v.bm < rows) ||
+                 (v.tier == 2 && v.occ == 1 && !one_round)) {
         continue;
       }
       // MX-format D runs on the MX-output variants, and only it does
@@ -738,10 +750,16 @@ int64_t persistent_grid(const Variant& v, int64_t problems, int64_t max_tiles) {
 // steps, the partial matrices' traffic and the second kernel cost more than
 // the split gains.  THL_FORCE_SPLITS=<s> asks for s splits on any eligible
 // variant (tests use it to cover the path at small sizes).
+int splits_for(const Prep& pr, const Batch& bt, int64_t tiles, int64_t kbytes);
+
 int choose_splits(const Prep& pr, const Variant& v, const Batch& bt, int64_t tiles, int64_t kbytes) {
-  if (bt.count != 1 || v.tier < 0 || pr.block_scaled || v.occ != 2 || v.bm * v.bn > 128 * 128 || kbytes <= 0 ||
-      pr.mx_out != MX_NONE)
-    return 1;
+  if (v.tier < 0 || v.occ != 2 || v.bm * v.bn > 128 * 128) return 1;
+  return splits_for(pr, bt, tiles, kbytes);
+}
+
+// The splits choose_splits gives a split-K variant for `tiles` tiles.
+int splits_for(const Prep& pr, const Batch& bt, int64_t tiles, int64_t kbytes) {
+  if (bt.count != 1 || pr.block_scaled || kbytes <= 0 || pr.mx_out != MX_NONE) return 1;
   const int64_t nk_all = (kbytes + 63) / 64;
   const char* forced = std::getenv("THL_FORCE_SPLITS");
   if (forced && *forced) {
@@ -749,7 +767,7 @@ int choose_splits(const Prep& pr, const Variant& v, const Batch& bt, int64_t til
     return static_cast<int>(f < 1 ? 1 : (f > nk_all ? nk_all : (f > 64 ? 64 : f)));
   }
   const int ncu = cu_count();
-  const int64_t resident = static_cast<int64_t>(ncu) * v.occ;
+  const int64_t resident = static_cast<int64_t>(ncu) * 2;
   if (ncu <= 0 || tiles * 4 > resident || nk_all < 128) return 1;
   int64_t sp = resident / tiles;
   if (sp > nk_all / 16) sp = nk_all / 16;
@@ -921,7 +939,11 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
       }
     }
   }
-  const Variant* pick = choose_variant(pr, true, m, want,
+  const int64_t tiles_128 = ((m + 127) / 128) * ((n + 127) / 128) * bt.count;
+  const int ncu = cu_count();
+  const bool one_round =
+      want == 2 && ncu > 0 && tiles_128 <= ncu && splits_for(pr, bt, tiles_128, bytes_of(dt->a, k)) == 1;
+  const Variant* pick = choose_variant(pr, true, m, want, one_round,
                                        [&](const Variant& v) { return fits(v, pr, bt, A, B, k); }, &st);
   if (!pick) return st;
   if (!pr.work) {
@@ -1232,7 +1254,7 @@ thl_status grouped_impl(int64_t count, const thl_group_problem* pb, const thl_gr
   const unsigned flags = epi ? epi->flags : 0u;
   const Batch one{};
   std::vector<Prep> preps(static_cast<size_t>(count));
-  int64_t tiles_256 = 0, tiles_256x128 = 0;
+  int64_t tiles_256 = 0, tiles_256x128 = 0, tiles_128 = 0;
   bool any_work = false, all_vec = true;
   int64_t ref = -1;  // the first problem with outputs: its family is the group's
   for (int64_t z = 0; z < count; ++z) {
@@ -1254,6 +1276,7 @@ thl_status grouped_impl(int64_t count, const thl_group_problem* pb, const thl_gr
       all_vec = all_vec && preps[z].vec;
       tiles_256 += ((q.m + 255) / 256) * ((q.n + 255) / 256);
       tiles_256x128 += ((q.m + 255) / 256) * ((q.n + 127) / 128);
+      tiles_128 += ((q.m + 127) / 128) * ((q.n + 127) / 128);
     }
   }
   if (count == 0) return THL_OK;
@@ -1307,7 +1330,9 @@ thl_status grouped_impl(int64_t count, const thl_group_problem* pb, const thl_gr
   // ---- one variant for every problem (tiled kernels only)
   thl_status st = THL_OK;
   const Prep& pref = preps[ref < 0 ? 0 : ref];
-  const Variant* pick = choose_variant(pref, false, 0, want_tier_of(tiles_256, tiles_256x128),
+  const int want = want_tier_of(tiles_256, tiles_256x128);
+  const int ncu = cu_count();
+  const Variant* pick = choose_variant(pref, false, 0, want, want == 2 && ncu > 0 && tiles_128 <= ncu,
                                        [&](const Variant& v) {
                                          for (int64_t z = 0; z < count; ++z)
                                            if (preps[z].work && !fits(v, preps[z], one, pb[z].A, pb[z].B, pb[z].k))

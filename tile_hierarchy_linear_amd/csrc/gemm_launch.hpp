@@ -48,5 +48,6 @@ hipError_t launch_gemm(const GemmArgs& a, dim3 grid, hipStream_t stream) {
 #define THL_INSTANTIATE_VARIANTS(FAM, AK, BK) \
   THL_INST(FAM, 256, 256, 16, 4, 1, AK, BK)    \
   THL_INST(FAM, 256, 128, 16, 3, 2, AK, BK)    \
+  THL_INST(FAM, 128, 128, 16, 6, 1, AK, BK)    \
   THL_INST(FAM, 128, 128, 16, 4, 2, AK, BK)    \
   THL_INST(FAM, 128, 128, 4, 4, 2, AK, BK)
