@@ -952,6 +952,21 @@ def test_more_tiles_than_cus_keep_two_workgroups_per_cu():
         assert thl.thl_last_variant() == "bf16_nn_128x128_v16_s4_o2", thl.thl_last_variant()
 
 
+@pytest.mark.parametrize("kind,shape", [("bf16", (3072, 3072, 3072)), ("fp8", (3840, 3840, 1024)),
+                                        ("mxfp4", (3072, 3072, 1024)), ("int8", (6144, 1536, 512))])
+def test_partial_round_of_256x256_tiles_beats_two_of_128x128(kind, shape):
+    # fewer 256x256 tiles than CUs, but more 128x128 tiles than two per CU:
+    # one partial round of 256x256 tiles; sampled outputs plus the last row
+    # and column against the oracle
+    import tile_hierarchy_linear_amd as thl
+    import workloads as wl
+
+    m, n, k = shape
+    _check_sampled(wl.make(kind, m, n, k, beta=1.0), extra_edges=True)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert "_256x256_" in thl.thl_last_variant(), thl.thl_last_variant()
+
+
 def test_one_round_batched_and_grouped():
     # four problems of 15 tiles each share one round; the batched and the
     # grouped launch both take the six-stage variant

@@ -634,15 +634,24 @@ bool fits(const Variant& v, const Prep& pr, const Batch& bt, const void* A, cons
   return ok;
 }
 
-// The tile tier the shape rule prefers for this many tiles of each size.
+// The tile tier the shape rule prefers for this many tiles of each size:
+// 256x256 from a whole round of them (one per CU); below that 128x128 while
+// its tiles fit one round at two workgroups per CU, else 256x256 again, whose
+// one partial round beats two of 128x128.  Measured on one box (bf16 N/N
+// relu(A B + C + bias); e4m3 T/N): 3072^3, 144 tiles of 256x256 and 576 of
+// 128x128: 62.7 us on 256x256 against 77.8 on 128x128 and 81.5 on 256x128;
+// e4m3 36.4, 43.8 and 49.9 us.  3584^3: 81.0, 94.1 and 99.7 us; e4m3 43.4,
+// 51.4 and 59.4 us.
 // A float problem whose D, C or bias column runs are not 16-byte units (an
 // odd leading dimension, say) takes the general epilogue with element-wise
 // accesses on every tile, and with one workgroup per CU nothing hides it: it
 // then starts at the two-workgroup tiers.  Measured at 4097^2 x 4096 (bf16 D, ldd = 4097): e4m3 192 us on
 // 256x256 against 124 us on 256x128 and 137 us on 128x128; bf16 390, 270
 // and 293 us.
-int want_tier_of(int64_t tiles_256, int64_t tiles_256x128, bool general_epilogue = false) {
-  const int t = tiles_256 >= 256 ? 0 : (tiles_256x128 >= 256 ? 1 : 2);
+int want_tier_of(int64_t tiles_256, int64_t tiles_128, bool general_epilogue = false) {
+  int64_t ncu = cu_count();
+  if (ncu <= 0) ncu = 256;
+  const int t = tiles_256 >= ncu ? 0 : (tiles_128 <= 2 * ncu ? 2 : 0);
   return general_epilogue && t == 0 ? 1 : t;
 }
 
@@ -902,8 +911,8 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
   // ---- variant: first fit on family, alignment and shape
   // (tile counts over the whole batch: its problems fill the device together)
   const int64_t tiles_256 = ((m + 255) / 256) * ((n + 255) / 256) * bt.count;
-  const int64_t tiles_256x128 = ((m + 255) / 256) * ((n + 127) / 128) * bt.count;
-  const int want = want_tier_of(tiles_256, tiles_256x128, !pr.int_path && !pr.rows16 && pr.mx_out == MX_NONE);
+  const int64_t tiles_128 = ((m + 127) / 128) * ((n + 127) / 128) * bt.count;
+  const int want = want_tier_of(tiles_256, tiles_128, !pr.int_path && !pr.rows16 && pr.mx_out == MX_NONE);
 
   // ---- a last round of 256x256 tiles that would leave most CUs idle: the
   // rows of whole rounds run first, the remaining rows as a problem of their
@@ -939,7 +948,6 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
       }
     }
   }
-  const int64_t tiles_128 = ((m + 127) / 128) * ((n + 127) / 128) * bt.count;
   const int ncu = cu_count();
   const bool one_round =
       want == 2 && ncu > 0 && tiles_128 <= ncu && splits_for(pr, bt, tiles_128, bytes_of(dt->a, k)) == 1;
@@ -1254,7 +1262,7 @@ thl_status grouped_impl(int64_t count, const thl_group_problem* pb, const thl_gr
   const unsigned flags = epi ? epi->flags : 0u;
   const Batch one{};
   std::vector<Prep> preps(static_cast<size_t>(count));
-  int64_t tiles_256 = 0, tiles_256x128 = 0, tiles_128 = 0;
+  int64_t tiles_256 = 0, tiles_128 = 0;
   bool any_work = false, all_vec = true;
   int64_t ref = -1;  // the first problem with outputs: its family is the group's
   for (int64_t z = 0; z < count; ++z) {
@@ -1275,7 +1283,6 @@ thl_status grouped_impl(int64_t count, const thl_group_problem* pb, const thl_gr
       any_work = true;
       all_vec = all_vec && preps[z].vec;
       tiles_256 += ((q.m + 255) / 256) * ((q.n + 255) / 256);
-      tiles_256x128 += ((q.m + 255) / 256) * ((q.n + 127) / 128);
       tiles_128 += ((q.m + 127) / 128) * ((q.n + 127) / 128);
     }
   }
@@ -1330,7 +1337,7 @@ thl_status grouped_impl(int64_t count, const thl_group_problem* pb, const thl_gr
   // ---- one variant for every problem (tiled kernels only)
   thl_status st = THL_OK;
   const Prep& pref = preps[ref < 0 ? 0 : ref];
-  const int want = want_tier_of(tiles_256, tiles_256x128);
+  const int want = want_tier_of(tiles_256, tiles_128);
   const int ncu = cu_count();
   const Variant* pick = choose_variant(pref, false, 0, want, want == 2 && ncu > 0 && tiles_128 <= ncu,
                                        [&](const Variant& v) {
