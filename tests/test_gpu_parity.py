@@ -881,10 +881,11 @@ def test_split_k_forced(case, splits):
 
 @pytest.mark.parametrize("kind,shape,want", [("bf16", (1024, 1024, 8192), 8), ("fp8", (1024, 1024, 8192), 8),
                                              ("int8", (1024, 512, 8192), 8), ("fp16", (640, 384, 8192), 16),
-                                             ("bf16", (2048, 2048, 8192), 1), ("int8", (1024, 512, 4096), 1)])
+                                             ("bf16", (2048, 2048, 8192), 1), ("int8", (1024, 512, 4096), 1),
+                                             ("bf16", (128, 8192, 8192), 8), ("fp8", (256, 8192, 8192), 1)])
 def test_split_k_automatic(kind, shape, want):
-    # few tiles and a long K: thl_gemm splits K on its own (not at 256 tiles,
-    # nor with K of 64 steps)
+    # few tiles and a long K: thl_gemm splits K on its own (not from 128
+    # tiles, which run unsplit in one round, nor with K of 64 steps)
     import tile_hierarchy_linear_amd as thl
     import workloads as wl
 

@@ -751,13 +751,16 @@ int64_t persistent_grid(const Variant& v, int64_t problems, int64_t max_tiles) {
 
 // Splits for one problem on variant v: only the variants built with split K
 // (128x128, two workgroups per CU, unscaled families) and a single problem.
-// Splitting pays when the tiles fill at most a quarter of the resident
+// Splitting pays when the tiles fill at most an eighth of the resident
 // workgroups and K is long (at least 128 K-steps): then as many splits as
 // fill them, at most 16, with at least 16 K-steps each.  Measured on bf16
 // and fp8 with K = 8192: 64 tiles went from 79 to 41 us (bf16) and 44 to
 // 32 us (fp8), 15 tiles from 81 to 30 us (fp16); at 256 tiles, or K of 64
 // steps, the partial matrices' traffic and the second kernel cost more than
-// the split gains.  THL_FORCE_SPLITS=<s> asks for s splits on any eligible
+// the split gains.  At 128 tiles (256 x 8192 x 8192) the unsplit six-stage
+// variant is faster than 4 splits: bf16 58.2 against 64.3 us, e4m3 34.0
+// against 42.6; at 64 tiles 8 splits still beat it for bf16 (42.6 against
+// 55.9 us) and tie for e4m3 (32.4 against 33.1).  THL_FORCE_SPLITS=<s> asks for s splits on any eligible
 // variant (tests use it to cover the path at small sizes).
 int splits_for(const Prep& pr, const Batch& bt, int64_t tiles, int64_t kbytes);
 
@@ -777,7 +780,7 @@ int splits_for(const Prep& pr, const Batch& bt, int64_t tiles, int64_t kbytes) {
   }
   const int ncu = cu_count();
   const int64_t resident = static_cast<int64_t>(ncu) * 2;
-  if (ncu <= 0 || tiles * 4 > resident || nk_all < 128) return 1;
+  if (ncu <= 0 || tiles * 8 > resident || nk_all < 128) return 1;
   int64_t sp = resident / tiles;
   if (sp > nk_all / 16) sp = nk_all / 16;
   if (sp > 16) sp = 16;
