@@ -1399,6 +1399,65 @@ def test_random_problems(i):
     _check_full(_fuzz_case(i))
 
 
+def _fuzz_mid(i):
+    """Seeded random mid-size problem i (M and N from 1200 to 4700, so that
+    the tile counts fall on either side of one round of the CUs): a family,
+    a layout for the 16-bit ones, K from 256 to 1024, an epilogue, and D's
+    leading dimension in whole 16-byte units or (one case in four) one
+    element past them.  Returns (workload, whether D's runs are 16-byte
+    units)."""
+    import workloads as wl
+
+    g = np.random.default_rng(11000 + i)
+    pick = lambda xs: xs[int(g.integers(len(xs)))]  # noqa: E731
+    kind = pick(["fp16", "bf16", "bf16", "int8", "fp8", "fp8e5m2", "mxfp8", "mxfp4"])
+    m, n = int(g.integers(1200, 4700)), int(g.integers(1200, 4700))
+    k = int(g.integers(256, 1025))
+    ops = pick([("T", "N"), ("N", "N"), ("T", "T"), ("N", "T")]) if kind in ("fp16", "bf16") else ("T", "N")
+    if kind in ("mxfp8", "mxfp4"):
+        k -= k % 32
+    q = 8 if kind in ("fp16", "bf16") else 16  # whole 16-byte operand rows
+    up = lambda x: -(-x // q) * q  # noqa: E731
+    a_rows = k if ops[0] == "T" else m
+    b_rows = k if ops[1] == "N" else n
+    aligned = bool(g.integers(4))
+    ldd = -(-m // 16) * 16 if aligned else m + 1
+    kw = dict(op_a=ops[0], op_b=ops[1], lda=up(a_rows), ldb=up(b_rows), ldd=ldd, bias=bool(g.integers(2)))
+    if kind == "int8":
+        kw.update(act=pick(["none", "relu"]), beta=pick([0.0, 1.0]))
+    else:
+        kw.update(act=pick(["none", "relu", "gelu"]), beta=pick([0.0, 1.0, -0.5]),
+                  type_d=pick(["f32", "f16", "bf16"]))
+        if kw["bias"]:
+            kw["type_bias"] = pick(["f32", "f16", "bf16"])
+    if kw["beta"] != 0.0:
+        kw["ldc"] = ldd
+        if kind != "int8":
+            kw["type_c"] = pick(["f16", "bf16"])
+    return wl.make(kind, m, n, k, seed=11000 + i, **kw), aligned
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_mid_size_problems(i):
+    # twenty-four seeded random mid-size problems: sampled outputs plus the
+    # last row and column against the oracle, and (16-byte D runs, a 256-CU
+    # device) the tile the shape rule names: 256x256 from a whole round of
+    # them, else 128x128 while those fit one round at two per CU, else
+    # 256x256 (with a poorly filled last round, the first of two row ranges)
+    import tile_hierarchy_linear_amd as thl
+
+    w, aligned = _fuzz_mid(i)
+    dp = _check_sampled(w, extra_edges=True)
+    v = thl.thl_last_variant()
+    _say(f"   ran {v} splits={thl.thl_last_splits()}")
+    t256 = -(-w.m // 256) * -(-w.n // 256)
+    t128 = -(-w.m // 128) * -(-w.n // 128)
+    if aligned and torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        want = "_256x256_" if t256 >= 256 or t128 > 512 else "_128x128_"
+        assert want in v.split("|")[0], (v, t256, t128)
+    del dp
+
+
 def test_fp8_matrix_core_error_at_small_k():
     # gfx950's fp8 MFMA does not sum in exact fp32: its error is about 2^-13 of
     # the largest product in one instruction.  The parity bar's operand term,
