@@ -157,6 +157,22 @@ def test_small_m_kernel(kind, fam, q, m, n, k):
     assert thl.thl_last_variant() == f"{fam}_tn_skinny{rows}_k4"
 
 
+@pytest.mark.parametrize("kind,m,n,k,tiled", [("bf16", 64, 8192, 8192, True), ("fp16", 24, 8192, 8192, True),
+                                              ("fp8", 64, 8192, 8192, True), ("int8", 48, 8192, 8192, True),
+                                              ("fp8", 33, 8192, 8192, False), ("bf16", 64, 4096, 4096, False)])
+def test_small_m_against_split_tiles(kind, m, n, k, tiled):
+    # M <= 64 with K-major operands: from M x N x K bytes of 3 GiB, where K
+    # splits over 128x128 tiles, the split tiles run instead of the small-M
+    # kernel; sampled outputs plus the last row and column against the oracle
+    import tile_hierarchy_linear_amd as thl
+    import workloads as wl
+
+    _check_sampled(wl.make(kind, m, n, k, op_a="T", op_b="N"), extra_edges=True)
+    v = thl.thl_last_variant()
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert ("skinny" not in v and thl.thl_last_splits() > 1) if tiled else "skinny" in v, (v, thl.thl_last_splits())
+
+
 @pytest.mark.parametrize("m", [3, 300])
 def test_mxfp4_nan_codes_in_scale_row_padding_are_never_used(m):
     # E8M0 0xFF is NaN: scale bytes past K/32 (row padding) must not reach an

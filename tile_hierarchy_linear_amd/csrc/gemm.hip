@@ -952,9 +952,20 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
     }
   }
   const int ncu = cu_count();
-  const bool one_round =
-      want == 2 && ncu > 0 && tiles_128 <= ncu && splits_for(pr, bt, tiles_128, bytes_of(dt->a, k)) == 1;
-  const Variant* pick = choose_variant(pr, true, m, want, one_round,
+  const int64_t kbytes = bytes_of(dt->a, k);
+  const int splits_128 = splits_for(pr, bt, tiles_128, kbytes);
+  const bool one_round = want == 2 && ncu > 0 && tiles_128 <= ncu && splits_128 == 1;
+  // The small-M kernel re-reads all of A from L2 in every 16-column
+  // workgroup, a cost that grows with M x N x K; split K over 128x128 tiles
+  // costs about the same at any M up to 128.  From M x N x K bytes of 3 GiB,
+  // where K splits, the tiles win.  Measured at N = K = 8192 (small-M kernel
+  // against 128x128 tiles with 8 splits): bf16 M = 24 42.5 against 36.0 us,
+  // M = 32 48.1 against 36.7, M = 64 80.1 against 43.7; e4m3 M = 48 34.3
+  // against 32.5, M = 64 39.9 against 33.4; int8 M = 64 39.3 against 26.6.
+  // Below it the small-M kernel wins: e4m3 M = 33 28.9 against 32.4, and at
+  // N = K = 4096 every M up to 64 (bf16 M = 64 26.2 against 29.6 us).
+  const bool small_m_kernel = !(pr.small_m && splits_128 > 1 && m * n * kbytes >= (INT64_C(3) << 30));
+  const Variant* pick = choose_variant(pr, small_m_kernel, m, want, one_round,
                                        [&](const Variant& v) { return fits(v, pr, bt, A, B, k); }, &st);
   if (!pick) return st;
   if (!pr.work) {
