@@ -1272,7 +1272,7 @@ def test_rows_of_odd_bytes_through_the_pass():
 def test_odd_leading_dimension_of_d_starts_at_the_two_workgroup_tiers():
     # 4096^2 bf16 N/N (relu(A.B + C + bias)) makes 256 tiles of 256x256; with
     # ldd = ldc = 4097 every column run of C and D is off a 16-byte unit, and
-    # the 256x128 two-workgroup tier runs instead
+    # as C is read the 256x128 two-workgroup tier runs instead
     import tile_hierarchy_linear_amd as thl
     import workloads as wl
 
@@ -1282,6 +1282,10 @@ def test_odd_leading_dimension_of_d_starts_at_the_two_workgroup_tiers():
     w = wl.make("bf16", 4096, 4096, 64, ldd=4097, ldc=4097)
     _check_sampled(w, extra_edges=True)
     assert "_256x128_" in thl.thl_last_variant(), thl.thl_last_variant()
+    # without C the general epilogue has no loads to wait for: 256x256 tiles
+    w = wl.make("fp8", 4096, 4096, 64, ldd=4097)
+    _check_sampled(w, extra_edges=True)
+    assert "_256x256_" in thl.thl_last_variant(), thl.thl_last_variant()
 
 
 def test_conversion_pass_with_k_zero_is_the_epilogue():

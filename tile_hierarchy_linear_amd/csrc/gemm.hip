@@ -642,12 +642,14 @@ bool fits(const Variant& v, const Prep& pr, const Batch& bt, const void* A, cons
 // 128x128: 62.7 us on 256x256 against 77.8 on 128x128 and 81.5 on 256x128;
 // e4m3 36.4, 43.8 and 49.9 us.  3584^3: 81.0, 94.1 and 99.7 us; e4m3 43.4,
 // 51.4 and 59.4 us.
-// A float problem whose D, C or bias column runs are not 16-byte units (an
-// odd leading dimension, say) takes the general epilogue with element-wise
-// accesses on every tile, and with one workgroup per CU nothing hides it: it
-// then starts at the two-workgroup tiers.  Measured at 4097^2 x 4096 (bf16 D, ldd = 4097): e4m3 192 us on
-// 256x256 against 124 us on 256x128 and 137 us on 128x128; bf16 390, 270
-// and 293 us.
+// A float problem that reads C and whose D, C or bias column runs are not
+// 16-byte units (an odd leading dimension, say) takes the general epilogue
+// on every tile, whose C loads wait block by block; with one workgroup per
+// CU nothing hides them, so it starts at the two-workgroup tiers.  Measured
+// with ldd = ldc = 4097 (8193): bf16 4096^3 relu(A B + C + bias) 132.7 us on
+// 256x256 against 148.5 us on 256x128; 8192^3 942 against 965 us; MXFP4 A B
+// + C 8192^3 400.6 us on 128x128 against 500.7 on 256x256.  Without C the
+// 256x256 tiles stay ahead: e4m3 4096^3 with ldd = 4097 74.0 against 79.5 us.
 int want_tier_of(int64_t tiles_256, int64_t tiles_128, bool general_epilogue = false) {
   int64_t ncu = cu_count();
   if (ncu <= 0) ncu = 256;
@@ -915,7 +917,8 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
   // (tile counts over the whole batch: its problems fill the device together)
   const int64_t tiles_256 = ((m + 255) / 256) * ((n + 255) / 256) * bt.count;
   const int64_t tiles_128 = ((m + 127) / 128) * ((n + 127) / 128) * bt.count;
-  const int want = want_tier_of(tiles_256, tiles_128, !pr.int_path && !pr.rows16 && pr.mx_out == MX_NONE);
+  const int want =
+      want_tier_of(tiles_256, tiles_128, !pr.int_path && !pr.rows16 && pr.mx_out == MX_NONE && beta != 0.0f);
 
   // ---- a last round of 256x256 tiles that would leave most CUs idle: the
   // rows of whole rounds run first, the remaining rows as a problem of their

@@ -39,6 +39,12 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+// 16-byte vectors at element alignment: one access for a run of 8 elements
+// whatever its offset (the HSA runtime runs the memory system in unaligned
+// mode, where a vector access need only be aligned to its element size)
+typedef int v4i_a2 __attribute__((ext_vector_type(4), aligned(2)));
+typedef int v4i_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef float v4f_a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
@@ -205,12 +211,12 @@ __device__ __forceinline__ float activate(float t, int flags) {
 }
 
 // Rows m .. m+rows-1 (rows <= 8) of one column of a float-family matrix, as
-// floats; one or two 16-byte loads when all 8 are wanted and aligned.
+// floats; one or two 16-byte loads when all 8 are wanted.
 __device__ __forceinline__ void load8_f(const void* base, int type, int64_t off, int rows, float (&v)[8]) {
   if (type == DT_F32) {
     const float* q = static_cast<const float*>(base) + off;
-    if (rows == 8 && (reinterpret_cast<uintptr_t>(q) & 15) == 0) {
-      const v4f a = *reinterpret_cast<const v4f*>(q), b = *reinterpret_cast<const v4f*>(q + 4);
+    if (rows == 8) {
+      const v4f_a4 a = *reinterpret_cast<const v4f_a4*>(q), b = *reinterpret_cast<const v4f_a4*>(q + 4);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         v[r] = a[r];
@@ -220,8 +226,8 @@ __device__ __forceinline__ void load8_f(const void* base, int type, int64_t off,
     }
   } else {
     const uint16_t* q = static_cast<const uint16_t*>(base) + off;
-    if (rows == 8 && (reinterpret_cast<uintptr_t>(q) & 15) == 0) {
-      const v4i w = *reinterpret_cast<const v4i*>(q);
+    if (rows == 8) {
+      const v4i_a2 w = *reinterpret_cast<const v4i_a2*>(q);
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         const uint16_t h = static_cast<uint16_t>(static_cast<unsigned>(w[r / 2]) >> (16 * (r & 1)));
@@ -236,13 +242,13 @@ __device__ __forceinline__ void load8_f(const void* base, int type, int64_t off,
 }
 
 // Store rows m .. m+rows-1 (rows <= 8) of one column, rounding to nearest
-// even; one or two 16-byte stores when all 8 go out and are aligned.
+// even; one or two 16-byte stores when all 8 go out.
 __device__ __forceinline__ void store8_f(void* base, int type, int64_t off, const float (&v)[8], int rows) {
   if (type == DT_F32) {
     float* q = static_cast<float*>(base) + off;
-    if (rows == 8 && (reinterpret_cast<uintptr_t>(q) & 15) == 0) {
-      *reinterpret_cast<v4f*>(q) = v4f{v[0], v[1], v[2], v[3]};
-      *reinterpret_cast<v4f*>(q + 4) = v4f{v[4], v[5], v[6], v[7]};
+    if (rows == 8) {
+      *reinterpret_cast<v4f_a4*>(q) = v4f_a4{v[0], v[1], v[2], v[3]};
+      *reinterpret_cast<v4f_a4*>(q + 4) = v4f_a4{v[4], v[5], v[6], v[7]};
       return;
     }
 #pragma unroll
@@ -255,8 +261,8 @@ __device__ __forceinline__ void store8_f(void* base, int type, int64_t off, cons
       h[r] = type == DT_BF16 ? __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[r]))
                              : __builtin_bit_cast(uint16_t, static_cast<_Float16>(v[r]));
     uint16_t* q = static_cast<uint16_t*>(base) + off;
-    if (rows == 8 && (reinterpret_cast<uintptr_t>(q) & 15) == 0) {
-      *reinterpret_cast<v4i*>(q) = __builtin_bit_cast(v4i, h);
+    if (rows == 8) {
+      *reinterpret_cast<v4i_a2*>(q) = __builtin_bit_cast(v4i, h);
       return;
     }
 #pragma unroll
@@ -267,8 +273,8 @@ __device__ __forceinline__ void store8_f(void* base, int type, int64_t off, cons
 
 __device__ __forceinline__ void load8_i(const void* base, int64_t off, int rows, int (&v)[8]) {
   const int* q = static_cast<const int*>(base) + off;
-  if (rows == 8 && (reinterpret_cast<uintptr_t>(q) & 15) == 0) {
-    const v4i a = *reinterpret_cast<const v4i*>(q), b = *reinterpret_cast<const v4i*>(q + 4);
+  if (rows == 8) {
+    const v4i_a4 a = *reinterpret_cast<const v4i_a4*>(q), b = *reinterpret_cast<const v4i_a4*>(q + 4);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       v[r] = a[r];
@@ -282,9 +288,9 @@ __device__ __forceinline__ void load8_i(const void* base, int64_t off, int rows,
 
 __device__ __forceinline__ void store8_i(void* base, int64_t off, const int (&v)[8], int rows) {
   int* q = static_cast<int*>(base) + off;
-  if (rows == 8 && (reinterpret_cast<uintptr_t>(q) & 15) == 0) {
-    *reinterpret_cast<v4i*>(q) = v4i{v[0], v[1], v[2], v[3]};
-    *reinterpret_cast<v4i*>(q + 4) = v4i{v[4], v[5], v[6], v[7]};
+  if (rows == 8) {
+    *reinterpret_cast<v4i_a4*>(q) = v4i_a4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<v4i_a4*>(q + 4) = v4i_a4{v[4], v[5], v[6], v[7]};
     return;
   }
 #pragma unroll
