@@ -211,9 +211,10 @@ def test_epilogue_variants(kind, act):
     _check_full(w)
 
 
-# Interior tiles with 16-byte aligned rows of C, D and bias take the batched
-# vector epilogue; edge tiles of the same call take the general one.  Each case
-# mixes both, over the C / D / bias types and the activations.
+# Interior tiles take the batched vector epilogue (16-bit or no C, no GELU),
+# with C and D columns in 16-byte units or (odd ld) off them; edge tiles of
+# the same call take the general one.  Each case mixes both, over the C / D /
+# bias types and the activations.
 VEC_CASES = [
     # kind, type_c, type_d, type_bias, act, beta, variant
     ("fp16", "f16", "f16", "f16", "gelu", 0.5, None),
@@ -227,13 +228,14 @@ VEC_CASES = [
 ]
 
 
+@pytest.mark.parametrize("odd_ld", [False, True])
 @pytest.mark.parametrize("case", VEC_CASES, ids=lambda c: "-".join(str(x) for x in c[:6]))
-def test_vector_epilogue_types(case):
+def test_vector_epilogue_types(case, odd_ld):
     import workloads as wl
 
     kind, tc, td, tb, act, beta, variant = case
     m, n, k = 392, 328, 256
-    ld = _pad(m, 16)
+    ld = m + 1 if odd_ld else _pad(m, 16)
     kw = dict(ldc=ld, ldd=ld, type_d=td, type_c=tc, type_bias=tb, act=act, beta=beta, bias=tb is not None)
     if kind in ("fp8", "mxfp4"):
         kw.update(lda=_pad(k, 32), ldb=_pad(k, 32))
@@ -516,24 +518,35 @@ def test_headline_kernel_is_deterministic_at_8192():
 
 
 def test_vector_epilogue_matches_general_path_at_8192():
-    """The same bf16 problem with 16-byte aligned C and D columns (vector
-    epilogue) and with ld = 8197 (general epilogue): every element of the two
-    D's agrees to within one bf16 ulp."""
+    """The same bf16 problem through the vector epilogue (16-bit C) and the
+    general one (the same C values in fp32, which only the general path
+    reads), with C and D columns in 16-byte units (ld = 8192) and off them
+    (ld = 8197, element-aligned vector accesses): every element agrees with
+    the first run to within one bf16 ulp, and the two vector runs bit for
+    bit."""
+    import dataclasses
+
+    import tile_hierarchy_linear_amd as thl
     import workloads as wl
     from workloads.device import DeviceProblem
 
-    outs = []
+    outs = {}
     for ld in (8192, 8197):
         w = wl.make("bf16", 8192, 8192, 512, ldc=ld, ldd=ld)
-        _say(f"[vector vs general] m={w.m} n={w.n} k={w.k} ldc=ldd={ld}")
-        dp = DeviceProblem(w)
-        assert dp.run() == 0
-        torch.cuda.synchronize()
-        outs.append(dp.d[:, : w.m].float().cpu())
-        del dp
-    a, b = outs
-    bad = (a - b).abs() > 2.0 ** -7 * torch.maximum(a.abs(), b.abs()) + 1e-6
-    assert int(bad.sum()) == 0, f"{int(bad.sum())} elements differ by more than one bf16 ulp"
+        w32 = dataclasses.replace(w, c=w.c.astype(np.uint32) << 16, type_c="f32")  # exact widening
+        for name, x in (("vector", w), ("general", w32)):
+            _say(f"[vector vs general] {name} m={x.m} n={x.n} k={x.k} ldc=ldd={ld}")
+            dp = DeviceProblem(x)
+            assert dp.run() == 0
+            torch.cuda.synchronize()
+            _say(f"   ran {thl.thl_last_variant()}")
+            outs[(name, ld)] = dp.d[:, : x.m].float().cpu()
+            del dp
+    a = outs[("vector", 8192)]
+    assert torch.equal(a, outs[("vector", 8197)]), "the vector path differs between aligned and odd ld"
+    for key, b in outs.items():
+        bad = (a - b).abs() > 2.0 ** -7 * torch.maximum(a.abs(), b.abs()) + 1e-6
+        assert int(bad.sum()) == 0, f"{key}: {int(bad.sum())} elements differ by more than one bf16 ulp"
 
 
 def _check_batched(ws, shared=(), expect=None):
@@ -1270,9 +1283,11 @@ def test_rows_of_odd_bytes_through_the_pass():
 
 
 def test_odd_leading_dimension_of_d_starts_at_the_two_workgroup_tiers():
-    # 4096^2 bf16 N/N (relu(A.B + C + bias)) makes 256 tiles of 256x256; with
-    # ldd = ldc = 4097 every column run of C and D is off a 16-byte unit, and
-    # as C is read the 256x128 two-workgroup tier runs instead
+    # 4096^2 bf16 N/N (relu(A.B + C + bias)) makes 256 tiles of 256x256.  With
+    # ldd = ldc = 4097 every column run of C and D is off a 16-byte unit: a
+    # 16-bit C still goes through the vector epilogue (element-aligned
+    # accesses) on 256x256 tiles; an fp32 C takes the general one, and then
+    # the 256x128 two-workgroup tier runs
     import tile_hierarchy_linear_amd as thl
     import workloads as wl
 
@@ -1281,8 +1296,11 @@ def test_odd_leading_dimension_of_d_starts_at_the_two_workgroup_tiers():
     assert "_256x256_" in thl.thl_last_variant(), thl.thl_last_variant()
     w = wl.make("bf16", 4096, 4096, 64, ldd=4097, ldc=4097)
     _check_sampled(w, extra_edges=True)
+    assert "_256x256_" in thl.thl_last_variant(), thl.thl_last_variant()
+    w = wl.make("bf16", 4096, 4096, 64, ldd=4097, ldc=4097, type_c="f32")
+    _check_sampled(w, extra_edges=True)
     assert "_256x128_" in thl.thl_last_variant(), thl.thl_last_variant()
-    # without C the general epilogue has no loads to wait for: 256x256 tiles
+    # without C: 256x256 tiles
     w = wl.make("fp8", 4096, 4096, 64, ldd=4097)
     _check_sampled(w, extra_edges=True)
     assert "_256x256_" in thl.thl_last_variant(), thl.thl_last_variant()

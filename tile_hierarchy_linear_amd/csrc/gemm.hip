@@ -602,22 +602,34 @@ thl_status prepare(const Batch& bt, int64_t m, int64_t n, int64_t k, const void*
   o.sa_bytes = bt.count > 1 ? bytes_of(dt->a, bt.a) : 0;
   o.sb_bytes = bt.count > 1 ? bytes_of(dt->b, bt.b) : 0;
   o.s = s;
-  // Vector epilogue: D (and C, bias) rows aligned for 16-byte runs along M,
-  // C 16-bit, and a 256-column panel within 32-bit offsets.
+  // Vector epilogue: D, C and bias at their elements' alignment (a run of 8
+  // elements moves as 16-byte accesses at any element offset, the memory
+  // system being in unaligned mode), C 16-bit, and a 256-column panel within
+  // 32-bit offsets.  rows16: every column run also a whole 16-byte unit.
   o.vec = false;
   if (!int_path && mx_out == MX_NONE) {
-    auto vec_ok = [](const void* ptr, int64_t ld_bytes) {
+    auto unit16 = [](const void* ptr, int64_t ld_bytes) {
       return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0 && ld_bytes % 16 == 0 && ld_bytes <= (INT64_C(1) << 23);
     };
-    bool vec = vec_ok(D, bytes_of(dt->d, ldd));
-    if (beta != 0.0f) vec = vec && vec_ok(C, bytes_of(dt->c, ldc));
-    if (has_bias) vec = vec && (reinterpret_cast<uintptr_t>(bias) & 15) == 0;
-    o.rows16 = vec;  // every column run of D, C and bias a whole 16-byte unit
-    if (beta != 0.0f) vec = vec && (dt->c == THL_F16 || dt->c == THL_BF16);
+    auto elem_ok = [](const void* ptr, int64_t ld_bytes, int64_t e) {
+      return reinterpret_cast<uintptr_t>(ptr) % e == 0 && ld_bytes % e == 0 && ld_bytes <= (INT64_C(1) << 23);
+    };
+    const int64_t ed = bytes_of(dt->d, 1), ec = beta != 0.0f ? bytes_of(dt->c, 1) : 1;
+    const int64_t eb = has_bias ? bytes_of(dt->bias, 1) : 1;
+    bool r16 = unit16(D, bytes_of(dt->d, ldd)), vec = elem_ok(D, bytes_of(dt->d, ldd), ed);
+    if (beta != 0.0f) {
+      r16 = r16 && unit16(C, bytes_of(dt->c, ldc));
+      vec = vec && elem_ok(C, bytes_of(dt->c, ldc), ec) && (dt->c == THL_F16 || dt->c == THL_BF16);
+    }
+    if (has_bias) {
+      r16 = r16 && (reinterpret_cast<uintptr_t>(bias) & 15) == 0;
+      vec = vec && reinterpret_cast<uintptr_t>(bias) % eb == 0;
+    }
+    o.rows16 = r16;
     if (bt.count > 1) {
       const int64_t bs_c = beta != 0.0f ? bytes_of(dt->c, bt.c) : 0, bs_d = bytes_of(dt->d, bt.d);
       const int64_t bs_bias = has_bias ? bytes_of(dt->bias, bt.bias) : 0;
-      if ((bs_c % 16) || (bs_d % 16) || (bs_bias % 16)) vec = false;
+      if ((bs_c % ec) || (bs_d % ed) || (bs_bias % eb)) vec = false;
     }
     o.vec = vec;
   }
@@ -642,14 +654,13 @@ bool fits(const Variant& v, const Prep& pr, const Batch& bt, const void* A, cons
 // 128x128: 62.7 us on 256x256 against 77.8 on 128x128 and 81.5 on 256x128;
 // e4m3 36.4, 43.8 and 49.9 us.  3584^3: 81.0, 94.1 and 99.7 us; e4m3 43.4,
 // 51.4 and 59.4 us.
-// A float problem that reads C and whose D, C or bias column runs are not
-// 16-byte units (an odd leading dimension, say) takes the general epilogue
-// on every tile, whose C loads wait block by block; with one workgroup per
-// CU nothing hides them, so it starts at the two-workgroup tiers.  Measured
-// with ldd = ldc = 4097 (8193): bf16 4096^3 relu(A B + C + bias) 132.7 us on
-// 256x256 against 148.5 us on 256x128; 8192^3 942 against 965 us; MXFP4 A B
-// + C 8192^3 400.6 us on 128x128 against 500.7 on 256x256.  Without C the
-// 256x256 tiles stay ahead: e4m3 4096^3 with ldd = 4097 74.0 against 79.5 us.
+// A float problem that reads C through the general epilogue (an fp32 C,
+// which the vector epilogue does not read) with D, C or bias column runs off
+// 16-byte units (an odd leading dimension, say) takes it on every tile, its
+// C loads waiting block by block; with one workgroup per CU nothing hides
+// them, so it starts at the two-workgroup tiers.  Measured with ldd = ldc =
+// 4097, bf16 4096^3 relu(A B + C + bias) with fp32 C: 134.2 us on 256x128
+// against 144.2 on 256x256.
 int want_tier_of(int64_t tiles_256, int64_t tiles_128, bool general_epilogue = false) {
   int64_t ncu = cu_count();
   if (ncu <= 0) ncu = 256;
@@ -918,7 +929,7 @@ thl_status gemm_impl(const Batch& bt, int64_t m, int64_t n, int64_t k, const voi
   const int64_t tiles_256 = ((m + 255) / 256) * ((n + 255) / 256) * bt.count;
   const int64_t tiles_128 = ((m + 127) / 128) * ((n + 127) / 128) * bt.count;
   const int want =
-      want_tier_of(tiles_256, tiles_128, !pr.int_path && !pr.rows16 && pr.mx_out == MX_NONE && beta != 0.0f);
+      want_tier_of(tiles_256, tiles_128, !pr.int_path && !pr.vec && !pr.rows16 && pr.mx_out == MX_NONE && beta != 0.0f);
 
   // ---- a last round of 256x256 tiles that would leave most CUs idle: the
   // rows of whole rounds run first, the remaining rows as a problem of their
