@@ -824,8 +824,9 @@ bool is_narrow_float(thl_dtype t) { return is_fp8(t) || t == THL_E2M1X2 || t == 
 // kernels' rate.  Measured on fp8 rows 8 bytes past a 16-byte unit: 8192^3
 // 1007 us on the 4-byte kernel against 488 us rewritten, 4096^3 144 against
 // 96 us; with few tiles the 16-byte kernel is bound by load latency as well
-// and the pass does not pay (4097 x 1000 x 2040: 44.6 against 57.1 us;
-// 2048 x 2048 x 8192: 76 against 83 us).
+// and the pass does not pay (4097 x 1000 x 2040: 44.6 against 57.1 us, and
+// since the epilogue's element-aligned accesses 34.4 us on the 4-byte
+// kernel; 2048 x 2048 x 8192: 76 against 83 us).
 bool plan_stage(const thl_dtypes* dt, thl_op opA, thl_op opB, const thl_scales* sc, int64_t m, int64_t n, int64_t k,
                 const void* A, int64_t lda, const void* B, int64_t ldb, const Batch& bt, Stage* sg) {
   if (!dt) return false;
