@@ -997,6 +997,32 @@ def test_partial_round_of_256x256_tiles_beats_two_of_128x128(kind, shape):
         assert "_256x256_" in thl.thl_last_variant(), thl.thl_last_variant()
 
 
+def test_batched_problems_at_odd_element_offsets():
+    # batch strides of an odd number of elements: every other problem's C, D
+    # and bias start 2 bytes past a 4-byte unit, and every column run (ldc =
+    # ldd = 391) is off a 16-byte unit; the vector epilogue takes the
+    # interior tiles with element-aligned accesses, the general one the edge
+    # tiles; every output of every problem against the oracle
+    import tile_hierarchy_linear_amd as thl
+    import workloads as wl
+    from oracle import compare
+    from workloads.device import BatchedDeviceProblem
+
+    ws = [wl.make("bf16", 391, 259, 256, ldc=391, ldd=391, seed=120 + z) for z in range(4)]
+    bp = BatchedDeviceProblem(ws, pad=2)
+    assert bp.stride_d % 2 == 1 and bp.strides["c"] % 2 == 1 and bp.strides["bias"] % 2 == 1, \
+        (bp.stride_d, bp.strides)
+    _say(f"[batched, odd element offsets] strides d={bp.stride_d} {bp.strides}")
+    assert bp.run() == 0
+    torch.cuda.synchronize()
+    _say(f"   ran {thl.thl_last_variant()}")
+    for z, w in enumerate(ws):
+        got = bp.d_all(z)
+        ii, jj = np.meshgrid(np.arange(w.m), np.arange(w.n), indexing="ij")
+        res = compare.parity_check(w, got.ravel(), ii.ravel(), jj.ravel())
+        assert res["ok"], (z, res)
+
+
 def test_one_round_batched_and_grouped():
     # four problems of 15 tiles each share one round; the batched and the
     # grouped launch both take the six-stage variant
