@@ -1776,6 +1776,39 @@ def test_16bit_base_off_4_bytes_and_no_alloc():
     assert torch.equal(dp.d[: w.n, : w.m], ref)
 
 
+@pytest.mark.parametrize("type_d", ["bf16", "f32"])
+def test_outputs_and_c_at_odd_element_offsets(type_d):
+    # D, C and bias based one element past a 16-byte unit (their leading
+    # dimensions whole units): every column run is off a 16-byte unit, and
+    # the vector epilogue takes them with element-aligned accesses; sampled
+    # outputs plus the last row and column against the oracle, and nothing
+    # written before D's first element
+    import workloads as wl
+    from oracle import compare
+    from workloads.device import DeviceProblem
+
+    w = wl.make("bf16", 4096, 512, 256, ldc=4096, ldd=4096, type_d=type_d)
+    dp = DeviceProblem(w)
+    for name in ("c", "bias"):
+        t = getattr(dp, name)
+        buf = torch.zeros(t.numel() + 2, dtype=torch.uint8, device="cuda")
+        buf[2:] = t.view(torch.uint8).reshape(-1)
+        setattr(dp, name, buf[2:])
+    es = dp.d.element_size()
+    dbuf = torch.full((dp.d.numel() + 1,), float("nan"), dtype=dp.d.dtype, device="cuda")
+    dp.d = dbuf[1:].view(dp.d.shape)
+    assert dp.d.data_ptr() % 16 == es and dp.c.data_ptr() % 4 == 2 and dp.bias.data_ptr() % 4 == 2
+    _say(f"[odd element offsets] D {type_d}")
+    assert dp.run() == 0
+    torch.cuda.synchronize()
+    rows, cols = w.sample(4096)
+    rows = np.concatenate([rows, np.full(w.n, w.m - 1), np.arange(w.m)])
+    cols = np.concatenate([cols, np.arange(w.n), np.full(w.m, w.n - 1)])
+    res = compare.parity_check(w, dp.d_values(rows, cols), rows, cols)
+    assert res["ok"], res
+    assert torch.isnan(dbuf[:1].float()).all()
+
+
 def test_16bit_batched_odd_leading_dimension():
     # three problems whose A lines (M-major, odd lda) fit no kernel: each
     # problem re-pitched at the batch stride of the copies
